@@ -1,0 +1,191 @@
+"""Independent CPU oracle for the S6 selective-scan forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()`` and by
+the CPU-baseline leg of ``bench.py``.  The GPU library never imports, links or calls
+anything here, and nothing here imports the GPU library.
+
+Two independent statements of the method live here:
+
+* ``fwd`` -- the plain sequential recurrence in double precision (``ssm_oracle.c``),
+  following the zero-order-hold discretisation and the recurrence/readout as written on
+  the "state-space models" page (aarnphm.xyz, sections "From continuous time to tokens"
+  and "One recurrence, one convolution") and the Algenta "Sequence and state-space
+  models" page (section on ``state_space_models``), with the feed-through and SiLU gate
+  of the TorchLean "Selective Mamba" page (``step``).
+* ``conv_ti`` -- for fixed (time-invariant) coefficients, the causal-convolution form of
+  the same layer with lag kernel K_k = C Abar^k Bbar ("state-space models", section "One
+  recurrence, one convolution"), written with numpy in float64 and sharing no code with
+  the recurrence.  Abar^k is evaluated as exp(k * delta * a), the exact composition of
+  k steps, not as a repeated product.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libssm_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ssm_oracle.c with gcc (-O2, no fast-math) into libssm_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-o", tmp, _SRC,
+                               "-lm", "-lpthread"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class OracleLib:
+    """ctypes view of one compiled oracle library (the default one, or a test-built variant)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        fp = ctypes.POINTER(ctypes.c_float)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.ssm_oracle_fwd.restype = ctypes.c_int
+        lib.ssm_oracle_fwd.argtypes = [fp, fp, fp, fp, fp, fp, fp, dp, dp, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+        lib.ssm_oracle_discretize.restype = None
+        lib.ssm_oracle_discretize.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, dp, dp]
+        self.lib = lib
+        self.path = path
+
+    def discretize(self, a: float, b: float, delta: float):
+        """ZOH coefficients (Abar, Bbar) of one scalar state."""
+        ab = ctypes.c_double()
+        bb = ctypes.c_double()
+        self.lib.ssm_oracle_discretize(float(a), float(b), float(delta), ctypes.byref(ab), ctypes.byref(bb))
+        return ab.value, bb.value
+
+    def fwd(self, u, delta, A, B, C, Dskip=None, z=None, *, time_invariant=False, want_last=True,
+            nthreads=None):
+        """Run the fp64 recurrence.  Returns (y [batch,L,D] float64, last_state [batch,D,N] float64
+        or None).
+
+        u, z: [batch, L, D]; delta: [batch, L, D] (time-invariant: [D]); B, C: [batch, L, N]
+        (time-invariant: [D, N]); A: [D, N]; Dskip: [D].  Inputs are converted to float32 first,
+        the precision the GPU library receives.
+        """
+        u = _f32(u)
+        delta = _f32(delta)
+        A = _f32(A)
+        B = _f32(B)
+        C = _f32(C)
+        Dskip = _f32(Dskip)
+        z = _f32(z)
+        batch, L, D = u.shape
+        N = A.shape[1]
+        assert A.shape == (D, N)
+        if time_invariant:
+            assert delta.shape == (D,) and B.shape == (D, N) and C.shape == (D, N)
+        else:
+            assert delta.shape == (batch, L, D) and B.shape == (batch, L, N) and C.shape == (batch, L, N)
+        if Dskip is not None:
+            assert Dskip.shape == (D,)
+        if z is not None:
+            assert z.shape == (batch, L, D)
+        y = np.empty((batch, L, D), dtype=np.float64)
+        last = np.empty((batch, D, N), dtype=np.float64) if want_last else None
+        if nthreads is None:
+            nthreads = os.cpu_count() or 1
+        rc = self.lib.ssm_oracle_fwd(
+            _fptr(u), _fptr(delta), _fptr(A), _fptr(B), _fptr(C), _fptr(Dskip), _fptr(z),
+            y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            None if last is None else last.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            batch, L, D, N, 1 if time_invariant else 0, int(nthreads))
+        if rc != 0:
+            raise RuntimeError("ssm_oracle_fwd failed with %d" % rc)
+        return y, last
+
+
+def _load() -> OracleLib:
+    global _lib
+    if _lib is None:
+        _lib = OracleLib(build())
+    return _lib
+
+
+def _fptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _f32(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def discretize(a: float, b: float, delta: float):
+    """ZOH coefficients (Abar, Bbar) of one scalar state, from the C oracle."""
+    return _load().discretize(a, b, delta)
+
+
+def fwd(u, delta, A, B, C, Dskip=None, z=None, *, time_invariant=False, want_last=True, nthreads=None):
+    """The fp64 recurrence of the default oracle library; see ``OracleLib.fwd``."""
+    return _load().fwd(u, delta, A, B, C, Dskip, z, time_invariant=time_invariant, want_last=want_last,
+                       nthreads=nthreads)
+
+
+def kernel_element(c: float, abar_power: float, bbar: float) -> float:
+    """One lag-kernel term C * Abar^k * Bbar for a single state (the factor the caller
+    sums over states and lags)."""
+    return float(c) * float(abar_power) * float(bbar)
+
+
+def ti_kernel(delta, A, B, C, L: int):
+    """Lag kernel K[k, d] = sum_n C[d,n] * exp(k*delta[d]*A[d,n]) * Bbar[d,n], k = 0..L-1,
+    in float64, with Bbar = expm1(delta*a)/a * b (delta * b when a == 0)."""
+    delta = np.asarray(delta, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    C = np.asarray(C, dtype=np.float64)
+    dA = delta[:, None] * A
+    with np.errstate(divide="ignore", invalid="ignore"):
+        coeff = np.where(A != 0.0, np.expm1(dA) / np.where(A != 0.0, A, 1.0), delta[:, None])
+    bbar = coeff * B
+    k = np.arange(L, dtype=np.float64)[:, None, None]
+    powers = np.exp(k * dA[None, :, :])                      # Abar^k = exp(k * delta * a)
+    return np.einsum("kdn,dn->kd", powers * C[None], bbar)    # [L, D]
+
+
+def conv_ti(u, delta, A, B, C, Dskip=None):
+    """Causal convolution y[b,t,d] = sum_{j<=t} K[t-j,d] u[b,j,d] + Dskip[d] u[b,t,d] (float64).
+
+    Uses an FFT of length >= 2L per channel (zero padded, so the circular product equals the
+    linear causal one)."""
+    u = np.asarray(u, dtype=np.float64)
+    batch, L, D = u.shape
+    K = ti_kernel(delta, A, B, C, L)
+    nfft = 1
+    while nfft < 2 * L:
+        nfft *= 2
+    Kf = np.fft.rfft(K, n=nfft, axis=0)                       # [F, D]
+    Uf = np.fft.rfft(u, n=nfft, axis=1)                       # [batch, F, D]
+    y = np.fft.irfft(Uf * Kf[None], n=nfft, axis=1)[:, :L, :]
+    if Dskip is not None:
+        y = y + np.asarray(Dskip, dtype=np.float64)[None, None, :] * u
+    return y
+
+
+def conv_ti_direct(u, delta, A, B, C, Dskip=None):
+    """The same causal convolution as an explicit double sum (O(L^2) per channel); for
+    small inputs."""
+    u = np.asarray(u, dtype=np.float64)
+    batch, L, D = u.shape
+    K = ti_kernel(delta, A, B, C, L)
+    y = np.zeros_like(u)
+    for t in range(L):
+        # sum_j K[t-j] u[j], j = 0..t
+        y[:, t, :] = np.einsum("jd,bjd->bd", K[t::-1], u[:, : t + 1, :])
+    if Dskip is not None:
+        y = y + np.asarray(Dskip, dtype=np.float64)[None, None, :] * u
+    return y

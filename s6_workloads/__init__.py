@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs for the S6 selective-scan forward.
+
+This module only draws random numbers and lays them out; it holds none of the scan's
+arithmetic.  It is shared by the tests, the smoke check and the benchmark so that the
+GPU library and the oracle always see the same inputs.
+
+Distributions follow the canonical S6 initialisation described in the rustytorch commit
+log ("canonical S6 init": A = -(1..N) from A_log = ln(1..N), a time step whose softplus is
+about 0.01, D = 1): A[d, n] = -(n + 1), Dskip = 1, and log-uniform step sizes in
+[1e-3, 1e-1].  u, B, C and z are standard normal.  Every workload below is synthetic;
+the pages measure nothing on a public dataset for this path.
+
+Draw order inside one workload: u, delta (or the softplus pre-activation g), B, C, z,
+each drawn in float64 from numpy's PCG64 with seed 1000 + workload number, then cast to
+float32 and, for bf16-I/O workloads, rounded to bfloat16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+# name -> spec.  "number" fixes the seed (1000 + number).
+WORKLOADS = {
+    "tiny_f32": dict(number=1, batch=1, L=64, D=4, N=4, io="f32", gate=False, last=True, ti=False,
+                     a_scale=1.0, delta="loguniform"),
+    "small_f32": dict(number=2, batch=2, L=1024, D=256, N=16, io="f32", gate=True, last=True, ti=False,
+                      a_scale=1.0, delta="loguniform"),
+    "mamba130m_f32": dict(number=3, batch=8, L=2048, D=1536, N=16, io="f32", gate=True, last=True, ti=False,
+                          a_scale=1.0, delta="loguniform"),
+    "longctx_bf16": dict(number=4, batch=4, L=16384, D=2560, N=16, io="bf16", gate=True, last=False,
+                         ti=False, a_scale=1.0, delta="softplus_normal"),
+    "s4d_ti_f32": dict(number=5, batch=4, L=8192, D=1024, N=64, io="f32", gate=False, last=False, ti=True,
+                       a_scale=0.5, delta="loguniform"),
+}
+
+VARIANTS = ("default", "scan_only", "active", "active_const")
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32 values
+    that are exactly representable in bfloat16.  Inputs here are finite."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    rounded = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
+    return rounded.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """The bfloat16 bit patterns (uint16) of float32 values that are already bf16-exact."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    """log(1 + e^x) in the overflow-free form log1p(e^-|x|) + max(x, 0); used only to draw
+    the step sizes of the long-context workload from a pre-activation."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.log1p(np.exp(-np.abs(x))) + np.maximum(x, 0.0)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """One workload's tensors as float32 numpy arrays (bf16 workloads: bf16-exact values)."""
+    name: str
+    io: str                       # "f32" or "bf16"
+    ti: bool                      # time-invariant: delta [D], B and C [D, N]
+    u: np.ndarray                 # [batch, L, D]
+    delta: np.ndarray             # [batch, L, D] or [D]
+    A: np.ndarray                 # [D, N]
+    B: np.ndarray                 # [batch, L, N] or [D, N]
+    C: np.ndarray                 # [batch, L, N] or [D, N]
+    Dskip: Optional[np.ndarray]   # [D] or None
+    z: Optional[np.ndarray]       # [batch, L, D] or None
+    want_last: bool
+
+    @property
+    def shape(self):
+        b, L, D = self.u.shape
+        return b, L, D, self.A.shape[1]
+
+    @property
+    def elements(self) -> int:
+        b, L, D, N = self.shape
+        return b * L * D * N
+
+
+def spec(name: str) -> dict:
+    return dict(WORKLOADS[name])
+
+
+def generate(name: str, variant: str = "default", *, seed: Optional[int] = None, batch: Optional[int] = None,
+             L: Optional[int] = None, D: Optional[int] = None, N: Optional[int] = None,
+             gate: Optional[bool] = None) -> Inputs:
+    """Draw a workload's inputs.  ``batch``/``L``/``D``/``N`` override the sizes (for
+    reduced parity cases); ``variant`` is one of VARIANTS:
+
+    * default      -- the workload as specified;
+    * scan_only    -- no feed-through and no gate, so y is the scan term alone;
+    * active       -- step sizes log-uniform in [0.1, 1] (large per-step decay);
+    * active_const -- every step size equal to 0.69 (about log 2).
+    """
+    if variant not in VARIANTS:
+        raise ValueError("unknown variant %r" % variant)
+    s = spec(name)
+    b = s["batch"] if batch is None else batch
+    Lq = s["L"] if L is None else L
+    Dq = s["D"] if D is None else D
+    Nq = s["N"] if N is None else N
+    use_gate = s["gate"] if gate is None else gate
+    rng = np.random.Generator(np.random.PCG64(1000 + s["number"] if seed is None else seed))
+    ti = s["ti"]
+
+    u = rng.standard_normal((b, Lq, Dq))
+    dshape = (Dq,) if ti else (b, Lq, Dq)
+    if variant == "active":
+        delta = np.exp(rng.uniform(np.log(0.1), np.log(1.0), dshape))
+    elif variant == "active_const":
+        delta = np.full(dshape, 0.69)
+    elif s["delta"] == "loguniform":
+        delta = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), dshape))
+    elif s["delta"] == "softplus_normal":
+        delta = softplus(rng.normal(-4.6, 0.5, dshape))
+    else:
+        raise ValueError(s["delta"])
+    bcshape = (Dq, Nq) if ti else (b, Lq, Nq)
+    B = rng.standard_normal(bcshape)
+    C = rng.standard_normal(bcshape)
+    z = rng.standard_normal((b, Lq, Dq)) if use_gate else None
+    A = -(np.arange(Nq, dtype=np.float64) + 1.0)[None, :].repeat(Dq, axis=0) * s["a_scale"]
+    Dskip = np.ones(Dq)
+
+    f32 = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+    u, delta, B, C, z, A, Dskip = map(f32, (u, delta, B, C, z, A, Dskip))
+    if s["io"] == "bf16":
+        u, delta, B, C = bf16_round(u), bf16_round(delta), bf16_round(B), bf16_round(C)
+        z = None if z is None else bf16_round(z)
+    if variant == "scan_only":
+        Dskip, z = None, None
+    return Inputs(name=name, io=s["io"], ti=ti, u=u, delta=delta, A=A, B=B, C=C, Dskip=Dskip, z=z,
+                  want_last=s["last"])
+
+
+def sample_channels(D: int, count: int, seed: int = 7) -> np.ndarray:
+    """A sorted, seeded sample of channel indices that always includes the first and last
+    channel (ragged edges) and a few channel-tile boundaries."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    must = {0, D - 1, min(D - 1, 3), min(D - 1, 4), min(D - 1, 63), min(D - 1, 64)}
+    extra = rng.choice(D, size=min(D, max(0, count - len(must))), replace=False)
+    return np.array(sorted(must.union(int(x) for x in extra)), dtype=np.int64)
