@@ -1,0 +1,241 @@
+"""Benchmark of the S6 selective-scan forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one selective_scan_fwd call over the whole workload (every row of the hot
+path: discretisation, recurrence, readout, feed-through, gate, store) with its inputs
+already resident in HBM.  The default workload is the long-context one the throughput
+target is stated on: batch 4, L 16384, D 2560, N 16, bf16 I/O with fp32 state, SiLU gate.
+Inputs are seeded synthetic data (s6_workloads), copied to the GPU once before timing.
+
+Prints ONE JSON line: elements/s (batch*L*D*N per second) as `value`, the algorithmic HBM
+bandwidth, the roofline of the scan kernel, and the CPU oracle timed on this host on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import s6_workloads  # noqa: E402
+
+METRIC = "scan elements/s (B*L*D*N per sec) + achieved HBM GB/s vs peak, 1 MI355X"
+HBM_PEAK_GBS = 8000.0            # MI355X published HBM3E bandwidth
+VALU_PEAK_TFLOPS = 157.3         # MI355X published fp32 vector peak (FMA = 2 flops)
+KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", "scan_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "scan_counters.json")
+
+# Algorithmic ALU work, in FMA-slot units (one fp32 VALU op = 1 slot = 2 flop-equivalents;
+# a quarter-rate transcendental = 4 slots):
+#   per (b, l, d, n): delta*A (1) + exp (4) + (Abar-1)/A as one FMA (1) + B*u (1) + times (1)
+#                     + state FMA (1) + readout FMA (1)                               = 10
+#   per (b, l, d):    feed-through FMA (1); gate: -z*log2e (1) + exp (4) + 1+e (1) + rcp (4)
+#                     + z*r (1) + y*silu (1)                                          = 1 + 12
+#   time-invariant:   per (b, l, d, n): state FMA (1) + readout FMA (1)               = 2
+SLOTS_PER_ELEMENT = {"selective": 10, "time_invariant": 2}
+SLOTS_PER_TOKEN_D = 1
+SLOTS_PER_TOKEN_GATE = 12
+
+
+def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool) -> int:
+    """Bytes the method must move: u, delta, z read once and y written once per (b, l, d);
+    B and C once; A, Dskip once; last_state once.  No expanded (x N) state touches HBM."""
+    b, L, D, N = inp.shape
+    es = 2 if inp.io == "bf16" else 4
+    tok = b * L * D
+    total = tok * es * 2                                       # u read, y written
+    total += (D if inp.ti else tok) * es                       # delta
+    if inp.z is not None:
+        total += tok * es
+    total += 2 * (D * N if inp.ti else b * L * N) * es        # B, C
+    total += D * N * 4                                          # A
+    if inp.Dskip is not None:
+        total += D * 4
+    if want_last:
+        total += b * D * N * 4
+    return total
+
+
+def algorithmic_slots(inp: s6_workloads.Inputs) -> int:
+    b, L, D, N = inp.shape
+    per_el = SLOTS_PER_ELEMENT["time_invariant" if inp.ti else "selective"]
+    slots = per_el * b * L * D * N
+    if inp.Dskip is not None:
+        slots += SLOTS_PER_TOKEN_D * b * L * D
+    if inp.z is not None:
+        slots += SLOTS_PER_TOKEN_GATE * b * L * D
+    return slots
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, per_launch_alg_bytes: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return int(entry["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0):
+    """The oracle (fp64, as it stands) on a bounded sample of the workload's channels,
+    timed on this host; scaled to elements/s."""
+    import oracle
+    cores = min(16, os.cpu_count() or 1)
+    b, L, D, N = inp.shape
+    oracle.build()
+    nch = min(D, max(cores, 8))
+    t_used = 0.0
+    while True:
+        ch = np.arange(nch)
+        sub = s6_workloads.select_channels(inp, ch)
+        t0 = time.perf_counter()
+        oracle.fwd(sub.u, sub.delta, sub.A, sub.B, sub.C, sub.Dskip, sub.z, time_invariant=sub.ti,
+                   want_last=False, nthreads=cores)
+        t_used = time.perf_counter() - t0
+        if t_used >= target_s * 0.5 or nch >= D:
+            break
+        nch = min(D, int(nch * max(2.0, target_s / max(t_used, 1e-3))))
+    elements = b * L * nch * N
+    return {"value": elements / t_used, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d channels (all %d batch rows x %d tokens x %d states), fp64 recurrence, %.1f s wall"
+                      % (nch, D, b, L, N, t_used)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="longctx_bf16", choices=sorted(s6_workloads.WORKLOADS))
+    ap.add_argument("--path", default="auto", choices=["auto", "single", "chunked"])
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the scan shards over batch/channels with no "
+              "communication; see DESIGN.md); --gpus %d is not supported" % max(args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_s6_amd as ss
+
+    spec = s6_workloads.spec(args.workload)
+    inp = s6_workloads.generate(args.workload)
+    want_last = bool(spec["last"])
+    b, L, D, N = inp.shape
+    E = b * L * D * N
+    io = inp.io
+
+    def dev(x):
+        if x is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+        return t.to(torch.bfloat16) if io == "bf16" else t
+
+    u, delta, B, C, z = dev(inp.u), dev(inp.delta), dev(inp.B), dev(inp.C), dev(inp.z)
+    A = torch.from_numpy(inp.A).cuda()
+    Ds = None if inp.Dskip is None else torch.from_numpy(inp.Dskip).cuda()
+    y = torch.empty_like(u)
+    last = torch.empty((b, D, N), dtype=torch.float32, device="cuda") if want_last else None
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ss.selective_scan_fwd(u, delta, A, B, C, Ds, z, y=y, last_state=last, path=args.path,
+                              stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # one GPU: the barrier is the device synchronisation itself
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    dims = ss.make_dims(u, delta, A, B, C, z, y, path=args.path)
+    chunked = ss.workspace_size(dims) > 0
+    alg_bytes = algorithmic_bytes(inp, want_last)
+    slots = algorithmic_slots(inp)
+    launch_s = launch_ms * 1e-3
+    hbm_gbs = alg_bytes / launch_s / 1e9
+    alu_tflops = 2.0 * slots / launch_s / 1e12
+    traffic = measured_traffic(args.workload, alg_bytes)
+    # the binding roof: the larger of the two lower bounds on time
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
+    t_alu = 2.0 * slots / (VALU_PEAK_TFLOPS * 1e12)
+    if t_alu >= t_hbm:
+        roof = {"bound": "alu", "achieved": round(alu_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(alu_tflops / VALU_PEAK_TFLOPS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    out = {
+        "metric": METRIC,
+        "value": E * args.steps / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, s6_workloads: %s)" % args.workload,
+        "config": {"workload": args.workload, "batch": b, "seq_len": L, "dim": D, "dstate": N, "io": io,
+                   "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
+                   "last_state": want_last, "time_invariant": inp.ti, "path": "chunked" if chunked else "single"},
+        "kernel_ms": launch_ms,
+        "hbm_gbs": round(hbm_gbs, 1),
+        "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": alg_bytes,
+        "algorithmic_slots": slots,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

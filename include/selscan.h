@@ -1,0 +1,181 @@
+/*
+ * selscan.h -- C ABI of the MI355X (gfx950) selective-scan forward library, libselscan.so.
+ *
+ * The operation (one call computes all of it, on the GPU, asynchronously on `stream`):
+ *
+ *   for every batch row b and channel d, with h = 0 before the first token
+ *   ("state-space models", aarnphm.xyz, section "One recurrence, one convolution": the
+ *   unrolled recurrence starts from a zero state):
+ *     for l = 0 .. L-1:
+ *       for n = 0 .. N-1:
+ *         Abar = exp(delta[b,l,d] * A[d,n])                       zero-order hold, diagonal A
+ *         Bbar = (Abar - 1) / A[d,n] * B[b,l,n]   (delta*B if A[d,n] == 0)
+ *         h[n] = Abar * h[n] + Bbar * u[b,l,d]
+ *       y[b,l,d] = sum_n C[b,l,n] * h[n] + Dskip[d] * u[b,l,d]
+ *       if z:  y[b,l,d] *= z[b,l,d] * sigmoid(z[b,l,d])
+ *     last_state[b,d,:] = h
+ *
+ *   Sources: the ZOH equations of "state-space models" (section "From continuous time to
+ *   tokens"); the per-element discretisation functions and their A == 0 fallback on the
+ *   Algenta page "Sequence and state-space models" (section on state_space_models); the
+ *   selective mechanism (per-token delta, B, C with a fixed diagonal A; B and C shared by
+ *   all channels of a token) of "state-space models" (section "Mamba") and the TorchLean
+ *   page "Selective Mamba" (Parameters bProj/cProj); the readout of the updated state,
+ *   the D * u feed-through and the SiLU gate of "Selective Mamba" (step); the final state
+ *   a following chunk resumes from of "Selective Mamba" (State.hidden, runArray).
+ *
+ * Time-invariant mode (fixed coefficients, "state-space models", section "One recurrence,
+ * one convolution"): delta is one value per channel and B, C are one N-vector per channel,
+ * expressed through strides (see selscan_dims).  The same recurrence is evaluated.
+ *
+ * Arithmetic: inputs are read in their I/O type and widened to fp32; the state, the
+ * discretisation and the reduction over states run in fp32; y is rounded to the I/O type
+ * (round-to-nearest-even for bf16).  A, Dskip and last_state are always fp32.  Values are
+ * not validated: a positive A or a huge delta may overflow to Inf/NaN, which propagates.
+ *
+ * Ownership: every tensor pointer is caller-owned device memory on the HIP device that is
+ * current when the call is made.  The library keeps no pointer after the call returns and
+ * writes only y, last_state and (chunked path) its workspace.  y and last_state must not
+ * overlap any input.  The call only enqueues work on `stream` (a hipStream_t; NULL = the
+ * null stream) and returns; it never synchronises.  Inputs must stay valid and unchanged
+ * until the enqueued work has run.
+ *
+ * Errors: every entry point returns an int status (enum selscan_status).  Argument errors
+ * are detected on the host before anything is enqueued, so nothing runs when a call
+ * fails.  No exception crosses the ABI.  Calls on different streams are independent; the
+ * library holds no global mutable state except a thread-local last HIP error code.
+ */
+#ifndef SELSCAN_H_
+#define SELSCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SELSCAN_ABI_VERSION 1
+
+/* Element type of u, delta, B, C, z and y. */
+enum selscan_dtype {
+  SELSCAN_F32 = 0,  /* IEEE binary32 */
+  SELSCAN_BF16 = 1  /* bfloat16 (upper 16 bits of binary32) */
+};
+
+enum selscan_status {
+  SELSCAN_OK = 0,
+  SELSCAN_ERR_NULL = -1,        /* a required pointer (u, delta, A, B, C, y, dims) is NULL;
+                                   only A and dims are required when batch * seqlen == 0 */
+  SELSCAN_ERR_DIMS = -2,        /* batch < 0, seqlen < 0, dim < 1, dstate < 1, or a negative stride */
+  SELSCAN_ERR_UNSUPPORTED = -3, /* dstate > 64, unknown dtype or path, or a B/C/delta stride
+                                   pattern that is neither per-token (shared over channels)
+                                   nor per-channel (time-invariant) */
+  SELSCAN_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
+  SELSCAN_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed; the HIP error
+                                   code is available from selective_scan_last_hip_error() */
+  SELSCAN_ERR_WORKSPACE = -6,   /* workspace pointer NULL or smaller than
+                                   selective_scan_workspace_size() */
+  SELSCAN_ERR_ABI = -7          /* dims->abi_version != SELSCAN_ABI_VERSION */
+};
+
+/* Which kernel schedule to run.  AUTO picks by shape; the others exist for tests and
+ * measurements and give results equal to AUTO within the fp32 rounding of a different
+ * association order. */
+enum selscan_path {
+  SELSCAN_PATH_AUTO = 0,
+  SELSCAN_PATH_SINGLE = 1,   /* one pass along the sequence per (batch, channel group) */
+  SELSCAN_PATH_CHUNKED = 2   /* two passes over chunks of the sequence, joined by a scan
+                                of per-chunk affine maps */
+};
+
+/*
+ * Sizes and strides.  All strides are in ELEMENTS (not bytes), must be >= 0, and the
+ * innermost axis of every tensor is unit-stride:
+ *   u[b,l,d]     at u     + b*u_sb     + l*u_sl     + d
+ *   delta[b,l,d] at delta + b*delta_sb + l*delta_sl + d
+ *   z[b,l,d]     at z     + b*z_sb     + l*z_sl     + d        (if z != NULL)
+ *   y[b,l,d]     at y     + b*y_sb     + l*y_sl     + d
+ *   B[b,l,d,n]   at B     + b*B_sb     + l*B_sl     + d*B_sd + n   (same for C)
+ *   A[d,n]       at A + d*dstate + n          (contiguous [dim][dstate])
+ *   Dskip[d]     at Dskip + d                 (contiguous [dim])
+ *   last_state[b,d,n] at last_state + (b*dim + d)*dstate + n   (contiguous [batch][dim][dstate])
+ * Two stride patterns are supported:
+ *   selective:       B_sd == 0 and C_sd == 0 (B, C per token, shared over channels);
+ *                    delta may be per token or, with delta_sb == delta_sl == 0, per channel.
+ *   time-invariant:  B_sb == B_sl == C_sb == C_sl == 0 and delta_sb == delta_sl == 0
+ *                    (B, C one vector per channel, delta one value per channel).
+ */
+typedef struct selscan_dims {
+  int32_t abi_version;  /* must be SELSCAN_ABI_VERSION */
+  int32_t io_dtype;     /* enum selscan_dtype */
+  int64_t batch;        /* B >= 0 */
+  int64_t seqlen;       /* L >= 0 */
+  int64_t dim;          /* D >= 1 (channels) */
+  int64_t dstate;       /* N, 1 .. 64 (states per channel) */
+  int64_t u_sb, u_sl;
+  int64_t delta_sb, delta_sl;
+  int64_t z_sb, z_sl;
+  int64_t y_sb, y_sl;
+  int64_t B_sb, B_sl, B_sd;
+  int64_t C_sb, C_sl, C_sd;
+  int32_t path;         /* enum selscan_path; 0 = automatic */
+  int32_t chunk_len;    /* chunked path: tokens per chunk, a multiple of 16 (0 = automatic) */
+} selscan_dims;
+
+/* Fill *dims for contiguous tensors: u, delta, z, y as [batch][seqlen][dim]; B, C as
+ * [batch][seqlen][dstate].  With time_invariant != 0: delta as [dim] and B, C as
+ * [dim][dstate].  path = AUTO, chunk_len = 0.  Never fails for a non-NULL dims. */
+void selscan_dims_init(selscan_dims* dims, int io_dtype, int64_t batch, int64_t seqlen,
+                       int64_t dim, int64_t dstate, int time_invariant);
+
+/*
+ * selective_scan_fwd -- enqueue the selective-scan forward pass described above.
+ *   u, delta, B, C : inputs in dims->io_dtype, required (non-NULL)
+ *   A              : [dim][dstate] fp32, required
+ *   Dskip          : [dim] fp32, or NULL for no feed-through term
+ *   z              : gate input in dims->io_dtype, or NULL for no gate
+ *   y              : output in dims->io_dtype, required
+ *   last_state     : [batch][dim][dstate] fp32 output, or NULL to skip it
+ *   dims           : sizes, strides and path selection, required
+ *   stream         : hipStream_t to enqueue on (NULL = null stream)
+ * When batch * seqlen == 0 the per-token tensors (u, delta, B, C, z, y) are not read and
+ * may be NULL; A is always required.
+ * batch == 0 enqueues nothing.  seqlen == 0 writes nothing to y and, if last_state is
+ * given, fills it with zeros (an empty sequence leaves the zero initial state; TorchLean
+ * "Selective Mamba", runArray).  The chunked path needs device scratch; this entry point
+ * takes it with hipMallocAsync/hipFreeAsync on `stream` (stream-ordered).
+ * Returns SELSCAN_OK or an error status; on error nothing was enqueued, except that
+ * SELSCAN_ERR_HIP may follow a partially enqueued sequence of launches.
+ */
+int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                       const void* C, const float* Dskip, const void* z, void* y,
+                       float* last_state, const selscan_dims* dims, void* stream);
+
+/* Bytes of device workspace the chunked path needs for these dims (0 when the automatic
+ * or forced path is the single pass).  Returns 0 for invalid dims. */
+size_t selective_scan_workspace_size(const selscan_dims* dims);
+
+/* selective_scan_fwd with caller-provided workspace (device memory, 256-byte aligned,
+ * at least selective_scan_workspace_size(dims) bytes; may be NULL when that size is 0).
+ * Never allocates.  The workspace must not be used by other work until the enqueued
+ * scan has finished on `stream`. */
+int selective_scan_fwd_ws(const void* u, const void* delta, const float* A, const void* B,
+                          const void* C, const float* Dskip, const void* z, void* y,
+                          float* last_state, const selscan_dims* dims, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* selective_scan_strerror(int status);
+
+/* The hipError_t of the most recent SELSCAN_ERR_HIP returned on this thread (0 if none). */
+int selective_scan_last_hip_error(void);
+
+/* SELSCAN_ABI_VERSION of the loaded library. */
+int selective_scan_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SELSCAN_H_ */

@@ -149,3 +149,18 @@ def sample_channels(D: int, count: int, seed: int = 7) -> np.ndarray:
     must = {0, D - 1, min(D - 1, 3), min(D - 1, 4), min(D - 1, 63), min(D - 1, 64)}
     extra = rng.choice(D, size=min(D, max(0, count - len(must))), replace=False)
     return np.array(sorted(must.union(int(x) for x in extra)), dtype=np.int64)
+
+
+def select_channels(inp: Inputs, ch) -> Inputs:
+    """The same workload restricted to channels ``ch``.  In the selective mode B and C are
+    shared by all channels of a token, so the restriction is exact."""
+    ch = np.asarray(ch)
+    sub = lambda a: None if a is None else np.ascontiguousarray(a[..., ch])
+    return Inputs(
+        name=inp.name, io=inp.io, ti=inp.ti, u=sub(inp.u),
+        delta=np.ascontiguousarray(inp.delta[ch]) if inp.ti else sub(inp.delta),
+        A=np.ascontiguousarray(inp.A[ch]),
+        B=np.ascontiguousarray(inp.B[ch]) if inp.ti else inp.B,
+        C=np.ascontiguousarray(inp.C[ch]) if inp.ti else inp.C,
+        Dskip=None if inp.Dskip is None else np.ascontiguousarray(inp.Dskip[ch]),
+        z=sub(inp.z), want_last=inp.want_last)

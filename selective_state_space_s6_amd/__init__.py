@@ -1,0 +1,231 @@
+"""MI355X (gfx950) selective-scan forward (S6): a thin Python binding over libselscan.so.
+
+Every step of the computation runs in the HIP kernels of ``csrc/``; this module only
+marshals torch tensors (device memory) and the current HIP stream into the C ABI declared
+in ``include/selscan.h``, and raises on a non-zero status.  There is no fallback: if the
+library is not built, importing the binding's functions raises.
+
+    y, last = selective_scan_fwd(u, delta, A, B, C, Dskip, z, return_last_state=True)
+
+Shapes (torch tensors on the current GPU):
+    u, z           [batch, L, D]        float32 or bfloat16 (same dtype for u, delta, B, C, z)
+    delta          [batch, L, D]        (selective) or [D] (time-invariant)
+    A              [D, N] float32
+    B, C           [batch, L, N]        (selective) or [D, N] (time-invariant)
+    Dskip          [D] float32 or None
+The innermost axis of every tensor must be unit-stride; other strides are passed through
+(zero strides, i.e. expanded views, are allowed).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libselscan.so")
+
+SELSCAN_ABI_VERSION = 1
+SELSCAN_F32, SELSCAN_BF16 = 0, 1
+SELSCAN_OK = 0
+SELSCAN_ERR_NULL, SELSCAN_ERR_DIMS, SELSCAN_ERR_UNSUPPORTED = -1, -2, -3
+SELSCAN_ERR_ALIGN, SELSCAN_ERR_HIP, SELSCAN_ERR_WORKSPACE, SELSCAN_ERR_ABI = -4, -5, -6, -7
+PATHS = {"auto": 0, "single": 1, "chunked": 2}
+
+
+class SelscanDims(ctypes.Structure):
+    """Mirror of ``selscan_dims`` in include/selscan.h (same field order and types)."""
+    _fields_ = [
+        ("abi_version", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("u_sb", ctypes.c_int64), ("u_sl", ctypes.c_int64),
+        ("delta_sb", ctypes.c_int64), ("delta_sl", ctypes.c_int64),
+        ("z_sb", ctypes.c_int64), ("z_sl", ctypes.c_int64),
+        ("y_sb", ctypes.c_int64), ("y_sl", ctypes.c_int64),
+        ("B_sb", ctypes.c_int64), ("B_sl", ctypes.c_int64), ("B_sd", ctypes.c_int64),
+        ("C_sb", ctypes.c_int64), ("C_sl", ctypes.c_int64), ("C_sd", ctypes.c_int64),
+        ("path", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
+    ]
+
+
+class SelscanError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = "%s failed: %s (status %d)" % (where, strerror(status), status)
+        if status == SELSCAN_ERR_HIP:
+            msg += ", hipError %d" % last_hip_error()
+        super().__init__(msg)
+
+
+_lib = None
+
+# (name, restype, argtypes) of every exported entry point
+_VP = ctypes.c_void_p
+_SIGNATURES = [
+    ("selscan_dims_init", None, [ctypes.POINTER(SelscanDims), ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
+    ("selective_scan_fwd", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP]),
+    ("selective_scan_workspace_size", ctypes.c_size_t, [ctypes.POINTER(SelscanDims)]),
+    ("selective_scan_fwd_ws", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
+    ("selective_scan_strerror", ctypes.c_char_p, [ctypes.c_int]),
+    ("selective_scan_last_hip_error", ctypes.c_int, []),
+    ("selective_scan_abi_version", ctypes.c_int, []),
+]
+
+
+def lib():
+    """The loaded libselscan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libselscan.so is not built (expected at %s); run "
+                               "`python -m selective_state_space_s6_amd.build`" % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, res, args in _SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        if handle.selective_scan_abi_version() != SELSCAN_ABI_VERSION:
+            raise RuntimeError("libselscan.so ABI version mismatch")
+        _lib = handle
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().selective_scan_strerror(int(status)).decode()
+
+
+def last_hip_error() -> int:
+    return int(lib().selective_scan_last_hip_error())
+
+
+def abi_version() -> int:
+    return int(lib().selective_scan_abi_version())
+
+
+def dims_init(io_dtype: int, batch: int, seqlen: int, dim: int, dstate: int, time_invariant: bool = False) -> SelscanDims:
+    d = SelscanDims()
+    lib().selscan_dims_init(ctypes.byref(d), int(io_dtype), int(batch), int(seqlen), int(dim), int(dstate),
+                            1 if time_invariant else 0)
+    return d
+
+
+def workspace_size(dims: SelscanDims) -> int:
+    return int(lib().selective_scan_workspace_size(ctypes.byref(dims)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _io_code(dtype):
+    import torch
+    if dtype == torch.float32:
+        return SELSCAN_F32
+    if dtype == torch.bfloat16:
+        return SELSCAN_BF16
+    raise TypeError("u/delta/B/C/z/y must be float32 or bfloat16, got %s" % dtype)
+
+
+def _strides_bld(t, name, batch, L, D):
+    """(sb, sl) element strides of a [batch, L, D] tensor whose last axis is unit-stride."""
+    if t.dim() != 3 or tuple(t.shape) != (batch, L, D):
+        raise ValueError("%s must have shape %s, got %s" % (name, (batch, L, D), tuple(t.shape)))
+    if D > 1 and t.stride(2) != 1:
+        raise ValueError("%s: the channel axis must be unit-stride" % name)
+    return t.stride(0), t.stride(1)
+
+
+def make_dims(u, delta, A, B, C, z=None, y=None, *, path: str = "auto", chunk_len: int = 0) -> SelscanDims:
+    """Build selscan_dims from tensor shapes and strides (see the module docstring)."""
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, L, D]")
+    batch, L, D = (int(x) for x in u.shape)
+    if A.dim() != 2 or int(A.shape[0]) != D:
+        raise ValueError("A must be [D, N]")
+    N = int(A.shape[1])
+    d = SelscanDims()
+    d.abi_version = SELSCAN_ABI_VERSION
+    d.io_dtype = _io_code(u.dtype)
+    d.batch, d.seqlen, d.dim, d.dstate = batch, L, D, N
+    d.u_sb, d.u_sl = _strides_bld(u, "u", batch, L, D)
+    if delta.dim() == 1:
+        if int(delta.shape[0]) != D or (D > 1 and delta.stride(0) != 1):
+            raise ValueError("per-channel delta must be a contiguous [D] tensor")
+        d.delta_sb = d.delta_sl = 0
+    else:
+        d.delta_sb, d.delta_sl = _strides_bld(delta, "delta", batch, L, D)
+    for name, t in (("B", B), ("C", C)):
+        if t.dim() == 2:
+            if tuple(t.shape) != (D, N) or (N > 1 and t.stride(1) != 1):
+                raise ValueError("per-channel %s must be [D, N] with a unit-stride state axis" % name)
+            sb, sl, sd = 0, 0, t.stride(0)
+        elif t.dim() == 3:
+            if tuple(t.shape) != (batch, L, N) or (N > 1 and t.stride(2) != 1):
+                raise ValueError("per-token %s must be [batch, L, N] with a unit-stride state axis" % name)
+            sb, sl, sd = t.stride(0), t.stride(1), 0
+        else:
+            raise ValueError("%s must be [batch, L, N] or [D, N]" % name)
+        setattr(d, name + "_sb", sb)
+        setattr(d, name + "_sl", sl)
+        setattr(d, name + "_sd", sd)
+    if z is not None:
+        d.z_sb, d.z_sl = _strides_bld(z, "z", batch, L, D)
+    if y is not None:
+        d.y_sb, d.y_sl = _strides_bld(y, "y", batch, L, D)
+    d.path = PATHS[path]
+    d.chunk_len = int(chunk_len)
+    return d
+
+
+def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state=None, *,
+                       return_last_state: bool = False, path: str = "auto", chunk_len: int = 0,
+                       workspace=None, stream=None) -> Tuple["object", Optional["object"]]:
+    """Selective-scan forward on the GPU.  Returns (y, last_state or None).
+
+    ``y`` / ``last_state`` may be given (outputs are written in place) or are allocated.
+    ``workspace`` (a uint8 CUDA tensor of at least ``workspace_size`` bytes) selects the
+    non-allocating entry point.  ``stream`` defaults to torch's current stream."""
+    import torch
+    io = u.dtype
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
+        if t is not None and t.dtype != io:
+            raise TypeError("%s has dtype %s, expected %s like u" % (name, t.dtype, io))
+    if A.dtype != torch.float32 or not A.is_contiguous():
+        raise TypeError("A must be a contiguous float32 [D, N] tensor")
+    if Dskip is not None and (Dskip.dtype != torch.float32 or not Dskip.is_contiguous()):
+        raise TypeError("Dskip must be a contiguous float32 [D] tensor")
+    for name, t in (("u", u), ("delta", delta), ("A", A), ("B", B), ("C", C), ("Dskip", Dskip), ("z", z), ("y", y),
+                    ("last_state", last_state)):
+        if t is not None and not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+    if y is None:
+        y = torch.empty(u.shape, dtype=io, device=u.device)
+    batch, L, D = (int(x) for x in u.shape)
+    N = int(A.shape[1])
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, D, N), dtype=torch.float32, device=u.device)
+    if last_state is not None and (last_state.dtype != torch.float32 or not last_state.is_contiguous()
+                                   or tuple(last_state.shape) != (batch, D, N)):
+        raise ValueError("last_state must be a contiguous float32 [batch, D, N] tensor")
+    dims = make_dims(u, delta, A, B, C, z, y, path=path, chunk_len=chunk_len)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args = [_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(y), _ptr(last_state),
+            ctypes.byref(dims)]
+    if workspace is not None:
+        st = lib().selective_scan_fwd_ws(*args, _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                         ctypes.c_void_p(stream))
+        where = "selective_scan_fwd_ws"
+    else:
+        st = lib().selective_scan_fwd(*args, ctypes.c_void_p(stream))
+        where = "selective_scan_fwd"
+    if st != SELSCAN_OK:
+        raise SelscanError(st, where)
+    return y, last_state
+
+
+__all__ = ["selective_scan_fwd", "make_dims", "dims_init", "workspace_size", "strerror", "last_hip_error",
+           "abi_version", "lib", "SelscanDims", "SelscanError", "LIB_PATH"]

@@ -1,0 +1,616 @@
+// scan_kernels.hip -- gfx950 kernels of the selective-scan forward (S6).
+//
+// Recurrence per (batch b, channel d, state n), from a zero state:
+//   Abar = exp(delta * A),  Bbar = (Abar - 1)/A * B  (delta * B when A == 0),
+//   h = Abar * h + Bbar * u,  y = sum_n C h + Dskip * u,  y *= z * sigmoid(z).
+// Discretisation: "state-space models" (aarnphm.xyz), section "From continuous time to
+// tokens" (ZOH); Algenta "Sequence and state-space models", section on state_space_models
+// (ssm_discretize_zoh / ssm_discretize_b with the A == 0 fallback).  Selectivity and the
+// shared per-token B/C: "state-space models", section "Mamba"; TorchLean "Selective Mamba",
+// Parameters.  Readout of the updated state, feed-through, SiLU gate: "Selective Mamba",
+// step.  Chunk composition by the associative combine (A1,b1).(A2,b2) = (A2 A1, A2 b1 + b2):
+// chipfoundry glossary "State-Space Models & Long-Context Sequence Architectures (Mamba)",
+// Appendix Lab 3.
+//
+// Work decomposition (one wavefront = 64 lanes):
+//   lane = (c, s): c in [0, CW) is a channel of the wave's channel group, s in [0, S) a
+//   state slot; CW * S = 64.  Lane (c, s) owns the K states n = s + S*k of channel c, held
+//   in VGPRs.  The sequence is walked in tiles of 16 tokens.  For each tile the wave loads
+//   its operands with plain per-lane global loads (issued one tile ahead) and stages them
+//   in a wave-private LDS region: B and C transposed to [n][token] so every lane reads its
+//   own state's four consecutive tokens with one 128-bit read, u and delta as [c][token]
+//   so the S lanes of a channel read the same 128-bit row (broadcast).  Each step computes
+//   a per-lane partial readout p[token] = sum_k C h_k.  After 16 steps the 16 x S partials
+//   of a channel are transposed through LDS so that lane (c, s) sums the S partials of
+//   tokens s, s+S, ...: every lane then finalises (feed-through, gate, store) 16/S tokens
+//   with all 64 lanes busy, instead of one lane in S doing it for every token.
+//   No block barrier is used: a wave only ever touches its own LDS region.
+//
+// Three modes share this code:
+//   MODE_SINGLE: scan the whole sequence from h = 0, write y and last_state.
+//   MODE_STATE : chunked pass 1 -- scan one chunk from h = 0 without readout; write the
+//                chunk's end state and its sum of delta (the chunk's decay is
+//                exp(A * sum delta), the product of its Abar).
+//   MODE_APPLY : chunked pass 2 -- scan one chunk from the carried-in state, write y and,
+//                for the final chunk, last_state.
+// Between the two chunked passes, chunk_prefix_kernel composes the per-chunk affine maps
+// (P, H) with a log-depth scan across the lanes of a wavefront (ds_bpermute shuffles) and
+// leaves each chunk's carried-in state.
+//
+// Time-invariant coefficients (delta[d], B[d,n], C[d,n]) use the same skeleton with a
+// scaled state g = h / Bbar (g = Abar g + u; y = sum_n (C Bbar) g), so a step costs two
+// fused multiply-adds per state and no exp.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "scan_launch.h"
+
+namespace selscan {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTile = 16;        // tokens per tile
+constexpr int kRowPad = 20;      // LDS row length (floats) of a 16-token row: 16 + 4 padding
+
+enum { MODE_SINGLE = 0, MODE_STATE = 1, MODE_APPLY = 2 };
+
+// ---------------------------------------------------------------------------------------
+// element I/O.  Loads address a wave-uniform base pointer (kept in SGPRs) plus a 32-bit
+// per-lane byte offset that is fixed for the whole kernel, so the per-tile address work is
+// scalar.
+
+template <typename IO> struct io_traits;
+template <> struct io_traits<float> {
+  static constexpr int kBytes = 4;
+  static __device__ __forceinline__ float widen(float v) { return v; }
+  // raw bit patterns, so a loaded value can stay untouched in a register until it is used
+  static __device__ __forceinline__ uint32_t raw_at(const char* base, uint32_t off) {
+    return *reinterpret_cast<const uint32_t*>(base + off);
+  }
+  static __device__ __forceinline__ uint32_t raw_stream(const char* base, uint32_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + off));
+  }
+  static __device__ __forceinline__ float from_raw(uint32_t r) { return __uint_as_float(r); }
+  static __device__ __forceinline__ float at(const char* base, uint32_t off) {
+    return *reinterpret_cast<const float*>(base + off);
+  }
+  static __device__ __forceinline__ float stream(const char* base, uint32_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
+  }
+  static __device__ __forceinline__ void put(char* base, uint32_t off, float v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<float*>(base + off));
+  }
+};
+template <> struct io_traits<uint16_t> {   // bfloat16 bit patterns
+  static constexpr int kBytes = 2;
+  static __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+  static __device__ __forceinline__ uint32_t raw_at(const char* base, uint32_t off) {
+    return *reinterpret_cast<const uint16_t*>(base + off);
+  }
+  static __device__ __forceinline__ uint32_t raw_stream(const char* base, uint32_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + off));
+  }
+  static __device__ __forceinline__ float from_raw(uint32_t r) { return __uint_as_float(r << 16); }
+  static __device__ __forceinline__ float at(const char* base, uint32_t off) {
+    return widen(*reinterpret_cast<const uint16_t*>(base + off));
+  }
+  static __device__ __forceinline__ float stream(const char* base, uint32_t off) {
+    return widen(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + off)));
+  }
+  static __device__ __forceinline__ void put(char* base, uint32_t off, float v) {
+    // round to nearest even; NaN stays a quiet NaN
+    const uint32_t x = __float_as_uint(v);
+    const uint32_t r = ((x & 0x7fffffffu) > 0x7f800000u) ? ((x >> 16) | 0x40u)
+                                                         : ((x + 0x7fffu + ((x >> 16) & 1u)) >> 16);
+    __builtin_nontemporal_store(uint16_t(r), reinterpret_cast<uint16_t*>(base + off));
+  }
+};
+
+// Order this wave's LDS traffic: every LDS write before the barrier is visible to every
+// lane's LDS read after it.  A wave's LDS instructions execute in issue order, so this
+// only has to stop the compiler from moving accesses across it.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Blocks are dealt round-robin to the 8 XCDs; remap so that each XCD gets a contiguous
+// range of work items (neighbouring channel groups of one batch row share B/C rows and
+// the cache lines of u/delta/z/y, and those live in that XCD's L2).
+__device__ __forceinline__ int xcd_contiguous_block(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int per = nblocks / kXcd, rem = nblocks % kXcd;
+  const int xcd = bid % kXcd, pos = bid / kXcd;
+  return (xcd < rem) ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
+}
+
+// LDS floats one wave needs.
+template <int S, int K, bool TI>
+struct wave_lds {
+  static constexpr int CW = 64 / S;
+  static constexpr int NP = S * K;                    // padded states per channel
+  static constexpr int kB = TI ? 0 : NP * kRowPad;    // sB[NP][20]
+  static constexpr int kC = kB;                       // sC[NP][20]
+  static constexpr int kU = CW * kRowPad;             // sU[CW][20]
+  static constexpr int kD = TI ? 0 : CW * kRowPad;    // sD[CW][20]
+  static constexpr int kChan = 21 * S;                // sP channel block: S rows of 20 + S pad
+  static constexpr int kP = CW * kChan;               // sP[CW][S][20] (+pad per channel)
+  static constexpr int total = kB + kC + kU + kD + kP;
+};
+
+// ---------------------------------------------------------------------------------------
+// the scan kernel
+
+template <typename IO, int S, int K, bool TI, int MODE>
+__global__ __launch_bounds__(kWavesPerBlock * 64)
+void scan_kernel(ScanParams p) {
+  using T = io_traits<IO>;
+  using LDS = wave_lds<S, K, TI>;
+  constexpr int CW = LDS::CW;
+  constexpr int NP = LDS::NP;
+  constexpr int M = kTile / S;          // tokens each lane stages / finalises per tile
+  constexpr int NB = (NP * kTile) / 64; // B (and C) tile elements per lane
+  constexpr bool READOUT = (MODE != MODE_STATE);
+  constexpr int ES = T::kBytes;
+
+  extern __shared__ __align__(16) float smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int c = lane / S, s = lane % S;
+
+  const int item = xcd_contiguous_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (item >= p.total_items) return;                      // whole wave exits together
+  // item = ((b * n_chunks) + chunk) * groups + g : neighbouring items share (b, chunk)
+  const int g = item % p.groups;
+  const int bc = item / p.groups;
+  const int chunk = bc % p.n_chunks;
+  const int64_t b = bc / p.n_chunks;
+
+  float* const sB = smem + wave * LDS::total;
+  float* const sC = sB + LDS::kB;
+  float* const sU = sC + LDS::kC;
+  float* const sD = sU + LDS::kU;
+  float* const sP = sD + LDS::kD;
+
+  const int64_t D = p.D, N = p.N;
+  const int64_t d0 = int64_t(g) * CW;                     // first channel of the group (uniform)
+  const int64_t d = d0 + c;
+  const bool dvalid = d < D;
+  const int cl = dvalid ? c : 0;                          // clamped channel for in-bounds loads
+  const int64_t l_begin = int64_t(chunk) * p.chunk_len;
+  const int64_t l_end = (l_begin + p.chunk_len < p.L) ? l_begin + p.chunk_len : p.L;
+
+  // ---- per-lane constants of the K owned states
+  float A2[K], iA[K], zf[K], h[K];
+  float Ab[K], CB[K];                 // time-invariant: Abar and C*Bbar, hoisted
+  bool any_zero = false;
+  float dt_ti = 0.f;
+  const char* const Bbase = static_cast<const char*>(p.B);
+  const char* const Cbase = static_cast<const char*>(p.C);
+  if (TI) dt_ti = dvalid ? T::at(static_cast<const char*>(p.delta), uint32_t(d * ES)) : 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t n = s + S * k;
+    const bool ok = dvalid && n < N;
+    const float a = ok ? p.A[d * N + n] : 0.f;
+    A2[k] = a * kLog2e;
+    iA[k] = (a != 0.f) ? 1.0f / a : 0.f;
+    zf[k] = (ok && a == 0.f) ? 1.f : 0.f;
+    any_zero |= (ok && a == 0.f);
+    h[k] = 0.f;
+    if (TI) {
+      // Abar = exp(delta a); Bbar = expm1(delta a)/a * B (delta * B when a == 0)
+      const float bv = ok ? T::widen(reinterpret_cast<const IO*>(Bbase)[d * p.B_sd + n]) : 0.f;
+      const float cv = ok ? T::widen(reinterpret_cast<const IO*>(Cbase)[d * p.C_sd + n]) : 0.f;
+      Ab[k] = ok ? expf(dt_ti * a) : 1.f;
+      const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
+      CB[k] = ok ? cv * coeff * bv : 0.f;
+    } else {
+      Ab[k] = 0.f;
+      CB[k] = 0.f;
+    }
+  }
+  // wave-uniform: does any owned state have A == 0 (needs the delta*B form)?
+  const bool wave_zero = __builtin_amdgcn_readfirstlane(__ballot(any_zero) != 0ull ? 1 : 0) != 0;
+
+  if (MODE == MODE_APPLY) {                // carried-in state (h, or g in time-invariant form)
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t n = s + S * k;
+      if (dvalid && n < N) h[k] = p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk];
+    }
+  }
+
+  // ---- per-lane byte offsets inside a tile (fixed for the kernel)
+  uint32_t offU[M], offD[M], offZ[M], offY[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int64_t tl = s + S * m;
+    offU[m] = uint32_t((tl * p.u_sl + cl) * ES);
+    offD[m] = uint32_t((tl * p.delta_sl + cl) * ES);
+    offZ[m] = uint32_t((tl * (p.z != nullptr ? p.z_sl : p.u_sl) + cl) * ES);
+    offY[m] = uint32_t((tl * p.y_sl + cl) * ES);
+  }
+  uint32_t offB[TI ? 1 : NB], offC[TI ? 1 : NB], maskB[TI ? 1 : NB];
+  int tlB[TI ? 1 : NB], nB[TI ? 1 : NB];
+#pragma unroll
+  for (int r = 0; r < (TI ? 1 : NB); ++r) {
+    const int e = lane + 64 * r;            // element of the [16][NP] tile
+    const int tl = e / NP, n = e % NP;
+    const int nc = n < N ? n : 0;           // padded state slots read state 0, then masked to zero
+    tlB[r] = tl;
+    nB[r] = nc;
+    maskB[r] = n < N ? 0xffffffffu : 0u;
+    offB[r] = uint32_t((tl * p.B_sl + nc) * ES);
+    offC[r] = uint32_t((tl * p.C_sl + nc) * ES);
+  }
+
+  // ---- staging registers: the next tile's operands as raw bit patterns (widened when staged
+  // into LDS at the top of the next tile, so no instruction waits on the loads before then)
+  uint32_t rB[TI ? 1 : NB], rC[TI ? 1 : NB];
+  uint32_t rU[M], rD[M], rZ[M];
+  const bool gate = (p.z != nullptr) && READOUT;
+  const bool has_d = (p.Dskip != nullptr) && READOUT;
+  const float dskip = (has_d && dvalid) ? p.Dskip[d] : 0.f;
+  const char* const ubase0 = static_cast<const char*>(p.u) + (b * p.u_sb + d0) * ES;
+  const char* const dbase0 = static_cast<const char*>(p.delta) + (b * p.delta_sb + d0) * ES;
+  // Without a gate the z loads re-read u (same shape, always in bounds) and are ignored,
+  // so that no load sits under a branch.
+  const int64_t z_sb = p.z != nullptr ? p.z_sb : p.u_sb, z_sl = p.z != nullptr ? p.z_sl : p.u_sl;
+  const char* const zbase0 = static_cast<const char*>(p.z != nullptr ? p.z : p.u) + (b * z_sb + d0) * ES;
+  char* const ybase0 = static_cast<char*>(p.y) + (b * p.y_sb + d0) * ES;
+  const char* const bbase0 = Bbase + b * p.B_sb * ES;
+  const char* const cbase0 = Cbase + b * p.C_sb * ES;
+
+  // Load the operands of the tile starting at token l0.  Every load is unconditional and
+  // in bounds (so the compiler emits straight-line loads whose latency overlaps the
+  // compute of the current tile).  FULL: all 16 tokens are inside the work item.
+  // Otherwise tokens at or past l_end re-read the last valid token and are then replaced
+  // by zero (delta = 0 and u = 0 leave the state unchanged: Abar = 1 and Bbar = 0).
+  auto load_tile = [&](int64_t l0, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int64_t rem = l_end - l0;         // tokens left from l0 (uniform, >= 1)
+    if (!TI) {
+      const char* bb = bbase0 + l0 * p.B_sl * ES;
+      const char* cb = cbase0 + l0 * p.C_sl * ES;
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        uint32_t ob = offB[r], oc = offC[r];
+        bool ok = true;
+        if (!FULL) {
+          ok = tlB[r] < rem;
+          const int64_t tlc = ok ? tlB[r] : rem - 1;
+          ob = uint32_t((tlc * p.B_sl + nB[r]) * ES);
+          oc = uint32_t((tlc * p.C_sl + nB[r]) * ES);
+        }
+        uint32_t vb = T::raw_at(bb, ob);
+        uint32_t vc = READOUT ? T::raw_at(cb, oc) : 0u;
+        if (!FULL) {              // last tile only: select (waits on these loads here)
+          vb = ok ? vb : 0u;
+          vc = ok ? vc : 0u;
+        }
+        rB[r] = vb;
+        if (READOUT) rC[r] = vc;
+      }
+    }
+    const char* ub = ubase0 + l0 * p.u_sl * ES;
+    const char* db = dbase0 + l0 * p.delta_sl * ES;
+    const char* zb = zbase0 + l0 * z_sl * ES;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      uint32_t ou = offU[m], od = offD[m], oz = offZ[m];
+      bool ok = true;
+      if (!FULL) {
+        const int64_t tl = s + S * m;
+        ok = tl < rem;
+        const int64_t tlc = ok ? tl : rem - 1;
+        ou = uint32_t((tlc * p.u_sl + cl) * ES);
+        od = uint32_t((tlc * p.delta_sl + cl) * ES);
+        oz = uint32_t((tlc * z_sl + cl) * ES);
+      }
+      uint32_t vu = T::raw_stream(ub, ou);
+      uint32_t vd = TI ? 0u : T::raw_stream(db, od);
+      uint32_t vz = READOUT ? T::raw_stream(zb, oz) : 0u;
+      if (!FULL) {
+        vu = ok ? vu : 0u;
+        vd = ok ? vd : 0u;
+        vz = ok ? vz : 0u;
+      }
+      rU[m] = vu;
+      if (!TI) rD[m] = vd;
+      rZ[m] = vz;
+    }
+  };
+
+  // Steps of the recurrence on the staged tile; partial readouts to pacc.  FULL: all 16
+  // tokens; otherwise only the first `nsteps` (a uniform count) -- needed for the
+  // time-invariant form, whose decay does not vanish on the zero-padded tokens.
+  auto compute_tile = [&](float (&pacc)[kTile], auto zero_tag, auto full_tag, int64_t nsteps) {
+    constexpr bool ZERO = decltype(zero_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) pacc[j] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 u4 = *reinterpret_cast<const float4*>(sU + c * kRowPad + 4 * q);
+      const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+      if (TI) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!FULL && 4 * q + j >= nsteps) break;
+          float acc = 0.f;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            h[k] = fmaf(Ab[k], h[k], uu[j]);                 // g = Abar g + u
+            if (READOUT) acc = fmaf(CB[k], h[k], acc);       // y += C Bbar g
+          }
+          pacc[4 * q + j] = acc;
+        }
+      } else {
+        const float4 d4 = *reinterpret_cast<const float4*>(sD + c * kRowPad + 4 * q);
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        float bb[K][4], cc[K][4];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float4 b4 = *reinterpret_cast<const float4*>(sB + (s + S * k) * kRowPad + 4 * q);
+          bb[k][0] = b4.x; bb[k][1] = b4.y; bb[k][2] = b4.z; bb[k][3] = b4.w;
+          if (READOUT) {
+            const float4 c4 = *reinterpret_cast<const float4*>(sC + (s + S * k) * kRowPad + 4 * q);
+            cc[k][0] = c4.x; cc[k][1] = c4.y; cc[k][2] = c4.z; cc[k][3] = c4.w;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!FULL && 4 * q + j >= nsteps) break;
+          float acc = 0.f;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            const float ab = __builtin_amdgcn_exp2f(dd[j] * A2[k]);   // Abar = exp(delta A)
+            float f = fmaf(ab, iA[k], -iA[k]);                        // (Abar - 1)/A
+            if (ZERO) f = fmaf(dd[j], zf[k], f);                       // A == 0: delta
+            h[k] = fmaf(ab, h[k], f * (bb[k][j] * uu[j]));             // h = Abar h + Bbar u
+            if (READOUT) acc = fmaf(cc[k][j], h[k], acc);              // C . h (updated state)
+          }
+          pacc[4 * q + j] = acc;
+        }
+      }
+    }
+  };
+
+  float dsum = 0.f;                         // MODE_STATE: sum of delta over the chunk
+  const int64_t nfull = (l_end - l_begin) / kTile;
+  const int64_t ntiles = (l_end - l_begin + kTile - 1) / kTile;
+  using full_t = std::integral_constant<bool, true>;
+  using part_t = std::integral_constant<bool, false>;
+  if (ntiles > 0) {
+    if (nfull > 0) load_tile(l_begin, full_t{});
+    else load_tile(l_begin, part_t{});
+  }
+
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t l0 = l_begin + t * kTile;
+    wave_lds_sync();                        // previous tile's LDS reads are done
+    if (!TI) {
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        const int e = lane + 64 * r;
+        const int tl = e / NP, n = e % NP;
+        sB[n * kRowPad + tl] = T::from_raw(rB[r] & maskB[r]);
+        if (READOUT) sC[n * kRowPad + tl] = T::from_raw(rC[r] & maskB[r]);
+      }
+    }
+    float uo[M], zo[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float fu = T::from_raw(rU[m]);
+      sU[c * kRowPad + s + S * m] = fu;
+      if (!TI) {
+        const float fd = T::from_raw(rD[m]);
+        sD[c * kRowPad + s + S * m] = fd;
+        if (MODE == MODE_STATE) dsum += fd;      // lane sums its own tokens; reduced below
+      }
+      uo[m] = fu;
+      zo[m] = gate ? T::from_raw(rZ[m]) : 0.f;
+    }
+    if (t + 1 < nfull) load_tile(l0 + kTile, full_t{});          // prefetch the next tile
+    else if (t + 1 < ntiles) load_tile(l0 + kTile, part_t{});
+    wave_lds_sync();
+
+    float pacc[kTile];
+    if (t < nfull) {
+      if (wave_zero) compute_tile(pacc, full_t{}, full_t{}, kTile);
+      else compute_tile(pacc, part_t{}, full_t{}, kTile);
+    } else {
+      const int64_t nsteps = l_end - l0;
+      if (wave_zero) compute_tile(pacc, full_t{}, part_t{}, nsteps);
+      else compute_tile(pacc, part_t{}, part_t{}, nsteps);
+    }
+
+    if (READOUT) {
+      // ---- transpose the partial readouts of this channel: lane (c, s) -> tokens s + S m
+      float* row = sP + c * LDS::kChan + s * kRowPad;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(row + 4 * q) =
+            make_float4(pacc[4 * q], pacc[4 * q + 1], pacc[4 * q + 2], pacc[4 * q + 3]);
+      wave_lds_sync();
+      char* yb = ybase0 + l0 * p.y_sl * ES;
+      const int64_t rem = l_end - l0;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int tl = s + S * m;
+        const float* col = sP + c * LDS::kChan + tl;
+        float yv = col[0];
+#pragma unroll
+        for (int r = 1; r < S; ++r) yv += col[r * kRowPad];
+        yv = fmaf(dskip, uo[m], yv);                                   // + D u
+        if (gate) {
+          const float zz = zo[m];
+          const float sig = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+          yv *= zz * sig;                                              // * SiLU(z)
+        }
+        if (dvalid && tl < rem) T::put(yb, offY[m], yv);
+      }
+    }
+  }
+
+  // ---- outputs that follow the last token of the work item
+  if (MODE == MODE_STATE) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t n = s + S * k;
+      if (dvalid && n < N) p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk] = h[k];
+    }
+    float sum;
+    if (TI) {
+      sum = dt_ti * float(l_end - l_begin);
+    } else {   // every lane of channel c summed its own 16/S tokens of each tile: add them up
+      sum = dsum;
+#pragma unroll
+      for (int off = 1; off < S; off <<= 1) sum += __shfl_xor(sum, off, S);
+    }
+    if (dvalid && s == 0) p.ws_dsum[(b * D + d) * p.n_chunks + chunk] = sum;
+  } else if (p.last_state != nullptr && (MODE == MODE_SINGLE || chunk == p.n_chunks - 1)) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t n = s + S * k;
+      if (dvalid && n < N) {
+        float hv = h[k];
+        if (TI) {   // h = Bbar * g
+          const float a = p.A[d * N + n];
+          const float bv = T::widen(reinterpret_cast<const IO*>(Bbase)[d * p.B_sd + n]);
+          const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
+          hv = coeff * bv * hv;
+        }
+        p.last_state[(b * D + d) * N + n] = hv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// chunk prefix: per (b, d, n), turn chunk end states into carried-in states.
+// Lanes of a segment are the chunks 0 .. n_chunks-1 (segment width W = pow2 >= n_chunks).
+// Chunk c's map is h -> P_c h + H_c with P_c = exp(A sum_{t in c} delta_t); an inclusive
+// log-depth scan composes (P1,H1).(P2,H2) = (P2 P1, P2 H1 + H2); the carried-in state of
+// chunk c is the composed H up to chunk c-1 (zero for chunk 0).
+
+__global__ __launch_bounds__(256)
+void chunk_prefix_kernel(PrefixParams p) {
+  const int lane = threadIdx.x & 63;
+  const int W = p.seg_width;                         // power of two, <= 64
+  const int seg_in_wave = lane / W, i = lane % W;
+  const int64_t seg = (int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6)) * (64 / W) + seg_in_wave;
+  const int64_t nseg = p.batch * p.D * p.N;
+  const bool live = seg < nseg && i < p.n_chunks;
+  float P = 1.f, H = 0.f;
+  int64_t b = 0, d = 0, n = 0;
+  if (live) {
+    n = seg % p.N;
+    d = (seg / p.N) % p.D;
+    b = seg / (p.N * p.D);
+    const float a2 = p.A[d * p.N + n] * kLog2e;
+    P = __builtin_amdgcn_exp2f(a2 * p.dsum[(b * p.D + d) * p.n_chunks + i]);
+    H = p.state[seg * p.n_chunks + i];
+  }
+  for (int off = 1; off < W; off <<= 1) {
+    const float Pp = __shfl_up(P, off, W);
+    const float Hp = __shfl_up(H, off, W);
+    if (i >= off) {
+      H = fmaf(P, Hp, H);
+      P = P * Pp;
+    }
+  }
+  const float carry = __shfl_up(H, 1, W);
+  if (live) p.state[seg * p.n_chunks + i] = (i == 0) ? 0.f : carry;
+}
+
+// zero-fill (empty sequence: last_state = 0); a kernel, not a memset, so callers may
+// capture it in a graph.
+__global__ __launch_bounds__(256)
+void fill_zero_kernel(float* x, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    x[i] = 0.f;
+}
+
+template <typename IO, int S, int K, bool TI, int MODE>
+hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
+  constexpr size_t lds = size_t(wave_lds<S, K, TI>::total) * sizeof(float) * kWavesPerBlock;
+  const int blocks = (p.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (lds > 65536) {   // above the default dynamic-LDS limit: opt in once per kernel
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&scan_kernel<IO, S, K, TI, MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL((scan_kernel<IO, S, K, TI, MODE>), dim3(blocks), dim3(kWavesPerBlock * 64), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <typename IO, bool TI, int MODE>
+hipError_t dispatch_sk(int S, int K, const ScanParams& p, hipStream_t stream) {
+  if (S == 4 && K == 1) return launch_scan<IO, 4, 1, TI, MODE>(p, stream);
+  if (S == 8 && K == 1) return launch_scan<IO, 8, 1, TI, MODE>(p, stream);
+  if (S == 16 && K == 1) return launch_scan<IO, 16, 1, TI, MODE>(p, stream);
+  if (S == 16 && K == 2) return launch_scan<IO, 16, 2, TI, MODE>(p, stream);
+  if (S == 16 && K == 4) return launch_scan<IO, 16, 4, TI, MODE>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+template <typename IO, bool TI>
+hipError_t dispatch_mode(int mode, int S, int K, const ScanParams& p, hipStream_t stream) {
+  switch (mode) {
+    case MODE_SINGLE: return dispatch_sk<IO, TI, MODE_SINGLE>(S, K, p, stream);
+    case MODE_STATE: return dispatch_sk<IO, TI, MODE_STATE>(S, K, p, stream);
+    case MODE_APPLY: return dispatch_sk<IO, TI, MODE_APPLY>(S, K, p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+void lanes_for_states(int64_t N, int* S, int* K) {
+  if (N <= 4) { *S = 4; *K = 1; }
+  else if (N <= 8) { *S = 8; *K = 1; }
+  else if (N <= 16) { *S = 16; *K = 1; }
+  else if (N <= 32) { *S = 16; *K = 2; }
+  else { *S = 16; *K = 4; }
+}
+
+hipError_t launch_scan_pass(int pass, bool bf16, bool ti, int S, int K, const ScanParams& p, hipStream_t stream) {
+  const int mode = pass == kPassSingle ? MODE_SINGLE : pass == kPassState ? MODE_STATE : MODE_APPLY;
+  if (bf16) return ti ? dispatch_mode<uint16_t, true>(mode, S, K, p, stream)
+                      : dispatch_mode<uint16_t, false>(mode, S, K, p, stream);
+  return ti ? dispatch_mode<float, true>(mode, S, K, p, stream) : dispatch_mode<float, false>(mode, S, K, p, stream);
+}
+
+hipError_t launch_chunk_prefix(const PrefixParams& p, hipStream_t stream) {
+  const int64_t segs = p.batch * p.D * p.N;
+  const int per_wave = 64 / p.seg_width;
+  const int64_t waves = (segs + per_wave - 1) / per_wave;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL(chunk_prefix_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, x, n);
+  return hipGetLastError();
+}
+
+size_t scan_lds_bytes(int S, int K, bool ti) {
+#define SELSCAN_LDS(SS, KK) \
+  if (S == SS && K == KK) return size_t(ti ? wave_lds<SS, KK, true>::total : wave_lds<SS, KK, false>::total) * 4 * kWavesPerBlock;
+  SELSCAN_LDS(4, 1) SELSCAN_LDS(8, 1) SELSCAN_LDS(16, 1) SELSCAN_LDS(16, 2) SELSCAN_LDS(16, 4)
+#undef SELSCAN_LDS
+  return 0;
+}
+
+}  // namespace selscan

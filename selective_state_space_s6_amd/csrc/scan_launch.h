@@ -1,0 +1,54 @@
+// scan_launch.h -- internal interface between the C ABI (selscan_api.cpp) and the
+// kernels (scan_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace selscan {
+
+constexpr int kWavesPerBlock = 4;
+enum { kPassSingle = 0, kPassState = 1, kPassApply = 2 };
+
+// Everything one scan-kernel launch needs.  Strides are in elements.
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;   // may be null
+  const void* z;        // may be null
+  void* y;
+  float* last_state;    // may be null
+  int64_t batch, L, D, N;
+  int64_t u_sb, u_sl, delta_sb, delta_sl, z_sb, z_sl, y_sb, y_sl;
+  int64_t B_sb, B_sl, B_sd, C_sb, C_sl, C_sd;
+  int64_t chunk_len;    // tokens per chunk (L for the single pass)
+  int32_t n_chunks;     // 1 for the single pass
+  int32_t groups;       // channel groups per batch row: ceil(D / channels-per-wave)
+  int32_t total_items;  // batch * n_chunks * groups (one wavefront each)
+  float* ws_state;      // chunked: [batch][D][N][n_chunks] end states, then carries
+  float* ws_dsum;       // chunked: [batch][D][n_chunks] sum of delta per chunk
+};
+
+struct PrefixParams {
+  const float* A;
+  const float* dsum;
+  float* state;
+  int64_t batch, D, N;
+  int32_t n_chunks;
+  int32_t seg_width;    // power of two >= n_chunks, <= 64
+};
+
+// Lanes per channel (S) and states per lane (K) for N states.
+void lanes_for_states(int64_t N, int* S, int* K);
+// Dynamic LDS bytes of one scan-kernel block.
+size_t scan_lds_bytes(int S, int K, bool ti);
+
+hipError_t launch_scan_pass(int pass, bool bf16, bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
+hipError_t launch_chunk_prefix(const PrefixParams& p, hipStream_t stream);
+hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream);
+
+}  // namespace selscan

@@ -1,0 +1,252 @@
+// selscan_api.cpp -- the C ABI of libselscan.so: argument checks, path choice, workspace,
+// and the launch sequence.  The operation itself is documented in include/selscan.h.
+#include "selscan.h"
+
+#include <hip/hip_runtime.h>
+
+#include "scan_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = int(e);
+  return SELSCAN_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Plan {
+  bool ti = false;
+  bool bf16 = false;
+  int S = 16, K = 1;
+  int64_t groups = 0;         // channel groups per batch row
+  bool chunked = false;
+  int64_t chunk_len = 0;
+  int32_t n_chunks = 1;
+  size_t ws_bytes = 0;        // workspace the chunked path needs
+  size_t ws_state_bytes = 0;
+};
+
+constexpr int64_t kMaxChunks = 64;
+constexpr int64_t kTargetWaves = 4096;   // about four wavefronts per SIMD on 256 CUs
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Validate dims and choose the schedule.  Does not look at pointers.
+int make_plan(const selscan_dims* dims, Plan* plan) {
+  if (!dims) return SELSCAN_ERR_NULL;
+  if (dims->abi_version != SELSCAN_ABI_VERSION) return SELSCAN_ERR_ABI;
+  const selscan_dims& d = *dims;
+  if (d.batch < 0 || d.seqlen < 0 || d.dim < 1 || d.dstate < 1) return SELSCAN_ERR_DIMS;
+  const int64_t strides[] = {d.u_sb, d.u_sl, d.delta_sb, d.delta_sl, d.z_sb, d.z_sl, d.y_sb, d.y_sl,
+                             d.B_sb, d.B_sl, d.B_sd, d.C_sb, d.C_sl, d.C_sd};
+  for (int64_t s : strides)
+    if (s < 0) return SELSCAN_ERR_DIMS;
+  if (d.dstate > 64) return SELSCAN_ERR_UNSUPPORTED;
+  if (d.io_dtype != SELSCAN_F32 && d.io_dtype != SELSCAN_BF16) return SELSCAN_ERR_UNSUPPORTED;
+  if (d.path != SELSCAN_PATH_AUTO && d.path != SELSCAN_PATH_SINGLE && d.path != SELSCAN_PATH_CHUNKED)
+    return SELSCAN_ERR_UNSUPPORTED;
+  if (d.chunk_len < 0 || d.chunk_len % 16 != 0) return SELSCAN_ERR_UNSUPPORTED;
+  // the kernels address a 16-token tile with 32-bit byte offsets from a per-tile base
+  const int64_t kMaxRowStride = int64_t(1) << 26;
+  if (d.u_sl > kMaxRowStride || d.delta_sl > kMaxRowStride || d.z_sl > kMaxRowStride || d.y_sl > kMaxRowStride ||
+      d.B_sl > kMaxRowStride || d.C_sl > kMaxRowStride || d.dim > kMaxRowStride)
+    return SELSCAN_ERR_UNSUPPORTED;
+  // grid-size limits of this implementation (item indices are 32-bit)
+  if (d.dim > (int64_t(1) << 30) || d.batch > (int64_t(1) << 30)) return SELSCAN_ERR_UNSUPPORTED;
+
+  const bool bc_per_token = d.B_sd == 0 && d.C_sd == 0;
+  const bool bc_per_channel = d.B_sb == 0 && d.B_sl == 0 && d.C_sb == 0 && d.C_sl == 0 && d.B_sd >= d.dstate &&
+                              d.C_sd >= d.dstate;
+  const bool delta_per_channel = d.delta_sb == 0 && d.delta_sl == 0;
+  Plan p;
+  if (bc_per_token) p.ti = false;
+  else if (bc_per_channel && delta_per_channel) p.ti = true;
+  else return SELSCAN_ERR_UNSUPPORTED;
+  p.bf16 = d.io_dtype == SELSCAN_BF16;
+  selscan::lanes_for_states(d.dstate, &p.S, &p.K);
+  const int cw = 64 / p.S;
+  p.groups = (d.dim + cw - 1) / cw;
+  const int64_t waves_single = d.batch * p.groups;
+  if (waves_single > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
+
+  // chunking: only when the single pass leaves the GPU under-filled and the sequence is long
+  bool chunk = false;
+  int64_t nc = 1;
+  if (d.path == SELSCAN_PATH_CHUNKED) {
+    chunk = d.seqlen > 0;
+    if (d.chunk_len > 0) nc = (d.seqlen + d.chunk_len - 1) / d.chunk_len;
+    else nc = (d.seqlen + 63) / 64 < kMaxChunks ? (d.seqlen + 63) / 64 : kMaxChunks;
+  } else if (d.path == SELSCAN_PATH_AUTO && d.seqlen >= 256 && waves_single > 0 && waves_single < kTargetWaves / 2) {
+    nc = (kTargetWaves + waves_single - 1) / waves_single;
+    const int64_t by_len = d.seqlen / 128;               // chunks of at least 128 tokens
+    if (nc > by_len) nc = by_len;
+    if (nc > kMaxChunks) nc = kMaxChunks;
+    chunk = nc >= 2;
+  }
+  if (chunk) {
+    if (nc < 1) nc = 1;
+    if (nc > kMaxChunks) return SELSCAN_ERR_UNSUPPORTED;   // forced chunk_len too small
+    p.chunk_len = d.chunk_len > 0 ? d.chunk_len : round_up((d.seqlen + nc - 1) / nc, 16);
+    p.n_chunks = int32_t((d.seqlen + p.chunk_len - 1) / p.chunk_len);
+    p.chunked = true;
+    p.ws_state_bytes = size_t(round_up(int64_t(sizeof(float)) * d.batch * d.dim * d.dstate * p.n_chunks, 256));
+    p.ws_bytes = p.ws_state_bytes + size_t(round_up(int64_t(sizeof(float)) * d.batch * d.dim * p.n_chunks, 256));
+  } else {
+    p.chunk_len = d.seqlen;
+    p.n_chunks = 1;
+  }
+  if (d.batch * p.n_chunks * p.groups > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
+  *plan = p;
+  return SELSCAN_OK;
+}
+
+int check_pointers(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* Dskip, const void* z, const void* y, const float* last_state, int io_dtype,
+                   bool no_tokens) {
+  // With no tokens (batch * seqlen == 0) nothing is read from the per-token tensors, and an
+  // empty tensor may legitimately have a NULL address.
+  if (!A || (!no_tokens && (!u || !delta || !B || !C || !y))) return SELSCAN_ERR_NULL;
+  const size_t es = io_dtype == SELSCAN_BF16 ? 2 : 4;
+  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(y, es) ||
+      (z && !aligned(z, es)))
+    return SELSCAN_ERR_ALIGN;
+  if (!aligned(A, 4) || (Dskip && !aligned(Dskip, 4)) || (last_state && !aligned(last_state, 4)))
+    return SELSCAN_ERR_ALIGN;
+  return SELSCAN_OK;
+}
+
+int run(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* Dskip,
+        const void* z, void* y, float* last_state, const selscan_dims* dims, const Plan& plan, void* workspace,
+        hipStream_t stream) {
+  const selscan_dims& d = *dims;
+  if (d.batch == 0) return SELSCAN_OK;
+  if (d.seqlen == 0) {
+    if (last_state) {
+      hipError_t e = selscan::launch_fill_zero(last_state, d.batch * d.dim * d.dstate, stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    return SELSCAN_OK;
+  }
+  selscan::ScanParams p{};
+  p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = z; p.y = y;
+  p.last_state = last_state;
+  p.batch = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = d.dstate;
+  p.u_sb = d.u_sb; p.u_sl = d.u_sl; p.delta_sb = d.delta_sb; p.delta_sl = d.delta_sl;
+  p.z_sb = d.z_sb; p.z_sl = d.z_sl; p.y_sb = d.y_sb; p.y_sl = d.y_sl;
+  p.B_sb = d.B_sb; p.B_sl = d.B_sl; p.B_sd = d.B_sd; p.C_sb = d.C_sb; p.C_sl = d.C_sl; p.C_sd = d.C_sd;
+  p.chunk_len = plan.chunk_len;
+  p.n_chunks = plan.n_chunks;
+  p.groups = int32_t(plan.groups);
+  p.total_items = int32_t(d.batch * plan.n_chunks * plan.groups);
+  hipError_t e;
+  if (!plan.chunked) {
+    e = selscan::launch_scan_pass(selscan::kPassSingle, plan.bf16, plan.ti, plan.S, plan.K, p, stream);
+    return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+  }
+  char* ws = static_cast<char*>(workspace);
+  p.ws_state = reinterpret_cast<float*>(ws);
+  p.ws_dsum = reinterpret_cast<float*>(ws + plan.ws_state_bytes);
+  e = selscan::launch_scan_pass(selscan::kPassState, plan.bf16, plan.ti, plan.S, plan.K, p, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  selscan::PrefixParams q{};
+  q.A = A; q.dsum = p.ws_dsum; q.state = p.ws_state;
+  q.batch = d.batch; q.D = d.dim; q.N = d.dstate; q.n_chunks = plan.n_chunks;
+  int w = 1;
+  while (w < plan.n_chunks) w <<= 1;
+  q.seg_width = w;
+  e = selscan::launch_chunk_prefix(q, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  e = selscan::launch_scan_pass(selscan::kPassApply, plan.bf16, plan.ti, plan.S, plan.K, p, stream);
+  return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+void selscan_dims_init(selscan_dims* dims, int io_dtype, int64_t batch, int64_t seqlen, int64_t dim,
+                       int64_t dstate, int time_invariant) {
+  if (!dims) return;
+  selscan_dims d{};
+  d.abi_version = SELSCAN_ABI_VERSION;
+  d.io_dtype = io_dtype;
+  d.batch = batch; d.seqlen = seqlen; d.dim = dim; d.dstate = dstate;
+  d.u_sb = d.z_sb = d.y_sb = seqlen * dim;
+  d.u_sl = d.z_sl = d.y_sl = dim;
+  if (time_invariant) {
+    d.delta_sb = d.delta_sl = 0;
+    d.B_sb = d.B_sl = d.C_sb = d.C_sl = 0;
+    d.B_sd = d.C_sd = dstate;
+  } else {
+    d.delta_sb = seqlen * dim;
+    d.delta_sl = dim;
+    d.B_sb = d.C_sb = seqlen * dstate;
+    d.B_sl = d.C_sl = dstate;
+    d.B_sd = d.C_sd = 0;
+  }
+  d.path = SELSCAN_PATH_AUTO;
+  d.chunk_len = 0;
+  *dims = d;
+}
+
+size_t selective_scan_workspace_size(const selscan_dims* dims) {
+  Plan plan;
+  if (make_plan(dims, &plan) != SELSCAN_OK) return 0;
+  return plan.ws_bytes;
+}
+
+int selective_scan_fwd_ws(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                          const float* Dskip, const void* z, void* y, float* last_state, const selscan_dims* dims,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  Plan plan;
+  int st = make_plan(dims, &plan);
+  if (st != SELSCAN_OK) return st;
+  st = check_pointers(u, delta, A, B, C, Dskip, z, y, last_state, dims->io_dtype, dims->batch * dims->seqlen == 0);
+  if (st != SELSCAN_OK) return st;
+  if (plan.chunked && dims->batch > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 256)))
+    return SELSCAN_ERR_WORKSPACE;
+  return run(u, delta, A, B, C, Dskip, z, y, last_state, dims, plan, workspace, static_cast<hipStream_t>(stream));
+}
+
+int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* Dskip, const void* z, void* y, float* last_state, const selscan_dims* dims,
+                       void* stream) {
+  Plan plan;
+  int st = make_plan(dims, &plan);
+  if (st != SELSCAN_OK) return st;
+  st = check_pointers(u, delta, A, B, C, Dskip, z, y, last_state, dims->io_dtype, dims->batch * dims->seqlen == 0);
+  if (st != SELSCAN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!plan.chunked || dims->batch == 0)
+    return run(u, delta, A, B, C, Dskip, z, y, last_state, dims, plan, nullptr, s);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
+  if (e != hipSuccess) return hip_fail(e);
+  st = run(u, delta, A, B, C, Dskip, z, y, last_state, dims, plan, ws, s);
+  e = hipFreeAsync(ws, s);
+  if (st == SELSCAN_OK && e != hipSuccess) return hip_fail(e);
+  return st;
+}
+
+const char* selective_scan_strerror(int status) {
+  switch (status) {
+    case SELSCAN_OK: return "success";
+    case SELSCAN_ERR_NULL: return "a required pointer is NULL";
+    case SELSCAN_ERR_DIMS: return "a size or stride is out of range";
+    case SELSCAN_ERR_UNSUPPORTED: return "unsupported dtype, state count, path or stride pattern";
+    case SELSCAN_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case SELSCAN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case SELSCAN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SELSCAN_ERR_ABI: return "selscan_dims.abi_version does not match the library";
+  }
+  return "unknown status";
+}
+
+int selective_scan_last_hip_error(void) { return g_last_hip_error; }
+
+int selective_scan_abi_version(void) { return SELSCAN_ABI_VERSION; }
+
+}  // extern "C"

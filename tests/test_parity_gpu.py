@@ -1,0 +1,137 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the same
+seeded inputs.  Bar: max|y_gpu - y_ref| / max|y_ref| <= 1e-4 for fp32 I/O and 2e-2 for
+bf16 I/O; last_state (always fp32) <= 1e-4 in the same normalised form."""
+import numpy as np
+import pytest
+
+import s6_workloads
+from tests.gpu_common import TOL, TOL_STATE, log_errors, rel_err, run_gpu, run_oracle, select_channels
+
+pytestmark = pytest.mark.gpu
+
+# reduced sizes: several 16-token tiles and channel groups plus ragged tails
+REDUCED = {
+    "tiny_f32": dict(),
+    "small_f32": dict(),
+    "mamba130m_f32": dict(batch=2, L=530, D=100),
+    "longctx_bf16": dict(batch=2, L=1000, D=130),
+    "s4d_ti_f32": dict(batch=2, L=700, D=70),
+}
+
+
+def check(inp, y, last, y_ref, l_ref, case):
+    e_y = rel_err(y, y_ref)
+    e_l = rel_err(last, l_ref) if last is not None else 0.0
+    log_errors(case, y=e_y, last_state=e_l, io=inp.io)
+    assert np.all(np.isfinite(y)), case
+    assert e_y <= TOL[inp.io], "%s: y error %.3e" % (case, e_y)
+    assert e_l <= TOL_STATE, "%s: last_state error %.3e" % (case, e_l)
+
+
+@pytest.mark.parametrize("path", ["auto", "single", "chunked"])
+@pytest.mark.parametrize("variant", s6_workloads.VARIANTS)
+@pytest.mark.parametrize("name", sorted(REDUCED))
+def test_reduced_workloads(name, variant, path):
+    inp = s6_workloads.generate(name, variant, **REDUCED[name])
+    y_ref, l_ref = run_oracle(inp)
+    y, last = run_gpu(inp, path=path)
+    check(inp, y, last, y_ref, l_ref, "%s/%s/%s" % (name, variant, path))
+
+
+@pytest.mark.parametrize("chunk_len", [16, 48, 64, 112])
+def test_forced_chunk_lengths(chunk_len):
+    inp = s6_workloads.generate("mamba130m_f32", "active", batch=2, L=1003, D=36)
+    y_ref, l_ref = run_oracle(inp)
+    y, last = run_gpu(inp, path="chunked", chunk_len=chunk_len)
+    check(inp, y, last, y_ref, l_ref, "chunk_len=%d" % chunk_len)
+
+
+@pytest.mark.parametrize("name", ["mamba130m_f32", "longctx_bf16", "s4d_ti_f32"])
+def test_full_size_sampled_channels(name):
+    """The full workload in the launch configuration the benchmark times (automatic path),
+    checked against the oracle on a sample of channels."""
+    inp = s6_workloads.generate(name)
+    y, last = run_gpu(inp, want_last=True)
+    assert np.all(np.isfinite(y))
+    ch = s6_workloads.sample_channels(inp.u.shape[2], 24)
+    sub = select_channels(inp, ch)
+    y_ref, l_ref = run_oracle(sub)
+    check(inp, y[..., ch], last[:, ch], y_ref, l_ref, "full/%s" % name)
+    # the benchmark's own call: no last_state
+    y2, _ = run_gpu(inp, want_last=False)
+    assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 50])
+def test_state_counts_and_short_sequences(N, L):
+    inp = s6_workloads.generate("small_f32", "active", batch=2, L=L, D=7, N=N)
+    y_ref, l_ref = run_oracle(inp)
+    for path in ("single", "chunked"):
+        y, last = run_gpu(inp, path=path)
+        check(inp, y, last, y_ref, l_ref, "N=%d L=%d %s" % (N, L, path))
+
+
+@pytest.mark.parametrize("ti", [False, True])
+def test_zero_rate_states(ti):
+    name = "s4d_ti_f32" if ti else "small_f32"
+    inp = s6_workloads.generate(name, "active", batch=2, L=90, D=9, N=16)
+    inp.A[0, 0] = 0.0
+    inp.A[4, 7] = 0.0
+    inp.A[8, 15] = 0.0
+    y_ref, l_ref = run_oracle(inp)
+    for path in ("single", "chunked"):
+        y, last = run_gpu(inp, path=path)
+        check(inp, y, last, y_ref, l_ref, "zero-A ti=%s %s" % (ti, path))
+
+
+def test_empty_sequence_and_empty_batch():
+    import torch
+    import selective_state_space_s6_amd as ss
+    u = torch.zeros((2, 0, 5), device="cuda")
+    A = -torch.ones((5, 3), device="cuda")
+    Bm = torch.zeros((2, 0, 3), device="cuda")
+    last = torch.full((2, 5, 3), 7.0, device="cuda")
+    y, last = ss.selective_scan_fwd(u, u, A, Bm, Bm, last_state=last)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 5) and not last.any()
+    u0 = torch.zeros((0, 4, 5), device="cuda")
+    B0 = torch.zeros((0, 4, 3), device="cuda")
+    y0 = torch.full((0, 4, 5), 3.0, device="cuda")
+    ss.selective_scan_fwd(u0, u0, A, B0, B0, y=y0)
+    torch.cuda.synchronize()
+
+
+def test_strided_and_broadcast_operands():
+    """Non-contiguous u/z/y, per-channel delta with per-token B/C, and B/C shared across
+    the batch through a zero batch stride."""
+    import torch
+    import selective_state_space_s6_amd as ss
+    rng = np.random.default_rng(9)
+    b, L, D, N = 3, 70, 12, 16
+    big_u = rng.standard_normal((b, L, 2 * D)).astype(np.float32)
+    u = big_u[:, :, 3:3 + D]
+    dl = np.exp(rng.uniform(np.log(1e-2), 0, D)).astype(np.float32)
+    A = (-rng.uniform(0.2, 2.0, (D, N))).astype(np.float32)
+    B1 = rng.standard_normal((1, L, N)).astype(np.float32)
+    C1 = rng.standard_normal((1, L, N)).astype(np.float32)
+    z = rng.standard_normal((b, L, D)).astype(np.float32)
+    Ds = rng.standard_normal(D).astype(np.float32)
+    import oracle
+    y_ref, l_ref = oracle.fwd(u, np.broadcast_to(dl, (b, L, D)), A, np.broadcast_to(B1, (b, L, N)),
+                              np.broadcast_to(C1, (b, L, N)), Ds, z)
+    tu = torch.from_numpy(big_u).cuda()[:, :, 3:3 + D]
+    tdl = torch.from_numpy(dl).cuda().expand(b, L, D)              # strides (0, 0, 1)
+    tB = torch.from_numpy(B1).cuda().expand(b, L, N)               # batch stride 0
+    tC = torch.from_numpy(C1).cuda().expand(b, L, N)
+    tz = torch.from_numpy(z).cuda()
+    ybig = torch.zeros((b, L, 3 * D), device="cuda")
+    yv = ybig[:, :, D:2 * D]
+    for path in ("single", "chunked"):
+        ybig.zero_()
+        _, last = ss.selective_scan_fwd(tu, tdl, torch.from_numpy(A).cuda(), tB, tC, torch.from_numpy(Ds).cuda(), tz,
+                                        y=yv, return_last_state=True, path=path)
+        torch.cuda.synchronize()
+        assert rel_err(yv.cpu().numpy(), y_ref) <= 1e-4
+        assert rel_err(last.cpu().numpy(), l_ref) <= 1e-4
+        assert not ybig[:, :, :D].any() and not ybig[:, :, 2 * D:].any()   # nothing outside the view
