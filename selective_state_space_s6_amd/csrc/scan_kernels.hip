@@ -54,6 +54,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTile = 16;        // tokens per tile
 constexpr int kRowPad = 20;      // LDS row length (floats) of a 16-token row: 16 + 4 padding
+constexpr int kPrefetchMax = 2;  // tiles of global loads kept in flight per wavefront (K <= 2)
 
 enum { MODE_SINGLE = 0, MODE_STATE = 1, MODE_APPLY = 2 };
 
@@ -71,17 +72,14 @@ template <> struct io_traits<float> {
     return *reinterpret_cast<const uint32_t*>(base + off);
   }
   static __device__ __forceinline__ uint32_t raw_stream(const char* base, uint32_t off) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + off));
+    return *reinterpret_cast<const uint32_t*>(base + off);
   }
   static __device__ __forceinline__ float from_raw(uint32_t r) { return __uint_as_float(r); }
   static __device__ __forceinline__ float at(const char* base, uint32_t off) {
     return *reinterpret_cast<const float*>(base + off);
   }
-  static __device__ __forceinline__ float stream(const char* base, uint32_t off) {
-    return __builtin_nontemporal_load(reinterpret_cast<const float*>(base + off));
-  }
   static __device__ __forceinline__ void put(char* base, uint32_t off, float v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<float*>(base + off));
+    *reinterpret_cast<float*>(base + off) = v;
   }
 };
 template <> struct io_traits<uint16_t> {   // bfloat16 bit patterns
@@ -91,21 +89,18 @@ template <> struct io_traits<uint16_t> {   // bfloat16 bit patterns
     return *reinterpret_cast<const uint16_t*>(base + off);
   }
   static __device__ __forceinline__ uint32_t raw_stream(const char* base, uint32_t off) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + off));
+    return *reinterpret_cast<const uint16_t*>(base + off);
   }
   static __device__ __forceinline__ float from_raw(uint32_t r) { return __uint_as_float(r << 16); }
   static __device__ __forceinline__ float at(const char* base, uint32_t off) {
     return widen(*reinterpret_cast<const uint16_t*>(base + off));
-  }
-  static __device__ __forceinline__ float stream(const char* base, uint32_t off) {
-    return widen(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(base + off)));
   }
   static __device__ __forceinline__ void put(char* base, uint32_t off, float v) {
     // round to nearest even; NaN stays a quiet NaN
     const uint32_t x = __float_as_uint(v);
     const uint32_t r = ((x & 0x7fffffffu) > 0x7f800000u) ? ((x >> 16) | 0x40u)
                                                          : ((x + 0x7fffu + ((x >> 16) & 1u)) >> 16);
-    __builtin_nontemporal_store(uint16_t(r), reinterpret_cast<uint16_t*>(base + off));
+    *reinterpret_cast<uint16_t*>(base + off) = uint16_t(r);
   }
 };
 
@@ -145,8 +140,12 @@ struct wave_lds {
 // ---------------------------------------------------------------------------------------
 // the scan kernel
 
+// Register budget: at least kMinWaves wavefronts per SIMD (512 / kMinWaves VGPRs each).
+template <int K> struct occupancy { static constexpr int kMinWaves = K == 1 ? 3 : 2; };
+
 template <typename IO, int S, int K, bool TI, int MODE>
 __global__ __launch_bounds__(kWavesPerBlock * 64)
+__attribute__((amdgpu_waves_per_eu(occupancy<K>::kMinWaves, 8)))
 void scan_kernel(ScanParams p) {
   using T = io_traits<IO>;
   using LDS = wave_lds<S, K, TI>;
@@ -156,6 +155,7 @@ void scan_kernel(ScanParams p) {
   constexpr int NB = (NP * kTile) / 64; // B (and C) tile elements per lane
   constexpr bool READOUT = (MODE != MODE_STATE);
   constexpr int ES = T::kBytes;
+  constexpr int kPrefetch = K <= 2 ? kPrefetchMax : 1;
 
   extern __shared__ __align__(16) float smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -235,24 +235,26 @@ void scan_kernel(ScanParams p) {
     offZ[m] = uint32_t((tl * (p.z != nullptr ? p.z_sl : p.u_sl) + cl) * ES);
     offY[m] = uint32_t((tl * p.y_sl + cl) * ES);
   }
-  uint32_t offB[TI ? 1 : NB], offC[TI ? 1 : NB], maskB[TI ? 1 : NB];
-  int tlB[TI ? 1 : NB], nB[TI ? 1 : NB];
-#pragma unroll
-  for (int r = 0; r < (TI ? 1 : NB); ++r) {
-    const int e = lane + 64 * r;            // element of the [16][NP] tile
-    const int tl = e / NP, n = e % NP;
-    const int nc = n < N ? n : 0;           // padded state slots read state 0, then masked to zero
-    tlB[r] = tl;
-    nB[r] = nc;
-    maskB[r] = n < N ? 0xffffffffu : 0u;
-    offB[r] = uint32_t((tl * p.B_sl + nc) * ES);
-    offC[r] = uint32_t((tl * p.C_sl + nc) * ES);
-  }
+  // B/C tile element r of this lane: token tl0 + r * (64 / NP), state n0 (the same state for
+  // every r, since NP divides 64).  Only the r = 0 offset is per-lane; the rest is a uniform
+  // multiple of the token stride.
+  static_assert(64 % NP == 0, "padded state count must divide the wavefront");
+  constexpr int kRowsPerLoad = 64 / NP;
+  const int tl0 = lane / NP, n0 = lane % NP;
+  const int n0c = n0 < N ? n0 : 0;          // padded state slots read state 0, then masked to zero
+  const uint32_t maskB = n0 < N ? 0xffffffffu : 0u;
+  const uint32_t offB0 = uint32_t((tl0 * p.B_sl + n0c) * ES);
+  const uint32_t offC0 = uint32_t((tl0 * p.C_sl + n0c) * ES);
+  const uint32_t stepB = uint32_t(kRowsPerLoad * p.B_sl * ES);   // uniform
+  const uint32_t stepC = uint32_t(kRowsPerLoad * p.C_sl * ES);
 
   // ---- staging registers: the next tile's operands as raw bit patterns (widened when staged
   // into LDS at the top of the next tile, so no instruction waits on the loads before then)
-  uint32_t rB[TI ? 1 : NB], rC[TI ? 1 : NB];
-  uint32_t rU[M], rD[M], rZ[M];
+  // kPrefetch register sets of full-tile loads in flight (tile t lives in set t % kPrefetch),
+  // plus one set for the ragged tail tile, which is loaded after the ring has drained.
+  constexpr int NSET = kPrefetch + 1;
+  uint32_t rB[NSET][TI ? 1 : NB], rC[NSET][TI ? 1 : NB];
+  uint32_t rU[NSET][M], rD[NSET][M], rZ[NSET][M];
   const bool gate = (p.z != nullptr) && READOUT;
   const bool has_d = (p.Dskip != nullptr) && READOUT;
   const float dskip = (has_d && dvalid) ? p.Dskip[d] : 0.f;
@@ -271,30 +273,32 @@ void scan_kernel(ScanParams p) {
   // compute of the current tile).  FULL: all 16 tokens are inside the work item.
   // Otherwise tokens at or past l_end re-read the last valid token and are then replaced
   // by zero (delta = 0 and u = 0 leave the state unchanged: Abar = 1 and Bbar = 0).
-  auto load_tile = [&](int64_t l0, auto full_tag) {
+  auto load_tile = [&](int64_t l0, auto full_tag, auto set_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
+    constexpr int SET = decltype(set_tag)::value;
     const int64_t rem = l_end - l0;         // tokens left from l0 (uniform, >= 1)
     if (!TI) {
       const char* bb = bbase0 + l0 * p.B_sl * ES;
       const char* cb = cbase0 + l0 * p.C_sl * ES;
 #pragma unroll
       for (int r = 0; r < NB; ++r) {
-        uint32_t ob = offB[r], oc = offC[r];
+        const int tl = tl0 + kRowsPerLoad * r;
+        uint32_t ob = offB0 + uint32_t(r) * stepB, oc = offC0 + uint32_t(r) * stepC;
         bool ok = true;
-        if (!FULL) {
-          ok = tlB[r] < rem;
-          const int64_t tlc = ok ? tlB[r] : rem - 1;
-          ob = uint32_t((tlc * p.B_sl + nB[r]) * ES);
-          oc = uint32_t((tlc * p.C_sl + nB[r]) * ES);
+        if (!FULL) {               // clamp to the last valid token (in bounds), zero below
+          ok = tl < rem;
+          const int64_t tlc = ok ? tl : rem - 1;
+          ob = uint32_t((tlc * p.B_sl + n0c) * ES);
+          oc = uint32_t((tlc * p.C_sl + n0c) * ES);
         }
         uint32_t vb = T::raw_at(bb, ob);
         uint32_t vc = READOUT ? T::raw_at(cb, oc) : 0u;
-        if (!FULL) {              // last tile only: select (waits on these loads here)
+        if (!FULL) {              // tail tile only: select (waits on these loads here)
           vb = ok ? vb : 0u;
           vc = ok ? vc : 0u;
         }
-        rB[r] = vb;
-        if (READOUT) rC[r] = vc;
+        rB[SET][r] = vb;
+        if (READOUT) rC[SET][r] = vc;
       }
     }
     const char* ub = ubase0 + l0 * p.u_sl * ES;
@@ -320,24 +324,42 @@ void scan_kernel(ScanParams p) {
         vd = ok ? vd : 0u;
         vz = ok ? vz : 0u;
       }
-      rU[m] = vu;
-      if (!TI) rD[m] = vd;
-      rZ[m] = vz;
+      rU[SET][m] = vu;
+      if (!TI) rD[SET][m] = vd;
+      rZ[SET][m] = vz;
     }
   };
 
   // Steps of the recurrence on the staged tile; partial readouts to pacc.  FULL: all 16
   // tokens; otherwise only the first `nsteps` (a uniform count) -- needed for the
   // time-invariant form, whose decay does not vanish on the zero-padded tokens.
-  auto compute_tile = [&](float (&pacc)[kTile], auto zero_tag, auto full_tag, int64_t nsteps) {
+  // The tile is walked in four groups of four tokens; the LDS operands of group q+1 are
+  // read while group q computes, and a scheduling barrier between groups keeps the
+  // compiler from hoisting every read of the tile (which would cost ~64 VGPRs).
+  // The group's four partial readouts are written straight to this lane's row of sP.
+  float* const prow = sP + c * LDS::kChan + s * kRowPad;
+  auto compute_tile = [&](auto zero_tag, auto full_tag, int64_t nsteps) {
     constexpr bool ZERO = decltype(zero_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
+    float4 u4[2], d4[2], b4[2][K], c4[2][K];
+    auto read_group = [&](int q, int buf) {
+      u4[buf] = *reinterpret_cast<const float4*>(sU + c * kRowPad + 4 * q);
+      if (!TI) {
+        d4[buf] = *reinterpret_cast<const float4*>(sD + c * kRowPad + 4 * q);
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) pacc[j] = 0.f;
+        for (int k = 0; k < K; ++k) {
+          b4[buf][k] = *reinterpret_cast<const float4*>(sB + (s + S * k) * kRowPad + 4 * q);
+          if (READOUT) c4[buf][k] = *reinterpret_cast<const float4*>(sC + (s + S * k) * kRowPad + 4 * q);
+        }
+      }
+    };
+    read_group(0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 u4 = *reinterpret_cast<const float4*>(sU + c * kRowPad + 4 * q);
-      const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+      const int cur = q & 1;
+      if (q + 1 < 4) read_group(q + 1, cur ^ 1);
+      const float uu[4] = {u4[cur].x, u4[cur].y, u4[cur].z, u4[cur].w};
+      float pacc[4] = {0.f, 0.f, 0.f, 0.f};
       if (TI) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -348,98 +370,80 @@ void scan_kernel(ScanParams p) {
             h[k] = fmaf(Ab[k], h[k], uu[j]);                 // g = Abar g + u
             if (READOUT) acc = fmaf(CB[k], h[k], acc);       // y += C Bbar g
           }
-          pacc[4 * q + j] = acc;
+          pacc[j] = acc;
         }
       } else {
-        const float4 d4 = *reinterpret_cast<const float4*>(sD + c * kRowPad + 4 * q);
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-        float bb[K][4], cc[K][4];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const float4 b4 = *reinterpret_cast<const float4*>(sB + (s + S * k) * kRowPad + 4 * q);
-          bb[k][0] = b4.x; bb[k][1] = b4.y; bb[k][2] = b4.z; bb[k][3] = b4.w;
-          if (READOUT) {
-            const float4 c4 = *reinterpret_cast<const float4*>(sC + (s + S * k) * kRowPad + 4 * q);
-            cc[k][0] = c4.x; cc[k][1] = c4.y; cc[k][2] = c4.z; cc[k][3] = c4.w;
-          }
-        }
+        const float dd[4] = {d4[cur].x, d4[cur].y, d4[cur].z, d4[cur].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (!FULL && 4 * q + j >= nsteps) break;
           float acc = 0.f;
 #pragma unroll
           for (int k = 0; k < K; ++k) {
+            const float bj = j == 0 ? b4[cur][k].x : j == 1 ? b4[cur][k].y : j == 2 ? b4[cur][k].z : b4[cur][k].w;
             const float ab = __builtin_amdgcn_exp2f(dd[j] * A2[k]);   // Abar = exp(delta A)
             float f = fmaf(ab, iA[k], -iA[k]);                        // (Abar - 1)/A
             if (ZERO) f = fmaf(dd[j], zf[k], f);                       // A == 0: delta
-            h[k] = fmaf(ab, h[k], f * (bb[k][j] * uu[j]));             // h = Abar h + Bbar u
-            if (READOUT) acc = fmaf(cc[k][j], h[k], acc);              // C . h (updated state)
+            h[k] = fmaf(ab, h[k], f * (bj * uu[j]));                   // h = Abar h + Bbar u
+            if (READOUT) {
+              const float cj = j == 0 ? c4[cur][k].x : j == 1 ? c4[cur][k].y : j == 2 ? c4[cur][k].z : c4[cur][k].w;
+              acc = fmaf(cj, h[k], acc);                               // C . h (updated state)
+            }
           }
-          pacc[4 * q + j] = acc;
+          pacc[j] = acc;
         }
       }
+      if (READOUT) *reinterpret_cast<float4*>(prow + 4 * q) = make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   float dsum = 0.f;                         // MODE_STATE: sum of delta over the chunk
   const int64_t nfull = (l_end - l_begin) / kTile;
-  const int64_t ntiles = (l_end - l_begin + kTile - 1) / kTile;
+  const bool has_partial = (l_end - l_begin) % kTile != 0;
   using full_t = std::integral_constant<bool, true>;
   using part_t = std::integral_constant<bool, false>;
-  if (ntiles > 0) {
-    if (nfull > 0) load_tile(l_begin, full_t{});
-    else load_tile(l_begin, part_t{});
-  }
+  using tail_set = std::integral_constant<int, kPrefetch>;
 
-  for (int64_t t = 0; t < ntiles; ++t) {
+  // One tile: stage set SET into LDS, refill SET with tile t + kPrefetch, run the steps,
+  // reduce the partial readouts and finalise this lane's tokens.
+  auto process = [&](int64_t t, auto set_tag, auto full_tag, auto zero_tag) {
+    constexpr int SET = decltype(set_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
     const int64_t l0 = l_begin + t * kTile;
     wave_lds_sync();                        // previous tile's LDS reads are done
     if (!TI) {
 #pragma unroll
       for (int r = 0; r < NB; ++r) {
-        const int e = lane + 64 * r;
-        const int tl = e / NP, n = e % NP;
-        sB[n * kRowPad + tl] = T::from_raw(rB[r] & maskB[r]);
-        if (READOUT) sC[n * kRowPad + tl] = T::from_raw(rC[r] & maskB[r]);
+        const int tl = tl0 + kRowsPerLoad * r;
+        sB[n0 * kRowPad + tl] = T::from_raw(rB[SET][r] & maskB);
+        if (READOUT) sC[n0 * kRowPad + tl] = T::from_raw(rC[SET][r] & maskB);
       }
     }
     float uo[M], zo[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float fu = T::from_raw(rU[m]);
+      const float fu = T::from_raw(rU[SET][m]);
       sU[c * kRowPad + s + S * m] = fu;
       if (!TI) {
-        const float fd = T::from_raw(rD[m]);
+        const float fd = T::from_raw(rD[SET][m]);
         sD[c * kRowPad + s + S * m] = fd;
         if (MODE == MODE_STATE) dsum += fd;      // lane sums its own tokens; reduced below
       }
       uo[m] = fu;
-      zo[m] = gate ? T::from_raw(rZ[m]) : 0.f;
+      zo[m] = gate ? T::from_raw(rZ[SET][m]) : 0.f;
     }
-    if (t + 1 < nfull) load_tile(l0 + kTile, full_t{});          // prefetch the next tile
-    else if (t + 1 < ntiles) load_tile(l0 + kTile, part_t{});
+    if (FULL && t + kPrefetch < nfull)           // keep kPrefetch tiles of loads in flight
+      load_tile(l_begin + (t + kPrefetch) * kTile, full_t{}, set_tag);
     wave_lds_sync();
 
-    float pacc[kTile];
-    if (t < nfull) {
-      if (wave_zero) compute_tile(pacc, full_t{}, full_t{}, kTile);
-      else compute_tile(pacc, part_t{}, full_t{}, kTile);
-    } else {
-      const int64_t nsteps = l_end - l0;
-      if (wave_zero) compute_tile(pacc, full_t{}, part_t{}, nsteps);
-      else compute_tile(pacc, part_t{}, part_t{}, nsteps);
-    }
+    const int64_t nsteps = FULL ? kTile : l_end - l0;
+    compute_tile(zero_tag, full_tag, nsteps);
 
     if (READOUT) {
       // ---- transpose the partial readouts of this channel: lane (c, s) -> tokens s + S m
-      float* row = sP + c * LDS::kChan + s * kRowPad;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(row + 4 * q) =
-            make_float4(pacc[4 * q], pacc[4 * q + 1], pacc[4 * q + 2], pacc[4 * q + 3]);
       wave_lds_sync();
       char* yb = ybase0 + l0 * p.y_sl * ES;
-      const int64_t rem = l_end - l0;
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const int tl = s + S * m;
@@ -453,10 +457,33 @@ void scan_kernel(ScanParams p) {
           const float sig = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
           yv *= zz * sig;                                              // * SiLU(z)
         }
-        if (dvalid && tl < rem) T::put(yb, offY[m], yv);
+        if (dvalid && (FULL || tl < nsteps)) T::put(yb, offY[m], yv);
       }
     }
-  }
+  };
+
+  // The whole tile loop, for one of the two forms of the input coefficient (a wave-uniform
+  // choice made once: waves with an A == 0 state need the delta*B form).
+  auto run = [&](auto zero_tag) {
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1 % kPrefetch>;
+    using I2 = std::integral_constant<int, 2 % kPrefetch>;
+    if (0 < nfull) load_tile(l_begin, full_t{}, I0{});
+    if (kPrefetch > 1 && 1 < nfull) load_tile(l_begin + kTile, full_t{}, I1{});
+    if (kPrefetch > 2 && 2 < nfull) load_tile(l_begin + 2 * kTile, full_t{}, I2{});
+    for (int64_t t0 = 0; t0 < nfull; t0 += kPrefetch) {
+      process(t0, I0{}, full_t{}, zero_tag);
+      if (kPrefetch > 1 && t0 + 1 < nfull) process(t0 + 1, I1{}, full_t{}, zero_tag);
+      if (kPrefetch > 2 && t0 + 2 < nfull) process(t0 + 2, I2{}, full_t{}, zero_tag);
+    }
+    if (has_partial) {
+      load_tile(l_begin + nfull * kTile, part_t{}, tail_set{});
+      process(nfull, tail_set{}, part_t{}, zero_tag);
+    }
+  };
+  static_assert(kPrefetch >= 1 && kPrefetch <= 3, "the ring prologue issues up to three tiles");
+  if (wave_zero) run(full_t{});
+  else run(part_t{});
 
   // ---- outputs that follow the last token of the work item
   if (MODE == MODE_STATE) {
