@@ -68,9 +68,11 @@ enum selscan_status {
   SELSCAN_ERR_NULL = -1,        /* a required pointer (u, delta, A, B, C, y, dims) is NULL;
                                    only A and dims are required when batch * seqlen == 0 */
   SELSCAN_ERR_DIMS = -2,        /* batch < 0, seqlen < 0, dim < 1, dstate < 1, or a negative stride */
-  SELSCAN_ERR_UNSUPPORTED = -3, /* dstate > 64, unknown dtype or path, or a B/C/delta stride
+  SELSCAN_ERR_UNSUPPORTED = -3, /* dstate > 64, unknown dtype or path, a B/C/delta stride
                                    pattern that is neither per-token (shared over channels)
-                                   nor per-channel (time-invariant) */
+                                   nor per-channel (time-invariant), overlapping y rows
+                                   (y_sl < dim or y_sb < seqlen * y_sl), or a size beyond the
+                                   32-bit tile addressing of the kernels */
   SELSCAN_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
   SELSCAN_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed; the HIP error
                                    code is available from selective_scan_last_hip_error() */
@@ -85,8 +87,11 @@ enum selscan_status {
 enum selscan_path {
   SELSCAN_PATH_AUTO = 0,
   SELSCAN_PATH_SINGLE = 1,   /* one pass along the sequence per (batch, channel group) */
-  SELSCAN_PATH_CHUNKED = 2   /* two passes over chunks of the sequence, joined by a scan
+  SELSCAN_PATH_CHUNKED = 2,  /* two passes over chunks of the sequence, joined by a scan
                                 of per-chunk affine maps */
+  /* Bit that may be or-ed into any path (tests only): use the per-element I/O kernels even
+   * where the 4-channel vector I/O kernels apply.  Results agree within fp32 rounding. */
+  SELSCAN_PATH_FLAG_SCALAR_IO = 0x100
 };
 
 /*
@@ -119,7 +124,7 @@ typedef struct selscan_dims {
   int64_t y_sb, y_sl;
   int64_t B_sb, B_sl, B_sd;
   int64_t C_sb, C_sl, C_sd;
-  int32_t path;         /* enum selscan_path; 0 = automatic */
+  int32_t path;         /* enum selscan_path, optionally | SELSCAN_PATH_FLAG_SCALAR_IO; 0 = automatic */
   int32_t chunk_len;    /* chunked path: tokens per chunk, a multiple of 16 (0 = automatic) */
 } selscan_dims;
 

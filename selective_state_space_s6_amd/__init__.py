@@ -31,6 +31,7 @@ SELSCAN_OK = 0
 SELSCAN_ERR_NULL, SELSCAN_ERR_DIMS, SELSCAN_ERR_UNSUPPORTED = -1, -2, -3
 SELSCAN_ERR_ALIGN, SELSCAN_ERR_HIP, SELSCAN_ERR_WORKSPACE, SELSCAN_ERR_ABI = -4, -5, -6, -7
 PATHS = {"auto": 0, "single": 1, "chunked": 2}
+FLAG_SCALAR_IO = 0x100   # tests only: force the per-element I/O kernels
 
 
 class SelscanDims(ctypes.Structure):
@@ -136,7 +137,8 @@ def _strides_bld(t, name, batch, L, D):
     return t.stride(0), t.stride(1)
 
 
-def make_dims(u, delta, A, B, C, z=None, y=None, *, path: str = "auto", chunk_len: int = 0) -> SelscanDims:
+def make_dims(u, delta, A, B, C, z=None, y=None, *, path: str = "auto", chunk_len: int = 0,
+              scalar_io: bool = False) -> SelscanDims:
     """Build selscan_dims from tensor shapes and strides (see the module docstring)."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, L, D]")
@@ -173,14 +175,14 @@ def make_dims(u, delta, A, B, C, z=None, y=None, *, path: str = "auto", chunk_le
         d.z_sb, d.z_sl = _strides_bld(z, "z", batch, L, D)
     if y is not None:
         d.y_sb, d.y_sl = _strides_bld(y, "y", batch, L, D)
-    d.path = PATHS[path]
+    d.path = PATHS[path] | (FLAG_SCALAR_IO if scalar_io else 0)
     d.chunk_len = int(chunk_len)
     return d
 
 
 def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state=None, *,
                        return_last_state: bool = False, path: str = "auto", chunk_len: int = 0,
-                       workspace=None, stream=None) -> Tuple["object", Optional["object"]]:
+                       scalar_io: bool = False, workspace=None, stream=None) -> Tuple["object", Optional["object"]]:
     """Selective-scan forward on the GPU.  Returns (y, last_state or None).
 
     ``y`` / ``last_state`` may be given (outputs are written in place) or are allocated.
@@ -208,7 +210,7 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
     if last_state is not None and (last_state.dtype != torch.float32 or not last_state.is_contiguous()
                                    or tuple(last_state.shape) != (batch, D, N)):
         raise ValueError("last_state must be a contiguous float32 [batch, D, N] tensor")
-    dims = make_dims(u, delta, A, B, C, z, y, path=path, chunk_len=chunk_len)
+    dims = make_dims(u, delta, A, B, C, z, y, path=path, chunk_len=chunk_len, scalar_io=scalar_io)
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):

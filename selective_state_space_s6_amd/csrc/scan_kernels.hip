@@ -59,49 +59,19 @@ constexpr int kPrefetchMax = 2;  // tiles of global loads kept in flight per wav
 enum { MODE_SINGLE = 0, MODE_STATE = 1, MODE_APPLY = 2 };
 
 // ---------------------------------------------------------------------------------------
-// element I/O.  Loads address a wave-uniform base pointer (kept in SGPRs) plus a 32-bit
-// per-lane byte offset that is fixed for the whole kernel, so the per-tile address work is
-// scalar.
+// element types: per-token tensors travel as raw bit patterns (see the buffer loads in the
+// kernel) and are widened to fp32 when staged.
 
 template <typename IO> struct io_traits;
 template <> struct io_traits<float> {
   static constexpr int kBytes = 4;
   static __device__ __forceinline__ float widen(float v) { return v; }
-  // raw bit patterns, so a loaded value can stay untouched in a register until it is used
-  static __device__ __forceinline__ uint32_t raw_at(const char* base, uint32_t off) {
-    return *reinterpret_cast<const uint32_t*>(base + off);
-  }
-  static __device__ __forceinline__ uint32_t raw_stream(const char* base, uint32_t off) {
-    return *reinterpret_cast<const uint32_t*>(base + off);
-  }
   static __device__ __forceinline__ float from_raw(uint32_t r) { return __uint_as_float(r); }
-  static __device__ __forceinline__ float at(const char* base, uint32_t off) {
-    return *reinterpret_cast<const float*>(base + off);
-  }
-  static __device__ __forceinline__ void put(char* base, uint32_t off, float v) {
-    *reinterpret_cast<float*>(base + off) = v;
-  }
 };
 template <> struct io_traits<uint16_t> {   // bfloat16 bit patterns
   static constexpr int kBytes = 2;
   static __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-  static __device__ __forceinline__ uint32_t raw_at(const char* base, uint32_t off) {
-    return *reinterpret_cast<const uint16_t*>(base + off);
-  }
-  static __device__ __forceinline__ uint32_t raw_stream(const char* base, uint32_t off) {
-    return *reinterpret_cast<const uint16_t*>(base + off);
-  }
   static __device__ __forceinline__ float from_raw(uint32_t r) { return __uint_as_float(r << 16); }
-  static __device__ __forceinline__ float at(const char* base, uint32_t off) {
-    return widen(*reinterpret_cast<const uint16_t*>(base + off));
-  }
-  static __device__ __forceinline__ void put(char* base, uint32_t off, float v) {
-    // round to nearest even; NaN stays a quiet NaN
-    const uint32_t x = __float_as_uint(v);
-    const uint32_t r = ((x & 0x7fffffffu) > 0x7f800000u) ? ((x >> 16) | 0x40u)
-                                                         : ((x + 0x7fffu + ((x >> 16) & 1u)) >> 16);
-    *reinterpret_cast<uint16_t*>(base + off) = uint16_t(r);
-  }
 };
 
 // Order this wave's LDS traffic: every LDS write before the barrier is visible to every
@@ -180,7 +150,6 @@ void scan_kernel(ScanParams p) {
   const int64_t d0 = int64_t(g) * CW;                     // first channel of the group (uniform)
   const int64_t d = d0 + c;
   const bool dvalid = d < D;
-  const int cl = dvalid ? c : 0;                          // clamped channel for in-bounds loads
   const int64_t l_begin = int64_t(chunk) * p.chunk_len;
   const int64_t l_end = (l_begin + p.chunk_len < p.L) ? l_begin + p.chunk_len : p.L;
 
@@ -189,9 +158,9 @@ void scan_kernel(ScanParams p) {
   float Ab[K], CB[K];                 // time-invariant: Abar and C*Bbar, hoisted
   bool any_zero = false;
   float dt_ti = 0.f;
-  const char* const Bbase = static_cast<const char*>(p.B);
-  const char* const Cbase = static_cast<const char*>(p.C);
-  if (TI) dt_ti = dvalid ? T::at(static_cast<const char*>(p.delta), uint32_t(d * ES)) : 0.f;
+  const IO* const Bti = static_cast<const IO*>(p.B);    // time-invariant: B[d][n], C[d][n]
+  const IO* const Cti = static_cast<const IO*>(p.C);
+  if (TI) dt_ti = dvalid ? T::widen(static_cast<const IO*>(p.delta)[d]) : 0.f;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t n = s + S * k;
@@ -204,8 +173,8 @@ void scan_kernel(ScanParams p) {
     h[k] = 0.f;
     if (TI) {
       // Abar = exp(delta a); Bbar = expm1(delta a)/a * B (delta * B when a == 0)
-      const float bv = ok ? T::widen(reinterpret_cast<const IO*>(Bbase)[d * p.B_sd + n]) : 0.f;
-      const float cv = ok ? T::widen(reinterpret_cast<const IO*>(Cbase)[d * p.C_sd + n]) : 0.f;
+      const float bv = ok ? T::widen(Bti[d * p.B_sd + n]) : 0.f;
+      const float cv = ok ? T::widen(Cti[d * p.C_sd + n]) : 0.f;
       Ab[k] = ok ? expf(dt_ti * a) : 1.f;
       const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
       CB[k] = ok ? cv * coeff * bv : 0.f;
@@ -225,124 +194,104 @@ void scan_kernel(ScanParams p) {
     }
   }
 
-  // ---- per-lane byte offsets inside a tile (fixed for the kernel)
+  // ---- buffer resources.  Every per-token tensor is addressed through a buffer descriptor
+  // whose base is this work item's first token (and, for u/delta/z/y, its first channel)
+  // and whose size ends at the work item's last valid element.  Each lane keeps a fixed
+  // 32-bit offset inside a tile; the tile's position goes into the scalar offset.  Reads
+  // past the end (tokens at or after l_end, channels at or after D) return 0 and writes
+  // there are dropped by the hardware range check, so no guard code is needed: a zero
+  // token (delta = 0, u = 0) leaves the selective state unchanged (Abar = 1, Bbar = 0).
+  constexpr uint32_t kOOB = 0x80000000u;    // an offset beyond every descriptor's size
+  constexpr int kRsrcWord3 = 0x00020000;
+  const int64_t nrows = l_end - l_begin;
+  auto rsrc = [&](const void* base, int64_t sb, int64_t sl, int64_t col0, int64_t ncols) __attribute__((always_inline)) {
+    const char* p0 = static_cast<const char*>(base) + (b * sb + l_begin * sl + col0) * ES;
+    const int64_t bytes = nrows > 0 ? ((nrows - 1) * sl + ncols) * ES : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p0), (short)0, int(bytes), kRsrcWord3);
+  };
+  const int64_t z_sb = p.z != nullptr ? p.z_sb : p.u_sb, z_sl = p.z != nullptr ? p.z_sl : p.u_sl;
+  const auto rU = rsrc(p.u, p.u_sb, p.u_sl, d0, D - d0);
+  const auto rD = rsrc(p.delta, p.delta_sb, p.delta_sl, d0, D - d0);
+  // without a gate the z loads re-read u (always valid memory) and are ignored
+  const auto rZ = rsrc(p.z != nullptr ? p.z : p.u, z_sb, z_sl, d0, D - d0);
+  const auto rY = rsrc(p.y, p.y_sb, p.y_sl, d0, D - d0);
+  const auto rBd = rsrc(p.B, p.B_sb, p.B_sl, 0, N);
+  const auto rCd = rsrc(p.C, p.C_sb, p.C_sl, 0, N);
+
+  // per-lane offsets: token s + S m of the tile, channel c (out of range when d >= D)
   uint32_t offU[M], offD[M], offZ[M], offY[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int64_t tl = s + S * m;
-    offU[m] = uint32_t((tl * p.u_sl + cl) * ES);
-    offD[m] = uint32_t((tl * p.delta_sl + cl) * ES);
-    offZ[m] = uint32_t((tl * (p.z != nullptr ? p.z_sl : p.u_sl) + cl) * ES);
-    offY[m] = uint32_t((tl * p.y_sl + cl) * ES);
+    offU[m] = dvalid ? uint32_t((tl * p.u_sl + c) * ES) : kOOB;
+    offD[m] = dvalid ? uint32_t((tl * p.delta_sl + c) * ES) : kOOB;
+    offZ[m] = dvalid ? uint32_t((tl * z_sl + c) * ES) : kOOB;
+    offY[m] = dvalid ? uint32_t((tl * p.y_sl + c) * ES) : kOOB;
   }
   // B/C tile element r of this lane: token tl0 + r * (64 / NP), state n0 (the same state for
-  // every r, since NP divides 64).  Only the r = 0 offset is per-lane; the rest is a uniform
-  // multiple of the token stride.
+  // every r, since NP divides 64).  The per-row part of the address is a scalar offset.
   static_assert(64 % NP == 0, "padded state count must divide the wavefront");
   constexpr int kRowsPerLoad = 64 / NP;
   const int tl0 = lane / NP, n0 = lane % NP;
-  const int n0c = n0 < N ? n0 : 0;          // padded state slots read state 0, then masked to zero
-  const uint32_t maskB = n0 < N ? 0xffffffffu : 0u;
-  const uint32_t offB0 = uint32_t((tl0 * p.B_sl + n0c) * ES);
-  const uint32_t offC0 = uint32_t((tl0 * p.C_sl + n0c) * ES);
-  const uint32_t stepB = uint32_t(kRowsPerLoad * p.B_sl * ES);   // uniform
-  const uint32_t stepC = uint32_t(kRowsPerLoad * p.C_sl * ES);
+  const uint32_t maskB = n0 < N ? 0xffffffffu : 0u;   // padded state slots read as zero
+  const uint32_t offB0 = uint32_t((tl0 * p.B_sl + (n0 < N ? n0 : 0)) * ES);
+  const uint32_t offC0 = uint32_t((tl0 * p.C_sl + (n0 < N ? n0 : 0)) * ES);
 
-  // ---- staging registers: the next tile's operands as raw bit patterns (widened when staged
-  // into LDS at the top of the next tile, so no instruction waits on the loads before then)
-  // kPrefetch register sets of full-tile loads in flight (tile t lives in set t % kPrefetch),
-  // plus one set for the ragged tail tile, which is loaded after the ring has drained.
-  constexpr int NSET = kPrefetch + 1;
-  uint32_t rB[NSET][TI ? 1 : NB], rC[NSET][TI ? 1 : NB];
-  uint32_t rU[NSET][M], rD[NSET][M], rZ[NSET][M];
+  // ---- staging registers: kPrefetch tiles of loads in flight, kept as raw bit patterns
+  // (widened when staged into LDS, so no instruction waits on a load before then).
+  uint32_t xB[kPrefetch][TI ? 1 : NB], xC[kPrefetch][TI ? 1 : NB];
+  uint32_t xU[kPrefetch][M], xD[kPrefetch][M], xZ[kPrefetch][M];
   const bool gate = (p.z != nullptr) && READOUT;
   const bool has_d = (p.Dskip != nullptr) && READOUT;
   const float dskip = (has_d && dvalid) ? p.Dskip[d] : 0.f;
-  const char* const ubase0 = static_cast<const char*>(p.u) + (b * p.u_sb + d0) * ES;
-  const char* const dbase0 = static_cast<const char*>(p.delta) + (b * p.delta_sb + d0) * ES;
-  // Without a gate the z loads re-read u (same shape, always in bounds) and are ignored,
-  // so that no load sits under a branch.
-  const int64_t z_sb = p.z != nullptr ? p.z_sb : p.u_sb, z_sl = p.z != nullptr ? p.z_sl : p.u_sl;
-  const char* const zbase0 = static_cast<const char*>(p.z != nullptr ? p.z : p.u) + (b * z_sb + d0) * ES;
-  char* const ybase0 = static_cast<char*>(p.y) + (b * p.y_sb + d0) * ES;
-  const char* const bbase0 = Bbase + b * p.B_sb * ES;
-  const char* const cbase0 = Cbase + b * p.C_sb * ES;
 
-  // Load the operands of the tile starting at token l0.  Every load is unconditional and
-  // in bounds (so the compiler emits straight-line loads whose latency overlaps the
-  // compute of the current tile).  FULL: all 16 tokens are inside the work item.
-  // Otherwise tokens at or past l_end re-read the last valid token and are then replaced
-  // by zero (delta = 0 and u = 0 leave the state unchanged: Abar = 1 and Bbar = 0).
-  auto load_tile = [&](int64_t l0, auto full_tag, auto set_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    constexpr int SET = decltype(set_tag)::value;
-    const int64_t rem = l_end - l0;         // tokens left from l0 (uniform, >= 1)
-    if (!TI) {
-      const char* bb = bbase0 + l0 * p.B_sl * ES;
-      const char* cb = cbase0 + l0 * p.C_sl * ES;
-#pragma unroll
-      for (int r = 0; r < NB; ++r) {
-        const int tl = tl0 + kRowsPerLoad * r;
-        uint32_t ob = offB0 + uint32_t(r) * stepB, oc = offC0 + uint32_t(r) * stepC;
-        bool ok = true;
-        if (!FULL) {               // clamp to the last valid token (in bounds), zero below
-          ok = tl < rem;
-          const int64_t tlc = ok ? tl : rem - 1;
-          ob = uint32_t((tlc * p.B_sl + n0c) * ES);
-          oc = uint32_t((tlc * p.C_sl + n0c) * ES);
-        }
-        uint32_t vb = T::raw_at(bb, ob);
-        uint32_t vc = READOUT ? T::raw_at(cb, oc) : 0u;
-        if (!FULL) {              // tail tile only: select (waits on these loads here)
-          vb = ok ? vb : 0u;
-          vc = ok ? vc : 0u;
-        }
-        rB[SET][r] = vb;
-        if (READOUT) rC[SET][r] = vc;
-      }
-    }
-    const char* ub = ubase0 + l0 * p.u_sl * ES;
-    const char* db = dbase0 + l0 * p.delta_sl * ES;
-    const char* zb = zbase0 + l0 * z_sl * ES;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      uint32_t ou = offU[m], od = offD[m], oz = offZ[m];
-      bool ok = true;
-      if (!FULL) {
-        const int64_t tl = s + S * m;
-        ok = tl < rem;
-        const int64_t tlc = ok ? tl : rem - 1;
-        ou = uint32_t((tlc * p.u_sl + cl) * ES);
-        od = uint32_t((tlc * p.delta_sl + cl) * ES);
-        oz = uint32_t((tlc * z_sl + cl) * ES);
-      }
-      uint32_t vu = T::raw_stream(ub, ou);
-      uint32_t vd = TI ? 0u : T::raw_stream(db, od);
-      uint32_t vz = READOUT ? T::raw_stream(zb, oz) : 0u;
-      if (!FULL) {
-        vu = ok ? vu : 0u;
-        vd = ok ? vd : 0u;
-        vz = ok ? vz : 0u;
-      }
-      rU[SET][m] = vu;
-      if (!TI) rD[SET][m] = vd;
-      rZ[SET][m] = vz;
+  auto load_raw = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int64_t soff) __attribute__((always_inline)) -> uint32_t {
+    if (ES == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, int(soff), 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, int(soff), 0);
+  };
+  auto store_y = [&](float v, uint32_t voff, int64_t soff) __attribute__((always_inline)) {
+    if (ES == 2) {
+      // round to nearest even; NaN stays a quiet NaN
+      const uint32_t x = __float_as_uint(v);
+      const uint32_t rr = ((x & 0x7fffffffu) > 0x7f800000u) ? ((x >> 16) | 0x40u)
+                                                            : ((x + 0x7fffu + ((x >> 16) & 1u)) >> 16);
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)rr, rY, voff, int(soff), 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rY, voff, int(soff), 0);
     }
   };
 
-  // Steps of the recurrence on the staged tile; partial readouts to pacc.  FULL: all 16
-  // tokens; otherwise only the first `nsteps` (a uniform count) -- needed for the
-  // time-invariant form, whose decay does not vanish on the zero-padded tokens.
-  // The tile is walked in four groups of four tokens; the LDS operands of group q+1 are
-  // read while group q computes, and a scheduling barrier between groups keeps the
-  // compiler from hoisting every read of the tile (which would cost ~64 VGPRs).
-  // The group's four partial readouts are written straight to this lane's row of sP.
+  // Issue the loads of tile t (0-based within the work item) into register set SET.
+  auto load_tile = [&](int64_t t, auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+    const int64_t row0 = t * kTile;
+    if (!TI) {
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        const int64_t row = row0 + int64_t(kRowsPerLoad) * r;
+        xB[SET][r] = load_raw(rBd, offB0, row * p.B_sl * ES);
+        if (READOUT) xC[SET][r] = load_raw(rCd, offC0, row * p.C_sl * ES);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      xU[SET][m] = load_raw(rU, offU[m], row0 * p.u_sl * ES);
+      if (!TI) xD[SET][m] = load_raw(rD, offD[m], row0 * p.delta_sl * ES);
+      if (READOUT) xZ[SET][m] = load_raw(rZ, offZ[m], row0 * z_sl * ES);
+    }
+  };
+
+  // Steps of the recurrence on the staged tile.  FULL: all 16 tokens; otherwise only the
+  // first `nsteps` (a uniform count).  The tile is walked in four groups of four
+  // tokens; the LDS operands of group q+1 are read while group q computes, and a scheduling
+  // barrier between groups keeps the compiler from hoisting every read of the tile.  Each
+  // group's four partial readouts go straight to this lane's row of sP.
   float* const prow = sP + c * LDS::kChan + s * kRowPad;
-  auto compute_tile = [&](auto zero_tag, auto full_tag, int64_t nsteps) {
+  auto compute_tile = [&](auto zero_tag, auto full_tag, int64_t nsteps) __attribute__((always_inline)) {
     constexpr bool ZERO = decltype(zero_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
     float4 u4[2], d4[2], b4[2][K], c4[2][K];
-    auto read_group = [&](int q, int buf) {
+    auto read_group = [&](int q, int buf) __attribute__((always_inline)) {
       u4[buf] = *reinterpret_cast<const float4*>(sU + c * kRowPad + 4 * q);
       if (!TI) {
         d4[buf] = *reinterpret_cast<const float4*>(sD + c * kRowPad + 4 * q);
@@ -399,51 +348,49 @@ void scan_kernel(ScanParams p) {
   };
 
   float dsum = 0.f;                         // MODE_STATE: sum of delta over the chunk
-  const int64_t nfull = (l_end - l_begin) / kTile;
-  const bool has_partial = (l_end - l_begin) % kTile != 0;
-  using full_t = std::integral_constant<bool, true>;
-  using part_t = std::integral_constant<bool, false>;
-  using tail_set = std::integral_constant<int, kPrefetch>;
+  const int64_t ntiles = (nrows + kTile - 1) / kTile;
+  const int64_t last_steps = nrows - (ntiles - 1) * kTile;   // tokens in the final tile
+  using true_t = std::integral_constant<bool, true>;
+  using false_t = std::integral_constant<bool, false>;
 
   // One tile: stage set SET into LDS, refill SET with tile t + kPrefetch, run the steps,
   // reduce the partial readouts and finalise this lane's tokens.
-  auto process = [&](int64_t t, auto set_tag, auto full_tag, auto zero_tag) {
+  auto process = [&](int64_t t, auto set_tag, auto zero_tag) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_tag)::value;
-    constexpr bool FULL = decltype(full_tag)::value;
-    const int64_t l0 = l_begin + t * kTile;
     wave_lds_sync();                        // previous tile's LDS reads are done
     if (!TI) {
 #pragma unroll
       for (int r = 0; r < NB; ++r) {
         const int tl = tl0 + kRowsPerLoad * r;
-        sB[n0 * kRowPad + tl] = T::from_raw(rB[SET][r] & maskB);
-        if (READOUT) sC[n0 * kRowPad + tl] = T::from_raw(rC[SET][r] & maskB);
+        sB[n0 * kRowPad + tl] = T::from_raw(xB[SET][r] & maskB);
+        if (READOUT) sC[n0 * kRowPad + tl] = T::from_raw(xC[SET][r] & maskB);
       }
     }
     float uo[M], zo[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float fu = T::from_raw(rU[SET][m]);
+      const float fu = T::from_raw(xU[SET][m]);
       sU[c * kRowPad + s + S * m] = fu;
       if (!TI) {
-        const float fd = T::from_raw(rD[SET][m]);
+        const float fd = T::from_raw(xD[SET][m]);
         sD[c * kRowPad + s + S * m] = fd;
         if (MODE == MODE_STATE) dsum += fd;      // lane sums its own tokens; reduced below
       }
       uo[m] = fu;
-      zo[m] = gate ? T::from_raw(rZ[SET][m]) : 0.f;
+      zo[m] = gate ? T::from_raw(xZ[SET][m]) : 0.f;
     }
-    if (FULL && t + kPrefetch < nfull)           // keep kPrefetch tiles of loads in flight
-      load_tile(l_begin + (t + kPrefetch) * kTile, full_t{}, set_tag);
+    if (t + kPrefetch < ntiles) load_tile(t + kPrefetch, set_tag);   // keep the ring full
     wave_lds_sync();
 
-    const int64_t nsteps = FULL ? kTile : l_end - l0;
-    compute_tile(zero_tag, full_tag, nsteps);
+    // The ragged final tile runs only its real tokens: operands given with a zero token
+    // stride (a per-channel delta, say) do not read as zero past the end.
+    if (t == ntiles - 1 && last_steps < kTile) compute_tile(zero_tag, false_t{}, last_steps);
+    else compute_tile(zero_tag, true_t{}, kTile);
 
     if (READOUT) {
       // ---- transpose the partial readouts of this channel: lane (c, s) -> tokens s + S m
       wave_lds_sync();
-      char* yb = ybase0 + l0 * p.y_sl * ES;
+      const int64_t soff_y = t * kTile * p.y_sl * ES;
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const int tl = s + S * m;
@@ -457,33 +404,29 @@ void scan_kernel(ScanParams p) {
           const float sig = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
           yv *= zz * sig;                                              // * SiLU(z)
         }
-        if (dvalid && (FULL || tl < nsteps)) T::put(yb, offY[m], yv);
+        store_y(yv, offY[m], soff_y);        // dropped past l_end or for d >= D
       }
     }
   };
 
-  // The whole tile loop, for one of the two forms of the input coefficient (a wave-uniform
+  // The tile loop, for one of the two forms of the input coefficient (a wave-uniform
   // choice made once: waves with an A == 0 state need the delta*B form).
-  auto run = [&](auto zero_tag) {
+  auto run = [&](auto zero_tag) __attribute__((always_inline)) {
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1 % kPrefetch>;
     using I2 = std::integral_constant<int, 2 % kPrefetch>;
-    if (0 < nfull) load_tile(l_begin, full_t{}, I0{});
-    if (kPrefetch > 1 && 1 < nfull) load_tile(l_begin + kTile, full_t{}, I1{});
-    if (kPrefetch > 2 && 2 < nfull) load_tile(l_begin + 2 * kTile, full_t{}, I2{});
-    for (int64_t t0 = 0; t0 < nfull; t0 += kPrefetch) {
-      process(t0, I0{}, full_t{}, zero_tag);
-      if (kPrefetch > 1 && t0 + 1 < nfull) process(t0 + 1, I1{}, full_t{}, zero_tag);
-      if (kPrefetch > 2 && t0 + 2 < nfull) process(t0 + 2, I2{}, full_t{}, zero_tag);
-    }
-    if (has_partial) {
-      load_tile(l_begin + nfull * kTile, part_t{}, tail_set{});
-      process(nfull, tail_set{}, part_t{}, zero_tag);
+    if (0 < ntiles) load_tile(0, I0{});
+    if (kPrefetch > 1 && 1 < ntiles) load_tile(1, I1{});
+    if (kPrefetch > 2 && 2 < ntiles) load_tile(2, I2{});
+    for (int64_t t0 = 0; t0 < ntiles; t0 += kPrefetch) {
+      process(t0, I0{}, zero_tag);
+      if (kPrefetch > 1 && t0 + 1 < ntiles) process(t0 + 1, I1{}, zero_tag);
+      if (kPrefetch > 2 && t0 + 2 < ntiles) process(t0 + 2, I2{}, zero_tag);
     }
   };
   static_assert(kPrefetch >= 1 && kPrefetch <= 3, "the ring prologue issues up to three tiles");
-  if (wave_zero) run(full_t{});
-  else run(part_t{});
+  if (wave_zero) run(true_t{});
+  else run(false_t{});
 
   // ---- outputs that follow the last token of the work item
   if (MODE == MODE_STATE) {
@@ -509,7 +452,376 @@ void scan_kernel(ScanParams p) {
         float hv = h[k];
         if (TI) {   // h = Bbar * g
           const float a = p.A[d * N + n];
-          const float bv = T::widen(reinterpret_cast<const IO*>(Bbase)[d * p.B_sd + n]);
+          const float bv = T::widen(Bti[d * p.B_sd + n]);
+          const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
+          hv = coeff * bv * hv;
+        }
+        p.last_state[(b * D + d) * N + n] = hv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// The same scan with vector I/O for the per-token tensors, used when 16 lanes share a
+// channel (so a wavefront owns 4 channels), D is a multiple of 4 and every row of u,
+// delta, z and y starts on a 4-element boundary.  The sequence is walked in super-tiles of
+// 64 tokens: lane (r, s) moves token 16 r + s of the wave's 4 channels as one 8-byte (bf16)
+// or 16-byte (fp32) access, so every lane is busy and each access covers a whole channel
+// group instead of one 2- or 4-byte element.  u and delta are staged channel-major for the
+// step loop; z is staged token-major for the epilogue; y is collected token-major in LDS
+// and written back once per super-tile.  B and C move per 16-token sub-tile exactly as in
+// scan_kernel.
+
+template <int K, bool TI>
+struct wave_lds_vec {
+  static constexpr int S = 16, CW = 4, NP = S * K;
+  static constexpr int kSuper = 64;                   // tokens per super-tile
+  static constexpr int kRowV = kSuper + 4;            // channel-major row of u / delta
+  static constexpr int kB = TI ? 0 : NP * kRowPad;    // sB[NP][20] (one 16-token sub-tile)
+  static constexpr int kC = kB;
+  static constexpr int kU = CW * kRowV;               // sU[4][68]
+  static constexpr int kD = TI ? 0 : CW * kRowV;      // sD[4][68]
+  static constexpr int kZ = kSuper * CW;              // sZ[64][4] token-major
+  static constexpr int kY = kSuper * CW;              // sY[64][4] token-major
+  static constexpr int kChan = 21 * S;
+  static constexpr int kP = CW * kChan;               // partial readouts, as in wave_lds
+  static constexpr int total = kB + kC + kU + kD + kZ + kY + kP;
+};
+
+template <typename IO> struct vec_io;
+template <> struct vec_io<float> {       // 4 channels = 16 bytes
+  using raw_t = uint32_t __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  }
+  static __device__ __forceinline__ float4 widen(raw_t v) {
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, float4 y) {
+    raw_t v = {__float_as_uint(y.x), __float_as_uint(y.y), __float_as_uint(y.z), __float_as_uint(y.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                           r, voff, soff, 0);
+  }
+};
+template <> struct vec_io<uint16_t> {    // 4 channels = 8 bytes of bfloat16
+  using raw_t = uint32_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+  }
+  static __device__ __forceinline__ float4 widen(raw_t v) {
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, float4 y) {
+    // round to nearest even (v_cvt_pk_bf16_f32)
+    const f32x2_t lo = {y.x, y.y}, hi = {y.z, y.w};
+    raw_t v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+               __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t))};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v),
+                                          r, voff, soff, 0);
+  }
+};
+
+template <typename IO, int K, bool TI, int MODE>
+__global__ __launch_bounds__(kWavesPerBlock * 64)
+__attribute__((amdgpu_waves_per_eu(occupancy<K>::kMinWaves, 8)))
+void scan_kernel_vec(ScanParams p) {
+  using T = io_traits<IO>;
+  using V = vec_io<IO>;
+  using LDS = wave_lds_vec<K, TI>;
+  constexpr int S = 16, CW = 4, NP = LDS::NP;
+  constexpr int NB = (NP * kTile) / 64;
+  constexpr bool READOUT = (MODE != MODE_STATE);
+  constexpr int ES = T::kBytes;
+  constexpr int kPrefetch = K <= 2 ? kPrefetchMax : 1;   // B/C sub-tiles in flight
+  constexpr int kSuper = LDS::kSuper, kRowV = LDS::kRowV;
+
+  extern __shared__ __align__(16) float smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int c = lane / S, s = lane % S;     // step layout: channel c, state slot s
+  const int vr = lane / 16, vs = lane % 16; // I/O layout: token 16 vr + vs of a super-tile
+
+  const int item = xcd_contiguous_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (item >= p.total_items) return;
+  const int g = item % p.groups;
+  const int bc = item / p.groups;
+  const int chunk = bc % p.n_chunks;
+  const int64_t b = bc / p.n_chunks;
+
+  float* const sB = smem + wave * LDS::total;
+  float* const sC = sB + LDS::kB;
+  float* const sU = sC + LDS::kC;
+  float* const sD = sU + LDS::kU;
+  float* const sZ = sD + LDS::kD;
+  float* const sY = sZ + LDS::kZ;
+  float* const sP = sY + LDS::kY;
+
+  const int64_t D = p.D, N = p.N;
+  const int64_t d0 = int64_t(g) * CW;
+  const int64_t d = d0 + c;                 // always < D here (D is a multiple of 4)
+  const int64_t l_begin = int64_t(chunk) * p.chunk_len;
+  const int64_t l_end = (l_begin + p.chunk_len < p.L) ? l_begin + p.chunk_len : p.L;
+
+  // ---- per-lane constants of the K owned states (see scan_kernel)
+  float A2[K], iA[K], zf[K], h[K], Ab[K], CB[K];
+  bool any_zero = false;
+  float dt_ti = 0.f;
+  const IO* const Bti = static_cast<const IO*>(p.B);
+  const IO* const Cti = static_cast<const IO*>(p.C);
+  if (TI) dt_ti = T::widen(static_cast<const IO*>(p.delta)[d]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t n = s + S * k;
+    const bool ok = n < N;
+    const float a = ok ? p.A[d * N + n] : 0.f;
+    A2[k] = a * kLog2e;
+    iA[k] = (a != 0.f) ? 1.0f / a : 0.f;
+    zf[k] = (ok && a == 0.f) ? 1.f : 0.f;
+    any_zero |= (ok && a == 0.f);
+    h[k] = 0.f;
+    Ab[k] = 0.f;
+    CB[k] = 0.f;
+    if (TI) {
+      const float bv = ok ? T::widen(Bti[d * p.B_sd + n]) : 0.f;
+      const float cv = ok ? T::widen(Cti[d * p.C_sd + n]) : 0.f;
+      Ab[k] = ok ? expf(dt_ti * a) : 1.f;
+      const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
+      CB[k] = ok ? cv * coeff * bv : 0.f;
+    }
+  }
+  const bool wave_zero = __builtin_amdgcn_readfirstlane(__ballot(any_zero) != 0ull ? 1 : 0) != 0;
+  if (MODE == MODE_APPLY) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t n = s + S * k;
+      if (n < N) h[k] = p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk];
+    }
+  }
+
+  // ---- buffer resources (see scan_kernel): base at this work item's first token
+  constexpr int kRsrcWord3 = 0x00020000;
+  const int64_t nrows = l_end - l_begin;
+  auto rsrc = [&](const void* base, int64_t sb, int64_t sl, int64_t col0, int64_t ncols) __attribute__((always_inline)) {
+    const char* p0 = static_cast<const char*>(base) + (b * sb + l_begin * sl + col0) * ES;
+    const int64_t bytes = nrows > 0 ? ((nrows - 1) * sl + ncols) * ES : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p0), (short)0, int(bytes), kRsrcWord3);
+  };
+  const int64_t z_sb = p.z != nullptr ? p.z_sb : p.u_sb, z_sl = p.z != nullptr ? p.z_sl : p.u_sl;
+  const auto rU = rsrc(p.u, p.u_sb, p.u_sl, d0, D - d0);
+  const auto rD = rsrc(p.delta, p.delta_sb, p.delta_sl, d0, D - d0);
+  const auto rZ = rsrc(p.z != nullptr ? p.z : p.u, z_sb, z_sl, d0, D - d0);
+  const auto rY = rsrc(p.y, p.y_sb, p.y_sl, d0, D - d0);
+  const auto rBd = rsrc(p.B, p.B_sb, p.B_sl, 0, N);
+  const auto rCd = rsrc(p.C, p.C_sb, p.C_sl, 0, N);
+  // I/O lane offsets: token 16 vr + vs of a super-tile, channels d0 .. d0 + 3
+  const uint32_t voU = uint32_t((16 * vr + vs) * p.u_sl * ES);
+  const uint32_t voD = uint32_t((16 * vr + vs) * p.delta_sl * ES);
+  const uint32_t voZ = uint32_t((16 * vr + vs) * z_sl * ES);
+  const uint32_t voY = uint32_t((16 * vr + vs) * p.y_sl * ES);
+  // B/C sub-tile element r of this lane: token tl0 + r * (64 / NP), state n0
+  static_assert(64 % NP == 0, "padded state count must divide the wavefront");
+  constexpr int kRowsPerLoad = 64 / NP;
+  const int tl0 = lane / NP, n0 = lane % NP;
+  const uint32_t maskB = n0 < N ? 0xffffffffu : 0u;
+  const uint32_t offB0 = uint32_t((tl0 * p.B_sl + (n0 < N ? n0 : 0)) * ES);
+  const uint32_t offC0 = uint32_t((tl0 * p.C_sl + (n0 < N ? n0 : 0)) * ES);
+
+  const bool gate = (p.z != nullptr) && READOUT;
+  const bool has_d = (p.Dskip != nullptr) && READOUT;
+  const float dskip = has_d ? p.Dskip[d] : 0.f;
+
+  auto load_raw = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int64_t soff) __attribute__((always_inline)) -> uint32_t {
+    if (ES == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, int(soff), 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, int(soff), 0);
+  };
+
+  // ---- B/C sub-tile ring (as in scan_kernel) and the super-tile u/delta/z registers
+  uint32_t xB[kPrefetch][TI ? 1 : NB], xC[kPrefetch][TI ? 1 : NB];
+  auto load_bc = [&](int64_t t, auto set_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+    if (!TI) {
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        const int64_t row = t * kTile + int64_t(kRowsPerLoad) * r;
+        xB[SET][r] = load_raw(rBd, offB0, row * p.B_sl * ES);
+        if (READOUT) xC[SET][r] = load_raw(rCd, offC0, row * p.C_sl * ES);
+      }
+    }
+  };
+  typename V::raw_t vU, vD, vZ;
+  auto load_super = [&](int64_t T0) __attribute__((always_inline)) {
+    const int64_t row0 = T0 * kSuper;
+    vU = V::load(rU, voU, int(row0 * p.u_sl * ES));
+    if (!TI) vD = V::load(rD, voD, int(row0 * p.delta_sl * ES));
+    if (READOUT) vZ = V::load(rZ, voZ, int(row0 * z_sl * ES));
+  };
+
+  float* const prow = sP + c * LDS::kChan + s * kRowPad;
+  float dsum = 0.f;
+
+  // 16 steps of sub-tile `sub` of the staged super-tile (channel-major rows of sU/sD).
+  auto compute_tile = [&](int sub, auto zero_tag, auto full_tag, int64_t nsteps) __attribute__((always_inline)) {
+    constexpr bool ZERO = decltype(zero_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
+    const float* uRow = sU + c * kRowV + kTile * sub;
+    const float* dRow = sD + c * kRowV + kTile * sub;
+    float4 u4[2], d4[2], b4[2][K], c4[2][K];
+    auto read_group = [&](int q, int buf) __attribute__((always_inline)) {
+      u4[buf] = *reinterpret_cast<const float4*>(uRow + 4 * q);
+      if (!TI) {
+        d4[buf] = *reinterpret_cast<const float4*>(dRow + 4 * q);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          b4[buf][k] = *reinterpret_cast<const float4*>(sB + (s + S * k) * kRowPad + 4 * q);
+          if (READOUT) c4[buf][k] = *reinterpret_cast<const float4*>(sC + (s + S * k) * kRowPad + 4 * q);
+        }
+      }
+    };
+    read_group(0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cur = q & 1;
+      if (q + 1 < 4) read_group(q + 1, cur ^ 1);
+      const float uu[4] = {u4[cur].x, u4[cur].y, u4[cur].z, u4[cur].w};
+      float pacc[4] = {0.f, 0.f, 0.f, 0.f};
+      if (TI) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!FULL && 4 * q + j >= nsteps) break;
+          float acc = 0.f;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            h[k] = fmaf(Ab[k], h[k], uu[j]);                 // g = Abar g + u
+            if (READOUT) acc = fmaf(CB[k], h[k], acc);       // y += C Bbar g
+          }
+          pacc[j] = acc;
+        }
+      } else {
+        const float dd[4] = {d4[cur].x, d4[cur].y, d4[cur].z, d4[cur].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!FULL && 4 * q + j >= nsteps) break;
+          if (MODE == MODE_STATE) dsum += dd[j];
+          float acc = 0.f;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            const float bj = j == 0 ? b4[cur][k].x : j == 1 ? b4[cur][k].y : j == 2 ? b4[cur][k].z : b4[cur][k].w;
+            const float ab = __builtin_amdgcn_exp2f(dd[j] * A2[k]);   // Abar = exp(delta A)
+            float f = fmaf(ab, iA[k], -iA[k]);                        // (Abar - 1)/A
+            if (ZERO) f = fmaf(dd[j], zf[k], f);                       // A == 0: delta
+            h[k] = fmaf(ab, h[k], f * (bj * uu[j]));                   // h = Abar h + Bbar u
+            if (READOUT) {
+              const float cj = j == 0 ? c4[cur][k].x : j == 1 ? c4[cur][k].y : j == 2 ? c4[cur][k].z : c4[cur][k].w;
+              acc = fmaf(cj, h[k], acc);                               // C . h (updated state)
+            }
+          }
+          pacc[j] = acc;
+        }
+      }
+      if (READOUT) *reinterpret_cast<float4*>(prow + 4 * q) = make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int64_t ntiles = (nrows + kTile - 1) / kTile;
+  const int64_t nsuper = (nrows + kSuper - 1) / kSuper;
+  const int64_t last_steps = nrows - (ntiles - 1) * kTile;
+  using true_t = std::integral_constant<bool, true>;
+  using false_t = std::integral_constant<bool, false>;
+
+  // One 16-token sub-tile (global tile t = 4 T + sub): stage its B/C, refill the ring, run
+  // the steps, reduce the partial readouts and finalise this lane's token into sY.
+  auto process = [&](int64_t t, int sub, auto set_tag, auto zero_tag) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+    if (!TI) {
+      wave_lds_sync();
+#pragma unroll
+      for (int r = 0; r < NB; ++r) {
+        const int tl = tl0 + kRowsPerLoad * r;
+        sB[n0 * kRowPad + tl] = T::from_raw(xB[SET][r] & maskB);
+        if (READOUT) sC[n0 * kRowPad + tl] = T::from_raw(xC[SET][r] & maskB);
+      }
+      if (t + kPrefetch < ntiles) load_bc(t + kPrefetch, set_tag);
+    }
+    wave_lds_sync();
+    if (t == ntiles - 1 && last_steps < kTile) compute_tile(sub, zero_tag, false_t{}, last_steps);
+    else compute_tile(sub, zero_tag, true_t{}, kTile);
+    if (READOUT) {
+      wave_lds_sync();
+      const float* col = sP + c * LDS::kChan + s;
+      float yv = col[0];
+#pragma unroll
+      for (int r = 1; r < S; ++r) yv += col[r * kRowPad];
+      const int tok = kTile * sub + s;                                  // token within the super-tile
+      yv = fmaf(dskip, sU[c * kRowV + tok], yv);                        // + D u
+      if (gate) {
+        const float zz = sZ[tok * CW + c];
+        const float sig = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+        yv *= zz * sig;                                                 // * SiLU(z)
+      }
+      sY[tok * CW + c] = yv;
+    }
+  };
+
+  auto run = [&](auto zero_tag) __attribute__((always_inline)) {
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1 % kPrefetch>;
+    if (0 < ntiles) load_bc(0, I0{});
+    if (kPrefetch > 1 && 1 < ntiles) load_bc(1, I1{});
+    if (nsuper > 0) load_super(0);
+    for (int64_t T0 = 0; T0 < nsuper; ++T0) {
+      // stage super-tile T0: u, delta channel-major; z token-major
+      wave_lds_sync();
+      {
+        const float4 fu = V::widen(vU);
+        const int tok = 16 * vr + vs;
+        sU[0 * kRowV + tok] = fu.x; sU[1 * kRowV + tok] = fu.y; sU[2 * kRowV + tok] = fu.z; sU[3 * kRowV + tok] = fu.w;
+        if (!TI) {
+          const float4 fd = V::widen(vD);
+          sD[0 * kRowV + tok] = fd.x; sD[1 * kRowV + tok] = fd.y; sD[2 * kRowV + tok] = fd.z; sD[3 * kRowV + tok] = fd.w;
+        }
+        if (gate) *reinterpret_cast<float4*>(sZ + tok * CW) = V::widen(vZ);
+      }
+      if (T0 + 1 < nsuper) load_super(T0 + 1);              // next super-tile in flight
+      const int64_t t0 = 4 * T0;
+      // four sub-tiles; the B/C ring alternates sets (kPrefetch divides 4)
+      process(t0, 0, I0{}, zero_tag);
+      if (t0 + 1 < ntiles) process(t0 + 1, 1, I1{}, zero_tag);
+      if (t0 + 2 < ntiles) process(t0 + 2, 2, I0{}, zero_tag);
+      if (t0 + 3 < ntiles) process(t0 + 3, 3, I1{}, zero_tag);
+      if (READOUT) {                                          // write back the super-tile's y
+        wave_lds_sync();
+        const float4 yv = *reinterpret_cast<const float4*>(sY + (16 * vr + vs) * CW);
+        V::store(rY, voY, int(T0 * kSuper * p.y_sl * ES), yv);   // dropped past l_end
+      }
+    }
+  };
+  static_assert(kPrefetch == 1 || kPrefetch == 2, "the B/C ring alternates over two sets");
+  if (wave_zero) run(true_t{});
+  else run(false_t{});
+
+  // ---- outputs after the last token (see scan_kernel)
+  if (MODE == MODE_STATE) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t n = s + S * k;
+      if (n < N) p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk] = h[k];
+    }
+    const float sum = TI ? dt_ti * float(l_end - l_begin) : dsum;    // every lane of c summed all tokens
+    if (s == 0) p.ws_dsum[(b * D + d) * p.n_chunks + chunk] = sum;
+  } else if (p.last_state != nullptr && (MODE == MODE_SINGLE || chunk == p.n_chunks - 1)) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t n = s + S * k;
+      if (n < N) {
+        float hv = h[k];
+        if (TI) {
+          const float a = p.A[d * N + n];
+          const float bv = T::widen(Bti[d * p.B_sd + n]);
           const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
           hv = coeff * bv * hv;
         }
@@ -578,8 +890,27 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename IO, int K, bool TI, int MODE>
+hipError_t launch_scan_vec(const ScanParams& p, hipStream_t stream) {
+  constexpr size_t lds = size_t(wave_lds_vec<K, TI>::total) * sizeof(float) * kWavesPerBlock;
+  const int blocks = (p.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (lds > 65536) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&scan_kernel_vec<IO, K, TI, MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL((scan_kernel_vec<IO, K, TI, MODE>), dim3(blocks), dim3(kWavesPerBlock * 64), lds, stream, p);
+  return hipGetLastError();
+}
+
 template <typename IO, bool TI, int MODE>
 hipError_t dispatch_sk(int S, int K, const ScanParams& p, hipStream_t stream) {
+  if (p.vec_io && S == 16) {
+    if (K == 1) return launch_scan_vec<IO, 1, TI, MODE>(p, stream);
+    if (K == 2) return launch_scan_vec<IO, 2, TI, MODE>(p, stream);
+    if (K == 4) return launch_scan_vec<IO, 4, TI, MODE>(p, stream);
+  }
   if (S == 4 && K == 1) return launch_scan<IO, 4, 1, TI, MODE>(p, stream);
   if (S == 8 && K == 1) return launch_scan<IO, 8, 1, TI, MODE>(p, stream);
   if (S == 16 && K == 1) return launch_scan<IO, 16, 1, TI, MODE>(p, stream);

@@ -31,6 +31,8 @@ struct ScanParams {
   int32_t total_items;  // batch * n_chunks * groups (one wavefront each)
   float* ws_state;      // chunked: [batch][D][N][n_chunks] end states, then carries
   float* ws_dsum;       // chunked: [batch][D][n_chunks] sum of delta per chunk
+  int32_t vec_io;       // 1: u/delta/z/y rows move as 4-channel vectors (16 lanes per channel,
+                        //    D % 4 == 0, rows aligned to 4 elements)
 };
 
 struct PrefixParams {

@@ -46,9 +46,13 @@ int make_plan(const selscan_dims* dims, Plan* plan) {
     if (s < 0) return SELSCAN_ERR_DIMS;
   if (d.dstate > 64) return SELSCAN_ERR_UNSUPPORTED;
   if (d.io_dtype != SELSCAN_F32 && d.io_dtype != SELSCAN_BF16) return SELSCAN_ERR_UNSUPPORTED;
-  if (d.path != SELSCAN_PATH_AUTO && d.path != SELSCAN_PATH_SINGLE && d.path != SELSCAN_PATH_CHUNKED)
+  const int32_t path = d.path & ~int32_t(SELSCAN_PATH_FLAG_SCALAR_IO);
+  if (path != SELSCAN_PATH_AUTO && path != SELSCAN_PATH_SINGLE && path != SELSCAN_PATH_CHUNKED)
     return SELSCAN_ERR_UNSUPPORTED;
   if (d.chunk_len < 0 || d.chunk_len % 16 != 0) return SELSCAN_ERR_UNSUPPORTED;
+  // y rows must not overlap (every (b, l, d) is written exactly once)
+  if ((d.seqlen > 1 && d.y_sl < d.dim) || (d.batch > 1 && d.y_sb < d.seqlen * d.y_sl && d.seqlen > 0))
+    return SELSCAN_ERR_UNSUPPORTED;
   // the kernels address a 16-token tile with 32-bit byte offsets from a per-tile base
   const int64_t kMaxRowStride = int64_t(1) << 26;
   if (d.u_sl > kMaxRowStride || d.delta_sl > kMaxRowStride || d.z_sl > kMaxRowStride || d.y_sl > kMaxRowStride ||
@@ -72,14 +76,31 @@ int make_plan(const selscan_dims* dims, Plan* plan) {
   const int64_t waves_single = d.batch * p.groups;
   if (waves_single > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
 
-  // chunking: only when the single pass leaves the GPU under-filled and the sequence is long
+  // Each work item addresses its tokens through 32-bit buffer offsets; inactive lanes use
+  // offset 2^31, so a work item may span at most 2^30 bytes of any tensor (no wrap-around).
+  const int64_t es = d.io_dtype == SELSCAN_BF16 ? 2 : 4;
+  int64_t max_sl = d.u_sl;
+  for (int64_t v : {d.delta_sl, d.z_sl, d.y_sl, d.B_sl, d.C_sl}) max_sl = v > max_sl ? v : max_sl;
+  const int64_t max_cols = d.dim > d.dstate ? d.dim : d.dstate;
+  const int64_t kSpan = int64_t(1) << 30;
+  auto span_ok = [&](int64_t rows) { return (rows * max_sl + max_cols + 16 * max_sl) * es <= kSpan; };
+  int64_t max_rows = max_sl > 0 ? (kSpan / es - max_cols) / max_sl - 16 : d.seqlen;
+  max_rows = max_rows / 16 * 16;
+  if (max_cols * es > kSpan / 2 || max_rows < 16) return SELSCAN_ERR_UNSUPPORTED;
+
+  // chunking: when the single pass leaves the GPU under-filled and the sequence is long,
+  // or when one pass over the whole sequence would exceed the addressing span
   bool chunk = false;
   int64_t nc = 1;
-  if (d.path == SELSCAN_PATH_CHUNKED) {
+  if (path != SELSCAN_PATH_CHUNKED && !span_ok(d.seqlen)) {
+    if (path == SELSCAN_PATH_SINGLE) return SELSCAN_ERR_UNSUPPORTED;
+    chunk = true;
+    nc = (d.seqlen + max_rows - 1) / max_rows;
+  } else if (path == SELSCAN_PATH_CHUNKED) {
     chunk = d.seqlen > 0;
     if (d.chunk_len > 0) nc = (d.seqlen + d.chunk_len - 1) / d.chunk_len;
     else nc = (d.seqlen + 63) / 64 < kMaxChunks ? (d.seqlen + 63) / 64 : kMaxChunks;
-  } else if (d.path == SELSCAN_PATH_AUTO && d.seqlen >= 256 && waves_single > 0 && waves_single < kTargetWaves / 2) {
+  } else if (path == SELSCAN_PATH_AUTO && d.seqlen >= 256 && waves_single > 0 && waves_single < kTargetWaves / 2) {
     nc = (kTargetWaves + waves_single - 1) / waves_single;
     const int64_t by_len = d.seqlen / 128;               // chunks of at least 128 tokens
     if (nc > by_len) nc = by_len;
@@ -90,6 +111,7 @@ int make_plan(const selscan_dims* dims, Plan* plan) {
     if (nc < 1) nc = 1;
     if (nc > kMaxChunks) return SELSCAN_ERR_UNSUPPORTED;   // forced chunk_len too small
     p.chunk_len = d.chunk_len > 0 ? d.chunk_len : round_up((d.seqlen + nc - 1) / nc, 16);
+    if (!span_ok(p.chunk_len)) return SELSCAN_ERR_UNSUPPORTED;
     p.n_chunks = int32_t((d.seqlen + p.chunk_len - 1) / p.chunk_len);
     p.chunked = true;
     p.ws_state_bytes = size_t(round_up(int64_t(sizeof(float)) * d.batch * d.dim * d.dstate * p.n_chunks, 256));
@@ -141,6 +163,18 @@ int run(const void* u, const void* delta, const float* A, const void* B, const v
   p.n_chunks = plan.n_chunks;
   p.groups = int32_t(plan.groups);
   p.total_items = int32_t(d.batch * plan.n_chunks * plan.groups);
+  // vector I/O: a wavefront owns 4 whole channels, and every u/delta/z/y row of those 4
+  // channels starts on a 4-element boundary (base address and row/batch strides)
+  {
+    const uintptr_t vbytes = uintptr_t(4) * (plan.bf16 ? 2 : 4);
+    auto row_ok = [&](const void* ptr, int64_t sb, int64_t sl) {
+      return ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) % vbytes == 0 && sb % 4 == 0 && sl % 4 == 0);
+    };
+    const bool delta_vec = plan.ti || row_ok(delta, d.delta_sb, d.delta_sl);
+    p.vec_io = (plan.S == 16 && d.dim % 4 == 0 && row_ok(u, d.u_sb, d.u_sl) && delta_vec &&
+                row_ok(z, d.z_sb, d.z_sl) && row_ok(y, d.y_sb, d.y_sl)) ? 1 : 0;
+    if (d.path & SELSCAN_PATH_FLAG_SCALAR_IO) p.vec_io = 0;
+  }
   hipError_t e;
   if (!plan.chunked) {
     e = selscan::launch_scan_pass(selscan::kPassSingle, plan.bf16, plan.ti, plan.S, plan.K, p, stream);

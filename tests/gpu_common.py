@@ -27,7 +27,7 @@ def dev(x, io):
     return t.to(torch().bfloat16) if io == "bf16" else t
 
 
-def run_gpu(inp, *, path="auto", chunk_len=0, want_last=True, stream=None, workspace=False):
+def run_gpu(inp, *, path="auto", chunk_len=0, want_last=True, stream=None, workspace=False, scalar_io=False):
     import selective_state_space_s6_amd as ss
     tc = torch()
     io = inp.io
@@ -40,10 +40,11 @@ def run_gpu(inp, *, path="auto", chunk_len=0, want_last=True, stream=None, works
     Ds = None if inp.Dskip is None else tc.from_numpy(inp.Dskip).cuda()
     ws = None
     if workspace:
-        need = ss.workspace_size(ss.make_dims(u, delta, A, B, C, z, u, path=path, chunk_len=chunk_len))
+        need = ss.workspace_size(ss.make_dims(u, delta, A, B, C, z, u, path=path, chunk_len=chunk_len,
+                                              scalar_io=scalar_io))
         ws = tc.empty(max(need, 1), dtype=tc.uint8, device="cuda")
     y, last = ss.selective_scan_fwd(u, delta, A, B, C, Ds, z, return_last_state=want_last, path=path,
-                                    chunk_len=chunk_len, stream=stream, workspace=ws)
+                                    chunk_len=chunk_len, stream=stream, workspace=ws, scalar_io=scalar_io)
     tc.cuda.synchronize()
     y = y.float().cpu().numpy().astype(np.float64)
     last = None if last is None else last.cpu().numpy().astype(np.float64)

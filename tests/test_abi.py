@@ -104,6 +104,8 @@ def test_null_pointers():
     ("path", 9, ss.SELSCAN_ERR_UNSUPPORTED),
     ("chunk_len", 24, ss.SELSCAN_ERR_UNSUPPORTED),
     ("B_sd", 16, ss.SELSCAN_ERR_UNSUPPORTED),      # B varying with both token and channel
+    ("y_sl", 0, ss.SELSCAN_ERR_UNSUPPORTED),       # overlapping output rows
+    ("y_sb", 8, ss.SELSCAN_ERR_UNSUPPORTED),
 ])
 def test_dims_errors(field, value, status):
     assert call(good_dims(**{field: value})) == status

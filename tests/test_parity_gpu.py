@@ -13,9 +13,9 @@ pytestmark = pytest.mark.gpu
 REDUCED = {
     "tiny_f32": dict(),
     "small_f32": dict(),
-    "mamba130m_f32": dict(batch=2, L=530, D=100),
-    "longctx_bf16": dict(batch=2, L=1000, D=130),
-    "s4d_ti_f32": dict(batch=2, L=700, D=70),
+    "mamba130m_f32": dict(batch=2, L=530, D=100),    # D % 4 == 0: vector I/O
+    "longctx_bf16": dict(batch=2, L=1000, D=132),    # vector I/O, ragged last super-tile
+    "s4d_ti_f32": dict(batch=2, L=700, D=70),        # D % 4 != 0: per-element I/O
 }
 
 
@@ -28,14 +28,15 @@ def check(inp, y, last, y_ref, l_ref, case):
     assert e_l <= TOL_STATE, "%s: last_state error %.3e" % (case, e_l)
 
 
+@pytest.mark.parametrize("scalar_io", [False, True])
 @pytest.mark.parametrize("path", ["auto", "single", "chunked"])
 @pytest.mark.parametrize("variant", s6_workloads.VARIANTS)
 @pytest.mark.parametrize("name", sorted(REDUCED))
-def test_reduced_workloads(name, variant, path):
+def test_reduced_workloads(name, variant, path, scalar_io):
     inp = s6_workloads.generate(name, variant, **REDUCED[name])
     y_ref, l_ref = run_oracle(inp)
-    y, last = run_gpu(inp, path=path)
-    check(inp, y, last, y_ref, l_ref, "%s/%s/%s" % (name, variant, path))
+    y, last = run_gpu(inp, path=path, scalar_io=scalar_io)
+    check(inp, y, last, y_ref, l_ref, "%s/%s/%s/%s" % (name, variant, path, "scalar_io" if scalar_io else "auto_io"))
 
 
 @pytest.mark.parametrize("chunk_len", [16, 48, 64, 112])
@@ -62,14 +63,15 @@ def test_full_size_sampled_channels(name):
     assert np.array_equal(y, y2)
 
 
+@pytest.mark.parametrize("D", [7, 12])
 @pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64])
-@pytest.mark.parametrize("L", [1, 15, 16, 17, 50])
-def test_state_counts_and_short_sequences(N, L):
-    inp = s6_workloads.generate("small_f32", "active", batch=2, L=L, D=7, N=N)
+@pytest.mark.parametrize("L", [1, 15, 16, 17, 50, 64, 65, 130])
+def test_state_counts_and_short_sequences(N, L, D):
+    inp = s6_workloads.generate("small_f32", "active", batch=2, L=L, D=D, N=N)
     y_ref, l_ref = run_oracle(inp)
     for path in ("single", "chunked"):
         y, last = run_gpu(inp, path=path)
-        check(inp, y, last, y_ref, l_ref, "N=%d L=%d %s" % (N, L, path))
+        check(inp, y, last, y_ref, l_ref, "N=%d L=%d D=%d %s" % (N, L, D, path))
 
 
 @pytest.mark.parametrize("ti", [False, True])
