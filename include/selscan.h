@@ -89,8 +89,9 @@ enum selscan_path {
   SELSCAN_PATH_SINGLE = 1,   /* one pass along the sequence per (batch, channel group) */
   SELSCAN_PATH_CHUNKED = 2,  /* two passes over chunks of the sequence, joined by a scan
                                 of per-chunk affine maps */
-  /* Bit that may be or-ed into any path (tests only): use the per-element I/O kernels even
-   * where the 4-channel vector I/O kernels apply.  Results agree within fp32 rounding. */
+  /* Bit that may be or-ed into any path (tests only): use the general per-element kernel
+   * even where the software-pipelined kernel applies.  Results agree within fp32
+   * rounding. */
   SELSCAN_PATH_FLAG_SCALAR_IO = 0x100
 };
 

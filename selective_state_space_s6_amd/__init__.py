@@ -31,7 +31,7 @@ SELSCAN_OK = 0
 SELSCAN_ERR_NULL, SELSCAN_ERR_DIMS, SELSCAN_ERR_UNSUPPORTED = -1, -2, -3
 SELSCAN_ERR_ALIGN, SELSCAN_ERR_HIP, SELSCAN_ERR_WORKSPACE, SELSCAN_ERR_ABI = -4, -5, -6, -7
 PATHS = {"auto": 0, "single": 1, "chunked": 2}
-FLAG_SCALAR_IO = 0x100   # tests only: force the per-element I/O kernels
+FLAG_SCALAR_IO = 0x100   # tests only: force the general per-element kernel
 
 
 class SelscanDims(ctypes.Structure):

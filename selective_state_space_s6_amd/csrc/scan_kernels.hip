@@ -463,108 +463,110 @@ void scan_kernel(ScanParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// The same scan with vector I/O for the per-token tensors, used when 16 lanes share a
-// channel (so a wavefront owns 4 channels), D is a multiple of 4 and every row of u,
-// delta, z and y starts on a 4-element boundary.  The sequence is walked in super-tiles of
-// 64 tokens: lane (r, s) moves token 16 r + s of the wave's 4 channels as one 8-byte (bf16)
-// or 16-byte (fp32) access, so every lane is busy and each access covers a whole channel
-// group instead of one 2- or 4-byte element.  u and delta are staged channel-major for the
-// step loop; z is staged token-major for the epilogue; y is collected token-major in LDS
-// and written back once per super-tile.  B and C move per 16-token sub-tile exactly as in
-// scan_kernel.
+// The software-pipelined scan, used when 16 lanes share a channel (N > 8, so a wavefront
+// owns 4 channels) and B/C rows can be read four states at a time (N % 4 == 0 and 4-state
+// aligned rows; always for time-invariant coefficients).  One wavefront per workgroup.
+//
+// Step layout as in scan_kernel: lane (c, s) owns states s + 16 k of channel c.
+// I/O layout: lane (it, ic) = (lane / 4, lane % 4) moves token it, channel ic of a 16-token
+// tile -- u, delta and z loads and the y store, one element each, four neighbouring lanes
+// on four neighbouring channels -- and the same lane finalises that (token, channel), so
+// the feed-through and the gate use the u and z it loaded itself.  B and C: each lane loads
+// four consecutive states of one token with a single 8- or 16-byte access and writes them
+// transposed ([n][token]) to LDS.
+//
+// Iteration t of the tile loop (one wave-level LDS sync at its top) runs three independent
+// streams:
+//   finalise tile t-1   read its partial readouts, sum, feed-through, gate, store y
+//   stage tile t+1      LDS writes of the operands loaded two iterations earlier, then the
+//                       loads of tile t+3
+//   steps of tile t     read the staged operands of tile t, write its partial readouts
+// Staged operands are double-buffered by tile parity.  The partial-readout buffer is single:
+// the finalise reads are issued before the steps write it (a wavefront's LDS accesses run
+// in issue order, and a compiler fence keeps that order).  Otherwise the streams touch
+// disjoint LDS within an iteration, so the compiler may interleave them and the latency of
+// one stream's memory traffic hides behind another's arithmetic.  Full tiles run in the
+// loop; a ragged last tile runs after it with a step count (its padded tokens must not
+// touch the state).
 
-template <int K, bool TI>
-struct wave_lds_vec {
-  static constexpr int S = 16, CW = 4, NP = S * K;
-  static constexpr int kSuper = 64;                   // tokens per super-tile
-  static constexpr int kRowV = kSuper + 4;            // channel-major row of u / delta
-  static constexpr int kB = TI ? 0 : NP * kRowPad;    // sB[NP][20] (one 16-token sub-tile)
-  static constexpr int kC = kB;
-  static constexpr int kU = CW * kRowV;               // sU[4][68]
-  static constexpr int kD = TI ? 0 : CW * kRowV;      // sD[4][68]
-  static constexpr int kZ = kSuper * CW;              // sZ[64][4] token-major
-  static constexpr int kY = kSuper * CW;              // sY[64][4] token-major
-  static constexpr int kChan = 21 * S;
-  static constexpr int kP = CW * kChan;               // partial readouts, as in wave_lds
-  static constexpr int total = kB + kC + kU + kD + kZ + kY + kP;
+constexpr int kRowUD = 24;     // LDS row (floats) of a channel's 16 u / delta values
+constexpr int kChanP = 264;    // LDS block of one channel's 16 x 16 partial readouts (+8)
+
+template <int K, bool TI, int MODE>
+struct pipe_lds {
+  static constexpr bool READOUT = MODE != MODE_STATE;
+  static constexpr int NP = 16 * K;
+  static constexpr int kB = TI ? 0 : NP * kRowPad;            // sB[NP][20]
+  static constexpr int kC = (TI || !READOUT) ? 0 : kB;         // sC[NP][20]
+  static constexpr int kU = 4 * kRowUD;                        // sU[4][24]
+  static constexpr int kD = TI ? 0 : 4 * kRowUD;               // sD[4][24]
+  static constexpr int kBuf = kB + kC + kU + kD;               // one tile parity
+  static constexpr int kP = READOUT ? 4 * kChanP : 0;          // sP[4][16 x 16, swizzled]
+  static constexpr int total = 2 * kBuf + kP;
 };
 
-template <typename IO> struct vec_io;
-template <> struct vec_io<float> {       // 4 channels = 16 bytes
+// B/C: four consecutive states of one token as raw bits (bf16: 8 bytes, fp32: 16 bytes).
+template <typename IO> struct quad_io;
+template <> struct quad_io<float> {
   using raw_t = uint32_t __attribute__((ext_vector_type(4)));
   static __device__ __forceinline__ raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
     return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
   }
-  static __device__ __forceinline__ float4 widen(raw_t v) {
-    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-  }
-  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, float4 y) {
-    raw_t v = {__float_as_uint(y.x), __float_as_uint(y.y), __float_as_uint(y.z), __float_as_uint(y.w)};
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
-                                           r, voff, soff, 0);
-  }
+  static __device__ __forceinline__ float get(raw_t v, int j) { return __uint_as_float(v[j]); }
 };
-template <> struct vec_io<uint16_t> {    // 4 channels = 8 bytes of bfloat16
+template <> struct quad_io<uint16_t> {
   using raw_t = uint32_t __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
     return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
   }
-  static __device__ __forceinline__ float4 widen(raw_t v) {
-    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-  }
-  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, float4 y) {
-    // round to nearest even (v_cvt_pk_bf16_f32)
-    const f32x2_t lo = {y.x, y.y}, hi = {y.z, y.w};
-    raw_t v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
-               __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t))};
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v),
-                                          r, voff, soff, 0);
+  static __device__ __forceinline__ float get(raw_t v, int j) {
+    const uint32_t w = v[j >> 1];
+    return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
   }
 };
 
+// Position of (state lane r, token j) in a channel's partial-readout block: rows of 16
+// tokens, the four 4-token groups of row r XOR-rotated by (r >> 1) & 3 so that the
+// 128-bit row writes of eight neighbouring lanes, and the column reads of the finalise
+// (a channel block starts 8 banks after the previous one), hit distinct banks.
+__device__ __forceinline__ int part_pos(int r, int j) { return r * 16 + 4 * ((j >> 2) ^ ((r >> 1) & 3)) + (j & 3); }
+
 template <typename IO, int K, bool TI, int MODE>
-__global__ __launch_bounds__(kWavesPerBlock * 64)
-__attribute__((amdgpu_waves_per_eu(occupancy<K>::kMinWaves, 8)))
-void scan_kernel_vec(ScanParams p) {
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(occupancy<K>::kMinWaves)))
+void scan_kernel_pipe(ScanParams p) {
   using T = io_traits<IO>;
-  using V = vec_io<IO>;
-  using LDS = wave_lds_vec<K, TI>;
-  constexpr int S = 16, CW = 4, NP = LDS::NP;
-  constexpr int NB = (NP * kTile) / 64;
-  constexpr bool READOUT = (MODE != MODE_STATE);
+  using Qd = quad_io<IO>;
+  using LDS = pipe_lds<K, TI, MODE>;
+  constexpr int S = 16, NP = LDS::NP;
+  constexpr int QG = NP / 4;                 // 4-state groups per token row
+  constexpr int TPL = 64 / QG;               // tokens covered by one B/C load instruction
+  constexpr int NL = kTile / TPL;            // B/C loads per lane per tile
+  constexpr bool READOUT = LDS::READOUT;
   constexpr int ES = T::kBytes;
-  constexpr int kPrefetch = K <= 2 ? kPrefetchMax : 1;   // B/C sub-tiles in flight
-  constexpr int kSuper = LDS::kSuper, kRowV = LDS::kRowV;
+  constexpr uint32_t kOOB = 0x80000000u;
+  constexpr int kRsrcWord3 = 0x00020000;
 
   extern __shared__ __align__(16) float smem[];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int c = lane / S, s = lane % S;     // step layout: channel c, state slot s
-  const int vr = lane / 16, vs = lane % 16; // I/O layout: token 16 vr + vs of a super-tile
+  const int lane = threadIdx.x;
+  const int c = lane / S, s = lane % S;      // step layout
+  const int it = lane >> 2, ic = lane & 3;   // I/O layout
 
-  const int item = xcd_contiguous_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  const int item = xcd_contiguous_block(blockIdx.x, gridDim.x);
   if (item >= p.total_items) return;
   const int g = item % p.groups;
   const int bc = item / p.groups;
   const int chunk = bc % p.n_chunks;
   const int64_t b = bc / p.n_chunks;
 
-  float* const sB = smem + wave * LDS::total;
-  float* const sC = sB + LDS::kB;
-  float* const sU = sC + LDS::kC;
-  float* const sD = sU + LDS::kU;
-  float* const sZ = sD + LDS::kD;
-  float* const sY = sZ + LDS::kZ;
-  float* const sP = sY + LDS::kY;
-
   const int64_t D = p.D, N = p.N;
-  const int64_t d0 = int64_t(g) * CW;
-  const int64_t d = d0 + c;                 // always < D here (D is a multiple of 4)
+  const int64_t d0 = int64_t(g) * 4;
+  const int64_t d = d0 + c;                  // channel of the step layout
+  const int64_t dio = d0 + ic;               // channel of the I/O layout
+  const bool dvalid = d < D, iovalid = dio < D;
   const int64_t l_begin = int64_t(chunk) * p.chunk_len;
   const int64_t l_end = (l_begin + p.chunk_len < p.L) ? l_begin + p.chunk_len : p.L;
+  const int64_t nrows = l_end - l_begin;
 
   // ---- per-lane constants of the K owned states (see scan_kernel)
   float A2[K], iA[K], zf[K], h[K], Ab[K], CB[K];
@@ -572,11 +574,11 @@ void scan_kernel_vec(ScanParams p) {
   float dt_ti = 0.f;
   const IO* const Bti = static_cast<const IO*>(p.B);
   const IO* const Cti = static_cast<const IO*>(p.C);
-  if (TI) dt_ti = T::widen(static_cast<const IO*>(p.delta)[d]);
+  if (TI) dt_ti = dvalid ? T::widen(static_cast<const IO*>(p.delta)[d]) : 0.f;
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t n = s + S * k;
-    const bool ok = n < N;
+    const bool ok = dvalid && n < N;
     const float a = ok ? p.A[d * N + n] : 0.f;
     A2[k] = a * kLog2e;
     iA[k] = (a != 0.f) ? 1.0f / a : 0.f;
@@ -598,13 +600,12 @@ void scan_kernel_vec(ScanParams p) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int64_t n = s + S * k;
-      if (n < N) h[k] = p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk];
+      if (dvalid && n < N) h[k] = p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk];
     }
   }
 
-  // ---- buffer resources (see scan_kernel): base at this work item's first token
-  constexpr int kRsrcWord3 = 0x00020000;
-  const int64_t nrows = l_end - l_begin;
+  // ---- buffer resources (see scan_kernel): reads past the work item's last element return
+  // 0, writes there are dropped; lanes of channels >= D use an offset beyond every size.
   auto rsrc = [&](const void* base, int64_t sb, int64_t sl, int64_t col0, int64_t ncols) __attribute__((always_inline)) {
     const char* p0 = static_cast<const char*>(base) + (b * sb + l_begin * sl + col0) * ES;
     const int64_t bytes = nrows > 0 ? ((nrows - 1) * sl + ncols) * ES : 0;
@@ -613,194 +614,257 @@ void scan_kernel_vec(ScanParams p) {
   const int64_t z_sb = p.z != nullptr ? p.z_sb : p.u_sb, z_sl = p.z != nullptr ? p.z_sl : p.u_sl;
   const auto rU = rsrc(p.u, p.u_sb, p.u_sl, d0, D - d0);
   const auto rD = rsrc(p.delta, p.delta_sb, p.delta_sl, d0, D - d0);
-  const auto rZ = rsrc(p.z != nullptr ? p.z : p.u, z_sb, z_sl, d0, D - d0);
+  const auto rZ = rsrc(p.z != nullptr ? p.z : p.u, z_sb, z_sl, d0, D - d0);   // no gate: re-reads u
   const auto rY = rsrc(p.y, p.y_sb, p.y_sl, d0, D - d0);
   const auto rBd = rsrc(p.B, p.B_sb, p.B_sl, 0, N);
   const auto rCd = rsrc(p.C, p.C_sb, p.C_sl, 0, N);
-  // I/O lane offsets: token 16 vr + vs of a super-tile, channels d0 .. d0 + 3
-  const uint32_t voU = uint32_t((16 * vr + vs) * p.u_sl * ES);
-  const uint32_t voD = uint32_t((16 * vr + vs) * p.delta_sl * ES);
-  const uint32_t voZ = uint32_t((16 * vr + vs) * z_sl * ES);
-  const uint32_t voY = uint32_t((16 * vr + vs) * p.y_sl * ES);
-  // B/C sub-tile element r of this lane: token tl0 + r * (64 / NP), state n0
-  static_assert(64 % NP == 0, "padded state count must divide the wavefront");
-  constexpr int kRowsPerLoad = 64 / NP;
-  const int tl0 = lane / NP, n0 = lane % NP;
-  const uint32_t maskB = n0 < N ? 0xffffffffu : 0u;
-  const uint32_t offB0 = uint32_t((tl0 * p.B_sl + (n0 < N ? n0 : 0)) * ES);
-  const uint32_t offC0 = uint32_t((tl0 * p.C_sl + (n0 < N ? n0 : 0)) * ES);
+  const uint32_t voU = iovalid ? uint32_t((it * p.u_sl + ic) * ES) : kOOB;
+  const uint32_t voD = iovalid ? uint32_t((it * p.delta_sl + ic) * ES) : kOOB;
+  const uint32_t voZ = iovalid ? uint32_t((it * z_sl + ic) * ES) : kOOB;
+  const uint32_t voY = iovalid ? uint32_t((it * p.y_sl + ic) * ES) : kOOB;
+  // B/C: lane -> 4-state group qg, token tq (+ TPL per load); groups past N read as zero
+  const int qg = lane / TPL, tq = lane % TPL;
+  const bool qvalid = 4 * qg < N;
+  const uint32_t voB = qvalid ? uint32_t((tq * p.B_sl + 4 * qg) * ES) : kOOB;
+  const uint32_t voC = qvalid ? uint32_t((tq * p.C_sl + 4 * qg) * ES) : kOOB;
 
   const bool gate = (p.z != nullptr) && READOUT;
-  const bool has_d = (p.Dskip != nullptr) && READOUT;
-  const float dskip = has_d ? p.Dskip[d] : 0.f;
+  const float dskip = (READOUT && p.Dskip != nullptr && iovalid) ? p.Dskip[dio] : 0.f;
 
-  auto load_raw = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int64_t soff) __attribute__((always_inline)) -> uint32_t {
+  auto load_elem = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int64_t soff) __attribute__((always_inline)) -> uint32_t {
     if (ES == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, int(soff), 0);
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, int(soff), 0);
   };
+  auto store_y = [&](float v, int64_t soff) __attribute__((always_inline)) {
+    if (ES == 2) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      const f32x2_t vv = {v, v};
+      const uint32_t rr = __builtin_bit_cast(uint32_t, __builtin_convertvector(vv, bf16x2_t));   // RNE
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(rr & 0xffffu), rY, voY, int(soff), 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rY, voY, int(soff), 0);
+    }
+  };
 
-  // ---- B/C sub-tile ring (as in scan_kernel) and the super-tile u/delta/z registers
-  uint32_t xB[kPrefetch][TI ? 1 : NB], xC[kPrefetch][TI ? 1 : NB];
-  auto load_bc = [&](int64_t t, auto set_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
+  // ---- load sets: two tiles in flight, by tile parity
+  typename Qd::raw_t xB[2][TI ? 1 : NL], xC[2][TI ? 1 : NL];
+  uint32_t xU[2], xD[2], xZ[2];
+  const int64_t ntiles = (nrows + kTile - 1) / kTile;
+  const int64_t nfull = nrows / kTile;
+  const int last_steps = int(nrows - nfull * kTile);       // tokens of a ragged last tile
+  auto issue = [&](int64_t t, auto par_tag) __attribute__((always_inline)) {
+    constexpr int P = decltype(par_tag)::value;
+    const int64_t tt = t < ntiles ? t : ntiles - 1;           // past the end: reload the last tile
+    const int64_t row0 = tt * kTile;
+    xU[P] = load_elem(rU, voU, row0 * p.u_sl * ES);
+    if (!TI) xD[P] = load_elem(rD, voD, row0 * p.delta_sl * ES);
+    if (READOUT) xZ[P] = load_elem(rZ, voZ, row0 * z_sl * ES);
     if (!TI) {
 #pragma unroll
-      for (int r = 0; r < NB; ++r) {
-        const int64_t row = t * kTile + int64_t(kRowsPerLoad) * r;
-        xB[SET][r] = load_raw(rBd, offB0, row * p.B_sl * ES);
-        if (READOUT) xC[SET][r] = load_raw(rCd, offC0, row * p.C_sl * ES);
+      for (int r = 0; r < NL; ++r) {
+        const int64_t row = row0 + int64_t(TPL) * r;
+        xB[P][r] = Qd::load(rBd, voB, int(row * p.B_sl * ES));
+        if (READOUT) xC[P][r] = Qd::load(rCd, voC, int(row * p.C_sl * ES));
       }
     }
   };
-  typename V::raw_t vU, vD, vZ;
-  auto load_super = [&](int64_t T0) __attribute__((always_inline)) {
-    const int64_t row0 = T0 * kSuper;
-    vU = V::load(rU, voU, int(row0 * p.u_sl * ES));
-    if (!TI) vD = V::load(rD, voD, int(row0 * p.delta_sl * ES));
-    if (READOUT) vZ = V::load(rZ, voZ, int(row0 * z_sl * ES));
+
+  // LDS regions of tile parity P
+  float* const sBase = smem;
+  float* const sP = smem + 2 * LDS::kBuf;
+  auto bufB = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf; };
+  auto bufC = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf + LDS::kB; };
+  auto bufU = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf + LDS::kB + LDS::kC; };
+  auto bufD = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf + LDS::kB + LDS::kC + LDS::kU; };
+
+  // u and z of a tile, widened, carried from staging to the finalise
+  float uSt = 0.f, zSt = 0.f, uCur = 0.f, zCur = 0.f, uFin = 0.f, zFin = 0.f;
+
+  // Stage the load set of parity P into LDS buffer P.
+  auto stage = [&](auto par_tag) __attribute__((always_inline)) {
+    constexpr int P = decltype(par_tag)::value;
+    const float uv = T::from_raw(xU[P]);
+    bufU(P)[ic * kRowUD + it] = uv;
+    uSt = uv;
+    if (READOUT) zSt = T::from_raw(xZ[P]);
+    if (!TI) {
+      bufD(P)[ic * kRowUD + it] = T::from_raw(xD[P]);
+#pragma unroll
+      for (int r = 0; r < NL; ++r) {
+        const int tok = tq + TPL * r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bufB(P)[(4 * qg + j) * kRowPad + tok] = Qd::get(xB[P][r], j);
+          if (READOUT) bufC(P)[(4 * qg + j) * kRowPad + tok] = Qd::get(xC[P][r], j);
+        }
+      }
+    }
   };
 
-  float* const prow = sP + c * LDS::kChan + s * kRowPad;
   float dsum = 0.f;
+  float* const prow = sP + c * kChanP;
 
-  // 16 steps of sub-tile `sub` of the staged super-tile (channel-major rows of sU/sD).
-  auto compute_tile = [&](int sub, auto zero_tag, auto full_tag, int64_t nsteps) __attribute__((always_inline)) {
+  // Steps of a staged tile, in four groups of four tokens: rd(P, q) reads group q's operands
+  // from LDS buffer P into register slot q & 1, cmp(q) runs its steps (FULL: all four
+  // tokens; otherwise only tokens below `nsteps`) and writes its four partial readouts.
+  float4 rU4[2], rD4[2], rB4[2][K], rC4[2][K];
+  auto rd = [&](int P, int q) __attribute__((always_inline)) {
+    const int sl = q & 1;
+    rU4[sl] = *reinterpret_cast<const float4*>(bufU(P) + c * kRowUD + 4 * q);
+    if (!TI) {
+      rD4[sl] = *reinterpret_cast<const float4*>(bufD(P) + c * kRowUD + 4 * q);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        rB4[sl][k] = *reinterpret_cast<const float4*>(bufB(P) + (s + S * k) * kRowPad + 4 * q);
+        if (READOUT) rC4[sl][k] = *reinterpret_cast<const float4*>(bufC(P) + (s + S * k) * kRowPad + 4 * q);
+      }
+    }
+  };
+  auto cmp = [&](int q, auto zero_tag, auto full_tag, int nsteps) __attribute__((always_inline)) {
     constexpr bool ZERO = decltype(zero_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
-    const float* uRow = sU + c * kRowV + kTile * sub;
-    const float* dRow = sD + c * kRowV + kTile * sub;
-    float4 u4[2], d4[2], b4[2][K], c4[2][K];
-    auto read_group = [&](int q, int buf) __attribute__((always_inline)) {
-      u4[buf] = *reinterpret_cast<const float4*>(uRow + 4 * q);
-      if (!TI) {
-        d4[buf] = *reinterpret_cast<const float4*>(dRow + 4 * q);
+    const int sl = q & 1;
+    const float uu[4] = {rU4[sl].x, rU4[sl].y, rU4[sl].z, rU4[sl].w};
+    const float dd[4] = {rD4[sl].x, rD4[sl].y, rD4[sl].z, rD4[sl].w};
+    float pacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          b4[buf][k] = *reinterpret_cast<const float4*>(sB + (s + S * k) * kRowPad + 4 * q);
-          if (READOUT) c4[buf][k] = *reinterpret_cast<const float4*>(sC + (s + S * k) * kRowPad + 4 * q);
-        }
-      }
-    };
-    read_group(0, 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cur = q & 1;
-      if (q + 1 < 4) read_group(q + 1, cur ^ 1);
-      const float uu[4] = {u4[cur].x, u4[cur].y, u4[cur].z, u4[cur].w};
-      float pacc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) {
+      if (!FULL && 4 * q + j >= nsteps) break;
+      float acc = 0.f;
       if (TI) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (!FULL && 4 * q + j >= nsteps) break;
-          float acc = 0.f;
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            h[k] = fmaf(Ab[k], h[k], uu[j]);                 // g = Abar g + u
-            if (READOUT) acc = fmaf(CB[k], h[k], acc);       // y += C Bbar g
-          }
-          pacc[j] = acc;
+        for (int k = 0; k < K; ++k) {
+          h[k] = fmaf(Ab[k], h[k], uu[j]);                        // g = Abar g + u
+          if (READOUT) acc = fmaf(CB[k], h[k], acc);              // y += C Bbar g
         }
       } else {
-        const float dd[4] = {d4[cur].x, d4[cur].y, d4[cur].z, d4[cur].w};
+        if (MODE == MODE_STATE) dsum += dd[j];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (!FULL && 4 * q + j >= nsteps) break;
-          if (MODE == MODE_STATE) dsum += dd[j];
-          float acc = 0.f;
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            const float bj = j == 0 ? b4[cur][k].x : j == 1 ? b4[cur][k].y : j == 2 ? b4[cur][k].z : b4[cur][k].w;
-            const float ab = __builtin_amdgcn_exp2f(dd[j] * A2[k]);   // Abar = exp(delta A)
-            float f = fmaf(ab, iA[k], -iA[k]);                        // (Abar - 1)/A
-            if (ZERO) f = fmaf(dd[j], zf[k], f);                       // A == 0: delta
-            h[k] = fmaf(ab, h[k], f * (bj * uu[j]));                   // h = Abar h + Bbar u
-            if (READOUT) {
-              const float cj = j == 0 ? c4[cur][k].x : j == 1 ? c4[cur][k].y : j == 2 ? c4[cur][k].z : c4[cur][k].w;
-              acc = fmaf(cj, h[k], acc);                               // C . h (updated state)
-            }
+        for (int k = 0; k < K; ++k) {
+          const float4 b4 = rB4[sl][k];
+          const float bj = j == 0 ? b4.x : j == 1 ? b4.y : j == 2 ? b4.z : b4.w;
+          const float ab = __builtin_amdgcn_exp2f(dd[j] * A2[k]);  // Abar = exp(delta A)
+          float f = fmaf(ab, iA[k], -iA[k]);                       // (Abar - 1)/A
+          if (ZERO) f = fmaf(dd[j], zf[k], f);                      // A == 0: delta
+          h[k] = fmaf(ab, h[k], f * (bj * uu[j]));                  // h = Abar h + Bbar u
+          if (READOUT) {
+            const float4 c4 = rC4[sl][k];
+            const float cj = j == 0 ? c4.x : j == 1 ? c4.y : j == 2 ? c4.z : c4.w;
+            acc = fmaf(cj, h[k], acc);                              // C . h (updated state)
           }
-          pacc[j] = acc;
         }
       }
-      if (READOUT) *reinterpret_cast<float4*>(prow + 4 * q) = make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
-      __builtin_amdgcn_sched_barrier(0);
+      pacc[j] = acc;
     }
+    if (READOUT)
+      *reinterpret_cast<float4*>(prow + s * 16 + 4 * (q ^ ((s >> 1) & 3))) =
+          make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
   };
 
-  const int64_t ntiles = (nrows + kTile - 1) / kTile;
-  const int64_t nsuper = (nrows + kSuper - 1) / kSuper;
-  const int64_t last_steps = nrows - (ntiles - 1) * kTile;
+  // Finalise: the 16 partial readouts of (token it, channel ic), then feed-through and gate.
+  float part[16];
+  auto fin_read = [&]() __attribute__((always_inline)) {
+    const float* const col = sP + ic * kChanP;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] = col[part_pos(r, it)];
+  };
+  auto fin_sum = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) {
+#pragma unroll
+      for (int r = 0; r < w; ++r) part[r] += part[r + w];
+    }
+  };
+  auto fin_out = [&](int64_t t, float uv, float zv) __attribute__((always_inline)) {
+    float yv = fmaf(dskip, uv, part[0]);                               // + D u
+    // * SiLU(z) = z / (1 + exp(-z)); computed unconditionally and selected, so that the
+    // iteration stays one basic block
+    const float silu = zv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zv * kLog2e));
+    yv *= gate ? silu : 1.f;
+    store_y(yv, t * kTile * p.y_sl * ES);                               // dropped past l_end
+  };
+  auto order_lds = [] () __attribute__((always_inline)) { __asm__ __volatile__("" ::: "memory"); };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   using true_t = std::integral_constant<bool, true>;
   using false_t = std::integral_constant<bool, false>;
 
-  // One 16-token sub-tile (global tile t = 4 T + sub): stage its B/C, refill the ring, run
-  // the steps, reduce the partial readouts and finalise this lane's token into sY.
-  auto process = [&](int64_t t, int sub, auto set_tag, auto zero_tag) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
-    if (!TI) {
-      wave_lds_sync();
-#pragma unroll
-      for (int r = 0; r < NB; ++r) {
-        const int tl = tl0 + kRowsPerLoad * r;
-        sB[n0 * kRowPad + tl] = T::from_raw(xB[SET][r] & maskB);
-        if (READOUT) sC[n0 * kRowPad + tl] = T::from_raw(xC[SET][r] & maskB);
-      }
-      if (t + kPrefetch < ntiles) load_bc(t + kPrefetch, set_tag);
-    }
+  auto region = [] () __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+
+  // One loop iteration for full tile t of parity P, in five scheduling regions; the
+  // operands of each step group are read one region ahead of their use.
+  auto iteration = [&](int64_t t, auto par_tag, auto zero_tag, auto fin_tag) __attribute__((always_inline)) {
+    constexpr int P = decltype(par_tag)::value;
+    constexpr bool FIN = decltype(fin_tag)::value && READOUT;
+    region();
     wave_lds_sync();
-    if (t == ntiles - 1 && last_steps < kTile) compute_tile(sub, zero_tag, false_t{}, last_steps);
-    else compute_tile(sub, zero_tag, true_t{}, kTile);
-    if (READOUT) {
-      wave_lds_sync();
-      const float* col = sP + c * LDS::kChan + s;
-      float yv = col[0];
+    if (FIN) fin_read();                               // tile t-1
+    order_lds();
+    rd(P, 0);
+    stage(std::integral_constant<int, 1 - P>{});       // tile t+1
+    issue(t + 3, std::integral_constant<int, 1 - P>{});
+    region();
+    rd(P, 1);
+    cmp(0, zero_tag, true_t{}, kTile);
+    if (FIN) fin_sum();
+    region();
+    rd(P, 2);
+    cmp(1, zero_tag, true_t{}, kTile);
+    if (FIN) fin_out(t - 1, uFin, zFin);
+    region();
+    rd(P, 3);
+    cmp(2, zero_tag, true_t{}, kTile);
+    region();
+    cmp(3, zero_tag, true_t{}, kTile);
+    uFin = uCur; zFin = zCur;
+    uCur = uSt; zCur = zSt;
+  };
+  // Steps of the ragged last tile (buffer P), one group after another.
+  auto ragged = [&](int P, auto zero_tag, int nsteps) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 1; r < S; ++r) yv += col[r * kRowPad];
-      const int tok = kTile * sub + s;                                  // token within the super-tile
-      yv = fmaf(dskip, sU[c * kRowV + tok], yv);                        // + D u
-      if (gate) {
-        const float zz = sZ[tok * CW + c];
-        const float sig = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
-        yv *= zz * sig;                                                 // * SiLU(z)
-      }
-      sY[tok * CW + c] = yv;
+    for (int q = 0; q < 4; ++q) {
+      rd(P, q);
+      cmp(q, zero_tag, false_t{}, nsteps);
     }
   };
 
   auto run = [&](auto zero_tag) __attribute__((always_inline)) {
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1 % kPrefetch>;
-    if (0 < ntiles) load_bc(0, I0{});
-    if (kPrefetch > 1 && 1 < ntiles) load_bc(1, I1{});
-    if (nsuper > 0) load_super(0);
-    for (int64_t T0 = 0; T0 < nsuper; ++T0) {
-      // stage super-tile T0: u, delta channel-major; z token-major
+    issue(0, I0{});
+    issue(1, I1{});
+    stage(I0{});                                        // tile 0 -> buffer 0
+    uCur = uSt; zCur = zSt;
+    issue(2, I0{});
+    int64_t t = 0;
+    if (nfull > 0) {
+      iteration(int64_t(0), I0{}, zero_tag, false_t{});
+      t = 1;
+    }
+    for (; t + 1 < nfull; t += 2) {
+      iteration(t, I1{}, zero_tag, true_t{});
+      iteration(t + 1, I0{}, zero_tag, true_t{});
+    }
+    if (t < nfull) {
+      iteration(t, I1{}, zero_tag, true_t{});
+      ++t;
+    }
+    // drain: finalise tile nfull-1, then the ragged tile (staged in buffer nfull % 2)
+    wave_lds_sync();
+    if (READOUT && nfull > 0) fin_read();
+    order_lds();
+    if (last_steps > 0) ragged(int(nfull & 1), zero_tag, last_steps);
+    if (READOUT && nfull > 0) {
+      fin_sum();
+      fin_out(nfull - 1, uFin, zFin);
+    }
+    if (READOUT && last_steps > 0) {
       wave_lds_sync();
-      {
-        const float4 fu = V::widen(vU);
-        const int tok = 16 * vr + vs;
-        sU[0 * kRowV + tok] = fu.x; sU[1 * kRowV + tok] = fu.y; sU[2 * kRowV + tok] = fu.z; sU[3 * kRowV + tok] = fu.w;
-        if (!TI) {
-          const float4 fd = V::widen(vD);
-          sD[0 * kRowV + tok] = fd.x; sD[1 * kRowV + tok] = fd.y; sD[2 * kRowV + tok] = fd.z; sD[3 * kRowV + tok] = fd.w;
-        }
-        if (gate) *reinterpret_cast<float4*>(sZ + tok * CW) = V::widen(vZ);
-      }
-      if (T0 + 1 < nsuper) load_super(T0 + 1);              // next super-tile in flight
-      const int64_t t0 = 4 * T0;
-      // four sub-tiles; the B/C ring alternates sets (kPrefetch divides 4)
-      process(t0, 0, I0{}, zero_tag);
-      if (t0 + 1 < ntiles) process(t0 + 1, 1, I1{}, zero_tag);
-      if (t0 + 2 < ntiles) process(t0 + 2, 2, I0{}, zero_tag);
-      if (t0 + 3 < ntiles) process(t0 + 3, 3, I1{}, zero_tag);
-      if (READOUT) {                                          // write back the super-tile's y
-        wave_lds_sync();
-        const float4 yv = *reinterpret_cast<const float4*>(sY + (16 * vr + vs) * CW);
-        V::store(rY, voY, int(T0 * kSuper * p.y_sl * ES), yv);   // dropped past l_end
-      }
+      fin_read();
+      fin_sum();
+      fin_out(nfull, uCur, zCur);
     }
   };
-  static_assert(kPrefetch == 1 || kPrefetch == 2, "the B/C ring alternates over two sets");
   if (wave_zero) run(true_t{});
   else run(false_t{});
 
@@ -809,15 +873,15 @@ void scan_kernel_vec(ScanParams p) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int64_t n = s + S * k;
-      if (n < N) p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk] = h[k];
+      if (dvalid && n < N) p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk] = h[k];
     }
-    const float sum = TI ? dt_ti * float(l_end - l_begin) : dsum;    // every lane of c summed all tokens
-    if (s == 0) p.ws_dsum[(b * D + d) * p.n_chunks + chunk] = sum;
+    const float sum = TI ? dt_ti * float(nrows) : dsum;     // every lane of c summed all tokens
+    if (dvalid && s == 0) p.ws_dsum[(b * D + d) * p.n_chunks + chunk] = sum;
   } else if (p.last_state != nullptr && (MODE == MODE_SINGLE || chunk == p.n_chunks - 1)) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int64_t n = s + S * k;
-      if (n < N) {
+      if (dvalid && n < N) {
         float hv = h[k];
         if (TI) {
           const float a = p.A[d * N + n];
@@ -891,25 +955,19 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
 }
 
 template <typename IO, int K, bool TI, int MODE>
-hipError_t launch_scan_vec(const ScanParams& p, hipStream_t stream) {
-  constexpr size_t lds = size_t(wave_lds_vec<K, TI>::total) * sizeof(float) * kWavesPerBlock;
-  const int blocks = (p.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (lds > 65536) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&scan_kernel_vec<IO, K, TI, MODE>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (attr != hipSuccess) return attr;
-  }
-  hipLaunchKernelGGL((scan_kernel_vec<IO, K, TI, MODE>), dim3(blocks), dim3(kWavesPerBlock * 64), lds, stream, p);
+hipError_t launch_scan_pipe(const ScanParams& p, hipStream_t stream) {
+  constexpr size_t lds = size_t(pipe_lds<K, TI, MODE>::total) * sizeof(float);
+  static_assert(lds <= 65536, "one wavefront's LDS stays within the default dynamic limit");
+  hipLaunchKernelGGL((scan_kernel_pipe<IO, K, TI, MODE>), dim3(unsigned(p.total_items)), dim3(64), lds, stream, p);
   return hipGetLastError();
 }
 
 template <typename IO, bool TI, int MODE>
 hipError_t dispatch_sk(int S, int K, const ScanParams& p, hipStream_t stream) {
-  if (p.vec_io && S == 16) {
-    if (K == 1) return launch_scan_vec<IO, 1, TI, MODE>(p, stream);
-    if (K == 2) return launch_scan_vec<IO, 2, TI, MODE>(p, stream);
-    if (K == 4) return launch_scan_vec<IO, 4, TI, MODE>(p, stream);
+  if (p.pipelined && S == 16) {
+    if (K == 1) return launch_scan_pipe<IO, 1, TI, MODE>(p, stream);
+    if (K == 2) return launch_scan_pipe<IO, 2, TI, MODE>(p, stream);
+    if (K == 4) return launch_scan_pipe<IO, 4, TI, MODE>(p, stream);
   }
   if (S == 4 && K == 1) return launch_scan<IO, 4, 1, TI, MODE>(p, stream);
   if (S == 8 && K == 1) return launch_scan<IO, 8, 1, TI, MODE>(p, stream);
@@ -961,14 +1019,6 @@ hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream) {
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, x, n);
   return hipGetLastError();
-}
-
-size_t scan_lds_bytes(int S, int K, bool ti) {
-#define SELSCAN_LDS(SS, KK) \
-  if (S == SS && K == KK) return size_t(ti ? wave_lds<SS, KK, true>::total : wave_lds<SS, KK, false>::total) * 4 * kWavesPerBlock;
-  SELSCAN_LDS(4, 1) SELSCAN_LDS(8, 1) SELSCAN_LDS(16, 1) SELSCAN_LDS(16, 2) SELSCAN_LDS(16, 4)
-#undef SELSCAN_LDS
-  return 0;
 }
 
 }  // namespace selscan

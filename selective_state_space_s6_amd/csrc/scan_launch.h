@@ -31,8 +31,8 @@ struct ScanParams {
   int32_t total_items;  // batch * n_chunks * groups (one wavefront each)
   float* ws_state;      // chunked: [batch][D][N][n_chunks] end states, then carries
   float* ws_dsum;       // chunked: [batch][D][n_chunks] sum of delta per chunk
-  int32_t vec_io;       // 1: u/delta/z/y rows move as 4-channel vectors (16 lanes per channel,
-                        //    D % 4 == 0, rows aligned to 4 elements)
+  int32_t pipelined;    // 1: scan_kernel_pipe (16 lanes per channel, B/C rows readable four
+                        //    states at a time); 0: scan_kernel
 };
 
 struct PrefixParams {
@@ -46,8 +46,6 @@ struct PrefixParams {
 
 // Lanes per channel (S) and states per lane (K) for N states.
 void lanes_for_states(int64_t N, int* S, int* K);
-// Dynamic LDS bytes of one scan-kernel block.
-size_t scan_lds_bytes(int S, int K, bool ti);
 
 hipError_t launch_scan_pass(int pass, bool bf16, bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
 hipError_t launch_chunk_prefix(const PrefixParams& p, hipStream_t stream);
