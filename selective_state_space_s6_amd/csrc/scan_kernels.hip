@@ -490,6 +490,12 @@ void scan_kernel(ScanParams p) {
 // touch the state).
 
 constexpr int kRowUD = 24;     // LDS row (floats) of a channel's 16 u / delta values
+// Wavefronts (neighbouring channel groups) per workgroup.  Measured on the long-context
+// workload: 1 is fastest (2 and 4 slower by 8-25 %: grouping only constrains placement).
+constexpr int kPipeWaves = 1;
+// Tiles of global loads in flight per wavefront: deeper hides more latency but costs
+// registers; measured best at 3 for bf16 I/O and 2 for fp32 (whose B/C sets are twice as
+// wide and would spill at 3 wavefronts per SIMD); 1 for 64 states per channel.
 constexpr int kChanP = 264;    // LDS block of one channel's 16 x 16 partial readouts (+8)
 
 template <int K, bool TI, int MODE>
@@ -525,6 +531,17 @@ template <> struct quad_io<uint16_t> {
   }
 };
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. n-1.
+template <int I, int Nn, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < Nn) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, Nn>(f);
+  }
+}
+template <int Nn, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, Nn>(f); }
+
 // Position of (state lane r, token j) in a channel's partial-readout block: rows of 16
 // tokens, the four 4-token groups of row r XOR-rotated by (r >> 1) & 3 so that the
 // 128-bit row writes of eight neighbouring lanes, and the column reads of the finalise
@@ -532,7 +549,7 @@ template <> struct quad_io<uint16_t> {
 __device__ __forceinline__ int part_pos(int r, int j) { return r * 16 + 4 * ((j >> 2) ^ ((r >> 1) & 3)) + (j & 3); }
 
 template <typename IO, int K, bool TI, int MODE>
-__global__ __launch_bounds__(64)
+__global__ __launch_bounds__(64 * kPipeWaves)
 __attribute__((amdgpu_waves_per_eu(occupancy<K>::kMinWaves)))
 void scan_kernel_pipe(ScanParams p) {
   using T = io_traits<IO>;
@@ -548,11 +565,12 @@ void scan_kernel_pipe(ScanParams p) {
   constexpr int kRsrcWord3 = 0x00020000;
 
   extern __shared__ __align__(16) float smem[];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane / S, s = lane % S;      // step layout
   const int it = lane >> 2, ic = lane & 3;   // I/O layout
 
-  const int item = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int item = xcd_contiguous_block(blockIdx.x, gridDim.x) * kPipeWaves + wave;
   if (item >= p.total_items) return;
   const int g = item % p.groups;
   const int bc = item / p.groups;
@@ -647,14 +665,16 @@ void scan_kernel_pipe(ScanParams p) {
     }
   };
 
-  // ---- load sets: two tiles in flight, by tile parity
-  typename Qd::raw_t xB[2][TI ? 1 : NL], xC[2][TI ? 1 : NL];
-  uint32_t xU[2], xD[2], xZ[2];
+  // ---- load sets: tile t's loads go to set t % NS and are issued NS - 1 iterations before
+  // the iteration that stages it
+  constexpr int NS = K >= 4 ? 1 : (ES == 2 ? 3 : 2);
+  typename Qd::raw_t xB[NS][TI ? 1 : NL], xC[NS][TI ? 1 : NL];
+  uint32_t xU[NS], xD[NS], xZ[NS];
   const int64_t ntiles = (nrows + kTile - 1) / kTile;
   const int64_t nfull = nrows / kTile;
   const int last_steps = int(nrows - nfull * kTile);       // tokens of a ragged last tile
-  auto issue = [&](int64_t t, auto par_tag) __attribute__((always_inline)) {
-    constexpr int P = decltype(par_tag)::value;
+  auto issue = [&](int64_t t, auto set_tag) __attribute__((always_inline)) {
+    constexpr int P = decltype(set_tag)::value;
     const int64_t tt = t < ntiles ? t : ntiles - 1;           // past the end: reload the last tile
     const int64_t row0 = tt * kTile;
     xU[P] = load_elem(rU, voU, row0 * p.u_sl * ES);
@@ -671,8 +691,8 @@ void scan_kernel_pipe(ScanParams p) {
   };
 
   // LDS regions of tile parity P
-  float* const sBase = smem;
-  float* const sP = smem + 2 * LDS::kBuf;
+  float* const sBase = smem + wave * LDS::total;
+  float* const sP = sBase + 2 * LDS::kBuf;
   auto bufB = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf; };
   auto bufC = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf + LDS::kB; };
   auto bufU = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf + LDS::kB + LDS::kC; };
@@ -681,22 +701,22 @@ void scan_kernel_pipe(ScanParams p) {
   // u and z of a tile, widened, carried from staging to the finalise
   float uSt = 0.f, zSt = 0.f, uCur = 0.f, zCur = 0.f, uFin = 0.f, zFin = 0.f;
 
-  // Stage the load set of parity P into LDS buffer P.
-  auto stage = [&](auto par_tag) __attribute__((always_inline)) {
-    constexpr int P = decltype(par_tag)::value;
-    const float uv = T::from_raw(xU[P]);
+  // Stage load set SET into LDS buffer P.
+  auto stage = [&](auto set_tag, int P) __attribute__((always_inline)) {
+    constexpr int SET = decltype(set_tag)::value;
+    const float uv = T::from_raw(xU[SET]);
     bufU(P)[ic * kRowUD + it] = uv;
     uSt = uv;
-    if (READOUT) zSt = T::from_raw(xZ[P]);
+    if (READOUT) zSt = T::from_raw(xZ[SET]);
     if (!TI) {
-      bufD(P)[ic * kRowUD + it] = T::from_raw(xD[P]);
+      bufD(P)[ic * kRowUD + it] = T::from_raw(xD[SET]);
 #pragma unroll
       for (int r = 0; r < NL; ++r) {
         const int tok = tq + TPL * r;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          bufB(P)[(4 * qg + j) * kRowPad + tok] = Qd::get(xB[P][r], j);
-          if (READOUT) bufC(P)[(4 * qg + j) * kRowPad + tok] = Qd::get(xC[P][r], j);
+          bufB(P)[(4 * qg + j) * kRowPad + tok] = Qd::get(xB[SET][r], j);
+          if (READOUT) bufC(P)[(4 * qg + j) * kRowPad + tok] = Qd::get(xC[SET][r], j);
         }
       }
     }
@@ -793,18 +813,21 @@ void scan_kernel_pipe(ScanParams p) {
 
   auto region = [] () __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
 
-  // One loop iteration for full tile t of parity P, in five scheduling regions; the
-  // operands of each step group are read one region ahead of their use.
-  auto iteration = [&](int64_t t, auto par_tag, auto zero_tag, auto fin_tag) __attribute__((always_inline)) {
-    constexpr int P = decltype(par_tag)::value;
+  // One loop iteration for full tile t (TM = t mod U, U = lcm(NS, 2)), in five scheduling
+  // regions; the operands of each step group are read one region ahead of their use.
+  constexpr int U = NS % 2 == 0 ? NS : 2 * NS;
+  auto iteration = [&](int64_t t, auto tm_tag, auto zero_tag, auto fin_tag) __attribute__((always_inline)) {
+    constexpr int TM = decltype(tm_tag)::value;
+    constexpr int P = TM % 2;                          // LDS buffer of tile t
+    constexpr int SET1 = (TM + 1) % NS;                // load set of tile t+1 (and t+1+NS)
     constexpr bool FIN = decltype(fin_tag)::value && READOUT;
     region();
     wave_lds_sync();
     if (FIN) fin_read();                               // tile t-1
     order_lds();
     rd(P, 0);
-    stage(std::integral_constant<int, 1 - P>{});       // tile t+1
-    issue(t + 3, std::integral_constant<int, 1 - P>{});
+    stage(std::integral_constant<int, SET1>{}, 1 - P); // tile t+1
+    issue(t + 1 + NS, std::integral_constant<int, SET1>{});
     region();
     rd(P, 1);
     cmp(0, zero_tag, true_t{}, kTile);
@@ -821,6 +844,15 @@ void scan_kernel_pipe(ScanParams p) {
     uFin = uCur; zFin = zCur;
     uCur = uSt; zCur = zSt;
   };
+  // U iterations starting at t (t mod U == TM0), each only while t < nfull when GUARD.
+  auto block = [&](int64_t t, auto zero_tag, auto guard_tag) __attribute__((always_inline)) {
+    constexpr bool GUARD = decltype(guard_tag)::value;
+    static_for<U>([&](auto k_tag) __attribute__((always_inline)) {
+      constexpr int KK = decltype(k_tag)::value;
+      constexpr int TM = (1 + KK) % U;
+      if (!GUARD || t + KK < nfull) iteration(t + KK, std::integral_constant<int, TM>{}, zero_tag, true_t{});
+    });
+  };
   // Steps of the ragged last tile (buffer P), one group after another.
   auto ragged = [&](int P, auto zero_tag, int nsteps) __attribute__((always_inline)) {
 #pragma unroll
@@ -831,23 +863,19 @@ void scan_kernel_pipe(ScanParams p) {
   };
 
   auto run = [&](auto zero_tag) __attribute__((always_inline)) {
-    issue(0, I0{});
-    issue(1, I1{});
-    stage(I0{});                                        // tile 0 -> buffer 0
+    static_for<NS>([&](auto k_tag) __attribute__((always_inline)) { issue(int64_t(decltype(k_tag)::value), k_tag); });
+    stage(I0{}, 0);                                     // tile 0 -> buffer 0
     uCur = uSt; zCur = zSt;
-    issue(2, I0{});
+    issue(int64_t(NS), I0{});
     int64_t t = 0;
     if (nfull > 0) {
       iteration(int64_t(0), I0{}, zero_tag, false_t{});
       t = 1;
     }
-    for (; t + 1 < nfull; t += 2) {
-      iteration(t, I1{}, zero_tag, true_t{});
-      iteration(t + 1, I0{}, zero_tag, true_t{});
-    }
+    for (; t + U <= nfull; t += U) block(t, zero_tag, false_t{});   // t mod U == 1 here
     if (t < nfull) {
-      iteration(t, I1{}, zero_tag, true_t{});
-      ++t;
+      block(t, zero_tag, true_t{});
+      t = nfull;
     }
     // drain: finalise tile nfull-1, then the ragged tile (staged in buffer nfull % 2)
     wave_lds_sync();
@@ -956,9 +984,15 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
 
 template <typename IO, int K, bool TI, int MODE>
 hipError_t launch_scan_pipe(const ScanParams& p, hipStream_t stream) {
-  constexpr size_t lds = size_t(pipe_lds<K, TI, MODE>::total) * sizeof(float);
-  static_assert(lds <= 65536, "one wavefront's LDS stays within the default dynamic limit");
-  hipLaunchKernelGGL((scan_kernel_pipe<IO, K, TI, MODE>), dim3(unsigned(p.total_items)), dim3(64), lds, stream, p);
+  constexpr size_t lds = size_t(pipe_lds<K, TI, MODE>::total) * sizeof(float) * kPipeWaves;
+  if (lds > 65536) {   // above the default dynamic-LDS limit: opt in once per kernel
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&scan_kernel_pipe<IO, K, TI, MODE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (attr != hipSuccess) return attr;
+  }
+  const unsigned blocks = unsigned((p.total_items + kPipeWaves - 1) / kPipeWaves);
+  hipLaunchKernelGGL((scan_kernel_pipe<IO, K, TI, MODE>), dim3(blocks), dim3(64 * kPipeWaves), lds, stream, p);
   return hipGetLastError();
 }
 
