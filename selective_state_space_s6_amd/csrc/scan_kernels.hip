@@ -463,55 +463,67 @@ void scan_kernel(ScanParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// The software-pipelined scan, used when 16 lanes share a channel (N > 8, so a wavefront
-// owns 4 channels) and B/C rows can be read four states at a time (N % 4 == 0 and 4-state
-// aligned rows; always for time-invariant coefficients).  One wavefront per workgroup.
+// The cooperative, software-pipelined scan.  Used when 16 lanes share a channel (N > 8),
+// D % 4 == 0, u/delta/z/y rows sit on 4-element boundaries and per-token B/C rows can be
+// read four states at a time (N % 4 == 0; always for time-invariant coefficients).
 //
-// Step layout as in scan_kernel: lane (c, s) owns states s + 16 k of channel c.
-// I/O layout: lane (it, ic) = (lane / 4, lane % 4) moves token it, channel ic of a 16-token
-// tile -- u, delta and z loads and the y store, one element each, four neighbouring lanes
-// on four neighbouring channels -- and the same lane finalises that (token, channel), so
-// the feed-through and the gate use the u and z it loaded itself.  B and C: each lane loads
-// four consecutive states of one token with a single 8- or 16-byte access and writes them
-// transposed ([n][token]) to LDS.
+// A workgroup of 4 wavefronts (2 for time-invariant coefficients) owns 16 (8) neighbouring
+// channels of one (batch row, chunk); wavefront w steps channels 4w .. 4w+3 exactly as scan_kernel does (lane (c, s)
+// owns states s + 16 k of channel c, held in VGPRs).  What the four wavefronts share is the
+// movement of data: each 16-token tile of u, delta, z, B and C is fetched ONCE per
+// workgroup -- one 8-byte (bf16) or 16-byte (fp32) access per lane covers 4 channels of one
+// token (or 4 states of B/C) -- and staged in LDS, and y leaves as one 32- or 64-byte row
+// segment per token.  A wavefront owning only 4 channels would otherwise make one memory
+// request per token row for 8 useful bytes; sharing cuts those requests by 4 and moves the
+// per-tile staging work off three of the four wavefronts.  The roles (which tensor a
+// wavefront fetches and stages, which one stores y) are fixed per wavefront and chosen
+// through its descriptors and LDS destinations, so every wavefront runs the same code.
 //
-// Iteration t of the tile loop (one wave-level LDS sync at its top) runs three independent
-// streams:
-//   finalise tile t-1   read its partial readouts, sum, feed-through, gate, store y
-//   stage tile t+1      LDS writes of the operands loaded two iterations earlier, then the
-//                       loads of tile t+3
-//   steps of tile t     read the staged operands of tile t, write its partial readouts
-// Staged operands are double-buffered by tile parity.  The partial-readout buffer is single:
-// the finalise reads are issued before the steps write it (a wavefront's LDS accesses run
-// in issue order, and a compiler fence keeps that order).  Otherwise the streams touch
-// disjoint LDS within an iteration, so the compiler may interleave them and the latency of
-// one stream's memory traffic hides behind another's arithmetic.  Full tiles run in the
-// loop; a ragged last tile runs after it with a step count (its padded tokens must not
-// touch the state).
+// Iteration t of the tile loop starts with one workgroup barrier and runs three
+// independent streams:
+//   finalise tile t-1   its partial readouts (private to the wavefront), D u, gate, y into
+//                       the shared y tile; the y tile of t-2 is stored
+//   stage tile t+1      LDS writes of the loads issued NS iterations earlier; loads of
+//                       tile t+1+NS issued
+//   steps of tile t     four groups of four tokens, each group's operands read one
+//                       scheduling region ahead
+// Staged tiles rotate over three LDS buffers (t mod 3): a tile is written in iteration t-1,
+// stepped in iteration t and read by its finalise in iteration t+1.  The y tile alternates
+// over two.  The partial-readout block is single: its finalise reads are issued before the
+// steps overwrite it (a wavefront's LDS accesses run in issue order, and a compiler fence
+// keeps that order).  Full tiles run in the loop; a ragged last tile runs after it with a
+// step count (its padded tokens must not touch the state).
 
-constexpr int kRowUD = 24;     // LDS row (floats) of a channel's 16 u / delta values
-// Wavefronts (neighbouring channel groups) per workgroup.  Measured on the long-context
-// workload: 1 is fastest (2 and 4 slower by 8-25 %: grouping only constrains placement).
-constexpr int kPipeWaves = 1;
-// Tiles of global loads in flight per wavefront: deeper hides more latency but costs
-// registers; measured best at 3 for bf16 I/O and 2 for fp32 (whose B/C sets are twice as
-// wide and would spill at 3 wavefronts per SIMD); 1 for 64 states per channel.
-constexpr int kChanP = 264;    // LDS block of one channel's 16 x 16 partial readouts (+8)
+constexpr int kChanP = 264;               // LDS block of one channel's 16 x 16 partial readouts (+8)
+
+// Wavefronts per workgroup: 4 for selective coefficients (u, delta, z, B, C to share);
+// 2 for time-invariant ones, where only u (and z) move per token and the per-tile work is
+// small, so fewer barrier partners pay (measured).
+template <bool TI> struct coop_width { static constexpr int W = TI ? 2 : 4; };
 
 template <int K, bool TI, int MODE>
-struct pipe_lds {
+struct coop_lds {
   static constexpr bool READOUT = MODE != MODE_STATE;
+  static constexpr int W = coop_width<TI>::W;
+  static constexpr int kCh = 4 * W;                             // channels per workgroup
+  static constexpr int kRowY = kCh + 4;                         // LDS row of the y tile
   static constexpr int NP = 16 * K;
-  static constexpr int kB = TI ? 0 : NP * kRowPad;            // sB[NP][20]
-  static constexpr int kC = (TI || !READOUT) ? 0 : kB;         // sC[NP][20]
-  static constexpr int kU = 4 * kRowUD;                        // sU[4][24]
-  static constexpr int kD = TI ? 0 : 4 * kRowUD;               // sD[4][24]
-  static constexpr int kBuf = kB + kC + kU + kD;               // one tile parity
-  static constexpr int kP = READOUT ? 4 * kChanP : 0;          // sP[4][16 x 16, swizzled]
-  static constexpr int total = 2 * kBuf + kP;
+  static constexpr int kT = kCh * kRowPad;                      // one token tile [channels][20]
+  static constexpr int kB = TI ? 0 : NP * kRowPad;              // [NP][20]
+  static constexpr int kC = (TI || !READOUT) ? 0 : kB;
+  static constexpr int kU = kT;
+  static constexpr int kD = TI ? 0 : kT;
+  static constexpr int kZ = READOUT ? kT : 0;
+  static constexpr int kBuf = kB + kC + kU + kD + kZ;           // one staged tile
+  static constexpr int kNBuf = 3;
+  static constexpr int kT4 = 16 * kRowPad;                      // a token tile of 4 vectors (16 channels)
+  static constexpr int kSink = kT4 > kB ? kT4 : kB;             // writes of idle staging lanes and roles
+  static constexpr int kP = READOUT ? 4 * kChanP : 0;           // per wavefront
+  static constexpr int kY = READOUT ? 2 * kTile * kRowY : 0;    // [2][16 tokens][kRowY]
+  static constexpr int total = kNBuf * kBuf + kSink + W * kP + kY;
 };
 
-// B/C: four consecutive states of one token as raw bits (bf16: 8 bytes, fp32: 16 bytes).
+// Four consecutive elements (channels of a token, or states of B/C) as raw bits.
 template <typename IO> struct quad_io;
 template <> struct quad_io<float> {
   using raw_t = uint32_t __attribute__((ext_vector_type(4)));
@@ -519,15 +531,30 @@ template <> struct quad_io<float> {
     return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
   }
   static __device__ __forceinline__ float get(raw_t v, int j) { return __uint_as_float(v[j]); }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, float4 y) {
+    const raw_t v = {__float_as_uint(y.x), __float_as_uint(y.y), __float_as_uint(y.z), __float_as_uint(y.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                           r, voff, soff, 0);
+  }
 };
 template <> struct quad_io<uint16_t> {
   using raw_t = uint32_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ raw_t load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
     return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
   }
   static __device__ __forceinline__ float get(raw_t v, int j) {
     const uint32_t w = v[j >> 1];
     return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, float4 y) {
+    // round to nearest even (v_cvt_pk_bf16_f32)
+    const f32x2_t lo = {y.x, y.y}, hi = {y.z, y.w};
+    const raw_t v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t))};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v),
+                                          r, voff, soff, 0);
   }
 };
 
@@ -548,13 +575,20 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, Nn>(f); }
 // (a channel block starts 8 banks after the previous one), hit distinct banks.
 __device__ __forceinline__ int part_pos(int r, int j) { return r * 16 + 4 * ((j >> 2) ^ ((r >> 1) & 3)) + (j & 3); }
 
+// Workgroup barrier for LDS traffic only: this wavefront's LDS accesses have completed and
+// every wavefront has arrived.  Global loads stay in flight (no vmcnt wait).
+__device__ __forceinline__ void block_lds_sync() {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <typename IO, int K, bool TI, int MODE>
-__global__ __launch_bounds__(64 * kPipeWaves)
+__global__ __launch_bounds__(64 * coop_width<TI>::W)
 __attribute__((amdgpu_waves_per_eu(occupancy<K>::kMinWaves)))
-void scan_kernel_pipe(ScanParams p) {
+void scan_kernel_coop(ScanParams p) {
   using T = io_traits<IO>;
   using Qd = quad_io<IO>;
-  using LDS = pipe_lds<K, TI, MODE>;
+  using LDS = coop_lds<K, TI, MODE>;
+  constexpr int W = LDS::W, kCh = LDS::kCh, kRowY = LDS::kRowY;
   constexpr int S = 16, NP = LDS::NP;
   constexpr int QG = NP / 4;                 // 4-state groups per token row
   constexpr int TPL = 64 / QG;               // tokens covered by one B/C load instruction
@@ -563,25 +597,31 @@ void scan_kernel_pipe(ScanParams p) {
   constexpr int ES = T::kBytes;
   constexpr uint32_t kOOB = 0x80000000u;
   constexpr int kRsrcWord3 = 0x00020000;
+  // tiles of global loads in flight: measured best at 3 for bf16 and 2 for fp32 (whose
+  // load sets are twice as wide); 1 for 64 states per channel
+  constexpr int NS = K >= 4 ? 1 : (ES == 2 ? 3 : 2);
 
   extern __shared__ __align__(16) float smem[];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane / S, s = lane % S;      // step layout
-  const int it = lane >> 2, ic = lane & 3;   // I/O layout
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane / S, s = lane % S;      // step layout: channel 4w + c, state slot s
+  const int it = lane >> 2, ic = lane & 3;   // finalise layout: token it, channel 4w + ic
+  const int vr = lane & 15, vq = lane >> 4;  // tile I/O layout: token vr, channels 4vq .. 4vq+3
 
-  const int item = xcd_contiguous_block(blockIdx.x, gridDim.x) * kPipeWaves + wave;
-  if (item >= p.total_items) return;
-  const int g = item % p.groups;
-  const int bc = item / p.groups;
-  const int chunk = bc % p.n_chunks;
+  const int64_t groups = (p.D + kCh - 1) / kCh;
+  const int64_t wg = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  if (wg >= p.batch * p.n_chunks * groups) return;          // whole workgroup exits together
+  const int64_t g = wg % groups;
+  const int64_t bc = wg / groups;
+  const int chunk = int(bc % p.n_chunks);
   const int64_t b = bc / p.n_chunks;
 
   const int64_t D = p.D, N = p.N;
-  const int64_t d0 = int64_t(g) * 4;
-  const int64_t d = d0 + c;                  // channel of the step layout
-  const int64_t dio = d0 + ic;               // channel of the I/O layout
-  const bool dvalid = d < D, iovalid = dio < D;
+  const int64_t d0 = g * kCh;                // first channel of the workgroup
+  const int64_t d = d0 + 4 * w + c;          // channel of the step layout
+  const int64_t df = d0 + 4 * w + ic;        // channel of the finalise layout
+  const bool dvalid = d < D, fvalid = df < D;
+  const bool vvalid = vq < W && d0 + 4 * vq < D;   // D % 4 == 0: a 4-channel vector is all in or all out
   const int64_t l_begin = int64_t(chunk) * p.chunk_len;
   const int64_t l_end = (l_begin + p.chunk_len < p.L) ? l_begin + p.chunk_len : p.L;
   const int64_t nrows = l_end - l_begin;
@@ -622,54 +662,60 @@ void scan_kernel_pipe(ScanParams p) {
     }
   }
 
-  // ---- buffer resources (see scan_kernel): reads past the work item's last element return
-  // 0, writes there are dropped; lanes of channels >= D use an offset beyond every size.
+  // ---- buffer resources (see scan_kernel): based at the workgroup's first token and
+  // channel, sized to its last element; reads past the end return 0, writes are dropped.
   auto rsrc = [&](const void* base, int64_t sb, int64_t sl, int64_t col0, int64_t ncols) __attribute__((always_inline)) {
     const char* p0 = static_cast<const char*>(base) + (b * sb + l_begin * sl + col0) * ES;
     const int64_t bytes = nrows > 0 ? ((nrows - 1) * sl + ncols) * ES : 0;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p0), (short)0, int(bytes), kRsrcWord3);
   };
   const int64_t z_sb = p.z != nullptr ? p.z_sb : p.u_sb, z_sl = p.z != nullptr ? p.z_sl : p.u_sl;
-  const auto rU = rsrc(p.u, p.u_sb, p.u_sl, d0, D - d0);
-  const auto rD = rsrc(p.delta, p.delta_sb, p.delta_sl, d0, D - d0);
-  const auto rZ = rsrc(p.z != nullptr ? p.z : p.u, z_sb, z_sl, d0, D - d0);   // no gate: re-reads u
   const auto rY = rsrc(p.y, p.y_sb, p.y_sl, d0, D - d0);
-  const auto rBd = rsrc(p.B, p.B_sb, p.B_sl, 0, N);
-  const auto rCd = rsrc(p.C, p.C_sb, p.C_sl, 0, N);
-  const uint32_t voU = iovalid ? uint32_t((it * p.u_sl + ic) * ES) : kOOB;
-  const uint32_t voD = iovalid ? uint32_t((it * p.delta_sl + ic) * ES) : kOOB;
-  const uint32_t voZ = iovalid ? uint32_t((it * z_sl + ic) * ES) : kOOB;
-  const uint32_t voY = iovalid ? uint32_t((it * p.y_sl + ic) * ES) : kOOB;
-  // B/C: lane -> 4-state group qg, token tq (+ TPL per load); groups past N read as zero
-  const int qg = lane / TPL, tq = lane % TPL;
-  const bool qvalid = 4 * qg < N;
-  const uint32_t voB = qvalid ? uint32_t((tq * p.B_sl + 4 * qg) * ES) : kOOB;
-  const uint32_t voC = qvalid ? uint32_t((tq * p.C_sl + 4 * qg) * ES) : kOOB;
+
+  // ---- staging roles.  Token-tile role (u, delta, z or none) and B/C-tile role (B, C or
+  // none) of this wavefront; an idle role reads past the descriptor (no memory traffic)
+  // and writes to an LDS sink.  Wavefront 0 also stores y.  Four wavefronts: u, delta, z
+  // (gate only); C (readout only), B.  Two (time-invariant): u, z (gate only).
+  static_assert(W == 4 || (W == 2 && TI), "two-wavefront workgroups move no delta, B or C");
+  const int roleT = W == 4 ? w : (w == 0 ? 0 : 2);   // 0 u, 1 delta, 2 z, 3 none
+  const bool onT = (roleT == 0) || (roleT == 1 && !TI) || (roleT == 2 && READOUT && p.z != nullptr);
+  const bool onQ = !TI && ((w == 3) || (w == 2 && READOUT));
+  const int64_t slT = roleT == 0 ? p.u_sl : roleT == 1 ? p.delta_sl : z_sl;
+  const int64_t slQ = w == 3 ? p.B_sl : p.C_sl;
+  const auto rT = roleT == 0 ? rsrc(p.u, p.u_sb, p.u_sl, d0, D - d0)
+                : roleT == 1 ? rsrc(p.delta, p.delta_sb, p.delta_sl, d0, D - d0)
+                             : rsrc(p.z != nullptr ? p.z : p.u, z_sb, z_sl, d0, D - d0);   // no gate: idle
+  const auto rQ = w == 3 ? rsrc(p.B, p.B_sb, p.B_sl, 0, N) : rsrc(p.C, p.C_sb, p.C_sl, 0, N);
+  const uint32_t voT = (onT && vvalid) ? uint32_t((vr * slT + 4 * vq) * ES) : kOOB;
+  const int qg = lane / TPL, tq = lane % TPL;   // B/C: 4-state group qg of token tq (+TPL per load)
+  const uint32_t voQ = (onQ && 4 * qg < N) ? uint32_t((tq * slQ + 4 * qg) * ES) : kOOB;
+  const uint32_t voY = (w == 0 && vvalid) ? uint32_t((vr * p.y_sl + 4 * vq) * ES) : kOOB;
 
   const bool gate = (p.z != nullptr) && READOUT;
-  const float dskip = (READOUT && p.Dskip != nullptr && iovalid) ? p.Dskip[dio] : 0.f;
+  const float dskip = (READOUT && p.Dskip != nullptr && fvalid) ? p.Dskip[df] : 0.f;
 
-  auto load_elem = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int64_t soff) __attribute__((always_inline)) -> uint32_t {
-    if (ES == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, voff, int(soff), 0);
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, int(soff), 0);
-  };
-  auto store_y = [&](float v, int64_t soff) __attribute__((always_inline)) {
-    if (ES == 2) {
-      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-      typedef float f32x2_t __attribute__((ext_vector_type(2)));
-      const f32x2_t vv = {v, v};
-      const uint32_t rr = __builtin_bit_cast(uint32_t, __builtin_convertvector(vv, bf16x2_t));   // RNE
-      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(rr & 0xffffu), rY, voY, int(soff), 0);
-    } else {
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rY, voY, int(soff), 0);
-    }
-  };
+  // ---- LDS layout: three staged-tile buffers, the sink, per-wavefront partial readouts,
+  // two y tiles
+  float* const sStage = smem;
+  float* const sSink = smem + LDS::kNBuf * LDS::kBuf;
+  float* const sP = sSink + LDS::kSink + w * LDS::kP;
+  float* const sY = sSink + LDS::kSink + W * LDS::kP;
+  auto bufB = [&](int q) __attribute__((always_inline)) { return sStage + q * LDS::kBuf; };
+  auto bufC = [&](int q) __attribute__((always_inline)) { return sStage + q * LDS::kBuf + LDS::kB; };
+  auto bufU = [&](int q) __attribute__((always_inline)) { return sStage + q * LDS::kBuf + LDS::kB + LDS::kC; };
+  auto bufD = [&](int q) __attribute__((always_inline)) { return bufU(q) + LDS::kU; };
+  auto bufZ = [&](int q) __attribute__((always_inline)) { return bufU(q) + LDS::kU + LDS::kD; };
+  // this wavefront's staging destinations inside buffer q
+  const int offT = !onT ? -1 : roleT == 0 ? LDS::kB + LDS::kC : roleT == 1 ? LDS::kB + LDS::kC + LDS::kU
+                                                                  : LDS::kB + LDS::kC + LDS::kU + LDS::kD;
+  const int offQ = !onQ ? -1 : w == 3 ? 0 : LDS::kB;
+  // lanes of channel vectors beyond the workgroup's W (two-wavefront groups) stage into the sink too
+  const bool tlane = offT >= 0 && vq < W;
+  auto dstT = [&](int q) __attribute__((always_inline)) { return tlane ? sStage + q * LDS::kBuf + offT : sSink; };
+  auto dstQ = [&](int q) __attribute__((always_inline)) { return offQ < 0 ? sSink : sStage + q * LDS::kBuf + offQ; };
 
-  // ---- load sets: tile t's loads go to set t % NS and are issued NS - 1 iterations before
-  // the iteration that stages it
-  constexpr int NS = K >= 4 ? 1 : (ES == 2 ? 3 : 2);
-  typename Qd::raw_t xB[NS][TI ? 1 : NL], xC[NS][TI ? 1 : NL];
-  uint32_t xU[NS], xD[NS], xZ[NS];
+  // ---- load sets: tile t's loads go to set t % NS, issued NS iterations before it is staged
+  typename Qd::raw_t xT[NS], xQ[NS][TI ? 1 : NL];
   const int64_t ntiles = (nrows + kTile - 1) / kTile;
   const int64_t nfull = nrows / kTile;
   const int last_steps = int(nrows - nfull * kTile);       // tokens of a ragged last tile
@@ -677,80 +723,58 @@ void scan_kernel_pipe(ScanParams p) {
     constexpr int P = decltype(set_tag)::value;
     const int64_t tt = t < ntiles ? t : ntiles - 1;           // past the end: reload the last tile
     const int64_t row0 = tt * kTile;
-    xU[P] = load_elem(rU, voU, row0 * p.u_sl * ES);
-    if (!TI) xD[P] = load_elem(rD, voD, row0 * p.delta_sl * ES);
-    if (READOUT) xZ[P] = load_elem(rZ, voZ, row0 * z_sl * ES);
+    xT[P] = Qd::load(rT, voT, int(row0 * slT * ES));
     if (!TI) {
 #pragma unroll
+      for (int r = 0; r < NL; ++r) xQ[P][r] = Qd::load(rQ, voQ, int((row0 + int64_t(TPL) * r) * slQ * ES));
+    }
+  };
+  // Stage load set SET into LDS buffer q: token tiles channel-major ([c][token]), B/C
+  // state-major ([n][token]).
+  auto stage = [&](auto set_tag, int q) __attribute__((always_inline)) {
+    constexpr int P = decltype(set_tag)::value;
+    float* const dt = dstT(q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dt[(4 * vq + j) * kRowPad + vr] = Qd::get(xT[P], j);
+    if (!TI) {
+      float* const dq = dstQ(q);
+#pragma unroll
       for (int r = 0; r < NL; ++r) {
-        const int64_t row = row0 + int64_t(TPL) * r;
-        xB[P][r] = Qd::load(rBd, voB, int(row * p.B_sl * ES));
-        if (READOUT) xC[P][r] = Qd::load(rCd, voC, int(row * p.C_sl * ES));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dq[(4 * qg + j) * kRowPad + tq + TPL * r] = Qd::get(xQ[P][r], j);
       }
     }
   };
 
-  // LDS regions of tile parity P
-  float* const sBase = smem + wave * LDS::total;
-  float* const sP = sBase + 2 * LDS::kBuf;
-  auto bufB = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf; };
-  auto bufC = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf + LDS::kB; };
-  auto bufU = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf + LDS::kB + LDS::kC; };
-  auto bufD = [&](int P) __attribute__((always_inline)) { return sBase + P * LDS::kBuf + LDS::kB + LDS::kC + LDS::kU; };
-
-  // u and z of a tile, widened, carried from staging to the finalise
-  float uSt = 0.f, zSt = 0.f, uCur = 0.f, zCur = 0.f, uFin = 0.f, zFin = 0.f;
-
-  // Stage load set SET into LDS buffer P.
-  auto stage = [&](auto set_tag, int P) __attribute__((always_inline)) {
-    constexpr int SET = decltype(set_tag)::value;
-    const float uv = T::from_raw(xU[SET]);
-    bufU(P)[ic * kRowUD + it] = uv;
-    uSt = uv;
-    if (READOUT) zSt = T::from_raw(xZ[SET]);
-    if (!TI) {
-      bufD(P)[ic * kRowUD + it] = T::from_raw(xD[SET]);
-#pragma unroll
-      for (int r = 0; r < NL; ++r) {
-        const int tok = tq + TPL * r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bufB(P)[(4 * qg + j) * kRowPad + tok] = Qd::get(xB[SET][r], j);
-          if (READOUT) bufC(P)[(4 * qg + j) * kRowPad + tok] = Qd::get(xC[SET][r], j);
-        }
-      }
-    }
-  };
-
+  // ---- steps: rd(q, grp) reads group grp's
+  // operands of the tile in buffer q into register slot grp & 1; cmp(grp) runs its steps
+  // and writes its four partial readouts.
   float dsum = 0.f;
   float* const prow = sP + c * kChanP;
-
-  // Steps of a staged tile, in four groups of four tokens: rd(P, q) reads group q's operands
-  // from LDS buffer P into register slot q & 1, cmp(q) runs its steps (FULL: all four
-  // tokens; otherwise only tokens below `nsteps`) and writes its four partial readouts.
+  const int cw = 4 * w + c;                  // step channel within the workgroup
   float4 rU4[2], rD4[2], rB4[2][K], rC4[2][K];
-  auto rd = [&](int P, int q) __attribute__((always_inline)) {
-    const int sl = q & 1;
-    rU4[sl] = *reinterpret_cast<const float4*>(bufU(P) + c * kRowUD + 4 * q);
+  auto rd = [&](int q, int grp) __attribute__((always_inline)) {
+    const int sl = grp & 1;
+    rU4[sl] = *reinterpret_cast<const float4*>(bufU(q) + cw * kRowPad + 4 * grp);
     if (!TI) {
-      rD4[sl] = *reinterpret_cast<const float4*>(bufD(P) + c * kRowUD + 4 * q);
+      rD4[sl] = *reinterpret_cast<const float4*>(bufD(q) + cw * kRowPad + 4 * grp);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        rB4[sl][k] = *reinterpret_cast<const float4*>(bufB(P) + (s + S * k) * kRowPad + 4 * q);
-        if (READOUT) rC4[sl][k] = *reinterpret_cast<const float4*>(bufC(P) + (s + S * k) * kRowPad + 4 * q);
+        rB4[sl][k] = *reinterpret_cast<const float4*>(bufB(q) + (s + S * k) * kRowPad + 4 * grp);
+        if (READOUT) rC4[sl][k] = *reinterpret_cast<const float4*>(bufC(q) + (s + S * k) * kRowPad + 4 * grp);
       }
     }
   };
-  auto cmp = [&](int q, auto zero_tag, auto full_tag, int nsteps) __attribute__((always_inline)) {
+  auto cmp = [&](int grp, auto zero_tag, auto full_tag, int nsteps) __attribute__((always_inline)) {
     constexpr bool ZERO = decltype(zero_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
-    const int sl = q & 1;
+    const int sl = grp & 1;
     const float uu[4] = {rU4[sl].x, rU4[sl].y, rU4[sl].z, rU4[sl].w};
     const float dd[4] = {rD4[sl].x, rD4[sl].y, rD4[sl].z, rD4[sl].w};
     float pacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (!FULL && 4 * q + j >= nsteps) break;
+      if (!FULL && 4 * grp + j >= nsteps) break;
       float acc = 0.f;
       if (TI) {
 #pragma unroll
@@ -778,119 +802,141 @@ void scan_kernel_pipe(ScanParams p) {
       pacc[j] = acc;
     }
     if (READOUT)
-      *reinterpret_cast<float4*>(prow + s * 16 + 4 * (q ^ ((s >> 1) & 3))) =
+      *reinterpret_cast<float4*>(prow + s * 16 + 4 * (grp ^ ((s >> 1) & 3))) =
           make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
   };
 
-  // Finalise: the 16 partial readouts of (token it, channel ic), then feed-through and gate.
-  float part[16];
-  auto fin_read = [&]() __attribute__((always_inline)) {
+  // ---- finalise: the 16 partial readouts of (token it, channel 4w + ic), feed-through and
+  // gate with u and z from the staged tile, result into the y tile.
+  float part[16], uF = 0.f, zF = 0.f;
+  auto fin_read = [&](int q) __attribute__((always_inline)) {
     const float* const col = sP + ic * kChanP;
 #pragma unroll
     for (int r = 0; r < 16; ++r) part[r] = col[part_pos(r, it)];
+    uF = bufU(q)[(4 * w + ic) * kRowPad + it];
+    zF = bufZ(q)[(4 * w + ic) * kRowPad + it];
   };
   auto fin_sum = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int w = 8; w >= 1; w >>= 1) {
+    for (int wd = 8; wd >= 1; wd >>= 1) {
 #pragma unroll
-      for (int r = 0; r < w; ++r) part[r] += part[r + w];
+      for (int r = 0; r < wd; ++r) part[r] += part[r + wd];
     }
   };
-  auto fin_out = [&](int64_t t, float uv, float zv) __attribute__((always_inline)) {
-    float yv = fmaf(dskip, uv, part[0]);                               // + D u
+  auto fin_out = [&](int yq) __attribute__((always_inline)) {
+    float yv = fmaf(dskip, uF, part[0]);                               // + D u
     // * SiLU(z) = z / (1 + exp(-z)); computed unconditionally and selected, so that the
     // iteration stays one basic block
-    const float silu = zv * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zv * kLog2e));
+    const float silu = zF * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zF * kLog2e));
     yv *= gate ? silu : 1.f;
-    store_y(yv, t * kTile * p.y_sl * ES);                               // dropped past l_end
+    sY[yq * (kTile * kRowY) + it * kRowY + 4 * w + ic] = yv;
+  };
+  // store the y tile of tile t from y buffer yq (wavefront 0; the others are dropped)
+  auto y_store = [&](int64_t t, int yq) __attribute__((always_inline)) {
+    const float4 yv = *reinterpret_cast<const float4*>(sY + yq * (kTile * kRowY) + vr * kRowY + 4 * (vq < W ? vq : 0));
+    Qd::store(rY, voY, int(t * kTile * p.y_sl * ES), yv);             // dropped past l_end
   };
   auto order_lds = [] () __attribute__((always_inline)) { __asm__ __volatile__("" ::: "memory"); };
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using true_t = std::integral_constant<bool, true>;
-  using false_t = std::integral_constant<bool, false>;
-
   auto region = [] () __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
 
-  // One loop iteration for full tile t (TM = t mod U, U = lcm(NS, 2)), in five scheduling
-  // regions; the operands of each step group are read one region ahead of their use.
-  constexpr int U = NS % 2 == 0 ? NS : 2 * NS;
-  auto iteration = [&](int64_t t, auto tm_tag, auto zero_tag, auto fin_tag) __attribute__((always_inline)) {
-    constexpr int TM = decltype(tm_tag)::value;
-    constexpr int P = TM % 2;                          // LDS buffer of tile t
-    constexpr int SET1 = (TM + 1) % NS;                // load set of tile t+1 (and t+1+NS)
+  using I0 = std::integral_constant<int, 0>;
+  using true_t = std::integral_constant<bool, true>;
+  using false_t = std::integral_constant<bool, false>;
+  auto mod3 = [] (int64_t t) __attribute__((always_inline)) { return int(t % 3); };
+
+  // One loop iteration for full tile t; SET1 = (t + 1) % NS is compile-time.
+  auto iteration = [&](int64_t t, auto set_tag, auto zero_tag, auto fin_tag, auto yst_tag) __attribute__((always_inline)) {
     constexpr bool FIN = decltype(fin_tag)::value && READOUT;
+    constexpr bool YST = decltype(yst_tag)::value && READOUT;
+    const int q0 = mod3(t), q1 = mod3(t + 1), qm = mod3(t + 2);   // buffers of t, t+1, t-1
     region();
-    wave_lds_sync();
-    if (FIN) fin_read();                               // tile t-1
+    block_lds_sync();
+    if (FIN) fin_read(qm);                             // tile t-1
+    if (YST) y_store(t - 2, int(t & 1));               // tile t-2
     order_lds();
-    rd(P, 0);
-    stage(std::integral_constant<int, SET1>{}, 1 - P); // tile t+1
-    issue(t + 1 + NS, std::integral_constant<int, SET1>{});
+    rd(q0, 0);
+    stage(set_tag, q1);                                // tile t+1
+    issue(t + 1 + NS, set_tag);
     region();
-    rd(P, 1);
+    rd(q0, 1);
     cmp(0, zero_tag, true_t{}, kTile);
     if (FIN) fin_sum();
     region();
-    rd(P, 2);
+    rd(q0, 2);
     cmp(1, zero_tag, true_t{}, kTile);
-    if (FIN) fin_out(t - 1, uFin, zFin);
+    if (FIN) fin_out(int((t - 1) & 1));
     region();
-    rd(P, 3);
+    rd(q0, 3);
     cmp(2, zero_tag, true_t{}, kTile);
     region();
     cmp(3, zero_tag, true_t{}, kTile);
-    uFin = uCur; zFin = zCur;
-    uCur = uSt; zCur = zSt;
   };
-  // U iterations starting at t (t mod U == TM0), each only while t < nfull when GUARD.
+  // NS iterations from t (t mod NS == 2 mod NS), each only while t < nfull when GUARD.
   auto block = [&](int64_t t, auto zero_tag, auto guard_tag) __attribute__((always_inline)) {
     constexpr bool GUARD = decltype(guard_tag)::value;
-    static_for<U>([&](auto k_tag) __attribute__((always_inline)) {
+    static_for<NS>([&](auto k_tag) __attribute__((always_inline)) {
       constexpr int KK = decltype(k_tag)::value;
-      constexpr int TM = (1 + KK) % U;
-      if (!GUARD || t + KK < nfull) iteration(t + KK, std::integral_constant<int, TM>{}, zero_tag, true_t{});
+      using SET = std::integral_constant<int, (3 + KK) % NS>;
+      if (!GUARD || t + KK < nfull) iteration(t + KK, SET{}, zero_tag, true_t{}, true_t{});
     });
-  };
-  // Steps of the ragged last tile (buffer P), one group after another.
-  auto ragged = [&](int P, auto zero_tag, int nsteps) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      rd(P, q);
-      cmp(q, zero_tag, false_t{}, nsteps);
-    }
   };
 
   auto run = [&](auto zero_tag) __attribute__((always_inline)) {
     static_for<NS>([&](auto k_tag) __attribute__((always_inline)) { issue(int64_t(decltype(k_tag)::value), k_tag); });
     stage(I0{}, 0);                                     // tile 0 -> buffer 0
-    uCur = uSt; zCur = zSt;
     issue(int64_t(NS), I0{});
     int64_t t = 0;
     if (nfull > 0) {
-      iteration(int64_t(0), I0{}, zero_tag, false_t{});
+      iteration(int64_t(0), std::integral_constant<int, 1 % NS>{}, zero_tag, false_t{}, false_t{});
       t = 1;
     }
-    for (; t + U <= nfull; t += U) block(t, zero_tag, false_t{});   // t mod U == 1 here
+    if (nfull > 1) {
+      iteration(int64_t(1), std::integral_constant<int, 2 % NS>{}, zero_tag, true_t{}, false_t{});
+      t = 2;
+    }
+    for (; t + NS <= nfull; t += NS) block(t, zero_tag, false_t{});
     if (t < nfull) {
       block(t, zero_tag, true_t{});
       t = nfull;
     }
-    // drain: finalise tile nfull-1, then the ragged tile (staged in buffer nfull % 2)
-    wave_lds_sync();
-    if (READOUT && nfull > 0) fin_read();
-    order_lds();
-    if (last_steps > 0) ragged(int(nfull & 1), zero_tag, last_steps);
-    if (READOUT && nfull > 0) {
-      fin_sum();
-      fin_out(nfull - 1, uFin, zFin);
+    if (!READOUT) {                                     // state pass: only the ragged tile is left
+      if (last_steps > 0) {
+        block_lds_sync();
+        const int qr = mod3(nfull);
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          rd(qr, grp);
+          cmp(grp, zero_tag, false_t{}, last_steps);
+        }
+      }
+      return;
     }
-    if (READOUT && last_steps > 0) {
-      wave_lds_sync();
-      fin_read();
+    // drain: finalise tile nfull-1 and store tile nfull-2; the ragged tile (staged in buffer
+    // nfull % 3) runs its steps; then tile nfull-1's y, then the ragged tile's finalise
+    block_lds_sync();
+    if (nfull > 0) fin_read(mod3(nfull + 2));
+    if (nfull > 1) y_store(nfull - 2, int(nfull & 1));
+    order_lds();
+    if (last_steps > 0) {
+      const int qr = mod3(nfull);
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        rd(qr, grp);
+        cmp(grp, zero_tag, false_t{}, last_steps);
+      }
+    }
+    if (nfull > 0) {
       fin_sum();
-      fin_out(nfull, uCur, zCur);
+      fin_out(int((nfull - 1) & 1));
+    }
+    block_lds_sync();
+    if (nfull > 0) y_store(nfull - 1, int((nfull - 1) & 1));
+    if (last_steps > 0) {
+      fin_read(mod3(nfull));
+      fin_sum();
+      fin_out(int(nfull & 1));
+      block_lds_sync();
+      y_store(nfull, int(nfull & 1));
     }
   };
   if (wave_zero) run(true_t{});
@@ -983,25 +1029,28 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
 }
 
 template <typename IO, int K, bool TI, int MODE>
-hipError_t launch_scan_pipe(const ScanParams& p, hipStream_t stream) {
-  constexpr size_t lds = size_t(pipe_lds<K, TI, MODE>::total) * sizeof(float) * kPipeWaves;
+hipError_t launch_scan_coop(const ScanParams& p, hipStream_t stream) {
+  constexpr size_t lds = size_t(coop_lds<K, TI, MODE>::total) * sizeof(float);
   if (lds > 65536) {   // above the default dynamic-LDS limit: opt in once per kernel
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&scan_kernel_pipe<IO, K, TI, MODE>),
+        reinterpret_cast<const void*>(&scan_kernel_coop<IO, K, TI, MODE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (attr != hipSuccess) return attr;
   }
-  const unsigned blocks = unsigned((p.total_items + kPipeWaves - 1) / kPipeWaves);
-  hipLaunchKernelGGL((scan_kernel_pipe<IO, K, TI, MODE>), dim3(blocks), dim3(64 * kPipeWaves), lds, stream, p);
+  constexpr int kCh = coop_lds<K, TI, MODE>::kCh;
+  const int64_t groups = (p.D + kCh - 1) / kCh;
+  const int64_t blocks = p.batch * p.n_chunks * groups;
+  hipLaunchKernelGGL((scan_kernel_coop<IO, K, TI, MODE>), dim3(unsigned(blocks)), dim3(64 * coop_width<TI>::W), lds,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <typename IO, bool TI, int MODE>
 hipError_t dispatch_sk(int S, int K, const ScanParams& p, hipStream_t stream) {
   if (p.pipelined && S == 16) {
-    if (K == 1) return launch_scan_pipe<IO, 1, TI, MODE>(p, stream);
-    if (K == 2) return launch_scan_pipe<IO, 2, TI, MODE>(p, stream);
-    if (K == 4) return launch_scan_pipe<IO, 4, TI, MODE>(p, stream);
+    if (K == 1) return launch_scan_coop<IO, 1, TI, MODE>(p, stream);
+    if (K == 2) return launch_scan_coop<IO, 2, TI, MODE>(p, stream);
+    if (K == 4) return launch_scan_coop<IO, 4, TI, MODE>(p, stream);
   }
   if (S == 4 && K == 1) return launch_scan<IO, 4, 1, TI, MODE>(p, stream);
   if (S == 8 && K == 1) return launch_scan<IO, 8, 1, TI, MODE>(p, stream);

@@ -31,8 +31,8 @@ struct ScanParams {
   int32_t total_items;  // batch * n_chunks * groups (one wavefront each)
   float* ws_state;      // chunked: [batch][D][N][n_chunks] end states, then carries
   float* ws_dsum;       // chunked: [batch][D][n_chunks] sum of delta per chunk
-  int32_t pipelined;    // 1: scan_kernel_pipe (16 lanes per channel, B/C rows readable four
-                        //    states at a time); 0: scan_kernel
+  int32_t pipelined;    // 1: scan_kernel_coop (16 lanes per channel, D % 4 == 0, u/delta/z/y
+                        //    rows and B/C rows readable four elements at a time); 0: scan_kernel
 };
 
 struct PrefixParams {

@@ -163,15 +163,18 @@ int run(const void* u, const void* delta, const float* A, const void* B, const v
   p.n_chunks = plan.n_chunks;
   p.groups = int32_t(plan.groups);
   p.total_items = int32_t(d.batch * plan.n_chunks * plan.groups);
-  // pipelined kernel: 16 lanes per channel, and per-token B/C rows readable four states
-  // at a time (N % 4 == 0, rows and batches on 4-element boundaries)
+  // cooperative pipelined kernel: 16 lanes per channel, whole 4-channel vectors (D % 4 == 0,
+  // u/delta/z/y rows on 4-element boundaries) and per-token B/C rows readable four states
+  // at a time (N % 4 == 0, rows on 4-element boundaries)
   {
     const uintptr_t qbytes = uintptr_t(4) * (plan.bf16 ? 2 : 4);
     auto quad_ok = [&](const void* ptr, int64_t sb, int64_t sl) {
-      return reinterpret_cast<uintptr_t>(ptr) % qbytes == 0 && sb % 4 == 0 && sl % 4 == 0;
+      return ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) % qbytes == 0 && sb % 4 == 0 && sl % 4 == 0);
     };
+    const bool io_ok = d.dim % 4 == 0 && quad_ok(u, d.u_sb, d.u_sl) && quad_ok(z, d.z_sb, d.z_sl) &&
+                       quad_ok(y, d.y_sb, d.y_sl) && (plan.ti || quad_ok(delta, d.delta_sb, d.delta_sl));
     const bool bc_ok = plan.ti || (d.dstate % 4 == 0 && quad_ok(B, d.B_sb, d.B_sl) && quad_ok(C, d.C_sb, d.C_sl));
-    p.pipelined = (plan.S == 16 && bc_ok && !(d.path & SELSCAN_PATH_FLAG_SCALAR_IO)) ? 1 : 0;
+    p.pipelined = (plan.S == 16 && io_ok && bc_ok && !(d.path & SELSCAN_PATH_FLAG_SCALAR_IO)) ? 1 : 0;
   }
   hipError_t e;
   if (!plan.chunked) {
