@@ -64,7 +64,7 @@ def test_full_size_sampled_channels(name):
 
 
 @pytest.mark.parametrize("D", [7, 12])
-@pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 9, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 9, 12, 16, 17, 20, 32, 33, 48, 64])
 @pytest.mark.parametrize("L", [1, 15, 16, 17, 50, 64, 65, 130])
 def test_state_counts_and_short_sequences(N, L, D):
     inp = s6_workloads.generate("small_f32", "active", batch=2, L=L, D=D, N=N)
@@ -72,6 +72,19 @@ def test_state_counts_and_short_sequences(N, L, D):
     for path in ("single", "chunked"):
         y, last = run_gpu(inp, path=path)
         check(inp, y, last, y_ref, l_ref, "N=%d L=%d D=%d %s" % (N, L, D, path))
+
+
+@pytest.mark.parametrize("D", [36, 44])
+@pytest.mark.parametrize("L", [31, 200])
+def test_partial_workgroups_time_invariant(D, L):
+    """Time-invariant coefficients with a channel count that leaves the last group of 8
+    channels half empty (D % 8 == 4), with and without a gate, both paths."""
+    for gate in (False, True):
+        inp = s6_workloads.generate("s4d_ti_f32", "active", batch=2, L=L, D=D, gate=gate)
+        y_ref, l_ref = run_oracle(inp)
+        for path in ("single", "chunked"):
+            y, last = run_gpu(inp, path=path)
+            check(inp, y, last, y_ref, l_ref, "TI D=%d L=%d gate=%s %s" % (D, L, gate, path))
 
 
 @pytest.mark.parametrize("ti", [False, True])
