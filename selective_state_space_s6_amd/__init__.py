@@ -187,7 +187,8 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
 
     ``y`` / ``last_state`` may be given (outputs are written in place) or are allocated.
     ``workspace`` (a uint8 CUDA tensor of at least ``workspace_size`` bytes) selects the
-    non-allocating entry point.  ``stream`` defaults to torch's current stream."""
+    non-allocating entry point; when it is omitted and the call needs one, it is taken from
+    torch's caching allocator.  ``stream`` defaults to torch's current stream."""
     import torch
     io = u.dtype
     for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
@@ -211,10 +212,20 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
                                    or tuple(last_state.shape) != (batch, D, N)):
         raise ValueError("last_state must be a contiguous float32 [batch, D, N] tensor")
     dims = make_dims(u, delta, A, B, C, z, y, path=path, chunk_len=chunk_len, scalar_io=scalar_io)
+    torch_stream = stream if (stream is None or hasattr(stream, "cuda_stream")) else None
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    if workspace is None and (torch_stream is not None or stream == torch.cuda.current_stream(u.device).cuda_stream):
+        # Scratch of the chunked path from torch's caching allocator (the C entry point
+        # would allocate it stream-ordered on every call); a raw stream handle that is not
+        # torch's current stream keeps the library's own allocation.
+        need = workspace_size(dims)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+            if torch_stream is not None:
+                workspace.record_stream(torch_stream)
     args = [_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(y), _ptr(last_state),
             ctypes.byref(dims)]
     if workspace is not None:

@@ -30,7 +30,8 @@
 //   MODE_SINGLE: scan the whole sequence from h = 0, write y and last_state.
 //   MODE_STATE : chunked pass 1 -- scan one chunk from h = 0 without readout; write the
 //                chunk's end state and its sum of delta (the chunk's decay is
-//                exp(A * sum delta), the product of its Abar).
+//                exp(A * sum delta), the product of its Abar).  The last chunk is skipped:
+//                its map is never carried into another chunk.
 //   MODE_APPLY : chunked pass 2 -- scan one chunk from the carried-in state, write y and,
 //                for the final chunk, last_state.
 // Between the two chunked passes, chunk_prefix_kernel composes the per-chunk affine maps
@@ -133,12 +134,14 @@ void scan_kernel(ScanParams p) {
   const int c = lane / S, s = lane % S;
 
   const int item = xcd_contiguous_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
-  if (item >= p.total_items) return;                      // whole wave exits together
-  // item = ((b * n_chunks) + chunk) * groups + g : neighbouring items share (b, chunk)
+  // The state pass skips the last chunk: its end state is never carried anywhere.
+  const int nc_run = MODE == MODE_STATE ? p.n_chunks - 1 : p.n_chunks;
+  if (item >= p.batch * nc_run * p.groups) return;       // whole wave exits together
+  // item = ((b * nc_run) + chunk) * groups + g : neighbouring items share (b, chunk)
   const int g = item % p.groups;
   const int bc = item / p.groups;
-  const int chunk = bc % p.n_chunks;
-  const int64_t b = bc / p.n_chunks;
+  const int chunk = bc % nc_run;
+  const int64_t b = bc / nc_run;
 
   float* const sB = smem + wave * LDS::total;
   float* const sC = sB + LDS::kB;
@@ -610,11 +613,13 @@ void scan_kernel_coop(ScanParams p) {
 
   const int64_t groups = (p.D + kCh - 1) / kCh;
   const int64_t wg = xcd_contiguous_block(blockIdx.x, gridDim.x);
-  if (wg >= p.batch * p.n_chunks * groups) return;          // whole workgroup exits together
+  // The state pass skips the last chunk: its end state is never carried anywhere.
+  const int nc_run = MODE == MODE_STATE ? p.n_chunks - 1 : p.n_chunks;
+  if (wg >= p.batch * nc_run * groups) return;               // whole workgroup exits together
   const int64_t g = wg % groups;
   const int64_t bc = wg / groups;
-  const int chunk = int(bc % p.n_chunks);
-  const int64_t b = bc / p.n_chunks;
+  const int chunk = int(bc % nc_run);
+  const int64_t b = bc / nc_run;
 
   const int64_t D = p.D, N = p.N;
   const int64_t d0 = g * kCh;                // first channel of the workgroup
@@ -991,8 +996,10 @@ void chunk_prefix_kernel(PrefixParams p) {
     d = (seg / p.N) % p.D;
     b = seg / (p.N * p.D);
     const float a2 = p.A[d * p.N + n] * kLog2e;
-    P = __builtin_amdgcn_exp2f(a2 * p.dsum[(b * p.D + d) * p.n_chunks + i]);
-    H = p.state[seg * p.n_chunks + i];
+    if (i < p.n_chunks - 1) {          // the last chunk's map is never used (nor computed)
+      P = __builtin_amdgcn_exp2f(a2 * p.dsum[(b * p.D + d) * p.n_chunks + i]);
+      H = p.state[seg * p.n_chunks + i];
+    }
   }
   for (int off = 1; off < W; off <<= 1) {
     const float Pp = __shfl_up(P, off, W);
@@ -1017,7 +1024,9 @@ void fill_zero_kernel(float* x, int64_t n) {
 template <typename IO, int S, int K, bool TI, int MODE>
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
   constexpr size_t lds = size_t(wave_lds<S, K, TI>::total) * sizeof(float) * kWavesPerBlock;
-  const int blocks = (p.total_items + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t items = p.batch * (MODE == MODE_STATE ? p.n_chunks - 1 : p.n_chunks) * p.groups;
+  const int blocks = int((items + kWavesPerBlock - 1) / kWavesPerBlock);
+  if (blocks == 0) return hipSuccess;
   if (lds > 65536) {   // above the default dynamic-LDS limit: opt in once per kernel
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&scan_kernel<IO, S, K, TI, MODE>),
@@ -1039,7 +1048,8 @@ hipError_t launch_scan_coop(const ScanParams& p, hipStream_t stream) {
   }
   constexpr int kCh = coop_lds<K, TI, MODE>::kCh;
   const int64_t groups = (p.D + kCh - 1) / kCh;
-  const int64_t blocks = p.batch * p.n_chunks * groups;
+  const int64_t blocks = p.batch * (MODE == MODE_STATE ? p.n_chunks - 1 : p.n_chunks) * groups;
+  if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((scan_kernel_coop<IO, K, TI, MODE>), dim3(unsigned(blocks)), dim3(64 * coop_width<TI>::W), lds,
                      stream, p);
   return hipGetLastError();

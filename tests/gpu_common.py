@@ -43,6 +43,8 @@ def run_gpu(inp, *, path="auto", chunk_len=0, want_last=True, stream=None, works
         need = ss.workspace_size(ss.make_dims(u, delta, A, B, C, z, u, path=path, chunk_len=chunk_len,
                                               scalar_io=scalar_io))
         ws = tc.empty(max(need, 1), dtype=tc.uint8, device="cuda")
+    if stream is not None:
+        tc.cuda.synchronize()            # inputs were prepared on the current stream
     y, last = ss.selective_scan_fwd(u, delta, A, B, C, Ds, z, return_last_state=want_last, path=path,
                                     chunk_len=chunk_len, stream=stream, workspace=ws, scalar_io=scalar_io)
     tc.cuda.synchronize()

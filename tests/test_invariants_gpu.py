@@ -66,3 +66,15 @@ def test_side_stream():
     with torch.cuda.stream(s):
         y2, _ = run_gpu(inp, stream=s)
     assert np.array_equal(y1, y2)
+
+
+def test_library_allocated_workspace_on_raw_stream():
+    """The C entry point that allocates its own (stream-ordered) workspace: reached from the
+    binding with a raw stream handle that is not torch's current stream."""
+    import torch
+    inp = s6_workloads.generate("small_f32")
+    y1, l1 = run_gpu(inp, path="chunked")
+    s = torch.cuda.Stream()
+    y2, l2 = run_gpu(inp, path="chunked", stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1, y2) and np.array_equal(l1, l2)
