@@ -50,7 +50,7 @@ class OracleLib:
         fp = ctypes.POINTER(ctypes.c_float)
         dp = ctypes.POINTER(ctypes.c_double)
         lib.ssm_oracle_fwd.restype = ctypes.c_int
-        lib.ssm_oracle_fwd.argtypes = [fp, fp, fp, fp, fp, fp, fp, dp, dp, ctypes.c_int64, ctypes.c_int64,
+        lib.ssm_oracle_fwd.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, dp, dp, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
         lib.ssm_oracle_discretize.restype = None
         lib.ssm_oracle_discretize.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, dp, dp]
@@ -64,14 +64,14 @@ class OracleLib:
         self.lib.ssm_oracle_discretize(float(a), float(b), float(delta), ctypes.byref(ab), ctypes.byref(bb))
         return ab.value, bb.value
 
-    def fwd(self, u, delta, A, B, C, Dskip=None, z=None, *, time_invariant=False, want_last=True,
+    def fwd(self, u, delta, A, B, C, Dskip=None, z=None, *, h0=None, time_invariant=False, want_last=True,
             nthreads=None):
         """Run the fp64 recurrence.  Returns (y [batch,L,D] float64, last_state [batch,D,N] float64
         or None).
 
         u, z: [batch, L, D]; delta: [batch, L, D] (time-invariant: [D]); B, C: [batch, L, N]
-        (time-invariant: [D, N]); A: [D, N]; Dskip: [D].  Inputs are converted to float32 first,
-        the precision the GPU library receives.
+        (time-invariant: [D, N]); A: [D, N]; Dskip: [D]; h0: [batch, D, N] initial state (None:
+        zero).  Inputs are converted to float32 first, the precision the GPU library receives.
         """
         u = _f32(u)
         delta = _f32(delta)
@@ -80,6 +80,7 @@ class OracleLib:
         C = _f32(C)
         Dskip = _f32(Dskip)
         z = _f32(z)
+        h0 = _f32(h0)
         batch, L, D = u.shape
         N = A.shape[1]
         assert A.shape == (D, N)
@@ -91,12 +92,14 @@ class OracleLib:
             assert Dskip.shape == (D,)
         if z is not None:
             assert z.shape == (batch, L, D)
+        if h0 is not None:
+            assert h0.shape == (batch, D, N)
         y = np.empty((batch, L, D), dtype=np.float64)
         last = np.empty((batch, D, N), dtype=np.float64) if want_last else None
         if nthreads is None:
             nthreads = os.cpu_count() or 1
         rc = self.lib.ssm_oracle_fwd(
-            _fptr(u), _fptr(delta), _fptr(A), _fptr(B), _fptr(C), _fptr(Dskip), _fptr(z),
+            _fptr(u), _fptr(delta), _fptr(A), _fptr(B), _fptr(C), _fptr(Dskip), _fptr(z), _fptr(h0),
             y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
             None if last is None else last.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
             batch, L, D, N, 1 if time_invariant else 0, int(nthreads))
@@ -129,9 +132,9 @@ def discretize(a: float, b: float, delta: float):
     return _load().discretize(a, b, delta)
 
 
-def fwd(u, delta, A, B, C, Dskip=None, z=None, *, time_invariant=False, want_last=True, nthreads=None):
+def fwd(u, delta, A, B, C, Dskip=None, z=None, *, h0=None, time_invariant=False, want_last=True, nthreads=None):
     """The fp64 recurrence of the default oracle library; see ``OracleLib.fwd``."""
-    return _load().fwd(u, delta, A, B, C, Dskip, z, time_invariant=time_invariant, want_last=want_last,
+    return _load().fwd(u, delta, A, B, C, Dskip, z, h0=h0, time_invariant=time_invariant, want_last=want_last,
                        nthreads=nthreads)
 
 

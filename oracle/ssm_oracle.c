@@ -39,6 +39,12 @@
  *   - The final hidden state after the last token, one N-vector per channel
  *     (TorchLean "Selective Mamba", State.hidden and runArray: the state a following
  *     chunk continues from).
+ *   - An optional initial state h_{-1} (default zero): a call continues from the state a
+ *     previous call ended in, so running two chunks one after the other equals running
+ *     their concatenation, and a call with no tokens hands its initial state back unchanged
+ *     (TorchLean "Selective Mamba", step / runArray with an explicit state; the zero state
+ *     is zeroState).  A one-token call is the recurrent decode step (aarnphm, "One
+ *     recurrence, one convolution": the recurrent form generates one token at a time).
  *
  * Layouts (row-major, all contiguous):
  *   u, delta, z, y : [batch][L][D]           (time-invariant mode: delta is [D])
@@ -46,6 +52,7 @@
  *   A              : [D][N]
  *   Dskip          : [D]      (may be NULL: no feed-through)
  *   z              : may be NULL (no gate)
+ *   h0             : [batch][D][N]  float, the initial state (may be NULL: zero)
  *   last_state     : [batch][D][N]  (may be NULL)
  * Inputs are fp32 (bf16 data arrives already widened to fp32, which is exact); every
  * intermediate and every output is double.  The summation over states runs n = 0..N-1
@@ -60,7 +67,7 @@
 #include <string.h>
 
 typedef struct {
-  const float *u, *delta, *A, *B, *C, *Dskip, *z;
+  const float *u, *delta, *A, *B, *C, *Dskip, *z, *h0;
   double *y, *last_state;
   int64_t batch, L, D, N;
   int time_invariant;
@@ -76,7 +83,8 @@ static double zoh_input_coeff(double dt, double a) {
 
 static void scan_one_channel(oracle_job* j, int64_t b, int64_t d, double* h) {
   const int64_t L = j->L, D = j->D, N = j->N;
-  for (int64_t n = 0; n < N; ++n) h[n] = 0.0;                    /* h_{-1} = 0 */
+  for (int64_t n = 0; n < N; ++n)                                /* h_{-1}: given, else 0 */
+    h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 0.0;
   for (int64_t l = 0; l < L; ++l) {
     const int64_t tok = (b * L + l) * D + d;
     const double uu = (double)j->u[tok];
@@ -121,18 +129,19 @@ static void* worker(void* arg) {
 
 /* Returns 0 on success, -1 on invalid arguments, -2 on allocation/thread failure. */
 int ssm_oracle_fwd(const float* u, const float* delta, const float* A, const float* B,
-                   const float* C, const float* Dskip, const float* z, double* y,
+                   const float* C, const float* Dskip, const float* z, const float* h0, double* y,
                    double* last_state, int64_t batch, int64_t L, int64_t D, int64_t N,
                    int time_invariant, int nthreads) {
   if (batch < 0 || L < 0 || D <= 0 || N <= 0) return -1;
   if (batch == 0) return 0;
   if (L > 0 && (!u || !delta || !A || !B || !C || !y)) return -1;
-  if (L == 0) {
-    if (last_state) memset(last_state, 0, sizeof(double) * (size_t)(batch * D * N));
+  if (L == 0) {                                 /* no tokens: the state is handed back */
+    if (last_state)
+      for (int64_t i = 0; i < batch * D * N; ++i) last_state[i] = h0 ? (double)h0[i] : 0.0;
     return 0;
   }
   oracle_job j;
-  j.u = u; j.delta = delta; j.A = A; j.B = B; j.C = C; j.Dskip = Dskip; j.z = z;
+  j.u = u; j.delta = delta; j.A = A; j.B = B; j.C = C; j.Dskip = Dskip; j.z = z; j.h0 = h0;
   j.y = y; j.last_state = last_state;
   j.batch = batch; j.L = L; j.D = D; j.N = N; j.time_invariant = time_invariant;
   j.next_pair = 0;

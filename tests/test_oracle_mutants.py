@@ -40,7 +40,11 @@ MUTANTS = {
     "euler_decay": ("const double abar = exp(dt * a);", "const double abar = 1.0 + dt * a;"),
     "ti_b_layout_transposed": ("const float* Brow = j->time_invariant ? j->B + d * N : j->B + (b * L + l) * N;",
                                "const float* Brow = j->time_invariant ? j->B + d : j->B + (b * L + l) * N;"),
-    "state_not_reset": ("for (int64_t n = 0; n < N; ++n) h[n] = 0.0;", "for (int64_t n = 0; n < N; ++n) h[n] = 1e-3;"),
+    "state_not_reset": ("h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 0.0;",
+                        "h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 1e-3;"),
+    "initial_state_ignored": ("h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    "initial_state_wrong_index": ("h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 0.0;",
+                                  "h[n] = j->h0 ? (double)j->h0[(d * j->batch + b) * N + n] : 0.0;"),
 }
 
 
@@ -112,6 +116,12 @@ def pin_battery(lib):
     h = np.cumsum(d3[0].astype(np.float64) * B3[0] * u3[0], axis=0)
     if np.max(np.abs(y[0, :, 0] - np.sum(C3[0] * h, axis=1))) > 1e-12:
         failed.append("zero_rate")
+    # initial state against the brute-force unroll
+    h0 = rng.standard_normal((b, D, N)).astype(np.float32)
+    y, last = lib.fwd(*args, h0=h0)
+    yb, lb = brute_force(*args, h0=h0)
+    if rel_err(y, yb) > 1e-12 or rel_err(last, lb) > 1e-12:
+        failed.append("initial_state")
     return failed
 
 

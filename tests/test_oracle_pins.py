@@ -38,10 +38,11 @@ def _rand_s6(rng, batch, L, D, N, gate=True, dskip=True, zero_a=False):
     return u, delta, A, B, C, Ds, z
 
 
-def brute_force(u, delta, A, B, C, Dskip=None, z=None):
-    """y_t = sum_{s<=t} sum_n C_t[n] (prod_{k=s+1..t} Abar_k[n]) Bbar_s[n] u_s + D u_t, then the gate;
-    and the final state h[n] = sum_s (prod_{k=s+1..L-1} Abar_k[n]) Bbar_s[n] u_s.  Pure Python
-    loops in float64 -- O(L^2 N) per channel, for tiny inputs only."""
+def brute_force(u, delta, A, B, C, Dskip=None, z=None, h0=None):
+    """y_t = sum_n C_t[n] [(prod_{k=0..t} Abar_k[n]) h0[n] + sum_{s<=t} (prod_{k=s+1..t} Abar_k[n])
+    Bbar_s[n] u_s] + D u_t, then the gate; and the final state h[n] = (prod_k Abar_k[n]) h0[n] +
+    sum_s (prod_{k=s+1..L-1} Abar_k[n]) Bbar_s[n] u_s.  h0 (the initial state) defaults to zero.
+    Pure Python loops in float64 -- O(L^2 N) per channel, for tiny inputs only."""
     u = np.asarray(u, np.float64)
     delta = np.asarray(delta, np.float64)
     A = np.asarray(A, np.float64)
@@ -69,6 +70,8 @@ def brute_force(u, delta, A, B, C, Dskip=None, z=None):
             for t in range(L):
                 total = 0.0
                 for n in range(N):
+                    if h0 is not None:
+                        total += C[b, t, n] * decay(abar, -1, t, n) * float(h0[b, d, n])
                     for s in range(t + 1):
                         total += C[b, t, n] * decay(abar, s, t, n) * bbar[s][n] * u[b, s, d]
                 if Dskip is not None:
@@ -79,6 +82,8 @@ def brute_force(u, delta, A, B, C, Dskip=None, z=None):
                 y[b, t, d] = total
             for n in range(N):
                 last[b, d, n] = sum(decay(abar, s, L - 1, n) * bbar[s][n] * u[b, s, d] for s in range(L))
+                if h0 is not None:
+                    last[b, d, n] += decay(abar, -1, L - 1, n) * float(h0[b, d, n])
     return y, last
 
 
@@ -372,3 +377,67 @@ def test_empty_sequence_gives_zero_state():
     y, last = oracle.fwd(u, np.zeros((1, 0, 2), np.float32), A, np.zeros((1, 0, 3), np.float32),
                          np.zeros((1, 0, 3), np.float32))
     assert y.shape == (1, 0, 2) and last.shape == (1, 2, 3) and not last.any()
+
+
+# ---- initial state (continuation of a previous call; TorchLean "Selective Mamba", step /
+# runArray with an explicit state; aarnphm "One recurrence, one convolution": the recurrent form)
+
+def test_initial_state_zero_input_closed_form():
+    """A = -1, B = C = 1, delta = ln 2, no input, h0 = 1: the state halves every step, so
+    y_t = 2^-(t+1) exactly (the zero-input half of the aarnphm halving example)."""
+    L = 24
+    dt32 = np.float32(math.log(2.0))
+    y, last = oracle.fwd(np.zeros((1, L, 1), np.float32), np.full((1, L, 1), dt32, np.float32),
+                         -np.ones((1, 1), np.float32), np.ones((1, L, 1), np.float32),
+                         np.ones((1, L, 1), np.float32), h0=np.ones((1, 1, 1), np.float32))
+    # delta is the fp32 value nearest ln 2, so the exact decay per step is exp(-delta)
+    e = math.exp(-float(dt32))
+    np.testing.assert_allclose(y[0, :, 0], e ** (np.arange(L) + 1.0), rtol=1e-12, atol=0)
+    np.testing.assert_allclose(y[0, :, 0], 0.5 ** (np.arange(L) + 1.0), rtol=1e-7, atol=0)
+    assert abs(last[0, 0, 0] - e ** L) < 1e-12 * e ** L
+
+
+def test_initial_state_brute_force():
+    rng = np.random.default_rng(77)
+    b, L, D, N = 3, 7, 4, 3
+    u = rng.standard_normal((b, L, D)).astype(np.float32)
+    dl = np.exp(rng.uniform(np.log(1e-2), 0.0, (b, L, D))).astype(np.float32)
+    A = (-rng.uniform(0.2, 3.0, (D, N))).astype(np.float32)
+    A[2, 1] = 0.0
+    Bm = rng.standard_normal((b, L, N)).astype(np.float32)
+    Cm = rng.standard_normal((b, L, N)).astype(np.float32)
+    Ds = rng.standard_normal(D).astype(np.float32)
+    z = rng.standard_normal((b, L, D)).astype(np.float32)
+    h0 = rng.standard_normal((b, D, N)).astype(np.float32)
+    y, last = oracle.fwd(u, dl, A, Bm, Cm, Ds, z, h0=h0)
+    yb, lb = brute_force(u, dl, A, Bm, Cm, Ds, z, h0=h0)
+    assert rel_err(y, yb) < 1e-12 and rel_err(last, lb) < 1e-12
+
+
+def test_continuation_equals_concatenation():
+    """Two calls with the state carried (rounded to fp32, as the GPU library hands it over)
+    equal one call over the concatenated tokens."""
+    rng = np.random.default_rng(5)
+    b, L, D, N = 2, 40, 3, 4
+    u = rng.standard_normal((b, L, D)).astype(np.float32)
+    dl = np.exp(rng.uniform(np.log(1e-2), 0.0, (b, L, D))).astype(np.float32)
+    A = (-rng.uniform(0.2, 3.0, (D, N))).astype(np.float32)
+    Bm = rng.standard_normal((b, L, N)).astype(np.float32)
+    Cm = rng.standard_normal((b, L, N)).astype(np.float32)
+    Ds = np.ones(D, np.float32)
+    y, last = oracle.fwd(u, dl, A, Bm, Cm, Ds)
+    k = 17
+    y1, l1 = oracle.fwd(u[:, :k], dl[:, :k], A, Bm[:, :k], Cm[:, :k], Ds)
+    y2, l2 = oracle.fwd(u[:, k:], dl[:, k:], A, Bm[:, k:], Cm[:, k:], Ds, h0=l1.astype(np.float32))
+    assert np.array_equal(y1, y[:, :k])
+    assert rel_err(y2, y[:, k:]) < 1e-6 and rel_err(l2, last) < 1e-6
+
+
+def test_empty_call_hands_back_initial_state():
+    """No tokens: the state is handed back unchanged (TorchLean: an empty chunk preserves
+    the state)."""
+    h0 = np.arange(2 * 3 * 4, dtype=np.float32).reshape(2, 3, 4) - 5.0
+    e = np.zeros((2, 0, 3), np.float32)
+    _, last = oracle.fwd(e, e, -np.ones((3, 4), np.float32), np.zeros((2, 0, 4), np.float32),
+                         np.zeros((2, 0, 4), np.float32), h0=h0)
+    assert np.array_equal(last, h0.astype(np.float64))
