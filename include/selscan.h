@@ -171,6 +171,46 @@ int selective_scan_fwd_ws(const void* u, const void* delta, const float* A, cons
                           float* last_state, const selscan_dims* dims, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * selective_scan_fwd_ex -- the forward pass continuing from a given state.
+ *   initial_state  : [batch][dim][dstate] fp32, the state h_{-1} the sequence starts from,
+ *                    or NULL for the zero state (then this is selective_scan_fwd /
+ *                    selective_scan_fwd_ws).  It may be the same buffer as last_state
+ *                    (continue in place): it is read before last_state is written; any
+ *                    other overlap with an output is undefined.  Selective coefficients
+ *                    only: with time-invariant ones a non-NULL initial_state returns
+ *                    SELSCAN_ERR_UNSUPPORTED.
+ *   workspace, workspace_bytes : as selective_scan_fwd_ws; a NULL workspace makes the call
+ *                    take it stream-ordered on `stream` when the chunked path needs it.
+ *   Other arguments as selective_scan_fwd.
+ * seqlen == 0 copies initial_state (zeros if NULL) to last_state.
+ * A call over tokens [0, k) followed by a call over [k, L) whose initial_state is the
+ * first call's last_state gives the result of one call over [0, L), up to the fp32
+ * rounding of the carried state (TorchLean "Selective Mamba": step and runArray carry an
+ * explicit hidden state from one chunk to the next).
+ */
+int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                          const void* C, const float* Dskip, const void* z, void* y,
+                          const float* initial_state, float* last_state, const selscan_dims* dims,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * selective_scan_step -- one recurrent decode step: the forward pass over a single token
+ * per batch row, updating the running state in place (aarnphm "state-space models", section
+ * "One recurrence, one convolution": the recurrent form yields one output per step from
+ * the state; chipfoundry glossary, "Computational Considerations": a fixed-size state per
+ * generated token).
+ *   dims   : dims->seqlen must be 1 (else SELSCAN_ERR_DIMS); strides as for the forward
+ *            pass (token strides are not used); both coefficient patterns are supported;
+ *            dims->path and dims->chunk_len are ignored.
+ *   state  : [batch][dim][dstate] fp32, required: read as h_{-1}, overwritten with h_0.
+ *   u, delta, A, B, C, Dskip, z, y : as selective_scan_fwd, for the one token.
+ * Never allocates.  Same status codes as selective_scan_fwd.
+ */
+int selective_scan_step(const void* u, const void* delta, const float* A, const void* B,
+                        const void* C, const float* Dskip, const void* z, void* y, float* state,
+                        const selscan_dims* dims, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* selective_scan_strerror(int status);
 

@@ -68,6 +68,8 @@ _SIGNATURES = [
     ("selective_scan_fwd", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP]),
     ("selective_scan_workspace_size", ctypes.c_size_t, [ctypes.POINTER(SelscanDims)]),
     ("selective_scan_fwd_ws", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
+    ("selective_scan_fwd_ex", ctypes.c_int, [_VP] * 10 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
+    ("selective_scan_step", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP]),
     ("selective_scan_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("selective_scan_last_hip_error", ctypes.c_int, []),
     ("selective_scan_abi_version", ctypes.c_int, []),
@@ -181,11 +183,15 @@ def make_dims(u, delta, A, B, C, z=None, y=None, *, path: str = "auto", chunk_le
 
 
 def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state=None, *,
-                       return_last_state: bool = False, path: str = "auto", chunk_len: int = 0,
-                       scalar_io: bool = False, workspace=None, stream=None) -> Tuple["object", Optional["object"]]:
+                       initial_state=None, return_last_state: bool = False, path: str = "auto",
+                       chunk_len: int = 0, scalar_io: bool = False, workspace=None,
+                       stream=None) -> Tuple["object", Optional["object"]]:
     """Selective-scan forward on the GPU.  Returns (y, last_state or None).
 
     ``y`` / ``last_state`` may be given (outputs are written in place) or are allocated.
+    ``initial_state`` ([batch, D, N] float32, selective coefficients only) is the state the
+    sequence continues from; it may be the ``last_state`` tensor itself (continue in place).
+
     ``workspace`` (a uint8 CUDA tensor of at least ``workspace_size`` bytes) selects the
     non-allocating entry point; when it is omitted and the call needs one, it is taken from
     torch's caching allocator.  ``stream`` defaults to torch's current stream."""
@@ -208,9 +214,10 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
     N = int(A.shape[1])
     if last_state is None and return_last_state:
         last_state = torch.empty((batch, D, N), dtype=torch.float32, device=u.device)
-    if last_state is not None and (last_state.dtype != torch.float32 or not last_state.is_contiguous()
-                                   or tuple(last_state.shape) != (batch, D, N)):
-        raise ValueError("last_state must be a contiguous float32 [batch, D, N] tensor")
+    for name, t in (("last_state", last_state), ("initial_state", initial_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (batch, D, N)
+                              or not t.is_cuda):
+            raise ValueError("%s must be a contiguous float32 [batch, D, N] GPU tensor" % name)
     dims = make_dims(u, delta, A, B, C, z, y, path=path, chunk_len=chunk_len, scalar_io=scalar_io)
     torch_stream = stream if (stream is None or hasattr(stream, "cuda_stream")) else None
     if stream is None:
@@ -226,6 +233,15 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
             workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
             if torch_stream is not None:
                 workspace.record_stream(torch_stream)
+    if initial_state is not None:
+        ws_args = ((_ptr(workspace), int(workspace.numel() * workspace.element_size())) if workspace is not None
+                   else (None, 0))
+        st = lib().selective_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
+                                         _ptr(y), _ptr(initial_state), _ptr(last_state), ctypes.byref(dims),
+                                         ws_args[0], ws_args[1], ctypes.c_void_p(stream))
+        if st != SELSCAN_OK:
+            raise SelscanError(st, "selective_scan_fwd_ex")
+        return y, last_state
     args = [_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(y), _ptr(last_state),
             ctypes.byref(dims)]
     if workspace is not None:
@@ -240,5 +256,78 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
     return y, last_state
 
 
-__all__ = ["selective_scan_fwd", "make_dims", "dims_init", "workspace_size", "strerror", "last_hip_error",
+def selective_scan_step(u, delta, A, B, C, Dskip=None, z=None, y=None, *, state, time_invariant: bool = False,
+                        stream=None):
+    """One recurrent decode step (one token per batch row); ``state`` ([batch, D, N] float32,
+    contiguous) is read as the running state and overwritten with the new one.
+
+    u, z, y: [batch, D]; A: [D, N]; Dskip: [D].  Selective coefficients: delta [batch, D]
+    (or [D] shared by the batch), B, C [batch, N].  time_invariant=True: delta [D], B, C
+    [D, N].  Returns y."""
+    import torch
+    if u.dim() != 2:
+        raise ValueError("u must be [batch, D] (one token per batch row)")
+    batch, D = (int(x) for x in u.shape)
+    if A.dim() != 2 or int(A.shape[0]) != D or A.dtype != torch.float32 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous float32 [D, N] tensor")
+    N = int(A.shape[1])
+    io = u.dtype
+    if y is None:
+        y = torch.empty((batch, D), dtype=io, device=u.device)
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
+        if t is not None and (t.dtype != io or not t.is_cuda):
+            raise TypeError("%s must be a GPU tensor of dtype %s like u" % (name, io))
+    if Dskip is not None and (Dskip.dtype != torch.float32 or not Dskip.is_contiguous() or not Dskip.is_cuda):
+        raise TypeError("Dskip must be a contiguous float32 [D] GPU tensor")
+    if (state.dtype != torch.float32 or not state.is_contiguous() or tuple(state.shape) != (batch, D, N)
+            or not state.is_cuda):
+        raise ValueError("state must be a contiguous float32 [batch, D, N] GPU tensor")
+
+    def rows(t, name, width):                  # [batch, width] with a unit-stride last axis
+        if t.dim() != 2 or tuple(t.shape) != (batch, width) or (width > 1 and t.stride(1) != 1):
+            raise ValueError("%s must be [batch, %d] with a unit-stride last axis" % (name, width))
+        return t.stride(0)
+
+    d = SelscanDims()
+    d.abi_version = SELSCAN_ABI_VERSION
+    d.io_dtype = _io_code(io)
+    d.batch, d.seqlen, d.dim, d.dstate = batch, 1, D, N
+    d.u_sb = rows(u, "u", D)
+    d.u_sl = D
+    d.y_sb = rows(y, "y", D)
+    d.y_sl = D                                 # rows of different batch entries must not overlap
+    if z is not None:
+        d.z_sb = rows(z, "z", D)
+        d.z_sl = D
+    if delta.dim() == 1:
+        if int(delta.shape[0]) != D or (D > 1 and delta.stride(0) != 1):
+            raise ValueError("per-channel delta must be a contiguous [D] tensor")
+        d.delta_sb = d.delta_sl = 0
+    else:
+        d.delta_sb = rows(delta, "delta", D)
+        d.delta_sl = D
+    if time_invariant and delta.dim() != 1:
+        raise ValueError("time-invariant coefficients take a per-channel [D] delta")
+    for name, t in (("B", B), ("C", C)):
+        if time_invariant:
+            if t.dim() != 2 or tuple(t.shape) != (D, N) or (N > 1 and t.stride(1) != 1):
+                raise ValueError("per-channel %s must be [D, N] with a unit-stride state axis" % name)
+            sb, sl, sd = 0, 0, t.stride(0)
+        else:
+            sb, sl, sd = rows(t, name, N), N, 0
+        setattr(d, name + "_sb", sb)
+        setattr(d, name + "_sl", sl)
+        setattr(d, name + "_sd", sd)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = lib().selective_scan_step(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(y),
+                                   _ptr(state), ctypes.byref(d), ctypes.c_void_p(stream))
+    if st != SELSCAN_OK:
+        raise SelscanError(st, "selective_scan_step")
+    return y
+
+
+__all__ = ["selective_scan_fwd", "selective_scan_step", "make_dims", "dims_init", "workspace_size", "strerror", "last_hip_error",
            "abi_version", "lib", "SelscanDims", "SelscanError", "LIB_PATH"]

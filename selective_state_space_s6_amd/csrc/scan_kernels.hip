@@ -195,6 +195,12 @@ void scan_kernel(ScanParams p) {
       const int64_t n = s + S * k;
       if (dvalid && n < N) h[k] = p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk];
     }
+  } else if (MODE == MODE_SINGLE && !TI && p.h0 != nullptr) {   // given initial state
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t n = s + S * k;
+      if (dvalid && n < N) h[k] = p.h0[(b * D + d) * N + n];
+    }
   }
 
   // ---- buffer resources.  Every per-token tensor is addressed through a buffer descriptor
@@ -665,6 +671,12 @@ void scan_kernel_coop(ScanParams p) {
       const int64_t n = s + S * k;
       if (dvalid && n < N) h[k] = p.ws_state[((b * D + d) * N + n) * p.n_chunks + chunk];
     }
+  } else if (MODE == MODE_SINGLE && !TI && p.h0 != nullptr) {   // given initial state
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t n = s + S * k;
+      if (dvalid && n < N) h[k] = p.h0[(b * D + d) * N + n];
+    }
   }
 
   // ---- buffer resources (see scan_kernel): based at the workgroup's first token and
@@ -979,7 +991,8 @@ void scan_kernel_coop(ScanParams p) {
 // Lanes of a segment are the chunks 0 .. n_chunks-1 (segment width W = pow2 >= n_chunks).
 // Chunk c's map is h -> P_c h + H_c with P_c = exp(A sum_{t in c} delta_t); an inclusive
 // log-depth scan composes (P1,H1).(P2,H2) = (P2 P1, P2 H1 + H2); the carried-in state of
-// chunk c is the composed H up to chunk c-1 (zero for chunk 0).
+// chunk c is the composed H up to chunk c-1 (the initial state for chunk 0, which also
+// enters chunk 0's map as P_0 h0 + H_0).
 
 __global__ __launch_bounds__(256)
 void chunk_prefix_kernel(PrefixParams p) {
@@ -989,7 +1002,7 @@ void chunk_prefix_kernel(PrefixParams p) {
   const int64_t seg = (int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6)) * (64 / W) + seg_in_wave;
   const int64_t nseg = p.batch * p.D * p.N;
   const bool live = seg < nseg && i < p.n_chunks;
-  float P = 1.f, H = 0.f;
+  float P = 1.f, H = 0.f, h0 = 0.f;
   int64_t b = 0, d = 0, n = 0;
   if (live) {
     n = seg % p.N;
@@ -999,6 +1012,10 @@ void chunk_prefix_kernel(PrefixParams p) {
     if (i < p.n_chunks - 1) {          // the last chunk's map is never used (nor computed)
       P = __builtin_amdgcn_exp2f(a2 * p.dsum[(b * p.D + d) * p.n_chunks + i]);
       H = p.state[seg * p.n_chunks + i];
+    }
+    if (p.h0 != nullptr) {             // a given initial state enters through chunk 0's map
+      h0 = p.h0[seg];
+      if (i == 0) H = fmaf(P, h0, H);
     }
   }
   for (int off = 1; off < W; off <<= 1) {
@@ -1010,7 +1027,7 @@ void chunk_prefix_kernel(PrefixParams p) {
     }
   }
   const float carry = __shfl_up(H, 1, W);
-  if (live) p.state[seg * p.n_chunks + i] = (i == 0) ? 0.f : carry;
+  if (live) p.state[seg * p.n_chunks + i] = (i == 0) ? h0 : carry;
 }
 
 // zero-fill (empty sequence: last_state = 0); a kernel, not a memset, so callers may
@@ -1019,6 +1036,76 @@ __global__ __launch_bounds__(256)
 void fill_zero_kernel(float* x, int64_t n) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
     x[i] = 0.f;
+}
+
+// copy (empty sequence with an initial state: last_state = initial_state)
+__global__ __launch_bounds__(256)
+void copy_kernel(float* dst, const float* src, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------------------
+// One recurrent decode step: a single token per batch row, state [batch][D][N] updated in
+// place (the recurrent form of the scan; aarnphm "state-space models", section "One
+// recurrence, one convolution").  Lane (c, s) of a wavefront owns states s, s+16, ... of
+// channel 4 g + c, so the state row of 4 channels is read and written as one contiguous
+// run; the readout is summed over the 16 lanes of a channel with cross-lane adds and lane
+// s == 0 applies the feed-through and the gate and stores y.  Moves state in and out once:
+// bound by HBM.
+template <typename IO, bool TI>
+__global__ __launch_bounds__(256)
+void step_kernel(StepParams p) {
+  using T = io_traits<IO>;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t groups = (p.D + 3) / 4;
+  if (wave >= p.batch * groups) return;                 // whole wavefront exits together
+  const int64_t b = wave / groups;
+  const int c = lane >> 4, s = lane & 15;
+  const int64_t d = (wave % groups) * 4 + c;
+  const bool dvalid = d < p.D;
+  const IO* const u = static_cast<const IO*>(p.u);
+  const IO* const dl = static_cast<const IO*>(p.delta);
+  const IO* const Bv = static_cast<const IO*>(p.B);
+  const IO* const Cv = static_cast<const IO*>(p.C);
+  float uu = 0.f, dt = 0.f, acc = 0.f;
+  if (dvalid) {
+    uu = T::widen(u[b * p.u_sb + d]);
+    dt = T::widen(TI ? dl[d] : dl[b * p.delta_sb + d]);
+    for (int64_t n = s; n < p.N; n += 16) {
+      const float a = p.A[d * p.N + n];
+      const float bv = T::widen(TI ? Bv[d * p.B_sd + n] : Bv[b * p.B_sb + n]);
+      const float cv = T::widen(TI ? Cv[d * p.C_sd + n] : Cv[b * p.C_sb + n]);
+      const float ab = __builtin_amdgcn_exp2f(dt * (a * kLog2e));            // Abar = exp(delta A)
+      const float ia = a != 0.f ? 1.0f / a : 0.f;
+      const float f = a != 0.f ? fmaf(ab, ia, -ia) : dt;                     // (Abar - 1)/A, or delta
+      float* const hp = p.state + (b * p.D + d) * p.N + n;
+      const float h = fmaf(ab, *hp, f * (bv * uu));                          // h = Abar h + Bbar u
+      *hp = h;
+      acc = fmaf(cv, h, acc);                                                // C . h
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);   // sum over the channel's lanes
+  if (dvalid && s == 0) {
+    float yv = acc;
+    if (p.Dskip != nullptr) yv = fmaf(p.Dskip[d], uu, yv);                   // + D u
+    if (p.z != nullptr) {
+      const float zz = T::widen(static_cast<const IO*>(p.z)[b * p.z_sb + d]);
+      yv *= zz * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));   // * SiLU(z)
+    }
+    IO* const y = static_cast<IO*>(p.y);
+    if (sizeof(IO) == 2) {
+      // round to nearest even; NaN stays a quiet NaN
+      const uint32_t x = __float_as_uint(yv);
+      const uint32_t rr = ((x & 0x7fffffffu) > 0x7f800000u) ? ((x >> 16) | 0x40u)
+                                                            : ((x + 0x7fffu + ((x >> 16) & 1u)) >> 16);
+      reinterpret_cast<uint16_t*>(y)[b * p.y_sb + d] = uint16_t(rr);
+    } else {
+      reinterpret_cast<float*>(y)[b * p.y_sb + d] = yv;
+    }
+  }
 }
 
 template <typename IO, int S, int K, bool TI, int MODE>
@@ -1103,6 +1190,28 @@ hipError_t launch_chunk_prefix(const PrefixParams& p, hipStream_t stream) {
   const int64_t waves = (segs + per_wave - 1) / per_wave;
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL(chunk_prefix_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(copy_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, dst, src, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_step(bool bf16, bool ti, const StepParams& p, hipStream_t stream) {
+  const int64_t waves = p.batch * ((p.D + 3) / 4);
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  if (bf16) {
+    if (ti) hipLaunchKernelGGL((step_kernel<uint16_t, true>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((step_kernel<uint16_t, false>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  } else {
+    if (ti) hipLaunchKernelGGL((step_kernel<float, true>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((step_kernel<float, false>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ struct ScanParams {
   const void* z;        // may be null
   void* y;
   float* last_state;    // may be null
+  const float* h0;      // initial state [batch][D][N], may be null (zero); selective only
   int64_t batch, L, D, N;
   int64_t u_sb, u_sl, delta_sb, delta_sl, z_sb, z_sl, y_sb, y_sl;
   int64_t B_sb, B_sl, B_sd, C_sb, C_sl, C_sd;
@@ -38,6 +39,7 @@ struct ScanParams {
 struct PrefixParams {
   const float* A;
   const float* dsum;
+  const float* h0;      // initial state [batch][D][N], may be null (zero)
   float* state;
   int64_t batch, D, N;
   int32_t n_chunks;
@@ -50,5 +52,22 @@ void lanes_for_states(int64_t N, int* S, int* K);
 hipError_t launch_scan_pass(int pass, bool bf16, bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
 hipError_t launch_chunk_prefix(const PrefixParams& p, hipStream_t stream);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream);
+hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream);
+
+// One decode step (seqlen 1), state updated in place.
+struct StepParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;   // may be null
+  const void* z;        // may be null
+  void* y;
+  float* state;         // [batch][D][N]
+  int64_t batch, D, N;
+  int64_t u_sb, delta_sb, z_sb, y_sb, B_sb, B_sd, C_sb, C_sd;
+};
+hipError_t launch_step(bool bf16, bool ti, const StepParams& p, hipStream_t stream);
 
 }  // namespace selscan

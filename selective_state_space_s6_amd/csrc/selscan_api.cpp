@@ -141,13 +141,14 @@ int check_pointers(const void* u, const void* delta, const float* A, const void*
 }
 
 int run(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* Dskip,
-        const void* z, void* y, float* last_state, const selscan_dims* dims, const Plan& plan, void* workspace,
-        hipStream_t stream) {
+        const void* z, void* y, const float* h0, float* last_state, const selscan_dims* dims, const Plan& plan,
+        void* workspace, hipStream_t stream) {
   const selscan_dims& d = *dims;
   if (d.batch == 0) return SELSCAN_OK;
-  if (d.seqlen == 0) {
-    if (last_state) {
-      hipError_t e = selscan::launch_fill_zero(last_state, d.batch * d.dim * d.dstate, stream);
+  if (d.seqlen == 0) {                     // no tokens: the initial state is handed back
+    if (last_state && last_state != h0) {
+      const int64_t n = d.batch * d.dim * d.dstate;
+      hipError_t e = h0 ? selscan::launch_copy(last_state, h0, n, stream) : selscan::launch_fill_zero(last_state, n, stream);
       if (e != hipSuccess) return hip_fail(e);
     }
     return SELSCAN_OK;
@@ -155,6 +156,7 @@ int run(const void* u, const void* delta, const float* A, const void* B, const v
   selscan::ScanParams p{};
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = z; p.y = y;
   p.last_state = last_state;
+  p.h0 = h0;
   p.batch = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = d.dstate;
   p.u_sb = d.u_sb; p.u_sl = d.u_sl; p.delta_sb = d.delta_sb; p.delta_sl = d.delta_sl;
   p.z_sb = d.z_sb; p.z_sl = d.z_sl; p.y_sb = d.y_sb; p.y_sl = d.y_sl;
@@ -187,7 +189,7 @@ int run(const void* u, const void* delta, const float* A, const void* B, const v
   e = selscan::launch_scan_pass(selscan::kPassState, plan.bf16, plan.ti, plan.S, plan.K, p, stream);
   if (e != hipSuccess) return hip_fail(e);
   selscan::PrefixParams q{};
-  q.A = A; q.dsum = p.ws_dsum; q.state = p.ws_state;
+  q.A = A; q.dsum = p.ws_dsum; q.state = p.ws_state; q.h0 = h0;
   q.batch = d.batch; q.D = d.dim; q.N = d.dstate; q.n_chunks = plan.n_chunks;
   int w = 1;
   while (w < plan.n_chunks) w <<= 1;
@@ -196,6 +198,35 @@ int run(const void* u, const void* delta, const float* A, const void* B, const v
   if (e != hipSuccess) return hip_fail(e);
   e = selscan::launch_scan_pass(selscan::kPassApply, plan.bf16, plan.ti, plan.S, plan.K, p, stream);
   return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+}
+
+// The forward pass with an optional initial state.  A missing workspace is allocated
+// stream-ordered when allow_alloc, else reported.
+int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* Dskip,
+             const void* z, void* y, const float* h0, float* last_state, const selscan_dims* dims, void* workspace,
+             size_t workspace_bytes, bool allow_alloc, hipStream_t stream) {
+  Plan plan;
+  int st = make_plan(dims, &plan);
+  if (st != SELSCAN_OK) return st;
+  st = check_pointers(u, delta, A, B, C, Dskip, z, y, last_state, dims->io_dtype, dims->batch * dims->seqlen == 0);
+  if (st != SELSCAN_OK) return st;
+  if (h0 != nullptr) {
+    if (plan.ti) return SELSCAN_ERR_UNSUPPORTED;      // the time-invariant kernels keep a scaled state
+    if (!aligned(h0, 4)) return SELSCAN_ERR_ALIGN;
+  }
+  const bool need_ws = plan.chunked && dims->batch > 0 && dims->seqlen > 0;
+  if (!need_ws || workspace != nullptr) {
+    if (need_ws && (workspace_bytes < plan.ws_bytes || !aligned(workspace, 256))) return SELSCAN_ERR_WORKSPACE;
+    return run(u, delta, A, B, C, Dskip, z, y, h0, last_state, dims, plan, workspace, stream);
+  }
+  if (!allow_alloc) return SELSCAN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  st = run(u, delta, A, B, C, Dskip, z, y, h0, last_state, dims, plan, ws, stream);
+  e = hipFreeAsync(ws, stream);
+  if (st == SELSCAN_OK && e != hipSuccess) return hip_fail(e);
+  return st;
 }
 
 }  // namespace
@@ -236,34 +267,43 @@ size_t selective_scan_workspace_size(const selscan_dims* dims) {
 int selective_scan_fwd_ws(const void* u, const void* delta, const float* A, const void* B, const void* C,
                           const float* Dskip, const void* z, void* y, float* last_state, const selscan_dims* dims,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  Plan plan;
-  int st = make_plan(dims, &plan);
-  if (st != SELSCAN_OK) return st;
-  st = check_pointers(u, delta, A, B, C, Dskip, z, y, last_state, dims->io_dtype, dims->batch * dims->seqlen == 0);
-  if (st != SELSCAN_OK) return st;
-  if (plan.chunked && dims->batch > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 256)))
-    return SELSCAN_ERR_WORKSPACE;
-  return run(u, delta, A, B, C, Dskip, z, y, last_state, dims, plan, workspace, static_cast<hipStream_t>(stream));
+  return fwd_impl(u, delta, A, B, C, Dskip, z, y, nullptr, last_state, dims, workspace, workspace_bytes, false,
+                  static_cast<hipStream_t>(stream));
 }
 
 int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                        const float* Dskip, const void* z, void* y, float* last_state, const selscan_dims* dims,
                        void* stream) {
+  return fwd_impl(u, delta, A, B, C, Dskip, z, y, nullptr, last_state, dims, nullptr, 0, true,
+                  static_cast<hipStream_t>(stream));
+}
+
+int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                          const float* Dskip, const void* z, void* y, const float* initial_state, float* last_state,
+                          const selscan_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(u, delta, A, B, C, Dskip, z, y, initial_state, last_state, dims, workspace, workspace_bytes,
+                  workspace == nullptr, static_cast<hipStream_t>(stream));
+}
+
+int selective_scan_step(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                        const float* Dskip, const void* z, void* y, float* state, const selscan_dims* dims,
+                        void* stream) {
   Plan plan;
   int st = make_plan(dims, &plan);
   if (st != SELSCAN_OK) return st;
-  st = check_pointers(u, delta, A, B, C, Dskip, z, y, last_state, dims->io_dtype, dims->batch * dims->seqlen == 0);
+  if (dims->seqlen != 1) return SELSCAN_ERR_DIMS;
+  if (!state) return SELSCAN_ERR_NULL;
+  st = check_pointers(u, delta, A, B, C, Dskip, z, y, state, dims->io_dtype, dims->batch == 0);
   if (st != SELSCAN_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!plan.chunked || dims->batch == 0)
-    return run(u, delta, A, B, C, Dskip, z, y, last_state, dims, plan, nullptr, s);
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, s);
-  if (e != hipSuccess) return hip_fail(e);
-  st = run(u, delta, A, B, C, Dskip, z, y, last_state, dims, plan, ws, s);
-  e = hipFreeAsync(ws, s);
-  if (st == SELSCAN_OK && e != hipSuccess) return hip_fail(e);
-  return st;
+  if (dims->batch * ((dims->dim + 3) / 4) > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return SELSCAN_OK;
+  selscan::StepParams q{};
+  q.u = u; q.delta = delta; q.A = A; q.B = B; q.C = C; q.Dskip = Dskip; q.z = z; q.y = y; q.state = state;
+  q.batch = dims->batch; q.D = dims->dim; q.N = dims->dstate;
+  q.u_sb = dims->u_sb; q.delta_sb = dims->delta_sb; q.z_sb = dims->z_sb; q.y_sb = dims->y_sb;
+  q.B_sb = dims->B_sb; q.B_sd = dims->B_sd; q.C_sb = dims->C_sb; q.C_sd = dims->C_sd;
+  const hipError_t e = selscan::launch_step(plan.bf16, plan.ti, q, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
 }
 
 const char* selective_scan_strerror(int status) {

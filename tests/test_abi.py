@@ -149,3 +149,32 @@ def test_auto_path_chunks_only_when_underfilled():
 def test_empty_batch_is_a_no_op():
     d = good_dims(batch=0)
     assert call(d) == ss.SELSCAN_OK                    # nothing enqueued, no workspace needed
+
+
+def call_ex(dims, h0=FAKE, ws=None, ws_bytes=0):
+    return ss.lib().selective_scan_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, h0, None,
+                                          ctypes.byref(dims), ws, ws_bytes, None)
+
+
+def test_initial_state_errors():
+    ti = ss.dims_init(ss.SELSCAN_F32, 2, 64, 8, 16, time_invariant=True)
+    assert call_ex(ti) == ss.SELSCAN_ERR_UNSUPPORTED           # time-invariant + initial state
+    assert call_ex(good_dims(), h0=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
+    d = good_dims()                                            # chunked path, workspace too small
+    assert call_ex(d, ws=FAKE, ws_bytes=ss.workspace_size(d) - 1) == ss.SELSCAN_ERR_WORKSPACE
+    bad = good_dims(dstate=0)
+    assert call_ex(bad) == ss.SELSCAN_ERR_DIMS
+
+
+def call_step(dims, state=FAKE):
+    return ss.lib().selective_scan_step(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, state, ctypes.byref(dims),
+                                        None)
+
+
+def test_step_errors():
+    assert call_step(ss.dims_init(ss.SELSCAN_F32, 2, 2, 8, 16)) == ss.SELSCAN_ERR_DIMS    # seqlen != 1
+    one = ss.dims_init(ss.SELSCAN_F32, 2, 1, 8, 16)
+    assert call_step(one, state=None) == ss.SELSCAN_ERR_NULL
+    assert call_step(one, state=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
+    assert call_step(ss.dims_init(ss.SELSCAN_F32, 2, 1, 8, 65)) == ss.SELSCAN_ERR_UNSUPPORTED
+    assert call_step(ss.dims_init(ss.SELSCAN_F32, 0, 1, 8, 16)) == ss.SELSCAN_OK             # empty batch
