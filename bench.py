@@ -65,6 +65,17 @@ def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool) -> int:
     return total
 
 
+def decode_bytes(inp: s6_workloads.Inputs) -> int:
+    """One decode step: the running state [batch, D, N] fp32 read and written once; u,
+    delta, z read and y written per (b, d); B, C per (b, n); A, Dskip once."""
+    b, _, D, N = inp.shape
+    es = 2 if inp.io == "bf16" else 4
+    total = 2 * b * D * N * 4
+    total += b * D * es * (3 + (1 if inp.z is not None else 0))
+    total += 2 * b * N * es + D * N * 4 + (D * 4 if inp.Dskip is not None else 0)
+    return total
+
+
 def algorithmic_slots(inp: s6_workloads.Inputs) -> int:
     b, L, D, N = inp.shape
     per_el = SLOTS_PER_ELEMENT["time_invariant" if inp.ti else "selective"]
@@ -95,9 +106,9 @@ def measured_traffic(workload: str, per_launch_alg_bytes: int):
     return int(entry["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0):
+def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0, h0=None):
     """The oracle (fp64, as it stands) on a bounded sample of the workload's channels,
-    timed on this host; scaled to elements/s."""
+    timed on this host; scaled to elements/s.  ``h0``: initial state [batch, D, N]."""
     import oracle
     cores = min(16, os.cpu_count() or 1)
     b, L, D, N = inp.shape
@@ -109,7 +120,8 @@ def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0):
         sub = s6_workloads.select_channels(inp, ch)
         t0 = time.perf_counter()
         oracle.fwd(sub.u, sub.delta, sub.A, sub.B, sub.C, sub.Dskip, sub.z, time_invariant=sub.ti,
-                   want_last=False, nthreads=cores)
+                   h0=None if h0 is None else np.ascontiguousarray(h0[:, ch]), want_last=h0 is not None,
+                   nthreads=cores)
         t_used = time.perf_counter() - t0
         if t_used >= target_s * 0.5 or nch >= D:
             break
@@ -134,8 +146,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the scan shards over batch/channels with no "
-              "communication; see DESIGN.md); --gpus %d is not supported" % max(args.gpus, world), file=sys.stderr)
+        print("bench.py: measures one GPU only (the scan shards over batch/channels with no "
+              "communication, or over the sequence with one exchange of per-segment state maps); --gpus %d is not "
+              "supported" % max(args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -143,6 +156,8 @@ def main():
 
     spec = s6_workloads.spec(args.workload)
     inp = s6_workloads.generate(args.workload)
+    if spec.get("decode"):
+        return bench_decode(args, inp)
     want_last = bool(spec["last"])
     b, L, D, N = inp.shape
     E = b * L * D * N
@@ -234,6 +249,88 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+def roofline(alg_bytes: int, slots: int, seconds: float, traffic):
+    """The binding roof (the larger of the two lower bounds on time) and the fraction of it."""
+    hbm_gbs = alg_bytes / seconds / 1e9
+    alu_tflops = 2.0 * slots / seconds / 1e12
+    if 2.0 * slots / (VALU_PEAK_TFLOPS * 1e12) >= alg_bytes / (HBM_PEAK_GBS * 1e9):
+        return {"bound": "alu", "achieved": round(alu_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(alu_tflops / VALU_PEAK_TFLOPS, 4), "traffic": traffic}
+    return {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def bench_decode(args, inp):
+    """One recurrent decode step per call (selective_scan_step) over the workload's batch:
+    one token per batch row, the running state updated in place."""
+    import torch
+    import selective_state_space_s6_amd as ss
+    b, _, D, N = inp.shape
+    io = inp.io
+
+    def dev(x):
+        if x is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(x[:, 0], dtype=np.float32)).cuda()
+        return t.to(torch.bfloat16) if io == "bf16" else t
+
+    u, delta, B, C, z = dev(inp.u), dev(inp.delta), dev(inp.B), dev(inp.C), dev(inp.z)
+    A = torch.from_numpy(inp.A).cuda()
+    Ds = None if inp.Dskip is None else torch.from_numpy(inp.Dskip).cuda()
+    h0 = s6_workloads.running_state(inp)
+    state = torch.from_numpy(h0).cuda()
+    y = torch.empty_like(u)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ss.selective_scan_step(u, delta, A, B, C, Ds, z, y=y, state=state, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+    E = b * D * N
+    alg = decode_bytes(inp)
+    slots = algorithmic_slots(inp)
+    out = {
+        "metric": METRIC,
+        "value": E * args.steps / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, s6_workloads: %s)" % args.workload,
+        "config": {"workload": args.workload, "batch": b, "seq_len": 1, "dim": D, "dstate": N, "io": io,
+                   "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
+                   "mode": "decode step (state in place)"},
+        "kernel_ms": launch_ms,
+        "hbm_gbs": round(alg / (launch_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(alg / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": alg,
+        "algorithmic_slots": slots,
+        "roofline": roofline(alg, slots, launch_ms * 1e-3, measured_traffic(args.workload, alg)),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, h0=h0)
     print(json.dumps(out), flush=True)
 
 

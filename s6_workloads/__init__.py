@@ -33,6 +33,10 @@ WORKLOADS = {
                          ti=False, a_scale=1.0, delta="softplus_normal"),
     "s4d_ti_f32": dict(number=5, batch=4, L=8192, D=1024, N=64, io="f32", gate=False, last=False, ti=True,
                        a_scale=0.5, delta="loguniform"),
+    # one recurrent decode step for 512 sequences of the long-context model's width: one
+    # token per batch row, the running state [512, 2560, 16] fp32 read and written once
+    "decode_bf16": dict(number=6, batch=512, L=1, D=2560, N=16, io="bf16", gate=True, last=True, ti=False,
+                        a_scale=1.0, delta="softplus_normal", decode=True),
 }
 
 VARIANTS = ("default", "scan_only", "active", "active_const")
@@ -140,6 +144,14 @@ def generate(name: str, variant: str = "default", *, seed: Optional[int] = None,
         Dskip, z = None, None
     return Inputs(name=name, io=s["io"], ti=ti, u=u, delta=delta, A=A, B=B, C=C, Dskip=Dskip, z=z,
                   want_last=s["last"])
+
+
+def running_state(inp: Inputs, seed: int = 11, scale: float = 0.1) -> np.ndarray:
+    """A seeded [batch, D, N] float32 state to continue from (the decode workload's running
+    state): normal with standard deviation ``scale``."""
+    b, _, D, N = inp.shape
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.ascontiguousarray(rng.standard_normal((b, D, N)) * scale, dtype=np.float32)
 
 
 def sample_channels(D: int, count: int, seed: int = 7) -> np.ndarray:
