@@ -1048,64 +1048,147 @@ void copy_kernel(float* dst, const float* src, int64_t n) {
 // ---------------------------------------------------------------------------------------
 // One recurrent decode step: a single token per batch row, state [batch][D][N] updated in
 // place (the recurrent form of the scan; aarnphm "state-space models", section "One
-// recurrence, one convolution").  Lane (c, s) of a wavefront owns states s, s+16, ... of
-// channel 4 g + c, so the state row of 4 channels is read and written as one contiguous
-// run; the readout is summed over the 16 lanes of a channel with cross-lane adds and lane
-// s == 0 applies the feed-through and the gate and stores y.  Moves state in and out once:
-// bound by HBM.
-template <typename IO, bool TI>
+// recurrence, one convolution").  Moves the state in and out once: bound by HBM.
+// Lane (c, s) owns states 4s .. 4s+3 of channel c of the wavefront's channel group (SL
+// lanes per channel, 64/SL channels), so a channel's state row moves as 16-byte accesses;
+// A and its derived constants stay in registers while the wavefront walks kStepRows batch
+// rows, issuing every row's loads before computing any.  The readout is summed over the
+// SL lanes of a channel with cross-lane adds; lane s == 0 adds the feed-through, applies
+// the gate and stores y.
+constexpr int kStepRows = 2;   // measured: 2 rows per wavefront beat 1, 4 and 8 (more loads in flight vs more waves)
+
+// VEC: N % 4 == 0 and state / B / C rows aligned to 4 elements, so a lane's 4 states and
+// its 4 B and C values move as one access each.
+template <typename IO, bool TI, int SL, bool VEC>
 __global__ __launch_bounds__(256)
 void step_kernel(StepParams p) {
   using T = io_traits<IO>;
+  using Qd = quad_io<IO>;
+  constexpr int CW = 64 / SL;
   const int lane = threadIdx.x & 63;
   const int64_t wave = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int64_t groups = (p.D + 3) / 4;
-  if (wave >= p.batch * groups) return;                 // whole wavefront exits together
-  const int64_t b = wave / groups;
-  const int c = lane >> 4, s = lane & 15;
-  const int64_t d = (wave % groups) * 4 + c;
+  const int64_t groups = (p.D + CW - 1) / CW;
+  const int64_t rowblocks = (p.batch + kStepRows - 1) / kStepRows;
+  if (wave >= groups * rowblocks) return;               // whole wavefront exits together
+  const int64_t g = wave % groups, b0 = (wave / groups) * kStepRows;
+  const int c = lane / SL, s = lane % SL;
+  const int64_t d = g * CW + c;
   const bool dvalid = d < p.D;
-  const IO* const u = static_cast<const IO*>(p.u);
-  const IO* const dl = static_cast<const IO*>(p.delta);
-  const IO* const Bv = static_cast<const IO*>(p.B);
-  const IO* const Cv = static_cast<const IO*>(p.C);
-  float uu = 0.f, dt = 0.f, acc = 0.f;
-  if (dvalid) {
-    uu = T::widen(u[b * p.u_sb + d]);
-    dt = T::widen(TI ? dl[d] : dl[b * p.delta_sb + d]);
-    for (int64_t n = s; n < p.N; n += 16) {
-      const float a = p.A[d * p.N + n];
-      const float bv = T::widen(TI ? Bv[d * p.B_sd + n] : Bv[b * p.B_sb + n]);
-      const float cv = T::widen(TI ? Cv[d * p.C_sd + n] : Cv[b * p.C_sb + n]);
-      const float ab = __builtin_amdgcn_exp2f(dt * (a * kLog2e));            // Abar = exp(delta A)
-      const float ia = a != 0.f ? 1.0f / a : 0.f;
-      const float f = a != 0.f ? fmaf(ab, ia, -ia) : dt;                     // (Abar - 1)/A, or delta
-      float* const hp = p.state + (b * p.D + d) * p.N + n;
-      const float h = fmaf(ab, *hp, f * (bv * uu));                          // h = Abar h + Bbar u
-      *hp = h;
-      acc = fmaf(cv, h, acc);                                                // C . h
-    }
-  }
+  const IO* __restrict__ const u = static_cast<const IO*>(p.u);
+  const IO* __restrict__ const dl = static_cast<const IO*>(p.delta);
+  const IO* __restrict__ const Bv = static_cast<const IO*>(p.B);
+  const IO* __restrict__ const Cv = static_cast<const IO*>(p.C);
+  const IO* __restrict__ const zv = static_cast<const IO*>(p.z);
+  float* __restrict__ const st = p.state;
+
+  // per-lane constants of the 4 owned states
+  float A2[4], iA[4], zf[4], Bt[4], Ct[4];
+  bool nok[4];
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);   // sum over the channel's lanes
-  if (dvalid && s == 0) {
-    float yv = acc;
-    if (p.Dskip != nullptr) yv = fmaf(p.Dskip[d], uu, yv);                   // + D u
-    if (p.z != nullptr) {
-      const float zz = T::widen(static_cast<const IO*>(p.z)[b * p.z_sb + d]);
-      yv *= zz * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));   // * SiLU(z)
-    }
-    IO* const y = static_cast<IO*>(p.y);
-    if (sizeof(IO) == 2) {
-      // round to nearest even; NaN stays a quiet NaN
-      const uint32_t x = __float_as_uint(yv);
-      const uint32_t rr = ((x & 0x7fffffffu) > 0x7f800000u) ? ((x >> 16) | 0x40u)
-                                                            : ((x + 0x7fffu + ((x >> 16) & 1u)) >> 16);
-      reinterpret_cast<uint16_t*>(y)[b * p.y_sb + d] = uint16_t(rr);
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = 4 * s + j;
+    nok[j] = dvalid && n < p.N;
+    const float a = nok[j] ? p.A[d * p.N + n] : 0.f;
+    A2[j] = a * kLog2e;
+    iA[j] = a != 0.f ? 1.0f / a : 0.f;
+    zf[j] = (nok[j] && a == 0.f) ? 1.f : 0.f;
+    Bt[j] = (TI && nok[j]) ? T::widen(Bv[d * p.B_sd + n]) : 0.f;
+    Ct[j] = (TI && nok[j]) ? T::widen(Cv[d * p.C_sd + n]) : 0.f;
+  }
+  const float dskip = (dvalid && p.Dskip != nullptr) ? p.Dskip[d] : 0.f;
+  const float dt_ti = (TI && dvalid) ? T::widen(dl[d]) : 0.f;
+
+  // loads of all rows first
+  float uu[kStepRows], dt[kStepRows], zz[kStepRows], h[kStepRows][4], bb[kStepRows][4], cc[kStepRows][4];
+#pragma unroll
+  for (int r = 0; r < kStepRows; ++r) {
+    const int64_t b = b0 + r;
+    const bool live = dvalid && b < p.batch;
+    uu[r] = live ? T::widen(u[b * p.u_sb + d]) : 0.f;
+    dt[r] = TI ? dt_ti : (live ? T::widen(dl[b * p.delta_sb + d]) : 0.f);
+    zz[r] = (live && zv != nullptr) ? T::widen(zv[b * p.z_sb + d]) : 0.f;
+    if (VEC) {                                                   // all 4 states valid or none
+      if (live && nok[0]) {
+        const float4 hv = *reinterpret_cast<const float4*>(st + (b * p.D + d) * p.N + 4 * s);
+        h[r][0] = hv.x; h[r][1] = hv.y; h[r][2] = hv.z; h[r][3] = hv.w;
+        if (!TI) {
+          const typename Qd::raw_t bq = *reinterpret_cast<const typename Qd::raw_t*>(Bv + b * p.B_sb + 4 * s);
+          const typename Qd::raw_t cq = *reinterpret_cast<const typename Qd::raw_t*>(Cv + b * p.C_sb + 4 * s);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { bb[r][j] = Qd::get(bq, j); cc[r][j] = Qd::get(cq, j); }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { h[r][j] = 0.f; bb[r][j] = 0.f; cc[r][j] = 0.f; }
+      }
+      if (TI) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { bb[r][j] = Bt[j]; cc[r][j] = Ct[j]; }
+      }
     } else {
-      reinterpret_cast<float*>(y)[b * p.y_sb + d] = yv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = 4 * s + j;
+        const bool ok = live && nok[j];
+        h[r][j] = ok ? st[(b * p.D + d) * p.N + n] : 0.f;
+        bb[r][j] = TI ? Bt[j] : (ok ? T::widen(Bv[b * p.B_sb + n]) : 0.f);
+        cc[r][j] = TI ? Ct[j] : (ok ? T::widen(Cv[b * p.C_sb + n]) : 0.f);
+      }
     }
   }
+  IO* __restrict__ const y = static_cast<IO*>(p.y);
+#pragma unroll
+  for (int r = 0; r < kStepRows; ++r) {
+    const int64_t b = b0 + r;
+    const bool live = dvalid && b < p.batch;
+    float acc = 0.f, hn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float ab = __builtin_amdgcn_exp2f(dt[r] * A2[j]);               // Abar = exp(delta A)
+      const float f = fmaf(dt[r], zf[j], fmaf(ab, iA[j], -iA[j]));          // (Abar - 1)/A, or delta
+      hn[j] = fmaf(ab, h[r][j], f * (bb[r][j] * uu[r]));                    // h = Abar h + Bbar u
+      acc = fmaf(cc[r][j], hn[j], acc);                                     // C . h
+      if (!VEC && live && nok[j]) st[(b * p.D + d) * p.N + 4 * s + j] = hn[j];
+    }
+    if (VEC && live && nok[0])
+      *reinterpret_cast<float4*>(st + (b * p.D + d) * p.N + 4 * s) = make_float4(hn[0], hn[1], hn[2], hn[3]);
+#pragma unroll
+    for (int off = SL / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, SL);   // sum over the channel's lanes
+    if (live && s == 0) {
+      float yv = fmaf(dskip, uu[r], acc);                                   // + D u
+      if (zv != nullptr) yv *= zz[r] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz[r] * kLog2e));   // * SiLU(z)
+      if (sizeof(IO) == 2) {
+        // round to nearest even; NaN stays a quiet NaN
+        const uint32_t x = __float_as_uint(yv);
+        const uint32_t rr = ((x & 0x7fffffffu) > 0x7f800000u) ? ((x >> 16) | 0x40u)
+                                                              : ((x + 0x7fffu + ((x >> 16) & 1u)) >> 16);
+        reinterpret_cast<uint16_t*>(y)[b * p.y_sb + d] = uint16_t(rr);
+      } else {
+        reinterpret_cast<float*>(y)[b * p.y_sb + d] = yv;
+      }
+    }
+  }
+}
+
+template <typename IO, bool TI, int SL>
+hipError_t launch_step_sl(const StepParams& p, hipStream_t stream) {
+  constexpr int CW = 64 / SL;
+  const int64_t waves = ((p.D + CW - 1) / CW) * ((p.batch + kStepRows - 1) / kStepRows);
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  if (p.vec) hipLaunchKernelGGL((step_kernel<IO, TI, SL, true>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((step_kernel<IO, TI, SL, false>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename IO, bool TI>
+hipError_t launch_step_t(const StepParams& p, hipStream_t stream) {
+  const int64_t quads = (p.N + 3) / 4;                  // lanes per channel: 4 states each
+  if (quads <= 1) return launch_step_sl<IO, TI, 1>(p, stream);
+  if (quads <= 2) return launch_step_sl<IO, TI, 2>(p, stream);
+  if (quads <= 4) return launch_step_sl<IO, TI, 4>(p, stream);
+  if (quads <= 8) return launch_step_sl<IO, TI, 8>(p, stream);
+  return launch_step_sl<IO, TI, 16>(p, stream);
 }
 
 template <typename IO, int S, int K, bool TI, int MODE>
@@ -1202,17 +1285,8 @@ hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stre
 }
 
 hipError_t launch_step(bool bf16, bool ti, const StepParams& p, hipStream_t stream) {
-  const int64_t waves = p.batch * ((p.D + 3) / 4);
-  const int64_t blocks = (waves + 3) / 4;
-  if (blocks == 0) return hipSuccess;
-  if (bf16) {
-    if (ti) hipLaunchKernelGGL((step_kernel<uint16_t, true>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((step_kernel<uint16_t, false>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
-  } else {
-    if (ti) hipLaunchKernelGGL((step_kernel<float, true>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((step_kernel<float, false>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
-  }
-  return hipGetLastError();
+  if (bf16) return ti ? launch_step_t<uint16_t, true>(p, stream) : launch_step_t<uint16_t, false>(p, stream);
+  return ti ? launch_step_t<float, true>(p, stream) : launch_step_t<float, false>(p, stream);
 }
 
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream) {

@@ -67,6 +67,7 @@ struct StepParams {
   float* state;         // [batch][D][N]
   int64_t batch, D, N;
   int64_t u_sb, delta_sb, z_sb, y_sb, B_sb, B_sd, C_sb, C_sd;
+  int32_t vec;          // 1: N % 4 == 0, state and per-token B/C rows aligned to 4 elements
 };
 hipError_t launch_step(bool bf16, bool ti, const StepParams& p, hipStream_t stream);
 

@@ -295,13 +295,18 @@ int selective_scan_step(const void* u, const void* delta, const float* A, const 
   if (!state) return SELSCAN_ERR_NULL;
   st = check_pointers(u, delta, A, B, C, Dskip, z, y, state, dims->io_dtype, dims->batch == 0);
   if (st != SELSCAN_OK) return st;
-  if (dims->batch * ((dims->dim + 3) / 4) > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
+  if (dims->batch * dims->dim > (int64_t(1) << 36)) return SELSCAN_ERR_UNSUPPORTED;   // grid size
   if (dims->batch == 0) return SELSCAN_OK;
   selscan::StepParams q{};
   q.u = u; q.delta = delta; q.A = A; q.B = B; q.C = C; q.Dskip = Dskip; q.z = z; q.y = y; q.state = state;
   q.batch = dims->batch; q.D = dims->dim; q.N = dims->dstate;
   q.u_sb = dims->u_sb; q.delta_sb = dims->delta_sb; q.z_sb = dims->z_sb; q.y_sb = dims->y_sb;
   q.B_sb = dims->B_sb; q.B_sd = dims->B_sd; q.C_sb = dims->C_sb; q.C_sd = dims->C_sd;
+  {
+    const uintptr_t qb = uintptr_t(4) * (plan.bf16 ? 2 : 4);
+    const bool bc_vec = plan.ti || (aligned(B, qb) && aligned(C, qb) && dims->B_sb % 4 == 0 && dims->C_sb % 4 == 0);
+    q.vec = (dims->dstate % 4 == 0 && aligned(state, 16) && bc_vec) ? 1 : 0;
+  }
   const hipError_t e = selscan::launch_step(plan.bf16, plan.ti, q, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
 }
