@@ -11,7 +11,9 @@ Two independent statements of the method live here:
   the "state-space models" page (aarnphm.xyz, sections "From continuous time to tokens"
   and "One recurrence, one convolution") and the Algenta "Sequence and state-space
   models" page (section on ``state_space_models``), with the feed-through and SiLU gate
-  of the TorchLean "Selective Mamba" page (``step``).
+  of the TorchLean "Selective Mamba" page (``step``).  Options: an initial state, the
+  first-order input coefficient Bbar = delta * B (Algenta, ``mamba_selective_scan_step``),
+  and the step-size transform softplus(delta + per-channel bias) (TorchLean, ``step``).
 * ``conv_ti`` -- for fixed (time-invariant) coefficients, the causal-convolution form of
   the same layer with lag kernel K_k = C Abar^k Bbar ("state-space models", section "One
   recurrence, one convolution"), written with numpy in float64 and sharing no code with
@@ -50,28 +52,39 @@ class OracleLib:
         fp = ctypes.POINTER(ctypes.c_float)
         dp = ctypes.POINTER(ctypes.c_double)
         lib.ssm_oracle_fwd.restype = ctypes.c_int
-        lib.ssm_oracle_fwd.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, dp, dp, ctypes.c_int64, ctypes.c_int64,
-                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
-        lib.ssm_oracle_discretize.restype = None
-        lib.ssm_oracle_discretize.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, dp, dp]
+        lib.ssm_oracle_fwd.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, fp, dp, dp, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int]
+        for name in ("ssm_oracle_discretize", "ssm_oracle_discretize_euler"):
+            getattr(lib, name).restype = None
+            getattr(lib, name).argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, dp, dp]
+        lib.ssm_oracle_softplus.restype = ctypes.c_double
+        lib.ssm_oracle_softplus.argtypes = [ctypes.c_double]
         self.lib = lib
         self.path = path
 
-    def discretize(self, a: float, b: float, delta: float):
-        """ZOH coefficients (Abar, Bbar) of one scalar state."""
+    def discretize(self, a: float, b: float, delta: float, euler: bool = False):
+        """Coefficients (Abar, Bbar) of one scalar state: ZOH, or the first-order input
+        coefficient with euler=True."""
         ab = ctypes.c_double()
         bb = ctypes.c_double()
-        self.lib.ssm_oracle_discretize(float(a), float(b), float(delta), ctypes.byref(ab), ctypes.byref(bb))
+        fn = self.lib.ssm_oracle_discretize_euler if euler else self.lib.ssm_oracle_discretize
+        fn(float(a), float(b), float(delta), ctypes.byref(ab), ctypes.byref(bb))
         return ab.value, bb.value
 
-    def fwd(self, u, delta, A, B, C, Dskip=None, z=None, *, h0=None, time_invariant=False, want_last=True,
-            nthreads=None):
+    def softplus(self, x: float) -> float:
+        return self.lib.ssm_oracle_softplus(float(x))
+
+    def fwd(self, u, delta, A, B, C, Dskip=None, z=None, *, h0=None, delta_bias=None, euler=False,
+            delta_softplus=False, time_invariant=False, want_last=True, nthreads=None):
         """Run the fp64 recurrence.  Returns (y [batch,L,D] float64, last_state [batch,D,N] float64
         or None).
 
         u, z: [batch, L, D]; delta: [batch, L, D] (time-invariant: [D]); B, C: [batch, L, N]
         (time-invariant: [D, N]); A: [D, N]; Dskip: [D]; h0: [batch, D, N] initial state (None:
-        zero).  Inputs are converted to float32 first, the precision the GPU library receives.
+        zero); delta_bias: [D] added to delta (None: zero).  euler: Bbar = delta * B;
+        delta_softplus: the step size is softplus(delta + delta_bias).  Inputs are converted to
+        float32 first, the precision the GPU library receives.
         """
         u = _f32(u)
         delta = _f32(delta)
@@ -81,6 +94,7 @@ class OracleLib:
         Dskip = _f32(Dskip)
         z = _f32(z)
         h0 = _f32(h0)
+        delta_bias = _f32(delta_bias)
         batch, L, D = u.shape
         N = A.shape[1]
         assert A.shape == (D, N)
@@ -94,15 +108,18 @@ class OracleLib:
             assert z.shape == (batch, L, D)
         if h0 is not None:
             assert h0.shape == (batch, D, N)
+        if delta_bias is not None:
+            assert delta_bias.shape == (D,)
         y = np.empty((batch, L, D), dtype=np.float64)
         last = np.empty((batch, D, N), dtype=np.float64) if want_last else None
         if nthreads is None:
             nthreads = os.cpu_count() or 1
         rc = self.lib.ssm_oracle_fwd(
             _fptr(u), _fptr(delta), _fptr(A), _fptr(B), _fptr(C), _fptr(Dskip), _fptr(z), _fptr(h0),
-            y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            _fptr(delta_bias), y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
             None if last is None else last.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-            batch, L, D, N, 1 if time_invariant else 0, int(nthreads))
+            batch, L, D, N, 1 if time_invariant else 0, 1 if euler else 0, 1 if delta_softplus else 0,
+            int(nthreads))
         if rc != 0:
             raise RuntimeError("ssm_oracle_fwd failed with %d" % rc)
         return y, last
@@ -127,14 +144,22 @@ def _f32(a):
     return np.ascontiguousarray(a, dtype=np.float32)
 
 
-def discretize(a: float, b: float, delta: float):
-    """ZOH coefficients (Abar, Bbar) of one scalar state, from the C oracle."""
-    return _load().discretize(a, b, delta)
+def discretize(a: float, b: float, delta: float, euler: bool = False):
+    """Coefficients (Abar, Bbar) of one scalar state, from the C oracle (ZOH, or the
+    first-order input coefficient with euler=True)."""
+    return _load().discretize(a, b, delta, euler)
 
 
-def fwd(u, delta, A, B, C, Dskip=None, z=None, *, h0=None, time_invariant=False, want_last=True, nthreads=None):
+def softplus(x: float) -> float:
+    """softplus(x) = log(1 + e^x) in double, from the C oracle."""
+    return _load().softplus(x)
+
+
+def fwd(u, delta, A, B, C, Dskip=None, z=None, *, h0=None, delta_bias=None, euler=False, delta_softplus=False,
+        time_invariant=False, want_last=True, nthreads=None):
     """The fp64 recurrence of the default oracle library; see ``OracleLib.fwd``."""
-    return _load().fwd(u, delta, A, B, C, Dskip, z, h0=h0, time_invariant=time_invariant, want_last=want_last,
+    return _load().fwd(u, delta, A, B, C, Dskip, z, h0=h0, delta_bias=delta_bias, euler=euler,
+                       delta_softplus=delta_softplus, time_invariant=time_invariant, want_last=want_last,
                        nthreads=nthreads)
 
 

@@ -23,6 +23,16 @@
  *                                                   singular and its limit is delta * b)
  *     (Abar - 1)/a is evaluated as expm1(delta*a)/a so that the small-|delta*a| regime
  *     keeps full double precision.
+ *   - Optional first-order input coefficient ("Euler"): Abar = exp(delta * a) as above but
+ *     Bbar = delta * b for every state (Algenta page, mamba_selective_scan_step and the
+ *     worked example after it: h_1 = delta * b * x = 1.0 at a = -1, delta = 0.5, b = 2,
+ *     x = 1; TorchLean "Selective Mamba", step: the input term is delta[d] * B[n] * u[d];
+ *     chipfoundry glossary, Lab 2: B_bar = delta * B).
+ *   - Optional step-size transform: delta_eff = delta + delta_bias[d], then, when asked,
+ *     softplus(delta_eff) = log(1 + exp(delta_eff))  (TorchLean "Selective Mamba", step:
+ *     the time step is softplus of the projection plus dtBias, one bias per channel;
+ *     Algenta page, mamba_delta_softplus), evaluated in the overflow-free form
+ *     log1p(exp(-|x|)) + max(x, 0)  (chipfoundry glossary, Lab 2, softplus).
  *   - Selectivity: delta, B and C are given per token (B, C shared by every channel of
  *     a token); A is fixed and diagonal per (channel, state)  ("state-space models",
  *     section "Mamba"; TorchLean "Selective Mamba", Parameters: bProj/cProj describe one
@@ -53,6 +63,7 @@
  *   Dskip          : [D]      (may be NULL: no feed-through)
  *   z              : may be NULL (no gate)
  *   h0             : [batch][D][N]  float, the initial state (may be NULL: zero)
+ *   delta_bias     : [D]      (may be NULL: zero)
  *   last_state     : [batch][D][N]  (may be NULL)
  * Inputs are fp32 (bf16 data arrives already widened to fp32, which is exact); every
  * intermediate and every output is double.  The summation over states runs n = 0..N-1
@@ -67,10 +78,12 @@
 #include <string.h>
 
 typedef struct {
-  const float *u, *delta, *A, *B, *C, *Dskip, *z, *h0;
+  const float *u, *delta, *A, *B, *C, *Dskip, *z, *h0, *delta_bias;
   double *y, *last_state;
   int64_t batch, L, D, N;
   int time_invariant;
+  int euler;               /* Bbar = delta * b instead of the ZOH coefficient */
+  int delta_softplus;      /* delta_eff = softplus(delta + bias) instead of delta + bias */
   int64_t next_pair;       /* work counter, guarded by mu */
   pthread_mutex_t mu;
 } oracle_job;
@@ -81,6 +94,17 @@ static double zoh_input_coeff(double dt, double a) {
   return expm1(dt * a) / a;
 }
 
+/* softplus(x) = log(1 + e^x), written so that e^x never overflows. */
+static double softplus(double x) { return log1p(exp(-fabs(x))) + fmax(x, 0.0); }
+
+/* The step size a token uses: the given delta, plus the channel's bias, through softplus
+ * when asked. */
+static double step_size(const oracle_job* j, double raw, int64_t d) {
+  double x = raw;
+  if (j->delta_bias) x += (double)j->delta_bias[d];
+  return j->delta_softplus ? softplus(x) : x;
+}
+
 static void scan_one_channel(oracle_job* j, int64_t b, int64_t d, double* h) {
   const int64_t L = j->L, D = j->D, N = j->N;
   for (int64_t n = 0; n < N; ++n)                                /* h_{-1}: given, else 0 */
@@ -88,14 +112,14 @@ static void scan_one_channel(oracle_job* j, int64_t b, int64_t d, double* h) {
   for (int64_t l = 0; l < L; ++l) {
     const int64_t tok = (b * L + l) * D + d;
     const double uu = (double)j->u[tok];
-    const double dt = j->time_invariant ? (double)j->delta[d] : (double)j->delta[tok];
+    const double dt = step_size(j, j->time_invariant ? (double)j->delta[d] : (double)j->delta[tok], d);
     const float* Brow = j->time_invariant ? j->B + d * N : j->B + (b * L + l) * N;
     const float* Crow = j->time_invariant ? j->C + d * N : j->C + (b * L + l) * N;
     double acc = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       const double a = (double)j->A[d * N + n];
       const double abar = exp(dt * a);
-      const double bbar = zoh_input_coeff(dt, a) * (double)Brow[n];
+      const double bbar = (j->euler ? dt : zoh_input_coeff(dt, a)) * (double)Brow[n];
       h[n] = abar * h[n] + bbar * uu;
       acc += (double)Crow[n] * h[n];
     }
@@ -129,9 +153,10 @@ static void* worker(void* arg) {
 
 /* Returns 0 on success, -1 on invalid arguments, -2 on allocation/thread failure. */
 int ssm_oracle_fwd(const float* u, const float* delta, const float* A, const float* B,
-                   const float* C, const float* Dskip, const float* z, const float* h0, double* y,
-                   double* last_state, int64_t batch, int64_t L, int64_t D, int64_t N,
-                   int time_invariant, int nthreads) {
+                   const float* C, const float* Dskip, const float* z, const float* h0,
+                   const float* delta_bias, double* y, double* last_state, int64_t batch, int64_t L,
+                   int64_t D, int64_t N, int time_invariant, int euler, int delta_softplus,
+                   int nthreads) {
   if (batch < 0 || L < 0 || D <= 0 || N <= 0) return -1;
   if (batch == 0) return 0;
   if (L > 0 && (!u || !delta || !A || !B || !C || !y)) return -1;
@@ -142,6 +167,7 @@ int ssm_oracle_fwd(const float* u, const float* delta, const float* A, const flo
   }
   oracle_job j;
   j.u = u; j.delta = delta; j.A = A; j.B = B; j.C = C; j.Dskip = Dskip; j.z = z; j.h0 = h0;
+  j.delta_bias = delta_bias; j.euler = euler; j.delta_softplus = delta_softplus;
   j.y = y; j.last_state = last_state;
   j.batch = batch; j.L = L; j.D = D; j.N = N; j.time_invariant = time_invariant;
   j.next_pair = 0;
@@ -170,3 +196,12 @@ void ssm_oracle_discretize(double a, double b, double dt, double* abar, double* 
   *abar = exp(dt * a);
   *bbar = zoh_input_coeff(dt, a) * b;
 }
+
+/* The first-order ("Euler") pair for one scalar: the same Abar, Bbar = delta * b. */
+void ssm_oracle_discretize_euler(double a, double b, double dt, double* abar, double* bbar) {
+  *abar = exp(dt * a);
+  *bbar = dt * b;
+}
+
+/* softplus of one value, exposed so the printed values can be checked on their own. */
+double ssm_oracle_softplus(double x) { return softplus(x); }

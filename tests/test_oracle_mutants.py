@@ -3,9 +3,10 @@ oracle's C source (on the CPU, in a temporary directory), build it, and check th
 battery below rejects every mutant while accepting the unmodified oracle.
 
 The battery uses only references the pages or the mathematics fix: the printed worked ZOH
-example, the halving closed form, a brute-force unrolled sum, the causal-convolution form
-for fixed coefficients, scipy's logistic function for the gate, and the integrator closed
-form for a zero continuous rate.
+and first-order examples, the printed softplus values, the halving closed form, a
+brute-force unrolled sum (also fed step sizes transformed with numpy's logaddexp), the
+causal-convolution form for fixed coefficients, scipy's logistic function for the gate, and
+the integrator closed form for a zero continuous rate.
 """
 import math
 import os
@@ -30,8 +31,8 @@ MUTANTS = {
     "dropped_feedthrough": ("if (j->Dskip) yv += (double)j->Dskip[d] * uu;", ";"),
     "sigmoid_instead_of_silu": ("yv *= zz / (1.0 + exp(-zz));", "yv *= 1.0 / (1.0 + exp(-zz));"),
     "wrong_sign_decay": ("const double abar = exp(dt * a);", "const double abar = exp(-dt * a);"),
-    "b_and_c_swapped": ("const double bbar = zoh_input_coeff(dt, a) * (double)Brow[n];",
-                        "const double bbar = zoh_input_coeff(dt, a) * (double)Crow[n];"),
+    "b_and_c_swapped": ("const double bbar = (j->euler ? dt : zoh_input_coeff(dt, a)) * (double)Brow[n];",
+                        "const double bbar = (j->euler ? dt : zoh_input_coeff(dt, a)) * (double)Crow[n];"),
     "a_transposed": ("const double a = (double)j->A[d * N + n];", "const double a = (double)j->A[n * D + d];"),
     "zero_rate_fallback_dropped": ("if (a == 0.0) return dt;", "if (a == 0.0) return 0.0;"),
     "feedthrough_after_gate": (
@@ -45,6 +46,15 @@ MUTANTS = {
     "initial_state_ignored": ("h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     "initial_state_wrong_index": ("h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 0.0;",
                                   "h[n] = j->h0 ? (double)j->h0[(d * j->batch + b) * N + n] : 0.0;"),
+    "euler_flag_ignored": ("(j->euler ? dt : zoh_input_coeff(dt, a))", "zoh_input_coeff(dt, a)"),
+    "euler_also_linearises_decay": ("const double abar = exp(dt * a);",
+                                    "const double abar = j->euler ? 1.0 + dt * a : exp(dt * a);"),
+    "softplus_not_applied": ("return j->delta_softplus ? softplus(x) : x;", "return x;"),
+    "softplus_wrong_branch": ("log1p(exp(-fabs(x))) + fmax(x, 0.0)", "log1p(exp(-fabs(x))) + fmax(-x, 0.0)"),
+    "bias_not_per_channel": ("if (j->delta_bias) x += (double)j->delta_bias[d];",
+                             "if (j->delta_bias) x += (double)j->delta_bias[0];"),
+    "bias_after_softplus": ("  double x = raw;\n  if (j->delta_bias) x += (double)j->delta_bias[d];\n  return j->delta_softplus ? softplus(x) : x;",
+                            "  double x = j->delta_softplus ? softplus(raw) : raw;\n  if (j->delta_bias) x += (double)j->delta_bias[d];\n  return x;"),
 }
 
 
@@ -122,6 +132,23 @@ def pin_battery(lib):
     yb, lb = brute_force(*args, h0=h0)
     if rel_err(y, yb) > 1e-12 or rel_err(last, lb) > 1e-12:
         failed.append("initial_state")
+    # printed first-order example through the recurrence
+    y, _ = lib.fwd(u, np.full((1, 2, 1), g["delta"], np.float32), np.array([[g["a"]]], np.float32),
+                   np.full((1, 2, 1), g["b"], np.float32), np.ones((1, 2, 1), np.float32), euler=True)
+    if y[0, 0, 0] != g["h1_first_order"] or abs(y[0, 1, 0] - g["abar"] * g["h1_first_order"]) > 1e-15:
+        failed.append("first_order_example")
+    # printed softplus values
+    sp = read_golden("softplus_values.txt")
+    if abs(lib.softplus(0.0) - sp["softplus_0"]) > 1e-16 or abs(lib.softplus(1.0) - sp["softplus_1"]) > 1e-15:
+        failed.append("softplus_values")
+    # bias per channel, then softplus, against the brute force fed logaddexp(0, raw + bias)
+    raw = rng.normal(-1.0, 1.5, args[0].shape).astype(np.float32)
+    bias = rng.normal(0.0, 1.0, D).astype(np.float32)
+    y, last = lib.fwd(args[0], raw, *args[2:], delta_bias=bias, delta_softplus=True)
+    dt = np.logaddexp(0.0, raw.astype(np.float64) + bias.astype(np.float64)[None, None, :])
+    yb, lb = brute_force(args[0], dt, *args[2:])
+    if rel_err(y, yb) > 1e-12 or rel_err(last, lb) > 1e-12:
+        failed.append("fused_softplus")
     return failed
 
 

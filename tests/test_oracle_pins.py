@@ -12,7 +12,14 @@ fix, not against a re-typed copy of its own loop.
   scalar decay a_k to a per-state decay Abar_k[n], evaluated by brute force on tiny inputs;
 * the associative combine of the chipfoundry glossary's Lab 3 (sequential vs parallel scan);
 * invariants: causality, linearity, batch independence, determinism, stability of Abar;
-* the SiLU gate against scipy's logistic function.
+* the SiLU gate against scipy's logistic function;
+* the first-order ("Euler") input coefficient: the worked value h_1 = 1.0 printed on the
+  Algenta page beside the ZOH one, its geometric-series closed form, and the brute-force
+  unroll with Bbar = delta * B;
+* softplus of the step size: the two values printed on the Algenta page (mamba_delta_softplus),
+  numpy's logaddexp(0, x) = log(e^0 + e^x), and the fused transform (per-channel bias, then
+  softplus, as in TorchLean "Selective Mamba", step) against the brute-force unroll fed the
+  transformed step sizes.
 """
 import math
 
@@ -38,10 +45,12 @@ def _rand_s6(rng, batch, L, D, N, gate=True, dskip=True, zero_a=False):
     return u, delta, A, B, C, Ds, z
 
 
-def brute_force(u, delta, A, B, C, Dskip=None, z=None, h0=None):
+def brute_force(u, delta, A, B, C, Dskip=None, z=None, h0=None, euler=False):
     """y_t = sum_n C_t[n] [(prod_{k=0..t} Abar_k[n]) h0[n] + sum_{s<=t} (prod_{k=s+1..t} Abar_k[n])
     Bbar_s[n] u_s] + D u_t, then the gate; and the final state h[n] = (prod_k Abar_k[n]) h0[n] +
     sum_s (prod_{k=s+1..L-1} Abar_k[n]) Bbar_s[n] u_s.  h0 (the initial state) defaults to zero.
+    Bbar is the ZOH coefficient, or delta * B with euler=True.  delta may be given in float64 (a
+    step size already transformed by the caller).
     Pure Python loops in float64 -- O(L^2 N) per channel, for tiny inputs only."""
     u = np.asarray(u, np.float64)
     delta = np.asarray(delta, np.float64)
@@ -65,8 +74,8 @@ def brute_force(u, delta, A, B, C, Dskip=None, z=None, h0=None):
             for t in range(L):
                 dt = delta[b, t, d]
                 abar.append([math.exp(dt * A[d, n]) for n in range(N)])
-                bbar.append([(math.expm1(dt * A[d, n]) / A[d, n] if A[d, n] != 0.0 else dt) * B[b, t, n]
-                             for n in range(N)])
+                bbar.append([(dt if euler else math.expm1(dt * A[d, n]) / A[d, n] if A[d, n] != 0.0 else dt)
+                             * B[b, t, n] for n in range(N)])
             for t in range(L):
                 total = 0.0
                 for n in range(N):
@@ -441,3 +450,123 @@ def test_empty_call_hands_back_initial_state():
     _, last = oracle.fwd(e, e, -np.ones((3, 4), np.float32), np.zeros((2, 0, 4), np.float32),
                          np.zeros((2, 0, 4), np.float32), h0=h0)
     assert np.array_equal(last, h0.astype(np.float64))
+
+
+# ---- first-order input coefficient ("Euler"): Algenta "Sequence and state-space models",
+# mamba_selective_scan_step and its worked example; TorchLean "Selective Mamba", step
+
+def test_euler_scalar_example(golden):
+    g = golden("zoh_scalar_example.txt")
+    abar, bbar = oracle.discretize(g["a"], g["b"], g["delta"], euler=True)
+    assert abar == pytest.approx(g["abar"], abs=1e-15)              # the same exact Abar
+    assert bbar * g["x"] + abar * g["h_prev"] == g["h1_first_order"]  # 1.0 exactly
+    u = np.array([[[g["x"]], [0.0]]], np.float32)
+    y, last = oracle.fwd(u, np.full((1, 2, 1), g["delta"], np.float32), np.array([[g["a"]]], np.float32),
+                         np.full((1, 2, 1), g["b"], np.float32), np.ones((1, 2, 1), np.float32), euler=True)
+    assert y[0, 0, 0] == g["h1_first_order"]
+    assert y[0, 1, 0] == pytest.approx(g["abar"] * g["h1_first_order"], abs=1e-15)
+    assert last[0, 0, 0] == pytest.approx(g["abar"] * g["h1_first_order"], abs=1e-15)
+    # the printed gap between the two methods at this step size (about 27 %)
+    assert (g["h1_first_order"] - g["h1_zoh"]) / g["h1_zoh"] == pytest.approx(0.27, abs=0.005)
+
+
+@pytest.mark.parametrize("L", [1, 9, 60])
+def test_euler_geometric_closed_form(L):
+    """Constant delta, a, b and a unit input: h_t = delta b (1 - Abar^(t+1)) / (1 - Abar)."""
+    dt, a, b = np.float32(0.37), np.float32(-1.3), np.float32(0.8)
+    y, _ = oracle.fwd(np.ones((1, L, 1), np.float32), np.full((1, L, 1), dt, np.float32),
+                      np.full((1, 1), a, np.float32), np.full((1, L, 1), b, np.float32),
+                      np.ones((1, L, 1), np.float32), euler=True)
+    q = math.exp(float(dt) * float(a))
+    t = np.arange(L)
+    np.testing.assert_allclose(y[0, :, 0], float(dt) * float(b) * (1 - q ** (t + 1)) / (1 - q), rtol=1e-13)
+
+
+def test_euler_brute_force_and_zero_rate():
+    rng = np.random.default_rng(91)
+    inp = _rand_s6(rng, 2, 9, 3, 4, zero_a=True)
+    y, last = oracle.fwd(*inp, euler=True)
+    yb, lb = brute_force(*inp, euler=True)
+    assert rel_err(y, yb) < 1e-12 and rel_err(last, lb) < 1e-12
+    h0 = rng.standard_normal((2, 3, 4)).astype(np.float32)
+    y, last = oracle.fwd(*inp, h0=h0, euler=True)
+    yb, lb = brute_force(*inp, h0=h0, euler=True)
+    assert rel_err(y, yb) < 1e-12 and rel_err(last, lb) < 1e-12
+    # with every rate zero the two discretisations coincide (both integrate delta * B * u)
+    u, delta, A, B, C, Ds, z = inp
+    A0 = np.zeros_like(A)
+    assert np.array_equal(oracle.fwd(u, delta, A0, B, C, Ds, z, euler=True)[0], oracle.fwd(u, delta, A0, B, C, Ds, z)[0])
+
+
+def test_euler_approaches_zoh_for_small_steps():
+    """Bbar_zoh / Bbar_euler = expm1(delta a) / (delta a) = 1 + delta a / 2 + O((delta a)^2)."""
+    for dt in (1e-2, 1e-3, 1e-4):
+        _, bz = oracle.discretize(-2.0, 1.0, dt)
+        _, be = oracle.discretize(-2.0, 1.0, dt, euler=True)
+        assert be == dt
+        assert bz / be - 1.0 == pytest.approx(-dt, rel=2 * dt)
+
+
+def test_euler_time_invariant_equals_selective():
+    rng = np.random.default_rng(93)
+    batch, L, N = 2, 40, 3
+    u = rng.standard_normal((batch, L, 1)).astype(np.float32)
+    A = -rng.uniform(0.1, 2.0, (1, N)).astype(np.float32)
+    B = rng.standard_normal((1, N)).astype(np.float32)
+    C = rng.standard_normal((1, N)).astype(np.float32)
+    y_ti, l_ti = oracle.fwd(u, np.array([0.3], np.float32), A, B, C, euler=True, time_invariant=True)
+    y_s6, l_s6 = oracle.fwd(u, np.full((batch, L, 1), 0.3, np.float32), A, np.broadcast_to(B, (batch, L, N)).copy(),
+                            np.broadcast_to(C, (batch, L, N)).copy(), euler=True)
+    assert np.array_equal(y_ti, y_s6) and np.array_equal(l_ti, l_s6)
+
+
+# ---- softplus of the step size: Algenta page, mamba_delta_softplus; TorchLean "Selective
+# Mamba", step (softplus of the projection plus dtBias)
+
+def test_softplus_printed_values_and_identities(golden):
+    g = golden("softplus_values.txt")
+    assert oracle.softplus(0.0) == pytest.approx(g["softplus_0"], abs=1e-16)
+    assert oracle.softplus(1.0) == pytest.approx(g["softplus_1"], abs=1e-15)
+    xs = np.concatenate([np.linspace(-40, 40, 801), [-700.0, -80.0, 80.0, 700.0, 1e-9, -1e-9]])
+    got = np.array([oracle.softplus(float(x)) for x in xs])
+    np.testing.assert_allclose(got, np.logaddexp(0.0, xs), rtol=4e-16, atol=0)
+    np.testing.assert_allclose(got - np.array([oracle.softplus(-float(x)) for x in xs]), xs, rtol=1e-12, atol=1e-15)
+    assert oracle.softplus(1000.0) == 1000.0 and 0.0 < oracle.softplus(-700.0) < 1e-300
+
+
+@pytest.mark.parametrize("euler", [False, True])
+def test_fused_step_size_transform_brute_force(euler):
+    rng = np.random.default_rng(95 + euler)
+    u, _, A, B, C, Ds, z = _rand_s6(rng, 2, 9, 3, 4, zero_a=True)
+    raw = rng.normal(-1.0, 1.5, u.shape).astype(np.float32)
+    bias = rng.normal(0.0, 1.0, 3).astype(np.float32)
+    x64 = raw.astype(np.float64) + bias.astype(np.float64)[None, None, :]
+    # bias, then softplus
+    y, last = oracle.fwd(u, raw, A, B, C, Ds, z, delta_bias=bias, delta_softplus=True, euler=euler)
+    yb, lb = brute_force(u, np.logaddexp(0.0, x64), A, B, C, Ds, z, euler=euler)
+    assert rel_err(y, yb) < 1e-12 and rel_err(last, lb) < 1e-12
+    # softplus without a bias
+    y, _ = oracle.fwd(u, raw, A, B, C, Ds, z, delta_softplus=True, euler=euler)
+    yb, _ = brute_force(u, np.logaddexp(0.0, raw.astype(np.float64)), A, B, C, Ds, z, euler=euler)
+    assert rel_err(y, yb) < 1e-12
+    # a bias alone shifts the step size (positive inputs keep it positive)
+    pos = np.abs(raw) + np.float32(0.05)
+    bpos = np.abs(bias) * np.float32(0.1)
+    y, _ = oracle.fwd(u, pos, A, B, C, Ds, z, delta_bias=bpos, euler=euler)
+    yb, _ = brute_force(u, pos.astype(np.float64) + bpos.astype(np.float64)[None, None, :], A, B, C, Ds, z,
+                        euler=euler)
+    assert rel_err(y, yb) < 1e-12
+
+
+def test_fused_step_size_time_invariant():
+    rng = np.random.default_rng(97)
+    D, N, L = 3, 4, 50
+    u = rng.standard_normal((2, L, D)).astype(np.float32)
+    raw = rng.normal(-2.0, 1.0, D).astype(np.float32)
+    bias = rng.normal(0.0, 0.5, D).astype(np.float32)
+    A = (-rng.uniform(0.2, 2.0, (D, N))).astype(np.float32)
+    B = rng.standard_normal((D, N)).astype(np.float32)
+    C = rng.standard_normal((D, N)).astype(np.float32)
+    y, _ = oracle.fwd(u, raw, A, B, C, delta_bias=bias, delta_softplus=True, time_invariant=True)
+    dt = np.logaddexp(0.0, raw.astype(np.float64) + bias.astype(np.float64))
+    assert rel_err(y, oracle.conv_ti_direct(u, dt, A, B, C)) < 1e-12
