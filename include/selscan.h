@@ -24,6 +24,17 @@
  *   the D * u feed-through and the SiLU gate of "Selective Mamba" (step); the final state
  *   a following chunk resumes from of "Selective Mamba" (State.hidden, runArray).
  *
+ * Options (selscan_dims.discretization, selscan_dims.delta_softplus; delta_bias of
+ * selective_scan_fwd_ex / selective_scan_step):
+ *   step size:  delta_eff[b,l,d] = delta[b,l,d] + delta_bias[d]  (delta_bias NULL = 0), and
+ *               with delta_softplus != 0, delta_eff = softplus(delta_eff) = log(1 + exp(.))
+ *               (TorchLean "Selective Mamba", step: softplus of the projection plus a
+ *               per-channel dtBias; Algenta "Sequence and state-space models",
+ *               mamba_delta_softplus).  delta_eff replaces delta everywhere above.
+ *   SELSCAN_DISC_EULER:  Bbar = delta_eff * B[b,l,n] for every state, Abar unchanged (the
+ *               first-order input coefficient of Algenta's mamba_selective_scan_step, also
+ *               TorchLean's step); it differs from ZOH by O(delta * A) relative.
+ *
  * Time-invariant mode (fixed coefficients, "state-space models", section "One recurrence,
  * one convolution"): delta is one value per channel and B, C are one N-vector per channel,
  * expressed through strides (see selscan_dims).  The same recurrence is evaluated.
@@ -55,7 +66,7 @@
 extern "C" {
 #endif
 
-#define SELSCAN_ABI_VERSION 1
+#define SELSCAN_ABI_VERSION 2
 
 /* Element type of u, delta, B, C, z and y. */
 enum selscan_dtype {
@@ -68,7 +79,7 @@ enum selscan_status {
   SELSCAN_ERR_NULL = -1,        /* a required pointer (u, delta, A, B, C, y, dims) is NULL;
                                    only A and dims are required when batch * seqlen == 0 */
   SELSCAN_ERR_DIMS = -2,        /* batch < 0, seqlen < 0, dim < 1, dstate < 1, or a negative stride */
-  SELSCAN_ERR_UNSUPPORTED = -3, /* dstate > 64, unknown dtype or path, a B/C/delta stride
+  SELSCAN_ERR_UNSUPPORTED = -3, /* dstate > 64, unknown dtype, path or discretization, a B/C/delta stride
                                    pattern that is neither per-token (shared over channels)
                                    nor per-channel (time-invariant), overlapping y rows
                                    (y_sl < dim or y_sb < seqlen * y_sl), or a size beyond the
@@ -93,6 +104,12 @@ enum selscan_path {
    * even where the software-pipelined kernel applies.  Results agree within fp32
    * rounding. */
   SELSCAN_PATH_FLAG_SCALAR_IO = 0x100
+};
+
+/* Input coefficient of the discretisation (the state coefficient is exp(delta * A) in both). */
+enum selscan_discretization {
+  SELSCAN_DISC_ZOH = 0,    /* Bbar = (exp(delta A) - 1) / A * B   (delta * B where A == 0) */
+  SELSCAN_DISC_EULER = 1   /* Bbar = delta * B */
 };
 
 /*
@@ -127,11 +144,14 @@ typedef struct selscan_dims {
   int64_t C_sb, C_sl, C_sd;
   int32_t path;         /* enum selscan_path, optionally | SELSCAN_PATH_FLAG_SCALAR_IO; 0 = automatic */
   int32_t chunk_len;    /* chunked path: tokens per chunk, a multiple of 16 (0 = automatic) */
+  int32_t discretization;  /* enum selscan_discretization (0 = ZOH) */
+  int32_t delta_softplus;  /* nonzero: the step size is softplus(delta + delta_bias) */
 } selscan_dims;
 
 /* Fill *dims for contiguous tensors: u, delta, z, y as [batch][seqlen][dim]; B, C as
  * [batch][seqlen][dstate].  With time_invariant != 0: delta as [dim] and B, C as
- * [dim][dstate].  path = AUTO, chunk_len = 0.  Never fails for a non-NULL dims. */
+ * [dim][dstate].  path = AUTO, chunk_len = 0, ZOH, no softplus.  Never fails for a
+ * non-NULL dims. */
 void selscan_dims_init(selscan_dims* dims, int io_dtype, int64_t batch, int64_t seqlen,
                        int64_t dim, int64_t dstate, int time_invariant);
 
@@ -182,6 +202,7 @@ int selective_scan_fwd_ws(const void* u, const void* delta, const float* A, cons
  *                    SELSCAN_ERR_UNSUPPORTED.
  *   workspace, workspace_bytes : as selective_scan_fwd_ws; a NULL workspace makes the call
  *                    take it stream-ordered on `stream` when the chunked path needs it.
+ *   delta_bias     : [dim] fp32 added to delta before the optional softplus, or NULL.
  *   Other arguments as selective_scan_fwd.
  * seqlen == 0 copies initial_state (zeros if NULL) to last_state.
  * A call over tokens [0, k) followed by a call over [k, L) whose initial_state is the
@@ -189,8 +210,8 @@ int selective_scan_fwd_ws(const void* u, const void* delta, const float* A, cons
  * rounding of the carried state (TorchLean "Selective Mamba": step and runArray carry an
  * explicit hidden state from one chunk to the next).
  */
-int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
-                          const void* C, const float* Dskip, const void* z, void* y,
+int selective_scan_fwd_ex(const void* u, const void* delta, const float* delta_bias, const float* A,
+                          const void* B, const void* C, const float* Dskip, const void* z, void* y,
                           const float* initial_state, float* last_state, const selscan_dims* dims,
                           void* workspace, size_t workspace_bytes, void* stream);
 
@@ -205,11 +226,12 @@ int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, cons
  *            dims->path and dims->chunk_len are ignored.
  *   state  : [batch][dim][dstate] fp32, required: read as h_{-1}, overwritten with h_0.
  *   u, delta, A, B, C, Dskip, z, y : as selective_scan_fwd, for the one token.
+ *   delta_bias : as selective_scan_fwd_ex.
  * Never allocates.  Same status codes as selective_scan_fwd.
  */
-int selective_scan_step(const void* u, const void* delta, const float* A, const void* B,
-                        const void* C, const float* Dskip, const void* z, void* y, float* state,
-                        const selscan_dims* dims, void* stream);
+int selective_scan_step(const void* u, const void* delta, const float* delta_bias, const float* A,
+                        const void* B, const void* C, const float* Dskip, const void* z, void* y,
+                        float* state, const selscan_dims* dims, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* selective_scan_strerror(int status);

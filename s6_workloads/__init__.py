@@ -154,6 +154,23 @@ def running_state(inp: Inputs, seed: int = 11, scale: float = 0.1) -> np.ndarray
     return np.ascontiguousarray(rng.standard_normal((b, D, N)) * scale, dtype=np.float32)
 
 
+def raw_step_sizes(inp: Inputs, seed: int = 17, spread: float = 0.5):
+    """Inputs for the fused step-size transform: (raw, bias) with raw shaped like ``inp.delta``
+    (float32; bf16-exact for bf16 workloads) and bias [D] float32, so that the step size is
+    softplus(raw + bias).  bias[d] is the inverse softplus of a log-uniform step in
+    [1e-3, 1e-1] (the canonical S6 time-step initialisation), raw is normal with standard
+    deviation ``spread`` (a projection's output around it)."""
+    D = inp.A.shape[0]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt0 = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), D))
+    bias = np.log(np.expm1(dt0))
+    raw = rng.normal(0.0, spread, inp.delta.shape)
+    raw = np.ascontiguousarray(raw, dtype=np.float32)
+    if inp.io == "bf16":
+        raw = bf16_round(raw)
+    return raw, np.ascontiguousarray(bias, dtype=np.float32)
+
+
 def sample_channels(D: int, count: int, seed: int = 7) -> np.ndarray:
     """A sorted, seeded sample of channel indices that always includes the first and last
     channel (ragged edges) and a few channel-tile boundaries."""

@@ -13,6 +13,9 @@ Shapes (torch tensors on the current GPU):
     A              [D, N] float32
     B, C           [batch, L, N]        (selective) or [D, N] (time-invariant)
     Dskip          [D] float32 or None
+Options: ``discretization="euler"`` (Bbar = delta * B instead of the ZOH coefficient),
+``delta_softplus=True`` and ``delta_bias`` ([D] float32): the step size is
+softplus(delta + delta_bias) (the bias alone is added without softplus).
 The innermost axis of every tensor must be unit-stride; other strides are passed through
 (zero strides, i.e. expanded views, are allowed).
 """
@@ -25,13 +28,14 @@ from typing import Optional, Tuple
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libselscan.so")
 
-SELSCAN_ABI_VERSION = 1
+SELSCAN_ABI_VERSION = 2
 SELSCAN_F32, SELSCAN_BF16 = 0, 1
 SELSCAN_OK = 0
 SELSCAN_ERR_NULL, SELSCAN_ERR_DIMS, SELSCAN_ERR_UNSUPPORTED = -1, -2, -3
 SELSCAN_ERR_ALIGN, SELSCAN_ERR_HIP, SELSCAN_ERR_WORKSPACE, SELSCAN_ERR_ABI = -4, -5, -6, -7
 PATHS = {"auto": 0, "single": 1, "chunked": 2}
 FLAG_SCALAR_IO = 0x100   # tests only: force the general per-element kernel
+DISCRETIZATIONS = {"zoh": 0, "euler": 1}
 
 
 class SelscanDims(ctypes.Structure):
@@ -46,6 +50,7 @@ class SelscanDims(ctypes.Structure):
         ("B_sb", ctypes.c_int64), ("B_sl", ctypes.c_int64), ("B_sd", ctypes.c_int64),
         ("C_sb", ctypes.c_int64), ("C_sl", ctypes.c_int64), ("C_sd", ctypes.c_int64),
         ("path", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
+        ("discretization", ctypes.c_int32), ("delta_softplus", ctypes.c_int32),
     ]
 
 
@@ -68,8 +73,8 @@ _SIGNATURES = [
     ("selective_scan_fwd", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP]),
     ("selective_scan_workspace_size", ctypes.c_size_t, [ctypes.POINTER(SelscanDims)]),
     ("selective_scan_fwd_ws", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
-    ("selective_scan_fwd_ex", ctypes.c_int, [_VP] * 10 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
-    ("selective_scan_step", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP]),
+    ("selective_scan_fwd_ex", ctypes.c_int, [_VP] * 11 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
+    ("selective_scan_step", ctypes.c_int, [_VP] * 10 + [ctypes.POINTER(SelscanDims), _VP]),
     ("selective_scan_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("selective_scan_last_hip_error", ctypes.c_int, []),
     ("selective_scan_abi_version", ctypes.c_int, []),
@@ -140,7 +145,7 @@ def _strides_bld(t, name, batch, L, D):
 
 
 def make_dims(u, delta, A, B, C, z=None, y=None, *, path: str = "auto", chunk_len: int = 0,
-              scalar_io: bool = False) -> SelscanDims:
+              scalar_io: bool = False, discretization: str = "zoh", delta_softplus: bool = False) -> SelscanDims:
     """Build selscan_dims from tensor shapes and strides (see the module docstring)."""
     if u.dim() != 3:
         raise ValueError("u must be [batch, L, D]")
@@ -179,11 +184,21 @@ def make_dims(u, delta, A, B, C, z=None, y=None, *, path: str = "auto", chunk_le
         d.y_sb, d.y_sl = _strides_bld(y, "y", batch, L, D)
     d.path = PATHS[path] | (FLAG_SCALAR_IO if scalar_io else 0)
     d.chunk_len = int(chunk_len)
+    d.discretization = DISCRETIZATIONS[discretization]
+    d.delta_softplus = 1 if delta_softplus else 0
     return d
 
 
+def _check_bias(delta_bias, D):
+    import torch
+    if delta_bias is not None and (delta_bias.dtype != torch.float32 or tuple(delta_bias.shape) != (D,)
+                                   or not delta_bias.is_contiguous() or not delta_bias.is_cuda):
+        raise ValueError("delta_bias must be a contiguous float32 [D] GPU tensor")
+
+
 def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state=None, *,
-                       initial_state=None, return_last_state: bool = False, path: str = "auto",
+                       initial_state=None, delta_bias=None, delta_softplus: bool = False,
+                       discretization: str = "zoh", return_last_state: bool = False, path: str = "auto",
                        chunk_len: int = 0, scalar_io: bool = False, workspace=None,
                        stream=None) -> Tuple["object", Optional["object"]]:
     """Selective-scan forward on the GPU.  Returns (y, last_state or None).
@@ -218,7 +233,9 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (batch, D, N)
                               or not t.is_cuda):
             raise ValueError("%s must be a contiguous float32 [batch, D, N] GPU tensor" % name)
-    dims = make_dims(u, delta, A, B, C, z, y, path=path, chunk_len=chunk_len, scalar_io=scalar_io)
+    _check_bias(delta_bias, D)
+    dims = make_dims(u, delta, A, B, C, z, y, path=path, chunk_len=chunk_len, scalar_io=scalar_io,
+                     discretization=discretization, delta_softplus=delta_softplus)
     torch_stream = stream if (stream is None or hasattr(stream, "cuda_stream")) else None
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
@@ -233,12 +250,12 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
             workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
             if torch_stream is not None:
                 workspace.record_stream(torch_stream)
-    if initial_state is not None:
+    if initial_state is not None or delta_bias is not None:
         ws_args = ((_ptr(workspace), int(workspace.numel() * workspace.element_size())) if workspace is not None
                    else (None, 0))
-        st = lib().selective_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z),
-                                         _ptr(y), _ptr(initial_state), _ptr(last_state), ctypes.byref(dims),
-                                         ws_args[0], ws_args[1], ctypes.c_void_p(stream))
+        st = lib().selective_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+                                         _ptr(Dskip), _ptr(z), _ptr(y), _ptr(initial_state), _ptr(last_state),
+                                         ctypes.byref(dims), ws_args[0], ws_args[1], ctypes.c_void_p(stream))
         if st != SELSCAN_OK:
             raise SelscanError(st, "selective_scan_fwd_ex")
         return y, last_state
@@ -257,13 +274,13 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
 
 
 def selective_scan_step(u, delta, A, B, C, Dskip=None, z=None, y=None, *, state, time_invariant: bool = False,
-                        stream=None):
+                        delta_bias=None, delta_softplus: bool = False, discretization: str = "zoh", stream=None):
     """One recurrent decode step (one token per batch row); ``state`` ([batch, D, N] float32,
     contiguous) is read as the running state and overwritten with the new one.
 
     u, z, y: [batch, D]; A: [D, N]; Dskip: [D].  Selective coefficients: delta [batch, D]
     (or [D] shared by the batch), B, C [batch, N].  time_invariant=True: delta [D], B, C
-    [D, N].  Returns y."""
+    [D, N].  delta_bias, delta_softplus, discretization: as selective_scan_fwd.  Returns y."""
     import torch
     if u.dim() != 2:
         raise ValueError("u must be [batch, D] (one token per batch row)")
@@ -288,10 +305,13 @@ def selective_scan_step(u, delta, A, B, C, Dskip=None, z=None, y=None, *, state,
             raise ValueError("%s must be [batch, %d] with a unit-stride last axis" % (name, width))
         return t.stride(0)
 
+    _check_bias(delta_bias, D)
     d = SelscanDims()
     d.abi_version = SELSCAN_ABI_VERSION
     d.io_dtype = _io_code(io)
     d.batch, d.seqlen, d.dim, d.dstate = batch, 1, D, N
+    d.discretization = DISCRETIZATIONS[discretization]
+    d.delta_softplus = 1 if delta_softplus else 0
     d.u_sb = rows(u, "u", D)
     d.u_sl = D
     d.y_sb = rows(y, "y", D)
@@ -322,8 +342,8 @@ def selective_scan_step(u, delta, A, B, C, Dskip=None, z=None, y=None, *, state,
         stream = torch.cuda.current_stream(u.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    st = lib().selective_scan_step(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(y),
-                                   _ptr(state), ctypes.byref(d), ctypes.c_void_p(stream))
+    st = lib().selective_scan_step(_ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip),
+                                   _ptr(z), _ptr(y), _ptr(state), ctypes.byref(d), ctypes.c_void_p(stream))
     if st != SELSCAN_OK:
         raise SelscanError(st, "selective_scan_step")
     return y

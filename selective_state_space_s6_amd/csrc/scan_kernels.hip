@@ -1,8 +1,13 @@
 // scan_kernels.hip -- gfx950 kernels of the selective-scan forward (S6).
 //
-// Recurrence per (batch b, channel d, state n), from a zero state:
+// Recurrence per (batch b, channel d, state n), from a zero (or given) state:
 //   Abar = exp(delta * A),  Bbar = (Abar - 1)/A * B  (delta * B when A == 0),
 //   h = Abar * h + Bbar * u,  y = sum_n C h + Dskip * u,  y *= z * sigmoid(z).
+// Options: the first-order input coefficient Bbar = delta * B (Algenta "Sequence and
+// state-space models", mamba_selective_scan_step), which every kernel runs through its
+// A == 0 form (delta * B) by setting that form's constants for every state; and the step
+// size delta + bias[d] through softplus (TorchLean "Selective Mamba", step), applied once
+// per (token, channel) where delta is staged.
 // Discretisation: "state-space models" (aarnphm.xyz), section "From continuous time to
 // tokens" (ZOH); Algenta "Sequence and state-space models", section on state_space_models
 // (ssm_discretize_zoh / ssm_discretize_b with the A == 0 fallback).  Selectivity and the
@@ -53,11 +58,29 @@ namespace selscan {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = 16;        // tokens per tile
 constexpr int kRowPad = 20;      // LDS row length (floats) of a 16-token row: 16 + 4 padding
 constexpr int kPrefetchMax = 2;  // tiles of global loads kept in flight per wavefront (K <= 2)
 
 enum { MODE_SINGLE = 0, MODE_STATE = 1, MODE_APPLY = 2 };
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|); e^-|x| lies in (0, 1], so nothing
+// overflows.  log1p(e) is formed from the rounded sum t = 1 + e as log(t) * e / (t - 1), which
+// gives back the bits of e that the sum drops (Goldberg, "What every computer scientist
+// should know about floating-point arithmetic", Theorem 4); t == 1 leaves log1p(e) = e.
+__device__ __forceinline__ float softplus_f32(float x) {
+  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  const float t = 1.f + e;
+  const float lp = (t == 1.f) ? e : __builtin_amdgcn_logf(t) * kLn2 * (e * __builtin_amdgcn_rcpf(t - 1.f));
+  return fmaxf(x, 0.f) + lp;
+}
+
+// The step size a token uses: delta + bias, through softplus when sp.
+__device__ __forceinline__ float step_size(float raw, float bias, bool sp) {
+  const float x = raw + bias;
+  return sp ? softplus_f32(x) : x;
+}
 
 // ---------------------------------------------------------------------------------------
 // element types: per-token tensors travel as raw bit patterns (see the buffer loads in the
@@ -163,30 +186,33 @@ void scan_kernel(ScanParams p) {
   float dt_ti = 0.f;
   const IO* const Bti = static_cast<const IO*>(p.B);    // time-invariant: B[d][n], C[d][n]
   const IO* const Cti = static_cast<const IO*>(p.C);
+  const float bias_d = (p.delta_bias != nullptr && dvalid) ? p.delta_bias[d] : 0.f;
   if (TI) dt_ti = dvalid ? T::widen(static_cast<const IO*>(p.delta)[d]) : 0.f;
+  if (TI && p.dxf && dvalid) dt_ti = step_size(dt_ti, bias_d, p.softplus != 0);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t n = s + S * k;
     const bool ok = dvalid && n < N;
     const float a = ok ? p.A[d * N + n] : 0.f;
+    const bool first_order = a == 0.f || p.euler;     // Bbar = delta * B
     A2[k] = a * kLog2e;
-    iA[k] = (a != 0.f) ? 1.0f / a : 0.f;
-    zf[k] = (ok && a == 0.f) ? 1.f : 0.f;
-    any_zero |= (ok && a == 0.f);
+    iA[k] = first_order ? 0.f : 1.0f / a;
+    zf[k] = (ok && first_order) ? 1.f : 0.f;
+    any_zero |= (ok && first_order);
     h[k] = 0.f;
     if (TI) {
-      // Abar = exp(delta a); Bbar = expm1(delta a)/a * B (delta * B when a == 0)
+      // Abar = exp(delta a); Bbar = expm1(delta a)/a * B (delta * B when a == 0 or first order)
       const float bv = ok ? T::widen(Bti[d * p.B_sd + n]) : 0.f;
       const float cv = ok ? T::widen(Cti[d * p.C_sd + n]) : 0.f;
       Ab[k] = ok ? expf(dt_ti * a) : 1.f;
-      const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
+      const float coeff = first_order ? dt_ti : expm1f(dt_ti * a) / a;
       CB[k] = ok ? cv * coeff * bv : 0.f;
     } else {
       Ab[k] = 0.f;
       CB[k] = 0.f;
     }
   }
-  // wave-uniform: does any owned state have A == 0 (needs the delta*B form)?
+  // wave-uniform: does any owned state need the delta*B form (A == 0, or first order)?
   const bool wave_zero = __builtin_amdgcn_readfirstlane(__ballot(any_zero) != 0ull ? 1 : 0) != 0;
 
   if (MODE == MODE_APPLY) {                // carried-in state (h, or g in time-invariant form)
@@ -381,7 +407,8 @@ void scan_kernel(ScanParams p) {
       const float fu = T::from_raw(xU[SET][m]);
       sU[c * kRowPad + s + S * m] = fu;
       if (!TI) {
-        const float fd = T::from_raw(xD[SET][m]);
+        float fd = T::from_raw(xD[SET][m]);
+        if (p.dxf) fd = step_size(fd, bias_d, p.softplus != 0);   // once per (token, channel)
         sD[c * kRowPad + s + S * m] = fd;
         if (MODE == MODE_STATE) dsum += fd;      // lane sums its own tokens; reduced below
       }
@@ -462,7 +489,7 @@ void scan_kernel(ScanParams p) {
         if (TI) {   // h = Bbar * g
           const float a = p.A[d * N + n];
           const float bv = T::widen(Bti[d * p.B_sd + n]);
-          const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
+          const float coeff = (a != 0.f && !p.euler) ? expm1f(dt_ti * a) / a : dt_ti;
           hv = coeff * bv * hv;
         }
         p.last_state[(b * D + d) * N + n] = hv;
@@ -590,7 +617,10 @@ __device__ __forceinline__ void block_lds_sync() {
   __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <typename IO, int K, bool TI, int MODE>
+// DXF: the step size is transformed (delta + bias, softplus) by the wavefront that stages
+// delta, once per (token, channel), before it reaches LDS; a separate instantiation so that
+// the plain kernel carries none of it.
+template <typename IO, int K, bool TI, int MODE, bool DXF>
 __global__ __launch_bounds__(64 * coop_width<TI>::W)
 __attribute__((amdgpu_waves_per_eu(occupancy<K>::kMinWaves)))
 void scan_kernel_coop(ScanParams p) {
@@ -644,15 +674,18 @@ void scan_kernel_coop(ScanParams p) {
   const IO* const Bti = static_cast<const IO*>(p.B);
   const IO* const Cti = static_cast<const IO*>(p.C);
   if (TI) dt_ti = dvalid ? T::widen(static_cast<const IO*>(p.delta)[d]) : 0.f;
+  if (TI && p.dxf && dvalid)
+    dt_ti = step_size(dt_ti, p.delta_bias != nullptr ? p.delta_bias[d] : 0.f, p.softplus != 0);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t n = s + S * k;
     const bool ok = dvalid && n < N;
     const float a = ok ? p.A[d * N + n] : 0.f;
+    const bool first_order = a == 0.f || p.euler;     // Bbar = delta * B
     A2[k] = a * kLog2e;
-    iA[k] = (a != 0.f) ? 1.0f / a : 0.f;
-    zf[k] = (ok && a == 0.f) ? 1.f : 0.f;
-    any_zero |= (ok && a == 0.f);
+    iA[k] = first_order ? 0.f : 1.0f / a;
+    zf[k] = (ok && first_order) ? 1.f : 0.f;
+    any_zero |= (ok && first_order);
     h[k] = 0.f;
     Ab[k] = 0.f;
     CB[k] = 0.f;
@@ -660,7 +693,7 @@ void scan_kernel_coop(ScanParams p) {
       const float bv = ok ? T::widen(Bti[d * p.B_sd + n]) : 0.f;
       const float cv = ok ? T::widen(Cti[d * p.C_sd + n]) : 0.f;
       Ab[k] = ok ? expf(dt_ti * a) : 1.f;
-      const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
+      const float coeff = first_order ? dt_ti : expm1f(dt_ti * a) / a;
       CB[k] = ok ? cv * coeff * bv : 0.f;
     }
   }
@@ -728,6 +761,13 @@ void scan_kernel_coop(ScanParams p) {
   const int offQ = !onQ ? -1 : w == 3 ? 0 : LDS::kB;
   // lanes of channel vectors beyond the workgroup's W (two-wavefront groups) stage into the sink too
   const bool tlane = offT >= 0 && vq < W;
+  // step-size transform: the bias of the four channels this lane stages (delta wavefront)
+  static_assert(!(DXF && TI), "time-invariant step sizes are transformed once, at set-up");
+  float dbias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (DXF && roleT == 1 && vvalid && p.delta_bias != nullptr) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dbias[j] = p.delta_bias[d0 + 4 * vq + j];
+  }
   auto dstT = [&](int q) __attribute__((always_inline)) { return tlane ? sStage + q * LDS::kBuf + offT : sSink; };
   auto dstQ = [&](int q) __attribute__((always_inline)) { return offQ < 0 ? sSink : sStage + q * LDS::kBuf + offQ; };
 
@@ -751,8 +791,15 @@ void scan_kernel_coop(ScanParams p) {
   auto stage = [&](auto set_tag, int q) __attribute__((always_inline)) {
     constexpr int P = decltype(set_tag)::value;
     float* const dt = dstT(q);
+    float tv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dt[(4 * vq + j) * kRowPad + vr] = Qd::get(xT[P], j);
+    for (int j = 0; j < 4; ++j) tv[j] = Qd::get(xT[P], j);
+    if (DXF && roleT == 1) {                 // wave-uniform: the delta wavefront
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tv[j] = step_size(tv[j], dbias[j], p.softplus != 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dt[(4 * vq + j) * kRowPad + vr] = tv[j];
     if (!TI) {
       float* const dq = dstQ(q);
 #pragma unroll
@@ -977,7 +1024,7 @@ void scan_kernel_coop(ScanParams p) {
         if (TI) {
           const float a = p.A[d * N + n];
           const float bv = T::widen(Bti[d * p.B_sd + n]);
-          const float coeff = (a != 0.f) ? expm1f(dt_ti * a) / a : dt_ti;
+          const float coeff = (a != 0.f && !p.euler) ? expm1f(dt_ti * a) / a : dt_ti;
           hv = coeff * bv * hv;
         }
         p.last_state[(b * D + d) * N + n] = hv;
@@ -1090,13 +1137,16 @@ void step_kernel(StepParams p) {
     nok[j] = dvalid && n < p.N;
     const float a = nok[j] ? p.A[d * p.N + n] : 0.f;
     A2[j] = a * kLog2e;
-    iA[j] = a != 0.f ? 1.0f / a : 0.f;
-    zf[j] = (nok[j] && a == 0.f) ? 1.f : 0.f;
+    const bool first_order = a == 0.f || p.euler;       // Bbar = delta * B
+    iA[j] = first_order ? 0.f : 1.0f / a;
+    zf[j] = (nok[j] && first_order) ? 1.f : 0.f;
     Bt[j] = (TI && nok[j]) ? T::widen(Bv[d * p.B_sd + n]) : 0.f;
     Ct[j] = (TI && nok[j]) ? T::widen(Cv[d * p.C_sd + n]) : 0.f;
   }
   const float dskip = (dvalid && p.Dskip != nullptr) ? p.Dskip[d] : 0.f;
-  const float dt_ti = (TI && dvalid) ? T::widen(dl[d]) : 0.f;
+  const float bias_d = (p.delta_bias != nullptr && dvalid) ? p.delta_bias[d] : 0.f;
+  float dt_ti = (TI && dvalid) ? T::widen(dl[d]) : 0.f;
+  if (TI && p.dxf) dt_ti = step_size(dt_ti, bias_d, p.softplus != 0);
 
   // loads of all rows first
   float uu[kStepRows], dt[kStepRows], zz[kStepRows], h[kStepRows][4], bb[kStepRows][4], cc[kStepRows][4];
@@ -1106,6 +1156,7 @@ void step_kernel(StepParams p) {
     const bool live = dvalid && b < p.batch;
     uu[r] = live ? T::widen(u[b * p.u_sb + d]) : 0.f;
     dt[r] = TI ? dt_ti : (live ? T::widen(dl[b * p.delta_sb + d]) : 0.f);
+    if (!TI && p.dxf) dt[r] = step_size(dt[r], bias_d, p.softplus != 0);
     zz[r] = (live && zv != nullptr) ? T::widen(zv[b * p.z_sb + d]) : 0.f;
     if (VEC) {                                                   // all 4 states valid or none
       if (live && nok[0]) {
@@ -1207,12 +1258,12 @@ hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename IO, int K, bool TI, int MODE>
+template <typename IO, int K, bool TI, int MODE, bool DXF>
 hipError_t launch_scan_coop(const ScanParams& p, hipStream_t stream) {
   constexpr size_t lds = size_t(coop_lds<K, TI, MODE>::total) * sizeof(float);
   if (lds > 65536) {   // above the default dynamic-LDS limit: opt in once per kernel
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&scan_kernel_coop<IO, K, TI, MODE>),
+        reinterpret_cast<const void*>(&scan_kernel_coop<IO, K, TI, MODE, DXF>),
         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (attr != hipSuccess) return attr;
   }
@@ -1220,17 +1271,22 @@ hipError_t launch_scan_coop(const ScanParams& p, hipStream_t stream) {
   const int64_t groups = (p.D + kCh - 1) / kCh;
   const int64_t blocks = p.batch * (MODE == MODE_STATE ? p.n_chunks - 1 : p.n_chunks) * groups;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((scan_kernel_coop<IO, K, TI, MODE>), dim3(unsigned(blocks)), dim3(64 * coop_width<TI>::W), lds,
-                     stream, p);
+  hipLaunchKernelGGL((scan_kernel_coop<IO, K, TI, MODE, DXF>), dim3(unsigned(blocks)), dim3(64 * coop_width<TI>::W),
+                     lds, stream, p);
   return hipGetLastError();
 }
 
 template <typename IO, bool TI, int MODE>
 hipError_t dispatch_sk(int S, int K, const ScanParams& p, hipStream_t stream) {
   if (p.pipelined && S == 16) {
-    if (K == 1) return launch_scan_coop<IO, 1, TI, MODE>(p, stream);
-    if (K == 2) return launch_scan_coop<IO, 2, TI, MODE>(p, stream);
-    if (K == 4) return launch_scan_coop<IO, 4, TI, MODE>(p, stream);
+    if (!TI && p.dxf) {
+      if (K == 1) return launch_scan_coop<IO, 1, false, MODE, true>(p, stream);
+      if (K == 2) return launch_scan_coop<IO, 2, false, MODE, true>(p, stream);
+      if (K == 4) return launch_scan_coop<IO, 4, false, MODE, true>(p, stream);
+    }
+    if (K == 1) return launch_scan_coop<IO, 1, TI, MODE, false>(p, stream);
+    if (K == 2) return launch_scan_coop<IO, 2, TI, MODE, false>(p, stream);
+    if (K == 4) return launch_scan_coop<IO, 4, TI, MODE, false>(p, stream);
   }
   if (S == 4 && K == 1) return launch_scan<IO, 4, 1, TI, MODE>(p, stream);
   if (S == 8 && K == 1) return launch_scan<IO, 8, 1, TI, MODE>(p, stream);

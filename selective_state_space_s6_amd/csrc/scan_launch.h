@@ -23,6 +23,10 @@ struct ScanParams {
   void* y;
   float* last_state;    // may be null
   const float* h0;      // initial state [batch][D][N], may be null (zero); selective only
+  const float* delta_bias;   // [D], may be null (zero)
+  int32_t euler;        // 1: Bbar = delta * B (first-order input coefficient)
+  int32_t dxf;          // 1: the step size is transformed: delta + delta_bias, then softplus if
+  int32_t softplus;     //    softplus is 1
   int64_t batch, L, D, N;
   int64_t u_sb, u_sl, delta_sb, delta_sl, z_sb, z_sl, y_sb, y_sl;
   int64_t B_sb, B_sl, B_sd, C_sb, C_sl, C_sd;
@@ -65,6 +69,10 @@ struct StepParams {
   const void* z;        // may be null
   void* y;
   float* state;         // [batch][D][N]
+  const float* delta_bias;   // [D], may be null (zero)
+  int32_t euler;        // 1: Bbar = delta * B
+  int32_t dxf;          // 1: step size delta + delta_bias, then softplus if softplus is 1
+  int32_t softplus;
   int64_t batch, D, N;
   int64_t u_sb, delta_sb, z_sb, y_sb, B_sb, B_sd, C_sb, C_sd;
   int32_t vec;          // 1: N % 4 == 0, state and per-token B/C rows aligned to 4 elements

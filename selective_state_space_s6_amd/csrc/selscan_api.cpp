@@ -50,6 +50,7 @@ int make_plan(const selscan_dims* dims, Plan* plan) {
   if (path != SELSCAN_PATH_AUTO && path != SELSCAN_PATH_SINGLE && path != SELSCAN_PATH_CHUNKED)
     return SELSCAN_ERR_UNSUPPORTED;
   if (d.chunk_len < 0 || d.chunk_len % 16 != 0) return SELSCAN_ERR_UNSUPPORTED;
+  if (d.discretization != SELSCAN_DISC_ZOH && d.discretization != SELSCAN_DISC_EULER) return SELSCAN_ERR_UNSUPPORTED;
   // y rows must not overlap (every (b, l, d) is written exactly once)
   if ((d.seqlen > 1 && d.y_sl < d.dim) || (d.batch > 1 && d.y_sb < d.seqlen * d.y_sl && d.seqlen > 0))
     return SELSCAN_ERR_UNSUPPORTED;
@@ -140,9 +141,9 @@ int check_pointers(const void* u, const void* delta, const float* A, const void*
   return SELSCAN_OK;
 }
 
-int run(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* Dskip,
-        const void* z, void* y, const float* h0, float* last_state, const selscan_dims* dims, const Plan& plan,
-        void* workspace, hipStream_t stream) {
+int run(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B, const void* C,
+        const float* Dskip, const void* z, void* y, const float* h0, float* last_state, const selscan_dims* dims,
+        const Plan& plan, void* workspace, hipStream_t stream) {
   const selscan_dims& d = *dims;
   if (d.batch == 0) return SELSCAN_OK;
   if (d.seqlen == 0) {                     // no tokens: the initial state is handed back
@@ -157,6 +158,10 @@ int run(const void* u, const void* delta, const float* A, const void* B, const v
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = z; p.y = y;
   p.last_state = last_state;
   p.h0 = h0;
+  p.delta_bias = delta_bias;
+  p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
+  p.softplus = d.delta_softplus != 0 ? 1 : 0;
+  p.dxf = (p.softplus || delta_bias != nullptr) ? 1 : 0;
   p.batch = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = d.dstate;
   p.u_sb = d.u_sb; p.u_sl = d.u_sl; p.delta_sb = d.delta_sb; p.delta_sl = d.delta_sl;
   p.z_sb = d.z_sb; p.z_sl = d.z_sl; p.y_sb = d.y_sb; p.y_sl = d.y_sl;
@@ -202,9 +207,10 @@ int run(const void* u, const void* delta, const float* A, const void* B, const v
 
 // The forward pass with an optional initial state.  A missing workspace is allocated
 // stream-ordered when allow_alloc, else reported.
-int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* Dskip,
-             const void* z, void* y, const float* h0, float* last_state, const selscan_dims* dims, void* workspace,
-             size_t workspace_bytes, bool allow_alloc, hipStream_t stream) {
+int fwd_impl(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B,
+             const void* C, const float* Dskip, const void* z, void* y, const float* h0, float* last_state,
+             const selscan_dims* dims, void* workspace, size_t workspace_bytes, bool allow_alloc,
+             hipStream_t stream) {
   Plan plan;
   int st = make_plan(dims, &plan);
   if (st != SELSCAN_OK) return st;
@@ -214,16 +220,17 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
     if (plan.ti) return SELSCAN_ERR_UNSUPPORTED;      // the time-invariant kernels keep a scaled state
     if (!aligned(h0, 4)) return SELSCAN_ERR_ALIGN;
   }
+  if (delta_bias != nullptr && !aligned(delta_bias, 4)) return SELSCAN_ERR_ALIGN;
   const bool need_ws = plan.chunked && dims->batch > 0 && dims->seqlen > 0;
   if (!need_ws || workspace != nullptr) {
     if (need_ws && (workspace_bytes < plan.ws_bytes || !aligned(workspace, 256))) return SELSCAN_ERR_WORKSPACE;
-    return run(u, delta, A, B, C, Dskip, z, y, h0, last_state, dims, plan, workspace, stream);
+    return run(u, delta, delta_bias, A, B, C, Dskip, z, y, h0, last_state, dims, plan, workspace, stream);
   }
   if (!allow_alloc) return SELSCAN_ERR_WORKSPACE;
   void* ws = nullptr;
   hipError_t e = hipMallocAsync(&ws, plan.ws_bytes, stream);
   if (e != hipSuccess) return hip_fail(e);
-  st = run(u, delta, A, B, C, Dskip, z, y, h0, last_state, dims, plan, ws, stream);
+  st = run(u, delta, delta_bias, A, B, C, Dskip, z, y, h0, last_state, dims, plan, ws, stream);
   e = hipFreeAsync(ws, stream);
   if (st == SELSCAN_OK && e != hipSuccess) return hip_fail(e);
   return st;
@@ -255,6 +262,8 @@ void selscan_dims_init(selscan_dims* dims, int io_dtype, int64_t batch, int64_t 
   }
   d.path = SELSCAN_PATH_AUTO;
   d.chunk_len = 0;
+  d.discretization = SELSCAN_DISC_ZOH;
+  d.delta_softplus = 0;
   *dims = d;
 }
 
@@ -267,27 +276,28 @@ size_t selective_scan_workspace_size(const selscan_dims* dims) {
 int selective_scan_fwd_ws(const void* u, const void* delta, const float* A, const void* B, const void* C,
                           const float* Dskip, const void* z, void* y, float* last_state, const selscan_dims* dims,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_impl(u, delta, A, B, C, Dskip, z, y, nullptr, last_state, dims, workspace, workspace_bytes, false,
-                  static_cast<hipStream_t>(stream));
+  return fwd_impl(u, delta, nullptr, A, B, C, Dskip, z, y, nullptr, last_state, dims, workspace, workspace_bytes,
+                  false, static_cast<hipStream_t>(stream));
 }
 
 int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                        const float* Dskip, const void* z, void* y, float* last_state, const selscan_dims* dims,
                        void* stream) {
-  return fwd_impl(u, delta, A, B, C, Dskip, z, y, nullptr, last_state, dims, nullptr, 0, true,
+  return fwd_impl(u, delta, nullptr, A, B, C, Dskip, z, y, nullptr, last_state, dims, nullptr, 0, true,
                   static_cast<hipStream_t>(stream));
 }
 
-int selective_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                          const float* Dskip, const void* z, void* y, const float* initial_state, float* last_state,
-                          const selscan_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_impl(u, delta, A, B, C, Dskip, z, y, initial_state, last_state, dims, workspace, workspace_bytes,
-                  workspace == nullptr, static_cast<hipStream_t>(stream));
+int selective_scan_fwd_ex(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B,
+                          const void* C, const float* Dskip, const void* z, void* y, const float* initial_state,
+                          float* last_state, const selscan_dims* dims, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return fwd_impl(u, delta, delta_bias, A, B, C, Dskip, z, y, initial_state, last_state, dims, workspace,
+                  workspace_bytes, workspace == nullptr, static_cast<hipStream_t>(stream));
 }
 
-int selective_scan_step(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                        const float* Dskip, const void* z, void* y, float* state, const selscan_dims* dims,
-                        void* stream) {
+int selective_scan_step(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B,
+                        const void* C, const float* Dskip, const void* z, void* y, float* state,
+                        const selscan_dims* dims, void* stream) {
   Plan plan;
   int st = make_plan(dims, &plan);
   if (st != SELSCAN_OK) return st;
@@ -295,10 +305,15 @@ int selective_scan_step(const void* u, const void* delta, const float* A, const 
   if (!state) return SELSCAN_ERR_NULL;
   st = check_pointers(u, delta, A, B, C, Dskip, z, y, state, dims->io_dtype, dims->batch == 0);
   if (st != SELSCAN_OK) return st;
+  if (delta_bias != nullptr && !aligned(delta_bias, 4)) return SELSCAN_ERR_ALIGN;
   if (dims->batch * dims->dim > (int64_t(1) << 36)) return SELSCAN_ERR_UNSUPPORTED;   // grid size
   if (dims->batch == 0) return SELSCAN_OK;
   selscan::StepParams q{};
   q.u = u; q.delta = delta; q.A = A; q.B = B; q.C = C; q.Dskip = Dskip; q.z = z; q.y = y; q.state = state;
+  q.delta_bias = delta_bias;
+  q.euler = dims->discretization == SELSCAN_DISC_EULER ? 1 : 0;
+  q.softplus = dims->delta_softplus != 0 ? 1 : 0;
+  q.dxf = (q.softplus || delta_bias != nullptr) ? 1 : 0;
   q.batch = dims->batch; q.D = dims->dim; q.N = dims->dstate;
   q.u_sb = dims->u_sb; q.delta_sb = dims->delta_sb; q.z_sb = dims->z_sb; q.y_sb = dims->y_sb;
   q.B_sb = dims->B_sb; q.B_sd = dims->B_sd; q.C_sb = dims->C_sb; q.C_sd = dims->C_sd;
@@ -316,7 +331,7 @@ const char* selective_scan_strerror(int status) {
     case SELSCAN_OK: return "success";
     case SELSCAN_ERR_NULL: return "a required pointer is NULL";
     case SELSCAN_ERR_DIMS: return "a size or stride is out of range";
-    case SELSCAN_ERR_UNSUPPORTED: return "unsupported dtype, state count, path or stride pattern";
+    case SELSCAN_ERR_UNSUPPORTED: return "unsupported dtype, state count, path, discretization or stride pattern";
     case SELSCAN_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case SELSCAN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case SELSCAN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";

@@ -67,6 +67,7 @@ def test_dims_init_contiguous():
     assert (d.B_sb, d.B_sl, d.B_sd) == (1600, 16, 0)
     t = ss.dims_init(ss.SELSCAN_F32, 4, 100, 24, 16, time_invariant=True)
     assert (t.delta_sb, t.delta_sl, t.B_sb, t.B_sl, t.B_sd, t.C_sd) == (0, 0, 0, 0, 16, 16)
+    assert (d.discretization, d.delta_softplus, t.discretization, t.delta_softplus) == (0, 0, 0, 0)
 
 
 FAKE = ctypes.c_void_p(0x100000)          # never dereferenced: every call below fails on the host
@@ -103,6 +104,8 @@ def test_null_pointers():
     ("io_dtype", 7, ss.SELSCAN_ERR_UNSUPPORTED),
     ("path", 9, ss.SELSCAN_ERR_UNSUPPORTED),
     ("chunk_len", 24, ss.SELSCAN_ERR_UNSUPPORTED),
+    ("discretization", 2, ss.SELSCAN_ERR_UNSUPPORTED),
+    ("discretization", -1, ss.SELSCAN_ERR_UNSUPPORTED),
     ("B_sd", 16, ss.SELSCAN_ERR_UNSUPPORTED),      # B varying with both token and channel
     ("y_sl", 0, ss.SELSCAN_ERR_UNSUPPORTED),       # overlapping output rows
     ("y_sb", 8, ss.SELSCAN_ERR_UNSUPPORTED),
@@ -151,8 +154,8 @@ def test_empty_batch_is_a_no_op():
     assert call(d) == ss.SELSCAN_OK                    # nothing enqueued, no workspace needed
 
 
-def call_ex(dims, h0=FAKE, ws=None, ws_bytes=0):
-    return ss.lib().selective_scan_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, h0, None,
+def call_ex(dims, h0=FAKE, ws=None, ws_bytes=0, bias=None):
+    return ss.lib().selective_scan_fwd_ex(FAKE, FAKE, bias, FAKE, FAKE, FAKE, None, None, FAKE, h0, None,
                                           ctypes.byref(dims), ws, ws_bytes, None)
 
 
@@ -166,9 +169,9 @@ def test_initial_state_errors():
     assert call_ex(bad) == ss.SELSCAN_ERR_DIMS
 
 
-def call_step(dims, state=FAKE):
-    return ss.lib().selective_scan_step(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, state, ctypes.byref(dims),
-                                        None)
+def call_step(dims, state=FAKE, bias=None):
+    return ss.lib().selective_scan_step(FAKE, FAKE, bias, FAKE, FAKE, FAKE, None, None, FAKE, state,
+                                        ctypes.byref(dims), None)
 
 
 def test_step_errors():
@@ -178,3 +181,14 @@ def test_step_errors():
     assert call_step(one, state=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
     assert call_step(ss.dims_init(ss.SELSCAN_F32, 2, 1, 8, 65)) == ss.SELSCAN_ERR_UNSUPPORTED
     assert call_step(ss.dims_init(ss.SELSCAN_F32, 0, 1, 8, 16)) == ss.SELSCAN_OK             # empty batch
+    assert call_step(one, bias=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
+    bad = ss.dims_init(ss.SELSCAN_F32, 2, 1, 8, 16)
+    bad.discretization = 5
+    assert call_step(bad) == ss.SELSCAN_ERR_UNSUPPORTED
+
+
+def test_step_size_options_errors():
+    d = good_dims()
+    assert call_ex(d, h0=None, ws=FAKE, ws_bytes=ss.workspace_size(d), bias=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
+    e = good_dims(discretization=ss.DISCRETIZATIONS["euler"], delta_softplus=1)
+    assert call_ex(e, h0=None, ws=FAKE, ws_bytes=ss.workspace_size(e) - 1) == ss.SELSCAN_ERR_WORKSPACE
