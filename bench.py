@@ -1,6 +1,7 @@
 """Benchmark of the S6 selective-scan forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--step-size given|softplus] [--discretization zoh|euler]
 
 A step is one selective_scan_fwd call over the whole workload (every row of the hot
 path: discretisation, recurrence, readout, feed-through, gate, store) with its inputs
@@ -11,10 +12,16 @@ Inputs are seeded synthetic data (s6_workloads), copied to the GPU once before t
 Prints ONE JSON line: elements/s (batch*L*D*N per second) as `value`, the algorithmic HBM
 bandwidth, the roofline of the scan kernel, and the CPU oracle timed on this host on a
 bounded sample of the same workload.
+
+Options measure the discretisation variants on the same workload: --step-size softplus
+feeds the pre-activation (raw step sizes and a per-channel bias, s6_workloads.raw_step_sizes)
+and lets the kernel apply softplus(raw + bias); --discretization euler uses the first-order
+input coefficient.  The defaults are the plain ZOH scan with given step sizes.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -41,14 +48,21 @@ COUNTERS = os.path.join(ROOT, "profiles", "scan_counters.json")
 #   per (b, l, d):    feed-through FMA (1); gate: -z*log2e (1) + exp (4) + 1+e (1) + rcp (4)
 #                     + z*r (1) + y*silu (1)                                          = 1 + 12
 #   time-invariant:   per (b, l, d, n): state FMA (1) + readout FMA (1)               = 2
-SLOTS_PER_ELEMENT = {"selective": 10, "time_invariant": 2}
+#   first order (Euler), per (b, l, d, n): delta*A (1) + exp (4) + B*(delta u) (1) + state FMA (1)
+#                     + readout FMA (1) = 8, plus delta*u (1) per (b, l, d)
+#   softplus step size, per (b, l, d): + bias (1), |x|*log2e (1), exp (4), 1+e (1), log (4),
+#                     t-1 (1), rcp (4), two products (2), max (1), add (1)            = 20
+SLOTS_PER_ELEMENT = {"selective": 10, "time_invariant": 2, "euler": 8}
 SLOTS_PER_TOKEN_D = 1
 SLOTS_PER_TOKEN_GATE = 12
+SLOTS_PER_TOKEN_EULER = 1
+SLOTS_PER_TOKEN_SOFTPLUS = 20
 
 
-def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool) -> int:
+def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool, bias: bool = False) -> int:
     """Bytes the method must move: u, delta, z read once and y written once per (b, l, d);
-    B and C once; A, Dskip once; last_state once.  No expanded (x N) state touches HBM."""
+    B and C once; A, Dskip (and a step-size bias) once; last_state once.  No expanded (x N)
+    state touches HBM."""
     b, L, D, N = inp.shape
     es = 2 if inp.io == "bf16" else 4
     tok = b * L * D
@@ -60,26 +74,32 @@ def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool) -> int:
     total += D * N * 4                                          # A
     if inp.Dskip is not None:
         total += D * 4
+    if bias:
+        total += D * 4
     if want_last:
         total += b * D * N * 4
     return total
 
 
-def decode_bytes(inp: s6_workloads.Inputs) -> int:
+def decode_bytes(inp: s6_workloads.Inputs, bias: bool = False) -> int:
     """One decode step: the running state [batch, D, N] fp32 read and written once; u,
     delta, z read and y written per (b, d); B, C per (b, n); A, Dskip once."""
     b, _, D, N = inp.shape
     es = 2 if inp.io == "bf16" else 4
     total = 2 * b * D * N * 4
     total += b * D * es * (3 + (1 if inp.z is not None else 0))
-    total += 2 * b * N * es + D * N * 4 + (D * 4 if inp.Dskip is not None else 0)
+    total += 2 * b * N * es + D * N * 4 + (D * 4 if inp.Dskip is not None else 0) + (D * 4 if bias else 0)
     return total
 
 
-def algorithmic_slots(inp: s6_workloads.Inputs) -> int:
+def algorithmic_slots(inp: s6_workloads.Inputs, softplus: bool = False, euler: bool = False) -> int:
     b, L, D, N = inp.shape
-    per_el = SLOTS_PER_ELEMENT["time_invariant" if inp.ti else "selective"]
+    per_el = SLOTS_PER_ELEMENT["time_invariant" if inp.ti else "euler" if euler else "selective"]
     slots = per_el * b * L * D * N
+    if euler and not inp.ti:
+        slots += SLOTS_PER_TOKEN_EULER * b * L * D
+    if softplus:
+        slots += SLOTS_PER_TOKEN_SOFTPLUS * (D if inp.ti else b * L * D)
     if inp.Dskip is not None:
         slots += SLOTS_PER_TOKEN_D * b * L * D
     if inp.z is not None:
@@ -106,9 +126,11 @@ def measured_traffic(workload: str, per_launch_alg_bytes: int):
     return int(entry["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0, h0=None):
+def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0, h0=None, bias=None, softplus=False,
+                 euler=False):
     """The oracle (fp64, as it stands) on a bounded sample of the workload's channels,
-    timed on this host; scaled to elements/s.  ``h0``: initial state [batch, D, N]."""
+    timed on this host; scaled to elements/s.  ``h0``: initial state [batch, D, N];
+    ``bias``/``softplus``/``euler``: the step-size and discretisation options."""
     import oracle
     cores = min(16, os.cpu_count() or 1)
     b, L, D, N = inp.shape
@@ -121,7 +143,8 @@ def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0, h0=None):
         t0 = time.perf_counter()
         oracle.fwd(sub.u, sub.delta, sub.A, sub.B, sub.C, sub.Dskip, sub.z, time_invariant=sub.ti,
                    h0=None if h0 is None else np.ascontiguousarray(h0[:, ch]), want_last=h0 is not None,
-                   nthreads=cores)
+                   delta_bias=None if bias is None else np.ascontiguousarray(bias[ch]), delta_softplus=softplus,
+                   euler=euler, nthreads=cores)
         t_used = time.perf_counter() - t0
         if t_used >= target_s * 0.5 or nch >= D:
             break
@@ -139,6 +162,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="longctx_bf16", choices=sorted(s6_workloads.WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "single", "chunked"])
+    ap.add_argument("--step-size", default="given", choices=["given", "softplus"],
+                    help="softplus: the kernel computes softplus(raw + bias) from a pre-activation")
+    ap.add_argument("--discretization", default="zoh", choices=["zoh", "euler"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -156,8 +182,15 @@ def main():
 
     spec = s6_workloads.spec(args.workload)
     inp = s6_workloads.generate(args.workload)
+    softplus = args.step_size == "softplus"
+    euler = args.discretization == "euler"
+    bias_np = None
+    if softplus:
+        raw, bias_np = s6_workloads.raw_step_sizes(inp)
+        inp = dataclasses.replace(inp, delta=raw)
+    opts = variant_options(args)
     if spec.get("decode"):
-        return bench_decode(args, inp)
+        return bench_decode(args, inp, bias_np, opts)
     want_last = bool(spec["last"])
     b, L, D, N = inp.shape
     E = b * L * D * N
@@ -172,6 +205,7 @@ def main():
     u, delta, B, C, z = dev(inp.u), dev(inp.delta), dev(inp.B), dev(inp.C), dev(inp.z)
     A = torch.from_numpy(inp.A).cuda()
     Ds = None if inp.Dskip is None else torch.from_numpy(inp.Dskip).cuda()
+    bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
     y = torch.empty_like(u)
     last = torch.empty((b, D, N), dtype=torch.float32, device="cuda") if want_last else None
     torch.cuda.synchronize()
@@ -179,7 +213,8 @@ def main():
 
     def step():
         ss.selective_scan_fwd(u, delta, A, B, C, Ds, z, y=y, last_state=last, path=args.path,
-                              stream=stream.cuda_stream)
+                              stream=stream.cuda_stream, delta_bias=bias, delta_softplus=softplus,
+                              discretization=args.discretization)
 
     for _ in range(args.warmup):
         step()
@@ -202,12 +237,12 @@ def main():
 
     dims = ss.make_dims(u, delta, A, B, C, z, y, path=args.path)
     chunked = ss.workspace_size(dims) > 0
-    alg_bytes = algorithmic_bytes(inp, want_last)
-    slots = algorithmic_slots(inp)
+    alg_bytes = algorithmic_bytes(inp, want_last, bias=softplus)
+    slots = algorithmic_slots(inp, softplus=softplus, euler=euler)
     launch_s = launch_ms * 1e-3
     hbm_gbs = alg_bytes / launch_s / 1e9
     alu_tflops = 2.0 * slots / launch_s / 1e12
-    traffic = measured_traffic(args.workload, alg_bytes)
+    traffic = measured_traffic(args.workload + opts["suffix"], alg_bytes)
     # the binding roof: the larger of the two lower bounds on time
     t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
     t_alu = 2.0 * slots / (VALU_PEAK_TFLOPS * 1e12)
@@ -233,7 +268,8 @@ def main():
         "data": "synthetic (seeded, s6_workloads: %s)" % args.workload,
         "config": {"workload": args.workload, "batch": b, "seq_len": L, "dim": D, "dstate": N, "io": io,
                    "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
-                   "last_state": want_last, "time_invariant": inp.ti, "path": "chunked" if chunked else "single"},
+                   "last_state": want_last, "time_invariant": inp.ti, "path": "chunked" if chunked else "single",
+                   "step_size": opts["step_size"], "discretization": args.discretization},
         "kernel_ms": launch_ms,
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
@@ -242,8 +278,16 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp)
+        out["cpu_baseline"] = cpu_baseline(inp, bias=bias_np, softplus=softplus, euler=euler)
     print(json.dumps(out), flush=True)
+
+
+def variant_options(args) -> dict:
+    """Names of the chosen options: the config entry and the key suffix of the committed
+    counter summary ("" for the defaults)."""
+    suffix = ("+softplus" if args.step_size == "softplus" else "") + ("+euler" if args.discretization == "euler" else "")
+    return {"suffix": suffix,
+            "step_size": "softplus(delta + bias[d]) in the kernel" if args.step_size == "softplus" else "given"}
 
 
 def copy_calibration():
@@ -269,7 +313,7 @@ def roofline(alg_bytes: int, slots: int, seconds: float, traffic):
             "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
 
 
-def bench_decode(args, inp):
+def bench_decode(args, inp, bias_np, opts):
     """One recurrent decode step per call (selective_scan_step) over the workload's batch:
     one token per batch row, the running state updated in place."""
     import torch
@@ -288,12 +332,15 @@ def bench_decode(args, inp):
     Ds = None if inp.Dskip is None else torch.from_numpy(inp.Dskip).cuda()
     h0 = s6_workloads.running_state(inp)
     state = torch.from_numpy(h0).cuda()
+    bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
+    softplus = bias_np is not None
     y = torch.empty_like(u)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step():
-        ss.selective_scan_step(u, delta, A, B, C, Ds, z, y=y, state=state, stream=stream.cuda_stream)
+        ss.selective_scan_step(u, delta, A, B, C, Ds, z, y=y, state=state, stream=stream.cuda_stream,
+                               delta_bias=bias, delta_softplus=softplus, discretization=args.discretization)
 
     for _ in range(args.warmup):
         step()
@@ -312,8 +359,8 @@ def bench_decode(args, inp):
     if args.copy_calibration:
         copy_calibration()
     E = b * D * N
-    alg = decode_bytes(inp)
-    slots = algorithmic_slots(inp)
+    alg = decode_bytes(inp, bias=softplus)
+    slots = algorithmic_slots(inp, softplus=softplus, euler=args.discretization == "euler")
     out = {
         "metric": METRIC,
         "value": E * args.steps / wall,
@@ -329,16 +376,18 @@ def bench_decode(args, inp):
         "data": "synthetic (seeded, s6_workloads: %s)" % args.workload,
         "config": {"workload": args.workload, "batch": b, "seq_len": 1, "dim": D, "dstate": N, "io": io,
                    "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
-                   "mode": "decode step (state in place)"},
+                   "mode": "decode step (state in place)", "step_size": opts["step_size"],
+                   "discretization": args.discretization},
         "kernel_ms": launch_ms,
         "hbm_gbs": round(alg / (launch_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(alg / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": alg,
         "algorithmic_slots": slots,
-        "roofline": roofline(alg, slots, launch_ms * 1e-3, measured_traffic(args.workload, alg)),
+        "roofline": roofline(alg, slots, launch_ms * 1e-3, measured_traffic(args.workload + opts["suffix"], alg)),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, h0=h0)
+        out["cpu_baseline"] = cpu_baseline(inp, h0=h0, bias=bias_np, softplus=softplus,
+                                           euler=args.discretization == "euler")
     print(json.dumps(out), flush=True)
 
 
