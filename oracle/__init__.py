@@ -14,6 +14,9 @@ Two independent statements of the method live here:
   of the TorchLean "Selective Mamba" page (``step``).  Options: an initial state, the
   first-order input coefficient Bbar = delta * B (Algenta, ``mamba_selective_scan_step``),
   and the step-size transform softplus(delta + per-channel bias) (TorchLean, ``step``).
+* ``bwd`` -- the gradients of that forward (its vector-Jacobian product) by the reverse-time
+  recurrence over the cached states, as the rustytorch commit log describes its hand-written
+  VJP of the selective scan.
 * ``conv_ti`` -- for fixed (time-invariant) coefficients, the causal-convolution form of
   the same layer with lag kernel K_k = C Abar^k Bbar ("state-space models", section "One
   recurrence, one convolution"), written with numpy in float64 and sharing no code with
@@ -60,6 +63,8 @@ class OracleLib:
             getattr(lib, name).argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, dp, dp]
         lib.ssm_oracle_softplus.restype = ctypes.c_double
         lib.ssm_oracle_softplus.argtypes = [ctypes.c_double]
+        lib.ssm_oracle_bwd.restype = ctypes.c_int
+        lib.ssm_oracle_bwd.argtypes = [fp] * 11 + [dp] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int] * 3
         self.lib = lib
         self.path = path
 
@@ -125,6 +130,43 @@ class OracleLib:
         return y, last
 
 
+    def bwd(self, u, delta, A, B, C, Dskip=None, z=None, *, dy, dlast=None, h0=None, delta_bias=None, euler=False,
+            delta_softplus=False, time_invariant=False):
+        """Gradients of the forward pass (the vector-Jacobian product with dy, plus dlast at the
+        final state), in float64, by the reverse-time recurrence over the cached states.
+        Returns a dict with du, ddelta, dA, dB, dC, dz (always), dDskip (if Dskip),
+        ddelta_bias (if delta_bias) and dh0 (if h0); shapes follow the inputs."""
+        u, delta, A, B, C, Dskip, z, h0, delta_bias = map(_f32, (u, delta, A, B, C, Dskip, z, h0, delta_bias))
+        dy, dlast = _f32(dy), _f32(dlast)
+        batch, L, D = u.shape
+        N = A.shape[1]
+        assert dy.shape == (batch, L, D)
+        if dlast is not None:
+            assert dlast.shape == (batch, D, N)
+        out = {"du": np.empty((batch, L, D)), "dz": np.empty((batch, L, D)),
+               "ddelta": np.empty((D,) if time_invariant else (batch, L, D)), "dA": np.empty((D, N)),
+               "dB": np.empty((D, N) if time_invariant else (batch, L, N)),
+               "dC": np.empty((D, N) if time_invariant else (batch, L, N))}
+        if Dskip is not None:
+            out["dDskip"] = np.empty(D)
+        if delta_bias is not None:
+            out["ddelta_bias"] = np.empty(D)
+        if h0 is not None:
+            out["dh0"] = np.empty((batch, D, N))
+        dpt = lambda k: out[k].ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if k in out else None
+        rc = self.lib.ssm_oracle_bwd(
+            _fptr(u), _fptr(delta), _fptr(A), _fptr(B), _fptr(C), _fptr(Dskip), _fptr(z), _fptr(h0),
+            _fptr(delta_bias), _fptr(dy), _fptr(dlast),
+            dpt("du"), dpt("ddelta"), dpt("dA"), dpt("dB"), dpt("dC"), dpt("dDskip"), dpt("dz"),
+            dpt("ddelta_bias"), dpt("dh0"), batch, L, D, N, 1 if time_invariant else 0, 1 if euler else 0,
+            1 if delta_softplus else 0)
+        if rc != 0:
+            raise RuntimeError("ssm_oracle_bwd failed with %d" % rc)
+        if z is None:
+            out["dz"][...] = 0.0
+        return out
+
+
 def _load() -> OracleLib:
     global _lib
     if _lib is None:
@@ -161,6 +203,13 @@ def fwd(u, delta, A, B, C, Dskip=None, z=None, *, h0=None, delta_bias=None, eule
     return _load().fwd(u, delta, A, B, C, Dskip, z, h0=h0, delta_bias=delta_bias, euler=euler,
                        delta_softplus=delta_softplus, time_invariant=time_invariant, want_last=want_last,
                        nthreads=nthreads)
+
+
+def bwd(u, delta, A, B, C, Dskip=None, z=None, *, dy, dlast=None, h0=None, delta_bias=None, euler=False,
+        delta_softplus=False, time_invariant=False):
+    """Gradients of the forward pass from the default oracle library; see ``OracleLib.bwd``."""
+    return _load().bwd(u, delta, A, B, C, Dskip, z, dy=dy, dlast=dlast, h0=h0, delta_bias=delta_bias, euler=euler,
+                       delta_softplus=delta_softplus, time_invariant=time_invariant)
 
 
 def kernel_element(c: float, abar_power: float, bbar: float) -> float:

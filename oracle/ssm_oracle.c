@@ -56,6 +56,18 @@
  *     is zeroState).  A one-token call is the recurrent decode step (aarnphm, "One
  *     recurrence, one convolution": the recurrent form generates one token at a time).
  *
+ * Backward pass (ssm_oracle_bwd): the vector-Jacobian product of the same forward, taken
+ * by the reverse-time recurrence over the cached state trajectory that the rustytorch commit
+ * log describes for its hand-written VJP of the selective scan ("Hand-written VJP of the
+ * selective-scan forward": the scan differentiated analytically, backwards in time, over the
+ * cached h).  With lambda_t = dL/dh_t (the total derivative through every later token):
+ *     lambda_t = dyp_t * C_t + Abar_{t+1} * lambda_{t+1}        (lambda_L-1 picks up dlast)
+ * where dyp_t = dy_t * SiLU(z_t) is the derivative at the pre-gate output; every input's
+ * gradient is then the chain rule through one step of the forward:
+ *     h_t = Abar_t h_{t-1} + c_t B_t u_t,   Abar_t = exp(delta_t a),  c_t = Bbar_t / B_t,
+ * with dc/ddelta = Abar_t (ZOH, also at a == 0) or 1 (first order), and dc/da =
+ * (delta Abar_t - c_t)/a (ZOH, limit delta^2/2 at a == 0) or 0 (first order).
+ *
  * Layouts (row-major, all contiguous):
  *   u, delta, z, y : [batch][L][D]           (time-invariant mode: delta is [D])
  *   B, C           : [batch][L][N]           (time-invariant mode: [D][N])
@@ -205,3 +217,122 @@ void ssm_oracle_discretize_euler(double a, double b, double dt, double* abar, do
 
 /* softplus of one value, exposed so the printed values can be checked on their own. */
 double ssm_oracle_softplus(double x) { return softplus(x); }
+
+
+/* ------------------------------------------------------------------------------------- */
+/* Backward pass.  Gradients (all double, all contiguous):
+ *   du, ddelta, dz : [batch][L][D]   (ddelta is the gradient of the GIVEN delta, i.e. of the
+ *                                     softplus argument's raw part when delta_softplus)
+ *   dB, dC         : [batch][L][N]   (time-invariant mode: [D][N])
+ *   dA             : [D][N]
+ *   dDskip, ddelta_bias : [D]       (may be NULL)
+ *   dh0            : [batch][D][N]   (may be NULL)
+ *   ddelta in time-invariant mode: [D]
+ * dy: [batch][L][D] float; dlast: [batch][D][N] float or NULL (the gradient reaching the
+ * final state).  Single-threaded over (b, d) in a fixed order, so the sums over channels
+ * (dB, dC) and over batch and tokens (dA, dDskip, ddelta_bias) have a fixed order. */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* d c / d a for the ZOH coefficient c = expm1(dt a)/a: (dt e^{dt a} - c)/a, written through
+ * x = dt a as dt^2 * (x e^x - expm1(x)) / x^2, with its series 1/2 + x/3 + x^2/8 + x^3/30
+ * + x^4/144 where |x| is small enough for the closed form to cancel. */
+static double zoh_coeff_da(double dt, double a) {
+  const double x = dt * a;
+  if (fabs(x) < 1e-3) return dt * dt * (0.5 + x * (1.0 / 3.0 + x * (1.0 / 8.0 + x * (1.0 / 30.0 + x / 144.0))));
+  return dt * dt * (x * exp(x) - expm1(x)) / (x * x);
+}
+
+int ssm_oracle_bwd(const float* u, const float* delta, const float* A, const float* B, const float* C,
+                   const float* Dskip, const float* z, const float* h0, const float* delta_bias,
+                   const float* dy, const float* dlast,
+                   double* du, double* ddelta, double* dA, double* dB, double* dC, double* dDskip,
+                   double* dz, double* ddelta_bias, double* dh0,
+                   int64_t batch, int64_t L, int64_t D, int64_t N, int time_invariant, int euler,
+                   int delta_softplus) {
+  if (batch < 0 || L < 0 || D <= 0 || N <= 0) return -1;
+  if (!A || !du || !ddelta || !dA || !dB || !dC || !dz) return -1;
+  if (batch * L > 0 && (!u || !delta || !B || !C || !dy)) return -1;
+  const int ti = time_invariant;
+  memset(du, 0, sizeof(double) * (size_t)(batch * L * D));
+  memset(dz, 0, sizeof(double) * (size_t)(batch * L * D));
+  memset(ddelta, 0, sizeof(double) * (size_t)(ti ? D : batch * L * D));
+  memset(dB, 0, sizeof(double) * (size_t)(ti ? D * N : batch * L * N));
+  memset(dC, 0, sizeof(double) * (size_t)(ti ? D * N : batch * L * N));
+  memset(dA, 0, sizeof(double) * (size_t)(D * N));
+  if (dDskip) memset(dDskip, 0, sizeof(double) * (size_t)D);
+  if (ddelta_bias) memset(ddelta_bias, 0, sizeof(double) * (size_t)D);
+  if (dh0) memset(dh0, 0, sizeof(double) * (size_t)(batch * D * N));
+  if (batch == 0) return 0;
+  double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));   /* h_{-1} .. h_{L-1} */
+  double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!hs || !lam) { free(hs); free(lam); return -2; }
+  oracle_job j;                       /* only the fields step_size reads */
+  memset(&j, 0, sizeof(j));
+  j.delta_bias = delta_bias; j.delta_softplus = delta_softplus;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      /* forward, caching the trajectory */
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? (double)h0[(b * D + d) * N + n] : 0.0;
+      for (int64_t l = 0; l < L; ++l) {
+        const int64_t tok = (b * L + l) * D + d;
+        const double uu = (double)u[tok];
+        const double dt = step_size(&j, ti ? (double)delta[d] : (double)delta[tok], d);
+        const float* Brow = ti ? B + d * N : B + (b * L + l) * N;
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = (double)A[d * N + n];
+          const double c = euler ? dt : zoh_input_coeff(dt, a);
+          hs[(l + 1) * N + n] = exp(dt * a) * hs[l * N + n] + c * (double)Brow[n] * uu;
+        }
+      }
+      /* reverse */
+      for (int64_t n = 0; n < N; ++n) lam[n] = dlast ? (double)dlast[(b * D + d) * N + n] : 0.0;
+      for (int64_t l = L - 1; l >= 0; --l) {
+        const int64_t tok = (b * L + l) * D + d;
+        const double uu = (double)u[tok];
+        const double raw = ti ? (double)delta[d] : (double)delta[tok];
+        const double dt = step_size(&j, raw, d);
+        const float* Brow = ti ? B + d * N : B + (b * L + l) * N;
+        const float* Crow = ti ? C + d * N : C + (b * L + l) * N;
+        double* dBrow = ti ? dB + d * N : dB + (b * L + l) * N;
+        double* dCrow = ti ? dC + d * N : dC + (b * L + l) * N;
+        /* pre-gate output and the gate */
+        double s = 0.0;
+        for (int64_t n = 0; n < N; ++n) s += (double)Crow[n] * hs[(l + 1) * N + n];
+        const double yp = s + (Dskip ? (double)Dskip[d] * uu : 0.0);
+        double dyp = (double)dy[tok];
+        if (z) {
+          const double zz = (double)z[tok], sg = sigmoid(zz);
+          dz[tok] = dyp * yp * sg * (1.0 + zz * (1.0 - sg));
+          dyp *= zz * sg;
+        }
+        if (Dskip) dDskip[d] += dyp * uu;
+        double g_u = Dskip ? (double)Dskip[d] * dyp : 0.0, g_dt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = (double)A[d * N + n];
+          const double abar = exp(dt * a);
+          const double c = euler ? dt : zoh_input_coeff(dt, a);
+          const double dc_ddt = euler ? 1.0 : abar;
+          const double dc_da = euler ? 0.0 : (a == 0.0 ? 0.5 * dt * dt : zoh_coeff_da(dt, a));
+          const double hp = hs[l * N + n], bn = (double)Brow[n];
+          const double ln = dyp * (double)Crow[n] + lam[n];        /* lambda_t */
+          dCrow[n] += dyp * hs[(l + 1) * N + n];
+          dBrow[n] += ln * c * uu;
+          g_u += ln * c * bn;
+          g_dt += ln * (a * abar * hp + dc_ddt * bn * uu);
+          dA[d * N + n] += ln * (dt * abar * hp + dc_da * bn * uu);
+          lam[n] = abar * ln;                                       /* carried to token l-1 */
+        }
+        du[tok] = g_u;
+        const double g_raw = g_dt * (delta_softplus ? sigmoid(raw + (delta_bias ? (double)delta_bias[d] : 0.0)) : 1.0);
+        if (ti) ddelta[d] += g_raw;
+        else ddelta[tok] = g_raw;
+        if (ddelta_bias) ddelta_bias[d] += g_raw;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = lam[n];
+    }
+  }
+  free(hs);
+  free(lam);
+  return 0;
+}
