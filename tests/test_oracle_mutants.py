@@ -23,6 +23,9 @@ from tests.test_oracle_pins import brute_force, rel_err
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssm_oracle.c")
 
+# the forward's decay line (the backward has a line of the same text)
+FWD_ABAR = "const double abar = exp(dt * a);\n      const double bbar"
+
 MUTANTS = {
     "first_order_input_coeff": ("return expm1(dt * a) / a;", "return dt;"),
     "readout_before_update": (
@@ -30,7 +33,7 @@ MUTANTS = {
         "      acc += (double)Crow[n] * h[n];\n      h[n] = abar * h[n] + bbar * uu;"),
     "dropped_feedthrough": ("if (j->Dskip) yv += (double)j->Dskip[d] * uu;", ";"),
     "sigmoid_instead_of_silu": ("yv *= zz / (1.0 + exp(-zz));", "yv *= 1.0 / (1.0 + exp(-zz));"),
-    "wrong_sign_decay": ("const double abar = exp(dt * a);", "const double abar = exp(-dt * a);"),
+    "wrong_sign_decay": (FWD_ABAR, FWD_ABAR.replace("exp(dt * a)", "exp(-dt * a)")),
     "b_and_c_swapped": ("const double bbar = (j->euler ? dt : zoh_input_coeff(dt, a)) * (double)Brow[n];",
                         "const double bbar = (j->euler ? dt : zoh_input_coeff(dt, a)) * (double)Crow[n];"),
     "a_transposed": ("const double a = (double)j->A[d * N + n];", "const double a = (double)j->A[n * D + d];"),
@@ -38,7 +41,7 @@ MUTANTS = {
     "feedthrough_after_gate": (
         "    if (j->Dskip) yv += (double)j->Dskip[d] * uu;\n    if (j->z) {\n      const double zz = (double)j->z[tok];\n      yv *= zz / (1.0 + exp(-zz));\n    }",
         "    if (j->z) {\n      const double zz = (double)j->z[tok];\n      yv *= zz / (1.0 + exp(-zz));\n    }\n    if (j->Dskip) yv += (double)j->Dskip[d] * uu;"),
-    "euler_decay": ("const double abar = exp(dt * a);", "const double abar = 1.0 + dt * a;"),
+    "euler_decay": (FWD_ABAR, FWD_ABAR.replace("exp(dt * a)", "1.0 + dt * a")),
     "ti_b_layout_transposed": ("const float* Brow = j->time_invariant ? j->B + d * N : j->B + (b * L + l) * N;",
                                "const float* Brow = j->time_invariant ? j->B + d : j->B + (b * L + l) * N;"),
     "state_not_reset": ("h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 0.0;",
@@ -47,8 +50,7 @@ MUTANTS = {
     "initial_state_wrong_index": ("h[n] = j->h0 ? (double)j->h0[(b * D + d) * N + n] : 0.0;",
                                   "h[n] = j->h0 ? (double)j->h0[(d * j->batch + b) * N + n] : 0.0;"),
     "euler_flag_ignored": ("(j->euler ? dt : zoh_input_coeff(dt, a))", "zoh_input_coeff(dt, a)"),
-    "euler_also_linearises_decay": ("const double abar = exp(dt * a);",
-                                    "const double abar = j->euler ? 1.0 + dt * a : exp(dt * a);"),
+    "euler_also_linearises_decay": (FWD_ABAR, FWD_ABAR.replace("exp(dt * a)", "j->euler ? 1.0 + dt * a : exp(dt * a)")),
     "softplus_not_applied": ("return j->delta_softplus ? softplus(x) : x;", "return x;"),
     "softplus_wrong_branch": ("log1p(exp(-fabs(x))) + fmax(x, 0.0)", "log1p(exp(-fabs(x))) + fmax(-x, 0.0)"),
     "bias_not_per_channel": ("if (j->delta_bias) x += (double)j->delta_bias[d];",
