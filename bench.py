@@ -1,7 +1,7 @@
 """Benchmark of the S6 selective-scan forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--step-size given|softplus] [--discretization zoh|euler]
+                    [--step-size given|softplus] [--discretization zoh|euler] [--backward]
 
 A step is one selective_scan_fwd call over the whole workload (every row of the hot
 path: discretisation, recurrence, readout, feed-through, gate, store) with its inputs
@@ -17,6 +17,8 @@ Options measure the discretisation variants on the same workload: --step-size so
 feeds the pre-activation (raw step sizes and a per-channel bias, s6_workloads.raw_step_sizes)
 and lets the kernel apply softplus(raw + bias); --discretization euler uses the first-order
 input coefficient.  The defaults are the plain ZOH scan with given step sizes.
+--backward times selective_scan_bwd (all gradients, from a seeded dy) on the same workload
+instead of the forward pass.
 """
 from __future__ import annotations
 
@@ -38,7 +40,8 @@ import s6_workloads  # noqa: E402
 METRIC = "scan elements/s (B*L*D*N per sec) + achieved HBM GB/s vs peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0            # MI355X published HBM3E bandwidth
 VALU_PEAK_TFLOPS = 157.3         # MI355X published fp32 vector peak (FMA = 2 flops)
-KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", "scan_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
+                  for f in ("scan_kernels.hip", "device_common.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "scan_counters.json")
 
 # Algorithmic ALU work, in FMA-slot units (one fp32 VALU op = 1 slot = 2 flop-equivalents;
@@ -57,6 +60,11 @@ SLOTS_PER_TOKEN_D = 1
 SLOTS_PER_TOKEN_GATE = 12
 SLOTS_PER_TOKEN_EULER = 1
 SLOTS_PER_TOKEN_SOFTPLUS = 20
+#   backward, per (b, l, d, n): exp (4), c (1), h_t (2), readout (1), lambda (1), du (2),
+#                     ddelta (3), dc/da (3), dA (3), dB (1), dC (1), carry (1)        = 23
+#             per (b, l, d): gate and its derivative (about 16), Dskip terms (2)      = 18
+SLOTS_BWD_PER_ELEMENT = 23
+SLOTS_BWD_PER_TOKEN_D = 18
 
 
 def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool, bias: bool = False) -> int:
@@ -79,6 +87,16 @@ def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool, bias: bool = Fa
     if want_last:
         total += b * D * N * 4
     return total
+
+
+def backward_bytes(inp: s6_workloads.Inputs) -> int:
+    """Bytes the backward pass must move: u, delta, z, dy read and du, ddelta, dz written per
+    (b, l, d); B, C read and dB, dC written per (b, l, n); A, Dskip read and dA, dDskip written
+    once."""
+    b, L, D, N = inp.shape
+    es = 2 if inp.io == "bf16" else 4
+    zt = 2 if inp.z is not None else 0
+    return b * L * D * es * (4 + zt) + b * L * N * es * 4 + 2 * (D * N + D) * 4
 
 
 def decode_bytes(inp: s6_workloads.Inputs, bias: bool = False) -> int:
@@ -108,8 +126,13 @@ def algorithmic_slots(inp: s6_workloads.Inputs, softplus: bool = False, euler: b
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernels' sources (the counters in the committed summary are valid
+    only for the source they were taken on)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, per_launch_alg_bytes: int):
@@ -165,6 +188,7 @@ def main():
     ap.add_argument("--step-size", default="given", choices=["given", "softplus"],
                     help="softplus: the kernel computes softplus(raw + bias) from a pre-activation")
     ap.add_argument("--discretization", default="zoh", choices=["zoh", "euler"])
+    ap.add_argument("--backward", action="store_true", help="time the backward pass instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -191,6 +215,8 @@ def main():
     opts = variant_options(args)
     if spec.get("decode"):
         return bench_decode(args, inp, bias_np, opts)
+    if args.backward:
+        return bench_backward(args, inp, bias_np, opts)
     want_last = bool(spec["last"])
     b, L, D, N = inp.shape
     E = b * L * D * N
@@ -288,6 +314,104 @@ def variant_options(args) -> dict:
     suffix = ("+softplus" if args.step_size == "softplus" else "") + ("+euler" if args.discretization == "euler" else "")
     return {"suffix": suffix,
             "step_size": "softplus(delta + bias[d]) in the kernel" if args.step_size == "softplus" else "given"}
+
+
+def bench_backward(args, inp, bias_np, opts):
+    """The backward pass (selective_scan_bwd: every gradient, states recomputed from
+    checkpoints) over the whole workload, from a seeded output gradient."""
+    import torch
+    import selective_state_space_s6_amd as ss
+    b, L, D, N = inp.shape
+    io = inp.io
+
+    def dev(x):
+        if x is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+        return t.to(torch.bfloat16) if io == "bf16" else t
+
+    u, delta, B, C, z = dev(inp.u), dev(inp.delta), dev(inp.B), dev(inp.C), dev(inp.z)
+    A = torch.from_numpy(inp.A).cuda()
+    Ds = None if inp.Dskip is None else torch.from_numpy(inp.Dskip).cuda()
+    bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
+    softplus = bias_np is not None
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    dy = torch.randn(u.shape, generator=gen, device="cuda", dtype=torch.float32).to(u.dtype)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ss.selective_scan_bwd(u, delta, A, B, C, Ds, z, dy=dy, delta_bias=bias, delta_softplus=softplus,
+                              discretization=args.discretization, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+    E = b * L * D * N
+    alg = backward_bytes(inp)
+    slots = SLOTS_BWD_PER_ELEMENT * E + SLOTS_BWD_PER_TOKEN_D * b * L * D
+    out = {
+        "metric": METRIC,
+        "value": E * args.steps / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, s6_workloads: %s; dy standard normal)" % args.workload,
+        "config": {"workload": args.workload, "batch": b, "seq_len": L, "dim": D, "dstate": N, "io": io,
+                   "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
+                   "pass": "backward", "step_size": opts["step_size"], "discretization": args.discretization},
+        "kernel_ms": launch_ms,
+        "hbm_gbs": round(alg / (launch_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(alg / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": alg,
+        "algorithmic_slots": slots,
+        "roofline": roofline(alg, slots, launch_ms * 1e-3, None),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(inp, bias_np, softplus, args.discretization == "euler")
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_backward(inp, bias, softplus, euler, target_s: float = 10.0):
+    """The oracle's backward (fp64, single thread, as it stands) on the first batch row and a
+    growing prefix of channels, timed on this host; scaled to elements/s."""
+    import oracle
+    oracle.build()
+    b, L, D, N = inp.shape
+    rng = np.random.default_rng(3)
+    nch = 4
+    while True:
+        sub = s6_workloads.select_channels(inp, np.arange(nch))
+        one = lambda a: None if a is None else a[:1]
+        dy = rng.standard_normal((1, L, nch)).astype(np.float32)
+        t0 = time.perf_counter()
+        oracle.bwd(one(sub.u), one(sub.delta), sub.A, one(sub.B), one(sub.C), sub.Dskip, one(sub.z), dy=dy,
+                   delta_bias=None if bias is None else bias[:nch], delta_softplus=softplus, euler=euler)
+        t_used = time.perf_counter() - t0
+        if t_used >= target_s * 0.5 or nch >= D:
+            break
+        nch = min(D, int(nch * max(2.0, target_s / max(t_used, 1e-3))))
+    return {"value": L * nch * N / t_used, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": "batch row 0, %d of %d channels x %d tokens x %d states, fp64 backward, %.1f s wall"
+                      % (nch, D, L, N, t_used)}
 
 
 def copy_calibration():

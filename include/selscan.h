@@ -233,6 +233,49 @@ int selective_scan_step(const void* u, const void* delta, const float* delta_bia
                         const void* B, const void* C, const float* Dskip, const void* z, void* y,
                         float* state, const selscan_dims* dims, void* stream);
 
+/*
+ * selective_scan_bwd -- the backward pass: gradients of the forward pass of
+ * selective_scan_fwd_ex with the same inputs and options, given the gradient dy of y and,
+ * optionally, the gradient dlast_state reaching its last_state (the vector-Jacobian product).
+ * It follows the reverse-time recurrence over the states of the rustytorch commit log's
+ * hand-written VJP of the selective scan ("Hand-written VJP of the selective-scan forward"):
+ * with lambda_t = dL/dh_t, lambda_t = dy'_t C_t + Abar_{t+1} lambda_{t+1}, where dy'_t is dy_t
+ * through the gate, and each input's gradient is the chain rule through one step.  States are
+ * recomputed from checkpoints taken every 16 tokens, so nothing from the forward call is
+ * needed.
+ *   u, delta, delta_bias, A, B, C, Dskip, z, initial_state : the forward call's inputs
+ *                    (dims->discretization and dims->delta_softplus as in that call).
+ *                    Selective coefficients only: fixed (time-invariant) coefficients return
+ *                    SELSCAN_ERR_UNSUPPORTED.
+ *   dy             : gradient of y, in dims->io_dtype with the y strides of dims, required.
+ *   dlast_state    : [batch][dim][dstate] fp32 gradient of last_state, or NULL (zero).
+ * Outputs (device memory, all written, never accumulated into):
+ *   du, ddelta, dz : [batch][seqlen][dim] contiguous, in dims->io_dtype.  ddelta is the
+ *                    gradient of the delta argument as given (of the softplus argument's
+ *                    raw part when delta_softplus).  dz is written only if z and dz are both
+ *                    non-NULL.  du and ddelta are required.
+ *   dB, dC         : [batch][seqlen][dstate] contiguous, in dims->io_dtype, required.
+ *   dA             : [dim][dstate] fp32, required.
+ *   dDskip, ddelta_bias : [dim] fp32, or NULL to skip.  ddelta_bias is the sum of ddelta
+ *                    over batch and tokens.
+ *   dinitial_state : [batch][dim][dstate] fp32 gradient of initial_state, or NULL.
+ *   workspace      : device memory of selective_scan_bwd_workspace_size(dims) bytes,
+ *                    256-byte aligned, or NULL to take it stream-ordered on `stream`.
+ * No output may overlap an input.  Same status codes as selective_scan_fwd.
+ */
+int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias, const float* A,
+                       const void* B, const void* C, const float* Dskip, const void* z,
+                       const float* initial_state, const void* dy, const float* dlast_state,
+                       void* du, void* ddelta, float* ddelta_bias, float* dA, void* dB, void* dC,
+                       float* dDskip, void* dz, float* dinitial_state, const selscan_dims* dims,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace selective_scan_bwd needs for these dims (0 for an empty call
+ * or invalid dims): the checkpoints, batch * ceil(seqlen/16) * dim * dstate floats, and the
+ * per-16-channel-group partial sums of dB and dC, 2 * ceil(dim/16) * batch * seqlen * dstate
+ * floats, plus O(batch * dim * dstate). */
+size_t selective_scan_bwd_workspace_size(const selscan_dims* dims);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* selective_scan_strerror(int status);
 

@@ -75,6 +75,8 @@ _SIGNATURES = [
     ("selective_scan_fwd_ws", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
     ("selective_scan_fwd_ex", ctypes.c_int, [_VP] * 11 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
     ("selective_scan_step", ctypes.c_int, [_VP] * 10 + [ctypes.POINTER(SelscanDims), _VP]),
+    ("selective_scan_bwd", ctypes.c_int, [_VP] * 20 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
+    ("selective_scan_bwd_workspace_size", ctypes.c_size_t, [ctypes.POINTER(SelscanDims)]),
     ("selective_scan_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("selective_scan_last_hip_error", ctypes.c_int, []),
     ("selective_scan_abi_version", ctypes.c_int, []),
@@ -349,5 +351,71 @@ def selective_scan_step(u, delta, A, B, C, Dskip=None, z=None, y=None, *, state,
     return y
 
 
-__all__ = ["selective_scan_fwd", "selective_scan_step", "make_dims", "dims_init", "workspace_size", "strerror", "last_hip_error",
+def bwd_workspace_size(dims: SelscanDims) -> int:
+    return int(lib().selective_scan_bwd_workspace_size(ctypes.byref(dims)))
+
+
+def selective_scan_bwd(u, delta, A, B, C, Dskip=None, z=None, *, dy, dlast_state=None, initial_state=None,
+                       delta_bias=None, delta_softplus: bool = False, discretization: str = "zoh", workspace=None,
+                       stream=None) -> dict:
+    """Gradients of selective_scan_fwd (same inputs and options) given dy, the gradient of y,
+    and optionally dlast_state, the gradient of last_state.  Selective coefficients only.
+
+    Returns a dict: du, ddelta, dz (if z) as [batch, L, D] and dB, dC as [batch, L, N], in
+    u's dtype; dA [D, N], dDskip [D] (if Dskip), ddelta_bias [D] (if delta_bias) and
+    dinitial_state [batch, D, N] (if initial_state), in float32.  ``workspace`` (a uint8
+    GPU tensor of bwd_workspace_size bytes) is taken from torch's caching allocator when
+    omitted."""
+    import torch
+    io = u.dtype
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("dy", dy)):
+        if t is not None and (t.dtype != io or not t.is_cuda):
+            raise TypeError("%s must be a GPU tensor of dtype %s like u" % (name, io))
+    if A.dtype != torch.float32 or not A.is_contiguous():
+        raise TypeError("A must be a contiguous float32 [D, N] tensor")
+    if Dskip is not None and (Dskip.dtype != torch.float32 or not Dskip.is_contiguous()):
+        raise TypeError("Dskip must be a contiguous float32 [D] tensor")
+    batch, L, D = (int(x) for x in u.shape)
+    N = int(A.shape[1])
+    for name, t in (("dlast_state", dlast_state), ("initial_state", initial_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (batch, D, N)
+                              or not t.is_cuda):
+            raise ValueError("%s must be a contiguous float32 [batch, D, N] GPU tensor" % name)
+    _check_bias(delta_bias, D)
+    dims = make_dims(u, delta, A, B, C, z, dy, discretization=discretization, delta_softplus=delta_softplus)
+    dev = u.device
+    g = {"du": torch.empty((batch, L, D), dtype=io, device=dev), "ddelta": torch.empty((batch, L, D), dtype=io, device=dev),
+         "dA": torch.empty((D, N), dtype=torch.float32, device=dev),
+         "dB": torch.empty((batch, L, N), dtype=io, device=dev), "dC": torch.empty((batch, L, N), dtype=io, device=dev)}
+    if z is not None:
+        g["dz"] = torch.empty((batch, L, D), dtype=io, device=dev)
+    if Dskip is not None:
+        g["dDskip"] = torch.empty((D,), dtype=torch.float32, device=dev)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty((D,), dtype=torch.float32, device=dev)
+    if initial_state is not None:
+        g["dinitial_state"] = torch.empty((batch, D, N), dtype=torch.float32, device=dev)
+    torch_stream = stream if (stream is None or hasattr(stream, "cuda_stream")) else None
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    if workspace is None and (torch_stream is not None or stream == torch.cuda.current_stream(dev).cuda_stream):
+        need = bwd_workspace_size(dims)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            if torch_stream is not None:
+                workspace.record_stream(torch_stream)
+    ws = (_ptr(workspace), int(workspace.numel() * workspace.element_size())) if workspace is not None else (None, 0)
+    st = lib().selective_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(initial_state),
+        _ptr(dy), _ptr(dlast_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g.get("ddelta_bias")), _ptr(g["dA"]),
+        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dDskip")), _ptr(g.get("dz")), _ptr(g.get("dinitial_state")),
+        ctypes.byref(dims), ws[0], ws[1], ctypes.c_void_p(stream))
+    if st != SELSCAN_OK:
+        raise SelscanError(st, "selective_scan_bwd")
+    return g
+
+
+__all__ = ["selective_scan_fwd", "selective_scan_step", "selective_scan_bwd", "bwd_workspace_size", "make_dims", "dims_init", "workspace_size", "strerror", "last_hip_error",
            "abi_version", "lib", "SelscanDims", "SelscanError", "LIB_PATH"]

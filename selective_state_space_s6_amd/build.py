@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libselscan.so")
-SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "selscan_api.cpp")]
+SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "bwd_kernels.hip"),
+           os.path.join(CSRC, "selscan_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -31,14 +32,18 @@ def build(verbose: bool = False) -> str:
     objs = []
     builddir = os.path.join(PKG, "_build")
     os.makedirs(builddir, exist_ok=True)
-    for src in SOURCES:
+    procs = []
+    for src in SOURCES:                                       # the sources compile concurrently
         obj = os.path.join(builddir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"]
         cmd = [HIPCC] + COMMON_FLAGS + lang + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        procs.append((subprocess.Popen(cmd), cmd))
         objs.append(obj)
+    for proc, cmd in procs:
+        if proc.wait() != 0:
+            raise subprocess.CalledProcessError(proc.returncode, cmd)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

@@ -52,51 +52,17 @@
 
 #include <type_traits>
 
+#include "device_common.h"
 #include "scan_launch.h"
 
 namespace selscan {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = 16;        // tokens per tile
 constexpr int kRowPad = 20;      // LDS row length (floats) of a 16-token row: 16 + 4 padding
 constexpr int kPrefetchMax = 2;  // tiles of global loads kept in flight per wavefront (K <= 2)
 
 enum { MODE_SINGLE = 0, MODE_STATE = 1, MODE_APPLY = 2 };
-
-// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|); e^-|x| lies in (0, 1], so nothing
-// overflows.  log1p(e) is formed from the rounded sum t = 1 + e as log(t) * e / (t - 1), which
-// gives back the bits of e that the sum drops (Goldberg, "What every computer scientist
-// should know about floating-point arithmetic", Theorem 4); t == 1 leaves log1p(e) = e.
-__device__ __forceinline__ float softplus_f32(float x) {
-  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
-  const float t = 1.f + e;
-  const float lp = (t == 1.f) ? e : __builtin_amdgcn_logf(t) * kLn2 * (e * __builtin_amdgcn_rcpf(t - 1.f));
-  return fmaxf(x, 0.f) + lp;
-}
-
-// The step size a token uses: delta + bias, through softplus when sp.
-__device__ __forceinline__ float step_size(float raw, float bias, bool sp) {
-  const float x = raw + bias;
-  return sp ? softplus_f32(x) : x;
-}
-
-// ---------------------------------------------------------------------------------------
-// element types: per-token tensors travel as raw bit patterns (see the buffer loads in the
-// kernel) and are widened to fp32 when staged.
-
-template <typename IO> struct io_traits;
-template <> struct io_traits<float> {
-  static constexpr int kBytes = 4;
-  static __device__ __forceinline__ float widen(float v) { return v; }
-  static __device__ __forceinline__ float from_raw(uint32_t r) { return __uint_as_float(r); }
-};
-template <> struct io_traits<uint16_t> {   // bfloat16 bit patterns
-  static constexpr int kBytes = 2;
-  static __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-  static __device__ __forceinline__ float from_raw(uint32_t r) { return __uint_as_float(r << 16); }
-};
 
 // Order this wave's LDS traffic: every LDS write before the barrier is visible to every
 // lane's LDS read after it.  A wave's LDS instructions execute in issue order, so this
@@ -105,16 +71,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Blocks are dealt round-robin to the 8 XCDs; remap so that each XCD gets a contiguous
-// range of work items (neighbouring channel groups of one batch row share B/C rows and
-// the cache lines of u/delta/z/y, and those live in that XCD's L2).
-__device__ __forceinline__ int xcd_contiguous_block(int bid, int nblocks) {
-  constexpr int kXcd = 8;
-  const int per = nblocks / kXcd, rem = nblocks % kXcd;
-  const int xcd = bid % kXcd, pos = bid / kXcd;
-  return (xcd < rem) ? xcd * (per + 1) + pos : rem * (per + 1) + (xcd - rem) * per + pos;
 }
 
 // LDS floats one wave needs.

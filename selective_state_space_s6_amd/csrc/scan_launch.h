@@ -80,3 +80,44 @@ struct StepParams {
 hipError_t launch_step(bool bf16, bool ti, const StepParams& p, hipStream_t stream);
 
 }  // namespace selscan
+
+namespace selscan {
+
+// The backward pass (selective coefficients).  Strides in elements; the gradients du,
+// ddelta, dz are contiguous [batch][L][D] in the I/O type.
+struct BwdParams {
+  const void* u;
+  const void* delta;
+  const float* delta_bias;   // may be null
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;   // may be null
+  const void* z;        // may be null
+  const float* h0;      // may be null
+  const void* dy;
+  const float* dlast;   // may be null
+  void* du;
+  void* ddelta;
+  void* dz;             // may be null (then not written)
+  float* dh0;           // may be null
+  float* ckpt;          // [batch][ntiles][D][N] state at the start of every tile
+  float* pB;            // [groups][batch][L][N] per-group partial sums of dB
+  float* pC;            // [groups][batch][L][N] per-group partial sums of dC
+  float* pA;            // [batch][D][N] per-batch partial sums of dA
+  float* pD;            // [batch][D] per-batch partial sums of dDskip
+  float* pbias;         // [batch][D] per-batch partial sums of the bias gradient
+  int64_t batch, L, D, N;
+  int64_t u_sb, u_sl, delta_sb, delta_sl, z_sb, z_sl, dy_sb, dy_sl, B_sb, B_sl, C_sb, C_sl;
+  int64_t ntiles;       // ceil(L / 16)
+  int32_t groups;       // ceil(D / 16)
+  int32_t euler;
+  int32_t dxf;
+  int32_t softplus;
+};
+hipError_t launch_bwd(bool bf16, int K, const BwdParams& p, hipStream_t stream);
+// out[i] = sum_{j < nparts} part[j * stride + i], i < m; out in the I/O type when bf16
+hipError_t launch_sum_partials(const float* part, int64_t nparts, int64_t stride, void* out, int64_t m, bool bf16,
+                               hipStream_t stream);
+
+}  // namespace selscan

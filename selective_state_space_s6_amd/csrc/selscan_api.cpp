@@ -236,6 +236,91 @@ int fwd_impl(const void* u, const void* delta, const float* delta_bias, const fl
   return st;
 }
 
+// ---- backward pass
+struct BwdPlan {
+  int K = 1;
+  int64_t groups = 0, ntiles = 0;
+  size_t off_pB = 0, off_pC = 0, off_pA = 0, off_pD = 0, off_pbias = 0, bytes = 0;
+};
+
+// Validate dims for the backward pass and lay out its workspace:
+//   ckpt [batch][ntiles][D][N], pB and pC [groups][batch][L][N], pA [batch][D][N],
+//   pD and pbias [batch][D]  (fp32, each 256-byte aligned).
+int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
+  Plan plan;
+  int st = make_plan(dims, &plan);
+  if (st != SELSCAN_OK) return st;
+  if (plan.ti) return SELSCAN_ERR_UNSUPPORTED;        // backward of fixed coefficients: not built
+  const selscan_dims& d = *dims;
+  BwdPlan b;
+  b.K = d.dstate <= 16 ? 1 : d.dstate <= 32 ? 2 : 4;
+  b.groups = (d.dim + 15) / 16;
+  b.ntiles = (d.seqlen + 15) / 16;
+  if (d.batch * b.groups > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
+  auto al = [](int64_t x) { return size_t(round_up(x, 256)); };
+  const int64_t f = int64_t(sizeof(float));
+  size_t off = al(f * d.batch * b.ntiles * d.dim * d.dstate);
+  b.off_pB = off;
+  off += al(f * b.groups * d.batch * d.seqlen * d.dstate);
+  b.off_pC = off;
+  off += al(f * b.groups * d.batch * d.seqlen * d.dstate);
+  b.off_pA = off;
+  off += al(f * d.batch * d.dim * d.dstate);
+  b.off_pD = off;
+  off += al(f * d.batch * d.dim);
+  b.off_pbias = off;
+  off += al(f * d.batch * d.dim);
+  b.bytes = (d.batch * d.seqlen > 0) ? off : 0;
+  *out = b;
+  return SELSCAN_OK;
+}
+
+int bwd_run(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B, const void* C,
+            const float* Dskip, const void* z, const float* h0, const void* dy, const float* dlast, void* du,
+            void* ddelta, float* ddelta_bias, float* dA, void* dB, void* dC, float* dDskip, void* dz, float* dh0,
+            const selscan_dims& d, const BwdPlan& plan, char* ws, hipStream_t stream) {
+  const bool bf16 = d.io_dtype == SELSCAN_BF16;
+  hipError_t e;
+  if (d.batch * d.seqlen == 0) {
+    // no tokens: every sum is empty; the initial state's gradient is dlast itself
+    e = selscan::launch_fill_zero(dA, d.dim * d.dstate, stream);
+    if (e == hipSuccess && dDskip) e = selscan::launch_fill_zero(dDskip, d.dim, stream);
+    if (e == hipSuccess && ddelta_bias) e = selscan::launch_fill_zero(ddelta_bias, d.dim, stream);
+    if (e == hipSuccess && dh0 && d.batch > 0)
+      e = dlast ? selscan::launch_copy(dh0, dlast, d.batch * d.dim * d.dstate, stream)
+                : selscan::launch_fill_zero(dh0, d.batch * d.dim * d.dstate, stream);
+    return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+  }
+  selscan::BwdParams p{};
+  p.u = u; p.delta = delta; p.delta_bias = delta_bias; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = z;
+  p.h0 = h0; p.dy = dy; p.dlast = dlast; p.du = du; p.ddelta = ddelta; p.dz = z ? dz : nullptr; p.dh0 = dh0;
+  p.ckpt = reinterpret_cast<float*>(ws);
+  p.pB = reinterpret_cast<float*>(ws + plan.off_pB);
+  p.pC = reinterpret_cast<float*>(ws + plan.off_pC);
+  p.pA = reinterpret_cast<float*>(ws + plan.off_pA);
+  p.pD = reinterpret_cast<float*>(ws + plan.off_pD);
+  p.pbias = reinterpret_cast<float*>(ws + plan.off_pbias);
+  p.batch = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = d.dstate;
+  p.u_sb = d.u_sb; p.u_sl = d.u_sl; p.delta_sb = d.delta_sb; p.delta_sl = d.delta_sl;
+  p.z_sb = d.z_sb; p.z_sl = d.z_sl; p.dy_sb = d.y_sb; p.dy_sl = d.y_sl;
+  p.B_sb = d.B_sb; p.B_sl = d.B_sl; p.C_sb = d.C_sb; p.C_sl = d.C_sl;
+  p.ntiles = plan.ntiles;
+  p.groups = int32_t(plan.groups);
+  p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
+  p.softplus = d.delta_softplus != 0 ? 1 : 0;
+  p.dxf = (p.softplus || delta_bias != nullptr) ? 1 : 0;
+  e = selscan::launch_bwd(bf16, plan.K, p, stream);
+  const int64_t m_bc = d.batch * d.seqlen * d.dstate;
+  if (e == hipSuccess) e = selscan::launch_sum_partials(p.pB, plan.groups, m_bc, dB, m_bc, bf16, stream);
+  if (e == hipSuccess) e = selscan::launch_sum_partials(p.pC, plan.groups, m_bc, dC, m_bc, bf16, stream);
+  if (e == hipSuccess)
+    e = selscan::launch_sum_partials(p.pA, d.batch, d.dim * d.dstate, dA, d.dim * d.dstate, false, stream);
+  if (e == hipSuccess && dDskip) e = selscan::launch_sum_partials(p.pD, d.batch, d.dim, dDskip, d.dim, false, stream);
+  if (e == hipSuccess && ddelta_bias)
+    e = selscan::launch_sum_partials(p.pbias, d.batch, d.dim, ddelta_bias, d.dim, false, stream);
+  return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +409,48 @@ int selective_scan_step(const void* u, const void* delta, const float* delta_bia
   }
   const hipError_t e = selscan::launch_step(plan.bf16, plan.ti, q, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+}
+
+size_t selective_scan_bwd_workspace_size(const selscan_dims* dims) {
+  BwdPlan plan;
+  if (make_bwd_plan(dims, &plan) != SELSCAN_OK) return 0;
+  return plan.bytes;
+}
+
+int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B,
+                       const void* C, const float* Dskip, const void* z, const float* initial_state, const void* dy,
+                       const float* dlast_state, void* du, void* ddelta, float* ddelta_bias, float* dA, void* dB,
+                       void* dC, float* dDskip, void* dz, float* dinitial_state, const selscan_dims* dims,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  BwdPlan plan;
+  int st = make_bwd_plan(dims, &plan);
+  if (st != SELSCAN_OK) return st;
+  const selscan_dims& d = *dims;
+  const bool no_tokens = d.batch * d.seqlen == 0;
+  st = check_pointers(u, delta, A, B, C, Dskip, z, dy, nullptr, d.io_dtype, no_tokens);
+  if (st != SELSCAN_OK) return st;
+  if (!dA || (!no_tokens && (!du || !ddelta || !dB || !dC))) return SELSCAN_ERR_NULL;
+  const size_t es = d.io_dtype == SELSCAN_BF16 ? 2 : 4;
+  if (!aligned(du, es) || !aligned(ddelta, es) || !aligned(dB, es) || !aligned(dC, es) || (dz && !aligned(dz, es)))
+    return SELSCAN_ERR_ALIGN;
+  for (const float* f : {delta_bias, initial_state, dlast_state, static_cast<const float*>(ddelta_bias),
+                         static_cast<const float*>(dA), static_cast<const float*>(dDskip),
+                         static_cast<const float*>(dinitial_state)})
+    if (f && !aligned(f, 4)) return SELSCAN_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.bytes == 0 || workspace != nullptr) {
+    if (plan.bytes > 0 && (workspace_bytes < plan.bytes || !aligned(workspace, 256))) return SELSCAN_ERR_WORKSPACE;
+    return bwd_run(u, delta, delta_bias, A, B, C, Dskip, z, initial_state, dy, dlast_state, du, ddelta, ddelta_bias,
+                   dA, dB, dC, dDskip, dz, dinitial_state, d, plan, static_cast<char*>(workspace), s);
+  }
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, plan.bytes, s);
+  if (e != hipSuccess) return hip_fail(e);
+  st = bwd_run(u, delta, delta_bias, A, B, C, Dskip, z, initial_state, dy, dlast_state, du, ddelta, ddelta_bias, dA,
+               dB, dC, dDskip, dz, dinitial_state, d, plan, static_cast<char*>(ws), s);
+  e = hipFreeAsync(ws, s);
+  if (st == SELSCAN_OK && e != hipSuccess) return hip_fail(e);
+  return st;
 }
 
 const char* selective_scan_strerror(int status) {

@@ -192,3 +192,25 @@ def test_step_size_options_errors():
     assert call_ex(d, h0=None, ws=FAKE, ws_bytes=ss.workspace_size(d), bias=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
     e = good_dims(discretization=ss.DISCRETIZATIONS["euler"], delta_softplus=1)
     assert call_ex(e, h0=None, ws=FAKE, ws_bytes=ss.workspace_size(e) - 1) == ss.SELSCAN_ERR_WORKSPACE
+
+
+def call_bwd(dims, du=FAKE, ws=None, ws_bytes=0, dA=FAKE):
+    return ss.lib().selective_scan_bwd(FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
+                                       du, FAKE, None, dA, FAKE, FAKE, None, None, None, ctypes.byref(dims), ws,
+                                       ws_bytes, None)
+
+
+def test_backward_errors():
+    d = ss.dims_init(ss.SELSCAN_F32, 2, 64, 40, 16)
+    need = ss.bwd_workspace_size(d)
+    # checkpoints (2 x 4 tiles x 40 x 16) and two partial sums (3 groups x 2 x 64 x 16) at least
+    assert need >= 4 * (2 * 4 * 40 * 16 + 2 * 3 * 2 * 64 * 16)
+    ti = ss.dims_init(ss.SELSCAN_F32, 2, 64, 40, 16, time_invariant=True)
+    assert ss.bwd_workspace_size(ti) == 0
+    assert call_bwd(ti, ws=FAKE, ws_bytes=1 << 30) == ss.SELSCAN_ERR_UNSUPPORTED
+    assert call_bwd(d, du=None, ws=FAKE, ws_bytes=need) == ss.SELSCAN_ERR_NULL
+    assert call_bwd(d, dA=None, ws=FAKE, ws_bytes=need) == ss.SELSCAN_ERR_NULL
+    assert call_bwd(d, du=FAKE_ODD, ws=FAKE, ws_bytes=need) == ss.SELSCAN_ERR_ALIGN
+    assert call_bwd(d, ws=FAKE, ws_bytes=need - 1) == ss.SELSCAN_ERR_WORKSPACE
+    assert call_bwd(good_dims(abi_version=3), ws=FAKE, ws_bytes=need) == ss.SELSCAN_ERR_ABI
+    assert ss.bwd_workspace_size(ss.dims_init(ss.SELSCAN_F32, 0, 64, 40, 16)) == 0

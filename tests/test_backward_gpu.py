@@ -1,0 +1,125 @@
+"""GPU parity of the backward pass (selective_scan_bwd) against the oracle's reverse-time
+recurrence (rustytorch commit log: hand-written VJP of the selective scan), gradient by
+gradient: max|g - g_ref| / max|g_ref| <= 1e-4 (fp32 I/O) or 2e-2 (bf16 I/O, whose du, ddelta,
+dz, dB and dC are rounded to bf16), for every gradient the call returns.  Cases span several
+16-token tiles with ragged tails, channel groups with a partial last group, every state
+layout (one, two and four states per lane, padded states), both discretisations, the fused
+softplus step size, an initial state and a gradient reaching the final state."""
+import numpy as np
+import pytest
+
+import oracle
+import s6_workloads
+from tests.gpu_common import TOL, dev, log_errors, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def run_case(inp, *, delta=None, bias=None, softplus=False, euler=False, h0=None, dlast=None, seed=5):
+    import selective_state_space_s6_amd as ss
+    t = torch()
+    rng = np.random.default_rng(seed)
+    b, L, D, N = inp.shape
+    dy = rng.standard_normal((b, L, D)).astype(np.float32)
+    if inp.io == "bf16":
+        dy = s6_workloads.bf16_round(dy)
+    dl = inp.delta if delta is None else delta
+    ref = oracle.bwd(inp.u, dl, inp.A, inp.B, inp.C, inp.Dskip, inp.z, dy=dy, dlast=dlast, h0=h0, delta_bias=bias,
+                     euler=euler, delta_softplus=softplus)
+    io = inp.io
+    g = ss.selective_scan_bwd(
+        dev(inp.u, io), dev(dl, io), t.from_numpy(inp.A).cuda(), dev(inp.B, io), dev(inp.C, io),
+        None if inp.Dskip is None else t.from_numpy(inp.Dskip).cuda(), dev(inp.z, io), dy=dev(dy, io),
+        dlast_state=None if dlast is None else t.from_numpy(dlast).cuda(),
+        initial_state=None if h0 is None else t.from_numpy(h0).cuda(),
+        delta_bias=None if bias is None else t.from_numpy(bias).cuda(), delta_softplus=softplus,
+        discretization="euler" if euler else "zoh")
+    t.cuda.synchronize()
+    names = {"dinitial_state": "dh0"}
+    errs = {}
+    for k, v in g.items():
+        errs[k] = rel_err(v.float().cpu().numpy(), ref[names.get(k, k)])
+    return errs
+
+
+def check(errs, io, case):
+    log_errors("bwd/" + case, io=io, **errs)
+    bad = {k: e for k, e in errs.items() if not e <= TOL[io]}
+    assert not bad, (case, errs)
+
+
+CASES = {
+    "small_f32": dict(batch=2, L=100, D=40),
+    "mamba130m_f32": dict(batch=2, L=130, D=36),
+    "longctx_bf16": dict(batch=2, L=150, D=36),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_parity(name):
+    inp = s6_workloads.generate(name, "active", **CASES[name])
+    check(run_case(inp), inp.io, name)
+
+
+@pytest.mark.parametrize("N", [3, 8, 16, 17, 32, 48, 64])
+@pytest.mark.parametrize("L", [1, 16, 37])
+def test_backward_state_counts_and_lengths(N, L):
+    inp = s6_workloads.generate("mamba130m_f32", "active", batch=2, L=L, D=20, N=N)
+    check(run_case(inp, seed=N + L), "f32", "N=%d L=%d" % (N, L))
+
+
+@pytest.mark.parametrize("name", ["small_f32", "longctx_bf16"])
+def test_backward_options(name):
+    inp = s6_workloads.generate(name, **CASES[name])
+    raw, bias = s6_workloads.raw_step_sizes(inp)
+    check(run_case(inp, delta=raw, bias=bias, softplus=True), inp.io, name + "/softplus")
+    check(run_case(inp, euler=True), inp.io, name + "/euler")
+    check(run_case(inp, delta=raw, bias=bias, softplus=True, euler=True), inp.io, name + "/softplus+euler")
+
+
+@pytest.mark.parametrize("name", ["mamba130m_f32", "longctx_bf16"])
+def test_backward_initial_and_final_state(name):
+    inp = s6_workloads.generate(name, "active", **CASES[name])
+    b, L, D, N = inp.shape
+    h0 = s6_workloads.running_state(inp, scale=1.0)
+    dlast = np.random.default_rng(9).standard_normal((b, D, N)).astype(np.float32)
+    check(run_case(inp, h0=h0, dlast=dlast), inp.io, name + "/h0+dlast")
+
+
+def test_backward_without_gate_or_feedthrough():
+    inp = s6_workloads.generate("small_f32", "scan_only", batch=2, L=70, D=24)
+    errs = run_case(inp)
+    assert "dz" not in errs and "dDskip" not in errs
+    check(errs, "f32", "scan_only")
+
+
+def test_backward_empty_sequence():
+    """No tokens: every sum is empty and the initial state's gradient is dlast."""
+    import selective_state_space_s6_amd as ss
+    t = torch()
+    D, N = 8, 16
+    e = lambda *s: t.zeros(s, dtype=t.float32, device="cuda")
+    dlast = t.randn(2, D, N, device="cuda")
+    g = ss.selective_scan_bwd(e(2, 0, D), e(2, 0, D), -t.ones(D, N, device="cuda"), e(2, 0, N), e(2, 0, N),
+                              t.ones(D, device="cuda"), dy=e(2, 0, D), dlast_state=dlast, initial_state=e(2, D, N))
+    t.cuda.synchronize()
+    assert not g["dA"].any() and not g["dDskip"].any()
+    assert t.equal(g["dinitial_state"], dlast)
+
+
+def test_backward_deterministic():
+    import selective_state_space_s6_amd as ss
+    t = torch()
+    inp = s6_workloads.generate("small_f32", batch=2, L=90, D=40)
+    args = (dev(inp.u, "f32"), dev(inp.delta, "f32"), t.from_numpy(inp.A).cuda(), dev(inp.B, "f32"),
+            dev(inp.C, "f32"), t.from_numpy(inp.Dskip).cuda(), dev(inp.z, "f32"))
+    dy = t.randn(2, 90, 40, device="cuda")
+    g1 = ss.selective_scan_bwd(*args, dy=dy)
+    g2 = ss.selective_scan_bwd(*args, dy=dy)
+    t.cuda.synchronize()
+    assert all(t.equal(g1[k], g2[k]) for k in g1)
