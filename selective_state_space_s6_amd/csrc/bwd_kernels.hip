@@ -14,8 +14,12 @@
 // dc/ddelta is Abar (ZOH, also at A == 0) or 1 (first order); dc/da is delta^2 phi(delta a)
 // with phi(x) = (x e^x - (e^x - 1)) / x^2 (ZOH; phi(0) = 1/2) or 0 (first order).
 //
-// Work decomposition: a workgroup of four wavefronts owns (batch row b, 16 channels); lane
-// (c, s) of wavefront w owns channel 4w + c and the K states n = s + 16k, in VGPRs.  The
+// Work decomposition: SL = N/4 (4, 8 or 16) lanes share a channel and each owns 4 of its
+// states, in VGPRs; a workgroup of four wavefronts owns (batch row b, chunk of the sequence,
+// 4 * 64 / SL channels).  Chunks give the parallelism the sequential walk lacks: each chunk
+// starts from its carried-in state (the forward pass's chunk states and prefix, computed
+// before) and from the adjoint reaching its end (a cheap adjoint-only pass per chunk and a
+// combine across chunks, since the adjoint recurrence needs no state).  The
 // sequence is walked in 16-token tiles whose operands the workgroup stages in LDS with
 // coalesced loads issued one tile ahead (the next tile's loads are in flight while the
 // current one computes).
@@ -24,10 +28,11 @@
 //   pass 2: tiles from last to first: the tile's states are recomputed from its checkpoint
 //           into registers, then its tokens are walked backwards carrying lambda.
 // Sums over states (du, ddelta, and the readout the gate's derivative needs) are DPP
-// reductions over the 16 lanes (one row) of a channel.  Sums over channels (dB, dC) go over the wavefront's four
-// channels by shuffles, over the workgroup's wavefronts through LDS in a fixed order, and
-// over channel groups in sum_partials_kernel, which also sums the per-batch partials of dA,
-// dDskip and the bias gradient.  Every sum has a fixed order: results are deterministic.
+// reductions over the SL lanes of a channel.  Sums over channels (dB, dC) go over the
+// wavefront's channels by DPP row rotations and the gfx950 row swaps, over the workgroup's
+// wavefronts through LDS in a fixed order, and over channel groups in sum_partials_kernel,
+// which also sums the per-batch partials of dA, dDskip and the bias gradient.  Every sum
+// has a fixed order: results are deterministic.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,111 +46,157 @@ namespace selscan {
 namespace {
 
 constexpr int kBTile = 16;      // tokens per tile (one checkpoint each)
-constexpr int kBRow = 20;       // LDS row of one 16-token row: 16 + 4 padding
+constexpr int kBRow = 20;       // LDS row of one channel's 16 tokens: 16 + 4 padding
 
-// Sum over the 16 lanes of a row (lanes 16r .. 16r+15), result in every lane of the row, by
-// DPP moves: quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float row16_sum(float v) {
+
+// Sum over the SL lanes of a channel (SL consecutive lanes, SL = 4, 8 or 16), result in every
+// one of them: DPP quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors.
+template <int SL>
+__device__ __forceinline__ float chan_sum(float v) {
   v += dpp_mov<0xB1>(v);
   v += dpp_mov<0x4E>(v);
-  v += dpp_mov<0x141>(v);
-  v += dpp_mov<0x140>(v);
+  if (SL >= 8) v += dpp_mov<0x141>(v);
+  if (SL >= 16) v += dpp_mov<0x140>(v);
   return v;
 }
 
-// at least this many wavefronts per SIMD (caps the registers)
-template <int K> struct bwd_occupancy { static constexpr int kMinWaves = K == 4 ? 2 : 3; };
+// Sum over the channels of a wavefront for a fixed sub-lane (lanes s, s + SL, s + 2 SL, ...),
+// result in every such lane: rotations by 4 and 8 inside a 16-lane row (channels sharing the
+// row), then the gfx950 row swaps across rows (permlane16_swap pairs rows 0-1 and 2-3,
+// permlane32_swap the two halves).
+template <int SL>
+__device__ __forceinline__ float wave_chan_sum(float v) {
+  if (SL <= 4) v += dpp_mov<0x124>(v);    // row_ror:4
+  if (SL <= 8) v += dpp_mov<0x128>(v);    // row_ror:8
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
 
-template <typename IO, int K>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_occupancy<K>::kMinWaves)))
+// at least this many wavefronts per SIMD (caps the registers)
+constexpr int kBwdMinWaves = 2;
+
+enum { BWD_ADJOINT = 0, BWD_MAIN = 1 };
+
+// SL lanes per channel, 4 states per lane (state n = 4 s + i); 64 / SL channels per wavefront.
+// One workgroup per (batch row, chunk, channel group).
+//   BWD_ADJOINT (chunks 1 ..): the adjoint recurrence alone over the chunk from a zero
+//       incoming adjoint; writes the adjoint it hands to the previous chunk and the chunk's
+//       sum of delta (its decay is exp(A sum delta)).  No state is needed for it.
+//   BWD_MAIN: the chunk's states from its carried-in state (checkpoint every 16 tokens), then
+//       the tiles backwards from the chunk's incoming adjoint, with every gradient.
+template <typename IO, int SL, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdMinWaves)))
 void bwd_kernel(BwdParams p) {
   using T = io_traits<IO>;
-  constexpr int S = 16, NP = S * K;
-  // the staged tile: u, delta (transformed), dy, z, and d delta / d raw as [channel][token];
-  // B and C as [state][token]
-  __shared__ __align__(16) float sTok[5][16][kBRow];
-  __shared__ __align__(16) float sBq[NP][kBRow];
-  __shared__ __align__(16) float sCq[NP][kBRow];
-  __shared__ float sBC[4][2][kBTile][NP];  // each wavefront's dB / dC sums of one tile
+  constexpr int CW = 64 / SL, CWG = 4 * CW, NP = 4 * SL;
+  constexpr int ET = CWG * kBTile / 256;     // token-tensor elements each thread stages
+  constexpr int EB = NP * kBTile / 256;      // B (and C) elements each thread stages
+  constexpr int kBCRow = NP + 4;
+  // the staged tile, per channel: u, delta (transformed), dy through the gate, dy times the
+  // gate's derivative factor, and d delta / d raw; per token: B and C
+  __shared__ __align__(16) float sTok[5][CWG][kBRow];
+  __shared__ __align__(16) float sBq[kBTile][kBCRow];
+  __shared__ __align__(16) float sCq[kBTile][kBCRow];
+  __shared__ __align__(16) float sBC[4][2][kBTile][NP];   // each wavefront's dB / dC sums
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = lane / S, s = lane % S;
-  const int cw = 4 * w + c;                  // channel within the workgroup
+  const int c = lane / SL, s = lane % SL;
+  const int cw = w * CW + c;                 // channel within the workgroup
   const int64_t item = xcd_contiguous_block(blockIdx.x, gridDim.x);
-  const int64_t g = item % p.groups, b = item / p.groups;
+  const int nc = p.n_chunks;
+  const int nc_run = MODE == BWD_ADJOINT ? nc - 1 : nc;
+  const int64_t g = item % p.groups, bc = item / p.groups;
+  const int chunk = int(bc % nc_run) + (MODE == BWD_ADJOINT ? 1 : 0);
+  const int64_t b = bc / nc_run;
   const int64_t D = p.D, N = p.N, L = p.L;
-  const int64_t d0 = g * 16, d = d0 + cw;
+  const int64_t d0 = g * CWG, d = d0 + cw;
   const bool dvalid = d < D;
-  const bool sp = p.softplus != 0, first = p.euler != 0;
-  const int64_t ntiles = p.ntiles;
-  const int last_nt = int(L - (ntiles - 1) * kBTile);
+  const bool sp = p.softplus != 0, first = p.euler != 0, gated = p.z != nullptr;
+  const int64_t l_begin = int64_t(chunk) * p.chunk_len;
+  const int64_t l_end = (l_begin + p.chunk_len < L) ? l_begin + p.chunk_len : L;
+  const int64_t ntiles = (l_end - l_begin + kBTile - 1) / kBTile;      // tiles of this chunk
+  const int64_t tile0 = l_begin / kBTile;                               // its first tile overall
+  const int last_nt = int(l_end - l_begin - (ntiles - 1) * kBTile);
 
-  float a[K], a2[K], iA[K], zf[K];
-  bool nok[K];
+  float a[4], a2[4], iA[4], zf[4];
+  bool nok[4];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int64_t n = s + S * k;
-    nok[k] = dvalid && n < N;
-    a[k] = nok[k] ? p.A[d * N + n] : 0.f;
-    a2[k] = a[k] * kLog2e;
-    const bool fo = a[k] == 0.f || first;               // c = delta
-    iA[k] = fo ? 0.f : 1.0f / a[k];
-    zf[k] = (nok[k] && fo) ? 1.f : 0.f;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t n = 4 * s + i;
+    nok[i] = dvalid && n < N;
+    a[i] = nok[i] ? p.A[d * N + n] : 0.f;
+    a2[i] = a[i] * kLog2e;
+    const bool fo = a[i] == 0.f || first;               // c = delta
+    iA[i] = fo ? 0.f : 1.0f / a[i];
+    zf[i] = (nok[i] && fo) ? 1.f : 0.f;
   }
   const float dskip = (dvalid && p.Dskip != nullptr) ? p.Dskip[d] : 0.f;
-  // this lane's states in the checkpoints (clamped to a valid address when out of range)
-  float* const ck_b = p.ckpt + b * ntiles * D * N;
-  int64_t ck_off[K];
+  float* const ck_b = p.ckpt + (b * p.ntiles + tile0) * D * N;   // this chunk's checkpoints
+  const int64_t ck_d = (dvalid ? d : D - 1) * N;
+  int nq[4];
 #pragma unroll
-  for (int k = 0; k < K; ++k) ck_off[k] = (dvalid ? d : D - 1) * N + ((s + S * k) < N ? s + S * k : N - 1);
+  for (int i = 0; i < 4; ++i) nq[i] = (4 * s + i) < N ? 4 * s + i : int(N) - 1;
 
-  // ---- staging.  Thread tid moves token sj = tid / 16 of channel d0 + tid % 16 of each token
-  // tensor, and elements tid + 256 r of the tile's [16][NP] B and C rows.  Loads read clamped,
-  // valid addresses and are zeroed afterwards when out of range, so none sits behind a branch.
-  // The step-size transform is applied here, once per (token, channel).
-  const int sj = tid >> 4, sc = tid & 15;
-  const bool sc_ok = d0 + sc < D;
-  const int64_t sdq = sc_ok ? d0 + sc : D - 1;
-  const float sbias = (sc_ok && p.delta_bias != nullptr) ? p.delta_bias[sdq] : 0.f;
+  // ---- staging.  Element e = tid + 256 r of the tile: token e / CWG of channel d0 + e % CWG
+  // for the token tensors, token e / NP and state e % NP for B and C.  Loads read clamped,
+  // valid addresses and are zeroed afterwards when out of range.  The per-(token, channel)
+  // factors (step-size transform, gate) are formed here, once.
   const IO* const u_b = static_cast<const IO*>(p.u) + b * p.u_sb;
   const IO* const dl_b = static_cast<const IO*>(p.delta) + b * p.delta_sb;
   const IO* const dy_b = static_cast<const IO*>(p.dy) + b * p.dy_sb;
-  const bool gated = p.z != nullptr;
   const IO* const z_b = gated ? static_cast<const IO*>(p.z) + b * p.z_sb : u_b;   // no gate: re-read u
   const int64_t z_sl = gated ? p.z_sl : p.u_sl;
   const IO* const B_b = static_cast<const IO*>(p.B) + b * p.B_sb;
   const IO* const C_b = static_cast<const IO*>(p.C) + b * p.C_sb;
-  int bj[K], bn[K];
+  int tj[ET], tc[ET];
+  float tbias[ET];
+  int64_t tdq[ET];
+  bool tcok[ET];
 #pragma unroll
-  for (int r = 0; r < K; ++r) {
+  for (int r = 0; r < ET; ++r) {
+    const int e = tid + 256 * r;
+    tj[r] = e / CWG;
+    tc[r] = e % CWG;
+    tcok[r] = d0 + tc[r] < D;
+    tdq[r] = tcok[r] ? d0 + tc[r] : D - 1;
+    tbias[r] = (tcok[r] && p.delta_bias != nullptr) ? p.delta_bias[tdq[r]] : 0.f;
+  }
+  int bj[EB], bn[EB];
+#pragma unroll
+  for (int r = 0; r < EB; ++r) {
     const int e = tid + 256 * r;
     bj[r] = e / NP;
     bn[r] = e % NP;
   }
-  float xT[4], xB[K], xC[K], xH[K];
+  float xu[ET], xd[ET], xy[ET], xz[ET], xB[EB], xC[EB], xH[4];
   auto issue = [&](int64_t t, bool all) __attribute__((always_inline)) {
     const int nt = t == ntiles - 1 ? last_nt : kBTile;
-    const int64_t l0 = t * kBTile;
-    const int jq = sj < nt ? sj : nt - 1;
-    const bool ok = sc_ok && sj < nt;
-    const float vu = T::widen(u_b[(l0 + jq) * p.u_sl + sdq]);
-    const float vd = T::widen(dl_b[(l0 + jq) * p.delta_sl + sdq]);
-    xT[0] = ok ? vu : 0.f;
-    xT[1] = ok ? vd : 0.f;
-    if (all) {
-      const float vy = T::widen(dy_b[(l0 + jq) * p.dy_sl + sdq]);
-      const float vz = T::widen(z_b[(l0 + jq) * z_sl + sdq]);
-      xT[2] = ok ? vy : 0.f;
-      xT[3] = ok ? vz : 0.f;
+    const int64_t l0 = l_begin + t * kBTile;
+#pragma unroll
+    for (int r = 0; r < ET; ++r) {
+      const int jq = tj[r] < nt ? tj[r] : nt - 1;
+      const bool ok = tcok[r] && tj[r] < nt;
+      const float vu = T::widen(u_b[(l0 + jq) * p.u_sl + tdq[r]]);
+      const float vd = T::widen(dl_b[(l0 + jq) * p.delta_sl + tdq[r]]);
+      xu[r] = ok ? vu : 0.f;
+      xd[r] = ok ? vd : 0.f;
+      if (all) {
+        const float vy = T::widen(dy_b[(l0 + jq) * p.dy_sl + tdq[r]]);
+        const float vz = T::widen(z_b[(l0 + jq) * z_sl + tdq[r]]);
+        xy[r] = ok ? vy : 0.f;
+        xz[r] = ok ? vz : 0.f;
+      }
     }
 #pragma unroll
-    for (int r = 0; r < K; ++r) {
+    for (int r = 0; r < EB; ++r) {
       const int jb = bj[r] < nt ? bj[r] : nt - 1;
       const int nb = bn[r] < N ? bn[r] : int(N) - 1;
       const bool okb = bn[r] < N && bj[r] < nt;
@@ -154,64 +205,127 @@ void bwd_kernel(BwdParams p) {
       if (all) {
         const float vc = T::widen(C_b[(l0 + jb) * p.C_sl + nb]);
         xC[r] = okb ? vc : 0.f;
-        const float vh = ck_b[t * D * N + ck_off[r]];
-        xH[r] = nok[r] ? vh : 0.f;
+      }
+    }
+    if (all && MODE == BWD_MAIN) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float vh = ck_b[t * D * N + ck_d + nq[i]];
+        xH[i] = nok[i] ? vh : 0.f;
       }
     }
   };
   auto stage = [&](bool all) __attribute__((always_inline)) {
-    sTok[0][sc][sj] = xT[0];
-    const float x = xT[1] + sbias;
-    sTok[1][sc][sj] = p.dxf ? (sp ? softplus_f32(x) : x) : xT[1];
-    if (all) {
-      sTok[2][sc][sj] = xT[2];
-      sTok[3][sc][sj] = xT[3];
-      // d delta / d raw: sigmoid of the softplus argument, or 1
-      sTok[4][sc][sj] = sp ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
+#pragma unroll
+    for (int r = 0; r < ET; ++r) {
+      const int cc = tc[r], j = tj[r];
+      sTok[0][cc][j] = xu[r];
+      const float x = xd[r] + tbias[r];
+      sTok[1][cc][j] = p.dxf ? (sp ? softplus_f32(x) : x) : xd[r];
+      if (all) {
+        float dyp = xy[r], gzf = 0.f;
+        if (gated) {           // y = yp * z sigmoid(z): dyp = dy z sigmoid(z); dz = yp * gzf
+          const float zz = xz[r];
+          const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+          dyp = xy[r] * zz * sg;
+          gzf = xy[r] * sg * fmaf(zz, 1.f - sg, 1.f);
+        }
+        sTok[2][cc][j] = dyp;
+        sTok[3][cc][j] = gzf;
+        sTok[4][cc][j] = sp ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
+      }
     }
 #pragma unroll
-    for (int r = 0; r < K; ++r) {
-      sBq[bn[r]][bj[r]] = xB[r];
-      if (all) sCq[bn[r]][bj[r]] = xC[r];
+    for (int r = 0; r < EB; ++r) {
+      sBq[bj[r]][bn[r]] = xB[r];
+      if (all) sCq[bj[r]][bn[r]] = xC[r];
     }
   };
+  auto ld4 = [](const float* q) { return *reinterpret_cast<const float4*>(q); };
+  auto el = [](const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
+
+  // (b, d, n) of a per-chunk workspace array [batch][D][N][n_chunks]
+  auto chunk_slot = [&](int i, int cc) { return ((b * D + d) * N + 4 * s + i) * nc + cc; };
+
+  if constexpr (MODE == BWD_ADJOINT) {
+    // mu_{t-1} = Abar_t (dyp_t C_t + mu_t), from mu = 0 after the chunk's last token
+    float mu[4] = {0.f, 0.f, 0.f, 0.f};
+    float dsum = 0.f;
+    issue(ntiles - 1, true);
+    for (int64_t t = ntiles - 1; t >= 0; --t) {
+      __syncthreads();                                      // the previous tile's LDS reads are done
+      stage(true);
+      __syncthreads();
+      if (t > 0) issue(t - 1, true);
+      const int nt = t == ntiles - 1 ? last_nt : kBTile;
+      for (int j = nt - 1; j >= 0; --j) {
+        const float dt = sTok[1][cw][j], dyp = sTok[2][cw][j];
+        const float4 C4 = ld4(&sCq[j][4 * s]);
+        dsum += dt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mu[i] = __builtin_amdgcn_exp2f(dt * a2[i]) * fmaf(dyp, el(C4, i), mu[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (nok[i]) p.adjG[chunk_slot(i, chunk)] = mu[i];
+    if (dvalid && s == 0) p.adjS[(b * D + d) * nc + chunk] = dsum;
+    return;
+  }
 
   // ---- pass 1: forward, checkpoint at every tile start (the last tile is recomputed in pass 2)
-  float h[K];
+  float h[4];
 #pragma unroll
-  for (int k = 0; k < K; ++k) h[k] = (nok[k] && p.h0 != nullptr) ? p.h0[(b * D + d) * N + s + S * k] : 0.f;
+  for (int i = 0; i < 4; ++i) {
+    float h_in = 0.f;
+    if (nok[i]) {
+      if (nc > 1) h_in = p.carry[chunk_slot(i, chunk)];             // the chunk's carried-in state
+      else if (p.h0 != nullptr) h_in = p.h0[(b * D + d) * N + 4 * s + i];
+    }
+    h[i] = h_in;
+  }
   if (ntiles > 1) issue(0, false);
   for (int64_t t = 0; t < ntiles - 1; ++t) {
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      if (nok[k]) ck_b[t * D * N + ck_off[k]] = h[k];
+    for (int i = 0; i < 4; ++i)
+      if (nok[i]) ck_b[t * D * N + ck_d + 4 * s + i] = h[i];
     __syncthreads();                                        // the previous tile's LDS reads are done
     stage(false);
     __syncthreads();
     if (t + 1 < ntiles - 1) issue(t + 1, false);
 #pragma unroll
-    for (int j = 0; j < kBTile; ++j) {                      // every tile before the last is full
-      const float uu = sTok[0][cw][j], dt = sTok[1][cw][j];
+    for (int q = 0; q < kBTile / 4; ++q) {                  // every tile before the last is full
+      const float4 u4 = ld4(&sTok[0][cw][4 * q]), d4 = ld4(&sTok[1][cw][4 * q]);
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const float ab = __builtin_amdgcn_exp2f(dt * a2[k]);
-        const float cf = fmaf(dt, zf[k], fmaf(ab, iA[k], -iA[k]));
-        h[k] = fmaf(ab, h[k], cf * (sBq[s + S * k][j] * uu));
+      for (int jj = 0; jj < 4; ++jj) {
+        const float uu = el(u4, jj), dt = el(d4, jj);
+        const float4 B4 = ld4(&sBq[4 * q + jj][4 * s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ab = __builtin_amdgcn_exp2f(dt * a2[i]);
+          const float cf = fmaf(dt, zf[i], fmaf(ab, iA[i], -iA[i]));
+          h[i] = fmaf(ab, h[i], cf * (el(B4, i) * uu));
+        }
       }
-      if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
-  for (int k = 0; k < K; ++k)
-    if (nok[k]) ck_b[(ntiles - 1) * D * N + ck_off[k]] = h[k];
+  for (int i = 0; i < 4; ++i)
+    if (nok[i]) ck_b[(ntiles - 1) * D * N + ck_d + 4 * s + i] = h[i];
   __syncthreads();                                          // pass 1's LDS reads are done
 
-  // ---- pass 2: tiles backwards
-  float mu[K], gA[K];
+  // ---- pass 2: tiles backwards, from the adjoint reaching the chunk's end
+  float mu[4], gA[4];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    mu[k] = (nok[k] && p.dlast != nullptr) ? p.dlast[(b * D + d) * N + s + S * k] : 0.f;
-    gA[k] = 0.f;
+  for (int i = 0; i < 4; ++i) {
+    float m = 0.f;
+    if (nok[i]) {
+      if (nc > 1) m = p.adj_in[chunk_slot(i, chunk)];
+      else if (p.dlast != nullptr) m = p.dlast[(b * D + d) * N + 4 * s + i];
+    }
+    mu[i] = m;
+    gA[i] = 0.f;
   }
   float gD = 0.f, gbias = 0.f;
   IO* const du_b = static_cast<IO*>(p.du) + b * L * D + d;
@@ -225,17 +339,18 @@ void bwd_kernel(BwdParams p) {
   // first nt.
   auto tile = [&](int64_t t, int nt, auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
-    float hp[kBTile][K];                                   // state before token j of the tile
+    float hp[kBTile][4];                                   // state before token j of the tile
 #pragma unroll
     for (int j = 0; j < kBTile; ++j) {
       if (FULL || j < nt) {
         const float uu = sTok[0][cw][j], dt = sTok[1][cw][j];
+        const float4 B4 = ld4(&sBq[j][4 * s]);
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          hp[j][k] = h[k];
-          const float ab = __builtin_amdgcn_exp2f(dt * a2[k]);
-          const float cf = fmaf(dt, zf[k], fmaf(ab, iA[k], -iA[k]));
-          h[k] = fmaf(ab, h[k], cf * (sBq[s + S * k][j] * uu));
+        for (int i = 0; i < 4; ++i) {
+          hp[j][i] = h[i];
+          const float ab = __builtin_amdgcn_exp2f(dt * a2[i]);
+          const float cf = fmaf(dt, zf[i], fmaf(ab, iA[i], -iA[i]));
+          h[i] = fmaf(ab, h[i], cf * (el(B4, i) * uu));
         }
       }
       if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
@@ -243,52 +358,48 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int j = kBTile - 1; j >= 0; --j) {
       if (FULL || j < nt) {
-        const int64_t l = t * kBTile + j;
-        const float uu = sTok[0][cw][j], dt = sTok[1][cw][j], dyv = sTok[2][cw][j], zz = sTok[3][cw][j];
-        float Bv[K], Cv[K], ab[K], cf[K], hj[K];
+        const int64_t l = l_begin + t * kBTile + j;
+        const float uu = sTok[0][cw][j], dt = sTok[1][cw][j], dyp = sTok[2][cw][j];
+        const float gzf = sTok[3][cw][j], sig = sTok[4][cw][j];
+        const float4 B4 = ld4(&sBq[j][4 * s]), C4 = ld4(&sCq[j][4 * s]);
+        const float dt2 = dt * dt;
+        float ab[4], cf[4], hj[4];
         float spart = 0.f;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          Bv[k] = sBq[s + S * k][j];
-          Cv[k] = sCq[s + S * k][j];
-          ab[k] = __builtin_amdgcn_exp2f(dt * a2[k]);
-          cf[k] = fmaf(dt, zf[k], fmaf(ab[k], iA[k], -iA[k]));
-          hj[k] = fmaf(ab[k], hp[j][k], cf[k] * (Bv[k] * uu));
-          spart = fmaf(Cv[k], hj[k], spart);
+        for (int i = 0; i < 4; ++i) {
+          ab[i] = __builtin_amdgcn_exp2f(dt * a2[i]);
+          cf[i] = fmaf(dt, zf[i], fmaf(ab[i], iA[i], -iA[i]));
+          hj[i] = fmaf(ab[i], hp[j][i], cf[i] * (el(B4, i) * uu));
+          spart = fmaf(el(C4, i), hj[i], spart);
         }
-        float dyp = dyv, gz = 0.f;
-        if (gated) {
-          const float yp = fmaf(dskip, uu, row16_sum(spart));               // readout s_t + D u
-          const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
-          gz = dyv * yp * sg * fmaf(zz, 1.f - sg, 1.f);
-          dyp = dyv * zz * sg;
-        }
-        float gu = 0.f, gdt = 0.f, pb[K], pc[K];
+        float gu = 0.f, gdt = 0.f, pb[4], pc[4];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const float lam = fmaf(dyp, Cv[k], mu[k]);
-          const float bu = Bv[k] * uu;
-          gu = fmaf(lam, cf[k] * Bv[k], gu);
-          const float dcdd = first ? 1.f : ab[k];
-          gdt = fmaf(lam, fmaf(a[k] * ab[k], hp[j][k], dcdd * bu), gdt);
+        for (int i = 0; i < 4; ++i) {
+          const float Bi = el(B4, i);
+          const float lam = fmaf(dyp, el(C4, i), mu[i]);
+          const float bu = Bi * uu;
+          gu = fmaf(lam, cf[i] * Bi, gu);
+          const float dcdd = first ? 1.f : ab[i];
+          gdt = fmaf(lam, fmaf(a[i] * ab[i], hp[j][i], dcdd * bu), gdt);
           // dc/da = delta^2 phi(x), x = delta a; phi by its series near 0
-          const float x = dt * a[k];
+          const float x = dt * a[i];
           const float series = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
-          const float closed = (x * ab[k] - (ab[k] - 1.f)) * __builtin_amdgcn_rcpf(x * x);
-          const float dcda = first ? 0.f : dt * dt * (fabsf(x) < 0.1f ? series : closed);
-          gA[k] = fmaf(lam, fmaf(dt * ab[k], hp[j][k], dcda * bu), gA[k]);
-          pb[k] = lam * cf[k] * uu;
-          pc[k] = dyp * hj[k];
-          mu[k] = ab[k] * lam;
+          const float closed = fmaf(x, ab[i], 1.f - ab[i]) * __builtin_amdgcn_rcpf(x * x);
+          const float dcda = first ? 0.f : dt2 * (fabsf(x) < 0.1f ? series : closed);
+          gA[i] = fmaf(lam, fmaf(dt * ab[i], hp[j][i], dcda * bu), gA[i]);
+          pb[i] = lam * cf[i] * uu;
+          pc[i] = dyp * hj[i];
+          mu[i] = ab[i] * lam;
         }
         // keep the accumulations here: left alone, the compiler sinks them to the end of the
         // tile and keeps every token's operands live until then
 #pragma unroll
-        for (int k = 0; k < K; ++k) __asm__ __volatile__("" : "+v"(gA[k]));
-        gu = row16_sum(gu);
-        gdt = row16_sum(gdt);
+        for (int i = 0; i < 4; ++i) __asm__ __volatile__("" : "+v"(gA[i]));
+        gu = chan_sum<SL>(gu);
+        gdt = chan_sum<SL>(gdt);
+        const float gz = gated ? fmaf(dskip, uu, chan_sum<SL>(spart)) * gzf : 0.f;   // yp * gzf
         const float du = fmaf(dskip, dyp, gu);
-        const float draw = gdt * sTok[4][cw][j];
+        const float draw = gdt * sig;
         gD = fmaf(dyp, uu, gD);
         gbias += draw;
         __asm__ __volatile__("" : "+v"(gD), "+v"(gbias));
@@ -297,17 +408,15 @@ void bwd_kernel(BwdParams p) {
           put(ddl_b + l * D, draw);
           if (dz_b != nullptr) put(dz_b + l * D, gz);
         }
-        // sums over the wavefront's four channels; the wavefront's sum goes to its LDS slot
+        // sums over the wavefront's channels; lanes of channel 0 write the wavefront's sum
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          pb[k] += __shfl_xor(pb[k], 16);
-          pb[k] += __shfl_xor(pb[k], 32);
-          pc[k] += __shfl_xor(pc[k], 16);
-          pc[k] += __shfl_xor(pc[k], 32);
-          if (c == 0) {
-            sBC[w][0][j][s + S * k] = pb[k];
-            sBC[w][1][j][s + S * k] = pc[k];
-          }
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = wave_chan_sum<SL>(pb[i]);
+          pc[i] = wave_chan_sum<SL>(pc[i]);
+        }
+        if (c == 0) {
+          *reinterpret_cast<float4*>(&sBC[w][0][j][4 * s]) = make_float4(pb[0], pb[1], pb[2], pb[3]);
+          *reinterpret_cast<float4*>(&sBC[w][1][j][4 * s]) = make_float4(pc[0], pc[1], pc[2], pc[3]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);   // one token at a time: bounds the live registers
@@ -318,15 +427,15 @@ void bwd_kernel(BwdParams p) {
     stage(true);                         // the previous tile's LDS reads ended at its barrier
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < K; ++k) h[k] = xH[k];               // the tile's checkpoint
+    for (int i = 0; i < 4; ++i) h[i] = xH[i];               // the tile's checkpoint
     if (t > 0) issue(t - 1, true);
     if (t == ntiles - 1 && last_nt < kBTile) tile(t, last_nt, std::false_type{});
     else tile(t, kBTile, std::true_type{});
     __syncthreads();
     // this tile's partial sums over the workgroup's channels (wavefronts in order)
     const int nt = t == ntiles - 1 ? last_nt : kBTile;
-    float* const gB = p.pB + ((int64_t(g) * p.batch + b) * L + t * kBTile) * N;
-    float* const gC = p.pC + ((int64_t(g) * p.batch + b) * L + t * kBTile) * N;
+    float* const gB = p.pB + ((int64_t(g) * p.batch + b) * L + l_begin + t * kBTile) * N;
+    float* const gC = p.pC + ((int64_t(g) * p.batch + b) * L + l_begin + t * kBTile) * N;
     for (int i = tid; i < kBTile * NP; i += 256) {
       const int j = i / NP, n = i % NP;
       if (j < nt && n < N) {
@@ -336,17 +445,18 @@ void bwd_kernel(BwdParams p) {
     }
   }
 
-  // ---- per-(b, d) results: partial sums over this batch row, and the initial state's gradient
+  // ---- per-(b, chunk, d) results: partial sums over this batch row and chunk, and (first
+  // chunk) the initial state's gradient
+  const int64_t bq = b * nc + chunk;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    if (!nok[k]) continue;
-    const int64_t o = (b * D + d) * N + s + S * k;
-    p.pA[o] = gA[k];
-    if (p.dh0 != nullptr) p.dh0[o] = mu[k];
+  for (int i = 0; i < 4; ++i) {
+    if (!nok[i]) continue;
+    p.pA[(bq * D + d) * N + 4 * s + i] = gA[i];
+    if (p.dh0 != nullptr && chunk == 0) p.dh0[(b * D + d) * N + 4 * s + i] = mu[i];
   }
   if (dvalid && s == 0) {
-    p.pD[b * D + d] = gD;
-    p.pbias[b * D + d] = gbias;
+    p.pD[bq * D + d] = gD;
+    p.pbias[bq * D + d] = gbias;
   }
 }
 
@@ -361,27 +471,56 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restri
   else out[i] = acc;
 }
 
-template <typename IO, int K>
+// mu_out[c] = adjoint reaching the end of chunk c: mu_out[nc-1] = dlast and
+// mu_out[c-1] = G_c + exp(A sum_{t in c} delta_t) mu_out[c]; one thread per (b, d, n).
+__global__ __launch_bounds__(256) void bwd_adjoint_combine_kernel(BwdParams p) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= p.batch * p.D * p.N) return;
+  const int64_t n = i % p.N, bd = i / p.N, d = bd % p.D;
+  const int nc = p.n_chunks;
+  const float a2 = p.A[d * p.N + n] * kLog2e;
+  float mu = p.dlast != nullptr ? p.dlast[i] : 0.f;
+  for (int c = nc - 1; c >= 0; --c) {
+    p.adj_in[i * nc + c] = mu;
+    if (c > 0) mu = fmaf(__builtin_amdgcn_exp2f(a2 * p.adjS[bd * nc + c]), mu, p.adjG[i * nc + c]);
+  }
+}
+
+template <typename IO, int SL, int MODE>
 hipError_t launch_bwd_k(const BwdParams& p, hipStream_t stream) {
-  const int64_t blocks = p.batch * int64_t(p.groups);
+  const int64_t blocks = p.batch * int64_t(MODE == BWD_ADJOINT ? p.n_chunks - 1 : p.n_chunks) * p.groups;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_kernel<IO, K>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_kernel<IO, SL, MODE>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename IO, int MODE>
+hipError_t launch_bwd_m(const BwdParams& p, hipStream_t stream) {
+  const int SL = bwd_lanes_per_channel(p.N);
+  if (SL == 4) return launch_bwd_k<IO, 4, MODE>(p, stream);
+  if (SL == 8) return launch_bwd_k<IO, 8, MODE>(p, stream);
+  return launch_bwd_k<IO, 16, MODE>(p, stream);
+}
+
+template <typename IO>
+hipError_t launch_bwd_io(const BwdParams& p, hipStream_t stream) {
+  if (p.n_chunks > 1) {
+    hipError_t e = launch_bwd_m<IO, BWD_ADJOINT>(p, stream);
+    if (e != hipSuccess) return e;
+    const int64_t m = p.batch * p.D * p.N;
+    hipLaunchKernelGGL(bwd_adjoint_combine_kernel, dim3(unsigned((m + 255) / 256)), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_bwd_m<IO, BWD_MAIN>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(bool bf16, int K, const BwdParams& p, hipStream_t stream) {
-  if (bf16) {
-    if (K == 1) return launch_bwd_k<uint16_t, 1>(p, stream);
-    if (K == 2) return launch_bwd_k<uint16_t, 2>(p, stream);
-    if (K == 4) return launch_bwd_k<uint16_t, 4>(p, stream);
-  } else {
-    if (K == 1) return launch_bwd_k<float, 1>(p, stream);
-    if (K == 2) return launch_bwd_k<float, 2>(p, stream);
-    if (K == 4) return launch_bwd_k<float, 4>(p, stream);
-  }
-  return hipErrorInvalidValue;
+int bwd_lanes_per_channel(int64_t N) { return N <= 16 ? 4 : N <= 32 ? 8 : 16; }
+
+hipError_t launch_bwd(bool bf16, const BwdParams& p, hipStream_t stream) {
+  return bf16 ? launch_bwd_io<uint16_t>(p, stream) : launch_bwd_io<float>(p, stream);
 }
 
 hipError_t launch_sum_partials(const float* part, int64_t nparts, int64_t stride, void* out, int64_t m, bool bf16,

@@ -102,20 +102,28 @@ struct BwdParams {
   void* dz;             // may be null (then not written)
   float* dh0;           // may be null
   float* ckpt;          // [batch][ntiles][D][N] state at the start of every tile
-  float* pB;            // [groups][batch][L][N] per-group partial sums of dB
+  float* pB;            // [groups][batch][L][N] per-channel-group partial sums of dB
   float* pC;            // [groups][batch][L][N] per-group partial sums of dC
-  float* pA;            // [batch][D][N] per-batch partial sums of dA
-  float* pD;            // [batch][D] per-batch partial sums of dDskip
-  float* pbias;         // [batch][D] per-batch partial sums of the bias gradient
+  float* pA;            // [batch][n_chunks][D][N] partial sums of dA
+  float* pD;            // [batch][n_chunks][D] partial sums of dDskip
+  float* pbias;         // [batch][n_chunks][D] partial sums of the bias gradient
+  float* carry;         // [batch][D][N][n_chunks] state entering each chunk (n_chunks > 1)
+  float* adjG;          // [batch][D][N][n_chunks] adjoint a chunk hands back from a zero start
+  float* adjS;          // [batch][D][n_chunks] sum of delta over each chunk
+  float* adj_in;        // [batch][D][N][n_chunks] adjoint reaching each chunk's end
   int64_t batch, L, D, N;
   int64_t u_sb, u_sl, delta_sb, delta_sl, z_sb, z_sl, dy_sb, dy_sl, B_sb, B_sl, C_sb, C_sl;
   int64_t ntiles;       // ceil(L / 16)
-  int32_t groups;       // ceil(D / 16)
+  int64_t chunk_len;    // tokens per chunk, a multiple of 16
+  int32_t n_chunks;
+  int32_t groups;       // ceil(D / channels per workgroup)
   int32_t euler;
   int32_t dxf;
   int32_t softplus;
 };
-hipError_t launch_bwd(bool bf16, int K, const BwdParams& p, hipStream_t stream);
+// lanes per channel of the backward kernel (4 states per lane): 4, 8 or 16
+int bwd_lanes_per_channel(int64_t N);
+hipError_t launch_bwd(bool bf16, const BwdParams& p, hipStream_t stream);
 // out[i] = sum_{j < nparts} part[j * stride + i], i < m; out in the I/O type when bf16
 hipError_t launch_sum_partials(const float* part, int64_t nparts, int64_t stride, void* out, int64_t m, bool bf16,
                                hipStream_t stream);

@@ -141,19 +141,11 @@ int check_pointers(const void* u, const void* delta, const float* A, const void*
   return SELSCAN_OK;
 }
 
-int run(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B, const void* C,
-        const float* Dskip, const void* z, void* y, const float* h0, float* last_state, const selscan_dims* dims,
-        const Plan& plan, void* workspace, hipStream_t stream) {
-  const selscan_dims& d = *dims;
-  if (d.batch == 0) return SELSCAN_OK;
-  if (d.seqlen == 0) {                     // no tokens: the initial state is handed back
-    if (last_state && last_state != h0) {
-      const int64_t n = d.batch * d.dim * d.dstate;
-      hipError_t e = h0 ? selscan::launch_copy(last_state, h0, n, stream) : selscan::launch_fill_zero(last_state, n, stream);
-      if (e != hipSuccess) return hip_fail(e);
-    }
-    return SELSCAN_OK;
-  }
+// Kernel parameters of one forward call (chunk plan, options, path choice); the chunked
+// path's workspace pointers are set by the caller.
+selscan::ScanParams scan_params(const void* u, const void* delta, const float* delta_bias, const float* A,
+                                const void* B, const void* C, const float* Dskip, const void* z, void* y,
+                                const float* h0, float* last_state, const selscan_dims& d, const Plan& plan) {
   selscan::ScanParams p{};
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = z; p.y = y;
   p.last_state = last_state;
@@ -183,6 +175,23 @@ int run(const void* u, const void* delta, const float* delta_bias, const float* 
     const bool bc_ok = plan.ti || (d.dstate % 4 == 0 && quad_ok(B, d.B_sb, d.B_sl) && quad_ok(C, d.C_sb, d.C_sl));
     p.pipelined = (plan.S == 16 && io_ok && bc_ok && !(d.path & SELSCAN_PATH_FLAG_SCALAR_IO)) ? 1 : 0;
   }
+  return p;
+}
+
+int run(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B, const void* C,
+        const float* Dskip, const void* z, void* y, const float* h0, float* last_state, const selscan_dims* dims,
+        const Plan& plan, void* workspace, hipStream_t stream) {
+  const selscan_dims& d = *dims;
+  if (d.batch == 0) return SELSCAN_OK;
+  if (d.seqlen == 0) {                     // no tokens: the initial state is handed back
+    if (last_state && last_state != h0) {
+      const int64_t n = d.batch * d.dim * d.dstate;
+      hipError_t e = h0 ? selscan::launch_copy(last_state, h0, n, stream) : selscan::launch_fill_zero(last_state, n, stream);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    return SELSCAN_OK;
+  }
+  selscan::ScanParams p = scan_params(u, delta, delta_bias, A, B, C, Dskip, z, y, h0, last_state, d, plan);
   hipError_t e;
   if (!plan.chunked) {
     e = selscan::launch_scan_pass(selscan::kPassSingle, plan.bf16, plan.ti, plan.S, plan.K, p, stream);
@@ -238,12 +247,17 @@ int fwd_impl(const void* u, const void* delta, const float* delta_bias, const fl
 
 // ---- backward pass
 struct BwdPlan {
-  int K = 1;
-  int64_t groups = 0, ntiles = 0;
-  size_t off_pB = 0, off_pC = 0, off_pA = 0, off_pD = 0, off_pbias = 0, bytes = 0;
+  Plan fwd;                   // the forward plan whose chunked state pass supplies the carries
+  int64_t groups = 0, ntiles = 0, chunk_len = 0;
+  int32_t n_chunks = 1;
+  size_t off_pB = 0, off_pC = 0, off_pA = 0, off_pD = 0, off_pbias = 0;
+  size_t off_state = 0, off_dsum = 0, off_adjG = 0, off_adjS = 0, off_adjin = 0, bytes = 0;
 };
 
-// Validate dims for the backward pass and lay out its workspace:
+constexpr int64_t kBwdTargetBlocks = 1024;   // about four wavefronts per SIMD
+
+// Validate dims for the backward pass and lay out its workspace (groups: channel groups of
+// one workgroup, 64, 32 or 16 channels):
 //   ckpt [batch][ntiles][D][N], pB and pC [groups][batch][L][N], pA [batch][D][N],
 //   pD and pbias [batch][D]  (fp32, each 256-byte aligned).
 int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
@@ -253,23 +267,56 @@ int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
   if (plan.ti) return SELSCAN_ERR_UNSUPPORTED;        // backward of fixed coefficients: not built
   const selscan_dims& d = *dims;
   BwdPlan b;
-  b.K = d.dstate <= 16 ? 1 : d.dstate <= 32 ? 2 : 4;
-  b.groups = (d.dim + 15) / 16;
+  const int64_t cwg = 4 * 64 / selscan::bwd_lanes_per_channel(d.dstate);   // channels per workgroup
+  b.groups = (d.dim + cwg - 1) / cwg;
   b.ntiles = (d.seqlen + 15) / 16;
-  if (d.batch * b.groups > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
+  // chunks of the sequence when (batch row, channel group) items alone leave the GPU idle
+  int64_t nc = 1;
+  const int64_t items = d.batch * b.groups;
+  if (items > 0 && items < kBwdTargetBlocks && d.seqlen >= 128) {
+    nc = (kBwdTargetBlocks + items - 1) / items;
+    if (nc > d.seqlen / 64) nc = d.seqlen / 64;                  // chunks of at least 64 tokens
+    if (nc > kMaxChunks) nc = kMaxChunks;
+    if (nc < 1) nc = 1;
+  }
+  b.chunk_len = nc > 1 ? round_up((d.seqlen + nc - 1) / nc, 16) : round_up(d.seqlen > 0 ? d.seqlen : 1, 16);
+  // a forward plan chunked for its 32-bit tile addressing bounds the chunk length
+  if (plan.chunked && plan.chunk_len < b.chunk_len) b.chunk_len = plan.chunk_len;
+  b.n_chunks = d.seqlen > 0 ? int32_t((d.seqlen + b.chunk_len - 1) / b.chunk_len) : 1;
+  if (d.batch * b.n_chunks * b.groups > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
+  b.fwd = plan;
+  if (b.n_chunks > 1) {
+    // the forward plan of the carries: its state pass over the same chunks
+    b.fwd.chunked = true;
+    b.fwd.chunk_len = b.chunk_len;
+    b.fwd.n_chunks = b.n_chunks;
+  }
   auto al = [](int64_t x) { return size_t(round_up(x, 256)); };
   const int64_t f = int64_t(sizeof(float));
+  const int64_t bdn = d.batch * d.dim * d.dstate, ncq = b.n_chunks;
   size_t off = al(f * d.batch * b.ntiles * d.dim * d.dstate);
   b.off_pB = off;
   off += al(f * b.groups * d.batch * d.seqlen * d.dstate);
   b.off_pC = off;
   off += al(f * b.groups * d.batch * d.seqlen * d.dstate);
   b.off_pA = off;
-  off += al(f * d.batch * d.dim * d.dstate);
+  off += al(f * ncq * bdn);
   b.off_pD = off;
-  off += al(f * d.batch * d.dim);
+  off += al(f * ncq * d.batch * d.dim);
   b.off_pbias = off;
-  off += al(f * d.batch * d.dim);
+  off += al(f * ncq * d.batch * d.dim);
+  if (b.n_chunks > 1) {
+    b.off_state = off;
+    off += al(f * ncq * bdn);
+    b.off_dsum = off;
+    off += al(f * ncq * d.batch * d.dim);
+    b.off_adjG = off;
+    off += al(f * ncq * bdn);
+    b.off_adjS = off;
+    off += al(f * ncq * d.batch * d.dim);
+    b.off_adjin = off;
+    off += al(f * ncq * bdn);
+  }
   b.bytes = (d.batch * d.seqlen > 0) ? off : 0;
   *out = b;
   return SELSCAN_OK;
@@ -305,19 +352,42 @@ int bwd_run(const void* u, const void* delta, const float* delta_bias, const flo
   p.z_sb = d.z_sb; p.z_sl = d.z_sl; p.dy_sb = d.y_sb; p.dy_sl = d.y_sl;
   p.B_sb = d.B_sb; p.B_sl = d.B_sl; p.C_sb = d.C_sb; p.C_sl = d.C_sl;
   p.ntiles = plan.ntiles;
+  p.chunk_len = plan.chunk_len;
+  p.n_chunks = plan.n_chunks;
   p.groups = int32_t(plan.groups);
   p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
   p.softplus = d.delta_softplus != 0 ? 1 : 0;
   p.dxf = (p.softplus || delta_bias != nullptr) ? 1 : 0;
-  e = selscan::launch_bwd(bf16, plan.K, p, stream);
+  if (plan.n_chunks > 1) {
+    // the state entering every chunk: the forward's chunked state pass and prefix
+    selscan::ScanParams f = scan_params(u, delta, delta_bias, A, B, C, Dskip, z, nullptr, h0, nullptr, d, plan.fwd);
+    f.ws_state = reinterpret_cast<float*>(ws + plan.off_state);
+    f.ws_dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
+    e = selscan::launch_scan_pass(selscan::kPassState, bf16, false, plan.fwd.S, plan.fwd.K, f, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    selscan::PrefixParams q{};
+    q.A = A; q.dsum = f.ws_dsum; q.state = f.ws_state; q.h0 = h0;
+    q.batch = d.batch; q.D = d.dim; q.N = d.dstate; q.n_chunks = plan.n_chunks;
+    int sw = 1;
+    while (sw < plan.n_chunks) sw <<= 1;
+    q.seg_width = sw;
+    e = selscan::launch_chunk_prefix(q, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    p.carry = f.ws_state;
+    p.adjG = reinterpret_cast<float*>(ws + plan.off_adjG);
+    p.adjS = reinterpret_cast<float*>(ws + plan.off_adjS);
+    p.adj_in = reinterpret_cast<float*>(ws + plan.off_adjin);
+  }
+  e = selscan::launch_bwd(bf16, p, stream);
   const int64_t m_bc = d.batch * d.seqlen * d.dstate;
   if (e == hipSuccess) e = selscan::launch_sum_partials(p.pB, plan.groups, m_bc, dB, m_bc, bf16, stream);
   if (e == hipSuccess) e = selscan::launch_sum_partials(p.pC, plan.groups, m_bc, dC, m_bc, bf16, stream);
+  const int64_t nbc = d.batch * plan.n_chunks;              // partials: one per (batch row, chunk)
   if (e == hipSuccess)
-    e = selscan::launch_sum_partials(p.pA, d.batch, d.dim * d.dstate, dA, d.dim * d.dstate, false, stream);
-  if (e == hipSuccess && dDskip) e = selscan::launch_sum_partials(p.pD, d.batch, d.dim, dDskip, d.dim, false, stream);
+    e = selscan::launch_sum_partials(p.pA, nbc, d.dim * d.dstate, dA, d.dim * d.dstate, false, stream);
+  if (e == hipSuccess && dDskip) e = selscan::launch_sum_partials(p.pD, nbc, d.dim, dDskip, d.dim, false, stream);
   if (e == hipSuccess && ddelta_bias)
-    e = selscan::launch_sum_partials(p.pbias, d.batch, d.dim, ddelta_bias, d.dim, false, stream);
+    e = selscan::launch_sum_partials(p.pbias, nbc, d.dim, ddelta_bias, d.dim, false, stream);
   return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
 }
 

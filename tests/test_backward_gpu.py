@@ -123,3 +123,21 @@ def test_backward_deterministic():
     g2 = ss.selective_scan_bwd(*args, dy=dy)
     t.cuda.synchronize()
     assert all(t.equal(g1[k], g2[k]) for k in g1)
+
+
+@pytest.mark.parametrize("N", [4, 16, 32, 64])
+@pytest.mark.parametrize("L", [333, 1000])
+def test_backward_sequence_chunks(N, L):
+    """Few (batch row, channel group) items and a long sequence: the backward splits the
+    sequence into chunks (ragged last chunk), carrying states forward and adjoints back."""
+    inp = s6_workloads.generate("mamba130m_f32", "active", batch=1, L=L, D=24, N=N)
+    b, _, D, _ = inp.shape
+    h0 = s6_workloads.running_state(inp, scale=1.0)
+    dlast = np.random.default_rng(L).standard_normal((b, D, N)).astype(np.float32)
+    check(run_case(inp, h0=h0, dlast=dlast, seed=L + N), "f32", "chunks N=%d L=%d" % (N, L))
+
+
+def test_backward_sequence_chunks_options_bf16():
+    inp = s6_workloads.generate("longctx_bf16", batch=1, L=900, D=40)
+    raw, bias = s6_workloads.raw_step_sizes(inp)
+    check(run_case(inp, delta=raw, bias=bias, softplus=True, euler=True), "bf16", "chunks bf16 options")
