@@ -81,6 +81,14 @@ __device__ __forceinline__ float wave_chan_sum(float v) {
 // at least this many wavefronts per SIMD (caps the registers)
 constexpr int kBwdMinWaves = 2;
 
+// Order this wavefront's LDS traffic (its accesses execute in issue order; this only stops
+// the compiler from moving them across).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 enum { BWD_ADJOINT = 0, BWD_MAIN = 1 };
 
 // SL lanes per channel, 4 states per lane (state n = 4 s + i); 64 / SL channels per wavefront.
@@ -104,6 +112,9 @@ void bwd_kernel(BwdParams p) {
   __shared__ __align__(16) float sBq[kBTile][kBCRow];
   __shared__ __align__(16) float sCq[kBTile][kBCRow];
   __shared__ __align__(16) float sBC[4][2][kBTile][NP];   // each wavefront's dB / dC sums
+  // each wavefront's per-channel dB / dC terms of four tokens, summed over its channels
+  // every fourth token
+  __shared__ __align__(16) float sRed[4][2][4][CW][NP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -156,54 +167,44 @@ void bwd_kernel(BwdParams p) {
   const int64_t z_sl = gated ? p.z_sl : p.u_sl;
   const IO* const B_b = static_cast<const IO*>(p.B) + b * p.B_sb;
   const IO* const C_b = static_cast<const IO*>(p.C) + b * p.C_sb;
-  int tj[ET], tc[ET];
-  float tbias[ET];
-  int64_t tdq[ET];
-  bool tcok[ET];
-#pragma unroll
-  for (int r = 0; r < ET; ++r) {
-    const int e = tid + 256 * r;
-    tj[r] = e / CWG;
-    tc[r] = e % CWG;
-    tcok[r] = d0 + tc[r] < D;
-    tdq[r] = tcok[r] ? d0 + tc[r] : D - 1;
-    tbias[r] = (tcok[r] && p.delta_bias != nullptr) ? p.delta_bias[tdq[r]] : 0.f;
-  }
-  int bj[EB], bn[EB];
-#pragma unroll
-  for (int r = 0; r < EB; ++r) {
-    const int e = tid + 256 * r;
-    bj[r] = e / NP;
-    bn[r] = e % NP;
-  }
+  // CWG and NP divide 256: a thread's channel (and B/C state) is the same for all its
+  // elements, which are 256 / CWG (256 / NP) tokens apart
+  constexpr int kTStep = 256 / CWG, kBStep = 256 / NP;
+  const int tj0 = tid / CWG, tc = tid % CWG;
+  const bool tcok = d0 + tc < D;
+  const int64_t tdq = tcok ? d0 + tc : D - 1;
+  const float tbias = (tcok && p.delta_bias != nullptr) ? p.delta_bias[tdq] : 0.f;
+  const int bj0 = tid / NP, bn = tid % NP;
+  const int bnq = bn < N ? bn : int(N) - 1;
   float xu[ET], xd[ET], xy[ET], xz[ET], xB[EB], xC[EB], xH[4];
   auto issue = [&](int64_t t, bool all) __attribute__((always_inline)) {
     const int nt = t == ntiles - 1 ? last_nt : kBTile;
     const int64_t l0 = l_begin + t * kBTile;
 #pragma unroll
     for (int r = 0; r < ET; ++r) {
-      const int jq = tj[r] < nt ? tj[r] : nt - 1;
-      const bool ok = tcok[r] && tj[r] < nt;
-      const float vu = T::widen(u_b[(l0 + jq) * p.u_sl + tdq[r]]);
-      const float vd = T::widen(dl_b[(l0 + jq) * p.delta_sl + tdq[r]]);
+      const int j = tj0 + kTStep * r;
+      const int jq = j < nt ? j : nt - 1;
+      const bool ok = tcok && j < nt;
+      const float vu = T::widen(u_b[(l0 + jq) * p.u_sl + tdq]);
+      const float vd = T::widen(dl_b[(l0 + jq) * p.delta_sl + tdq]);
       xu[r] = ok ? vu : 0.f;
       xd[r] = ok ? vd : 0.f;
       if (all) {
-        const float vy = T::widen(dy_b[(l0 + jq) * p.dy_sl + tdq[r]]);
-        const float vz = T::widen(z_b[(l0 + jq) * z_sl + tdq[r]]);
+        const float vy = T::widen(dy_b[(l0 + jq) * p.dy_sl + tdq]);
+        const float vz = T::widen(z_b[(l0 + jq) * z_sl + tdq]);
         xy[r] = ok ? vy : 0.f;
         xz[r] = ok ? vz : 0.f;
       }
     }
 #pragma unroll
     for (int r = 0; r < EB; ++r) {
-      const int jb = bj[r] < nt ? bj[r] : nt - 1;
-      const int nb = bn[r] < N ? bn[r] : int(N) - 1;
-      const bool okb = bn[r] < N && bj[r] < nt;
-      const float vb = T::widen(B_b[(l0 + jb) * p.B_sl + nb]);
+      const int j = bj0 + kBStep * r;
+      const int jb = j < nt ? j : nt - 1;
+      const bool okb = bn < N && j < nt;
+      const float vb = T::widen(B_b[(l0 + jb) * p.B_sl + bnq]);
       xB[r] = okb ? vb : 0.f;
       if (all) {
-        const float vc = T::widen(C_b[(l0 + jb) * p.C_sl + nb]);
+        const float vc = T::widen(C_b[(l0 + jb) * p.C_sl + bnq]);
         xC[r] = okb ? vc : 0.f;
       }
     }
@@ -218,10 +219,10 @@ void bwd_kernel(BwdParams p) {
   auto stage = [&](bool all) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < ET; ++r) {
-      const int cc = tc[r], j = tj[r];
-      sTok[0][cc][j] = xu[r];
-      const float x = xd[r] + tbias[r];
-      sTok[1][cc][j] = p.dxf ? (sp ? softplus_f32(x) : x) : xd[r];
+      const int j = tj0 + kTStep * r;
+      sTok[0][tc][j] = xu[r];
+      const float x = xd[r] + tbias;
+      sTok[1][tc][j] = p.dxf ? (sp ? softplus_f32(x) : x) : xd[r];
       if (all) {
         float dyp = xy[r], gzf = 0.f;
         if (gated) {           // y = yp * z sigmoid(z): dyp = dy z sigmoid(z); dz = yp * gzf
@@ -230,15 +231,16 @@ void bwd_kernel(BwdParams p) {
           dyp = xy[r] * zz * sg;
           gzf = xy[r] * sg * fmaf(zz, 1.f - sg, 1.f);
         }
-        sTok[2][cc][j] = dyp;
-        sTok[3][cc][j] = gzf;
-        sTok[4][cc][j] = sp ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
+        sTok[2][tc][j] = dyp;
+        sTok[3][tc][j] = gzf;
+        sTok[4][tc][j] = sp ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
       }
     }
 #pragma unroll
     for (int r = 0; r < EB; ++r) {
-      sBq[bj[r]][bn[r]] = xB[r];
-      if (all) sCq[bj[r]][bn[r]] = xC[r];
+      const int j = bj0 + kBStep * r;
+      sBq[j][bn] = xB[r];
+      if (all) sCq[j][bn] = xC[r];
     }
   };
   auto ld4 = [](const float* q) { return *reinterpret_cast<const float4*>(q); };
@@ -355,6 +357,8 @@ void bwd_kernel(BwdParams p) {
       }
       if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
+    // re-read the tile from LDS below rather than keep the values read above live
+    __asm__ __volatile__("" ::: "memory");
 #pragma unroll
     for (int j = kBTile - 1; j >= 0; --j) {
       if (FULL || j < nt) {
@@ -381,11 +385,12 @@ void bwd_kernel(BwdParams p) {
           gu = fmaf(lam, cf[i] * Bi, gu);
           const float dcdd = first ? 1.f : ab[i];
           gdt = fmaf(lam, fmaf(a[i] * ab[i], hp[j][i], dcdd * bu), gdt);
-          // dc/da = delta^2 phi(x), x = delta a; phi by its series near 0
+          // dc/da = (delta Abar - c) / a, or delta^2 phi(x), x = delta a, by the series of
+          // phi(x) = (x e^x - (e^x - 1)) / x^2 near 0 where the first form cancels (and at a == 0)
           const float x = dt * a[i];
           const float series = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
-          const float closed = fmaf(x, ab[i], 1.f - ab[i]) * __builtin_amdgcn_rcpf(x * x);
-          const float dcda = first ? 0.f : dt2 * (fabsf(x) < 0.1f ? series : closed);
+          const float closed = fmaf(dt, ab[i], -cf[i]) * iA[i];
+          const float dcda = first ? 0.f : (fabsf(x) < 0.1f ? dt2 * series : closed);
           gA[i] = fmaf(lam, fmaf(dt * ab[i], hp[j][i], dcda * bu), gA[i]);
           pb[i] = lam * cf[i] * uu;
           pc[i] = dyp * hj[i];
@@ -408,16 +413,25 @@ void bwd_kernel(BwdParams p) {
           put(ddl_b + l * D, draw);
           if (dz_b != nullptr) put(dz_b + l * D, gz);
         }
-        // sums over the wavefront's channels; lanes of channel 0 write the wavefront's sum
+        // this lane's dB / dC terms; every fourth token the wavefront sums its channels
+        *reinterpret_cast<float4*>(&sRed[w][0][j & 3][c][4 * s]) = make_float4(pb[0], pb[1], pb[2], pb[3]);
+        *reinterpret_cast<float4*>(&sRed[w][1][j & 3][c][4 * s]) = make_float4(pc[0], pc[1], pc[2], pc[3]);
+      }
+      if (j % 4 == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        wave_sync();
+        // outputs (array, token j + jj, state n) of the group, SL / 2 per lane
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = wave_chan_sum<SL>(pb[i]);
-          pc[i] = wave_chan_sum<SL>(pc[i]);
+        for (int r = 0; r < SL / 2; ++r) {
+          const int o = lane + 64 * r;
+          const int arr = o / (4 * NP), jj = (o / NP) % 4, n = o % NP;
+          float acc = 0.f;
+#pragma unroll
+          for (int cc = 0; cc < CW; ++cc) acc += sRed[w][arr][jj][cc][n];
+          sBC[w][arr][j + jj][n] = acc;
         }
-        if (c == 0) {
-          *reinterpret_cast<float4*>(&sBC[w][0][j][4 * s]) = make_float4(pb[0], pb[1], pb[2], pb[3]);
-          *reinterpret_cast<float4*>(&sBC[w][1][j][4 * s]) = make_float4(pc[0], pc[1], pc[2], pc[3]);
-        }
+        wave_sync();
+        __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_sched_barrier(0);   // one token at a time: bounds the live registers
     }
