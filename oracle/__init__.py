@@ -14,6 +14,9 @@ Two independent statements of the method live here:
   of the TorchLean "Selective Mamba" page (``step``).  Options: an initial state, the
   first-order input coefficient Bbar = delta * B (Algenta, ``mamba_selective_scan_step``),
   and the step-size transform softplus(delta + per-channel bias) (TorchLean, ``step``).
+* ``ssd_fwd`` / ``ssd_quadratic`` -- the scalar-decay (Mamba-2) layer: as the recurrence above
+  with one decay per head, and in its pairwise masked form ("state-space models", section
+  "Mamba-2 and state-space duality").
 * ``bwd`` -- the gradients of that forward (its vector-Jacobian product) by the reverse-time
   recurrence over the cached states, as the rustytorch commit log describes its hand-written
   VJP of the selective scan.
@@ -210,6 +213,61 @@ def bwd(u, delta, A, B, C, Dskip=None, z=None, *, dy, dlast=None, h0=None, delta
     """Gradients of the forward pass from the default oracle library; see ``OracleLib.bwd``."""
     return _load().bwd(u, delta, A, B, C, Dskip, z, dy=dy, dlast=dlast, h0=h0, delta_bias=delta_bias, euler=euler,
                        delta_softplus=delta_softplus, time_invariant=time_invariant)
+
+
+def ssd_as_s6(x, delta, A_head, Dskip=None):
+    """The scalar-decay (Mamba-2 "SSD") layer as an S6 layer: Abar_t = a_t I within a head
+    ("state-space models", section "Mamba-2 and state-space duality") is the diagonal S6
+    transition with A[d, n] = A_head[h] for every state n and every channel d = h * P + p of
+    head h, and one step size per (token, head) shared by the head's P channels.  Returns the
+    S6 per-token operands (u [b, L, H*P], delta [b, L, H*P]); ssd_fwd builds A and runs fwd."""
+    x = np.asarray(x, np.float32)
+    b, L, H, P = x.shape
+    u = x.reshape(b, L, H * P)
+    dl = np.repeat(np.asarray(delta, np.float32), P, axis=2)
+    return u, dl
+
+
+def ssd_fwd(x, delta, A_head, B, C, Dskip=None, z=None, *, h0=None, euler=False, want_last=True, nthreads=None):
+    """The scalar-decay layer by the fp64 recurrence of ``fwd``: x, z [b, L, H, P]; delta
+    [b, L, H]; A_head [H]; B, C [b, L, N] (one group shared by every head); Dskip [H*P].
+    Returns (y [b, L, H, P], last_state [b, H, P, N] or None)."""
+    x = np.asarray(x, np.float32)
+    b, L, H, P = x.shape
+    N = np.asarray(B).shape[2]
+    u, dl = ssd_as_s6(x, delta, A_head)
+    A = np.repeat(np.asarray(A_head, np.float32), P)[:, None].repeat(N, axis=1)
+    zz = None if z is None else np.asarray(z, np.float32).reshape(b, L, H * P)
+    y, last = fwd(u, dl, A, B, C, Dskip, zz, h0=None if h0 is None else np.asarray(h0, np.float32).reshape(b, H * P, N),
+                  euler=euler, want_last=want_last, nthreads=nthreads)
+    return y.reshape(b, L, H, P), None if last is None else last.reshape(b, H, P, N)
+
+
+def ssd_quadratic(x, delta, A_head, B, C, euler=False):
+    """The same layer in its pairwise form Y = (L o Q K^T) V per head, in float64 (O(L^2)):
+    L[t, s] = prod_{k=s+1..t} a_k for s <= t (else 0), Q = C, K rows = Bbar_s = c_s B_s, V = x
+    ("state-space models", section "Mamba-2 and state-space duality": the unrolled sum and
+    its masked-attention form).  a_k = exp(delta_k A_h); c_s = (a_s - 1)/A_h (ZOH; delta_s
+    when A_h == 0) or delta_s (first order).  No feed-through, no gate."""
+    x = np.asarray(x, np.float64)
+    b, L, H, P = x.shape
+    dl = np.asarray(delta, np.float64)
+    A = np.asarray(A_head, np.float64)
+    B = np.asarray(B, np.float64)
+    C = np.asarray(C, np.float64)
+    y = np.zeros_like(x)
+    for bi in range(b):
+        QK = C[bi] @ B[bi].T                                    # [L, L]: C_t . B_s
+        for h in range(H):
+            logs = dl[bi, :, h] * A[h]                          # log a_k
+            cum = np.concatenate([[0.0], np.cumsum(logs)])      # cum[t+1] = sum_{k<=t} log a_k
+            Lmask = np.tril(np.exp(cum[1:, None] - cum[None, 1:]))   # prod_{k=s+1..t} a_k
+            if euler or A[h] == 0.0:
+                c = dl[bi, :, h]
+            else:
+                c = np.expm1(logs) / A[h]
+            y[bi, :, h, :] = (Lmask * QK * c[None, :]) @ x[bi, :, h, :]
+    return y
 
 
 def kernel_element(c: float, abar_power: float, bbar: float) -> float:
