@@ -276,6 +276,50 @@ int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias
  * floats, plus O(batch * dim * dstate). */
 size_t selective_scan_bwd_workspace_size(const selscan_dims* dims);
 
+/*
+ * The scalar-decay ("SSD", Mamba-2) layer: within each head the transition is a scalar,
+ * Abar_t = a_t I with a_t = exp(delta_t A_h), and
+ *     y_t = sum_{s<=t} (C_t . Bbar_s) (prod_{k=s+1..t} a_k) x_s  (+ Dskip x_t, then * SiLU(z_t)),
+ * i.e. Y = (L o C Bbar^T) X per head with the causal decay mask L ("state-space models",
+ * aarnphm.xyz, section "Mamba-2 and state-space duality").  Bbar_s = c_s B_s with
+ * c_s = (a_s - 1)/A_h (ZOH; delta_s where A_h == 0) or delta_s (SELSCAN_DISC_EULER).  It is
+ * the selective scan above with A[d][n] = A_h for every state and channel of head h and one
+ * step size per (token, head); it is computed as the page describes Mamba-2's algorithm:
+ * matrix products inside 64-token chunks (on the matrix cores), a state carried between them.
+ */
+typedef struct selscan_ssd_dims {
+  int32_t abi_version;     /* SELSCAN_ABI_VERSION */
+  int32_t discretization;  /* enum selscan_discretization */
+  int64_t batch;           /* >= 0 */
+  int64_t seqlen;          /* >= 0 */
+  int64_t nheads;          /* H >= 1 */
+  int64_t headdim;         /* P: 64 */
+  int64_t dstate;          /* N: 64 or 128 */
+} selscan_ssd_dims;
+
+/*
+ * selective_scan_ssd_fwd -- enqueue the scalar-decay layer.  Every tensor is contiguous,
+ * device memory on the current device; x, delta, B, C, z and y are bfloat16, the rest fp32:
+ *   x, z, y        : [batch][seqlen][nheads][headdim]   (z may be NULL: no gate)
+ *   delta          : [batch][seqlen][nheads]   step size per (token, head)
+ *   A              : [nheads]   (the head's continuous rate, normally negative)
+ *   B, C           : [batch][seqlen][dstate]   shared by every head
+ *   Dskip          : [nheads * headdim], or NULL
+ *   initial_state, last_state : [batch][nheads][headdim][dstate], or NULL (zero / not written)
+ *   workspace      : selective_scan_ssd_workspace_size(dims) bytes, 256-byte aligned, or NULL
+ *                    to take it stream-ordered on `stream`.
+ * headdim other than 64 or dstate other than 64 / 128 return SELSCAN_ERR_UNSUPPORTED.
+ * Other status codes as selective_scan_fwd.
+ */
+int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                           const float* Dskip, const void* z, void* y, const float* initial_state,
+                           float* last_state, const selscan_ssd_dims* dims, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of selective_scan_ssd_fwd (0 for an empty call or invalid dims): one fp32
+ * [dstate][headdim] state and one decay per (batch row, head, 64-token chunk). */
+size_t selective_scan_ssd_workspace_size(const selscan_ssd_dims* dims);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* selective_scan_strerror(int status);
 

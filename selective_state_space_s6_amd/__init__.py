@@ -77,6 +77,8 @@ _SIGNATURES = [
     ("selective_scan_step", ctypes.c_int, [_VP] * 10 + [ctypes.POINTER(SelscanDims), _VP]),
     ("selective_scan_bwd", ctypes.c_int, [_VP] * 20 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
     ("selective_scan_bwd_workspace_size", ctypes.c_size_t, [ctypes.POINTER(SelscanDims)]),
+    ("selective_scan_ssd_fwd", ctypes.c_int, [_VP] * 10 + [ctypes.c_void_p, _VP, ctypes.c_size_t, _VP]),
+    ("selective_scan_ssd_workspace_size", ctypes.c_size_t, [ctypes.c_void_p]),
     ("selective_scan_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("selective_scan_last_hip_error", ctypes.c_int, []),
     ("selective_scan_abi_version", ctypes.c_int, []),
@@ -417,5 +419,68 @@ def selective_scan_bwd(u, delta, A, B, C, Dskip=None, z=None, *, dy, dlast_state
     return g
 
 
-__all__ = ["selective_scan_fwd", "selective_scan_step", "selective_scan_bwd", "bwd_workspace_size", "make_dims", "dims_init", "workspace_size", "strerror", "last_hip_error",
+class SsdDims(ctypes.Structure):
+    """Mirror of ``selscan_ssd_dims`` in include/selscan.h."""
+    _fields_ = [("abi_version", ctypes.c_int32), ("discretization", ctypes.c_int32), ("batch", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64)]
+
+
+def ssd_dims(batch, seqlen, nheads, headdim, dstate, discretization="zoh") -> SsdDims:
+    d = SsdDims()
+    d.abi_version = SELSCAN_ABI_VERSION
+    d.discretization = DISCRETIZATIONS[discretization]
+    d.batch, d.seqlen, d.nheads, d.headdim, d.dstate = int(batch), int(seqlen), int(nheads), int(headdim), int(dstate)
+    return d
+
+
+def ssd_workspace_size(dims: SsdDims) -> int:
+    return int(lib().selective_scan_ssd_workspace_size(ctypes.byref(dims)))
+
+
+def selective_scan_ssd_fwd(x, delta, A, B, C, Dskip=None, z=None, y=None, *, initial_state=None,
+                           return_last_state: bool = False, discretization: str = "zoh", workspace=None, stream=None):
+    """The scalar-decay (Mamba-2) layer on the GPU (bf16 x, delta, B, C, z, y; fp32 A, Dskip,
+    states).  x, z: [batch, L, H, 64]; delta: [batch, L, H]; A: [H]; B, C: [batch, L, N] with
+    N = 64 or 128; Dskip: [H * 64]; initial_state: [batch, H, 64, N].  All contiguous.
+    Returns (y, last_state or None)."""
+    import torch
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, L, H, headdim]")
+    batch, L, H, P = (int(v) for v in x.shape)
+    N = int(B.shape[-1])
+    for name, t in (("x", x), ("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda):
+            raise TypeError("%s must be a contiguous bfloat16 GPU tensor" % name)
+    if tuple(delta.shape) != (batch, L, H) or tuple(B.shape) != (batch, L, N) or tuple(C.shape) != (batch, L, N):
+        raise ValueError("delta must be [batch, L, H]; B, C [batch, L, N]")
+    for name, t, shape in (("A", A, (H,)), ("Dskip", Dskip, (H * P,)), ("initial_state", initial_state, (batch, H, P, N))):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape or not t.is_cuda):
+            raise ValueError("%s must be a contiguous float32 %s GPU tensor" % (name, shape))
+    if y is None:
+        y = torch.empty_like(x)
+    last = torch.empty((batch, H, P, N), dtype=torch.float32, device=x.device) if return_last_state else None
+    dims = ssd_dims(batch, L, H, P, N, discretization)
+    torch_stream = stream if (stream is None or hasattr(stream, "cuda_stream")) else None
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    if workspace is None and (torch_stream is not None or stream == torch.cuda.current_stream(x.device).cuda_stream):
+        need = ssd_workspace_size(dims)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            if torch_stream is not None:
+                workspace.record_stream(torch_stream)
+    ws = (_ptr(workspace), int(workspace.numel() * workspace.element_size())) if workspace is not None else (None, 0)
+    st = lib().selective_scan_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(Dskip), _ptr(z), _ptr(y),
+                                      _ptr(initial_state), _ptr(last), ctypes.byref(dims), ws[0], ws[1],
+                                      ctypes.c_void_p(stream))
+    if st != SELSCAN_OK:
+        raise SelscanError(st, "selective_scan_ssd_fwd")
+    return y, last
+
+
+__all__ = ["selective_scan_fwd", "selective_scan_step", "selective_scan_bwd", "bwd_workspace_size",
+           "selective_scan_ssd_fwd", "ssd_dims", "ssd_workspace_size", "SsdDims", "make_dims", "dims_init", "workspace_size", "strerror", "last_hip_error",
            "abi_version", "lib", "SelscanDims", "SelscanError", "LIB_PATH"]

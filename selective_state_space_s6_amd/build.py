@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libselscan.so")
 SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "bwd_kernels.hip"),
-           os.path.join(CSRC, "selscan_api.cpp")]
+           os.path.join(CSRC, "ssd_kernels.hip"), os.path.join(CSRC, "selscan_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -129,3 +129,28 @@ hipError_t launch_sum_partials(const float* part, int64_t nparts, int64_t stride
                                hipStream_t stream);
 
 }  // namespace selscan
+
+namespace selscan {
+
+// The scalar-decay (Mamba-2) layer: bf16 x, delta, B, C, z, y; fp32 A [H], Dskip [H*P],
+// states.  Contiguous: x, z, y [batch][L][H][64]; delta [batch][L][H]; B, C [batch][L][N].
+struct SsdParams {
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;   // may be null
+  const void* z;        // may be null
+  void* y;
+  const float* h0;      // [batch][H][64][N], may be null
+  float* last_state;    // [batch][H][64][N], may be null
+  float* state;         // workspace [batch][H][n_chunks][N][64]: chunk states, then carries
+  float* decay;         // workspace [batch][H][n_chunks]: exp(A sum delta) of each chunk
+  int64_t batch, L, H, N;
+  int64_t n_chunks;     // ceil(L / 64)
+  int32_t euler;
+};
+hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);
+
+}  // namespace selscan

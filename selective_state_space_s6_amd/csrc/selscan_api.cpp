@@ -523,6 +523,78 @@ int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias
   return st;
 }
 
+static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chunks) {
+  if (!d) return SELSCAN_ERR_NULL;
+  if (d->abi_version != SELSCAN_ABI_VERSION) return SELSCAN_ERR_ABI;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1) return SELSCAN_ERR_DIMS;
+  if (d->headdim != 64 || (d->dstate != 64 && d->dstate != 128)) return SELSCAN_ERR_UNSUPPORTED;
+  if (d->discretization != SELSCAN_DISC_ZOH && d->discretization != SELSCAN_DISC_EULER) return SELSCAN_ERR_UNSUPPORTED;
+  const int64_t nc = (d->seqlen + 63) / 64;
+  if (d->batch * d->nheads * nc > (int64_t(1) << 31) - 1 || d->batch * d->nheads * d->dstate * 64 > (int64_t(1) << 36))
+    return SELSCAN_ERR_UNSUPPORTED;
+  const int64_t bhc = d->batch * d->nheads * nc;
+  *n_chunks = nc;
+  *ws_bytes = (d->batch * d->seqlen > 0)
+                  ? size_t(round_up(bhc * d->dstate * 64 * int64_t(sizeof(float)), 256) +
+                           round_up(bhc * int64_t(sizeof(float)), 256))
+                  : 0;
+  return SELSCAN_OK;
+}
+
+size_t selective_scan_ssd_workspace_size(const selscan_ssd_dims* dims) {
+  size_t ws = 0;
+  int64_t nc = 0;
+  return ssd_check(dims, &ws, &nc) == SELSCAN_OK ? ws : 0;
+}
+
+int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                           const float* Dskip, const void* z, void* y, const float* initial_state, float* last_state,
+                           const selscan_ssd_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  int64_t nc = 0;
+  int st = ssd_check(dims, &need, &nc);
+  if (st != SELSCAN_OK) return st;
+  const selscan_ssd_dims& d = *dims;
+  const bool no_tokens = d.batch * d.seqlen == 0;
+  if (!A || (!no_tokens && (!x || !delta || !B || !C || !y))) return SELSCAN_ERR_NULL;
+  for (const void* q : {x, delta, B, C, z, static_cast<const void*>(y)})
+    if (q && !aligned(q, 2)) return SELSCAN_ERR_ALIGN;
+  for (const float* f : {A, Dskip, initial_state, static_cast<const float*>(last_state)})
+    if (f && !aligned(f, 4)) return SELSCAN_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (d.batch == 0) return SELSCAN_OK;
+  if (d.seqlen == 0) {                         // no tokens: the initial state is handed back
+    if (last_state && last_state != initial_state) {
+      const int64_t n = d.batch * d.nheads * 64 * d.dstate;
+      e = initial_state ? selscan::launch_copy(last_state, initial_state, n, s) : selscan::launch_fill_zero(last_state, n, s);
+    }
+    return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+  }
+  void* ws = workspace;
+  if (ws != nullptr) {
+    if (workspace_bytes < need || !aligned(ws, 256)) return SELSCAN_ERR_WORKSPACE;
+  } else {
+    e = hipMallocAsync(&ws, need, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  selscan::SsdParams p{};
+  p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.Dskip = Dskip; p.z = z; p.y = y;
+  p.h0 = initial_state; p.last_state = last_state;
+  p.batch = d.batch; p.L = d.seqlen; p.H = d.nheads; p.N = d.dstate; p.n_chunks = nc;
+  p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
+  p.state = static_cast<float*>(ws);
+  p.decay = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                     round_up(d.batch * d.nheads * nc * d.dstate * 64 * int64_t(sizeof(float)), 256));
+  e = selscan::launch_ssd(p, s);
+  st = e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+  if (workspace == nullptr) {
+    const hipError_t f = hipFreeAsync(ws, s);
+    if (st == SELSCAN_OK && f != hipSuccess) st = hip_fail(f);
+  }
+  return st;
+}
+
 const char* selective_scan_strerror(int status) {
   switch (status) {
     case SELSCAN_OK: return "success";

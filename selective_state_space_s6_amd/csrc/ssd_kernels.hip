@@ -1,0 +1,260 @@
+// ssd_kernels.hip -- gfx950 kernels of the scalar-decay (Mamba-2, "SSD") selective scan.
+//
+// Within a head the transition is a scalar times the identity, Abar_t = a_t I with
+// a_t = exp(delta_t A_h) ("state-space models", section "Mamba-2 and state-space duality"),
+// so the layer is y_t = sum_{s<=t} (C_t . Bbar_s) (prod_{k=s+1..t} a_k) x_s, i.e.
+// Y = (L o Q K^T) V with L the causal decay mask, Q = C, K = Bbar, V = x.  As the page puts
+// Mamba-2's algorithm: matrix products inside chunks, a state carried between chunks.  With
+// cum_t = sum_{k<=t} delta_k A_h inside a 64-token chunk and c_s the input coefficient
+// (Bbar_s = c_s B_s: (a_s - 1)/A_h for ZOH, delta_s for the first-order form):
+//   chunk state   S = sum_s exp(cum_end - cum_s) c_s B_s x_s^T                   [N x P]
+//   carry         H_in(chunk c+1) = exp(cum_end) H_in(c) + S(c)                  [N x P]
+//   output        y_t = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) c_s x_s
+//                       + exp(cum_t) C_t H_in + Dskip x_t,   then * SiLU(z_t)
+// The three products (B^T diag(w) X, C B^T, masked (C B^T) X and C H) run on the matrix
+// cores: v_mfma_f32_16x16x32_bf16, bf16 operands staged in LDS, fp32 accumulation.
+//
+// MFMA 16x16x32 operand layout (64 lanes, lane l, q = l / 16, r = l % 16):
+//   A (16 x 32, row-major): lane l holds A[r][8q .. 8q+7];
+//   B (32 x 16):            lane l holds B[8q .. 8q+7][r];
+//   D (16 x 16):            lane l holds D[4q .. 4q+3][r].
+// Every operand is therefore staged so that the 8 values a lane needs are contiguous: A as
+// [row][k], B as [column][k].
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "scan_launch.h"
+
+namespace selscan {
+namespace {
+
+constexpr int kT = 64;          // tokens per chunk
+constexpr int kP = 64;          // head dimension
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __bf16 to_bf16(float v) { return __builtin_bit_cast(__bf16, bf16_rne(v)); }
+__device__ __forceinline__ float bf16_f(__bf16 v) { return __uint_as_float(uint32_t(__builtin_bit_cast(uint16_t, v)) << 16); }
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// the 8 contiguous bf16 a lane feeds to the matrix core, from an LDS row
+__device__ __forceinline__ bf16x8 frag(const __bf16* row_k) { return *reinterpret_cast<const bf16x8*>(row_k); }
+
+// Per chunk: log-decay prefix cum_t (inclusive) and input coefficient c_t of the 64 tokens
+// of head h, computed by wavefront 0 (one token per lane) into LDS; padded tokens past L
+// get delta = 0 (a = 1, c = 0: they change nothing).
+__device__ __forceinline__ void chunk_decay(const uint16_t* delta, int64_t b, int64_t l0, int64_t L, int64_t H,
+                                            int64_t h, float A, bool euler, float* s_cum, float* s_c) {
+  const int lane = threadIdx.x;
+  if (lane >= 64) return;
+  const int64_t l = l0 + lane;
+  const float dt = l < L ? __uint_as_float(uint32_t(delta[(b * L + l) * H + h]) << 16) : 0.f;
+  float x = dt * A;                                        // log a_t
+  // inclusive prefix sum over the 64 lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  s_cum[lane] = x;
+  const float a = __builtin_amdgcn_exp2f(dt * A * kLog2e);
+  s_c[lane] = (euler || A == 0.f) ? dt : (a - 1.f) / A;
+}
+
+// ---- kernel 1: chunk states S = B^T diag(w) X, w_s = exp(cum_end - cum_s) c_s.
+// One workgroup (4 wavefronts) per (b, h, chunk); wavefront w computes the N/4 x 64 block of
+// rows n in [w N/4, (w+1) N/4).
+template <int N>
+__global__ __launch_bounds__(256) void ssd_chunk_state_kernel(SsdParams p) {
+  constexpr int kRowK = kT + 8;                           // LDS row of 64 tokens (+8 pad)
+  __shared__ __align__(16) __bf16 sBT[N][kRowK];          // w_s B[s][n] as [n][s]
+  __shared__ __align__(16) __bf16 sXT[kP][kRowK];         // x[s][p] as [p][s]
+  __shared__ float s_cum[kT], s_c[kT];
+  const int64_t nch = p.n_chunks;
+  const int64_t item = blockIdx.x;
+  const int64_t chunk = item % nch, bh = item / nch, h = bh % p.H, b = bh / p.H;
+  const int64_t l0 = chunk * kT, L = p.L, H = p.H;
+  const float A = p.A[h];
+  chunk_decay(static_cast<const uint16_t*>(p.delta), b, l0, L, H, h, A, p.euler != 0, s_cum, s_c);
+  __syncthreads();
+  const float cum_end = s_cum[kT - 1];
+  const uint16_t* const Bg = static_cast<const uint16_t*>(p.B);
+  const uint16_t* const xg = static_cast<const uint16_t*>(p.x);
+  // stage: B rows (scaled by w_s) transposed, x rows of head h transposed
+  for (int i = threadIdx.x; i < kT * N; i += 256) {
+    const int s = i / N, n = i % N;
+    const int64_t l = l0 + s;
+    const float v = l < L ? __uint_as_float(uint32_t(Bg[(b * L + l) * N + n]) << 16) : 0.f;
+    const float w = __builtin_amdgcn_exp2f((cum_end - s_cum[s]) * kLog2e) * s_c[s];
+    sBT[n][s] = to_bf16(v * w);
+  }
+  for (int i = threadIdx.x; i < kT * kP; i += 256) {
+    const int s = i / kP, pp = i % kP;
+    const int64_t l = l0 + s;
+    const uint16_t v = l < L ? xg[((b * L + l) * H + h) * kP + pp] : uint16_t(0);
+    sXT[pp][s] = __builtin_bit_cast(__bf16, v);
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+  constexpr int kRowTiles = N / 64;                        // 16-row tiles per wavefront
+  float* const S = p.state + (bh * nch + chunk) * N * kP;
+#pragma unroll
+  for (int ti = 0; ti < kRowTiles; ++ti) {
+    const int n0 = (w * kRowTiles + ti) * 16;
+#pragma unroll
+    for (int tj = 0; tj < kP / 16; ++tj) {
+      const int p0 = tj * 16;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < kT; k0 += 32)
+        acc = mfma(frag(&sBT[n0 + r][k0 + 8 * q]), frag(&sXT[p0 + r][k0 + 8 * q]), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[(n0 + 4 * q + i) * kP + p0 + r] = acc[i];
+    }
+  }
+  if (threadIdx.x == 0) p.decay[bh * nch + chunk] = __builtin_amdgcn_exp2f(cum_end * kLog2e);
+}
+
+// ---- kernel 2: carries across chunks, in place: state[c] <- state entering chunk c; the
+// state after the last chunk goes to last_state ([b][h][p][n]).  One thread per (b, h, n, p).
+__global__ __launch_bounds__(256) void ssd_state_scan_kernel(SsdParams p, int N) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t np = int64_t(N) * kP;
+  if (i >= p.batch * p.H * np) return;
+  const int64_t bh = i / np, e = i % np, n = e / kP, pp = e % kP;
+  const int64_t nch = p.n_chunks;
+  float run = p.h0 != nullptr ? p.h0[(bh * kP + pp) * N + n] : 0.f;
+  float* const S = p.state + bh * nch * np + e;
+  for (int64_t c = 0; c < nch; ++c) {
+    const float s = S[c * np];
+    S[c * np] = run;
+    run = fmaf(p.decay[bh * nch + c], run, s);
+  }
+  if (p.last_state != nullptr) p.last_state[(bh * kP + pp) * N + n] = run;
+}
+
+// ---- kernel 3: outputs.  One workgroup per (b, h, chunk); wavefront w computes the 16
+// output rows (tokens) [16 w, 16 w + 16) of all 64 head channels.
+template <int N>
+__global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdParams p) {
+  constexpr int kRowN = N + 8, kRowK = kT + 8;
+  static_assert(kRowN >= kRowK, "the mask tile reuses the rows of B");
+  __shared__ __align__(16) __bf16 sC[kT][kRowN];          // C[t][n]
+  __shared__ __align__(16) __bf16 sB[kT][kRowN];          // B[s][n]
+  __shared__ __align__(16) __bf16 sXT[kP][kRowK];         // x[s][p] as [p][s]
+  __shared__ __align__(16) __bf16 sHT[kP][kRowN];         // H_in[n][p] as [p][n]
+  // the masked, scaled C B^T replaces B in LDS once every C B^T tile is computed
+  __bf16* const sM = &sB[0][0];
+  __shared__ float s_cum[kT], s_c[kT];
+  const int64_t nch = p.n_chunks;
+  const int64_t item = blockIdx.x;
+  const int64_t chunk = item % nch, bh = item / nch, h = bh % p.H, b = bh / p.H;
+  const int64_t l0 = chunk * kT, L = p.L, H = p.H;
+  const float A = p.A[h];
+  chunk_decay(static_cast<const uint16_t*>(p.delta), b, l0, L, H, h, A, p.euler != 0, s_cum, s_c);
+  const uint16_t* const Bg = static_cast<const uint16_t*>(p.B);
+  const uint16_t* const Cg = static_cast<const uint16_t*>(p.C);
+  const uint16_t* const xg = static_cast<const uint16_t*>(p.x);
+  for (int i = threadIdx.x; i < kT * N; i += 256) {
+    const int t = i / N, n = i % N;
+    const int64_t l = l0 + t;
+    const bool ok = l < L;
+    sC[t][n] = __builtin_bit_cast(__bf16, ok ? Cg[(b * L + l) * N + n] : uint16_t(0));
+    sB[t][n] = __builtin_bit_cast(__bf16, ok ? Bg[(b * L + l) * N + n] : uint16_t(0));
+  }
+  for (int i = threadIdx.x; i < kT * kP; i += 256) {
+    const int s = i / kP, pp = i % kP;
+    const int64_t l = l0 + s;
+    sXT[pp][s] = __builtin_bit_cast(__bf16, l < L ? xg[((b * L + l) * H + h) * kP + pp] : uint16_t(0));
+  }
+  const float* const Hin = p.state + (bh * nch + chunk) * N * kP;
+  for (int i = threadIdx.x; i < N * kP; i += 256) {
+    const int n = i / kP, pp = i % kP;
+    sHT[pp][n] = to_bf16(Hin[i]);
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+  const int t0 = 16 * w;
+  // M = (C B^T) o L o c, rows t0 .. t0+15, all 64 columns s (zero above the diagonal)
+  f32x4 g[kT / 16];
+#pragma unroll
+  for (int tj = 0; tj < kT / 16; ++tj) {
+    const int s0 = 16 * tj;
+    g[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s0 <= t0) {
+#pragma unroll
+      for (int k0 = 0; k0 < N; k0 += 32) g[tj] = mfma(frag(&sC[t0 + r][k0 + 8 * q]), frag(&sB[s0 + r][k0 + 8 * q]), g[tj]);
+    }
+  }
+  __syncthreads();                                        // every wavefront is done with B
+#pragma unroll
+  for (int tj = 0; tj < kT / 16; ++tj) {
+    const int s = 16 * tj + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * q + i;
+      const float m = s <= t ? g[tj][i] * __builtin_amdgcn_exp2f((s_cum[t] - s_cum[s]) * kLog2e) * s_c[s] : 0.f;
+      sM[t * kRowN + s] = to_bf16(m);
+    }
+  }
+  __syncthreads();
+  // Y rows t0 .. t0+15: exp(cum_t) (C H_in) + M X, then feed-through and gate
+  const uint16_t* const zg = static_cast<const uint16_t*>(p.z);
+  uint16_t* const yg = static_cast<uint16_t*>(p.y);
+#pragma unroll
+  for (int tj = 0; tj < kP / 16; ++tj) {
+    const int p0 = 16 * tj;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < N; k0 += 32) acc = mfma(frag(&sC[t0 + r][k0 + 8 * q]), frag(&sHT[p0 + r][k0 + 8 * q]), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= __builtin_amdgcn_exp2f(s_cum[t0 + 4 * q + i] * kLog2e);
+#pragma unroll
+    for (int k0 = 0; k0 < kT; k0 += 32)
+      if (k0 <= t0 + 15) acc = mfma(frag(&sM[(t0 + r) * kRowN + k0 + 8 * q]), frag(&sXT[p0 + r][k0 + 8 * q]), acc);
+    const int pp = p0 + r;
+    const float dskip = p.Dskip != nullptr ? p.Dskip[h * kP + pp] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * q + i;
+      const int64_t l = l0 + t;
+      if (l >= L) continue;
+      const int64_t o = ((b * L + l) * H + h) * kP + pp;
+      float yv = fmaf(dskip, bf16_f(sXT[pp][t]), acc[i]);
+      if (zg != nullptr) {
+        const float zz = __uint_as_float(uint32_t(zg[o]) << 16);
+        yv *= zz * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+      }
+      yg[o] = bf16_rne(yv);
+    }
+  }
+}
+
+template <int N>
+hipError_t launch_ssd_n(const SsdParams& p, hipStream_t stream) {
+  const int64_t blocks = p.batch * p.H * p.n_chunks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(ssd_chunk_state_kernel<N>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t m = p.batch * p.H * int64_t(N) * kP;
+  hipLaunchKernelGGL(ssd_state_scan_kernel, dim3(unsigned((m + 255) / 256)), dim3(256), 0, stream, p, N);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ssd_chunk_out_kernel<N>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ssd(const SsdParams& p, hipStream_t stream) {
+  if (p.N == 64) return launch_ssd_n<64>(p, stream);
+  if (p.N == 128) return launch_ssd_n<128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace selscan

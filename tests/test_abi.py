@@ -214,3 +214,38 @@ def test_backward_errors():
     assert call_bwd(d, ws=FAKE, ws_bytes=need - 1) == ss.SELSCAN_ERR_WORKSPACE
     assert call_bwd(good_dims(abi_version=3), ws=FAKE, ws_bytes=need) == ss.SELSCAN_ERR_ABI
     assert ss.bwd_workspace_size(ss.dims_init(ss.SELSCAN_F32, 0, 64, 40, 16)) == 0
+
+
+def test_ssd_errors():
+    d = ss.ssd_dims(2, 200, 3, 64, 128)
+    need = ss.ssd_workspace_size(d)
+    assert need >= 4 * 2 * 3 * 4 * 128 * 64                 # one fp32 state per (b, h, chunk)
+    call = lambda dd, x=FAKE, ws=FAKE, nb=need: ss.lib().selective_scan_ssd_fwd(
+        x, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None, ctypes.byref(dd), ws, nb, None)
+    assert call(ss.ssd_dims(2, 200, 3, 32, 128)) == ss.SELSCAN_ERR_UNSUPPORTED     # head dimension
+    assert call(ss.ssd_dims(2, 200, 3, 64, 96)) == ss.SELSCAN_ERR_UNSUPPORTED      # state size
+    assert call(ss.ssd_dims(2, 200, 0, 64, 64)) == ss.SELSCAN_ERR_DIMS
+    assert call(d, x=None) == ss.SELSCAN_ERR_NULL
+    assert call(d, x=ctypes.c_void_p(0x100001)) == ss.SELSCAN_ERR_ALIGN
+    assert call(d, nb=need - 1) == ss.SELSCAN_ERR_WORKSPACE
+    bad = ss.ssd_dims(2, 200, 3, 64, 128)
+    bad.abi_version = 1
+    assert call(bad) == ss.SELSCAN_ERR_ABI
+    assert ss.ssd_workspace_size(ss.ssd_dims(0, 200, 3, 64, 128)) == 0
+
+
+def test_ssd_struct_layout_matches_header():
+    fields = [f for f, _ in ss.SsdDims._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"selscan.h\"\nint main(void){printf(\"%zu\\n\", sizeof(selscan_ssd_dims));\n"
+    for f in fields:
+        src += 'printf("%%zu\\n", offsetof(selscan_ssd_dims, %s));\n' % f
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe])
+        vals = [int(v) for v in subprocess.check_output([exe]).split()]
+    assert vals[0] == ctypes.sizeof(ss.SsdDims)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(ss.SsdDims, f).offset == off, f

@@ -1,0 +1,77 @@
+"""GPU parity of the scalar-decay (Mamba-2) layer, selective_scan_ssd_fwd, against the oracle
+(the fp64 recurrence with one decay per head, itself pinned to the pairwise masked form of
+"state-space models", section "Mamba-2 and state-space duality").  Operands are bf16 and the
+chunk products run on bf16 matrix cores with fp32 accumulation, so the bar is the bf16 one:
+max|y - y_ref| / max|y_ref| <= 2e-2, and the same for the final state.  Cases: several 64-token
+chunks with a ragged last one, one chunk, a single token, both state sizes, both input
+coefficients, with and without gate and feed-through, and an initial state."""
+import numpy as np
+import pytest
+
+import oracle
+import s6_workloads
+from tests.gpu_common import TOL, log_errors, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def make(rng, b, L, H, N, gate=True, dskip=True):
+    bf = s6_workloads.bf16_round
+    x = bf(rng.standard_normal((b, L, H, 64)).astype(np.float32))
+    dl = bf(np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), (b, L, H))).astype(np.float32))
+    A = (-np.exp(rng.uniform(np.log(1.0), np.log(16.0), H))).astype(np.float32)
+    B = bf(rng.standard_normal((b, L, N)).astype(np.float32))
+    C = bf(rng.standard_normal((b, L, N)).astype(np.float32))
+    Ds = rng.standard_normal(H * 64).astype(np.float32) if dskip else None
+    z = bf(rng.standard_normal((b, L, H, 64)).astype(np.float32)) if gate else None
+    return x, dl, A, B, C, Ds, z
+
+
+def run(inp, h0=None, euler=False):
+    import selective_state_space_s6_amd as ss
+    t = torch()
+    x, dl, A, B, C, Ds, z = inp
+    g = lambda a: None if a is None else t.from_numpy(a).cuda().to(t.bfloat16)
+    y, last = ss.selective_scan_ssd_fwd(g(x), g(dl), t.from_numpy(A).cuda(), g(B), g(C),
+                                        None if Ds is None else t.from_numpy(Ds).cuda(), g(z),
+                                        initial_state=None if h0 is None else t.from_numpy(h0).cuda(),
+                                        return_last_state=True, discretization="euler" if euler else "zoh")
+    t.cuda.synchronize()
+    y_ref, l_ref = oracle.ssd_fwd(x, dl, A, B, C, Ds, z, h0=h0, euler=euler)
+    return rel_err(y.float().cpu().numpy(), y_ref), rel_err(last.cpu().numpy(), l_ref)
+
+
+@pytest.mark.parametrize("euler", [False, True])
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("L", [1, 64, 200])
+def test_ssd_parity(L, N, euler):
+    rng = np.random.default_rng(L + N + euler)
+    e_y, e_l = run(make(rng, 2, L, 3, N), euler=euler)
+    log_errors("ssd/L=%d N=%d euler=%s" % (L, N, euler), y=e_y, last_state=e_l, io="bf16")
+    assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
+
+
+def test_ssd_without_gate_or_feedthrough():
+    rng = np.random.default_rng(7)
+    e_y, e_l = run(make(rng, 1, 150, 2, 64, gate=False, dskip=False))
+    assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
+
+
+def test_ssd_initial_state():
+    rng = np.random.default_rng(8)
+    inp = make(rng, 2, 130, 2, 128)
+    h0 = rng.standard_normal((2, 2, 64, 128)).astype(np.float32)
+    e_y, e_l = run(inp, h0=h0)
+    assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
+
+
+def test_ssd_many_heads_long():
+    """A longer sequence (33 chunks) over 8 heads: the carried state crosses many chunks."""
+    rng = np.random.default_rng(9)
+    e_y, e_l = run(make(rng, 1, 2100, 8, 128))
+    assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
