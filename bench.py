@@ -183,7 +183,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="longctx_bf16", choices=sorted(s6_workloads.WORKLOADS))
+    ap.add_argument("--workload", default="longctx_bf16",
+                    choices=sorted(s6_workloads.WORKLOADS) + sorted(s6_workloads.SSD_WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "single", "chunked"])
     ap.add_argument("--step-size", default="given", choices=["given", "softplus"],
                     help="softplus: the kernel computes softplus(raw + bias) from a pre-activation")
@@ -204,6 +205,8 @@ def main():
     import torch
     import selective_state_space_s6_amd as ss
 
+    if args.workload in s6_workloads.SSD_WORKLOADS:
+        return bench_ssd(args)
     spec = s6_workloads.spec(args.workload)
     inp = s6_workloads.generate(args.workload)
     softplus = args.step_size == "softplus"
@@ -412,6 +415,121 @@ def cpu_baseline_backward(inp, bias, softplus, euler, target_s: float = 10.0):
     return {"value": L * nch * N / t_used, "unit": "elements/s", "cores": 1, "kind": "oracle",
             "sample": "batch row 0, %d of %d channels x %d tokens x %d states, fp64 backward, %.1f s wall"
                       % (nch, D, L, N, t_used)}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X published dense bf16 matrix peak
+SSD_CHUNK = 64
+
+
+def ssd_flops(b, L, H, N, P=64, T=SSD_CHUNK) -> float:
+    """Algorithmic matrix work of the chunked scalar-decay layer: per (batch row, head, chunk)
+    the causal halves of C B^T (T(T+1)/2 x N) and of (mask o C B^T) X (T(T+1)/2 x P), the chunk
+    state B^T diag(w) X (N x P x T) and the carried-state readout C H (T x N x P); 2 flops per
+    multiply-add."""
+    nch = (L + T - 1) // T
+    per = T * (T + 1) / 2 * N * 2 + T * (T + 1) / 2 * P * 2 + N * P * T * 2 + T * N * P * 2
+    return b * H * nch * per
+
+
+def ssd_bytes(b, L, H, N, P=64) -> int:
+    """Bytes the layer must move: x, z read and y written (bf16) per (b, l, h, p); delta per
+    (b, l, h); B, C per (b, l, n); A, Dskip once."""
+    return 3 * b * L * H * P * 2 + b * L * H * 2 + 2 * b * L * N * 2 + H * 4 + H * P * 4
+
+
+def bench_ssd(args):
+    """The scalar-decay (Mamba-2) layer, selective_scan_ssd_fwd, over the whole workload."""
+    import torch
+    import selective_state_space_s6_amd as ss
+    inp = s6_workloads.generate_ssd(args.workload)
+    b, L, H, P = inp.x.shape
+    N = inp.B.shape[2]
+    g = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    x, dl, B, C, z = g(inp.x), g(inp.delta), g(inp.B), g(inp.C), g(inp.z)
+    A = torch.from_numpy(inp.A).cuda()
+    Ds = torch.from_numpy(inp.Dskip).cuda()
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ss.selective_scan_ssd_fwd(x, dl, A, B, C, Ds, z, y=y, discretization=args.discretization, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+    E = b * L * H * P * N
+    alg = ssd_bytes(b, L, H, N, P)
+    fl = ssd_flops(b, L, H, N, P)
+    sec = launch_ms * 1e-3
+    t_hbm, t_mfma = alg / (HBM_PEAK_GBS * 1e9), fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(fl / sec / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fl / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(args.workload, alg)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(alg / sec / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, alg)}
+    out = {
+        "metric": METRIC,
+        "value": E * args.steps / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, s6_workloads: %s)" % args.workload,
+        "config": {"workload": args.workload, "batch": b, "seq_len": L, "heads": H, "headdim": P, "dstate": N,
+                   "io": "bf16", "state": "f32", "gate": True, "feedthrough": True, "chunk": SSD_CHUNK,
+                   "discretization": args.discretization, "layer": "scalar decay per head (Mamba-2 SSD)"},
+        "kernel_ms": launch_ms,
+        "hbm_gbs": round(alg / sec / 1e9, 1),
+        "hbm_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_tflops": round(fl / sec / 1e12, 2),
+        "algorithmic_bytes": alg,
+        "algorithmic_flops": fl,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_ssd(inp)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_ssd(inp, target_s: float = 10.0):
+    """The oracle's recurrence with one decay per head (fp64, as it stands), on the first batch
+    row and a growing number of heads, timed on this host; scaled to elements/s."""
+    import oracle
+    oracle.build()
+    b, L, H, P = inp.x.shape
+    N = inp.B.shape[2]
+    cores = min(16, os.cpu_count() or 1)
+    nh = 1
+    while True:
+        t0 = time.perf_counter()
+        oracle.ssd_fwd(inp.x[:1, :, :nh], inp.delta[:1, :, :nh], inp.A[:nh], inp.B[:1], inp.C[:1],
+                       inp.Dskip[:nh * P], inp.z[:1, :, :nh], want_last=False, nthreads=cores)
+        t_used = time.perf_counter() - t0
+        if t_used >= target_s * 0.5 or nh >= H:
+            break
+        nh = min(H, int(nh * max(2.0, target_s / max(t_used, 1e-3))))
+    return {"value": L * nh * P * N / t_used, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "sample": "batch row 0, %d of %d heads x %d tokens x %d channels x %d states, fp64, %.1f s wall"
+                      % (nh, H, L, P, N, t_used)}
 
 
 def copy_calibration():

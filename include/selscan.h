@@ -308,6 +308,7 @@ typedef struct selscan_ssd_dims {
  *   initial_state, last_state : [batch][nheads][headdim][dstate], or NULL (zero / not written)
  *   workspace      : selective_scan_ssd_workspace_size(dims) bytes, 256-byte aligned, or NULL
  *                    to take it stream-ordered on `stream`.
+ * x, B, C, z and y must be 16-byte aligned (else SELSCAN_ERR_ALIGN); delta 2-byte aligned.
  * headdim other than 64 or dstate other than 64 / 128 return SELSCAN_ERR_UNSUPPORTED.
  * Other status codes as selective_scan_fwd.
  */
@@ -316,8 +317,9 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
                            float* last_state, const selscan_ssd_dims* dims, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of selective_scan_ssd_fwd (0 for an empty call or invalid dims): one fp32
- * [dstate][headdim] state and one decay per (batch row, head, 64-token chunk). */
+/* Workspace bytes of selective_scan_ssd_fwd (0 for an empty call or invalid dims): per
+ * (batch row, head, 64-token chunk) one fp32 [dstate][headdim] chunk state, one decay, and
+ * one bf16 carried-in state. */
 size_t selective_scan_ssd_workspace_size(const selscan_ssd_dims* dims);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

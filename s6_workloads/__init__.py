@@ -39,6 +39,13 @@ WORKLOADS = {
                         a_scale=1.0, delta="softplus_normal", decode=True),
 }
 
+# Scalar-decay (Mamba-2) layers: x [batch, L, H, 64], delta [batch, L, H], B, C [batch, L, N].
+# Widths of the Mamba-2 130M (24 heads) and 2.7B (80 heads) layers, 64-wide heads, 128 states.
+SSD_WORKLOADS = {
+    "ssd_mamba2_130m_bf16": dict(number=7, batch=8, L=2048, H=24, N=128),
+    "ssd_mamba2_2p7b_bf16": dict(number=8, batch=4, L=8192, H=80, N=128),
+}
+
 VARIANTS = ("default", "scan_only", "active", "active_const")
 
 
@@ -144,6 +151,37 @@ def generate(name: str, variant: str = "default", *, seed: Optional[int] = None,
         Dskip, z = None, None
     return Inputs(name=name, io=s["io"], ti=ti, u=u, delta=delta, A=A, B=B, C=C, Dskip=Dskip, z=z,
                   want_last=s["last"])
+
+
+@dataclasses.dataclass
+class SsdInputs:
+    """One scalar-decay workload (float32 arrays holding bf16-exact values; A, Dskip fp32)."""
+    name: str
+    x: np.ndarray        # [batch, L, H, 64]
+    delta: np.ndarray    # [batch, L, H]
+    A: np.ndarray        # [H]
+    B: np.ndarray        # [batch, L, N]
+    C: np.ndarray        # [batch, L, N]
+    Dskip: np.ndarray    # [H * 64]
+    z: np.ndarray        # [batch, L, H, 64]
+
+
+def generate_ssd(name: str, *, seed: Optional[int] = None) -> SsdInputs:
+    """Draw a scalar-decay workload: x, B, C, z standard normal; delta log-uniform in
+    [1e-3, 1e-1] (the canonical time-step range); A_h = -exp(U(0, ln 16)) per head (Mamba-2
+    draws its per-head rate from a range of that kind); Dskip = 1.  Draw order x, delta, A, B, C, z;
+    bf16 rounding (nearest even) for x, delta, B, C, z."""
+    s = SSD_WORKLOADS[name]
+    rng = np.random.Generator(np.random.PCG64(1000 + s["number"] if seed is None else seed))
+    b, L, H, N = s["batch"], s["L"], s["H"], s["N"]
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    x = bf16_round(f32(rng.standard_normal((b, L, H, 64))))
+    delta = bf16_round(f32(np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), (b, L, H)))))
+    A = f32(-np.exp(rng.uniform(0.0, np.log(16.0), H)))
+    B = bf16_round(f32(rng.standard_normal((b, L, N))))
+    C = bf16_round(f32(rng.standard_normal((b, L, N))))
+    z = bf16_round(f32(rng.standard_normal((b, L, H, 64))))
+    return SsdInputs(name=name, x=x, delta=delta, A=A, B=B, C=C, Dskip=np.ones(H * 64, np.float32), z=z)
 
 
 def running_state(inp: Inputs, seed: int = 11, scale: float = 0.1) -> np.ndarray:

@@ -145,7 +145,8 @@ struct SsdParams {
   void* y;
   const float* h0;      // [batch][H][64][N], may be null
   float* last_state;    // [batch][H][64][N], may be null
-  float* state;         // workspace [batch][H][n_chunks][N][64]: chunk states, then carries
+  float* state;         // workspace [batch][H][n_chunks][64][N]: chunk states (transposed)
+  uint16_t* carry;      // workspace [batch][H][n_chunks][64][N]: bf16 state entering each chunk
   float* decay;         // workspace [batch][H][n_chunks]: exp(A sum delta) of each chunk
   int64_t batch, L, H, N;
   int64_t n_chunks;     // ceil(L / 64)

@@ -536,7 +536,7 @@ static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chu
   *n_chunks = nc;
   *ws_bytes = (d->batch * d->seqlen > 0)
                   ? size_t(round_up(bhc * d->dstate * 64 * int64_t(sizeof(float)), 256) +
-                           round_up(bhc * int64_t(sizeof(float)), 256))
+                           round_up(bhc * int64_t(sizeof(float)), 256) + round_up(bhc * d->dstate * 64 * 2, 256))
                   : 0;
   return SELSCAN_OK;
 }
@@ -557,8 +557,9 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
   const selscan_ssd_dims& d = *dims;
   const bool no_tokens = d.batch * d.seqlen == 0;
   if (!A || (!no_tokens && (!x || !delta || !B || !C || !y))) return SELSCAN_ERR_NULL;
-  for (const void* q : {x, delta, B, C, z, static_cast<const void*>(y)})
-    if (q && !aligned(q, 2)) return SELSCAN_ERR_ALIGN;
+  if (delta && !aligned(delta, 2)) return SELSCAN_ERR_ALIGN;
+  for (const void* q : {x, B, C, z, static_cast<const void*>(y)})     // moved 16 bytes at a time
+    if (q && !aligned(q, 16)) return SELSCAN_ERR_ALIGN;
   for (const float* f : {A, Dskip, initial_state, static_cast<const float*>(last_state)})
     if (f && !aligned(f, 4)) return SELSCAN_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -584,8 +585,11 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
   p.batch = d.batch; p.L = d.seqlen; p.H = d.nheads; p.N = d.dstate; p.n_chunks = nc;
   p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
   p.state = static_cast<float*>(ws);
-  p.decay = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                     round_up(d.batch * d.nheads * nc * d.dstate * 64 * int64_t(sizeof(float)), 256));
+  const int64_t bhc = d.batch * d.nheads * nc;
+  char* const wsc = static_cast<char*>(ws);
+  p.decay = reinterpret_cast<float*>(wsc + round_up(bhc * d.dstate * 64 * int64_t(sizeof(float)), 256));
+  p.carry = reinterpret_cast<uint16_t*>(wsc + round_up(bhc * d.dstate * 64 * int64_t(sizeof(float)), 256) +
+                                        round_up(bhc * int64_t(sizeof(float)), 256));
   e = selscan::launch_ssd(p, s);
   st = e == hipSuccess ? SELSCAN_OK : hip_fail(e);
   if (workspace == nullptr) {

@@ -44,6 +44,15 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
 // the 8 contiguous bf16 a lane feeds to the matrix core, from an LDS row
 __device__ __forceinline__ bf16x8 frag(const __bf16* row_k) { return *reinterpret_cast<const bf16x8*>(row_k); }
 
+// 8 consecutive bf16 (16 bytes) of a row, or zeros past the sequence end
+__device__ __forceinline__ uint4 ld8(const uint16_t* row, bool ok) {
+  return ok ? *reinterpret_cast<const uint4*>(row) : make_uint4(0u, 0u, 0u, 0u);
+}
+__device__ __forceinline__ __bf16 bf16_at(const uint4& v, int i) {
+  const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
+  return __builtin_bit_cast(__bf16, uint16_t((i & 1) ? (w >> 16) : (w & 0xffffu)));
+}
+
 // Per chunk: log-decay prefix cum_t (inclusive) and input coefficient c_t of the 64 tokens
 // of head h, computed by wavefront 0 (one token per lane) into LDS; padded tokens past L
 // get delta = 0 (a = 1, c = 0: they change nothing).
@@ -65,7 +74,8 @@ __device__ __forceinline__ void chunk_decay(const uint16_t* delta, int64_t b, in
   s_c[lane] = (euler || A == 0.f) ? dt : (a - 1.f) / A;
 }
 
-// ---- kernel 1: chunk states S = B^T diag(w) X, w_s = exp(cum_end - cum_s) c_s.
+// ---- kernel 1: chunk states S = B^T diag(w) X, w_s = exp(cum_end - cum_s) c_s, stored as
+// [p][n] (S^T).
 // One workgroup (4 wavefronts) per (b, h, chunk); wavefront w computes the N/4 x 64 block of
 // rows n in [w N/4, (w+1) N/4).
 template <int N>
@@ -84,19 +94,21 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(SsdParams p) {
   const float cum_end = s_cum[kT - 1];
   const uint16_t* const Bg = static_cast<const uint16_t*>(p.B);
   const uint16_t* const xg = static_cast<const uint16_t*>(p.x);
-  // stage: B rows (scaled by w_s) transposed, x rows of head h transposed
-  for (int i = threadIdx.x; i < kT * N; i += 256) {
-    const int s = i / N, n = i % N;
+  // stage (16-byte loads): B rows scaled by w_s, transposed; x rows of head h, transposed
+  for (int i = threadIdx.x; i < kT * N / 8; i += 256) {
+    const int s = i / (N / 8), n0 = (i % (N / 8)) * 8;
     const int64_t l = l0 + s;
-    const float v = l < L ? __uint_as_float(uint32_t(Bg[(b * L + l) * N + n]) << 16) : 0.f;
+    const uint4 v = ld8(Bg + (b * L + l) * N + n0, l < L);
     const float w = __builtin_amdgcn_exp2f((cum_end - s_cum[s]) * kLog2e) * s_c[s];
-    sBT[n][s] = to_bf16(v * w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sBT[n0 + e][s] = to_bf16(bf16_f(bf16_at(v, e)) * w);
   }
-  for (int i = threadIdx.x; i < kT * kP; i += 256) {
-    const int s = i / kP, pp = i % kP;
+  for (int i = threadIdx.x; i < kT * kP / 8; i += 256) {
+    const int s = i / (kP / 8), p0 = (i % (kP / 8)) * 8;
     const int64_t l = l0 + s;
-    const uint16_t v = l < L ? xg[((b * L + l) * H + h) * kP + pp] : uint16_t(0);
-    sXT[pp][s] = __builtin_bit_cast(__bf16, v);
+    const uint4 v = ld8(xg + ((b * L + l) * H + h) * kP + p0, l < L);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sXT[p0 + e][s] = bf16_at(v, e);
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
@@ -112,26 +124,29 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(SsdParams p) {
 #pragma unroll
       for (int k0 = 0; k0 < kT; k0 += 32)
         acc = mfma(frag(&sBT[n0 + r][k0 + 8 * q]), frag(&sXT[p0 + r][k0 + 8 * q]), acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[(n0 + 4 * q + i) * kP + p0 + r] = acc[i];
+      // stored transposed, [p][n]: the lane's four rows n are consecutive there
+      *reinterpret_cast<f32x4*>(&S[(p0 + r) * N + n0 + 4 * q]) = acc;
     }
   }
   if (threadIdx.x == 0) p.decay[bh * nch + chunk] = __builtin_amdgcn_exp2f(cum_end * kLog2e);
 }
 
-// ---- kernel 2: carries across chunks, in place: state[c] <- state entering chunk c; the
-// state after the last chunk goes to last_state ([b][h][p][n]).  One thread per (b, h, n, p).
+// ---- kernel 2: carries across chunks: carry[c] <- state entering chunk c, in bf16 (the
+// precision the output kernel's matrix product takes it in), transposed to [p][n]; the sum
+// runs in fp32 and the state after the last chunk goes to last_state ([b][h][p][n]).  One
+// thread per (b, h, n, p).
 __global__ __launch_bounds__(256) void ssd_state_scan_kernel(SsdParams p, int N) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t np = int64_t(N) * kP;
   if (i >= p.batch * p.H * np) return;
-  const int64_t bh = i / np, e = i % np, n = e / kP, pp = e % kP;
+  const int64_t bh = i / np, e = i % np, pp = e / N, n = e % N;     // [p][n] order
   const int64_t nch = p.n_chunks;
   float run = p.h0 != nullptr ? p.h0[(bh * kP + pp) * N + n] : 0.f;
-  float* const S = p.state + bh * nch * np + e;
+  const float* const S = p.state + bh * nch * np + e;
+  uint16_t* const Hc = p.carry + bh * nch * np + e;
   for (int64_t c = 0; c < nch; ++c) {
     const float s = S[c * np];
-    S[c * np] = run;
+    Hc[c * np] = bf16_rne(run);
     run = fmaf(p.decay[bh * nch + c], run, s);
   }
   if (p.last_state != nullptr) p.last_state[(bh * kP + pp) * N + n] = run;
@@ -159,22 +174,25 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdParams p) {
   const uint16_t* const Bg = static_cast<const uint16_t*>(p.B);
   const uint16_t* const Cg = static_cast<const uint16_t*>(p.C);
   const uint16_t* const xg = static_cast<const uint16_t*>(p.x);
-  for (int i = threadIdx.x; i < kT * N; i += 256) {
-    const int t = i / N, n = i % N;
+  // stage (16-byte loads): C and B rows as they are, x rows of head h transposed, the
+  // carried-in state (already [p][n] bf16)
+  for (int i = threadIdx.x; i < kT * N / 8; i += 256) {
+    const int t = i / (N / 8), n0 = (i % (N / 8)) * 8;
     const int64_t l = l0 + t;
-    const bool ok = l < L;
-    sC[t][n] = __builtin_bit_cast(__bf16, ok ? Cg[(b * L + l) * N + n] : uint16_t(0));
-    sB[t][n] = __builtin_bit_cast(__bf16, ok ? Bg[(b * L + l) * N + n] : uint16_t(0));
+    *reinterpret_cast<uint4*>(&sC[t][n0]) = ld8(Cg + (b * L + l) * N + n0, l < L);
+    *reinterpret_cast<uint4*>(&sB[t][n0]) = ld8(Bg + (b * L + l) * N + n0, l < L);
   }
-  for (int i = threadIdx.x; i < kT * kP; i += 256) {
-    const int s = i / kP, pp = i % kP;
+  for (int i = threadIdx.x; i < kT * kP / 8; i += 256) {
+    const int s = i / (kP / 8), p0 = (i % (kP / 8)) * 8;
     const int64_t l = l0 + s;
-    sXT[pp][s] = __builtin_bit_cast(__bf16, l < L ? xg[((b * L + l) * H + h) * kP + pp] : uint16_t(0));
+    const uint4 v = ld8(xg + ((b * L + l) * H + h) * kP + p0, l < L);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sXT[p0 + e][s] = bf16_at(v, e);
   }
-  const float* const Hin = p.state + (bh * nch + chunk) * N * kP;
-  for (int i = threadIdx.x; i < N * kP; i += 256) {
-    const int n = i / kP, pp = i % kP;
-    sHT[pp][n] = to_bf16(Hin[i]);
+  const uint16_t* const Hin = p.carry + (bh * nch + chunk) * N * kP;    // [p][n], bf16
+  for (int i = threadIdx.x; i < N * kP / 8; i += 256) {
+    const int pp = i / (N / 8), n0 = (i % (N / 8)) * 8;
+    *reinterpret_cast<uint4*>(&sHT[pp][n0]) = *reinterpret_cast<const uint4*>(Hin + pp * N + n0);
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
@@ -202,9 +220,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdParams p) {
     }
   }
   __syncthreads();
-  // Y rows t0 .. t0+15: exp(cum_t) (C H_in) + M X, then feed-through and gate
-  const uint16_t* const zg = static_cast<const uint16_t*>(p.z);
-  uint16_t* const yg = static_cast<uint16_t*>(p.y);
+  // Y rows t0 .. t0+15: exp(cum_t) (C H_in) + M X
+  f32x4 yacc[kP / 16];
 #pragma unroll
   for (int tj = 0; tj < kP / 16; ++tj) {
     const int p0 = 16 * tj;
@@ -216,21 +233,46 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdParams p) {
 #pragma unroll
     for (int k0 = 0; k0 < kT; k0 += 32)
       if (k0 <= t0 + 15) acc = mfma(frag(&sM[(t0 + r) * kRowN + k0 + 8 * q]), frag(&sXT[p0 + r][k0 + 8 * q]), acc);
-    const int pp = p0 + r;
-    const float dskip = p.Dskip != nullptr ? p.Dskip[h * kP + pp] : 0.f;
+    yacc[tj] = acc;
+  }
+  // the tile goes through LDS (fp32, over C, which is no longer read) so that feed-through,
+  // gate and store move 8 consecutive channels per thread
+  __syncthreads();
+  constexpr int kRowY = kP + 4;
+  constexpr bool kInC = kT * kRowY * 4 <= kT * kRowN * 2;  // the tile fits in the rows of C
+  __shared__ __align__(16) float sYown[kInC ? 1 : kT * kRowY];
+  float* const sY = kInC ? reinterpret_cast<float*>(&sC[0][0]) : sYown;   // [64][kP + 4] floats
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * q + i;
-      const int64_t l = l0 + t;
-      if (l >= L) continue;
-      const int64_t o = ((b * L + l) * H + h) * kP + pp;
-      float yv = fmaf(dskip, bf16_f(sXT[pp][t]), acc[i]);
-      if (zg != nullptr) {
-        const float zz = __uint_as_float(uint32_t(zg[o]) << 16);
-        yv *= zz * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+  for (int tj = 0; tj < kP / 16; ++tj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sY[(t0 + 4 * q + i) * kRowY + 16 * tj + r] = yacc[tj][i];
+  __syncthreads();
+  const uint16_t* const zg = static_cast<const uint16_t*>(p.z);
+  uint16_t* const yg = static_cast<uint16_t*>(p.y);
+  for (int i = threadIdx.x; i < kT * kP / 8; i += 256) {
+    const int t = i / (kP / 8), p0 = (i % (kP / 8)) * 8;
+    const int64_t l = l0 + t;
+    if (l >= L) continue;
+    const int64_t o = ((b * L + l) * H + h) * kP + p0;
+    const uint4 zv = zg != nullptr ? *reinterpret_cast<const uint4*>(zg + o) : make_uint4(0u, 0u, 0u, 0u);
+    uint32_t packed[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float v2[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int pp = p0 + e + k;
+        float yv = sY[t * kRowY + pp];
+        if (p.Dskip != nullptr) yv = fmaf(p.Dskip[h * kP + pp], bf16_f(sXT[pp][t]), yv);
+        if (zg != nullptr) {
+          const float zz = bf16_f(bf16_at(zv, e + k));
+          yv *= zz * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+        }
+        v2[k] = yv;
       }
-      yg[o] = bf16_rne(yv);
+      packed[e / 2] = uint32_t(bf16_rne(v2[0])) | (uint32_t(bf16_rne(v2[1])) << 16);
     }
+    *reinterpret_cast<uint4*>(yg + o) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   }
 }
 

@@ -227,6 +227,7 @@ def test_ssd_errors():
     assert call(ss.ssd_dims(2, 200, 0, 64, 64)) == ss.SELSCAN_ERR_DIMS
     assert call(d, x=None) == ss.SELSCAN_ERR_NULL
     assert call(d, x=ctypes.c_void_p(0x100001)) == ss.SELSCAN_ERR_ALIGN
+    assert call(d, x=ctypes.c_void_p(0x100008)) == ss.SELSCAN_ERR_ALIGN             # 16 bytes needed
     assert call(d, nb=need - 1) == ss.SELSCAN_ERR_WORKSPACE
     bad = ss.ssd_dims(2, 200, 3, 64, 128)
     bad.abi_version = 1
