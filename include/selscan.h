@@ -295,6 +295,10 @@ typedef struct selscan_ssd_dims {
   int64_t nheads;          /* H >= 1 */
   int64_t headdim;         /* P: 64 */
   int64_t dstate;          /* N: 64 or 128 */
+  int32_t path;            /* 0 automatic; 1 one workgroup per (batch, head) walking the chunks
+                              with the state on chip (no workspace); 2 chunk-parallel (chunk
+                              states in the workspace, a scan over them, then the outputs) */
+  int32_t reserved;        /* 0 */
 } selscan_ssd_dims;
 
 /*
@@ -317,9 +321,10 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
                            float* last_state, const selscan_ssd_dims* dims, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* Workspace bytes of selective_scan_ssd_fwd (0 for an empty call or invalid dims): per
- * (batch row, head, 64-token chunk) one fp32 [dstate][headdim] chunk state, one decay, and
- * one bf16 carried-in state. */
+/* Workspace bytes of selective_scan_ssd_fwd (0 for an empty call, invalid dims or the
+ * on-chip path): for the chunk-parallel path, per (batch row, head, 64-token chunk) one fp32
+ * [dstate][headdim] chunk state, one decay, and one bf16 carried-in state.  The automatic
+ * path takes the on-chip one when batch * nheads >= 256 (a workgroup per compute unit). */
 size_t selective_scan_ssd_workspace_size(const selscan_ssd_dims* dims);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

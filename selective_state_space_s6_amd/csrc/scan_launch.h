@@ -151,6 +151,7 @@ struct SsdParams {
   int64_t batch, L, H, N;
   int64_t n_chunks;     // ceil(L / 64)
   int32_t euler;
+  int32_t fused;        // 1: one workgroup per (batch, head) keeps the state on chip (no workspace)
 };
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);
 

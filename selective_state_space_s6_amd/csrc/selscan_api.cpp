@@ -523,7 +523,9 @@ int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias
   return st;
 }
 
-static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chunks) {
+constexpr int64_t kSsdFusedMinItems = 256;   // (batch, head) workgroups for the on-chip path: one per CU
+
+static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chunks, bool* fused) {
   if (!d) return SELSCAN_ERR_NULL;
   if (d->abi_version != SELSCAN_ABI_VERSION) return SELSCAN_ERR_ABI;
   if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1) return SELSCAN_ERR_DIMS;
@@ -532,9 +534,11 @@ static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chu
   const int64_t nc = (d->seqlen + 63) / 64;
   if (d->batch * d->nheads * nc > (int64_t(1) << 31) - 1 || d->batch * d->nheads * d->dstate * 64 > (int64_t(1) << 36))
     return SELSCAN_ERR_UNSUPPORTED;
+  if (d->path < 0 || d->path > 2 || d->reserved != 0) return SELSCAN_ERR_UNSUPPORTED;
   const int64_t bhc = d->batch * d->nheads * nc;
   *n_chunks = nc;
-  *ws_bytes = (d->batch * d->seqlen > 0)
+  *fused = d->path == 1 || (d->path == 0 && d->batch * d->nheads >= kSsdFusedMinItems);
+  *ws_bytes = (d->batch * d->seqlen > 0 && !*fused)
                   ? size_t(round_up(bhc * d->dstate * 64 * int64_t(sizeof(float)), 256) +
                            round_up(bhc * int64_t(sizeof(float)), 256) + round_up(bhc * d->dstate * 64 * 2, 256))
                   : 0;
@@ -544,7 +548,8 @@ static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chu
 size_t selective_scan_ssd_workspace_size(const selscan_ssd_dims* dims) {
   size_t ws = 0;
   int64_t nc = 0;
-  return ssd_check(dims, &ws, &nc) == SELSCAN_OK ? ws : 0;
+  bool fused = false;
+  return ssd_check(dims, &ws, &nc, &fused) == SELSCAN_OK ? ws : 0;
 }
 
 int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
@@ -552,7 +557,8 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
                            const selscan_ssd_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
   size_t need = 0;
   int64_t nc = 0;
-  int st = ssd_check(dims, &need, &nc);
+  bool fused = false;
+  int st = ssd_check(dims, &need, &nc, &fused);
   if (st != SELSCAN_OK) return st;
   const selscan_ssd_dims& d = *dims;
   const bool no_tokens = d.batch * d.seqlen == 0;
@@ -573,9 +579,9 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
     return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
   }
   void* ws = workspace;
-  if (ws != nullptr) {
+  if (need > 0 && ws != nullptr) {
     if (workspace_bytes < need || !aligned(ws, 256)) return SELSCAN_ERR_WORKSPACE;
-  } else {
+  } else if (need > 0) {
     e = hipMallocAsync(&ws, need, s);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -584,15 +590,18 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
   p.h0 = initial_state; p.last_state = last_state;
   p.batch = d.batch; p.L = d.seqlen; p.H = d.nheads; p.N = d.dstate; p.n_chunks = nc;
   p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
-  p.state = static_cast<float*>(ws);
-  const int64_t bhc = d.batch * d.nheads * nc;
-  char* const wsc = static_cast<char*>(ws);
-  p.decay = reinterpret_cast<float*>(wsc + round_up(bhc * d.dstate * 64 * int64_t(sizeof(float)), 256));
-  p.carry = reinterpret_cast<uint16_t*>(wsc + round_up(bhc * d.dstate * 64 * int64_t(sizeof(float)), 256) +
-                                        round_up(bhc * int64_t(sizeof(float)), 256));
+  p.fused = fused ? 1 : 0;
+  if (!fused) {
+    p.state = static_cast<float*>(ws);
+    const int64_t bhc = d.batch * d.nheads * nc;
+    char* const wsc = static_cast<char*>(ws);
+    p.decay = reinterpret_cast<float*>(wsc + round_up(bhc * d.dstate * 64 * int64_t(sizeof(float)), 256));
+    p.carry = reinterpret_cast<uint16_t*>(wsc + round_up(bhc * d.dstate * 64 * int64_t(sizeof(float)), 256) +
+                                          round_up(bhc * int64_t(sizeof(float)), 256));
+  }
   e = selscan::launch_ssd(p, s);
   st = e == hipSuccess ? SELSCAN_OK : hip_fail(e);
-  if (workspace == nullptr) {
+  if (workspace == nullptr && need > 0) {
     const hipError_t f = hipFreeAsync(ws, s);
     if (st == SELSCAN_OK && f != hipSuccess) st = hip_fail(f);
   }

@@ -276,10 +276,191 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdParams p) {
   }
 }
 
+// ---- fused: one workgroup per (b, h) walks the chunks in order with the head's state
+// H [N x 64] held in the matrix cores' accumulator registers (wavefront w owns rows
+// [w N/4, (w+1) N/4)); no state touches memory.  Per chunk:
+//   stage C, B, w-scaled B^T, x^T, the decay prefix; copy H (bf16) to LDS for C H;
+//   M = (C B^T) o mask;  Y = e^cum (C H) + M X  (then feed-through, gate, store);
+//   H <- e^cum_end H + B^T diag(w) X  (accumulated onto the scaled registers).
+template <int N>
+__global__ __launch_bounds__(256) void ssd_fused_kernel(SsdParams p) {
+  constexpr int kRowN = N + 8, kRowK = kT + 8, kRowY = kP + 4;
+  constexpr int kRowTiles = N / 64;                        // 16-row state tiles per wavefront
+  __shared__ __align__(16) __bf16 sC[kT][kRowN];          // C[t][n]; later the fp32 output tile
+  __shared__ __align__(16) __bf16 sB[kT][kRowN];          // B[s][n]; later the mask tile M
+  __shared__ __align__(16) __bf16 sBT[N][kRowK];          // w_s B[s][n] as [n][s]
+  __shared__ __align__(16) __bf16 sXT[kP][kRowK];         // x[s][p] as [p][s]
+  __shared__ __align__(16) __bf16 sHT[kP][kRowN];         // H[n][p] as [p][n], bf16
+  __shared__ float s_cum[kT], s_c[kT];
+  constexpr bool kInC = kT * kRowY * 4 <= kT * kRowN * 2;
+  __shared__ __align__(16) float sYown[kInC ? 1 : kT * kRowY];
+  float* const sY = kInC ? reinterpret_cast<float*>(&sC[0][0]) : sYown;
+  __bf16* const sM = &sB[0][0];
+
+  const int64_t bh = blockIdx.x, h = bh % p.H, b = bh / p.H;
+  const int64_t L = p.L, H = p.H;
+  const float A = p.A[h];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
+  const uint16_t* const Bg = static_cast<const uint16_t*>(p.B);
+  const uint16_t* const Cg = static_cast<const uint16_t*>(p.C);
+  const uint16_t* const xg = static_cast<const uint16_t*>(p.x);
+  const uint16_t* const zg = static_cast<const uint16_t*>(p.z);
+  uint16_t* const yg = static_cast<uint16_t*>(p.y);
+
+  // the state: tile (ti, tj) of wavefront w covers rows n0 = (w kRowTiles + ti) 16 + 4q + i,
+  // columns 16 tj + r
+  f32x4 hs[kRowTiles][kP / 16];
+#pragma unroll
+  for (int ti = 0; ti < kRowTiles; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < kP / 16; ++tj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = (w * kRowTiles + ti) * 16 + 4 * q + i, pp = 16 * tj + r;
+        hs[ti][tj][i] = p.h0 != nullptr ? p.h0[(bh * kP + pp) * N + n] : 0.f;
+      }
+
+  for (int64_t chunk = 0; chunk < p.n_chunks; ++chunk) {
+    const int64_t l0 = chunk * kT;
+    __syncthreads();                                      // the previous chunk's LDS reads are done
+    chunk_decay(static_cast<const uint16_t*>(p.delta), b, l0, L, H, h, A, p.euler != 0, s_cum, s_c);
+    for (int i = threadIdx.x; i < kT * N / 8; i += 256) {
+      const int t = i / (N / 8), n0 = (i % (N / 8)) * 8;
+      const int64_t l = l0 + t;
+      *reinterpret_cast<uint4*>(&sC[t][n0]) = ld8(Cg + (b * L + l) * N + n0, l < L);
+      *reinterpret_cast<uint4*>(&sB[t][n0]) = ld8(Bg + (b * L + l) * N + n0, l < L);
+    }
+    for (int i = threadIdx.x; i < kT * kP / 8; i += 256) {
+      const int s = i / (kP / 8), p0 = (i % (kP / 8)) * 8;
+      const int64_t l = l0 + s;
+      const uint4 v = ld8(xg + ((b * L + l) * H + h) * kP + p0, l < L);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sXT[p0 + e][s] = bf16_at(v, e);
+    }
+    // H (the state entering this chunk) to LDS in bf16, for C H: a lane's four rows n are
+    // consecutive in the [p][n] layout, one 8-byte store
+#pragma unroll
+    for (int ti = 0; ti < kRowTiles; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < kP / 16; ++tj) {
+        const uint2 v = make_uint2(uint32_t(bf16_rne(hs[ti][tj][0])) | (uint32_t(bf16_rne(hs[ti][tj][1])) << 16),
+                                   uint32_t(bf16_rne(hs[ti][tj][2])) | (uint32_t(bf16_rne(hs[ti][tj][3])) << 16));
+        *reinterpret_cast<uint2*>(&sHT[16 * tj + r][(w * kRowTiles + ti) * 16 + 4 * q]) = v;
+      }
+    __syncthreads();                                      // C, B, x, H and the decay prefix are in
+    const float cum_end = s_cum[kT - 1];
+    // w-scaled B^T for the state update (needs the prefix)
+    for (int i = threadIdx.x; i < kT * N / 8; i += 256) {
+      const int s = i / (N / 8), n0 = (i % (N / 8)) * 8;
+      const float wgt = __builtin_amdgcn_exp2f((cum_end - s_cum[s]) * kLog2e) * s_c[s];
+      const uint4 v = *reinterpret_cast<const uint4*>(&sB[s][n0]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sBT[n0 + e][s] = to_bf16(bf16_f(bf16_at(v, e)) * wgt);
+    }
+    const int t0 = 16 * w;
+    f32x4 g[kT / 16];
+#pragma unroll
+    for (int tj = 0; tj < kT / 16; ++tj) {
+      const int s0 = 16 * tj;
+      g[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s0 <= t0) {
+#pragma unroll
+        for (int k0 = 0; k0 < N; k0 += 32) g[tj] = mfma(frag(&sC[t0 + r][k0 + 8 * q]), frag(&sB[s0 + r][k0 + 8 * q]), g[tj]);
+      }
+    }
+    __syncthreads();                                      // B and the w-scaled B^T are done
+#pragma unroll
+    for (int tj = 0; tj < kT / 16; ++tj) {
+      const int s = 16 * tj + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * q + i;
+        const float m = s <= t ? g[tj][i] * __builtin_amdgcn_exp2f((s_cum[t] - s_cum[s]) * kLog2e) * s_c[s] : 0.f;
+        sM[t * kRowN + s] = to_bf16(m);
+      }
+    }
+    // state update: H <- e^cum_end H + B^T diag(w) X (reads sBT and sXT only)
+    const float dec = __builtin_amdgcn_exp2f(cum_end * kLog2e);
+#pragma unroll
+    for (int ti = 0; ti < kRowTiles; ++ti) {
+      const int n0 = (w * kRowTiles + ti) * 16;
+#pragma unroll
+      for (int tj = 0; tj < kP / 16; ++tj) {
+        f32x4 acc = hs[ti][tj] * dec;
+#pragma unroll
+        for (int k0 = 0; k0 < kT; k0 += 32)
+          acc = mfma(frag(&sBT[n0 + r][k0 + 8 * q]), frag(&sXT[16 * tj + r][k0 + 8 * q]), acc);
+        hs[ti][tj] = acc;
+      }
+    }
+    __syncthreads();                                      // M is complete
+    f32x4 yacc[kP / 16];
+#pragma unroll
+    for (int tj = 0; tj < kP / 16; ++tj) {
+      const int p0 = 16 * tj;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < N; k0 += 32) acc = mfma(frag(&sC[t0 + r][k0 + 8 * q]), frag(&sHT[p0 + r][k0 + 8 * q]), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= __builtin_amdgcn_exp2f(s_cum[t0 + 4 * q + i] * kLog2e);
+#pragma unroll
+      for (int k0 = 0; k0 < kT; k0 += 32)
+        if (k0 <= t0 + 15) acc = mfma(frag(&sM[(t0 + r) * kRowN + k0 + 8 * q]), frag(&sXT[p0 + r][k0 + 8 * q]), acc);
+      yacc[tj] = acc;
+    }
+    __syncthreads();                                      // C is no longer read
+#pragma unroll
+    for (int tj = 0; tj < kP / 16; ++tj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sY[(t0 + 4 * q + i) * kRowY + 16 * tj + r] = yacc[tj][i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < kT * kP / 8; i += 256) {
+      const int t = i / (kP / 8), p0 = (i % (kP / 8)) * 8;
+      const int64_t l = l0 + t;
+      if (l >= L) continue;
+      const int64_t o = ((b * L + l) * H + h) * kP + p0;
+      const uint4 zv = zg != nullptr ? *reinterpret_cast<const uint4*>(zg + o) : make_uint4(0u, 0u, 0u, 0u);
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float v2[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int pp = p0 + e + k;
+          float yv = sY[t * kRowY + pp];
+          if (p.Dskip != nullptr) yv = fmaf(p.Dskip[h * kP + pp], bf16_f(sXT[pp][t]), yv);
+          if (zg != nullptr) {
+            const float zz = bf16_f(bf16_at(zv, e + k));
+            yv *= zz * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+          }
+          v2[k] = yv;
+        }
+        packed[e / 2] = uint32_t(bf16_rne(v2[0])) | (uint32_t(bf16_rne(v2[1])) << 16);
+      }
+      *reinterpret_cast<uint4*>(yg + o) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    }
+  }
+  if (p.last_state != nullptr) {
+#pragma unroll
+    for (int ti = 0; ti < kRowTiles; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < kP / 16; ++tj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = (w * kRowTiles + ti) * 16 + 4 * q + i, pp = 16 * tj + r;
+          p.last_state[(bh * kP + pp) * N + n] = hs[ti][tj][i];
+        }
+  }
+}
+
 template <int N>
 hipError_t launch_ssd_n(const SsdParams& p, hipStream_t stream) {
+  if (p.batch * p.H == 0) return hipSuccess;
+  if (p.fused) {
+    hipLaunchKernelGGL(ssd_fused_kernel<N>, dim3(unsigned(p.batch * p.H)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   const int64_t blocks = p.batch * p.H * p.n_chunks;
-  if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(ssd_chunk_state_kernel<N>, dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

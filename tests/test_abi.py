@@ -233,6 +233,13 @@ def test_ssd_errors():
     bad.abi_version = 1
     assert call(bad) == ss.SELSCAN_ERR_ABI
     assert ss.ssd_workspace_size(ss.ssd_dims(0, 200, 3, 64, 128)) == 0
+    assert ss.ssd_workspace_size(ss.ssd_dims(2, 200, 3, 64, 128, path="fused")) == 0     # state on chip
+    assert ss.ssd_workspace_size(ss.ssd_dims(4, 200, 80, 64, 128)) == 0                  # automatic: on chip
+    assert ss.ssd_workspace_size(ss.ssd_dims(8, 200, 24, 64, 128)) > 0                   # automatic: chunks
+    assert ss.ssd_workspace_size(ss.ssd_dims(2, 200, 3, 64, 128, path="chunked")) == need
+    bad_path = ss.ssd_dims(2, 200, 3, 64, 128)
+    bad_path.path = 3
+    assert call(bad_path) == ss.SELSCAN_ERR_UNSUPPORTED
 
 
 def test_ssd_struct_layout_matches_header():

@@ -32,7 +32,7 @@ def make(rng, b, L, H, N, gate=True, dskip=True):
     return x, dl, A, B, C, Ds, z
 
 
-def run(inp, h0=None, euler=False):
+def run(inp, h0=None, euler=False, path="auto"):
     import selective_state_space_s6_amd as ss
     t = torch()
     x, dl, A, B, C, Ds, z = inp
@@ -40,38 +40,43 @@ def run(inp, h0=None, euler=False):
     y, last = ss.selective_scan_ssd_fwd(g(x), g(dl), t.from_numpy(A).cuda(), g(B), g(C),
                                         None if Ds is None else t.from_numpy(Ds).cuda(), g(z),
                                         initial_state=None if h0 is None else t.from_numpy(h0).cuda(),
-                                        return_last_state=True, discretization="euler" if euler else "zoh")
+                                        return_last_state=True, discretization="euler" if euler else "zoh",
+                                        path=path)
     t.cuda.synchronize()
     y_ref, l_ref = oracle.ssd_fwd(x, dl, A, B, C, Ds, z, h0=h0, euler=euler)
     return rel_err(y.float().cpu().numpy(), y_ref), rel_err(last.cpu().numpy(), l_ref)
 
 
+@pytest.mark.parametrize("path", ["fused", "chunked"])
 @pytest.mark.parametrize("euler", [False, True])
 @pytest.mark.parametrize("N", [64, 128])
 @pytest.mark.parametrize("L", [1, 64, 200])
-def test_ssd_parity(L, N, euler):
+def test_ssd_parity(L, N, euler, path):
     rng = np.random.default_rng(L + N + euler)
-    e_y, e_l = run(make(rng, 2, L, 3, N), euler=euler)
-    log_errors("ssd/L=%d N=%d euler=%s" % (L, N, euler), y=e_y, last_state=e_l, io="bf16")
+    e_y, e_l = run(make(rng, 2, L, 3, N), euler=euler, path=path)
+    log_errors("ssd/%s L=%d N=%d euler=%s" % (path, L, N, euler), y=e_y, last_state=e_l, io="bf16")
     assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
 
 
-def test_ssd_without_gate_or_feedthrough():
+@pytest.mark.parametrize("path", ["fused", "chunked"])
+def test_ssd_without_gate_or_feedthrough(path):
     rng = np.random.default_rng(7)
-    e_y, e_l = run(make(rng, 1, 150, 2, 64, gate=False, dskip=False))
+    e_y, e_l = run(make(rng, 1, 150, 2, 64, gate=False, dskip=False), path=path)
     assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
 
 
-def test_ssd_initial_state():
+@pytest.mark.parametrize("path", ["fused", "chunked"])
+def test_ssd_initial_state(path):
     rng = np.random.default_rng(8)
     inp = make(rng, 2, 130, 2, 128)
     h0 = rng.standard_normal((2, 2, 64, 128)).astype(np.float32)
-    e_y, e_l = run(inp, h0=h0)
+    e_y, e_l = run(inp, h0=h0, path=path)
     assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
 
 
-def test_ssd_many_heads_long():
+@pytest.mark.parametrize("path", ["auto", "fused", "chunked"])
+def test_ssd_many_heads_long(path):
     """A longer sequence (33 chunks) over 8 heads: the carried state crosses many chunks."""
     rng = np.random.default_rng(9)
-    e_y, e_l = run(make(rng, 1, 2100, 8, 128))
+    e_y, e_l = run(make(rng, 1, 2100, 8, 128), path=path)
     assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
