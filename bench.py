@@ -42,6 +42,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X published HBM3E bandwidth
 VALU_PEAK_TFLOPS = 157.3         # MI355X published fp32 vector peak (FMA = 2 flops)
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
                   for f in ("scan_kernels.hip", "device_common.h")]
+SSD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
+                      for f in ("ssd_kernels.hip", "device_common.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "scan_counters.json")
 
 # Algorithmic ALU work, in FMA-slot units (one fp32 VALU op = 1 slot = 2 flop-equivalents;
@@ -125,11 +127,12 @@ def algorithmic_slots(inp: s6_workloads.Inputs, softplus: bool = False, euler: b
     return slots
 
 
-def kernel_source_hash() -> str:
-    """Hash of the forward kernels' sources (the counters in the committed summary are valid
-    only for the source they were taken on)."""
+def kernel_source_hash(workload: str = "") -> str:
+    """Hash of the sources of the kernels a workload runs (the scan kernels, or for the
+    scalar-decay workloads its kernels): the counters in the committed summary are valid only
+    for the source they were taken on."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in (SSD_KERNEL_SOURCES if workload.startswith("ssd_") else KERNEL_SOURCES):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -144,7 +147,7 @@ def measured_traffic(workload: str, per_launch_alg_bytes: int):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return int(entry["hbm_bytes_per_launch"])
 
@@ -469,6 +472,8 @@ def bench_ssd(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+    if args.copy_calibration:
+        copy_calibration()
     E = b * L * H * P * N
     alg = ssd_bytes(b, L, H, N, P)
     fl = ssd_flops(b, L, H, N, P)

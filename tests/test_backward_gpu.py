@@ -141,3 +141,37 @@ def test_backward_sequence_chunks_options_bf16():
     inp = s6_workloads.generate("longctx_bf16", batch=1, L=900, D=40)
     raw, bias = s6_workloads.raw_step_sizes(inp)
     check(run_case(inp, delta=raw, bias=bias, softplus=True, euler=True), "bf16", "chunks bf16 options")
+
+
+def test_backward_full_size_sampled_channels():
+    """The benchmark's backward (mamba130m_f32 at full size, automatic chunking): the
+    per-channel gradients (du, ddelta, dz, dA, dDskip) against the oracle on sampled channels;
+    dB and dC, sums over every channel, by additivity: the full call's dB equals the sum of
+    the calls on the two halves of the channels."""
+    import selective_state_space_s6_amd as ss
+    t = torch()
+    inp = s6_workloads.generate("mamba130m_f32")
+    b, L, D, N = inp.shape
+    dy = np.random.default_rng(4).standard_normal((b, L, D)).astype(np.float32)
+
+    def gpu(sub, dys):
+        return ss.selective_scan_bwd(dev(sub.u, "f32"), dev(sub.delta, "f32"), t.from_numpy(sub.A).cuda(),
+                                     dev(sub.B, "f32"), dev(sub.C, "f32"), t.from_numpy(sub.Dskip).cuda(),
+                                     dev(sub.z, "f32"), dy=dev(dys, "f32"))
+
+    g = gpu(inp, dy)
+    ch = s6_workloads.sample_channels(D, 16)
+    sub = s6_workloads.select_channels(inp, ch)
+    ref = oracle.bwd(sub.u, sub.delta, sub.A, sub.B, sub.C, sub.Dskip, sub.z, dy=np.ascontiguousarray(dy[..., ch]))
+    t.cuda.synchronize()
+    errs = {k: rel_err(g[k][..., ch].cpu().numpy() if k in ("du", "ddelta", "dz") else
+                       (g[k][ch].cpu().numpy()), ref[k]) for k in ("du", "ddelta", "dz", "dA", "dDskip")}
+    check(errs, "f32", "full/mamba130m sampled")
+    half = D // 2
+    parts = [gpu(s6_workloads.select_channels(inp, np.arange(lo, hi)), np.ascontiguousarray(dy[..., lo:hi]))
+             for lo, hi in ((0, half), (half, D))]
+    t.cuda.synchronize()
+    for k in ("dB", "dC"):
+        whole = g[k].cpu().numpy().astype(np.float64)
+        summed = sum(pp[k].cpu().numpy().astype(np.float64) for pp in parts)
+        assert rel_err(whole, summed) <= 1e-5, (k, rel_err(whole, summed))

@@ -153,3 +153,23 @@ def test_decode_loop_equals_scan(name):
     y = t.stack(ys, dim=1).cpu().numpy()
     assert rel_err(y, y_ref) <= TOL["f32"]
     assert rel_err(state.cpu().numpy(), l_ref) <= TOL_STATE
+
+
+def test_decode_step_full_size():
+    """The decode workload at its full size (512 sequences x 2560 channels x 16 states) in the
+    benchmark's call, against the oracle over all of it."""
+    import selective_state_space_s6_amd as ss
+    t = torch()
+    inp = s6_workloads.generate("decode_bf16")
+    h0 = s6_workloads.running_state(inp)
+    y_ref, l_ref = oracle.fwd(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z, h0=h0)
+    g = to_gpu(inp)
+    row = lambda x: x[:, 0].contiguous()
+    state = t.from_numpy(h0).cuda()
+    y = ss.selective_scan_step(row(g["u"]), row(g["delta"]), g["A"], row(g["B"]), row(g["C"]), g["Dskip"], row(g["z"]),
+                               state=state)
+    t.cuda.synchronize()
+    e_y = rel_err(y.float().cpu().numpy(), y_ref[:, 0])
+    e_l = rel_err(state.cpu().numpy(), l_ref)
+    log_errors("decode/full", y=e_y, last_state=e_l, io="bf16")
+    assert e_y <= TOL["bf16"] and e_l <= TOL_STATE, (e_y, e_l)
