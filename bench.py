@@ -189,6 +189,8 @@ def main():
     ap.add_argument("--workload", default="longctx_bf16",
                     choices=sorted(s6_workloads.WORKLOADS) + sorted(s6_workloads.SSD_WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "single", "chunked"])
+    ap.add_argument("--ssd-path", default="auto", choices=["auto", "fused", "chunked"],
+                    help="scalar-decay workloads: state kept on chip (fused) or chunk-parallel")
     ap.add_argument("--step-size", default="given", choices=["given", "softplus"],
                     help="softplus: the kernel computes softplus(raw + bias) from a pre-activation")
     ap.add_argument("--discretization", default="zoh", choices=["zoh", "euler"])
@@ -456,7 +458,8 @@ def bench_ssd(args):
     stream = torch.cuda.current_stream()
 
     def step():
-        ss.selective_scan_ssd_fwd(x, dl, A, B, C, Ds, z, y=y, discretization=args.discretization, stream=stream)
+        ss.selective_scan_ssd_fwd(x, dl, A, B, C, Ds, z, y=y, discretization=args.discretization,
+                                  path=args.ssd_path, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -501,7 +504,8 @@ def bench_ssd(args):
         "data": "synthetic (seeded, s6_workloads: %s)" % args.workload,
         "config": {"workload": args.workload, "batch": b, "seq_len": L, "heads": H, "headdim": P, "dstate": N,
                    "io": "bf16", "state": "f32", "gate": True, "feedthrough": True, "chunk": SSD_CHUNK,
-                   "discretization": args.discretization, "layer": "scalar decay per head (Mamba-2 SSD)"},
+                   "discretization": args.discretization, "layer": "scalar decay per head (Mamba-2 SSD)",
+                   "path": args.ssd_path},
         "kernel_ms": launch_ms,
         "hbm_gbs": round(alg / sec / 1e9, 1),
         "hbm_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),

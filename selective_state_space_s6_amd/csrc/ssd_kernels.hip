@@ -35,7 +35,13 @@ constexpr int kP = 64;          // head dimension
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ __bf16 to_bf16(float v) { return __builtin_bit_cast(__bf16, bf16_rne(v)); }
+// fp32 -> bf16, round to nearest even, on the hardware converter (one instruction, no branch)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __bf16 to_bf16(float v) { return static_cast<__bf16>(v); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
 __device__ __forceinline__ float bf16_f(__bf16 v) { return __uint_as_float(uint32_t(__builtin_bit_cast(uint16_t, v)) << 16); }
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(256) void ssd_state_scan_kernel(SsdParams p, int N)
   uint16_t* const Hc = p.carry + bh * nch * np + e;
   for (int64_t c = 0; c < nch; ++c) {
     const float s = S[c * np];
-    Hc[c * np] = bf16_rne(run);
+    Hc[c * np] = __builtin_bit_cast(uint16_t, to_bf16(run));
     run = fmaf(p.decay[bh * nch + c], run, s);
   }
   if (p.last_state != nullptr) p.last_state[(bh * kP + pp) * N + n] = run;
@@ -270,186 +276,325 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdParams p) {
         }
         v2[k] = yv;
       }
-      packed[e / 2] = uint32_t(bf16_rne(v2[0])) | (uint32_t(bf16_rne(v2[1])) << 16);
+      packed[e / 2] = pack_bf16(v2[0], v2[1]);
     }
     *reinterpret_cast<uint4*>(yg + o) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   }
 }
 
 // ---- fused: one workgroup per (b, h) walks the chunks in order with the head's state
-// H [N x 64] held in the matrix cores' accumulator registers (wavefront w owns rows
-// [w N/4, (w+1) N/4)); no state touches memory.  Per chunk:
-//   stage C, B, w-scaled B^T, x^T, the decay prefix; copy H (bf16) to LDS for C H;
-//   M = (C B^T) o mask;  Y = e^cum (C H) + M X  (then feed-through, gate, store);
-//   H <- e^cum_end H + B^T diag(w) X  (accumulated onto the scaled registers).
+// H [N x 64] held in the matrix cores' accumulator registers; no state touches memory.
+// Wavefront w owns the head channels p in [16 w, 16 w + 16): its state columns and its output
+// columns.  Each chunk's inputs are loaded into registers one chunk ahead, so the global
+// loads overlap the previous chunk's arithmetic.  Per chunk (three workgroup barriers):
+//   stage C and B rows, w-scaled B^T and x^T into LDS: every thread owns an 8-token block of
+//     B and x and transposes it in registers, so the transposed rows go out 16 bytes at a
+//     time; every wavefront forms the chunk's decay prefix itself (one token per lane);
+//   Y[:, cols] = e^cum (C H[:, cols]) + M X[:, cols]: the causal C B^T tiles are formed by
+//     each wavefront as B C^T, whose accumulator layout (lane: 4 consecutive tokens s of one
+//     row t) is, after the decay mask, the A operand of M X under a fixed permutation of the
+//     contraction index that X's operand repeats -- M never touches LDS; C H takes H straight
+//     from the accumulators (the 16x16x16 B operand has the accumulator layout);
+//   H[:, cols] <- e^cum_end H[:, cols] + B^T diag(w) X[:, cols];
+//   feed-through, gate and 4-byte stores through an fp32 tile in LDS, with x, z and D from
+//     registers.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// One chunk's inputs as a thread holds them between the global loads and the LDS staging.
+// Thread t: C pieces t + 256 k (16 bytes each); tokens 8 (t >> 5) .. + 7 of B (states
+// (t & 31) N/32 .. + N/32 - 1) and of x (channels 2 (t & 31), + 1); the step size of token
+// t & 63.  The gate z (same tokens and channels as x) is loaded on its own, after the
+// previous chunk's output, since only the output reads it.
 template <int N>
-__global__ __launch_bounds__(256) void ssd_fused_kernel(SsdParams p) {
+struct ChunkRegs {
+  static constexpr int kCv = kT * N / 8 / 256;   // 16-byte pieces of C per thread
+  static constexpr int kBw = N / 64;             // 32-bit words of B per token
+  uint4 c[kCv];
+  uint32_t b[8][kBw];
+  uint32_t x[8];
+  uint32_t dt;
+};
+
+// Loads address memory as a chunk base common to the workgroup plus a 32-bit offset per
+// thread, so that no 64-bit address per token stays live in vector registers.
+template <int N>
+__device__ __forceinline__ void load_chunk(ChunkRegs<N>& rg, const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
+  const int tid = threadIdx.x, sb = tid >> 5, lo = tid & 31;
+  const int64_t L = p.L, H = p.H;
+  const int rows = int(L - l0 < kT ? L - l0 : kT);        // tokens of this chunk inside the sequence
+  const uint16_t* const Bc = static_cast<const uint16_t*>(p.B) + (b * L + l0) * N;
+  const uint16_t* const Cc = static_cast<const uint16_t*>(p.C) + (b * L + l0) * N;
+  const uint16_t* const xc = static_cast<const uint16_t*>(p.x) + ((b * L + l0) * H + h) * kP;
+  const uint32_t tok_stride = uint32_t(H) * kP;            // elements between tokens of x, z
+  // tokens past the sequence end read the last token's row (in bounds) and keep zeros
+#pragma unroll
+  for (int k = 0; k < ChunkRegs<N>::kCv; ++k) {
+    const int i = tid + 256 * k, t = i / (N / 8), n0 = (i % (N / 8)) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(Cc + uint32_t(min(t, rows - 1) * N + n0));
+    rg.c[k] = t < rows ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = 8 * sb + j, tc = min(t, rows - 1);
+    const bool ok = t < rows;
+    const uint32_t* const bs = reinterpret_cast<const uint32_t*>(Bc + uint32_t(tc * N + lo * (N / 32)));
+    if constexpr (ChunkRegs<N>::kBw == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(bs);
+      rg.b[j][0] = ok ? v.x : 0u;
+      rg.b[j][1] = ok ? v.y : 0u;
+    } else {
+      const uint32_t v = *bs;
+      rg.b[j][0] = ok ? v : 0u;
+    }
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(xc + (uint32_t(tc) * tok_stride + uint32_t(2 * lo)));
+    rg.x[j] = ok ? v : 0u;
+  }
+  const int t = tid & 63;
+  const uint16_t d = static_cast<const uint16_t*>(p.delta)[(b * L + l0) * H + h + uint32_t(min(t, rows - 1)) * uint32_t(H)];
+  rg.dt = t < rows ? d : 0u;
+}
+
+__device__ __forceinline__ void load_gate(uint32_t (&zr)[8], const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
+  const int sb = threadIdx.x >> 5, lo = threadIdx.x & 31;
+  const int64_t L = p.L, H = p.H;
+  const int rows = int(L - l0 < kT ? L - l0 : kT);
+  const uint16_t* const zc = static_cast<const uint16_t*>(p.z) + ((b * L + l0) * H + h) * kP;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = 8 * sb + j;
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(zc + (uint32_t(min(t, rows - 1)) * uint32_t(H * kP) + uint32_t(2 * lo)));
+    zr[j] = t < rows ? v : 0u;
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront: within rows of 16 lanes by DPP row
+// shifts (lanes shifted in from outside the row read 0), then row 0's total into row 1 and
+// row 2's into row 3, then rows 0-1's total into rows 2 and 3.
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_get(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, BOUND_ZERO));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += dpp_get<0x111, 0xf, true>(x);                       // row_shr:1
+  x += dpp_get<0x112, 0xf, true>(x);                       // row_shr:2
+  x += dpp_get<0x114, 0xf, true>(x);                       // row_shr:4
+  x += dpp_get<0x118, 0xf, true>(x);                       // row_shr:8
+  x += dpp_get<0x142, 0xa, false>(x);                      // row_bcast:15 into rows 1, 3
+  x += dpp_get<0x143, 0xc, false>(x);                      // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int N>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_fused_kernel(SsdParams p) {
   constexpr int kRowN = N + 8, kRowK = kT + 8, kRowY = kP + 4;
-  constexpr int kRowTiles = N / 64;                        // 16-row state tiles per wavefront
-  __shared__ __align__(16) __bf16 sC[kT][kRowN];          // C[t][n]; later the fp32 output tile
-  __shared__ __align__(16) __bf16 sB[kT][kRowN];          // B[s][n]; later the mask tile M
+  constexpr int kKT = N / 16;                              // 16-state tiles of the state
+  constexpr int kNV = N / 32;                              // states of B per thread
+  __shared__ __align__(16) __bf16 sC[kT][kRowN];          // C[t][n]
+  __shared__ __align__(16) __bf16 sB[kT][kRowN];          // B[s][n]
   __shared__ __align__(16) __bf16 sBT[N][kRowK];          // w_s B[s][n] as [n][s]
   __shared__ __align__(16) __bf16 sXT[kP][kRowK];         // x[s][p] as [p][s]
-  __shared__ __align__(16) __bf16 sHT[kP][kRowN];         // H[n][p] as [p][n], bf16
-  __shared__ float s_cum[kT], s_c[kT];
-  constexpr bool kInC = kT * kRowY * 4 <= kT * kRowN * 2;
-  __shared__ __align__(16) float sYown[kInC ? 1 : kT * kRowY];
-  float* const sY = kInC ? reinterpret_cast<float*>(&sC[0][0]) : sYown;
-  __bf16* const sM = &sB[0][0];
+  __shared__ __align__(16) float sY[kT][kRowY];           // the chunk's output before D, gate
+  __shared__ __align__(16) float s_cum[kT], s_c[kT], s_w[kT];
 
   const int64_t bh = blockIdx.x, h = bh % p.H, b = bh / p.H;
   const int64_t L = p.L, H = p.H;
   const float A = p.A[h];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, r = lane & 15;
-  const uint16_t* const Bg = static_cast<const uint16_t*>(p.B);
-  const uint16_t* const Cg = static_cast<const uint16_t*>(p.C);
-  const uint16_t* const xg = static_cast<const uint16_t*>(p.x);
-  const uint16_t* const zg = static_cast<const uint16_t*>(p.z);
+  const bool euler = p.euler != 0;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int sb = tid >> 5, lo = tid & 31;                 // staging / output block of this thread
+  const int pc = 16 * w + r;                               // this lane's state/output column
   uint16_t* const yg = static_cast<uint16_t*>(p.y);
+  const bool gate = p.z != nullptr;
+  const float d0 = p.Dskip != nullptr ? p.Dskip[h * kP + 2 * lo] : 0.f;
+  const float d1 = p.Dskip != nullptr ? p.Dskip[h * kP + 2 * lo + 1] : 0.f;
 
-  // the state: tile (ti, tj) of wavefront w covers rows n0 = (w kRowTiles + ti) 16 + 4q + i,
-  // columns 16 tj + r
-  f32x4 hs[kRowTiles][kP / 16];
+  // the state: tile kt covers rows n = 16 kt + 4q + i of column pc
+  f32x4 hs[kKT];
 #pragma unroll
-  for (int ti = 0; ti < kRowTiles; ++ti)
+  for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-    for (int tj = 0; tj < kP / 16; ++tj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = (w * kRowTiles + ti) * 16 + 4 * q + i, pp = 16 * tj + r;
-        hs[ti][tj][i] = p.h0 != nullptr ? p.h0[(bh * kP + pp) * N + n] : 0.f;
-      }
+    for (int i = 0; i < 4; ++i) hs[kt][i] = p.h0 != nullptr ? p.h0[(bh * kP + pc) * N + 16 * kt + 4 * q + i] : 0.f;
 
+  ChunkRegs<N> rg;
+  load_chunk<N>(rg, p, b, h, 0);
+  uint32_t zr[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  if (gate) load_gate(zr, p, b, h, 0);
+  const float invA = A != 0.f ? 1.f / A : 0.f;
   for (int64_t chunk = 0; chunk < p.n_chunks; ++chunk) {
     const int64_t l0 = chunk * kT;
+    const int rows = int(L - l0 < kT ? L - l0 : kT);      // tokens of this chunk inside the sequence
+    // the chunk's decay prefix, formed by every wavefront (token = lane)
+    const float dt = bf16_lo(rg.dt);
+    const float cum = wave_prefix_sum(dt * A);             // log of the decay since the chunk start
+    const float a = __builtin_amdgcn_exp2f(dt * A * kLog2e);
+    const float cc = (euler || A == 0.f) ? dt : (a - 1.f) * invA;
+    const float cum_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
     __syncthreads();                                      // the previous chunk's LDS reads are done
-    chunk_decay(static_cast<const uint16_t*>(p.delta), b, l0, L, H, h, A, p.euler != 0, s_cum, s_c);
-    for (int i = threadIdx.x; i < kT * N / 8; i += 256) {
-      const int t = i / (N / 8), n0 = (i % (N / 8)) * 8;
-      const int64_t l = l0 + t;
-      *reinterpret_cast<uint4*>(&sC[t][n0]) = ld8(Cg + (b * L + l) * N + n0, l < L);
-      *reinterpret_cast<uint4*>(&sB[t][n0]) = ld8(Bg + (b * L + l) * N + n0, l < L);
+    if (w == 0) {
+      s_cum[lane] = cum;
+      s_c[lane] = cc;
+      s_w[lane] = __builtin_amdgcn_exp2f((cum_end - cum) * kLog2e) * cc;
     }
-    for (int i = threadIdx.x; i < kT * kP / 8; i += 256) {
-      const int s = i / (kP / 8), p0 = (i % (kP / 8)) * 8;
-      const int64_t l = l0 + s;
-      const uint4 v = ld8(xg + ((b * L + l) * H + h) * kP + p0, l < L);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sXT[p0 + e][s] = bf16_at(v, e);
+    for (int k = 0; k < ChunkRegs<N>::kCv; ++k) {
+      const int i = tid + 256 * k, t = i / (N / 8), n0 = (i % (N / 8)) * 8;
+      *reinterpret_cast<uint4*>(&sC[t][n0]) = rg.c[k];
     }
-    // H (the state entering this chunk) to LDS in bf16, for C H: a lane's four rows n are
-    // consecutive in the [p][n] layout, one 8-byte store
 #pragma unroll
-    for (int ti = 0; ti < kRowTiles; ++ti)
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (ChunkRegs<N>::kBw == 2)
+        *reinterpret_cast<uint2*>(&sB[8 * sb + j][lo * kNV]) = make_uint2(rg.b[j][0], rg.b[j][1]);
+      else
+        *reinterpret_cast<uint32_t*>(&sB[8 * sb + j][lo * kNV]) = rg.b[j][0];
+    }
+    {                                                      // x^T rows 2 lo, 2 lo + 1
+      uint32_t o0[4], o1[4];
 #pragma unroll
-      for (int tj = 0; tj < kP / 16; ++tj) {
-        const uint2 v = make_uint2(uint32_t(bf16_rne(hs[ti][tj][0])) | (uint32_t(bf16_rne(hs[ti][tj][1])) << 16),
-                                   uint32_t(bf16_rne(hs[ti][tj][2])) | (uint32_t(bf16_rne(hs[ti][tj][3])) << 16));
-        *reinterpret_cast<uint2*>(&sHT[16 * tj + r][(w * kRowTiles + ti) * 16 + 4 * q]) = v;
+      for (int j = 0; j < 8; j += 2) {
+        const uint32_t a0 = rg.x[j], a1 = rg.x[j + 1];
+        o0[j >> 1] = (a0 & 0xffffu) | (a1 << 16);
+        o1[j >> 1] = (a0 >> 16) | (a1 & 0xffff0000u);
       }
-    __syncthreads();                                      // C, B, x, H and the decay prefix are in
-    const float cum_end = s_cum[kT - 1];
-    // w-scaled B^T for the state update (needs the prefix)
-    for (int i = threadIdx.x; i < kT * N / 8; i += 256) {
-      const int s = i / (N / 8), n0 = (i % (N / 8)) * 8;
-      const float wgt = __builtin_amdgcn_exp2f((cum_end - s_cum[s]) * kLog2e) * s_c[s];
-      const uint4 v = *reinterpret_cast<const uint4*>(&sB[s][n0]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sBT[n0 + e][s] = to_bf16(bf16_f(bf16_at(v, e)) * wgt);
+      *reinterpret_cast<uint4*>(&sXT[2 * lo][8 * sb]) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+      *reinterpret_cast<uint4*>(&sXT[2 * lo + 1][8 * sb]) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
     }
-    const int t0 = 16 * w;
-    f32x4 g[kT / 16];
+    __syncthreads();                                      // C, B, x and the decay prefix are staged
+    {                                                      // w-scaled B^T rows, 8 tokens each
+      const float4 wa = *reinterpret_cast<const float4*>(&s_w[8 * sb]);
+      const float4 wb = *reinterpret_cast<const float4*>(&s_w[8 * sb + 4]);
+      const float wj[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
-    for (int tj = 0; tj < kT / 16; ++tj) {
-      const int s0 = 16 * tj;
-      g[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (s0 <= t0) {
+      for (int e = 0; e < kNV; ++e) {
+        uint32_t o[4];
 #pragma unroll
-        for (int k0 = 0; k0 < N; k0 += 32) g[tj] = mfma(frag(&sC[t0 + r][k0 + 8 * q]), frag(&sB[s0 + r][k0 + 8 * q]), g[tj]);
-      }
-    }
-    __syncthreads();                                      // B and the w-scaled B^T are done
-#pragma unroll
-    for (int tj = 0; tj < kT / 16; ++tj) {
-      const int s = 16 * tj + r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * q + i;
-        const float m = s <= t ? g[tj][i] * __builtin_amdgcn_exp2f((s_cum[t] - s_cum[s]) * kLog2e) * s_c[s] : 0.f;
-        sM[t * kRowN + s] = to_bf16(m);
+        for (int j = 0; j < 8; j += 2) {
+          const uint32_t w0 = rg.b[j][e >> 1], w1 = rg.b[j + 1][e >> 1];
+          const float v0 = (e & 1) ? bf16_hi(w0) : bf16_lo(w0);
+          const float v1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
+          o[j >> 1] = pack_bf16(v0 * wj[j], v1 * wj[j + 1]);
+        }
+        *reinterpret_cast<uint4*>(&sBT[lo * kNV + e][8 * sb]) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
-    // state update: H <- e^cum_end H + B^T diag(w) X (reads sBT and sXT only)
-    const float dec = __builtin_amdgcn_exp2f(cum_end * kLog2e);
+    __builtin_amdgcn_sched_barrier(0);                     // the staged registers are free: reuse them
+    if (chunk + 1 < p.n_chunks) load_chunk<N>(rg, p, b, h, l0 + kT);   // lands during the arithmetic
+
+    // Y[:, cols] = e^cum (C H) + M X
+    s16x4 hb[kKT];
 #pragma unroll
-    for (int ti = 0; ti < kRowTiles; ++ti) {
-      const int n0 = (w * kRowTiles + ti) * 16;
-#pragma unroll
-      for (int tj = 0; tj < kP / 16; ++tj) {
-        f32x4 acc = hs[ti][tj] * dec;
-#pragma unroll
-        for (int k0 = 0; k0 < kT; k0 += 32)
-          acc = mfma(frag(&sBT[n0 + r][k0 + 8 * q]), frag(&sXT[16 * tj + r][k0 + 8 * q]), acc);
-        hs[ti][tj] = acc;
-      }
+    for (int kt = 0; kt < kKT; ++kt) {
+      const uint32_t lo2 = pack_bf16(hs[kt][0], hs[kt][1]), hi2 = pack_bf16(hs[kt][2], hs[kt][3]);
+      hb[kt] = __builtin_bit_cast(s16x4, make_uint2(lo2, hi2));
     }
-    __syncthreads();                                      // M is complete
-    f32x4 yacc[kP / 16];
 #pragma unroll
-    for (int tj = 0; tj < kP / 16; ++tj) {
-      const int p0 = 16 * tj;
+    for (int ti = 0; ti < kT / 16; ++ti) {
+      __builtin_amdgcn_sched_barrier(0);                   // one row tile at a time: bounds the live set
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k0 = 0; k0 < N; k0 += 32) acc = mfma(frag(&sC[t0 + r][k0 + 8 * q]), frag(&sHT[p0 + r][k0 + 8 * q]), acc);
+      for (int kt = 0; kt < kKT; ++kt)
+        acc = mfma16(*reinterpret_cast<const s16x4*>(&sC[16 * ti + r][16 * kt + 4 * q]), hb[kt], acc);
+      const float4 ct = *reinterpret_cast<const float4*>(&s_cum[16 * ti + 4 * q]);
+      acc[0] *= __builtin_amdgcn_exp2f(ct.x * kLog2e);
+      acc[1] *= __builtin_amdgcn_exp2f(ct.y * kLog2e);
+      acc[2] *= __builtin_amdgcn_exp2f(ct.z * kLog2e);
+      acc[3] *= __builtin_amdgcn_exp2f(ct.w * kLog2e);
+      const int t = 16 * ti + r;                           // this lane's row of M
+      const float cum_t = s_cum[t];
+      bf16x8 cfr[N / 32];                                  // row t of C, the B operand of B C^T
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= __builtin_amdgcn_exp2f(s_cum[t0 + 4 * q + i] * kLog2e);
+      for (int k = 0; k < N / 32; ++k) cfr[k] = frag(&sC[t][32 * k + 8 * q]);
 #pragma unroll
-      for (int k0 = 0; k0 < kT; k0 += 32)
-        if (k0 <= t0 + 15) acc = mfma(frag(&sM[(t0 + r) * kRowN + k0 + 8 * q]), frag(&sXT[p0 + r][k0 + 8 * q]), acc);
-      yacc[tj] = acc;
-    }
-    __syncthreads();                                      // C is no longer read
+      for (int kk = 0; kk <= ti / 2; ++kk) {
+        // M[t][s] for s = 32 kk + 4q + i (i < 4) and 32 kk + 16 + 4q + i: contraction slot
+        // 8q + j of the 32 holds token 32 kk + 4q + j (j < 4), 32 kk + 16 + 4q + j - 4 (j >= 4)
+        bf16x8 am;
 #pragma unroll
-    for (int tj = 0; tj < kP / 16; ++tj)
+        for (int half = 0; half < 2; ++half) {
+          const int tj = 2 * kk + half;
+          if (tj > ti) {                                    // above the diagonal: M is zero
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sY[(t0 + 4 * q + i) * kRowY + 16 * tj + r] = yacc[tj][i];
-    __syncthreads();
-    for (int i = threadIdx.x; i < kT * kP / 8; i += 256) {
-      const int t = i / (kP / 8), p0 = (i % (kP / 8)) * 8;
-      const int64_t l = l0 + t;
-      if (l >= L) continue;
-      const int64_t o = ((b * L + l) * H + h) * kP + p0;
-      const uint4 zv = zg != nullptr ? *reinterpret_cast<const uint4*>(zg + o) : make_uint4(0u, 0u, 0u, 0u);
-      uint32_t packed[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float v2[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int pp = p0 + e + k;
-          float yv = sY[t * kRowY + pp];
-          if (p.Dskip != nullptr) yv = fmaf(p.Dskip[h * kP + pp], bf16_f(sXT[pp][t]), yv);
-          if (zg != nullptr) {
-            const float zz = bf16_f(bf16_at(zv, e + k));
-            yv *= zz * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+            for (int i = 0; i < 4; ++i) am[4 * half + i] = to_bf16(0.f);
+            continue;
           }
-          v2[k] = yv;
+          f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < N / 32; ++k) g = mfma(frag(&sB[16 * tj + r][32 * k + 8 * q]), cfr[k], g);
+          const float4 cs = *reinterpret_cast<const float4*>(&s_cum[16 * tj + 4 * q]);
+          const float4 cw = *reinterpret_cast<const float4*>(&s_c[16 * tj + 4 * q]);
+          const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, cwv[4] = {cw.x, cw.y, cw.z, cw.w};
+          float mv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = 16 * tj + 4 * q + i;
+            const float m = g[i] * __builtin_amdgcn_exp2f((cum_t - csv[i]) * kLog2e) * cwv[i];
+            mv[i] = s <= t ? m : 0.f;                        // a select: the causal mask
+          }
+          const uint2 mp = make_uint2(pack_bf16(mv[0], mv[1]), pack_bf16(mv[2], mv[3]));
+          const bf16x2 m01 = __builtin_bit_cast(bf16x2, mp.x), m23 = __builtin_bit_cast(bf16x2, mp.y);
+          am[4 * half + 0] = m01[0];
+          am[4 * half + 1] = m01[1];
+          am[4 * half + 2] = m23[0];
+          am[4 * half + 3] = m23[1];
         }
-        packed[e / 2] = uint32_t(bf16_rne(v2[0])) | (uint32_t(bf16_rne(v2[1])) << 16);
+        const uint2 x0 = *reinterpret_cast<const uint2*>(&sXT[pc][32 * kk + 4 * q]);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(&sXT[pc][32 * kk + 16 + 4 * q]);
+        const uint4 xv = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        acc = mfma(am, __builtin_bit_cast(bf16x8, xv), acc);
       }
-      *reinterpret_cast<uint4*>(yg + o) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sY[16 * ti + 4 * q + i][pc] = acc[i];
     }
+    __syncthreads();                                      // the output tile and B^T are complete
+    // H[:, cols] <- e^cum_end H + B^T diag(w) X[:, cols]
+    const float dec = __builtin_amdgcn_exp2f(cum_end * kLog2e);
+    const bf16x8 xf0 = frag(&sXT[pc][8 * q]), xf1 = frag(&sXT[pc][32 + 8 * q]);
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) {
+      f32x4 acc = hs[kt] * dec;
+      acc = mfma(frag(&sBT[16 * kt + r][8 * q]), xf0, acc);
+      acc = mfma(frag(&sBT[16 * kt + r][32 + 8 * q]), xf1, acc);
+      hs[kt] = acc;
+    }
+    // feed-through, gate, bf16 stores: tokens 8 sb .. + 7, channels 2 lo, 2 lo + 1
+    uint16_t* const yc = yg + ((b * L + l0) * H + h) * kP;
+    const uint4 xa = *reinterpret_cast<const uint4*>(&sXT[2 * lo][8 * sb]);      // x[8 sb + j][2 lo]
+    const uint4 xb = *reinterpret_cast<const uint4*>(&sXT[2 * lo + 1][8 * sb]);  // x[8 sb + j][2 lo + 1]
+    uint32_t yo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float2 yv = *reinterpret_cast<const float2*>(&sY[8 * sb + j][2 * lo]);
+      float y0 = fmaf(d0, bf16_f(bf16_at(xa, j)), yv.x), y1 = fmaf(d1, bf16_f(bf16_at(xb, j)), yv.y);
+      if (gate) {
+        const float z0 = bf16_lo(zr[j]), z1 = bf16_hi(zr[j]);
+        y0 *= z0 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z0 * kLog2e));
+        y1 *= z1 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z1 * kLog2e));
+      }
+      yo[j] = pack_bf16(y0, y1);
+    }
+    if (rows == kT) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (8 * sb + j < rows)
+          *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[j];
+    }
+    if (gate && chunk + 1 < p.n_chunks) load_gate(zr, p, b, h, l0 + kT);   // lands during the next chunk
   }
   if (p.last_state != nullptr) {
 #pragma unroll
-    for (int ti = 0; ti < kRowTiles; ++ti)
+    for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-      for (int tj = 0; tj < kP / 16; ++tj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = (w * kRowTiles + ti) * 16 + 4 * q + i, pp = 16 * tj + r;
-          p.last_state[(bh * kP + pp) * N + n] = hs[ti][tj][i];
-        }
+      for (int i = 0; i < 4; ++i) p.last_state[(bh * kP + pc) * N + 16 * kt + 4 * q + i] = hs[kt][i];
   }
 }
 
