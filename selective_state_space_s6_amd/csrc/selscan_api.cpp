@@ -523,7 +523,7 @@ int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias
   return st;
 }
 
-constexpr int64_t kSsdFusedMinItems = 256;   // (batch, head) workgroups for the on-chip path: one per CU
+constexpr int64_t kSsdFusedMinItems = 112;   // (batch, head) workgroups from which the on-chip path is faster
 
 static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chunks, bool* fused) {
   if (!d) return SELSCAN_ERR_NULL;

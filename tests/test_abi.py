@@ -235,7 +235,8 @@ def test_ssd_errors():
     assert ss.ssd_workspace_size(ss.ssd_dims(0, 200, 3, 64, 128)) == 0
     assert ss.ssd_workspace_size(ss.ssd_dims(2, 200, 3, 64, 128, path="fused")) == 0     # state on chip
     assert ss.ssd_workspace_size(ss.ssd_dims(4, 200, 80, 64, 128)) == 0                  # automatic: on chip
-    assert ss.ssd_workspace_size(ss.ssd_dims(8, 200, 24, 64, 128)) > 0                   # automatic: chunks
+    assert ss.ssd_workspace_size(ss.ssd_dims(8, 200, 24, 64, 128)) == 0                  # automatic: on chip
+    assert ss.ssd_workspace_size(ss.ssd_dims(2, 200, 24, 64, 128)) > 0                   # automatic: chunks
     assert ss.ssd_workspace_size(ss.ssd_dims(2, 200, 3, 64, 128, path="chunked")) == need
     bad_path = ss.ssd_dims(2, 200, 3, 64, 128)
     bad_path.path = 3

@@ -82,23 +82,36 @@ def test_ssd_many_heads_long(path):
     assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
 
 
+_FULL_REF = {}
+
+
+def _full_reference(name):
+    """Workload inputs and the oracle's output on three of its heads (heads are independent
+    given B and C), computed once per workload."""
+    if name not in _FULL_REF:
+        inp = s6_workloads.generate_ssd(name)
+        H = inp.x.shape[2]
+        hs = np.array([0, H // 2, H - 1])
+        ch = (hs[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+        y_ref, l_ref = oracle.ssd_fwd(inp.x[:, :, hs], inp.delta[:, :, hs], inp.A[hs], inp.B, inp.C, inp.Dskip[ch],
+                                      inp.z[:, :, hs])
+        _FULL_REF[name] = (inp, hs, y_ref, l_ref)
+    return _FULL_REF[name]
+
+
+@pytest.mark.parametrize("path", ["auto", "chunked"])
 @pytest.mark.parametrize("name", sorted(s6_workloads.SSD_WORKLOADS))
-def test_ssd_full_size_sampled_heads(name):
-    """The benchmark's workloads at full size on the automatic path, checked against the oracle
-    on three heads (heads are independent given B and C)."""
+def test_ssd_full_size_sampled_heads(name, path):
+    """The benchmark's workloads at full size (the automatic path, which the benchmark times,
+    and the chunk-parallel one), checked against the oracle on three heads."""
     import selective_state_space_s6_amd as ss
     t = torch()
-    inp = s6_workloads.generate_ssd(name)
+    inp, hs, y_ref, l_ref = _full_reference(name)
     g = lambda a: t.from_numpy(a).cuda().to(t.bfloat16)
     y, last = ss.selective_scan_ssd_fwd(g(inp.x), g(inp.delta), t.from_numpy(inp.A).cuda(), g(inp.B), g(inp.C),
-                                        t.from_numpy(inp.Dskip).cuda(), g(inp.z), return_last_state=True)
+                                        t.from_numpy(inp.Dskip).cuda(), g(inp.z), return_last_state=True, path=path)
     t.cuda.synchronize()
-    H = inp.x.shape[2]
-    hs = np.array([0, H // 2, H - 1])
-    ch = (hs[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
-    y_ref, l_ref = oracle.ssd_fwd(inp.x[:, :, hs], inp.delta[:, :, hs], inp.A[hs], inp.B, inp.C, inp.Dskip[ch],
-                                  inp.z[:, :, hs])
     e_y = rel_err(y[:, :, hs].float().cpu().numpy(), y_ref)
     e_l = rel_err(last[:, hs].cpu().numpy(), l_ref)
-    log_errors("ssd/full/%s" % name, y=e_y, last_state=e_l, io="bf16")
+    log_errors("ssd/full/%s/%s" % (name, path), y=e_y, last_state=e_l, io="bf16")
     assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
