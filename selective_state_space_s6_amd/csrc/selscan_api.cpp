@@ -254,7 +254,9 @@ struct BwdPlan {
   size_t off_state = 0, off_dsum = 0, off_adjG = 0, off_adjS = 0, off_adjin = 0, bytes = 0;
 };
 
-constexpr int64_t kBwdTargetBlocks = 1024;   // about four wavefronts per SIMD
+// Main-pass workgroups resident on MI355X at once: 256 compute units x 2 (every main-pass
+// instantiation takes 256 VGPRs per lane and at most 80.6 KB of LDS).
+constexpr int64_t kBwdSlots = 512;
 
 // Validate dims for the backward pass and lay out its workspace (groups: channel groups of
 // one workgroup, 64, 32 or 16 channels):
@@ -270,14 +272,27 @@ int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
   const int64_t cwg = 4 * 64 / selscan::bwd_lanes_per_channel(d.dstate);   // channels per workgroup
   b.groups = (d.dim + cwg - 1) / cwg;
   b.ntiles = (d.seqlen + 15) / 16;
-  // chunks of the sequence when (batch row, channel group) items alone leave the GPU idle
+  // Chunks of the sequence: each workgroup's tokens are a serial chain, so the time is about
+  // (rounds of resident workgroups) x (tokens per workgroup).  The smallest such cost wins;
+  // fewer chunks win unless more are at least 3 % cheaper (each chunk adds a carry and an
+  // adjoint pass over its tokens).
   int64_t nc = 1;
   const int64_t items = d.batch * b.groups;
-  if (items > 0 && items < kBwdTargetBlocks && d.seqlen >= 128) {
-    nc = (kBwdTargetBlocks + items - 1) / items;
-    if (nc > d.seqlen / 64) nc = d.seqlen / 64;                  // chunks of at least 64 tokens
-    if (nc > kMaxChunks) nc = kMaxChunks;
-    if (nc < 1) nc = 1;
+  if (items > 0 && d.seqlen >= 128) {
+    int64_t max_nc = d.seqlen / 64;                              // chunks of at least 64 tokens
+    if (max_nc > kMaxChunks) max_nc = kMaxChunks;
+    auto cost = [&](int64_t n) {
+      const int64_t rounds = (items * n + kBwdSlots - 1) / kBwdSlots;
+      return rounds * round_up((d.seqlen + n - 1) / n, 16);
+    };
+    int64_t best = cost(1);
+    for (int64_t n = 2; n <= max_nc; ++n) {
+      const int64_t c = cost(n);
+      if (c * 100 < best * 97) {
+        best = c;
+        nc = n;
+      }
+    }
   }
   b.chunk_len = nc > 1 ? round_up((d.seqlen + nc - 1) / nc, 16) : round_up(d.seqlen > 0 ? d.seqlen : 1, 16);
   // a forward plan chunked for its 32-bit tile addressing bounds the chunk length
