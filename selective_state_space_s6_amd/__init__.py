@@ -92,6 +92,13 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libselscan.so is not built (expected at %s); run "
                                "`python -m selective_state_space_s6_amd.build`" % LIB_PATH)
+        # PyTorch's wheel carries its own HIP runtime; it is loaded first so that this library
+        # binds to the runtime that owns PyTorch's streams and memory (loaded the other way
+        # round, HIP calls from here fail with hipErrorNoDevice)
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         handle = ctypes.CDLL(LIB_PATH)
         for name, res, args in _SIGNATURES:
             fn = getattr(handle, name)

@@ -176,60 +176,57 @@ void bwd_kernel(BwdParams p) {
   const float tbias = (tcok && p.delta_bias != nullptr) ? p.delta_bias[tdq] : 0.f;
   const int bj0 = tid / NP, bn = tid % NP;
   const int bnq = bn < N ? bn : int(N) - 1;
-  float xu[ET], xd[ET], xy[ET], xz[ET], xB[EB], xC[EB], xH[4];
+  // The loads of the next tile stay in flight while the current one computes: the raw
+  // values are kept as loaded and only widened and range-masked when staged (any use at
+  // load time would wait for them).
+  IO xu[ET], xd[ET], xy[ET], xz[ET], xB[EB], xC[EB];
+  float xH[4];
+  int pend_nt = kBTile;                                     // valid tokens of the tile in flight
   auto issue = [&](int64_t t, bool all) __attribute__((always_inline)) {
     const int nt = t == ntiles - 1 ? last_nt : kBTile;
+    pend_nt = nt;
     const int64_t l0 = l_begin + t * kBTile;
 #pragma unroll
     for (int r = 0; r < ET; ++r) {
       const int j = tj0 + kTStep * r;
       const int jq = j < nt ? j : nt - 1;
-      const bool ok = tcok && j < nt;
-      const float vu = T::widen(u_b[(l0 + jq) * p.u_sl + tdq]);
-      const float vd = T::widen(dl_b[(l0 + jq) * p.delta_sl + tdq]);
-      xu[r] = ok ? vu : 0.f;
-      xd[r] = ok ? vd : 0.f;
+      xu[r] = u_b[(l0 + jq) * p.u_sl + tdq];
+      xd[r] = dl_b[(l0 + jq) * p.delta_sl + tdq];
       if (all) {
-        const float vy = T::widen(dy_b[(l0 + jq) * p.dy_sl + tdq]);
-        const float vz = T::widen(z_b[(l0 + jq) * z_sl + tdq]);
-        xy[r] = ok ? vy : 0.f;
-        xz[r] = ok ? vz : 0.f;
+        xy[r] = dy_b[(l0 + jq) * p.dy_sl + tdq];
+        xz[r] = z_b[(l0 + jq) * z_sl + tdq];
       }
     }
 #pragma unroll
     for (int r = 0; r < EB; ++r) {
       const int j = bj0 + kBStep * r;
       const int jb = j < nt ? j : nt - 1;
-      const bool okb = bn < N && j < nt;
-      const float vb = T::widen(B_b[(l0 + jb) * p.B_sl + bnq]);
-      xB[r] = okb ? vb : 0.f;
-      if (all) {
-        const float vc = T::widen(C_b[(l0 + jb) * p.C_sl + bnq]);
-        xC[r] = okb ? vc : 0.f;
-      }
+      xB[r] = B_b[(l0 + jb) * p.B_sl + bnq];
+      if (all) xC[r] = C_b[(l0 + jb) * p.C_sl + bnq];
     }
     if (all && MODE == BWD_MAIN) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float vh = ck_b[t * D * N + ck_d + nq[i]];
-        xH[i] = nok[i] ? vh : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) xH[i] = ck_b[t * D * N + ck_d + nq[i]];
     }
   };
   auto stage = [&](bool all) __attribute__((always_inline)) {
+    const int nt = pend_nt;
 #pragma unroll
     for (int r = 0; r < ET; ++r) {
       const int j = tj0 + kTStep * r;
-      sTok[0][tc][j] = xu[r];
-      const float x = xd[r] + tbias;
-      sTok[1][tc][j] = p.dxf ? (sp ? softplus_f32(x) : x) : xd[r];
+      const bool ok = tcok && j < nt;
+      const float vd = ok ? T::widen(xd[r]) : 0.f;
+      sTok[0][tc][j] = ok ? T::widen(xu[r]) : 0.f;
+      const float x = vd + tbias;
+      sTok[1][tc][j] = p.dxf ? (sp ? softplus_f32(x) : x) : vd;
       if (all) {
-        float dyp = xy[r], gzf = 0.f;
+        const float vy = ok ? T::widen(xy[r]) : 0.f;
+        float dyp = vy, gzf = 0.f;
         if (gated) {           // y = yp * z sigmoid(z): dyp = dy z sigmoid(z); dz = yp * gzf
-          const float zz = xz[r];
+          const float zz = ok ? T::widen(xz[r]) : 0.f;
           const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
-          dyp = xy[r] * zz * sg;
-          gzf = xy[r] * sg * fmaf(zz, 1.f - sg, 1.f);
+          dyp = vy * zz * sg;
+          gzf = vy * sg * fmaf(zz, 1.f - sg, 1.f);
         }
         sTok[2][tc][j] = dyp;
         sTok[3][tc][j] = gzf;
@@ -239,8 +236,9 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < EB; ++r) {
       const int j = bj0 + kBStep * r;
-      sBq[j][bn] = xB[r];
-      if (all) sCq[j][bn] = xC[r];
+      const bool okb = bn < N && j < nt;
+      sBq[j][bn] = okb ? T::widen(xB[r]) : 0.f;
+      if (all) sCq[j][bn] = okb ? T::widen(xC[r]) : 0.f;
     }
   };
   auto ld4 = [](const float* q) { return *reinterpret_cast<const float4*>(q); };
@@ -441,7 +439,7 @@ void bwd_kernel(BwdParams p) {
     stage(true);                         // the previous tile's LDS reads ended at its barrier
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = xH[i];               // the tile's checkpoint
+    for (int i = 0; i < 4; ++i) h[i] = nok[i] ? xH[i] : 0.f;   // the tile's checkpoint
     if (t > 0) issue(t - 1, true);
     if (t == ntiles - 1 && last_nt < kBTile) tile(t, last_nt, std::false_type{});
     else tile(t, kBTile, std::true_type{});
