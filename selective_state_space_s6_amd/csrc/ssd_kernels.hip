@@ -330,32 +330,29 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<N>& rg, const SsdParams& p,
   const uint16_t* const Cc = static_cast<const uint16_t*>(p.C) + (b * L + l0) * N;
   const uint16_t* const xc = static_cast<const uint16_t*>(p.x) + ((b * L + l0) * H + h) * kP;
   const uint32_t tok_stride = uint32_t(H) * kP;            // elements between tokens of x, z
-  // tokens past the sequence end read the last token's row (in bounds) and keep zeros
+  // Tokens past the sequence end read the last token's row (in bounds).  The values stay
+  // as loaded (a use here would wait for the load); B, x and the step size of such tokens
+  // are zeroed when staged, and their C and z reach only outputs that are never stored.
 #pragma unroll
   for (int k = 0; k < ChunkRegs<N>::kCv; ++k) {
     const int i = tid + 256 * k, t = i / (N / 8), n0 = (i % (N / 8)) * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(Cc + uint32_t(min(t, rows - 1) * N + n0));
-    rg.c[k] = t < rows ? v : make_uint4(0u, 0u, 0u, 0u);
+    rg.c[k] = *reinterpret_cast<const uint4*>(Cc + uint32_t(min(t, rows - 1) * N + n0));
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int t = 8 * sb + j, tc = min(t, rows - 1);
-    const bool ok = t < rows;
+    const int tc = min(8 * sb + j, rows - 1);
     const uint32_t* const bs = reinterpret_cast<const uint32_t*>(Bc + uint32_t(tc * N + lo * (N / 32)));
     if constexpr (ChunkRegs<N>::kBw == 2) {
       const uint2 v = *reinterpret_cast<const uint2*>(bs);
-      rg.b[j][0] = ok ? v.x : 0u;
-      rg.b[j][1] = ok ? v.y : 0u;
+      rg.b[j][0] = v.x;
+      rg.b[j][1] = v.y;
     } else {
-      const uint32_t v = *bs;
-      rg.b[j][0] = ok ? v : 0u;
+      rg.b[j][0] = *bs;
     }
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(xc + (uint32_t(tc) * tok_stride + uint32_t(2 * lo)));
-    rg.x[j] = ok ? v : 0u;
+    rg.x[j] = *reinterpret_cast<const uint32_t*>(xc + (uint32_t(tc) * tok_stride + uint32_t(2 * lo)));
   }
   const int t = tid & 63;
-  const uint16_t d = static_cast<const uint16_t*>(p.delta)[(b * L + l0) * H + h + uint32_t(min(t, rows - 1)) * uint32_t(H)];
-  rg.dt = t < rows ? d : 0u;
+  rg.dt = static_cast<const uint16_t*>(p.delta)[(b * L + l0) * H + h + uint32_t(min(t, rows - 1)) * uint32_t(H)];
 }
 
 __device__ __forceinline__ void load_gate(uint32_t (&zr)[8], const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
@@ -365,9 +362,8 @@ __device__ __forceinline__ void load_gate(uint32_t (&zr)[8], const SsdParams& p,
   const uint16_t* const zc = static_cast<const uint16_t*>(p.z) + ((b * L + l0) * H + h) * kP;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int t = 8 * sb + j;
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(zc + (uint32_t(min(t, rows - 1)) * uint32_t(H * kP) + uint32_t(2 * lo)));
-    zr[j] = t < rows ? v : 0u;
+    const int t = min(8 * sb + j, rows - 1);               // past the end: read in bounds, never stored
+    zr[j] = *reinterpret_cast<const uint32_t*>(zc + (uint32_t(t) * uint32_t(H * kP) + uint32_t(2 * lo)));
   }
 }
 
@@ -431,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t l0 = chunk * kT;
     const int rows = int(L - l0 < kT ? L - l0 : kT);      // tokens of this chunk inside the sequence
     // the chunk's decay prefix, formed by every wavefront (token = lane)
-    const float dt = bf16_lo(rg.dt);
+    const float dt = lane < rows ? bf16_lo(rg.dt) : 0.f;   // padded tokens: no step
     const float cum = wave_prefix_sum(dt * A);             // log of the decay since the chunk start
     const float a = __builtin_amdgcn_exp2f(dt * A * kLog2e);
     const float cc = (euler || A == 0.f) ? dt : (a - 1.f) * invA;
@@ -445,10 +441,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int k = 0; k < ChunkRegs<N>::kCv; ++k) {
       const int i = tid + 256 * k, t = i / (N / 8), n0 = (i % (N / 8)) * 8;
-      *reinterpret_cast<uint4*>(&sC[t][n0]) = rg.c[k];
+      const uint4 cv = rg.c[k];
+      *reinterpret_cast<uint4*>(&sC[t][n0]) = make_uint4(cv.x, cv.y, cv.z, cv.w);   // by value: keeps rg in registers
     }
+    // B and x of padded tokens are zero (they must not reach the state)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      const bool ok = 8 * sb + j < rows;
+#pragma unroll
+      for (int e = 0; e < ChunkRegs<N>::kBw; ++e) rg.b[j][e] = ok ? rg.b[j][e] : 0u;
+      rg.x[j] = ok ? rg.x[j] : 0u;
       if constexpr (ChunkRegs<N>::kBw == 2)
         *reinterpret_cast<uint2*>(&sB[8 * sb + j][lo * kNV]) = make_uint2(rg.b[j][0], rg.b[j][1]);
       else
