@@ -44,6 +44,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
                   for f in ("scan_kernels.hip", "device_common.h")]
 SSD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
                       for f in ("ssd_kernels.hip", "device_common.h")]
+BWD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
+                      for f in ("bwd_kernels.hip", "scan_kernels.hip", "device_common.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "scan_counters.json")
 
 # Algorithmic ALU work, in FMA-slot units (one fp32 VALU op = 1 slot = 2 flop-equivalents;
@@ -128,11 +130,14 @@ def algorithmic_slots(inp: s6_workloads.Inputs, softplus: bool = False, euler: b
 
 
 def kernel_source_hash(workload: str = "") -> str:
-    """Hash of the sources of the kernels a workload runs (the scan kernels, or for the
-    scalar-decay workloads its kernels): the counters in the committed summary are valid only
-    for the source they were taken on."""
+    """Hash of the sources of the kernels a workload runs (the scan kernels; for the
+    scalar-decay workloads theirs; for a backward tag, "backward_<workload>", the backward's
+    and the forward state pass's): the counters in the committed summary are valid only for
+    the source they were taken on."""
     h = hashlib.sha256()
-    for path in (SSD_KERNEL_SOURCES if workload.startswith("ssd_") else KERNEL_SOURCES):
+    srcs = (SSD_KERNEL_SOURCES if workload.startswith("ssd_")
+            else BWD_KERNEL_SOURCES if workload.startswith("backward_") else KERNEL_SOURCES)
+    for path in srcs:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -342,12 +342,14 @@ void bwd_kernel(BwdParams p) {
     float hp[kBTile][4];                                   // state before token j of the tile
 #pragma unroll
     for (int j = 0; j < kBTile; ++j) {
+      // recorded for padded tokens too: there it is the state after the last token
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hp[j][i] = h[i];
       if (FULL || j < nt) {
         const float uu = sTok[0][cw][j], dt = sTok[1][cw][j];
         const float4 B4 = ld4(&sBq[j][4 * s]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          hp[j][i] = h[i];
           const float ab = __builtin_amdgcn_exp2f(dt * a2[i]);
           const float cf = fmaf(dt, zf[i], fmaf(ab, iA[i], -iA[i]));
           h[i] = fmaf(ab, h[i], cf * (el(B4, i) * uu));
@@ -365,33 +367,36 @@ void bwd_kernel(BwdParams p) {
         const float gzf = sTok[3][cw][j], sig = sTok[4][cw][j];
         const float4 B4 = ld4(&sBq[j][4 * s]), C4 = ld4(&sCq[j][4 * s]);
         const float dt2 = dt * dt;
-        float ab[4], cf[4], hj[4];
+        float ab[4], cf[4];
         float spart = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ab[i] = __builtin_amdgcn_exp2f(dt * a2[i]);
           cf[i] = fmaf(dt, zf[i], fmaf(ab[i], iA[i], -iA[i]));
-          hj[i] = fmaf(ab[i], hp[j][i], cf[i] * (el(B4, i) * uu));
-          spart = fmaf(el(C4, i), hj[i], spart);
+          // the state after token j: the one recorded before token j + 1 (h: after the tile)
+          spart = fmaf(el(C4, i), j + 1 < kBTile ? hp[j + 1][i] : h[i], spart);
         }
         float gu = 0.f, gdt = 0.f, pb[4], pc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float Bi = el(B4, i);
+          const float hj = j + 1 < kBTile ? hp[j + 1][i] : h[i];
           const float lam = fmaf(dyp, el(C4, i), mu[i]);
           const float bu = Bi * uu;
-          gu = fmaf(lam, cf[i] * Bi, gu);
-          const float dcdd = first ? 1.f : ab[i];
-          gdt = fmaf(lam, fmaf(a[i] * ab[i], hp[j][i], dcdd * bu), gdt);
+          const float lc = lam * cf[i];
+          gu = fmaf(lc, Bi, gu);
+          const float abh = ab[i] * hp[j][i];                 // Abar h_{t-1}
+          const float dcdd_bu = first ? bu : ab[i] * bu;
+          gdt = fmaf(lam, fmaf(a[i], abh, dcdd_bu), gdt);
           // dc/da = (delta Abar - c) / a, or delta^2 phi(x), x = delta a, by the series of
           // phi(x) = (x e^x - (e^x - 1)) / x^2 near 0 where the first form cancels (and at a == 0)
           const float x = dt * a[i];
           const float series = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
           const float closed = fmaf(dt, ab[i], -cf[i]) * iA[i];
           const float dcda = first ? 0.f : (fabsf(x) < 0.1f ? dt2 * series : closed);
-          gA[i] = fmaf(lam, fmaf(dt * ab[i], hp[j][i], dcda * bu), gA[i]);
-          pb[i] = lam * cf[i] * uu;
-          pc[i] = dyp * hj[i];
+          gA[i] = fmaf(lam, fmaf(dt, abh, dcda * bu), gA[i]);
+          pb[i] = lc * uu;
+          pc[i] = dyp * hj;
           mu[i] = ab[i] * lam;
         }
         // keep the accumulations here: left alone, the compiler sinks them to the end of the
