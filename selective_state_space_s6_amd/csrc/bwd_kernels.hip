@@ -89,14 +89,15 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-enum { BWD_ADJOINT = 0, BWD_MAIN = 1 };
+enum { BWD_ADJOINT = 0, BWD_MAIN = 1, BWD_MAIN_EULER = 2 };
 
 // SL lanes per channel, 4 states per lane (state n = 4 s + i); 64 / SL channels per wavefront.
 // One workgroup per (batch row, chunk, channel group).
 //   BWD_ADJOINT (chunks 1 ..): the adjoint recurrence alone over the chunk from a zero
 //       incoming adjoint; writes the adjoint it hands to the previous chunk and the chunk's
 //       sum of delta (its decay is exp(A sum delta)).  No state is needed for it.
-//   BWD_MAIN: the chunk's states from its carried-in state (checkpoint every 16 tokens), then
+//   BWD_MAIN, BWD_MAIN_EULER (ZOH or first-order coefficients, fixed at compile time): the
+//       chunk's states from its carried-in state (checkpoint every 16 tokens), then
 //       the tiles backwards from the chunk's incoming adjoint, with every gradient.
 template <typename IO, int SL, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdMinWaves)))
@@ -130,7 +131,10 @@ void bwd_kernel(BwdParams p) {
   const int64_t D = p.D, N = p.N, L = p.L;
   const int64_t d0 = g * CWG, d = d0 + cw;
   const bool dvalid = d < D;
-  const bool sp = p.softplus != 0, first = p.euler != 0, gated = p.z != nullptr;
+  // first order (Bbar = delta B): a template constant on the main pass, where it selects
+  // terms per state and token
+  const bool sp = p.softplus != 0, gated = p.z != nullptr;
+  const bool first = MODE == BWD_ADJOINT ? p.euler != 0 : MODE == BWD_MAIN_EULER;
   const int64_t l_begin = int64_t(chunk) * p.chunk_len;
   const int64_t l_end = (l_begin + p.chunk_len < L) ? l_begin + p.chunk_len : L;
   const int64_t ntiles = (l_end - l_begin + kBTile - 1) / kBTile;      // tiles of this chunk
@@ -204,7 +208,7 @@ void bwd_kernel(BwdParams p) {
       xB[r] = B_b[(l0 + jb) * p.B_sl + bnq];
       if (all) xC[r] = C_b[(l0 + jb) * p.C_sl + bnq];
     }
-    if (all && MODE == BWD_MAIN) {
+    if (all && MODE != BWD_ADJOINT) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) xH[i] = ck_b[t * D * N + ck_d + nq[i]];
     }
@@ -529,7 +533,7 @@ hipError_t launch_bwd_io(const BwdParams& p, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_bwd_m<IO, BWD_MAIN>(p, stream);
+  return p.euler ? launch_bwd_m<IO, BWD_MAIN_EULER>(p, stream) : launch_bwd_m<IO, BWD_MAIN>(p, stream);
 }
 
 }  // namespace
