@@ -567,6 +567,13 @@ __device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, Nn>(f); }
 // (a channel block starts 8 banks after the previous one), hit distinct banks.
 __device__ __forceinline__ int part_pos(int r, int j) { return r * 16 + 4 * ((j >> 2) ^ ((r >> 1) & 3)) + (j & 3); }
 
+// The value lane L of this lane's 16-lane row holds (DPP row_newbcast; folded into the VOP2
+// instruction that consumes it).
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + L, 0xF, 0xF, false));
+}
+
 // Workgroup barrier for LDS traffic only: this wavefront's LDS accesses have completed and
 // every wavefront has arrived.  Global loads stay in flight (no vmcnt wait).
 __device__ __forceinline__ void block_lds_sync() {
@@ -768,16 +775,30 @@ void scan_kernel_coop(ScanParams p) {
 
   // ---- steps: rd(q, grp) reads group grp's
   // operands of the tile in buffer q into register slot grp & 1; cmp(grp) runs its steps
-  // and writes its four partial readouts.
+  // and writes its four partial readouts.  Selective coefficients: the 16 lanes of a
+  // channel form one DPP row, and lane s holds u and delta of the tile's token s (one
+  // 4-byte LDS read each per tile, at group 0); step j of group grp takes them from lane
+  // 4 grp + j of the row by a row broadcast folded into the multiply that consumes them.
+  // A broadcast operand costs issue time of its own, which the LDS bandwidth saved pays for
+  // only where both u and delta are broadcast: with zero rates or first-order coefficients
+  // (ZERO) delta also feeds an FMA, which cannot take one, so there (measured) and for
+  // time-invariant coefficients u and delta are read four tokens at a time.
   float dsum = 0.f;
   float* const prow = sP + c * kChanP;
   const int cw = 4 * w + c;                  // step channel within the workgroup
   float4 rU4[2], rD4[2], rB4[2][K], rC4[2][K];
-  auto rd = [&](int q, int grp) __attribute__((always_inline)) {
+  float rU1 = 0.f, rD1 = 0.f;
+  auto rd = [&](int q, auto grp_tag, auto zero_tag) __attribute__((always_inline)) {
+    constexpr int grp = decltype(grp_tag)::value;
+    constexpr bool ZERO = decltype(zero_tag)::value;
     const int sl = grp & 1;
-    rU4[sl] = *reinterpret_cast<const float4*>(bufU(q) + cw * kRowPad + 4 * grp);
+    if (TI || ZERO) rU4[sl] = *reinterpret_cast<const float4*>(bufU(q) + cw * kRowPad + 4 * grp);
     if (!TI) {
-      rD4[sl] = *reinterpret_cast<const float4*>(bufD(q) + cw * kRowPad + 4 * grp);
+      if (grp == 0 && !ZERO) {
+        rU1 = bufU(q)[cw * kRowPad + s];
+        rD1 = bufD(q)[cw * kRowPad + s];
+      }
+      if (ZERO) rD4[sl] = *reinterpret_cast<const float4*>(bufD(q) + cw * kRowPad + 4 * grp);
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         rB4[sl][k] = *reinterpret_cast<const float4*>(bufB(q) + (s + S * k) * kRowPad + 4 * grp);
@@ -785,33 +806,37 @@ void scan_kernel_coop(ScanParams p) {
       }
     }
   };
-  auto cmp = [&](int grp, auto zero_tag, auto full_tag, int nsteps) __attribute__((always_inline)) {
+  auto cmp = [&](auto grp_tag, auto zero_tag, auto full_tag, int nsteps) __attribute__((always_inline)) {
+    constexpr int grp = decltype(grp_tag)::value;
     constexpr bool ZERO = decltype(zero_tag)::value;
     constexpr bool FULL = decltype(full_tag)::value;
-    const int sl = grp & 1;
-    const float uu[4] = {rU4[sl].x, rU4[sl].y, rU4[sl].z, rU4[sl].w};
-    const float dd[4] = {rD4[sl].x, rD4[sl].y, rD4[sl].z, rD4[sl].w};
+    constexpr int sl = grp & 1;
     float pacc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (!FULL && 4 * grp + j >= nsteps) break;
+    static_for<4>([&](auto j_tag) __attribute__((always_inline)) {
+      constexpr int j = decltype(j_tag)::value;
+      if (!FULL && 4 * grp + j >= nsteps) return;           // ragged tile: steps past its end
       float acc = 0.f;
       if (TI) {
+        const float uu = j == 0 ? rU4[sl].x : j == 1 ? rU4[sl].y : j == 2 ? rU4[sl].z : rU4[sl].w;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          h[k] = fmaf(Ab[k], h[k], uu[j]);                        // g = Abar g + u
+          h[k] = fmaf(Ab[k], h[k], uu);                           // g = Abar g + u
           if (READOUT) acc = fmaf(CB[k], h[k], acc);              // y += C Bbar g
         }
       } else {
-        if (MODE == MODE_STATE) dsum += dd[j];
+        const float uu = !ZERO ? row_bcast<4 * grp + j>(rU1)
+                               : j == 0 ? rU4[sl].x : j == 1 ? rU4[sl].y : j == 2 ? rU4[sl].z : rU4[sl].w;
+        const float dd = !ZERO ? row_bcast<4 * grp + j>(rD1)
+                               : j == 0 ? rD4[sl].x : j == 1 ? rD4[sl].y : j == 2 ? rD4[sl].z : rD4[sl].w;
+        if (MODE == MODE_STATE) dsum += dd;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
           const float4 b4 = rB4[sl][k];
           const float bj = j == 0 ? b4.x : j == 1 ? b4.y : j == 2 ? b4.z : b4.w;
-          const float ab = __builtin_amdgcn_exp2f(dd[j] * A2[k]);  // Abar = exp(delta A)
+          const float ab = __builtin_amdgcn_exp2f(dd * A2[k]);     // Abar = exp(delta A)
           float f = fmaf(ab, iA[k], -iA[k]);                       // (Abar - 1)/A
-          if (ZERO) f = fmaf(dd[j], zf[k], f);                      // A == 0: delta
-          h[k] = fmaf(ab, h[k], f * (bj * uu[j]));                  // h = Abar h + Bbar u
+          if (ZERO) f = fmaf(dd, zf[k], f);                         // A == 0: delta
+          h[k] = fmaf(ab, h[k], f * (bj * uu));                     // h = Abar h + Bbar u
           if (READOUT) {
             const float4 c4 = rC4[sl][k];
             const float cj = j == 0 ? c4.x : j == 1 ? c4.y : j == 2 ? c4.z : c4.w;
@@ -820,7 +845,7 @@ void scan_kernel_coop(ScanParams p) {
         }
       }
       pacc[j] = acc;
-    }
+    });
     if (READOUT)
       *reinterpret_cast<float4*>(prow + s * 16 + 4 * (grp ^ ((s >> 1) & 3))) =
           make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
@@ -860,6 +885,10 @@ void scan_kernel_coop(ScanParams p) {
   auto region = [] () __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
 
   using I0 = std::integral_constant<int, 0>;
+  using G0 = std::integral_constant<int, 0>;
+  using G1 = std::integral_constant<int, 1>;
+  using G2 = std::integral_constant<int, 2>;
+  using G3 = std::integral_constant<int, 3>;
   using true_t = std::integral_constant<bool, true>;
   using false_t = std::integral_constant<bool, false>;
   auto mod3 = [] (int64_t t) __attribute__((always_inline)) { return int(t % 3); };
@@ -874,22 +903,22 @@ void scan_kernel_coop(ScanParams p) {
     if (FIN) fin_read(qm);                             // tile t-1
     if (YST) y_store(t - 2, int(t & 1));               // tile t-2
     order_lds();
-    rd(q0, 0);
+    rd(q0, G0{}, zero_tag);
     stage(set_tag, q1);                                // tile t+1
     issue(t + 1 + NS, set_tag);
     region();
-    rd(q0, 1);
-    cmp(0, zero_tag, true_t{}, kTile);
+    rd(q0, G1{}, zero_tag);
+    cmp(G0{}, zero_tag, true_t{}, kTile);
     if (FIN) fin_sum();
     region();
-    rd(q0, 2);
-    cmp(1, zero_tag, true_t{}, kTile);
+    rd(q0, G2{}, zero_tag);
+    cmp(G1{}, zero_tag, true_t{}, kTile);
     if (FIN) fin_out(int((t - 1) & 1));
     region();
-    rd(q0, 3);
-    cmp(2, zero_tag, true_t{}, kTile);
+    rd(q0, G3{}, zero_tag);
+    cmp(G2{}, zero_tag, true_t{}, kTile);
     region();
-    cmp(3, zero_tag, true_t{}, kTile);
+    cmp(G3{}, zero_tag, true_t{}, kTile);
   };
   // NS iterations from t (t mod NS == 2 mod NS), each only while t < nfull when GUARD.
   auto block = [&](int64_t t, auto zero_tag, auto guard_tag) __attribute__((always_inline)) {
@@ -923,11 +952,10 @@ void scan_kernel_coop(ScanParams p) {
       if (last_steps > 0) {
         block_lds_sync();
         const int qr = mod3(nfull);
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          rd(qr, grp);
-          cmp(grp, zero_tag, false_t{}, last_steps);
-        }
+        static_for<4>([&](auto g_tag) __attribute__((always_inline)) {
+          rd(qr, g_tag, zero_tag);
+          cmp(g_tag, zero_tag, false_t{}, last_steps);
+        });
       }
       return;
     }
@@ -939,11 +967,10 @@ void scan_kernel_coop(ScanParams p) {
     order_lds();
     if (last_steps > 0) {
       const int qr = mod3(nfull);
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        rd(qr, grp);
-        cmp(grp, zero_tag, false_t{}, last_steps);
-      }
+      static_for<4>([&](auto g_tag) __attribute__((always_inline)) {
+        rd(qr, g_tag, zero_tag);
+        cmp(g_tag, zero_tag, false_t{}, last_steps);
+      });
     }
     if (nfull > 0) {
       fin_sum();
