@@ -114,8 +114,11 @@ void bwd_kernel(BwdParams p) {
   __shared__ __align__(16) float sCq[kBTile][kBCRow];
   __shared__ __align__(16) float sBC[4][2][kBTile][NP];   // each wavefront's dB / dC sums
   // each wavefront's per-channel dB / dC terms of four tokens, summed over its channels
-  // every fourth token
-  __shared__ __align__(16) float sRed[4][2][4][CW][NP];
+  // every fourth token.  One read instruction of the sum covers 4 (SL = 4) or 2 (SL = 8)
+  // tokens' blocks, which unpadded sit 1 KB apart in the same banks: those blocks are padded
+  // by 16 floats (with SL = 16 a read covers one block and the padding would cost occupancy)
+  constexpr int kRedTok = CW * NP + (SL < 16 ? 16 : 0);
+  __shared__ __align__(16) float sRed[4][2][4][kRedTok];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -421,8 +424,8 @@ void bwd_kernel(BwdParams p) {
           if (dz_b != nullptr) put(dz_b + l * D, gz);
         }
         // this lane's dB / dC terms; every fourth token the wavefront sums its channels
-        *reinterpret_cast<float4*>(&sRed[w][0][j & 3][c][4 * s]) = make_float4(pb[0], pb[1], pb[2], pb[3]);
-        *reinterpret_cast<float4*>(&sRed[w][1][j & 3][c][4 * s]) = make_float4(pc[0], pc[1], pc[2], pc[3]);
+        *reinterpret_cast<float4*>(&sRed[w][0][j & 3][c * NP + 4 * s]) = make_float4(pb[0], pb[1], pb[2], pb[3]);
+        *reinterpret_cast<float4*>(&sRed[w][1][j & 3][c * NP + 4 * s]) = make_float4(pc[0], pc[1], pc[2], pc[3]);
       }
       if (j % 4 == 0) {
         __builtin_amdgcn_sched_barrier(0);
@@ -434,7 +437,7 @@ void bwd_kernel(BwdParams p) {
           const int arr = o / (4 * NP), jj = (o / NP) % 4, n = o % NP;
           float acc = 0.f;
 #pragma unroll
-          for (int cc = 0; cc < CW; ++cc) acc += sRed[w][arr][jj][cc][n];
+          for (int cc = 0; cc < CW; ++cc) acc += sRed[w][arr][jj][cc * NP + n];
           sBC[w][arr][j + jj][n] = acc;
         }
         wave_sync();
