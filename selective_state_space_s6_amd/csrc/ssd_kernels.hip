@@ -305,9 +305,8 @@ __device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f3
 }
 
 // One chunk's inputs as a thread holds them between the global loads and the LDS staging.
-// Thread t: C pieces t + 256 k (16 bytes each); tokens 8 (t >> 5) .. + 7 of B (states
-// (t & 31) N/32 .. + N/32 - 1) and of x (channels 2 (t & 31), + 1); the step size of token
-// t & 63.  The gate z (same tokens and channels as x) is loaded on its own, after the
+// Thread t < 256: C pieces t + 256 k (16 bytes each); tokens 8 (t >> 5) .. + 7 of B
+// (states (t & 31) N/32 .. + N/32 - 1) and of x (channels 2 (t & 31), + 1).  The gate z (same tokens and channels as x) is loaded on its own, after the
 // previous chunk's output, since only the output reads it.
 template <int N>
 struct ChunkRegs {
@@ -316,7 +315,6 @@ struct ChunkRegs {
   uint4 c[kCv];
   uint32_t b[8][kBw];
   uint32_t x[8];
-  uint32_t dt;
 };
 
 // Loads address memory as a chunk base common to the workgroup plus a 32-bit offset per
@@ -351,8 +349,15 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<N>& rg, const SsdParams& p,
     }
     rg.x[j] = *reinterpret_cast<const uint32_t*>(xc + (uint32_t(tc) * tok_stride + uint32_t(2 * lo)));
   }
-  const int t = tid & 63;
-  rg.dt = static_cast<const uint16_t*>(p.delta)[(b * L + l0) * H + h + uint32_t(min(t, rows - 1)) * uint32_t(H)];
+}
+
+// The step size of token (lane) of the chunk at l0, for the decay prefix every wavefront
+// forms (past the sequence end: the last token's, masked when used).
+__device__ __forceinline__ uint32_t load_dt(const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
+  const int64_t L = p.L, H = p.H;
+  const int rows = int(L - l0 < kT ? L - l0 : kT);
+  const int t = threadIdx.x & 63;
+  return static_cast<const uint16_t*>(p.delta)[(b * L + l0) * H + h + uint32_t(min(t, rows - 1)) * uint32_t(H)];
 }
 
 __device__ __forceinline__ void load_gate(uint32_t (&zr)[8], const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
@@ -387,8 +392,12 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <int N>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_fused_kernel(SsdParams p) {
+// NW = 4: wavefront w owns channel block w and all four 16-token output tiles of a chunk.
+// NW = 8 (for at most one workgroup per CU): wavefronts w and w + 4 share channel block w & 3,
+// each holding its state (updated identically by both), and split the output tiles
+// {0, 3} / {1, 2} (equal causal work); the first four stage the chunk and store the output.
+template <int N, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_fused_kernel(SsdParams p) {
   constexpr int kRowN = N + 8, kRowK = kT + 8, kRowY = kP + 4;
   constexpr int kKT = N / 16;                              // 16-state tiles of the state
   constexpr int kNV = N / 32;                              // states of B per thread
@@ -404,8 +413,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float A = p.A[h];
   const bool euler = p.euler != 0;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q = lane >> 4, r = lane & 15;
-  const int sb = tid >> 5, lo = tid & 31;                 // staging / output block of this thread
-  const int pc = 16 * w + r;                               // this lane's state/output column
+  const int sb = (tid >> 5) & 7, lo = tid & 31;           // staging / output block of this thread
+  const bool stager = NW == 4 || w < 4;                    // stages the chunk and stores y
+  const int half = NW == 4 ? 0 : (w >> 2);                 // output tiles {0, 3} or {1, 2} (NW = 8)
+  const int pc = 16 * (w & 3) + r;                         // this lane's state/output column
   uint16_t* const yg = static_cast<uint16_t*>(p.y);
   const bool gate = p.z != nullptr;
   const float d0 = p.Dskip != nullptr ? p.Dskip[h * kP + 2 * lo] : 0.f;
@@ -419,15 +430,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 4; ++i) hs[kt][i] = p.h0 != nullptr ? p.h0[(bh * kP + pc) * N + 16 * kt + 4 * q + i] : 0.f;
 
   ChunkRegs<N> rg;
-  load_chunk<N>(rg, p, b, h, 0);
+  if (stager) load_chunk<N>(rg, p, b, h, 0);
+  uint32_t dtr = load_dt(p, b, h, 0);
   uint32_t zr[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  if (gate) load_gate(zr, p, b, h, 0);
+  if (gate && stager) load_gate(zr, p, b, h, 0);
   const float invA = A != 0.f ? 1.f / A : 0.f;
   for (int64_t chunk = 0; chunk < p.n_chunks; ++chunk) {
     const int64_t l0 = chunk * kT;
     const int rows = int(L - l0 < kT ? L - l0 : kT);      // tokens of this chunk inside the sequence
     // the chunk's decay prefix, formed by every wavefront (token = lane)
-    const float dt = lane < rows ? bf16_lo(rg.dt) : 0.f;   // padded tokens: no step
+    const float dt = lane < rows ? bf16_lo(dtr) : 0.f;     // padded tokens: no step
     const float cum = wave_prefix_sum(dt * A);             // log of the decay since the chunk start
     const float a = __builtin_amdgcn_exp2f(dt * A * kLog2e);
     const float cc = (euler || A == 0.f) ? dt : (a - 1.f) * invA;
@@ -438,6 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       s_c[lane] = cc;
       s_w[lane] = __builtin_amdgcn_exp2f((cum_end - cum) * kLog2e) * cc;
     }
+    if (stager) {
 #pragma unroll
     for (int k = 0; k < ChunkRegs<N>::kCv; ++k) {
       const int i = tid + 256 * k, t = i / (N / 8), n0 = (i % (N / 8)) * 8;
@@ -467,8 +480,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       *reinterpret_cast<uint4*>(&sXT[2 * lo][8 * sb]) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
       *reinterpret_cast<uint4*>(&sXT[2 * lo + 1][8 * sb]) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
     }
+    }
     __syncthreads();                                      // C, B, x and the decay prefix are staged
-    {                                                      // w-scaled B^T rows, 8 tokens each
+    if (stager) {                                          // w-scaled B^T rows, 8 tokens each
       const float4 wa = *reinterpret_cast<const float4*>(&s_w[8 * sb]);
       const float4 wb = *reinterpret_cast<const float4*>(&s_w[8 * sb + 4]);
       const float wj[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
@@ -486,7 +500,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     __builtin_amdgcn_sched_barrier(0);                     // the staged registers are free: reuse them
-    if (chunk + 1 < p.n_chunks) load_chunk<N>(rg, p, b, h, l0 + kT);   // lands during the arithmetic
+    if (chunk + 1 < p.n_chunks) {                          // lands during the arithmetic
+      if (stager) load_chunk<N>(rg, p, b, h, l0 + kT);
+      dtr = load_dt(p, b, h, l0 + kT);
+    }
 
     // Y[:, cols] = e^cum (C H) + M X
     s16x4 hb[kKT];
@@ -498,6 +515,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int ti = 0; ti < kT / 16; ++ti) {
       __builtin_amdgcn_sched_barrier(0);                   // one row tile at a time: bounds the live set
+      if (NW == 8 && half != ((ti == 1 || ti == 2) ? 1 : 0)) continue;   // the other wavefront's tile
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
@@ -565,6 +583,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       hs[kt] = acc;
     }
     // feed-through, gate, bf16 stores: tokens 8 sb .. + 7, channels 2 lo, 2 lo + 1
+    if (stager) {
     uint16_t* const yc = yg + ((b * L + l0) * H + h) * kP;
     const uint4 xa = *reinterpret_cast<const uint4*>(&sXT[2 * lo][8 * sb]);      // x[8 sb + j][2 lo]
     const uint4 xb = *reinterpret_cast<const uint4*>(&sXT[2 * lo + 1][8 * sb]);  // x[8 sb + j][2 lo + 1]
@@ -591,8 +610,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[j];
     }
     if (gate && chunk + 1 < p.n_chunks) load_gate(zr, p, b, h, l0 + kT);   // lands during the next chunk
+    }
   }
-  if (p.last_state != nullptr) {
+  if (p.last_state != nullptr && half == 0) {                // (NW = 8: both halves hold the same state)
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
@@ -600,11 +620,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+constexpr int64_t kFusedWideMaxItems = 256;   // (batch, head) workgroups: one per CU of MI355X
+
 template <int N>
 hipError_t launch_ssd_n(const SsdParams& p, hipStream_t stream) {
   if (p.batch * p.H == 0) return hipSuccess;
   if (p.fused) {
-    hipLaunchKernelGGL(ssd_fused_kernel<N>, dim3(unsigned(p.batch * p.H)), dim3(256), 0, stream, p);
+    // up to one workgroup per CU: eight wavefronts, two per SIMD, split each chunk's output
+    // tiles; beyond that four, so that two workgroups share a CU
+    if (p.batch * p.H <= kFusedWideMaxItems)
+      hipLaunchKernelGGL((ssd_fused_kernel<N, 8>), dim3(unsigned(p.batch * p.H)), dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((ssd_fused_kernel<N, 4>), dim3(unsigned(p.batch * p.H)), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   const int64_t blocks = p.batch * p.H * p.n_chunks;
