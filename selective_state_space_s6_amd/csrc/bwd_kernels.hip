@@ -335,9 +335,6 @@ void bwd_kernel(BwdParams p) {
     gA[i] = 0.f;
   }
   float gD = 0.f, gbias = 0.f;
-  IO* const du_b = static_cast<IO*>(p.du) + b * L * D + d;
-  IO* const ddl_b = static_cast<IO*>(p.ddelta) + b * L * D + d;
-  IO* const dz_b = p.dz != nullptr ? static_cast<IO*>(p.dz) + b * L * D + d : nullptr;
   auto put = [&](IO* ptr, float v) __attribute__((always_inline)) {
     if constexpr (sizeof(IO) == 2) *ptr = bf16_rne(v);
     else *ptr = v;
@@ -369,7 +366,6 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int j = kBTile - 1; j >= 0; --j) {
       if (FULL || j < nt) {
-        const int64_t l = l_begin + t * kBTile + j;
         const float uu = sTok[0][cw][j], dt = sTok[1][cw][j], dyp = sTok[2][cw][j];
         const float gzf = sTok[3][cw][j], sig = sTok[4][cw][j];
         const float4 B4 = ld4(&sBq[j][4 * s]), C4 = ld4(&sCq[j][4 * s]);
@@ -418,10 +414,12 @@ void bwd_kernel(BwdParams p) {
         gD = fmaf(dyp, uu, gD);
         gbias += draw;
         __asm__ __volatile__("" : "+v"(gD), "+v"(gbias));
-        if (dvalid && s == 0) {
-          put(du_b + l * D, du);
-          put(ddl_b + l * D, draw);
-          if (dz_b != nullptr) put(dz_b + l * D, gz);
+        // the token's gradients leave with the tile, through its staged rows (this wavefront
+        // owns the channel's rows, and every lane has read them above)
+        if (s == 0) {
+          sTok[0][cw][j] = du;
+          sTok[1][cw][j] = draw;
+          sTok[2][cw][j] = gz;
         }
         // this lane's dB / dC terms; every fourth token the wavefront sums its channels
         *reinterpret_cast<float4*>(&sRed[w][0][j & 3][c * NP + 4 * s]) = make_float4(pb[0], pb[1], pb[2], pb[3]);
@@ -467,6 +465,23 @@ void bwd_kernel(BwdParams p) {
         gC[j * N + n] = ((sBC[0][1][j][n] + sBC[1][1][j][n]) + sBC[2][1][j][n]) + sBC[3][1][j][n];
       }
     }
+    // the tile's du, ddelta (and dz), coalesced over the workgroup's channels
+    {
+      const int64_t o = (b * L + l_begin + t * kBTile) * D + d0 + tc;
+      IO* const du_t = static_cast<IO*>(p.du) + o;
+      IO* const ddl_t = static_cast<IO*>(p.ddelta) + o;
+      IO* const dz_t = p.dz != nullptr ? static_cast<IO*>(p.dz) + o : nullptr;
+#pragma unroll
+      for (int r = 0; r < ET; ++r) {
+        const int j = tj0 + kTStep * r;
+        if (tcok && j < nt) {
+          put(du_t + j * D, sTok[0][tc][j]);
+          put(ddl_t + j * D, sTok[1][tc][j]);
+          if (dz_t != nullptr) put(dz_t + j * D, sTok[2][tc][j]);
+        }
+      }
+    }
+    if (t > 0) __syncthreads();                             // the next tile's staging reuses the rows
   }
 
   // ---- per-(b, chunk, d) results: partial sums over this batch row and chunk, and (first
