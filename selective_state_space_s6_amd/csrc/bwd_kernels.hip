@@ -142,6 +142,8 @@ void bwd_kernel(BwdParams p) {
   const int64_t l_end = (l_begin + p.chunk_len < L) ? l_begin + p.chunk_len : L;
   const int64_t ntiles = (l_end - l_begin + kBTile - 1) / kBTile;      // tiles of this chunk
   const int64_t tile0 = l_begin / kBTile;                               // its first tile overall
+  // the forward state pass checkpointed this chunk's tiles (from a zero start)
+  const bool ck_fwd = MODE != BWD_ADJOINT && p.ck_fwd != 0 && chunk < nc - 1;
   const int last_nt = int(l_end - l_begin - (ntiles - 1) * kBTile);
 
   float a[4], a2[4], iA[4], zf[4];
@@ -187,7 +189,7 @@ void bwd_kernel(BwdParams p) {
   // values are kept as loaded and only widened and range-masked when staged (any use at
   // load time would wait for them).
   IO xu[ET], xd[ET], xy[ET], xz[ET], xB[EB], xC[EB];
-  float xH[4];
+  float xH[4], xS = 0.f;
   int pend_nt = kBTile;                                     // valid tokens of the tile in flight
   auto issue = [&](int64_t t, bool all) __attribute__((always_inline)) {
     const int nt = t == ntiles - 1 ? last_nt : kBTile;
@@ -214,6 +216,7 @@ void bwd_kernel(BwdParams p) {
     if (all && MODE != BWD_ADJOINT) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) xH[i] = ck_b[t * D * N + ck_d + nq[i]];
+      if (ck_fwd) xS = p.ck_dsum[(b * p.ntiles + tile0 + t) * D + (dvalid ? d : D - 1)];
     }
   };
   auto stage = [&](bool all) __attribute__((always_inline)) {
@@ -280,8 +283,11 @@ void bwd_kernel(BwdParams p) {
     return;
   }
 
-  // ---- pass 1: forward, checkpoint at every tile start (the last tile is recomputed in pass 2)
-  float h[4];
+  // ---- pass 1: forward, checkpoint at every tile start (the last tile is recomputed in pass 2).
+  // Skipped where the forward state pass has written the chunk's tile states from a zero
+  // start (every chunk but the last): a tile's state is then that plus the carried-in state
+  // decayed over the chunk's tokens before the tile, exp(A sum delta).
+  float h[4], hc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float h_in = 0.f;
@@ -290,9 +296,10 @@ void bwd_kernel(BwdParams p) {
       else if (p.h0 != nullptr) h_in = p.h0[(b * D + d) * N + 4 * s + i];
     }
     h[i] = h_in;
+    hc[i] = h_in;
   }
-  if (ntiles > 1) issue(0, false);
-  for (int64_t t = 0; t < ntiles - 1; ++t) {
+  if (ntiles > 1 && !ck_fwd) issue(0, false);
+  for (int64_t t = 0; t < (ck_fwd ? 0 : ntiles - 1); ++t) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (nok[i]) ck_b[t * D * N + ck_d + 4 * s + i] = h[i];
@@ -317,9 +324,11 @@ void bwd_kernel(BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if (!ck_fwd) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (nok[i]) ck_b[(ntiles - 1) * D * N + ck_d + 4 * s + i] = h[i];
+    for (int i = 0; i < 4; ++i)
+      if (nok[i]) ck_b[(ntiles - 1) * D * N + ck_d + 4 * s + i] = h[i];
+  }
   __syncthreads();                                          // pass 1's LDS reads are done
 
   // ---- pass 2: tiles backwards, from the adjoint reaching the chunk's end
@@ -449,7 +458,8 @@ void bwd_kernel(BwdParams p) {
     stage(true);                         // the previous tile's LDS reads ended at its barrier
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = nok[i] ? xH[i] : 0.f;   // the tile's checkpoint
+    for (int i = 0; i < 4; ++i)                               // the tile's checkpoint
+      h[i] = !nok[i] ? 0.f : ck_fwd ? fmaf(__builtin_amdgcn_exp2f(a2[i] * xS), hc[i], xH[i]) : xH[i];
     if (t > 0) issue(t - 1, true);
     if (t == ntiles - 1 && last_nt < kBTile) tile(t, last_nt, std::false_type{});
     else tile(t, kBTile, std::true_type{});

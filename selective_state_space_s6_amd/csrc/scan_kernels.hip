@@ -894,10 +894,25 @@ void scan_kernel_coop(ScanParams p) {
   auto mod3 = [] (int64_t t) __attribute__((always_inline)) { return int(t % 3); };
 
   // One loop iteration for full tile t; SET1 = (t + 1) % NS is compile-time.
+  // state pass, optional: the state (from the chunk's zero start) and the running sum of
+  // delta at the start of tile t
+  auto checkpoint = [&](int64_t t) __attribute__((always_inline)) {
+    if constexpr (MODE == MODE_STATE && !TI) {
+      if (p.ckpt != nullptr && dvalid) {
+        const int64_t tile = l_begin / kTile + t;
+        float* const ck = p.ckpt + ((b * p.ck_ntiles + tile) * D + d) * N;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+          if (s + S * k < N) ck[s + S * k] = h[k];
+        if (s == 0) p.ck_dsum[(b * p.ck_ntiles + tile) * D + d] = dsum;
+      }
+    }
+  };
   auto iteration = [&](int64_t t, auto set_tag, auto zero_tag, auto fin_tag, auto yst_tag) __attribute__((always_inline)) {
     constexpr bool FIN = decltype(fin_tag)::value && READOUT;
     constexpr bool YST = decltype(yst_tag)::value && READOUT;
     const int q0 = mod3(t), q1 = mod3(t + 1), qm = mod3(t + 2);   // buffers of t, t+1, t-1
+    checkpoint(t);
     region();
     block_lds_sync();
     if (FIN) fin_read(qm);                             // tile t-1
@@ -950,6 +965,7 @@ void scan_kernel_coop(ScanParams p) {
     }
     if (!READOUT) {                                     // state pass: only the ragged tile is left
       if (last_steps > 0) {
+        checkpoint(nfull);
         block_lds_sync();
         const int qr = mod3(nfull);
         static_for<4>([&](auto g_tag) __attribute__((always_inline)) {

@@ -38,6 +38,11 @@ struct ScanParams {
   float* ws_dsum;       // chunked: [batch][D][n_chunks] sum of delta per chunk
   int32_t pipelined;    // 1: scan_kernel_coop (16 lanes per channel, D % 4 == 0, u/delta/z/y
                         //    rows and B/C rows readable four elements at a time); 0: scan_kernel
+  // state pass of scan_kernel_coop, selective coefficients, optional: the state from a zero
+  // start and the running sum of delta at the start of every 16-token tile of the chunk
+  float* ckpt;          // [batch][ck_ntiles][D][N], tile index l / 16, or null
+  float* ck_dsum;       // [batch][ck_ntiles][D]
+  int64_t ck_ntiles;
 };
 
 struct PrefixParams {
@@ -120,6 +125,10 @@ struct BwdParams {
   int32_t euler;
   int32_t dxf;
   int32_t softplus;
+  // 1: the forward state pass wrote each tile's zero-start state into ckpt and its running
+  // sum of delta into ck_dsum for every chunk but the last (which checkpoints itself)
+  int32_t ck_fwd;
+  const float* ck_dsum; // [batch][ntiles][D]
 };
 // lanes per channel of the backward kernel (4 states per lane): 4, 8 or 16
 int bwd_lanes_per_channel(int64_t N);

@@ -251,7 +251,7 @@ struct BwdPlan {
   int64_t groups = 0, ntiles = 0, chunk_len = 0;
   int32_t n_chunks = 1;
   size_t off_pB = 0, off_pC = 0, off_pA = 0, off_pD = 0, off_pbias = 0;
-  size_t off_state = 0, off_dsum = 0, off_adjG = 0, off_adjS = 0, off_adjin = 0, bytes = 0;
+  size_t off_state = 0, off_dsum = 0, off_adjG = 0, off_adjS = 0, off_adjin = 0, off_ckdsum = 0, bytes = 0;
 };
 
 // Main-pass workgroups resident on MI355X at once: 256 compute units x 2 (every main-pass
@@ -331,6 +331,8 @@ int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
     off += al(f * ncq * d.batch * d.dim);
     b.off_adjin = off;
     off += al(f * ncq * bdn);
+    b.off_ckdsum = off;                                   // running sum of delta at every tile start
+    off += al(f * d.batch * b.ntiles * d.dim);
   }
   b.bytes = (d.batch * d.seqlen > 0) ? off : 0;
   *out = b;
@@ -378,6 +380,13 @@ int bwd_run(const void* u, const void* delta, const float* delta_bias, const flo
     selscan::ScanParams f = scan_params(u, delta, delta_bias, A, B, C, Dskip, z, nullptr, h0, nullptr, d, plan.fwd);
     f.ws_state = reinterpret_cast<float*>(ws + plan.off_state);
     f.ws_dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
+    if (f.pipelined) {                                    // the state pass also checkpoints its tiles
+      f.ckpt = p.ckpt;
+      f.ck_dsum = reinterpret_cast<float*>(ws + plan.off_ckdsum);
+      f.ck_ntiles = plan.ntiles;
+      p.ck_fwd = 1;
+      p.ck_dsum = f.ck_dsum;
+    }
     e = selscan::launch_scan_pass(selscan::kPassState, bf16, false, plan.fwd.S, plan.fwd.K, f, stream);
     if (e != hipSuccess) return hip_fail(e);
     selscan::PrefixParams q{};
