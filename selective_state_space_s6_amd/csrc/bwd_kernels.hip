@@ -143,7 +143,7 @@ void bwd_kernel(BwdParams p) {
   const int64_t ntiles = (l_end - l_begin + kBTile - 1) / kBTile;      // tiles of this chunk
   const int64_t tile0 = l_begin / kBTile;                               // its first tile overall
   // the forward state pass checkpointed this chunk's tiles (from a zero start)
-  const bool ck_fwd = MODE != BWD_ADJOINT && p.ck_fwd != 0 && chunk < nc - 1;
+  const bool ck_fwd = MODE != BWD_ADJOINT && p.ck_fwd != 0;
   const int last_nt = int(l_end - l_begin - (ntiles - 1) * kBTile);
 
   float a[4], a2[4], iA[4], zf[4];
@@ -285,8 +285,8 @@ void bwd_kernel(BwdParams p) {
 
   // ---- pass 1: forward, checkpoint at every tile start (the last tile is recomputed in pass 2).
   // Skipped where the forward state pass has written the chunk's tile states from a zero
-  // start (every chunk but the last): a tile's state is then that plus the carried-in state
-  // decayed over the chunk's tokens before the tile, exp(A sum delta).
+  // start (a split sequence): a tile's state is then that plus the carried-in state decayed
+  // over the chunk's tokens before the tile, exp(A sum delta).
   float h[4], hc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

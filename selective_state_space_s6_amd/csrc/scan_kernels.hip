@@ -612,8 +612,9 @@ void scan_kernel_coop(ScanParams p) {
 
   const int64_t groups = (p.D + kCh - 1) / kCh;
   const int64_t wg = xcd_contiguous_block(blockIdx.x, gridDim.x);
-  // The state pass skips the last chunk: its end state is never carried anywhere.
-  const int nc_run = MODE == MODE_STATE ? p.n_chunks - 1 : p.n_chunks;
+  // The state pass skips the last chunk (its end state is never carried anywhere) unless
+  // it checkpoints every chunk's tiles.
+  const int nc_run = MODE == MODE_STATE && !p.state_all ? p.n_chunks - 1 : p.n_chunks;
   if (wg >= p.batch * nc_run * groups) return;               // whole workgroup exits together
   const int64_t g = wg % groups;
   const int64_t bc = wg / groups;
@@ -1268,7 +1269,7 @@ hipError_t launch_scan_coop(const ScanParams& p, hipStream_t stream) {
   }
   constexpr int kCh = coop_lds<K, TI, MODE>::kCh;
   const int64_t groups = (p.D + kCh - 1) / kCh;
-  const int64_t blocks = p.batch * (MODE == MODE_STATE ? p.n_chunks - 1 : p.n_chunks) * groups;
+  const int64_t blocks = p.batch * (MODE == MODE_STATE && !p.state_all ? p.n_chunks - 1 : p.n_chunks) * groups;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((scan_kernel_coop<IO, K, TI, MODE, DXF>), dim3(unsigned(blocks)), dim3(64 * coop_width<TI>::W),
                      lds, stream, p);

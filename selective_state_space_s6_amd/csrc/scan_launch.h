@@ -43,6 +43,8 @@ struct ScanParams {
   float* ckpt;          // [batch][ck_ntiles][D][N], tile index l / 16, or null
   float* ck_dsum;       // [batch][ck_ntiles][D]
   int64_t ck_ntiles;
+  int32_t state_all;    // scan_kernel_coop: the state pass runs the last chunk too (its end
+                        //    state is never carried; wanted for its checkpoints)
 };
 
 struct PrefixParams {
@@ -126,7 +128,7 @@ struct BwdParams {
   int32_t dxf;
   int32_t softplus;
   // 1: the forward state pass wrote each tile's zero-start state into ckpt and its running
-  // sum of delta into ck_dsum for every chunk but the last (which checkpoints itself)
+  // sum of delta into ck_dsum, for every chunk
   int32_t ck_fwd;
   const float* ck_dsum; // [batch][ntiles][D]
 };

@@ -384,6 +384,7 @@ int bwd_run(const void* u, const void* delta, const float* delta_bias, const flo
       f.ckpt = p.ckpt;
       f.ck_dsum = reinterpret_cast<float*>(ws + plan.off_ckdsum);
       f.ck_ntiles = plan.ntiles;
+      f.state_all = 1;                                    // the last chunk's tiles too
       p.ck_fwd = 1;
       p.ck_dsum = f.ck_dsum;
     }
