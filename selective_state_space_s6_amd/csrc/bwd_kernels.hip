@@ -23,16 +23,20 @@
 // sequence is walked in 16-token tiles whose operands the workgroup stages in LDS with
 // coalesced loads issued one tile ahead (the next tile's loads are in flight while the
 // current one computes).
-//   pass 1: the forward recurrence over the whole sequence, writing the state at the start
-//           of every tile (checkpoints) to the workspace;
+//   checkpoints: the state at the start of every tile, in the workspace.  With a split
+//           sequence the forward state pass writes them (each tile's state from the chunk's
+//           zero start, and the running sum of delta), and a tile's state is that plus the
+//           carried-in state decayed by exp(A sum delta); otherwise pass 1 here runs the
+//           forward recurrence over the sequence and writes them;
 //   pass 2: tiles from last to first: the tile's states are recomputed from its checkpoint
-//           into registers, then its tokens are walked backwards carrying lambda.
+//           into registers, then its tokens are walked backwards carrying lambda; du, ddelta
+//           and dz leave once per tile through the tile's staged rows.
 // Sums over states (du, ddelta, and the readout the gate's derivative needs) are DPP
 // reductions over the SL lanes of a channel.  Sums over channels (dB, dC) go over the
-// wavefront's channels by DPP row rotations and the gfx950 row swaps, over the workgroup's
-// wavefronts through LDS in a fixed order, and over channel groups in sum_partials_kernel,
-// which also sums the per-batch partials of dA, dDskip and the bias gradient.  Every sum
-// has a fixed order: results are deterministic.
+// wavefront's channels through a wavefront-private LDS block every fourth token, over the
+// workgroup's wavefronts through LDS in a fixed order, and over channel groups in
+// sum_partials_kernel, which also sums the per-batch partials of dA, dDskip and the bias
+// gradient.  Every sum has a fixed order: results are deterministic.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -62,20 +66,6 @@ __device__ __forceinline__ float chan_sum(float v) {
   if (SL >= 8) v += dpp_mov<0x141>(v);
   if (SL >= 16) v += dpp_mov<0x140>(v);
   return v;
-}
-
-// Sum over the channels of a wavefront for a fixed sub-lane (lanes s, s + SL, s + 2 SL, ...),
-// result in every such lane: rotations by 4 and 8 inside a 16-lane row (channels sharing the
-// row), then the gfx950 row swaps across rows (permlane16_swap pairs rows 0-1 and 2-3,
-// permlane32_swap the two halves).
-template <int SL>
-__device__ __forceinline__ float wave_chan_sum(float v) {
-  if (SL <= 4) v += dpp_mov<0x124>(v);    // row_ror:4
-  if (SL <= 8) v += dpp_mov<0x128>(v);    // row_ror:8
-  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 // at least this many wavefronts per SIMD (caps the registers)
