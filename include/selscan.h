@@ -271,9 +271,12 @@ int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace selective_scan_bwd needs for these dims (0 for an empty call
- * or invalid dims): the checkpoints, batch * ceil(seqlen/16) * dim * dstate floats, and the
- * per-16-channel-group partial sums of dB and dC, 2 * ceil(dim/16) * batch * seqlen * dstate
- * floats, plus O(batch * dim * dstate). */
+ * or invalid dims): the checkpoints, batch * ceil(seqlen/16) * dim * dstate floats; the
+ * per-channel-group partial sums of dB and dC (groups of 64, 32 or 16 channels for dstate up
+ * to 16, 32, 64), at most 2 * ceil(dim/16) * batch * seqlen * dstate floats; when the
+ * sequence is split into chunks, the running sums of delta at the checkpoints,
+ * batch * ceil(seqlen/16) * dim floats, and per-chunk states and adjoints,
+ * O(batch * dim * dstate * chunks). */
 size_t selective_scan_bwd_workspace_size(const selscan_dims* dims);
 
 /*
