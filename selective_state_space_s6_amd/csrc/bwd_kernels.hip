@@ -189,7 +189,7 @@ void bwd_kernel(BwdParams p) {
     for (int r = 0; r < ET; ++r) {
       const int j = tj0 + kTStep * r;
       const int jq = j < nt ? j : nt - 1;
-      xu[r] = u_b[(l0 + jq) * p.u_sl + tdq];
+      if (MODE != BWD_ADJOINT) xu[r] = u_b[(l0 + jq) * p.u_sl + tdq];   // the adjoint needs no u, B
       xd[r] = dl_b[(l0 + jq) * p.delta_sl + tdq];
       if (all) {
         xy[r] = dy_b[(l0 + jq) * p.dy_sl + tdq];
@@ -200,7 +200,7 @@ void bwd_kernel(BwdParams p) {
     for (int r = 0; r < EB; ++r) {
       const int j = bj0 + kBStep * r;
       const int jb = j < nt ? j : nt - 1;
-      xB[r] = B_b[(l0 + jb) * p.B_sl + bnq];
+      if (MODE != BWD_ADJOINT) xB[r] = B_b[(l0 + jb) * p.B_sl + bnq];
       if (all) xC[r] = C_b[(l0 + jb) * p.C_sl + bnq];
     }
     if (all && MODE != BWD_ADJOINT) {
@@ -216,7 +216,7 @@ void bwd_kernel(BwdParams p) {
       const int j = tj0 + kTStep * r;
       const bool ok = tcok && j < nt;
       const float vd = ok ? T::widen(xd[r]) : 0.f;
-      sTok[0][tc][j] = ok ? T::widen(xu[r]) : 0.f;
+      if (MODE != BWD_ADJOINT) sTok[0][tc][j] = ok ? T::widen(xu[r]) : 0.f;
       const float x = vd + tbias;
       sTok[1][tc][j] = p.dxf ? (sp ? softplus_f32(x) : x) : vd;
       if (all) {
@@ -229,15 +229,17 @@ void bwd_kernel(BwdParams p) {
           gzf = vy * sg * fmaf(zz, 1.f - sg, 1.f);
         }
         sTok[2][tc][j] = dyp;
-        sTok[3][tc][j] = gzf;
-        sTok[4][tc][j] = sp ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
+        if (MODE != BWD_ADJOINT) {                         // the gradients' factors: main pass only
+          sTok[3][tc][j] = gzf;
+          sTok[4][tc][j] = sp ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
+        }
       }
     }
 #pragma unroll
     for (int r = 0; r < EB; ++r) {
       const int j = bj0 + kBStep * r;
       const bool okb = bn < N && j < nt;
-      sBq[j][bn] = okb ? T::widen(xB[r]) : 0.f;
+      if (MODE != BWD_ADJOINT) sBq[j][bn] = okb ? T::widen(xB[r]) : 0.f;
       if (all) sCq[j][bn] = okb ? T::widen(xC[r]) : 0.f;
     }
   };
