@@ -360,14 +360,17 @@ __device__ __forceinline__ uint32_t load_dt(const SsdParams& p, int64_t b, int64
   return static_cast<const uint16_t*>(p.delta)[(b * L + l0) * H + h + uint32_t(min(t, rows - 1)) * uint32_t(H)];
 }
 
-__device__ __forceinline__ void load_gate(uint32_t (&zr)[8], const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
-  const int sb = threadIdx.x >> 5, lo = threadIdx.x & 31;
+// z of tokens 8 sb + j0 .. + JN - 1 (sb = (t >> 5) & 7), channels 2 lo, 2 lo + 1
+template <int JN>
+__device__ __forceinline__ void load_gate(uint32_t (&zr)[8], const SsdParams& p, int64_t b, int64_t h, int64_t l0,
+                                          int j0) {
+  const int sb = (threadIdx.x >> 5) & 7, lo = threadIdx.x & 31;
   const int64_t L = p.L, H = p.H;
   const int rows = int(L - l0 < kT ? L - l0 : kT);
   const uint16_t* const zc = static_cast<const uint16_t*>(p.z) + ((b * L + l0) * H + h) * kP;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = min(8 * sb + j, rows - 1);               // past the end: read in bounds, never stored
+  for (int j = 0; j < JN; ++j) {
+    const int t = min(8 * sb + j0 + j, rows - 1);          // past the end: read in bounds, never stored
     zr[j] = *reinterpret_cast<const uint32_t*>(zc + (uint32_t(t) * uint32_t(H * kP) + uint32_t(2 * lo)));
   }
 }
@@ -417,6 +420,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool stager = NW == 4 || w < 4;                    // stages the chunk and stores y
   const int half = NW == 4 ? 0 : (w >> 2);                 // output tiles {0, 3} or {1, 2} (NW = 8)
   const int pc = 16 * (w & 3) + r;                         // this lane's state/output column
+  // output block of this thread: tokens 8 sb + j0 .. + JN - 1 (NW = 8: the two halves of the
+  // workgroup take 4 tokens each)
+  constexpr int JN = NW == 8 ? 4 : 8;
+  const int j0 = NW == 8 ? 4 * (tid >> 8) : 0;
   uint16_t* const yg = static_cast<uint16_t*>(p.y);
   const bool gate = p.z != nullptr;
   const float d0 = p.Dskip != nullptr ? p.Dskip[h * kP + 2 * lo] : 0.f;
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   if (stager) load_chunk<N>(rg, p, b, h, 0);
   uint32_t dtr = load_dt(p, b, h, 0);
   uint32_t zr[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  if (gate && stager) load_gate(zr, p, b, h, 0);
+  if (gate) load_gate<JN>(zr, p, b, h, 0, j0);
   const float invA = A != 0.f ? 1.f / A : 0.f;
   for (int64_t chunk = 0; chunk < p.n_chunks; ++chunk) {
     const int64_t l0 = chunk * kT;
@@ -582,35 +589,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       acc = mfma(frag(&sBT[16 * kt + r][32 + 8 * q]), xf1, acc);
       hs[kt] = acc;
     }
-    // feed-through, gate, bf16 stores: tokens 8 sb .. + 7, channels 2 lo, 2 lo + 1
-    if (stager) {
+    // feed-through, gate, bf16 stores: tokens 8 sb + j0 .. + JN - 1, channels 2 lo, 2 lo + 1
     uint16_t* const yc = yg + ((b * L + l0) * H + h) * kP;
     const uint4 xa = *reinterpret_cast<const uint4*>(&sXT[2 * lo][8 * sb]);      // x[8 sb + j][2 lo]
     const uint4 xb = *reinterpret_cast<const uint4*>(&sXT[2 * lo + 1][8 * sb]);  // x[8 sb + j][2 lo + 1]
     uint32_t yo[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int jj = 0; jj < JN; ++jj) {
+      const int j = j0 + jj;
       const float2 yv = *reinterpret_cast<const float2*>(&sY[8 * sb + j][2 * lo]);
       float y0 = fmaf(d0, bf16_f(bf16_at(xa, j)), yv.x), y1 = fmaf(d1, bf16_f(bf16_at(xb, j)), yv.y);
       if (gate) {
-        const float z0 = bf16_lo(zr[j]), z1 = bf16_hi(zr[j]);
+        const float z0 = bf16_lo(zr[jj]), z1 = bf16_hi(zr[jj]);
         y0 *= z0 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z0 * kLog2e));
         y1 *= z1 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z1 * kLog2e));
       }
-      yo[j] = pack_bf16(y0, y1);
+      yo[jj] = pack_bf16(y0, y1);
     }
     if (rows == kT) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[j];
+      for (int jj = 0; jj < JN; ++jj)
+        *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j0 + jj) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[jj];
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (8 * sb + j < rows)
-          *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[j];
+      for (int jj = 0; jj < JN; ++jj)
+        if (8 * sb + j0 + jj < rows)
+          *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j0 + jj) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[jj];
     }
-    if (gate && chunk + 1 < p.n_chunks) load_gate(zr, p, b, h, l0 + kT);   // lands during the next chunk
-    }
+    if (gate && chunk + 1 < p.n_chunks) load_gate<JN>(zr, p, b, h, l0 + kT, j0);   // lands during the next chunk
   }
   if (p.last_state != nullptr && half == 0) {                // (NW = 8: both halves hold the same state)
 #pragma unroll
