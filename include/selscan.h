@@ -327,7 +327,7 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
 /* Workspace bytes of selective_scan_ssd_fwd (0 for an empty call, invalid dims or the
  * on-chip path): for the chunk-parallel path, per (batch row, head, 64-token chunk) one fp32
  * [dstate][headdim] chunk state, one decay, and one bf16 carried-in state.  The automatic
- * path takes the on-chip one when batch * nheads >= 112 (measured crossover on MI355X). */
+ * path takes the on-chip one when batch * nheads >= 96 (measured crossover on MI355X). */
 size_t selective_scan_ssd_workspace_size(const selscan_ssd_dims* dims);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

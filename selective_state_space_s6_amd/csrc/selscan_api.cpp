@@ -548,7 +548,7 @@ int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias
   return st;
 }
 
-constexpr int64_t kSsdFusedMinItems = 112;   // (batch, head) workgroups from which the on-chip path is faster
+constexpr int64_t kSsdFusedMinItems = 96;    // (batch, head) workgroups from which the on-chip path is faster
 
 static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chunks, bool* fused) {
   if (!d) return SELSCAN_ERR_NULL;
