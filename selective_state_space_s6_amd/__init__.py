@@ -200,6 +200,16 @@ def make_dims(u, delta, A, B, C, z=None, y=None, *, path: str = "auto", chunk_le
     return d
 
 
+def _check_dskip(Dskip, D):
+    """Dskip is read as Dskip[d] for every channel d < D: anything but a contiguous float32
+    [D] GPU tensor is rejected before any launch."""
+    import torch
+    if Dskip is not None and (Dskip.dtype != torch.float32 or tuple(Dskip.shape) != (D,)
+                              or not Dskip.is_contiguous() or not Dskip.is_cuda):
+        raise ValueError("Dskip must be a contiguous float32 [D] GPU tensor (D = %d), got %s %s"
+                         % (D, tuple(Dskip.shape), Dskip.dtype))
+
+
 def _check_bias(delta_bias, D):
     import torch
     if delta_bias is not None and (delta_bias.dtype != torch.float32 or tuple(delta_bias.shape) != (D,)
@@ -228,8 +238,9 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
             raise TypeError("%s has dtype %s, expected %s like u" % (name, t.dtype, io))
     if A.dtype != torch.float32 or not A.is_contiguous():
         raise TypeError("A must be a contiguous float32 [D, N] tensor")
-    if Dskip is not None and (Dskip.dtype != torch.float32 or not Dskip.is_contiguous()):
-        raise TypeError("Dskip must be a contiguous float32 [D] tensor")
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, L, D]")
+    _check_dskip(Dskip, int(u.shape[2]))
     for name, t in (("u", u), ("delta", delta), ("A", A), ("B", B), ("C", C), ("Dskip", Dskip), ("z", z), ("y", y),
                     ("last_state", last_state)):
         if t is not None and not t.is_cuda:
@@ -296,6 +307,7 @@ def selective_scan_step(u, delta, A, B, C, Dskip=None, z=None, y=None, *, state,
     if u.dim() != 2:
         raise ValueError("u must be [batch, D] (one token per batch row)")
     batch, D = (int(x) for x in u.shape)
+    _check_dskip(Dskip, D)
     if A.dim() != 2 or int(A.shape[0]) != D or A.dtype != torch.float32 or not A.is_contiguous():
         raise ValueError("A must be a contiguous float32 [D, N] tensor")
     N = int(A.shape[1])
@@ -305,8 +317,6 @@ def selective_scan_step(u, delta, A, B, C, Dskip=None, z=None, y=None, *, state,
     for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
         if t is not None and (t.dtype != io or not t.is_cuda):
             raise TypeError("%s must be a GPU tensor of dtype %s like u" % (name, io))
-    if Dskip is not None and (Dskip.dtype != torch.float32 or not Dskip.is_contiguous() or not Dskip.is_cuda):
-        raise TypeError("Dskip must be a contiguous float32 [D] GPU tensor")
     if (state.dtype != torch.float32 or not state.is_contiguous() or tuple(state.shape) != (batch, D, N)
             or not state.is_cuda):
         raise ValueError("state must be a contiguous float32 [batch, D, N] GPU tensor")
@@ -377,14 +387,15 @@ def selective_scan_bwd(u, delta, A, B, C, Dskip=None, z=None, *, dy, dlast_state
     omitted."""
     import torch
     io = u.dtype
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, L, D]")
+    batch, L, D = (int(x) for x in u.shape)
+    _check_dskip(Dskip, D)
     for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("dy", dy)):
         if t is not None and (t.dtype != io or not t.is_cuda):
             raise TypeError("%s must be a GPU tensor of dtype %s like u" % (name, io))
     if A.dtype != torch.float32 or not A.is_contiguous():
         raise TypeError("A must be a contiguous float32 [D, N] tensor")
-    if Dskip is not None and (Dskip.dtype != torch.float32 or not Dskip.is_contiguous()):
-        raise TypeError("Dskip must be a contiguous float32 [D] tensor")
-    batch, L, D = (int(x) for x in u.shape)
     N = int(A.shape[1])
     for name, t in (("dlast_state", dlast_state), ("initial_state", initial_state)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (batch, D, N)

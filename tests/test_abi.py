@@ -258,3 +258,25 @@ def test_ssd_struct_layout_matches_header():
     assert vals[0] == ctypes.sizeof(ss.SsdDims)
     for f, off in zip(fields, vals[1:]):
         assert getattr(ss.SsdDims, f).offset == off, f
+
+
+def test_binding_rejects_a_short_dskip_before_any_launch(monkeypatch):
+    """Every kernel reads Dskip[d] for all D channels: a Dskip of the wrong length (or not on
+    the GPU) is refused by the binding before the library is touched."""
+    import torch
+
+    def no_library():
+        raise AssertionError("the library was reached")
+
+    monkeypatch.setattr(ss, "lib", no_library)
+    batch, L, D, N = 2, 8, 4, 3
+    u = torch.zeros(batch, L, D)
+    A = -torch.ones(D, N)
+    B = torch.zeros(batch, L, N)
+    for bad in (torch.ones(D - 1), torch.ones(D + 1), torch.ones(D, 1), torch.ones(D)):   # the last: on the host
+        with pytest.raises(ValueError, match="Dskip"):
+            ss.selective_scan_fwd(u, u, A, B, B, bad)
+        with pytest.raises(ValueError, match="Dskip"):
+            ss.selective_scan_bwd(u, u, A, B, B, bad, dy=u)
+        with pytest.raises(ValueError, match="Dskip"):
+            ss.selective_scan_step(u[:, 0], u[:, 0], A, B[:, 0], B[:, 0], bad, state=torch.zeros(batch, D, N))
