@@ -184,6 +184,40 @@ def generate_ssd(name: str, *, seed: Optional[int] = None) -> SsdInputs:
     return SsdInputs(name=name, x=x, delta=delta, A=A, B=B, C=C, Dskip=np.ones(H * 64, np.float32), z=z)
 
 
+# Rates whose product with a step of 1e-3 is 1e-6 .. 1e-10, and zero: the ZOH input
+# coefficient (exp(delta a) - 1)/a cancels there in float32.
+SMALL_RATES = (-1e-3, -1e-5, -1e-7, 0.0)
+
+
+def small_rates(batch: int, L: int, D: int, N: int, io: str = "f32", seed: int = 31,
+                step: float = 1e-3, block: int = 64) -> Inputs:
+    """Inputs with rates near zero.  Channels come in blocks of ``block``; block k is of
+    kind k mod 3: (0) every rate small, cycling over SMALL_RATES by channel and state; (1)
+    small and canonical rates alternating over the states; (2) canonical rates only,
+    A[d, n] = -(n + 1).  Channels that own a small rate take the constant step ``step``, so
+    that every token rounds the same way; the others draw log-uniform steps in [1e-3, 1e-1].
+    u, B, C ~ N(0, 1); no feed-through and no gate, so y is the scan's term alone.  Draw
+    order: u, delta, B, C."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = rng.standard_normal((batch, L, D))
+    delta = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), (batch, L, D)))
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    A = -(np.arange(N, dtype=np.float64) + 1.0)[None, :].repeat(D, axis=0)
+    kind = (np.arange(D) // block) % 3
+    for d in range(D):
+        for n in range(N):
+            if kind[d] == 0 or (kind[d] == 1 and n % 2 == 0):
+                A[d, n] = SMALL_RATES[(d + n) % len(SMALL_RATES)]
+    delta[..., kind != 2] = step
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    u, delta, B, C, A = map(f32, (u, delta, B, C, A))
+    if io == "bf16":
+        u, delta, B, C = bf16_round(u), bf16_round(delta), bf16_round(B), bf16_round(C)
+    return Inputs(name="small_rates", io=io, ti=False, u=u, delta=delta, A=A, B=B, C=C, Dskip=None, z=None,
+                  want_last=True)
+
+
 def running_state(inp: Inputs, seed: int = 11, scale: float = 0.1) -> np.ndarray:
     """A seeded [batch, D, N] float32 state to continue from (the decode workload's running
     state): normal with standard deviation ``scale``."""

@@ -14,8 +14,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libselscan.so")
-SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "bwd_kernels.hip"),
-           os.path.join(CSRC, "ssd_kernels.hip"), os.path.join(CSRC, "selscan_api.cpp")]
+# the forward scan's kernels are instantiated per element type and pass in units of their
+# own (scan_inst_*.hip), which compile in parallel
+SCAN_UNITS = [os.path.join(CSRC, "scan_inst_%s_%s.hip" % (io, ps))
+              for io in ("f32", "bf16") for ps in ("single", "state", "apply")]
+SOURCES = SCAN_UNITS + [os.path.join(CSRC, "bwd_kernels.hip"), os.path.join(CSRC, "scan_kernels.hip"),
+                        os.path.join(CSRC, "ssd_kernels.hip"), os.path.join(CSRC, "selscan_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -32,17 +36,23 @@ def build(verbose: bool = False) -> str:
     objs = []
     builddir = os.path.join(PKG, "_build")
     os.makedirs(builddir, exist_ok=True)
-    procs = []
-    for src in SOURCES:                                       # the sources compile concurrently
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
+    pending = []
+    for src in SOURCES:
         obj = os.path.join(builddir, os.path.basename(src) + ".o")
-        lang = ["-x", "hip"]
-        cmd = [HIPCC] + COMMON_FLAGS + lang + ["-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        procs.append((subprocess.Popen(cmd), cmd))
+        pending.append(([HIPCC] + COMMON_FLAGS + ["-x", "hip", "-c", src, "-o", obj]))
         objs.append(obj)
-    for proc, cmd in procs:
+    running = []
+    while pending or running:                                 # at most `jobs` compiles at once
+        while pending and len(running) < jobs:
+            cmd = pending.pop(0)
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            running.append((subprocess.Popen(cmd), cmd))
+        proc, cmd = running.pop(0)
         if proc.wait() != 0:
+            for other, _ in running:
+                other.wait()
             raise subprocess.CalledProcessError(proc.returncode, cmd)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs

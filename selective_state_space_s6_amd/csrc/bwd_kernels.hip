@@ -79,16 +79,20 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-enum { BWD_ADJOINT = 0, BWD_MAIN = 1, BWD_MAIN_EULER = 2 };
+enum { BWD_ADJOINT = 0, BWD_MAIN = 1, BWD_MAIN_EULER = 2, BWD_MAIN_EXACT = 3 };
 
 // SL lanes per channel, 4 states per lane (state n = 4 s + i); 64 / SL channels per wavefront.
 // One workgroup per (batch row, chunk, channel group).
 //   BWD_ADJOINT (chunks 1 ..): the adjoint recurrence alone over the chunk from a zero
 //       incoming adjoint; writes the adjoint it hands to the previous chunk and the chunk's
 //       sum of delta (its decay is exp(A sum delta)).  No state is needed for it.
-//   BWD_MAIN, BWD_MAIN_EULER (ZOH or first-order coefficients, fixed at compile time): the
-//       chunk's states from its carried-in state (checkpoint every 16 tokens), then
-//       the tiles backwards from the chunk's incoming adjoint, with every gradient.
+//   BWD_MAIN, BWD_MAIN_EXACT, BWD_MAIN_EULER (the form of the input coefficient, fixed at
+//       compile time): the chunk's states from its carried-in state (checkpoint every 16
+//       tokens), then the tiles backwards from the chunk's incoming adjoint, with every
+//       gradient.  ZOH launches both BWD_MAIN (one fma from Abar and 1/A) and BWD_MAIN_EXACT
+//       (zoh_coeff_exact); a workgroup whose channels own a rate below kSmallRate (zero
+//       included) runs in the second, every other one in the first, and each exits at once
+//       in the other kernel.
 template <typename IO, int SL, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdMinWaves)))
 void bwd_kernel(BwdParams p) {
@@ -136,7 +140,7 @@ void bwd_kernel(BwdParams p) {
   const bool ck_fwd = MODE != BWD_ADJOINT && p.ck_fwd != 0;
   const int last_nt = int(l_end - l_begin - (ntiles - 1) * kBTile);
 
-  float a[4], a2[4], iA[4], zf[4];
+  float a[4], a2[4], iA[4];
   bool nok[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -146,8 +150,20 @@ void bwd_kernel(BwdParams p) {
     a2[i] = a[i] * kLog2e;
     const bool fo = a[i] == 0.f || first;               // c = delta
     iA[i] = fo ? 0.f : 1.0f / a[i];
-    zf[i] = (nok[i] && fo) ? 1.f : 0.f;
   }
+  if constexpr (MODE == BWD_MAIN || MODE == BWD_MAIN_EXACT) {
+    bool small = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) small |= nok[i] && fabsf(a[i]) < kSmallRate;
+    // workgroup-uniform, before any other barrier: the whole workgroup leaves together
+    if ((__syncthreads_or(small ? 1 : 0) != 0) != (MODE == BWD_MAIN_EXACT)) return;
+  }
+  // the input coefficient c = Bbar / B of state i at step size dt, Abar = ab
+  auto coeff = [&](float dt, float ab, int i) __attribute__((always_inline)) {
+    if constexpr (MODE == BWD_MAIN_EULER) return dt;
+    else if constexpr (MODE == BWD_MAIN_EXACT) return zoh_coeff_exact(dt, a[i], iA[i], ab);
+    else return fmaf(ab, iA[i], -iA[i]);
+  };
   const float dskip = (dvalid && p.Dskip != nullptr) ? p.Dskip[d] : 0.f;
   float* const ck_b = p.ckpt + (b * p.ntiles + tile0) * D * N;   // this chunk's checkpoints
   const int64_t ck_d = (dvalid ? d : D - 1) * N;
@@ -309,7 +325,7 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ab = __builtin_amdgcn_exp2f(dt * a2[i]);
-          const float cf = fmaf(dt, zf[i], fmaf(ab, iA[i], -iA[i]));
+          const float cf = coeff(dt, ab, i);
           h[i] = fmaf(ab, h[i], cf * (el(B4, i) * uu));
         }
       }
@@ -356,7 +372,7 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ab = __builtin_amdgcn_exp2f(dt * a2[i]);
-          const float cf = fmaf(dt, zf[i], fmaf(ab, iA[i], -iA[i]));
+          const float cf = coeff(dt, ab, i);
           h[i] = fmaf(ab, h[i], cf * (el(B4, i) * uu));
         }
       }
@@ -376,7 +392,7 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ab[i] = __builtin_amdgcn_exp2f(dt * a2[i]);
-          cf[i] = fmaf(dt, zf[i], fmaf(ab[i], iA[i], -iA[i]));
+          cf[i] = coeff(dt, ab[i], i);
           // the state after token j: the one recorded before token j + 1 (h: after the tile)
           spart = fmaf(el(C4, i), j + 1 < kBTile ? hp[j + 1][i] : h[i], spart);
         }
@@ -553,7 +569,9 @@ hipError_t launch_bwd_io(const BwdParams& p, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return p.euler ? launch_bwd_m<IO, BWD_MAIN_EULER>(p, stream) : launch_bwd_m<IO, BWD_MAIN>(p, stream);
+  if (p.euler) return launch_bwd_m<IO, BWD_MAIN_EULER>(p, stream);
+  const hipError_t e = launch_bwd_m<IO, BWD_MAIN>(p, stream);
+  return e != hipSuccess ? e : launch_bwd_m<IO, BWD_MAIN_EXACT>(p, stream);
 }
 
 }  // namespace

@@ -28,6 +28,27 @@ __device__ __forceinline__ float step_size(float raw, float bias, bool sp) {
   return sp ? softplus_f32(x) : x;
 }
 
+// The zero-order-hold input coefficient (e^x - 1)/a, x = delta * a, of one state with rate
+// a != 0 ("state-space models" (aarnphm.xyz), section "From continuous time to tokens";
+// Algenta "Sequence and state-space models", ssm_discretize_b), given ab = e^x already
+// formed for the transition and ia = 1/a.  ab carries an error of about one ulp of 1
+// whatever x is, so ab - 1 loses relative accuracy as |x| shrinks; from |x| = 1/8 down the
+// coefficient is instead delta times the Taylor series of (e^x - 1)/x = 1 + x/2 + x^2/6 +
+// x^3/24 + x^4/120 (truncation below 5e-8 relative at |x| = 1/8), and above it (ab - 1)/a
+// is one fma, within about 1e-6 relative.  a == 0 (with ia == 0) gives x = 0: delta, the
+// coefficient's limit.
+__device__ __forceinline__ float zoh_coeff_exact(float dd, float a, float ia, float ab) {
+  const float x = dd * a;
+  const float ser = dd * fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
+  return fabsf(x) < 0.125f ? ser : fmaf(ab, ia, -ia);
+}
+
+// Rates below this magnitude (zero included) send a wavefront to the form above for every
+// step.  The one-fma form (ab - 1)/a alone is kept where every rate a wavefront owns is at
+// least this large: its relative error is about 2^-23 / |delta a|, 5e-4 at the smallest
+// step of the canonical initialisation (delta = 1e-3) and this rate, less for larger ones.
+constexpr float kSmallRate = 0.25f;
+
 // element types: per-token tensors travel as raw bit patterns (see the buffer loads in the
 // forward kernels) and are widened to fp32 when staged.
 

@@ -1,5 +1,5 @@
 // scan_launch.h -- internal interface between the C ABI (selscan_api.cpp) and the
-// kernels (scan_kernels.hip).  Not installed, not part of the ABI.
+// kernels (scan_kernels.h and the units that instantiate it).  Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -61,6 +61,13 @@ struct PrefixParams {
 void lanes_for_states(int64_t N, int* S, int* K);
 
 hipError_t launch_scan_pass(int pass, bool bf16, bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
+// one scan pass of one element type (scan_inst_<io>_<pass>.hip); launch_scan_pass picks one
+hipError_t launch_scan_f32_single(bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
+hipError_t launch_scan_f32_state(bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
+hipError_t launch_scan_f32_apply(bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
+hipError_t launch_scan_bf16_single(bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
+hipError_t launch_scan_bf16_state(bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
+hipError_t launch_scan_bf16_apply(bool ti, int S, int K, const ScanParams& p, hipStream_t stream);
 hipError_t launch_chunk_prefix(const PrefixParams& p, hipStream_t stream);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream);
 hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t stream);

@@ -77,7 +77,7 @@ __device__ __forceinline__ void chunk_decay(const uint16_t* delta, int64_t b, in
   }
   s_cum[lane] = x;
   const float a = __builtin_amdgcn_exp2f(dt * A * kLog2e);
-  s_c[lane] = (euler || A == 0.f) ? dt : (a - 1.f) / A;
+  s_c[lane] = euler ? dt : zoh_coeff_exact(dt, A, A != 0.f ? 1.f / A : 0.f, a);   // (a - 1)/A, exact near 0
 }
 
 // ---- kernel 1: chunk states S = B^T diag(w) X, w_s = exp(cum_end - cum_s) c_s, stored as
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float dt = lane < rows ? bf16_lo(dtr) : 0.f;     // padded tokens: no step
     const float cum = wave_prefix_sum(dt * A);             // log of the decay since the chunk start
     const float a = __builtin_amdgcn_exp2f(dt * A * kLog2e);
-    const float cc = (euler || A == 0.f) ? dt : (a - 1.f) * invA;
+    const float cc = euler ? dt : zoh_coeff_exact(dt, A, invA, a);   // (a - 1)/A, exact near 0
     const float cum_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
     __syncthreads();                                      // the previous chunk's LDS reads are done
     if (w == 0) {

@@ -175,3 +175,31 @@ def test_backward_full_size_sampled_channels():
         whole = g[k].cpu().numpy().astype(np.float64)
         summed = sum(pp[k].cpu().numpy().astype(np.float64) for pp in parts)
         assert rel_err(whole, summed) <= 1e-5, (k, rel_err(whole, summed))
+
+
+def test_backward_full_size_longctx_against_oracle():
+    """The long-context backward at full size (batch 4, L 16384, D 2560, N 16, bf16 I/O; the
+    planner splits the sequence into chunks), in the launch configuration the benchmark times:
+    du, ddelta, dz, dA and dDskip against the oracle on sampled channels over every batch row,
+    and dB and dC, sums over every channel, against the oracle over all channels of batch row 0
+    (rustytorch commit log: hand-written VJP of the selective scan)."""
+    import selective_state_space_s6_amd as ss
+    t = torch()
+    inp = s6_workloads.generate("longctx_bf16")
+    b, L, D, N = inp.shape
+    dy = s6_workloads.bf16_round(np.random.default_rng(4).standard_normal((b, L, D)).astype(np.float32))
+    g = ss.selective_scan_bwd(dev(inp.u, "bf16"), dev(inp.delta, "bf16"), t.from_numpy(inp.A).cuda(),
+                              dev(inp.B, "bf16"), dev(inp.C, "bf16"), t.from_numpy(inp.Dskip).cuda(),
+                              dev(inp.z, "bf16"), dy=dev(dy, "bf16"))
+    t.cuda.synchronize()
+    g = {k: v.float().cpu().numpy() for k, v in g.items()}
+    ch = s6_workloads.sample_channels(D, 16)
+    sub = s6_workloads.select_channels(inp, ch)
+    ref = oracle.bwd(sub.u, sub.delta, sub.A, sub.B, sub.C, sub.Dskip, sub.z, dy=np.ascontiguousarray(dy[..., ch]))
+    errs = {k: rel_err(g[k][..., ch] if k in ("du", "ddelta", "dz") else g[k][ch], ref[k])
+            for k in ("du", "ddelta", "dz", "dA", "dDskip")}
+    row = lambda a: np.ascontiguousarray(a[:1])
+    ref0 = oracle.bwd(row(inp.u), row(inp.delta), inp.A, row(inp.B), row(inp.C), inp.Dskip, row(inp.z), dy=row(dy))
+    for k in ("dB", "dC", "du", "ddelta", "dz"):
+        errs[k + "[row 0, all channels]"] = rel_err(g[k][:1], ref0[k])
+    check(errs, "bf16", "full/longctx")

@@ -176,3 +176,32 @@ def test_decode_loop_with_options_equals_scan():
     y_loop = t.stack(ys, dim=1)
     assert rel_err(y_loop.cpu().numpy(), y_scan.cpu().numpy()) <= 1e-5
     assert rel_err(state.cpu().numpy(), l_scan.cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("option", ["softplus", "euler"])
+def test_full_size_longctx_options(option):
+    """The long-context forward at full size in the benchmark's launch configuration, with the
+    fused step size softplus(raw + bias[d]) (TorchLean "Selective Mamba", step) or with the
+    first-order coefficient (Algenta "Sequence and state-space models",
+    mamba_selective_scan_step), against the oracle on sampled channels of every batch row."""
+    import dataclasses
+    import selective_state_space_s6_amd as ss
+    t = torch()
+    inp = s6_workloads.generate("longctx_bf16")
+    bias = None
+    if option == "softplus":
+        raw, bias = s6_workloads.raw_step_sizes(inp)
+        inp = dataclasses.replace(inp, delta=raw)
+    g = to_gpu(inp)
+    y, _ = ss.selective_scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], g["Dskip"], g["z"],
+                                 delta_bias=None if bias is None else t.from_numpy(bias).cuda(),
+                                 delta_softplus=option == "softplus", discretization=option if option == "euler" else "zoh")
+    t.cuda.synchronize()
+    ch = s6_workloads.sample_channels(inp.u.shape[2], 24)
+    sub = s6_workloads.select_channels(inp, ch)
+    y_ref, _ = oracle.fwd(sub.u, sub.delta, sub.A, sub.B, sub.C, sub.Dskip, sub.z,
+                          delta_bias=None if bias is None else np.ascontiguousarray(bias[ch]),
+                          delta_softplus=option == "softplus", euler=option == "euler", want_last=False)
+    e_y = rel_err(y.float().cpu().numpy()[..., ch], y_ref)
+    log_errors("full/longctx/%s" % option, y=e_y, io="bf16")
+    assert e_y <= TOL["bf16"], e_y
