@@ -89,7 +89,9 @@ enum selscan_status {
                                    code is available from selective_scan_last_hip_error() */
   SELSCAN_ERR_WORKSPACE = -6,   /* workspace pointer NULL or smaller than
                                    selective_scan_workspace_size() */
-  SELSCAN_ERR_ABI = -7          /* dims->abi_version != SELSCAN_ABI_VERSION */
+  SELSCAN_ERR_ABI = -7,         /* dims->abi_version != SELSCAN_ABI_VERSION */
+  SELSCAN_ERR_SCRATCH_LIMIT = -8 /* selective_scan_fwd_noalloc: the chunked path needs more than
+                                    SELSCAN_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 /* Which kernel schedule to run.  AUTO picks by shape; the others exist for tests and
@@ -214,6 +216,31 @@ int selective_scan_fwd_ex(const void* u, const void* delta, const float* delta_b
                           const void* B, const void* C, const float* Dskip, const void* z, void* y,
                           const float* initial_state, float* last_state, const selscan_dims* dims,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * selective_scan_fwd_noalloc -- selective_scan_fwd_ex for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * It allocates nothing: no hipMalloc / hipFree / stream-ordered allocation and no
+ * allocating library call.  When the chunked path runs, its scratch (each chunk's end
+ * state and step sum, then the carried-in states) is a device array inside the library,
+ * SELSCAN_NOALLOC_SCRATCH_BYTES per GPU, created when the library's code is loaded on that
+ * GPU and held until the process ends; its device address is looked up on the first call
+ * on each GPU (the GPU of `stream`).
+ *   Arguments as selective_scan_fwd_ex without the workspace pair; dims as for the
+ *   forward (selective_scan_workspace_size(dims) is the scratch a call uses).
+ *   Returns SELSCAN_ERR_SCRATCH_LIMIT, before anything is enqueued, when
+ *   selective_scan_workspace_size(dims) > SELSCAN_NOALLOC_SCRATCH_BYTES (use
+ *   selective_scan_fwd_ws or selective_scan_fwd_ex with a workspace instead); other errors
+ *   as selective_scan_fwd_ex.
+ * Every call on one GPU shares that GPU's array.  Nothing in it needs to start at zero
+ * (each call writes every slot it reads), but two calls whose execution overlaps on one
+ * GPU (different streams, or another thread's call) race on it: callers serialise them.
+ */
+#define SELSCAN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int selective_scan_fwd_noalloc(const void* u, const void* delta, const float* delta_bias,
+                               const float* A, const void* B, const void* C, const float* Dskip,
+                               const void* z, void* y, const float* initial_state,
+                               float* last_state, const selscan_dims* dims, void* stream);
 
 /*
  * selective_scan_step -- one recurrent decode step: the forward pass over a single token

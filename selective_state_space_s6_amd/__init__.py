@@ -33,6 +33,8 @@ SELSCAN_F32, SELSCAN_BF16 = 0, 1
 SELSCAN_OK = 0
 SELSCAN_ERR_NULL, SELSCAN_ERR_DIMS, SELSCAN_ERR_UNSUPPORTED = -1, -2, -3
 SELSCAN_ERR_ALIGN, SELSCAN_ERR_HIP, SELSCAN_ERR_WORKSPACE, SELSCAN_ERR_ABI = -4, -5, -6, -7
+SELSCAN_ERR_SCRATCH_LIMIT = -8
+NOALLOC_SCRATCH_BYTES = 64 << 20          # SELSCAN_NOALLOC_SCRATCH_BYTES
 PATHS = {"auto": 0, "single": 1, "chunked": 2}
 FLAG_SCALAR_IO = 0x100   # tests only: force the general per-element kernel
 DISCRETIZATIONS = {"zoh": 0, "euler": 1}
@@ -74,6 +76,7 @@ _SIGNATURES = [
     ("selective_scan_workspace_size", ctypes.c_size_t, [ctypes.POINTER(SelscanDims)]),
     ("selective_scan_fwd_ws", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
     ("selective_scan_fwd_ex", ctypes.c_int, [_VP] * 11 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
+    ("selective_scan_fwd_noalloc", ctypes.c_int, [_VP] * 11 + [ctypes.POINTER(SelscanDims), _VP]),
     ("selective_scan_step", ctypes.c_int, [_VP] * 10 + [ctypes.POINTER(SelscanDims), _VP]),
     ("selective_scan_bwd", ctypes.c_int, [_VP] * 20 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
     ("selective_scan_bwd_workspace_size", ctypes.c_size_t, [ctypes.POINTER(SelscanDims)]),
@@ -292,6 +295,45 @@ def selective_scan_fwd(u, delta, A, B, C, Dskip=None, z=None, y=None, last_state
         where = "selective_scan_fwd"
     if st != SELSCAN_OK:
         raise SelscanError(st, where)
+    return y, last_state
+
+
+def selective_scan_fwd_noalloc(u, delta, A, B, C, Dskip=None, z=None, *, y, last_state=None, initial_state=None,
+                               delta_bias=None, delta_softplus: bool = False, discretization: str = "zoh",
+                               path: str = "auto", chunk_len: int = 0, stream=None):
+    """The forward pass through selective_scan_fwd_noalloc, which allocates nothing: the
+    chunked path's scratch is the library's own per-GPU array (NOALLOC_SCRATCH_BYTES).  The
+    outputs ``y`` (and ``last_state`` if wanted) must be given; nothing is allocated here
+    either.  Arguments otherwise as selective_scan_fwd.  Calls that overlap on one GPU race
+    on the shared scratch.  Returns (y, last_state)."""
+    import torch
+    io = u.dtype
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, L, D]")
+    batch, L, D = (int(x) for x in u.shape)
+    _check_dskip(Dskip, D)
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z), ("y", y)):
+        if t is not None and (t.dtype != io or not t.is_cuda):
+            raise TypeError("%s must be a GPU tensor of dtype %s like u" % (name, io))
+    if A.dtype != torch.float32 or not A.is_contiguous() or not A.is_cuda:
+        raise TypeError("A must be a contiguous float32 [D, N] GPU tensor")
+    N = int(A.shape[1])
+    for name, t in (("last_state", last_state), ("initial_state", initial_state)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (batch, D, N)
+                              or not t.is_cuda):
+            raise ValueError("%s must be a contiguous float32 [batch, D, N] GPU tensor" % name)
+    _check_bias(delta_bias, D)
+    dims = make_dims(u, delta, A, B, C, z, y, path=path, chunk_len=chunk_len, discretization=discretization,
+                     delta_softplus=delta_softplus)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = lib().selective_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+                                          _ptr(Dskip), _ptr(z), _ptr(y), _ptr(initial_state), _ptr(last_state),
+                                          ctypes.byref(dims), ctypes.c_void_p(stream))
+    if st != SELSCAN_OK:
+        raise SelscanError(st, "selective_scan_fwd_noalloc")
     return y, last_state
 
 

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "scan_launch.h"
 
 namespace {
@@ -245,6 +247,65 @@ int fwd_impl(const void* u, const void* delta, const float* delta_bias, const fl
   return st;
 }
 
+// ---- the no-allocation forward (selective_scan_fwd_noalloc)
+// The chunked path's workspace lives in this file-scope device array, one copy per GPU that
+// loads the library, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is a stand-in, not a device address): the device address of
+// each GPU's copy is looked up once, with that GPU current, and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = SELSCAN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of the scratch array on the GPU that `stream` belongs to.
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return SELSCAN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e);
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e);
+    if (back != hipSuccess) return hip_fail(back);
+    if (ptr == nullptr) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SELSCAN_OK;
+}
+
+int fwd_noalloc(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B,
+                const void* C, const float* Dskip, const void* z, void* y, const float* h0, float* last_state,
+                const selscan_dims* dims, hipStream_t stream) {
+  Plan plan;
+  int st = make_plan(dims, &plan);
+  if (st != SELSCAN_OK) return st;
+  const bool need_ws = plan.chunked && dims->batch > 0 && dims->seqlen > 0;
+  if (!need_ws)
+    return fwd_impl(u, delta, delta_bias, A, B, C, Dskip, z, y, h0, last_state, dims, nullptr, 0, false, stream);
+  if (plan.ws_bytes > kScratchBytes) return SELSCAN_ERR_SCRATCH_LIMIT;
+  // argument errors are reported before the device is touched (fwd_impl repeats them)
+  st = check_pointers(u, delta, A, B, C, Dskip, z, y, last_state, dims->io_dtype, false);
+  if (st != SELSCAN_OK) return st;
+  if (h0 != nullptr && plan.ti) return SELSCAN_ERR_UNSUPPORTED;
+  if ((h0 != nullptr && !aligned(h0, 4)) || (delta_bias != nullptr && !aligned(delta_bias, 4)))
+    return SELSCAN_ERR_ALIGN;
+  void* ws = nullptr;
+  st = scratch_for_stream(stream, &ws);
+  if (st != SELSCAN_OK) return st;
+  return fwd_impl(u, delta, delta_bias, A, B, C, Dskip, z, y, h0, last_state, dims, ws, kScratchBytes, false,
+                  stream);
+}
+
 // ---- backward pass
 struct BwdPlan {
   Plan fwd;                   // the forward plan whose chunked state pass supplies the carries
@@ -475,6 +536,14 @@ int selective_scan_fwd_ex(const void* u, const void* delta, const float* delta_b
                   workspace_bytes, workspace == nullptr, static_cast<hipStream_t>(stream));
 }
 
+int selective_scan_fwd_noalloc(const void* u, const void* delta, const float* delta_bias, const float* A,
+                               const void* B, const void* C, const float* Dskip, const void* z, void* y,
+                               const float* initial_state, float* last_state, const selscan_dims* dims,
+                               void* stream) {
+  return fwd_noalloc(u, delta, delta_bias, A, B, C, Dskip, z, y, initial_state, last_state, dims,
+                     static_cast<hipStream_t>(stream));
+}
+
 int selective_scan_step(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B,
                         const void* C, const float* Dskip, const void* z, void* y, float* state,
                         const selscan_dims* dims, void* stream) {
@@ -643,6 +712,9 @@ const char* selective_scan_strerror(int status) {
     case SELSCAN_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case SELSCAN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case SELSCAN_ERR_ABI: return "selscan_dims.abi_version does not match the library";
+    case SELSCAN_ERR_SCRATCH_LIMIT:
+      return "the chunked path needs more scratch than the no-allocation entry point holds "
+             "(SELSCAN_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

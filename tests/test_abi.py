@@ -280,3 +280,27 @@ def test_binding_rejects_a_short_dskip_before_any_launch(monkeypatch):
             ss.selective_scan_bwd(u, u, A, B, B, bad, dy=u)
         with pytest.raises(ValueError, match="Dskip"):
             ss.selective_scan_step(u[:, 0], u[:, 0], A, B[:, 0], B[:, 0], bad, state=torch.zeros(batch, D, N))
+
+
+def call_noalloc(dims, u=FAKE, h0=None, bias=None):
+    return ss.lib().selective_scan_fwd_noalloc(u, FAKE, bias, FAKE, FAKE, FAKE, None, None, FAKE, h0, None,
+                                               ctypes.byref(dims), None)
+
+
+def test_noalloc_errors_before_the_device():
+    """The no-allocation forward refuses, on the host, a call whose chunked path needs more
+    scratch than its per-GPU array holds, and argument errors, before touching a GPU."""
+    big = ss.dims_init(ss.SELSCAN_F32, 64, 4096, 4096, 64)
+    big.path = ss.PATHS["chunked"]
+    big.chunk_len = 64
+    assert ss.workspace_size(big) > ss.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(big) == ss.SELSCAN_ERR_SCRATCH_LIMIT
+    assert "scratch" in ss.strerror(ss.SELSCAN_ERR_SCRATCH_LIMIT)
+    assert call_noalloc(good_dims(), u=None) == ss.SELSCAN_ERR_NULL
+    assert call_noalloc(good_dims(), u=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
+    assert call_noalloc(good_dims(dstate=0)) == ss.SELSCAN_ERR_DIMS
+    ti = ss.dims_init(ss.SELSCAN_F32, 2, 64, 8, 16, time_invariant=True)
+    ti.path = ss.PATHS["chunked"]
+    assert call_noalloc(ti, h0=FAKE) == ss.SELSCAN_ERR_UNSUPPORTED
+    assert call_noalloc(good_dims(), h0=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
+    assert call_noalloc(good_dims(batch=0)) == ss.SELSCAN_OK     # nothing to do, nothing touched
