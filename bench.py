@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--step-size given|softplus] [--discretization zoh|euler] [--backward]
+    python bench.py --microbench
 
 A step is one selective_scan_fwd call over the whole workload (every row of the hot
 path: discretisation, recurrence, readout, feed-through, gate, store) with its inputs
@@ -19,6 +20,16 @@ and lets the kernel apply softplus(raw + bias); --discretization euler uses the 
 input coefficient.  The defaults are the plain ZOH scan with given step sizes.
 --backward times selective_scan_bwd (all gradients, from a seeded dy) on the same workload
 instead of the forward pass.
+
+Timing: after the warm-up, the K timed calls run back to back between two device
+synchronisations (ms_per_step, value) with HIP events around each call on its stream (the
+kernel time the roofline uses: mean, median and minimum are reported).  Then K more calls are
+timed the same way, each after 512 MiB written to a scratch buffer outside the events, which
+evicts the L2 caches and the 256 MB Infinity Cache ("cold_cache").
+
+--microbench instead prints the issue-rate and bandwidth probes of libselscan_microbench.so
+(fp32 FMA and v_exp_f32 rates against wavefronts per SIMD, their overlap, streaming copy and
+write bandwidth, and the shader clock the GPU held), the practical roofs of the scan.
 """
 from __future__ import annotations
 
@@ -39,36 +50,44 @@ import s6_workloads  # noqa: E402
 
 METRIC = "scan elements/s (B*L*D*N per sec) + achieved HBM GB/s vs peak, 1 MI355X"
 HBM_PEAK_GBS = 8000.0            # MI355X published HBM3E bandwidth
-VALU_PEAK_TFLOPS = 157.3         # MI355X published fp32 vector peak (FMA = 2 flops)
+# fp32 vector ALU: 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz = 78.6 TFLOP/s issuing
+# one fp32 operation per lane per instruction.  The published 157.3 TFLOP/s counts packed fp32
+# (two operations per lane per instruction), which this build disables for every kernel, so
+# 78.6 is the ceiling the kernels can reach; the published figure is reported beside it.
+VALU_PEAK_TFLOPS = 78.6
+VALU_PUBLISHED_TFLOPS = 157.3
+FLUSH_BYTES = 512 << 20          # written between cold-cache calls: more than L2 + 256 MB MALL
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
-                  for f in ("scan_kernels.hip", "device_common.h")]
+                  for f in ("scan_kernels.h", "scan_kernels.hip", "device_common.h")]
 SSD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
                       for f in ("ssd_kernels.hip", "device_common.h")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
-                      for f in ("bwd_kernels.hip", "scan_kernels.hip", "device_common.h")]
+                      for f in ("bwd_kernels.hip", "scan_kernels.h", "scan_kernels.hip", "device_common.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "scan_counters.json")
 
-# Algorithmic ALU work, in FMA-slot units (one fp32 VALU op = 1 slot = 2 flop-equivalents;
-# a quarter-rate transcendental = 4 slots):
-#   per (b, l, d, n): delta*A (1) + exp (4) + (Abar-1)/A as one FMA (1) + B*u (1) + times (1)
-#                     + state FMA (1) + readout FMA (1)                               = 10
-#   per (b, l, d):    feed-through FMA (1); gate: -z*log2e (1) + exp (4) + 1+e (1) + rcp (4)
-#                     + z*r (1) + y*silu (1)                                          = 1 + 12
+# Algorithmic ALU work, in FMA-slot units (one fp32 VALU instruction per lane = 1 slot = 2
+# flop-equivalents).  The transcendentals (v_exp_f32, v_log_f32, v_rcp_f32) issue at half that
+# rate on this GPU (bench.py --microbench: 7.7 against 15.6 lanes per clock per SIMD with eight
+# wavefronts, and they overlap FMA issue only slightly), so each counts 2 slots:
+#   per (b, l, d, n): delta*A (1) + exp (2) + (Abar-1)/A as one FMA (1) + B*u (1) + times (1)
+#                     + state FMA (1) + readout FMA (1)                               = 8
+#   per (b, l, d):    feed-through FMA (1); gate: -z*log2e (1) + exp (2) + 1+e (1) + rcp (2)
+#                     + z*r (1) + y*silu (1)                                          = 1 + 8
 #   time-invariant:   per (b, l, d, n): state FMA (1) + readout FMA (1)               = 2
-#   first order (Euler), per (b, l, d, n): delta*A (1) + exp (4) + B*(delta u) (1) + state FMA (1)
-#                     + readout FMA (1) = 8, plus delta*u (1) per (b, l, d)
-#   softplus step size, per (b, l, d): + bias (1), |x|*log2e (1), exp (4), 1+e (1), log (4),
-#                     t-1 (1), rcp (4), two products (2), max (1), add (1)            = 20
-SLOTS_PER_ELEMENT = {"selective": 10, "time_invariant": 2, "euler": 8}
+#   first order (Euler), per (b, l, d, n): delta*A (1) + exp (2) + B*(delta u) (1) + state FMA (1)
+#                     + readout FMA (1) = 6, plus delta*u (1) per (b, l, d)
+#   softplus step size, per (b, l, d): + bias (1), |x|*log2e (1), exp (2), 1+e (1), log (2),
+#                     t-1 (1), rcp (2), two products (2), max (1), add (1)            = 14
+SLOTS_PER_ELEMENT = {"selective": 8, "time_invariant": 2, "euler": 6}
 SLOTS_PER_TOKEN_D = 1
-SLOTS_PER_TOKEN_GATE = 12
+SLOTS_PER_TOKEN_GATE = 8
 SLOTS_PER_TOKEN_EULER = 1
-SLOTS_PER_TOKEN_SOFTPLUS = 20
-#   backward, per (b, l, d, n): exp (4), c (1), h_t (2), readout (1), lambda (1), du (2),
-#                     ddelta (3), dc/da (3), dA (3), dB (1), dC (1), carry (1)        = 23
-#             per (b, l, d): gate and its derivative (about 16), Dskip terms (2)      = 18
-SLOTS_BWD_PER_ELEMENT = 23
-SLOTS_BWD_PER_TOKEN_D = 18
+SLOTS_PER_TOKEN_SOFTPLUS = 14
+#   backward, per (b, l, d, n): exp (2), c (1), h_t (2), readout (1), lambda (1), du (2),
+#                     ddelta (3), dc/da (3), dA (3), dB (1), dC (1), carry (1)        = 21
+#             per (b, l, d): gate and its derivative (about 12), Dskip terms (2)      = 14
+SLOTS_BWD_PER_ELEMENT = 21
+SLOTS_BWD_PER_TOKEN_D = 14
 
 
 def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool, bias: bool = False) -> int:
@@ -157,13 +176,62 @@ def measured_traffic(workload: str, per_launch_alg_bytes: int):
     return int(entry["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0, h0=None, bias=None, softplus=False,
-                 euler=False):
-    """The oracle (fp64, as it stands) on a bounded sample of the workload's channels,
-    timed on this host; scaled to elements/s.  ``h0``: initial state [batch, D, N];
-    ``bias``/``softplus``/``euler``: the step-size and discretisation options."""
+def host_cpu() -> dict:
+    """This host's processor and the threads the oracle may use: the CPUs this process may
+    run on, capped by OMP_NUM_THREADS where the environment sets the process's CPU share."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    nproc = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = nproc
+    threads = allowed
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        threads = min(threads, int(share))
+    return {"cpu_model": model, "nproc": nproc, "affinity": allowed, "omp_num_threads": share or None,
+            "threads": threads}
+
+
+def cpu_per_core(target_s: float = 1.5) -> dict:
+    """The oracle's forward on one thread, elements/s, on the small and Mamba-130M widths
+    workloads (the latter on a channel slice sized to about target_s)."""
     import oracle
-    cores = min(16, os.cpu_count() or 1)
+    out = {}
+    for name, D in (("small_f32", None), ("mamba130m_f32", 64)):
+        inp = s6_workloads.generate(name, D=D)
+        t0 = time.perf_counter()
+        oracle.fwd(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z, nthreads=1)
+        dt = time.perf_counter() - t0
+        if D is not None and dt < target_s:                       # grow the slice once
+            D = min(1536, max(64, int(64 * target_s / max(dt, 1e-3)) // 4 * 4))
+            inp = s6_workloads.generate(name, D=D)
+            t0 = time.perf_counter()
+            oracle.fwd(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z, nthreads=1)
+            dt = time.perf_counter() - t0
+        b, L, Dq, N = inp.shape
+        out[name] = {"value": b * L * Dq * N / dt, "unit": "elements/s",
+                     "sample": "%d x %d x %d x %d, %.2f s" % (b, L, Dq, N, dt)}
+    return out
+
+
+def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0, h0=None, bias=None, softplus=False,
+                 euler=False, per_core: bool = False):
+    """The oracle (fp64, as it stands) on a bounded sample of the workload's channels,
+    timed on this host on every thread the process may use; scaled to elements/s.  ``h0``:
+    initial state [batch, D, N]; ``bias``/``softplus``/``euler``: the step-size and
+    discretisation options.  ``per_core`` adds one-thread figures on two other workloads."""
+    import oracle
+    host = host_cpu()
+    cores = host["threads"]
     b, L, D, N = inp.shape
     oracle.build()
     nch = min(D, max(cores, 8))
@@ -181,9 +249,117 @@ def cpu_baseline(inp: s6_workloads.Inputs, target_s: float = 12.0, h0=None, bias
             break
         nch = min(D, int(nch * max(2.0, target_s / max(t_used, 1e-3))))
     elements = b * L * nch * N
-    return {"value": elements / t_used, "unit": "elements/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of %d channels (all %d batch rows x %d tokens x %d states), fp64 recurrence, %.1f s wall"
-                      % (nch, D, b, L, N, t_used)}
+    out = {"value": elements / t_used, "unit": "elements/s", "cores": cores, "kind": "oracle",
+           "sample": "%d of %d channels (all %d batch rows x %d tokens x %d states), fp64 recurrence, %.1f s wall"
+                     % (nch, D, b, L, N, t_used), "host": host}
+    if per_core:
+        out["per_core"] = cpu_per_core()
+    return out
+
+
+MICROBENCH_LIB = os.path.join(ROOT, "selective_state_space_s6_amd", "libselscan_microbench.so")
+SIMDS = 256 * 4                  # MI355X: 256 compute units of 4 SIMDs
+
+
+def run_microbench():
+    """The practical roofs, from libselscan_microbench.so (built with the scan's flags): fp32
+    FMA and v_exp_f32 issue rates against wavefronts per SIMD (8 independent chains per lane),
+    exp2/FMA overlap, streaming copy and write bandwidth, and the shader clock held meanwhile
+    (clock64 cycles against the constant-rate wall clock of the same wavefront)."""
+    import ctypes
+    import torch
+    torch.cuda.init()                                # the library binds to the runtime torch loaded
+    lib = ctypes.CDLL(MICROBENCH_LIB)
+    lib.selscan_mb_compute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]
+    lib.selscan_mb_bandwidth.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_float)]
+    wall_khz = lib.selscan_mb_wall_clock_khz()
+    chains_rounds = 8 * 8                            # operations per lane per loop iteration
+
+    def compute(kind, waves_per_simd, iters):
+        ms, cyc, tck = ctypes.c_float(), ctypes.c_uint64(), ctypes.c_uint64()
+        rc = lib.selscan_mb_compute(kind, 256 * waves_per_simd, iters, ctypes.byref(ms), ctypes.byref(cyc),
+                                    ctypes.byref(tck))
+        if rc != 0:
+            raise RuntimeError("microbench kind %d failed: %d (hip %d)" % (kind, rc, lib.selscan_mb_last_error()))
+        mhz = cyc.value / (tck.value / (wall_khz * 1e3)) / 1e6 if tck.value and wall_khz else float("nan")
+        lanes = 256 * waves_per_simd * 256 * iters * chains_rounds     # lane operations of one kind
+        per_clk = lanes / (ms.value * 1e-3) / (mhz * 1e6) / SIMDS
+        return {"waves_per_simd": waves_per_simd, "ms": round(ms.value, 4), "clock_mhz": round(mhz, 1),
+                "lane_ops_per_s": lanes / (ms.value * 1e-3), "lanes_per_clk_per_simd": round(per_clk, 3)}
+
+    out = {"fma": [compute(0, w, 4000) for w in (1, 2, 3, 4, 8)],
+           "exp2": [compute(1, w, 1000) for w in (1, 2, 3, 4, 8)]}
+    # overlap: exp2 and r fma per exp2 (8 chains of each), 4 wavefronts per SIMD; compare the
+    # time with the exp2 and fma runs of the same counts taken alone
+    fma4 = next(r for r in out["fma"] if r["waves_per_simd"] == 4)
+    exp4 = next(r for r in out["exp2"] if r["waves_per_simd"] == 4)
+    t_fma_op = fma4["ms"] / (256 * 4 * 256 * 4000 * chains_rounds)
+    t_exp_op = exp4["ms"] / (256 * 4 * 256 * 1000 * chains_rounds)
+    mix = []
+    for kind, ratio in ((2, 1), (3, 2), (4, 4), (5, 8)):
+        r = compute(kind, 4, 1000)
+        n = 256 * 4 * 256 * 1000 * chains_rounds
+        r.update(ratio=ratio, ms_if_serial=round(n * (t_exp_op + ratio * t_fma_op), 4),
+                 ms_if_overlapped=round(n * max(t_exp_op, ratio * t_fma_op), 4))
+        mix.append(r)
+    out["exp2_with_fma"] = mix
+    bw = []
+    for kind, name in ((0, "copy"), (1, "write")):
+        nbytes = 1 << 30
+        moved = nbytes * (2 if kind == 0 else 1)
+        for blocks in (1024, 4096, 16384, 65536):       # workgroups of a grid-stride loop
+            ms = ctypes.c_float()
+            if lib.selscan_mb_bandwidth(kind, nbytes, blocks, 5, ctypes.byref(ms)) != 0:
+                raise RuntimeError("bandwidth probe failed (hip %d)" % lib.selscan_mb_last_error())
+            bw.append({"probe": name, "workgroups": blocks, "bytes": moved, "ms": round(ms.value, 4),
+                       "gbs": round(moved / (ms.value * 1e-3) / 1e9, 1)})
+    out["bandwidth"] = bw
+    out["wall_clock_khz"] = wall_khz
+    print(json.dumps({"microbench": out}), flush=True)
+
+
+def time_calls(step, stream, steps: int, warmup: int) -> dict:
+    """Warm up, then time `steps` calls back to back (wall clock between device
+    synchronisations, and HIP events around each call on `stream`), then `steps` more calls
+    each after FLUSH_BYTES written to a scratch buffer outside the events."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    starts, ends = ev(), ev()
+    torch.cuda.synchronize()                     # one GPU: the barrier is the device synchronisation
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    warm = [a.elapsed_time(e) for a, e in zip(starts, ends)]
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    cstarts, cends = ev(), ev()
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            flush.fill_(float(i))
+            cstarts[i].record(stream)
+            step()
+            cends[i].record(stream)
+    torch.cuda.synchronize()
+    cold = [a.elapsed_time(e) for a, e in zip(cstarts, cends)]
+    del flush
+    return {"wall": wall, "warm": warm, "cold": cold}
+
+
+def timing_fields(tm: dict) -> dict:
+    """kernel_ms (mean of the back-to-back calls: the roofline's time), its median and
+    minimum, and the cold-cache statistics."""
+    w, c = np.asarray(tm["warm"]), np.asarray(tm["cold"])
+    return {"kernel_ms": float(w.mean()), "kernel_ms_median": float(np.median(w)), "kernel_ms_min": float(w.min()),
+            "cold_cache": {"flush_bytes": FLUSH_BYTES, "calls": int(c.size), "ms_mean": float(c.mean()),
+                           "ms_median": float(np.median(c)), "ms_min": float(c.min())}}
 
 
 def main():
@@ -203,6 +379,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--microbench", action="store_true",
+                    help="print the issue-rate and bandwidth probes (the practical roofs) instead")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -212,6 +390,8 @@ def main():
               "supported" % max(args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
+    if args.microbench:
+        return run_microbench()
     import torch
     import selective_state_space_s6_amd as ss
 
@@ -255,21 +435,9 @@ def main():
                               stream=stream.cuda_stream, delta_bias=bias, delta_softplus=softplus,
                               discretization=args.discretization)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    # one GPU: the barrier is the device synchronisation itself
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    tm = time_calls(step, stream, args.steps, args.warmup)
+    wall = tm["wall"]
+    launch_ms = float(np.mean(tm["warm"]))
 
     if args.copy_calibration:
         copy_calibration()
@@ -280,17 +448,8 @@ def main():
     slots = algorithmic_slots(inp, softplus=softplus, euler=euler)
     launch_s = launch_ms * 1e-3
     hbm_gbs = alg_bytes / launch_s / 1e9
-    alu_tflops = 2.0 * slots / launch_s / 1e12
     traffic = measured_traffic(args.workload + opts["suffix"], alg_bytes)
-    # the binding roof: the larger of the two lower bounds on time
-    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
-    t_alu = 2.0 * slots / (VALU_PEAK_TFLOPS * 1e12)
-    if t_alu >= t_hbm:
-        roof = {"bound": "alu", "achieved": round(alu_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(alu_tflops / VALU_PEAK_TFLOPS, 4), "traffic": traffic}
-    else:
-        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    roof = roofline(alg_bytes, slots, launch_s, traffic)        # the binding roof
 
     out = {
         "metric": METRIC,
@@ -309,7 +468,7 @@ def main():
                    "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
                    "last_state": want_last, "time_invariant": inp.ti, "path": "chunked" if chunked else "single",
                    "step_size": opts["step_size"], "discretization": args.discretization},
-        "kernel_ms": launch_ms,
+        **timing_fields(tm),
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": alg_bytes,
@@ -317,7 +476,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, bias=bias_np, softplus=softplus, euler=euler)
+        out["cpu_baseline"] = cpu_baseline(inp, bias=bias_np, softplus=softplus, euler=euler, per_core=True)
     print(json.dumps(out), flush=True)
 
 
@@ -358,20 +517,9 @@ def bench_backward(args, inp, bias_np, opts):
         ss.selective_scan_bwd(u, delta, A, B, C, Ds, z, dy=dy, delta_bias=bias, delta_softplus=softplus,
                               discretization=args.discretization, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+    tm = time_calls(step, stream, args.steps, args.warmup)
+    wall = tm["wall"]
+    launch_ms = float(np.mean(tm["warm"]))
     E = b * L * D * N
     alg = backward_bytes(inp)
     slots = SLOTS_BWD_PER_ELEMENT * E + SLOTS_BWD_PER_TOKEN_D * b * L * D
@@ -391,7 +539,7 @@ def bench_backward(args, inp, bias_np, opts):
         "config": {"workload": args.workload, "batch": b, "seq_len": L, "dim": D, "dstate": N, "io": io,
                    "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
                    "pass": "backward", "step_size": opts["step_size"], "discretization": args.discretization},
-        "kernel_ms": launch_ms,
+        **timing_fields(tm),
         "hbm_gbs": round(alg / (launch_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(alg / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": alg,
@@ -466,20 +614,9 @@ def bench_ssd(args):
         ss.selective_scan_ssd_fwd(x, dl, A, B, C, Ds, z, y=y, discretization=args.discretization,
                                   path=args.ssd_path, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+    tm = time_calls(step, stream, args.steps, args.warmup)
+    wall = tm["wall"]
+    launch_ms = float(np.mean(tm["warm"]))
     if args.copy_calibration:
         copy_calibration()
     E = b * L * H * P * N
@@ -511,7 +648,7 @@ def bench_ssd(args):
                    "io": "bf16", "state": "f32", "gate": True, "feedthrough": True, "chunk": SSD_CHUNK,
                    "discretization": args.discretization, "layer": "scalar decay per head (Mamba-2 SSD)",
                    "path": args.ssd_path},
-        "kernel_ms": launch_ms,
+        **timing_fields(tm),
         "hbm_gbs": round(alg / sec / 1e9, 1),
         "hbm_frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4),
         "mfma_tflops": round(fl / sec / 1e12, 2),
@@ -559,12 +696,18 @@ def copy_calibration():
 
 
 def roofline(alg_bytes: int, slots: int, seconds: float, traffic):
-    """The binding roof (the larger of the two lower bounds on time) and the fraction of it."""
+    """The binding roof (the larger of the two lower bounds on time) and the fraction of it.
+    The ALU roof is the non-packed fp32 ceiling (VALU_PEAK_TFLOPS); the published, packed
+    figure and the fraction of it are reported beside it."""
     hbm_gbs = alg_bytes / seconds / 1e9
     alu_tflops = 2.0 * slots / seconds / 1e12
     if 2.0 * slots / (VALU_PEAK_TFLOPS * 1e12) >= alg_bytes / (HBM_PEAK_GBS * 1e9):
         return {"bound": "alu", "achieved": round(alu_tflops, 2), "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(alu_tflops / VALU_PEAK_TFLOPS, 4), "traffic": traffic}
+                "frac": round(alu_tflops / VALU_PEAK_TFLOPS, 4), "traffic": traffic,
+                "peak_basis": "fp32 VALU without packed fp32 (the build disables it): 256 CU x 4 SIMD x 16 lanes "
+                              "x 2 flop x 2.4 GHz",
+                "published_peak": VALU_PUBLISHED_TFLOPS,
+                "frac_of_published": round(alu_tflops / VALU_PUBLISHED_TFLOPS, 4)}
     return {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
 
@@ -598,20 +741,9 @@ def bench_decode(args, inp, bias_np, opts):
         ss.selective_scan_step(u, delta, A, B, C, Ds, z, y=y, state=state, stream=stream.cuda_stream,
                                delta_bias=bias, delta_softplus=softplus, discretization=args.discretization)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = float(np.mean([a.elapsed_time(e) for a, e in zip(starts, ends)]))
+    tm = time_calls(step, stream, args.steps, args.warmup)
+    wall = tm["wall"]
+    launch_ms = float(np.mean(tm["warm"]))
     if args.copy_calibration:
         copy_calibration()
     E = b * D * N
@@ -634,7 +766,7 @@ def bench_decode(args, inp, bias_np, opts):
                    "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
                    "mode": "decode step (state in place)", "step_size": opts["step_size"],
                    "discretization": args.discretization},
-        "kernel_ms": launch_ms,
+        **timing_fields(tm),
         "hbm_gbs": round(alg / (launch_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(alg / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": alg,

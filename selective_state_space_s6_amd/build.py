@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libselscan.so")
+# issue-rate and bandwidth probes (bench.py --microbench), same flags, a library of their own
+MICROBENCH_SRC = os.path.join(CSRC, "microbench.hip")
+MICROBENCH_LIB = os.path.join(PKG, "libselscan_microbench.so")
 # the forward scan's kernels are instantiated per element type and pass in units of their
 # own (scan_inst_*.hip), which compile in parallel
 SCAN_UNITS = [os.path.join(CSRC, "scan_inst_%s_%s.hip" % (io, ps))
@@ -38,10 +41,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(builddir, exist_ok=True)
     jobs = max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
     pending = []
-    for src in SOURCES:
+    for src in SOURCES + [MICROBENCH_SRC]:
         obj = os.path.join(builddir, os.path.basename(src) + ".o")
         pending.append(([HIPCC] + COMMON_FLAGS + ["-x", "hip", "-c", src, "-o", obj]))
         objs.append(obj)
+    mb_obj = objs.pop()
     running = []
     while pending or running:                                 # at most `jobs` compiles at once
         while pending and len(running) < jobs:
@@ -60,12 +64,16 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    tmp = MICROBENCH_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, mb_obj])
+    os.replace(tmp, MICROBENCH_LIB)
     return LIB
 
 
-def asm(out_path: str) -> None:
-    """Write the gfx950 assembly of the kernels (for inspection)."""
-    cmd = [HIPCC] + COMMON_FLAGS + ["-x", "hip", "--cuda-device-only", "-S", SOURCES[0], "-o", out_path]
+def asm(out_path: str, source: str = "") -> None:
+    """Write the gfx950 assembly of one unit's kernels (for inspection; default: the first
+    scan unit)."""
+    cmd = [HIPCC] + COMMON_FLAGS + ["-x", "hip", "--cuda-device-only", "-S", source or SOURCES[0], "-o", out_path]
     subprocess.check_call(cmd)
 
 

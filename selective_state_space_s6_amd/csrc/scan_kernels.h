@@ -750,33 +750,39 @@ void scan_kernel_coop(ScanParams p) {
 
   // ---- load sets: tile t's loads go to set t % NS, issued NS iterations before it is staged
   typename Qd::raw_t xT[NS], xQ[NS][TI ? 1 : NL];
-  const int64_t ntiles = (nrows + kTile - 1) / kTile;
-  const int64_t nfull = nrows / kTile;
-  const int last_steps = int(nrows - nfull * kTile);       // tokens of a ragged last tile
-  auto issue = [&](int64_t t, auto set_tag) __attribute__((always_inline)) {
+  // tile counts and byte offsets inside a work item fit 32 bits (its span is below 2^30 bytes),
+  // so the loop bookkeeping stays on the scalar unit
+  const int ntiles = int((nrows + kTile - 1) / kTile);
+  const int nfull = int(nrows / kTile);
+  const int last_steps = int(nrows) - nfull * kTile;        // tokens of a ragged last tile
+  const int tstrideT = kTile * int(slT) * ES, tstrideQ = kTile * int(slQ) * ES;
+  // Idle roles load through an offset past their descriptor (no memory traffic) and stage
+  // into the sink, so that every wavefront runs the same instruction stream.
+  auto issue = [&](int t, auto set_tag) __attribute__((always_inline)) {
     constexpr int P = decltype(set_tag)::value;
-    const int64_t tt = t < ntiles ? t : ntiles - 1;           // past the end: reload the last tile
-    const int64_t row0 = tt * kTile;
-    xT[P] = Qd::load(rT, voT, int(row0 * slT * ES));
+    const int tt = t < ntiles ? t : ntiles - 1;               // past the end: reload the last tile
+    xT[P] = Qd::load(rT, voT, tt * tstrideT);
     if (!TI) {
 #pragma unroll
-      for (int r = 0; r < NL; ++r) xQ[P][r] = Qd::load(rQ, voQ, int((row0 + int64_t(TPL) * r) * slQ * ES));
+      for (int r = 0; r < NL; ++r) xQ[P][r] = Qd::load(rQ, voQ, tt * tstrideQ + r * (TPL * int(slQ) * ES));
     }
   };
   // Stage load set SET into LDS buffer q: token tiles channel-major ([c][token]), B/C
   // state-major ([n][token]).
   auto stage = [&](auto set_tag, int q) __attribute__((always_inline)) {
     constexpr int P = decltype(set_tag)::value;
-    float* const dt = dstT(q);
-    float tv[4];
+    {
+      float* const dt = dstT(q);
+      float tv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tv[j] = Qd::get(xT[P], j);
-    if (DXF && roleT == 1) {                 // wave-uniform: the delta wavefront
+      for (int j = 0; j < 4; ++j) tv[j] = Qd::get(xT[P], j);
+      if (DXF && roleT == 1) {               // wave-uniform: the delta wavefront
 #pragma unroll
-      for (int j = 0; j < 4; ++j) tv[j] = step_size(tv[j], dbias[j], p.softplus != 0);
+        for (int j = 0; j < 4; ++j) tv[j] = step_size(tv[j], dbias[j], p.softplus != 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dt[(4 * vq + j) * kRowPad + vr] = tv[j];
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dt[(4 * vq + j) * kRowPad + vr] = tv[j];
     if (!TI) {
       float* const dq = dstQ(q);
 #pragma unroll
@@ -897,10 +903,12 @@ void scan_kernel_coop(ScanParams p) {
     yv *= gate ? silu : 1.f;
     sY[yq * (kTile * kRowY) + it * kRowY + 4 * w + ic] = yv;
   };
-  // store the y tile of tile t from y buffer yq (wavefront 0; the others are dropped)
-  auto y_store = [&](int64_t t, int yq) __attribute__((always_inline)) {
+  // store the y tile of tile t from y buffer yq (wavefront 0 only)
+  const int tstrideY = kTile * int(p.y_sl) * ES;
+  auto y_store = [&](int t, int yq) __attribute__((always_inline)) {
+    if (w != 0) return;                                               // wave-uniform
     const float4 yv = *reinterpret_cast<const float4*>(sY + yq * (kTile * kRowY) + vr * kRowY + 4 * (vq < W ? vq : 0));
-    Qd::store(rY, voY, int(t * kTile * p.y_sl * ES), yv);             // dropped past l_end
+    Qd::store(rY, voY, t * tstrideY, yv);                             // dropped past l_end
   };
   auto order_lds = [] () __attribute__((always_inline)) { __asm__ __volatile__("" ::: "memory"); };
   auto region = [] () __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
@@ -912,12 +920,12 @@ void scan_kernel_coop(ScanParams p) {
   using G3 = std::integral_constant<int, 3>;
   using true_t = std::integral_constant<bool, true>;
   using false_t = std::integral_constant<bool, false>;
-  auto mod3 = [] (int64_t t) __attribute__((always_inline)) { return int(t % 3); };
+  auto mod3 = [] (int t) __attribute__((always_inline)) { return t % 3; };
 
   // One loop iteration for full tile t; SET1 = (t + 1) % NS is compile-time.
   // state pass, optional: the state (from the chunk's zero start) and the running sum of
   // delta at the start of tile t
-  auto checkpoint = [&](int64_t t) __attribute__((always_inline)) {
+  auto checkpoint = [&](int t) __attribute__((always_inline)) {
     if constexpr (MODE == MODE_STATE && !TI) {
       if (p.ckpt != nullptr && dvalid) {
         const int64_t tile = l_begin / kTile + t;
@@ -929,19 +937,23 @@ void scan_kernel_coop(ScanParams p) {
       }
     }
   };
-  auto iteration = [&](int64_t t, auto set_tag, auto var_tag, auto fin_tag, auto yst_tag) __attribute__((always_inline)) {
+  // RES = t mod 6, known at compile time: the LDS buffers (t mod 3), the y tile (t mod 2) and
+  // the load set ((t + 1) mod NS) are constants, folded into the instructions' offsets
+  auto iteration = [&](int t, auto res_tag, auto var_tag, auto fin_tag, auto yst_tag) __attribute__((always_inline)) {
+    constexpr int RES = decltype(res_tag)::value;
     constexpr bool FIN = decltype(fin_tag)::value && READOUT;
     constexpr bool YST = decltype(yst_tag)::value && READOUT;
-    const int q0 = mod3(t), q1 = mod3(t + 1), qm = mod3(t + 2);   // buffers of t, t+1, t-1
+    constexpr int q0 = RES % 3, q1 = (RES + 1) % 3, qm = (RES + 2) % 3;   // buffers of t, t+1, t-1
+    using SET = std::integral_constant<int, (RES + 1) % NS>;
     checkpoint(t);
     region();
     block_lds_sync();
     if (FIN) fin_read(qm);                             // tile t-1
-    if (YST) y_store(t - 2, int(t & 1));               // tile t-2
+    if (YST) y_store(t - 2, RES & 1);                  // tile t-2
     order_lds();
     rd(q0, G0{}, var_tag);
-    stage(set_tag, q1);                                // tile t+1
-    issue(t + 1 + NS, set_tag);
+    stage(SET{}, q1);                                  // tile t+1
+    issue(t + 1 + NS, SET{});
     region();
     rd(q0, G1{}, var_tag);
     cmp(G0{}, var_tag, true_t{}, kTile);
@@ -949,37 +961,37 @@ void scan_kernel_coop(ScanParams p) {
     region();
     rd(q0, G2{}, var_tag);
     cmp(G1{}, var_tag, true_t{}, kTile);
-    if (FIN) fin_out(int((t - 1) & 1));
+    if (FIN) fin_out((RES + 1) & 1);
     region();
     rd(q0, G3{}, var_tag);
     cmp(G2{}, var_tag, true_t{}, kTile);
     region();
     cmp(G3{}, var_tag, true_t{}, kTile);
   };
-  // NS iterations from t (t mod NS == 2 mod NS), each only while t < nfull when GUARD.
-  auto block = [&](int64_t t, auto var_tag, auto guard_tag) __attribute__((always_inline)) {
+  // Six iterations from t (t mod 6 == 2), each only while t < nfull when GUARD.
+  auto block = [&](int t, auto var_tag, auto guard_tag) __attribute__((always_inline)) {
     constexpr bool GUARD = decltype(guard_tag)::value;
-    static_for<NS>([&](auto k_tag) __attribute__((always_inline)) {
+    static_for<6>([&](auto k_tag) __attribute__((always_inline)) {
       constexpr int KK = decltype(k_tag)::value;
-      using SET = std::integral_constant<int, (3 + KK) % NS>;
-      if (!GUARD || t + KK < nfull) iteration(t + KK, SET{}, var_tag, true_t{}, true_t{});
+      using RES = std::integral_constant<int, (2 + KK) % 6>;
+      if (!GUARD || t + KK < nfull) iteration(t + KK, RES{}, var_tag, true_t{}, true_t{});
     });
   };
 
   auto run = [&](auto var_tag) __attribute__((always_inline)) {
-    static_for<NS>([&](auto k_tag) __attribute__((always_inline)) { issue(int64_t(decltype(k_tag)::value), k_tag); });
+    static_for<NS>([&](auto k_tag) __attribute__((always_inline)) { issue(int(decltype(k_tag)::value), k_tag); });
     stage(I0{}, 0);                                     // tile 0 -> buffer 0
-    issue(int64_t(NS), I0{});
-    int64_t t = 0;
+    issue(NS, I0{});
+    int t = 0;
     if (nfull > 0) {
-      iteration(int64_t(0), std::integral_constant<int, 1 % NS>{}, var_tag, false_t{}, false_t{});
+      iteration(0, std::integral_constant<int, 0>{}, var_tag, false_t{}, false_t{});
       t = 1;
     }
     if (nfull > 1) {
-      iteration(int64_t(1), std::integral_constant<int, 2 % NS>{}, var_tag, true_t{}, false_t{});
+      iteration(1, std::integral_constant<int, 1>{}, var_tag, true_t{}, false_t{});
       t = 2;
     }
-    for (; t + NS <= nfull; t += NS) block(t, var_tag, false_t{});
+    for (; t + 6 <= nfull; t += 6) block(t, var_tag, false_t{});
     if (t < nfull) {
       block(t, var_tag, true_t{});
       t = nfull;
