@@ -369,7 +369,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="longctx_bf16",
                     choices=sorted(s6_workloads.WORKLOADS) + sorted(s6_workloads.SSD_WORKLOADS))
-    ap.add_argument("--path", default="auto", choices=["auto", "single", "chunked"])
+    ap.add_argument("--path", default="auto", choices=["auto", "single", "chunked", "conv"],
+                    help="conv: the convolution mode (fixed coefficients only)")
     ap.add_argument("--ssd-path", default="auto", choices=["auto", "fused", "chunked"],
                     help="scalar-decay workloads: state kept on chip (fused) or chunk-parallel")
     ap.add_argument("--step-size", default="given", choices=["given", "softplus"],
@@ -442,14 +443,18 @@ def main():
     if args.copy_calibration:
         copy_calibration()
 
-    dims = ss.make_dims(u, delta, A, B, C, z, y, path=args.path)
-    chunked = ss.workspace_size(dims) > 0
+    dims = ss.make_dims(u, delta, A, B, C, z, y, path=args.path, discretization=args.discretization,
+                        delta_softplus=softplus)
+    taken = ss.plan_path(dims)
     alg_bytes = algorithmic_bytes(inp, want_last, bias=softplus)
     slots = algorithmic_slots(inp, softplus=softplus, euler=euler)
     launch_s = launch_ms * 1e-3
     hbm_gbs = alg_bytes / launch_s / 1e9
-    traffic = measured_traffic(args.workload + opts["suffix"], alg_bytes)
-    roof = roofline(alg_bytes, slots, launch_s, traffic)        # the binding roof
+    traffic = measured_traffic(args.workload + opts["suffix"] + ("+conv" if taken == "conv" else ""), alg_bytes)
+    if taken == "conv":                                          # matrix products on the fp32 matrix cores
+        roof = matrix_roofline(alg_bytes, conv_flops(inp), launch_s, traffic, MFMA_F32_PEAK_TFLOPS)
+    else:
+        roof = roofline(alg_bytes, slots, launch_s, traffic)    # the binding roof
 
     out = {
         "metric": METRIC,
@@ -466,7 +471,7 @@ def main():
         "data": "synthetic (seeded, s6_workloads: %s)" % args.workload,
         "config": {"workload": args.workload, "batch": b, "seq_len": L, "dim": D, "dstate": N, "io": io,
                    "state": "f32", "gate": inp.z is not None, "feedthrough": inp.Dskip is not None,
-                   "last_state": want_last, "time_invariant": inp.ti, "path": "chunked" if chunked else "single",
+                   "last_state": want_last, "time_invariant": inp.ti, "path": taken,
                    "step_size": opts["step_size"], "discretization": args.discretization},
         **timing_fields(tm),
         "hbm_gbs": round(hbm_gbs, 1),
@@ -576,6 +581,29 @@ def cpu_baseline_backward(inp, bias, softplus, euler, target_s: float = 10.0):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X published dense bf16 matrix peak
+MFMA_F32_PEAK_TFLOPS = 157.3      # MI355X published dense fp32 matrix peak
+
+
+def conv_flops(inp: s6_workloads.Inputs) -> float:
+    """Algorithmic matrix work of the convolution mode: per (batch row, channel, 16-token block)
+    the causal half of the 16 x 16 Toeplitz product of the lag kernel (136 multiply-adds), the
+    block's end state from its tokens (16 N) and the readout of the carried state (16 N); 2 flops
+    per multiply-add."""
+    b, L, D, N = inp.shape
+    blocks = (L + 15) // 16
+    return 2.0 * b * D * blocks * (136 + 32 * N)
+
+
+def matrix_roofline(alg_bytes: int, flops: float, seconds: float, traffic, peak: float):
+    """The binding roof of a matrix-core kernel: its matrix work against `peak` or its bytes
+    against HBM, whichever bounds the time more."""
+    tflops = flops / seconds / 1e12
+    if flops / (peak * 1e12) >= alg_bytes / (HBM_PEAK_GBS * 1e9):
+        return {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": traffic}
+    gbs = alg_bytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
 SSD_CHUNK = 64
 
 

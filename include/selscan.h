@@ -102,6 +102,15 @@ enum selscan_path {
   SELSCAN_PATH_SINGLE = 1,   /* one pass along the sequence per (batch, channel group) */
   SELSCAN_PATH_CHUNKED = 2,  /* two passes over chunks of the sequence, joined by a scan
                                 of per-chunk affine maps */
+  SELSCAN_PATH_CONV = 3,     /* fixed (time-invariant) coefficients only: the causal
+                                convolution y = K * u with the lag kernel
+                                K_k = sum_n C_n Abar_n^k Bbar_n ("state-space models"
+                                (aarnphm.xyz), "One recurrence, one convolution"), as
+                                16-token block Toeplitz products on the fp32 matrix cores with
+                                the state carried between blocks.  Needs dim % 4 == 0 and
+                                u / z / y rows aligned to 4 elements; no initial state.  Other
+                                cases return SELSCAN_ERR_UNSUPPORTED.  Results agree with the
+                                recurrence within fp32 rounding of a different association. */
   /* Bit that may be or-ed into any path (tests only): use the general per-element kernel
    * even where the software-pipelined kernel applies.  Results agree within fp32
    * rounding. */
@@ -179,6 +188,11 @@ void selscan_dims_init(selscan_dims* dims, int io_dtype, int64_t batch, int64_t 
 int selective_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
                        const void* C, const float* Dskip, const void* z, void* y,
                        float* last_state, const selscan_dims* dims, void* stream);
+
+/* The path a forward call with these dims takes: SELSCAN_PATH_SINGLE, SELSCAN_PATH_CHUNKED or
+ * SELSCAN_PATH_CONV (the automatic choice resolved, assuming the operand pointers are aligned
+ * to 4 elements), or a negative status for invalid dims.  Host-only, touches no device. */
+int selective_scan_plan_path(const selscan_dims* dims);
 
 /* Bytes of device workspace the chunked path needs for these dims (0 when the automatic
  * or forced path is the single pass).  Returns 0 for invalid dims. */

@@ -35,7 +35,7 @@ SELSCAN_ERR_NULL, SELSCAN_ERR_DIMS, SELSCAN_ERR_UNSUPPORTED = -1, -2, -3
 SELSCAN_ERR_ALIGN, SELSCAN_ERR_HIP, SELSCAN_ERR_WORKSPACE, SELSCAN_ERR_ABI = -4, -5, -6, -7
 SELSCAN_ERR_SCRATCH_LIMIT = -8
 NOALLOC_SCRATCH_BYTES = 64 << 20          # SELSCAN_NOALLOC_SCRATCH_BYTES
-PATHS = {"auto": 0, "single": 1, "chunked": 2}
+PATHS = {"auto": 0, "single": 1, "chunked": 2, "conv": 3}   # conv: fixed coefficients only
 FLAG_SCALAR_IO = 0x100   # tests only: force the general per-element kernel
 DISCRETIZATIONS = {"zoh": 0, "euler": 1}
 
@@ -74,6 +74,7 @@ _SIGNATURES = [
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
     ("selective_scan_fwd", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP]),
     ("selective_scan_workspace_size", ctypes.c_size_t, [ctypes.POINTER(SelscanDims)]),
+    ("selective_scan_plan_path", ctypes.c_int, [ctypes.POINTER(SelscanDims)]),
     ("selective_scan_fwd_ws", ctypes.c_int, [_VP] * 9 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
     ("selective_scan_fwd_ex", ctypes.c_int, [_VP] * 11 + [ctypes.POINTER(SelscanDims), _VP, ctypes.c_size_t, _VP]),
     ("selective_scan_fwd_noalloc", ctypes.c_int, [_VP] * 11 + [ctypes.POINTER(SelscanDims), _VP]),
@@ -134,6 +135,14 @@ def dims_init(io_dtype: int, batch: int, seqlen: int, dim: int, dstate: int, tim
 
 def workspace_size(dims: SelscanDims) -> int:
     return int(lib().selective_scan_workspace_size(ctypes.byref(dims)))
+
+
+def plan_path(dims: SelscanDims) -> str:
+    """The path a forward call with these dims takes ("single", "chunked" or "conv")."""
+    code = int(lib().selective_scan_plan_path(ctypes.byref(dims)))
+    if code < 0:
+        raise SelscanError(code, "selective_scan_plan_path")
+    return {v: k for k, v in PATHS.items()}[code]
 
 
 def _ptr(t):

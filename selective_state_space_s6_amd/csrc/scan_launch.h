@@ -93,6 +93,26 @@ struct StepParams {
 };
 hipError_t launch_step(bool bf16, bool ti, const StepParams& p, hipStream_t stream);
 
+// The convolution mode of fixed coefficients (conv_kernels.hip): delta [D], B/C [D][*] with
+// channel strides B_sd / C_sd; u, z, y rows of D channels, D % 4 == 0, rows 16-byte (fp32) or
+// 8-byte (bf16) aligned.
+struct ConvParams {
+  const void* u;
+  const void* delta;
+  const float* delta_bias;   // may be null
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;        // may be null
+  const void* z;             // may be null
+  void* y;
+  float* last_state;         // may be null
+  int32_t euler, dxf, softplus;
+  int64_t batch, L, D, N;
+  int64_t u_sb, u_sl, z_sb, z_sl, y_sb, y_sl, B_sd, C_sd;
+};
+hipError_t launch_conv_ti(bool bf16, const ConvParams& p, hipStream_t stream);
+
 }  // namespace selscan
 
 namespace selscan {

@@ -25,6 +25,7 @@ struct Plan {
   int S = 16, K = 1;
   int64_t groups = 0;         // channel groups per batch row
   bool chunked = false;
+  bool conv = false;          // the convolution mode of fixed coefficients
   int64_t chunk_len = 0;
   int32_t n_chunks = 1;
   size_t ws_bytes = 0;        // workspace the chunked path needs
@@ -37,7 +38,15 @@ constexpr int64_t kTargetWaves = 4096;   // about four wavefronts per SIMD on 25
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Validate dims and choose the schedule.  Does not look at pointers.
-int make_plan(const selscan_dims* dims, Plan* plan) {
+// The automatic path takes the convolution mode for fixed coefficients when it has one
+// wavefront per (batch row, channel) for at least this many and the sequence fills a 256-token
+// super-tile: measured faster than the recurrence on the time-invariant workload (batch 4,
+// L 8192, D 1024, N 64).  Fewer (batch, channel) pairs leave the recurrence's sequence chunks
+// as the better source of parallelism.
+constexpr int64_t kConvMinWaves = 1024;
+constexpr int64_t kConvMinLen = 256;
+
+int make_plan(const selscan_dims* dims, Plan* plan, bool allow_auto_conv = true) {
   if (!dims) return SELSCAN_ERR_NULL;
   if (dims->abi_version != SELSCAN_ABI_VERSION) return SELSCAN_ERR_ABI;
   const selscan_dims& d = *dims;
@@ -49,7 +58,8 @@ int make_plan(const selscan_dims* dims, Plan* plan) {
   if (d.dstate > 64) return SELSCAN_ERR_UNSUPPORTED;
   if (d.io_dtype != SELSCAN_F32 && d.io_dtype != SELSCAN_BF16) return SELSCAN_ERR_UNSUPPORTED;
   const int32_t path = d.path & ~int32_t(SELSCAN_PATH_FLAG_SCALAR_IO);
-  if (path != SELSCAN_PATH_AUTO && path != SELSCAN_PATH_SINGLE && path != SELSCAN_PATH_CHUNKED)
+  if (path != SELSCAN_PATH_AUTO && path != SELSCAN_PATH_SINGLE && path != SELSCAN_PATH_CHUNKED &&
+      path != SELSCAN_PATH_CONV)
     return SELSCAN_ERR_UNSUPPORTED;
   if (d.chunk_len < 0 || d.chunk_len % 16 != 0) return SELSCAN_ERR_UNSUPPORTED;
   if (d.discretization != SELSCAN_DISC_ZOH && d.discretization != SELSCAN_DISC_EULER) return SELSCAN_ERR_UNSUPPORTED;
@@ -73,6 +83,20 @@ int make_plan(const selscan_dims* dims, Plan* plan) {
   else if (bc_per_channel && delta_per_channel) p.ti = true;
   else return SELSCAN_ERR_UNSUPPORTED;
   p.bf16 = d.io_dtype == SELSCAN_BF16;
+  // whole 4-channel vectors of u, z and y per token (their pointers are checked per call)
+  const bool conv_ok = p.ti && d.dim % 4 == 0 && d.u_sb % 4 == 0 && d.u_sl % 4 == 0 && d.z_sb % 4 == 0 &&
+                       d.z_sl % 4 == 0 && d.y_sb % 4 == 0 && d.y_sl % 4 == 0 && d.chunk_len == 0;
+  const bool auto_conv = path == SELSCAN_PATH_AUTO && allow_auto_conv && conv_ok &&
+                         d.batch * d.dim >= kConvMinWaves && d.seqlen >= kConvMinLen;
+  if (path == SELSCAN_PATH_CONV || auto_conv) {
+    if (!conv_ok) return SELSCAN_ERR_UNSUPPORTED;
+    p.conv = true;
+    p.chunk_len = d.seqlen;
+    p.n_chunks = 1;
+    p.groups = (d.dim + 15) / 16;
+    *plan = p;
+    return SELSCAN_OK;
+  }
   selscan::lanes_for_states(d.dstate, &p.S, &p.K);
   const int cw = 64 / p.S;
   p.groups = (d.dim + cw - 1) / cw;
@@ -193,8 +217,21 @@ int run(const void* u, const void* delta, const float* delta_bias, const float* 
     }
     return SELSCAN_OK;
   }
-  selscan::ScanParams p = scan_params(u, delta, delta_bias, A, B, C, Dskip, z, y, h0, last_state, d, plan);
   hipError_t e;
+  if (plan.conv) {
+    selscan::ConvParams c{};
+    c.u = u; c.delta = delta; c.delta_bias = delta_bias; c.A = A; c.B = B; c.C = C; c.Dskip = Dskip; c.z = z;
+    c.y = y; c.last_state = last_state;
+    c.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
+    c.softplus = d.delta_softplus != 0 ? 1 : 0;
+    c.dxf = (c.softplus || delta_bias != nullptr) ? 1 : 0;
+    c.batch = d.batch; c.L = d.seqlen; c.D = d.dim; c.N = d.dstate;
+    c.u_sb = d.u_sb; c.u_sl = d.u_sl; c.z_sb = d.z_sb; c.z_sl = d.z_sl; c.y_sb = d.y_sb; c.y_sl = d.y_sl;
+    c.B_sd = d.B_sd; c.C_sd = d.C_sd;
+    e = selscan::launch_conv_ti(plan.bf16, c, stream);
+    return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
+  }
+  selscan::ScanParams p = scan_params(u, delta, delta_bias, A, B, C, Dskip, z, y, h0, last_state, d, plan);
   if (!plan.chunked) {
     e = selscan::launch_scan_pass(selscan::kPassSingle, plan.bf16, plan.ti, plan.S, plan.K, p, stream);
     return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
@@ -232,6 +269,15 @@ int fwd_impl(const void* u, const void* delta, const float* delta_bias, const fl
     if (!aligned(h0, 4)) return SELSCAN_ERR_ALIGN;
   }
   if (delta_bias != nullptr && !aligned(delta_bias, 4)) return SELSCAN_ERR_ALIGN;
+  if (plan.conv) {                                    // vectors of 4 channels per access
+    const size_t vb = dims->io_dtype == SELSCAN_BF16 ? 8 : 16;
+    if (!aligned(u, vb) || !aligned(y, vb) || (z != nullptr && !aligned(z, vb))) {
+      const int32_t path = dims->path & ~int32_t(SELSCAN_PATH_FLAG_SCALAR_IO);
+      if (path != SELSCAN_PATH_AUTO) return SELSCAN_ERR_UNSUPPORTED;
+      st = make_plan(dims, &plan, false);               // the automatic path falls back to the recurrence
+      if (st != SELSCAN_OK) return st;
+    }
+  }
   const bool need_ws = plan.chunked && dims->batch > 0 && dims->seqlen > 0;
   if (!need_ws || workspace != nullptr) {
     if (need_ws && (workspace_bytes < plan.ws_bytes || !aligned(workspace, 256))) return SELSCAN_ERR_WORKSPACE;
@@ -506,6 +552,13 @@ void selscan_dims_init(selscan_dims* dims, int io_dtype, int64_t batch, int64_t 
   d.discretization = SELSCAN_DISC_ZOH;
   d.delta_softplus = 0;
   *dims = d;
+}
+
+int selective_scan_plan_path(const selscan_dims* dims) {
+  Plan plan;
+  const int st = make_plan(dims, &plan);
+  if (st != SELSCAN_OK) return st;
+  return plan.conv ? SELSCAN_PATH_CONV : plan.chunked ? SELSCAN_PATH_CHUNKED : SELSCAN_PATH_SINGLE;
 }
 
 size_t selective_scan_workspace_size(const selscan_dims* dims) {

@@ -304,3 +304,27 @@ def test_noalloc_errors_before_the_device():
     assert call_noalloc(ti, h0=FAKE) == ss.SELSCAN_ERR_UNSUPPORTED
     assert call_noalloc(good_dims(), h0=FAKE_ODD) == ss.SELSCAN_ERR_ALIGN
     assert call_noalloc(good_dims(batch=0)) == ss.SELSCAN_OK     # nothing to do, nothing touched
+
+
+def test_plan_path_resolves_the_automatic_choice():
+    small = ss.dims_init(ss.SELSCAN_F32, 2, 1024, 256, 16)               # 128 wavefronts: chunked
+    assert ss.plan_path(small) == "chunked"
+    big = ss.dims_init(ss.SELSCAN_BF16, 4, 16384, 2560, 16)              # one pass
+    assert ss.plan_path(big) == "single"
+    ti = ss.dims_init(ss.SELSCAN_F32, 4, 8192, 1024, 64, time_invariant=True)   # fixed coefficients: convolution
+    assert ss.plan_path(ti) == "conv" and ss.workspace_size(ti) == 0
+    few = ss.dims_init(ss.SELSCAN_F32, 1, 8192, 64, 64, time_invariant=True)    # too few channels: recurrence
+    assert ss.plan_path(few) in ("single", "chunked")
+    odd = ss.dims_init(ss.SELSCAN_F32, 4, 8192, 1022, 64, time_invariant=True)  # D % 4 != 0: recurrence
+    assert ss.plan_path(odd) in ("single", "chunked")
+    odd.path = ss.PATHS["conv"]
+    assert call(odd) == ss.SELSCAN_ERR_UNSUPPORTED
+    sel = ss.dims_init(ss.SELSCAN_F32, 4, 8192, 1024, 16)                # selective: no convolution
+    sel.path = ss.PATHS["conv"]
+    assert call(sel) == ss.SELSCAN_ERR_UNSUPPORTED
+    bad = ss.dims_init(ss.SELSCAN_F32, 4, 8192, 1024, 65)
+    assert lib_status(bad) == ss.SELSCAN_ERR_UNSUPPORTED
+
+
+def lib_status(dims):
+    return ss.lib().selective_scan_plan_path(ctypes.byref(dims))
