@@ -63,6 +63,8 @@ SSD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc",
                       for f in ("ssd_kernels.hip", "device_common.h")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
                       for f in ("bwd_kernels.hip", "scan_kernels.h", "scan_kernels.hip", "device_common.h")]
+CONV_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
+                       for f in ("conv_kernels.hip", "device_common.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "scan_counters.json")
 
 # Algorithmic ALU work, in FMA-slot units (one fp32 VALU instruction per lane = 1 slot = 2
@@ -151,11 +153,12 @@ def algorithmic_slots(inp: s6_workloads.Inputs, softplus: bool = False, euler: b
 def kernel_source_hash(workload: str = "") -> str:
     """Hash of the sources of the kernels a workload runs (the scan kernels; for the
     scalar-decay workloads theirs; for a backward tag, "backward_<workload>", the backward's
-    and the forward state pass's): the counters in the committed summary are valid only for
-    the source they were taken on."""
+    and the forward state pass's; for a tag ending in "+conv", the convolution mode's): the
+    counters in the committed summary are valid only for the source they were taken on."""
     h = hashlib.sha256()
     srcs = (SSD_KERNEL_SOURCES if workload.startswith("ssd_")
-            else BWD_KERNEL_SOURCES if workload.startswith("backward_") else KERNEL_SOURCES)
+            else BWD_KERNEL_SOURCES if workload.startswith("backward_")
+            else CONV_KERNEL_SOURCES if workload.endswith("+conv") else KERNEL_SOURCES)
     for path in srcs:
         with open(path, "rb") as f:
             h.update(f.read())
@@ -525,6 +528,8 @@ def bench_backward(args, inp, bias_np, opts):
     tm = time_calls(step, stream, args.steps, args.warmup)
     wall = tm["wall"]
     launch_ms = float(np.mean(tm["warm"]))
+    if args.copy_calibration:
+        copy_calibration()
     E = b * L * D * N
     alg = backward_bytes(inp)
     slots = SLOTS_BWD_PER_ELEMENT * E + SLOTS_BWD_PER_TOKEN_D * b * L * D
@@ -549,7 +554,7 @@ def bench_backward(args, inp, bias_np, opts):
         "hbm_frac": round(alg / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": alg,
         "algorithmic_slots": slots,
-        "roofline": roofline(alg, slots, launch_ms * 1e-3, None),
+        "roofline": roofline(alg, slots, launch_ms * 1e-3, measured_traffic("backward_" + args.workload + opts["suffix"], alg)),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_backward(inp, bias_np, softplus, args.discretization == "euler")
