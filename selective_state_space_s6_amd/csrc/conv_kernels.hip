@@ -21,7 +21,7 @@
 //
 // Work decomposition: one wavefront per (batch row, channel), 8 wavefronts (8 neighbouring
 // channels) per workgroup, so that the workgroup stages u, and writes y, as rows of 8 channels
-// through LDS.  With 64 states the fragments take about 160 VGPRs: two wavefronts per SIMD
+// through LDS; workgroups are dealt to the XCDs in contiguous runs of channel groups.  With 64 states the fragments take about 160 VGPRs: two wavefronts per SIMD
 // (512-thread workgroups leave the compiler 256); with up to 32 states, four.  Per wavefront, the constant matrices live in VGPRs as MFMA
 // fragments.  Fragment layouts of v_mfma_f32_16x16x4_f32 (wave64): lane l = 16 g + j holds
 // A[i = j][k = g] and B[k = g][col = j]; the four result registers r hold D[4 g + r][j].
@@ -101,9 +101,12 @@ void conv_ti_kernel(ConvParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;                // fragment lane: column (block) j, row group g
+  // neighbouring channel groups share the 128-byte lines of u and y: the XCD-contiguous order
+  // puts them on one XCD, whose L2 then fetches each line once
   const int64_t groups = (p.D + kCW - 1) / kCW;
-  const int64_t b = blockIdx.x / groups;
-  const int64_t d0 = (blockIdx.x % groups) * kCW;
+  const int64_t item = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int64_t b = item / groups;
+  const int64_t d0 = (item % groups) * kCW;
   const int64_t d = d0 + w;                              // this wavefront's channel
   const bool dvalid = d < p.D;
   const int64_t L = p.L, N = p.N;
