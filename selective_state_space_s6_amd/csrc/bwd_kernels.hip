@@ -386,7 +386,6 @@ void bwd_kernel(BwdParams p) {
         const float uu = sTok[0][cw][j], dt = sTok[1][cw][j], dyp = sTok[2][cw][j];
         const float gzf = sTok[3][cw][j], sig = sTok[4][cw][j];
         const float4 B4 = ld4(&sBq[j][4 * s]), C4 = ld4(&sCq[j][4 * s]);
-        const float dt2 = dt * dt;
         float ab[4], cf[4];
         float spart = 0.f;
 #pragma unroll
@@ -406,15 +405,28 @@ void bwd_kernel(BwdParams p) {
           const float lc = lam * cf[i];
           gu = fmaf(lc, Bi, gu);
           const float abh = ab[i] * hp[j][i];                 // Abar h_{t-1}
-          const float dcdd_bu = first ? bu : ab[i] * bu;
-          gdt = fmaf(lam, fmaf(a[i], abh, dcdd_bu), gdt);
-          // dc/da = (delta Abar - c) / a, or delta^2 phi(x), x = delta a, by the series of
-          // phi(x) = (x e^x - (e^x - 1)) / x^2 near 0 where the first form cancels (and at a == 0)
-          const float x = dt * a[i];
-          const float series = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
-          const float closed = fmaf(dt, ab[i], -cf[i]) * iA[i];
-          const float dcda = first ? 0.f : (fabsf(x) < 0.1f ? dt2 * series : closed);
-          gA[i] = fmaf(lam, fmaf(dt, abh, dcda * bu), gA[i]);
+          if constexpr (MODE == BWD_MAIN) {
+            // ZOH, every rate away from zero.  With g = lam (a Abar h + Abar B u), the token's
+            // ddelta term, and dc/da = (delta Abar - c) / a, the token's dA term is
+            // (delta g - lam c B u) / a: accumulated here without the 1 / a, which the
+            // partial sum takes once at the end
+            const float gt = lam * fmaf(a[i], abh, ab[i] * bu);
+            gdt += gt;
+            gA[i] = fmaf(-lc, bu, fmaf(dt, gt, gA[i]));
+          } else if constexpr (MODE == BWD_MAIN_EULER) {
+            // c = delta: dc/ddelta = 1 and dc/da = 0
+            gdt = fmaf(lam, fmaf(a[i], abh, bu), gdt);
+            gA[i] = fmaf(lam * dt, abh, gA[i]);
+          } else {
+            gdt = fmaf(lam, fmaf(a[i], abh, ab[i] * bu), gdt);
+            // dc/da = (delta Abar - c) / a, or delta^2 phi(x), x = delta a, by the series of
+            // phi(x) = (x e^x - (e^x - 1)) / x^2 near 0 where the first form cancels (and at a == 0)
+            const float x = dt * a[i];
+            const float series = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
+            const float closed = fmaf(dt, ab[i], -cf[i]) * iA[i];
+            const float dcda = fabsf(x) < 0.1f ? dt * dt * series : closed;
+            gA[i] = fmaf(lam, fmaf(dt, abh, dcda * bu), gA[i]);
+          }
           pb[i] = lc * uu;
           pc[i] = dyp * hj;
           mu[i] = ab[i] * lam;
@@ -508,7 +520,7 @@ void bwd_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (!nok[i]) continue;
-    p.pA[(bq * D + d) * N + 4 * s + i] = gA[i];
+    p.pA[(bq * D + d) * N + 4 * s + i] = MODE == BWD_MAIN ? gA[i] * iA[i] : gA[i];
     if (p.dh0 != nullptr && chunk == 0) p.dh0[(b * D + d) * N + 4 * s + i] = mu[i];
   }
   if (dvalid && s == 0) {
