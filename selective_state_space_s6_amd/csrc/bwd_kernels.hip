@@ -404,20 +404,21 @@ void bwd_kernel(BwdParams p) {
           const float bu = Bi * uu;
           const float lc = lam * cf[i];
           gu = fmaf(lc, Bi, gu);
-          const float abh = ab[i] * hp[j][i];                 // Abar h_{t-1}
           if constexpr (MODE == BWD_MAIN) {
-            // ZOH, every rate away from zero.  With g = lam (a Abar h + Abar B u), the token's
-            // ddelta term, and dc/da = (delta Abar - c) / a, the token's dA term is
-            // (delta g - lam c B u) / a: accumulated here without the 1 / a, which the
+            // ZOH, every rate away from zero.  The token's ddelta term is
+            // g = lam Abar (a h_{t-1} + B u), and with dc/da = (delta Abar - c) / a its dA term
+            // is (delta g - lam c B u) / a: accumulated here without the 1 / a, which the
             // partial sum takes once at the end
-            const float gt = lam * fmaf(a[i], abh, ab[i] * bu);
+            const float gt = ab[i] * lam * fmaf(a[i], hp[j][i], bu);
             gdt += gt;
             gA[i] = fmaf(-lc, bu, fmaf(dt, gt, gA[i]));
           } else if constexpr (MODE == BWD_MAIN_EULER) {
             // c = delta: dc/ddelta = 1 and dc/da = 0
+            const float abh = ab[i] * hp[j][i];               // Abar h_{t-1}
             gdt = fmaf(lam, fmaf(a[i], abh, bu), gdt);
             gA[i] = fmaf(lam * dt, abh, gA[i]);
           } else {
+            const float abh = ab[i] * hp[j][i];
             gdt = fmaf(lam, fmaf(a[i], abh, ab[i] * bu), gdt);
             // dc/da = (delta Abar - c) / a, or delta^2 phi(x), x = delta a, by the series of
             // phi(x) = (x e^x - (e^x - 1)) / x^2 near 0 where the first form cancels (and at a == 0)
