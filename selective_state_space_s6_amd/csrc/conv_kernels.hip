@@ -21,9 +21,12 @@
 //
 // Work decomposition: one wavefront per (batch row, channel), 8 wavefronts (8 neighbouring
 // channels) per workgroup, so that the workgroup stages u, and writes y, as rows of 8 channels
-// through LDS; workgroups are dealt to the XCDs in contiguous runs of channel groups.  With 64 states the fragments take about 160 VGPRs: two wavefronts per SIMD
-// (512-thread workgroups leave the compiler 256); with up to 32 states, four.  Per wavefront, the constant matrices live in VGPRs as MFMA
-// fragments.  Fragment layouts of v_mfma_f32_16x16x4_f32 (wave64): lane l = 16 g + j holds
+// through LDS; workgroups are dealt to the XCDs in contiguous runs of channel groups.  Per
+// wavefront, the Toeplitz, W and V matrices live in VGPRs as MFMA fragments; the carry factors
+// Abar^16 go to LDS and are read back per super-tile, and the readout over the state blocks
+// accumulates into one register set, so that every state count fits 128 VGPRs: four
+// wavefronts per SIMD, two workgroups per compute unit (the latency of the chain MFMA -> DPP
+// scan -> MFMA is what a second workgroup hides).  Fragment layouts of v_mfma_f32_16x16x4_f32 (wave64): lane l = 16 g + j holds
 // A[i = j][k = g] and B[k = g][col = j]; the four result registers r hold D[4 g + r][j].
 // The state index of the carried product's k-steps is chosen as n = 16 a + 4 g + r, which is
 // the row of the W.U result in register (a, r): the scanned states feed V.H without a
@@ -91,12 +94,13 @@ template <> struct conv_io<uint16_t> {       // bfloat16 bit patterns
 
 // NB: blocks of 16 states (N <= 16 NB; states past N are padded with Bbar = C = 0).
 template <typename IO, int NB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NB <= 2 ? 4 : 3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void conv_ti_kernel(ConvParams p) {
   using T = io_traits<IO>;
   using Io = conv_io<IO>;
   __shared__ __align__(16) float sU[2][kCW * kRow];      // u of a super-tile, [channel][token], two buffers
   __shared__ __align__(16) float sY[kCW * kRow];         // y of a super-tile (and set-up scratch)
+  __shared__ __align__(16) float4 sQ[kCW][NB][64];       // each lane's Abar^16 of its four result rows, per state block
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,7 +152,7 @@ void conv_ti_kernel(ConvParams p) {
     if (k >= 0) kv = scr[192 + k] + scr[192 + 16 + k] + scr[192 + 32 + k] + scr[192 + 48 + k];
     tf[s] = kv;
   }
-  float wf[NB][4], vf[NB][4], q[NB][4];
+  float wf[NB][4], vf[NB][4], q[NB][4];                  // q goes to LDS (sQ)
 #pragma unroll
   for (int a = 0; a < NB; ++a) {
 #pragma unroll
@@ -170,7 +174,8 @@ void conv_ti_kernel(ConvParams p) {
 #pragma unroll
   for (int a = 0; a < NB; ++a) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) __asm__ __volatile__("" : "+v"(wf[a][k]), "+v"(vf[a][k]), "+v"(q[a][k]));
+    for (int k = 0; k < 4; ++k) __asm__ __volatile__("" : "+v"(wf[a][k]), "+v"(vf[a][k]));
+    sQ[w][a][lane] = make_float4(q[a][0], q[a][1], q[a][2], q[a][3]);
   }
   __syncthreads();                                        // the scratch (in sY) is free again
 
@@ -225,21 +230,23 @@ void conv_ti_kernel(ConvParams p) {
     const int jl = e >> 4, m = (e & 15) + 1;
     float* const hs = sU[cur ^ 1] + w * kRow;             // nothing is staged after the last tile
     // per block of 16 states: W . U, the scan over the 16 blocks, and its readout V . X
-    f32x4 Za[NB];
+    f32x4 Z = {0.f, 0.f, 0.f, 0.f};                       // V . X summed over the state blocks
 #pragma unroll
     for (int a = 0; a < NB; ++a) {
       f32x4 S = zero4;
 #pragma unroll
       for (int s = 0; s < 4; ++s) S = mfma4(wf[a][s], uf[s], S);           // W . U
+      const float4 qa = sQ[w][a][lane];
+      const float qv[4] = {qa.x, qa.y, qa.z, qa.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // the state entering the super-tile (last column of the previous one) enters block 0
         const float hin = dpp<kBcast15>(X[a][r]);
         if (fin && jl == 0 && j == 0) hs[16 * a + 4 * g + r] = hin;
         float x = S[r];
-        if (j == 0) x = fmaf(q[a][r], hin, x);
+        if (j == 0) x = fmaf(qv[r], hin, x);
         // inclusive scan over the 16 blocks: x_j += q^m x_{j-m}, m = 1, 2, 4, 8
-        float qm = q[a][r];
+        float qm = qv[r];
         x = fmaf(dpp<kShr1>(x), qm, x);
         qm *= qm;
         x = fmaf(dpp<kShr2>(x), qm, x);
@@ -250,13 +257,9 @@ void conv_ti_kernel(ConvParams p) {
         X[a][r] = x;
         if (fin && jl > 0 && j == jl - 1) hs[16 * a + 4 * g + r] = x;
       }
-      Za[a] = zero4;                                      // V . X: readout of the state after block j
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Za[a] = mfma4(vf[a][r], X[a][r], Za[a]);
+      for (int r = 0; r < 4; ++r) Z = mfma4(vf[a][r], X[a][r], Z);   // readout of the state after block j
     }
-    f32x4 Z = Za[0];
-#pragma unroll
-    for (int a = 1; a < NB; ++a) Z += Za[a];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {                         // block j takes the readout of block j - 1
       const float prev = dpp<kShr1>(Z[r]);
