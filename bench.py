@@ -63,6 +63,8 @@ SSD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc",
                       for f in ("ssd_kernels.hip", "device_common.h")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
                       for f in ("bwd_kernels.hip", "scan_kernels.h", "scan_kernels.hip", "device_common.h")]
+BWD_TI_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
+                         for f in ("bwd_ti_kernels.hip", "bwd_kernels.hip", "scan_kernels.hip", "device_common.h")]
 CONV_KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_s6_amd", "csrc", f)
                        for f in ("conv_kernels.hip", "device_common.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "scan_counters.json")
@@ -90,6 +92,9 @@ SLOTS_PER_TOKEN_SOFTPLUS = 14
 #             per (b, l, d): gate and its derivative (about 12), Dskip terms (2)      = 14
 SLOTS_BWD_PER_ELEMENT = 21
 SLOTS_BWD_PER_TOKEN_D = 14
+#   backward of fixed coefficients, per (b, l, d, n): h_t (2), lambda (1), Abar h (1), B u (1),
+#             readout (1), du (1), dB (1), dC (1), ddelta (3), dA (3), carry (1)        = 16
+SLOTS_BWD_TI_PER_ELEMENT = 16
 
 
 def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool, bias: bool = False) -> int:
@@ -117,10 +122,12 @@ def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool, bias: bool = Fa
 def backward_bytes(inp: s6_workloads.Inputs) -> int:
     """Bytes the backward pass must move: u, delta, z, dy read and du, ddelta, dz written per
     (b, l, d); B, C read and dB, dC written per (b, l, n); A, Dskip read and dA, dDskip written
-    once."""
+    once.  Fixed coefficients: delta, ddelta per channel and B, C, dB, dC per (d, n)."""
     b, L, D, N = inp.shape
     es = 2 if inp.io == "bf16" else 4
     zt = 2 if inp.z is not None else 0
+    if inp.ti:
+        return b * L * D * es * (3 + zt) + 2 * D * es + 4 * D * N * es + 2 * (D * N + D) * 4
     return b * L * D * es * (4 + zt) + b * L * N * es * 4 + 2 * (D * N + D) * 4
 
 
@@ -153,10 +160,12 @@ def algorithmic_slots(inp: s6_workloads.Inputs, softplus: bool = False, euler: b
 def kernel_source_hash(workload: str = "") -> str:
     """Hash of the sources of the kernels a workload runs (the scan kernels; for the
     scalar-decay workloads theirs; for a backward tag, "backward_<workload>", the backward's
-    and the forward state pass's; for a tag ending in "+conv", the convolution mode's): the
+    and the forward state pass's (fixed coefficients: their own backward's); for a tag ending
+    in "+conv", the convolution mode's): the
     counters in the committed summary are valid only for the source they were taken on."""
     h = hashlib.sha256()
     srcs = (SSD_KERNEL_SOURCES if workload.startswith("ssd_")
+            else BWD_TI_KERNEL_SOURCES if workload.startswith("backward_s4d_ti")
             else BWD_KERNEL_SOURCES if workload.startswith("backward_")
             else CONV_KERNEL_SOURCES if workload.endswith("+conv") else KERNEL_SOURCES)
     for path in srcs:
@@ -532,7 +541,7 @@ def bench_backward(args, inp, bias_np, opts):
         copy_calibration()
     E = b * L * D * N
     alg = backward_bytes(inp)
-    slots = SLOTS_BWD_PER_ELEMENT * E + SLOTS_BWD_PER_TOKEN_D * b * L * D
+    slots = (SLOTS_BWD_TI_PER_ELEMENT if inp.ti else SLOTS_BWD_PER_ELEMENT) * E + SLOTS_BWD_PER_TOKEN_D * b * L * D
     out = {
         "metric": METRIC,
         "value": E * args.steps / wall,
@@ -574,8 +583,13 @@ def cpu_baseline_backward(inp, bias, softplus, euler, target_s: float = 10.0):
         one = lambda a: None if a is None else a[:1]
         dy = rng.standard_normal((1, L, nch)).astype(np.float32)
         t0 = time.perf_counter()
-        oracle.bwd(one(sub.u), one(sub.delta), sub.A, one(sub.B), one(sub.C), sub.Dskip, one(sub.z), dy=dy,
-                   delta_bias=None if bias is None else bias[:nch], delta_softplus=softplus, euler=euler)
+        if inp.ti:                                    # delta, B, C per channel
+            oracle.bwd(one(sub.u), sub.delta, sub.A, sub.B, sub.C, sub.Dskip, one(sub.z), dy=dy,
+                       delta_bias=None if bias is None else bias[:nch], delta_softplus=softplus, euler=euler,
+                       time_invariant=True)
+        else:
+            oracle.bwd(one(sub.u), one(sub.delta), sub.A, one(sub.B), one(sub.C), sub.Dskip, one(sub.z), dy=dy,
+                       delta_bias=None if bias is None else bias[:nch], delta_softplus=softplus, euler=euler)
         t_used = time.perf_counter() - t0
         if t_used >= target_s * 0.5 or nch >= D:
             break

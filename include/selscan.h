@@ -285,9 +285,8 @@ int selective_scan_step(const void* u, const void* delta, const float* delta_bia
  * recomputed from checkpoints taken every 16 tokens, so nothing from the forward call is
  * needed.
  *   u, delta, delta_bias, A, B, C, Dskip, z, initial_state : the forward call's inputs
- *                    (dims->discretization and dims->delta_softplus as in that call).
- *                    Selective coefficients only: fixed (time-invariant) coefficients return
- *                    SELSCAN_ERR_UNSUPPORTED.
+ *                    (dims->discretization and dims->delta_softplus as in that call), with
+ *                    selective (per-token) or fixed (per-channel delta, B and C) coefficients.
  *   dy             : gradient of y, in dims->io_dtype with the y strides of dims, required.
  *   dlast_state    : [batch][dim][dstate] fp32 gradient of last_state, or NULL (zero).
  * Outputs (device memory, all written, never accumulated into):
@@ -296,6 +295,10 @@ int selective_scan_step(const void* u, const void* delta, const float* delta_bia
  *                    raw part when delta_softplus).  dz is written only if z and dz are both
  *                    non-NULL.  du and ddelta are required.
  *   dB, dC         : [batch][seqlen][dstate] contiguous, in dims->io_dtype, required.
+ *   Fixed coefficients: ddelta is [dim] and dB, dC are [dim][dstate], contiguous in
+ *                    dims->io_dtype: the sums over batch rows and tokens of the per-token
+ *                    terms (the same reverse-time recurrence with Abar and the input
+ *                    coefficient constant per channel and state).
  *   dA             : [dim][dstate] fp32, required.
  *   dDskip, ddelta_bias : [dim] fp32, or NULL to skip.  ddelta_bias is the sum of ddelta
  *                    over batch and tokens.
@@ -314,10 +317,11 @@ int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias
 /* Bytes of device workspace selective_scan_bwd needs for these dims (0 for an empty call
  * or invalid dims): the checkpoints, batch * ceil(seqlen/16) * dim * dstate floats; the
  * per-channel-group partial sums of dB and dC (groups of 64, 32 or 16 channels for dstate up
- * to 16, 32, 64), at most 2 * ceil(dim/16) * batch * seqlen * dstate floats; when the
- * sequence is split into chunks, the running sums of delta at the checkpoints,
- * batch * ceil(seqlen/16) * dim floats, and per-chunk states and adjoints,
- * O(batch * dim * dstate * chunks). */
+ * to 16, 32, 64), at most 2 * ceil(dim/16) * batch * seqlen * dstate floats (fixed
+ * coefficients: 2 * batch * chunks * dim * dstate); when the sequence is split into chunks,
+ * the running sums of delta at the checkpoints, batch * ceil(seqlen/16) * dim floats
+ * (selective coefficients), and per-chunk states and adjoints, O(batch * dim * dstate *
+ * chunks). */
 size_t selective_scan_bwd_workspace_size(const selscan_dims* dims);
 
 /*

@@ -429,13 +429,14 @@ def selective_scan_bwd(u, delta, A, B, C, Dskip=None, z=None, *, dy, dlast_state
                        delta_bias=None, delta_softplus: bool = False, discretization: str = "zoh", workspace=None,
                        stream=None) -> dict:
     """Gradients of selective_scan_fwd (same inputs and options) given dy, the gradient of y,
-    and optionally dlast_state, the gradient of last_state.  Selective coefficients only.
+    and optionally dlast_state, the gradient of last_state.
 
     Returns a dict: du, ddelta, dz (if z) as [batch, L, D] and dB, dC as [batch, L, N], in
     u's dtype; dA [D, N], dDskip [D] (if Dskip), ddelta_bias [D] (if delta_bias) and
-    dinitial_state [batch, D, N] (if initial_state), in float32.  ``workspace`` (a uint8
-    GPU tensor of bwd_workspace_size bytes) is taken from torch's caching allocator when
-    omitted."""
+    dinitial_state [batch, D, N] (if initial_state), in float32.  With fixed coefficients
+    (delta [D], B and C [D, N]) ddelta is [D] and dB, dC are [D, N], in u's dtype.
+    ``workspace`` (a uint8 GPU tensor of bwd_workspace_size bytes) is taken from torch's
+    caching allocator when omitted."""
     import torch
     io = u.dtype
     if u.dim() != 3:
@@ -455,9 +456,12 @@ def selective_scan_bwd(u, delta, A, B, C, Dskip=None, z=None, *, dy, dlast_state
     _check_bias(delta_bias, D)
     dims = make_dims(u, delta, A, B, C, z, dy, discretization=discretization, delta_softplus=delta_softplus)
     dev = u.device
-    g = {"du": torch.empty((batch, L, D), dtype=io, device=dev), "ddelta": torch.empty((batch, L, D), dtype=io, device=dev),
+    ti = delta.dim() == 1 and B.dim() == 2 and C.dim() == 2      # fixed coefficients
+    g = {"du": torch.empty((batch, L, D), dtype=io, device=dev),
+         "ddelta": torch.empty((D,) if ti else (batch, L, D), dtype=io, device=dev),
          "dA": torch.empty((D, N), dtype=torch.float32, device=dev),
-         "dB": torch.empty((batch, L, N), dtype=io, device=dev), "dC": torch.empty((batch, L, N), dtype=io, device=dev)}
+         "dB": torch.empty((D, N) if ti else (batch, L, N), dtype=io, device=dev),
+         "dC": torch.empty((D, N) if ti else (batch, L, N), dtype=io, device=dev)}
     if z is not None:
         g["dz"] = torch.empty((batch, L, D), dtype=io, device=dev)
     if Dskip is not None:

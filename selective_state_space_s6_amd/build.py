@@ -21,7 +21,7 @@ MICROBENCH_LIB = os.path.join(PKG, "libselscan_microbench.so")
 # own (scan_inst_*.hip), which compile in parallel
 SCAN_UNITS = [os.path.join(CSRC, "scan_inst_%s_%s.hip" % (io, ps))
               for io in ("f32", "bf16") for ps in ("single", "state", "apply")]
-SOURCES = SCAN_UNITS + [os.path.join(CSRC, "bwd_kernels.hip"), os.path.join(CSRC, "scan_kernels.hip"),
+SOURCES = SCAN_UNITS + [os.path.join(CSRC, "bwd_kernels.hip"), os.path.join(CSRC, "bwd_ti_kernels.hip"), os.path.join(CSRC, "scan_kernels.hip"),
                         os.path.join(CSRC, "conv_kernels.hip"), os.path.join(CSRC, "ssd_kernels.hip"),
                         os.path.join(CSRC, "selscan_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -595,6 +595,13 @@ hipError_t launch_bwd(bool bf16, const BwdParams& p, hipStream_t stream) {
   return bf16 ? launch_bwd_io<uint16_t>(p, stream) : launch_bwd_io<float>(p, stream);
 }
 
+hipError_t launch_bwd_adjoint_combine(const BwdParams& p, hipStream_t stream) {
+  const int64_t m = p.batch * p.D * p.N;
+  if (m == 0 || p.n_chunks <= 1) return hipSuccess;
+  hipLaunchKernelGGL(bwd_adjoint_combine_kernel, dim3(unsigned((m + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_sum_partials(const float* part, int64_t nparts, int64_t stride, void* out, int64_t m, bool bf16,
                                hipStream_t stream) {
   if (m <= 0) return hipSuccess;

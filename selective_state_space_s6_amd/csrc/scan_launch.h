@@ -158,10 +158,22 @@ struct BwdParams {
   // sum of delta into ck_dsum, for every chunk
   int32_t ck_fwd;
   const float* ck_dsum; // [batch][ntiles][D]
+  // fixed coefficients: [batch][D][n_chunks] each chunk's sum of delta (the chunk state pass
+  // writes it for chunk_prefix_kernel)
+  float* sdsum;
+  // fixed coefficients: B_sd, C_sd (element stride between channels of B[d][n], C[d][n])
+  int64_t B_sd, C_sd;
 };
 // lanes per channel of the backward kernel (4 states per lane): 4, 8 or 16
 int bwd_lanes_per_channel(int64_t N);
 hipError_t launch_bwd(bool bf16, const BwdParams& p, hipStream_t stream);
+// backward of fixed coefficients (bwd_ti_kernels.hip): the chunk end states from zero (for
+// chunk_prefix_kernel), the chunk adjoints from zero (for bwd_adjoint_combine_kernel), or the
+// main pass
+enum { kTiPassState = 0, kTiPassAdjoint = 1, kTiPassMain = 2 };
+hipError_t launch_bwd_ti(bool bf16, int pass, const BwdParams& p, hipStream_t stream);
+// the adjoint combine of the selective backward, on its own (fixed coefficients)
+hipError_t launch_bwd_adjoint_combine(const BwdParams& p, hipStream_t stream);
 // out[i] = sum_{j < nparts} part[j * stride + i], i < m; out in the I/O type when bf16
 hipError_t launch_sum_partials(const float* part, int64_t nparts, int64_t stride, void* out, int64_t m, bool bf16,
                                hipStream_t stream);

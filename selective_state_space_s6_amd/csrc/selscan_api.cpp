@@ -355,6 +355,7 @@ int fwd_noalloc(const void* u, const void* delta, const float* delta_bias, const
 // ---- backward pass
 struct BwdPlan {
   Plan fwd;                   // the forward plan whose chunked state pass supplies the carries
+  bool ti = false;            // fixed coefficients (bwd_ti_kernels.hip)
   int64_t groups = 0, ntiles = 0, chunk_len = 0;
   int32_t n_chunks = 1;
   size_t off_pB = 0, off_pC = 0, off_pA = 0, off_pD = 0, off_pbias = 0;
@@ -373,9 +374,9 @@ int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
   Plan plan;
   int st = make_plan(dims, &plan);
   if (st != SELSCAN_OK) return st;
-  if (plan.ti) return SELSCAN_ERR_UNSUPPORTED;        // backward of fixed coefficients: not built
   const selscan_dims& d = *dims;
   BwdPlan b;
+  b.ti = plan.ti;
   const int64_t cwg = 4 * 64 / selscan::bwd_lanes_per_channel(d.dstate);   // channels per workgroup
   b.groups = (d.dim + cwg - 1) / cwg;
   b.ntiles = (d.seqlen + 15) / 16;
@@ -402,8 +403,9 @@ int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
     }
   }
   b.chunk_len = nc > 1 ? round_up((d.seqlen + nc - 1) / nc, 16) : round_up(d.seqlen > 0 ? d.seqlen : 1, 16);
-  // a forward plan chunked for its 32-bit tile addressing bounds the chunk length
-  if (plan.chunked && plan.chunk_len < b.chunk_len) b.chunk_len = plan.chunk_len;
+  // a forward plan chunked for its 32-bit tile addressing bounds the chunk length (the
+  // selective backward takes its carries from that plan's state pass)
+  if (!plan.ti && plan.chunked && plan.chunk_len < b.chunk_len) b.chunk_len = plan.chunk_len;
   b.n_chunks = d.seqlen > 0 ? int32_t((d.seqlen + b.chunk_len - 1) / b.chunk_len) : 1;
   if (d.batch * b.n_chunks * b.groups > (int64_t(1) << 31) - 1) return SELSCAN_ERR_UNSUPPORTED;
   b.fwd = plan;
@@ -417,10 +419,12 @@ int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
   const int64_t f = int64_t(sizeof(float));
   const int64_t bdn = d.batch * d.dim * d.dstate, ncq = b.n_chunks;
   size_t off = al(f * d.batch * b.ntiles * d.dim * d.dstate);
+  // dB, dC partials: per channel group and token (selective), per batch row and chunk (fixed)
+  const int64_t pbc = b.ti ? ncq * bdn : b.groups * d.batch * d.seqlen * d.dstate;
   b.off_pB = off;
-  off += al(f * b.groups * d.batch * d.seqlen * d.dstate);
+  off += al(f * pbc);
   b.off_pC = off;
-  off += al(f * b.groups * d.batch * d.seqlen * d.dstate);
+  off += al(f * pbc);
   b.off_pA = off;
   off += al(f * ncq * bdn);
   b.off_pD = off;
@@ -438,12 +442,53 @@ int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
     off += al(f * ncq * d.batch * d.dim);
     b.off_adjin = off;
     off += al(f * ncq * bdn);
-    b.off_ckdsum = off;                                   // running sum of delta at every tile start
-    off += al(f * d.batch * b.ntiles * d.dim);
+    if (!b.ti) {
+      b.off_ckdsum = off;                                 // running sum of delta at every tile start
+      off += al(f * d.batch * b.ntiles * d.dim);
+    }
   }
   b.bytes = (d.batch * d.seqlen > 0) ? off : 0;
   *out = b;
   return SELSCAN_OK;
+}
+
+// Fixed coefficients: chunk end states and prefix, chunk adjoints and combine (a split
+// sequence), the main pass, then the sums of the per-(batch row, chunk) partials: dB, dC and
+// ddelta in the I/O type ([D][N], [D][N], [D]), dA, dDskip and ddelta_bias in fp32.
+int bwd_run_ti(selscan::BwdParams& p, const float* A, const float* h0, void* ddelta, float* ddelta_bias, float* dA,
+               void* dB, void* dC, float* dDskip, const selscan_dims& d, const BwdPlan& plan, char* ws,
+               hipStream_t stream) {
+  const bool bf16 = d.io_dtype == SELSCAN_BF16;
+  p.B_sd = d.B_sd;
+  p.C_sd = d.C_sd;
+  hipError_t e = hipSuccess;
+  if (plan.n_chunks > 1) {
+    p.carry = reinterpret_cast<float*>(ws + plan.off_state);
+    p.sdsum = reinterpret_cast<float*>(ws + plan.off_dsum);
+    p.adjG = reinterpret_cast<float*>(ws + plan.off_adjG);
+    p.adjS = reinterpret_cast<float*>(ws + plan.off_adjS);
+    p.adj_in = reinterpret_cast<float*>(ws + plan.off_adjin);
+    e = selscan::launch_bwd_ti(bf16, selscan::kTiPassState, p, stream);
+    selscan::PrefixParams q{};
+    q.A = A; q.dsum = p.sdsum; q.state = p.carry; q.h0 = h0;
+    q.batch = d.batch; q.D = d.dim; q.N = d.dstate; q.n_chunks = plan.n_chunks;
+    int sw = 1;
+    while (sw < plan.n_chunks) sw <<= 1;
+    q.seg_width = sw;
+    if (e == hipSuccess) e = selscan::launch_chunk_prefix(q, stream);
+    if (e == hipSuccess) e = selscan::launch_bwd_ti(bf16, selscan::kTiPassAdjoint, p, stream);
+    if (e == hipSuccess) e = selscan::launch_bwd_adjoint_combine(p, stream);
+  }
+  if (e == hipSuccess) e = selscan::launch_bwd_ti(bf16, selscan::kTiPassMain, p, stream);
+  const int64_t nbc = d.batch * plan.n_chunks, dn = d.dim * d.dstate;
+  if (e == hipSuccess) e = selscan::launch_sum_partials(p.pB, nbc, dn, dB, dn, bf16, stream);
+  if (e == hipSuccess) e = selscan::launch_sum_partials(p.pC, nbc, dn, dC, dn, bf16, stream);
+  if (e == hipSuccess) e = selscan::launch_sum_partials(p.pA, nbc, dn, dA, dn, false, stream);
+  if (e == hipSuccess && dDskip) e = selscan::launch_sum_partials(p.pD, nbc, d.dim, dDskip, d.dim, false, stream);
+  if (e == hipSuccess) e = selscan::launch_sum_partials(p.pbias, nbc, d.dim, ddelta, d.dim, bf16, stream);
+  if (e == hipSuccess && ddelta_bias)
+    e = selscan::launch_sum_partials(p.pbias, nbc, d.dim, ddelta_bias, d.dim, false, stream);
+  return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
 }
 
 int bwd_run(const void* u, const void* delta, const float* delta_bias, const float* A, const void* B, const void* C,
@@ -460,6 +505,12 @@ int bwd_run(const void* u, const void* delta, const float* delta_bias, const flo
     if (e == hipSuccess && dh0 && d.batch > 0)
       e = dlast ? selscan::launch_copy(dh0, dlast, d.batch * d.dim * d.dstate, stream)
                 : selscan::launch_fill_zero(dh0, d.batch * d.dim * d.dstate, stream);
+    if (plan.ti) {          // the shared coefficients' gradients are empty sums too (zero parts)
+      const int64_t dn = d.dim * d.dstate;
+      if (e == hipSuccess && dB) e = selscan::launch_sum_partials(nullptr, 0, 0, dB, dn, bf16, stream);
+      if (e == hipSuccess && dC) e = selscan::launch_sum_partials(nullptr, 0, 0, dC, dn, bf16, stream);
+      if (e == hipSuccess && ddelta) e = selscan::launch_sum_partials(nullptr, 0, 0, ddelta, d.dim, bf16, stream);
+    }
     return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
   }
   selscan::BwdParams p{};
@@ -482,6 +533,7 @@ int bwd_run(const void* u, const void* delta, const float* delta_bias, const flo
   p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
   p.softplus = d.delta_softplus != 0 ? 1 : 0;
   p.dxf = (p.softplus || delta_bias != nullptr) ? 1 : 0;
+  if (plan.ti) return bwd_run_ti(p, A, h0, ddelta, ddelta_bias, dA, dB, dC, dDskip, d, plan, ws, stream);
   if (plan.n_chunks > 1) {
     // the state entering every chunk: the forward's chunked state pass and prefix
     selscan::ScanParams f = scan_params(u, delta, delta_bias, A, B, C, Dskip, z, nullptr, h0, nullptr, d, plan.fwd);

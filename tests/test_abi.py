@@ -206,8 +206,10 @@ def test_backward_errors():
     # checkpoints (2 x 4 tiles x 40 x 16) and two partial sums (one 64-channel group x 2 x 64 x 16)
     assert need >= 4 * (2 * 4 * 40 * 16 + 2 * 1 * 2 * 64 * 16)
     ti = ss.dims_init(ss.SELSCAN_F32, 2, 64, 40, 16, time_invariant=True)
-    assert ss.bwd_workspace_size(ti) == 0
-    assert call_bwd(ti, ws=FAKE, ws_bytes=1 << 30) == ss.SELSCAN_ERR_UNSUPPORTED
+    need_ti = ss.bwd_workspace_size(ti)
+    # fixed coefficients: checkpoints, and partial sums of dB, dC and dA per (batch row, chunk)
+    assert need_ti >= 4 * (2 * 4 * 40 * 16 + 3 * 2 * 40 * 16)
+    assert call_bwd(ti, ws=FAKE, ws_bytes=need_ti - 1) == ss.SELSCAN_ERR_WORKSPACE
     assert call_bwd(d, du=None, ws=FAKE, ws_bytes=need) == ss.SELSCAN_ERR_NULL
     assert call_bwd(d, dA=None, ws=FAKE, ws_bytes=need) == ss.SELSCAN_ERR_NULL
     assert call_bwd(d, du=FAKE_ODD, ws=FAKE, ws_bytes=need) == ss.SELSCAN_ERR_ALIGN
