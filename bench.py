@@ -275,7 +275,8 @@ SIMDS = 256 * 4                  # MI355X: 256 compute units of 4 SIMDs
 
 def run_microbench():
     """The practical roofs, from libselscan_microbench.so (built with the scan's flags): fp32
-    FMA and v_exp_f32 issue rates against wavefronts per SIMD (8 independent chains per lane),
+    FMA, v_exp_f32 and DPP-operand multiply issue rates against wavefronts per SIMD (8
+    independent chains per lane),
     exp2/FMA overlap, streaming copy and write bandwidth, and the shader clock held meanwhile
     (clock64 cycles against the constant-rate wall clock of the same wavefront)."""
     import ctypes
@@ -302,7 +303,8 @@ def run_microbench():
                 "lane_ops_per_s": lanes / (ms.value * 1e-3), "lanes_per_clk_per_simd": round(per_clk, 3)}
 
     out = {"fma": [compute(0, w, 4000) for w in (1, 2, 3, 4, 8)],
-           "exp2": [compute(1, w, 1000) for w in (1, 2, 3, 4, 8)]}
+           "exp2": [compute(1, w, 1000) for w in (1, 2, 3, 4, 8)],
+           "mul_dpp_row_broadcast": [compute(6, w, 2000) for w in (1, 2, 4, 8)]}
     # overlap: exp2 and r fma per exp2 (8 chains of each), 4 wavefronts per SIMD; compare the
     # time with the exp2 and fma runs of the same counts taken alone
     fma4 = next(r for r in out["fma"] if r["waves_per_simd"] == 4)

@@ -4,6 +4,8 @@
 //   fma     : independent fp32 fused multiply-add chains, one VALU instruction per lane each
 //   exp     : independent v_exp_f32 (exp2) chains, the transcendental the scan issues per element
 //   mix     : one exp2 per `ratio` FMAs in independent chains (does the transcendental overlap?)
+//   dpp     : independent fp32 multiplies whose first operand is a DPP row broadcast of another
+//             lane (v_mul_f32 with row_newbcast), the form the scan uses for u and delta
 //   copy    : streaming 16-byte-per-lane copy of one buffer into another (HBM read + write)
 //   fill    : streaming 16-byte-per-lane writes (HBM write only)
 // Every probe records, in wavefront 0 of workgroup 0, the shader-clock counter (clock64) and the
@@ -55,6 +57,27 @@ __global__ __launch_bounds__(kThreads) void exp_kernel(float* out, int iters, fl
     for (int r = 0; r < kRounds; ++r) {
 #pragma unroll
       for (int c = 0; c < kChains; ++c) x[c] = __builtin_amdgcn_exp2f(x[c]);
+    }
+  }
+  stamp(clk, 1);
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += x[c];
+  out[blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+// kChains chains x[c] = bcast15(x[c]) * a: the row-broadcast operand folds into the multiply
+__global__ __launch_bounds__(kThreads) void dpp_kernel(float* out, int iters, float a, uint64_t* clk) {
+  float x[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) x[c] = float(threadIdx.x) * 1e-3f + float(c);
+  stamp(clk, 0);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+#pragma unroll
+      for (int c = 0; c < kChains; ++c)
+        x[c] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[c]), 0x15F, 0xF, 0xF, true)) * a;
     }
   }
   stamp(clk, 1);
@@ -131,11 +154,11 @@ extern "C" {
 int selscan_mb_last_error(void) { return g_err; }
 
 // Compute-rate probes.  kind: 0 fma, 1 exp2, 2 mix with 1 fma per exp2, 3 ratio 2, 4 ratio 4,
-// 5 ratio 8.  blocks workgroups of 256 lanes run `iters` loop iterations of 8 rounds over 8
+// 5 ratio 8, 6 multiply with a DPP row-broadcast operand.  blocks workgroups of 256 lanes run `iters` loop iterations of 8 rounds over 8
 // independent chains.  Outputs: kernel milliseconds, the shader-clock cycles and the wall-clock
 // ticks wavefront 0 of workgroup 0 measured around its loop.  Returns 0 on success.
 int selscan_mb_compute(int kind, int blocks, int iters, float* ms, uint64_t* cycles, uint64_t* ticks) {
-  if (blocks < 1 || iters < 1 || kind < 0 || kind > 5) return -2;
+  if (blocks < 1 || iters < 1 || kind < 0 || kind > 6) return -2;
   float* out = nullptr;
   uint64_t* clk = nullptr;
   hipStream_t s = nullptr;
@@ -151,7 +174,8 @@ int selscan_mb_compute(int kind, int blocks, int iters, float* ms, uint64_t* cyc
       case 2: hipLaunchKernelGGL(mix_kernel<1>, g, t, 0, s, out, iters, a, b, clk); break;
       case 3: hipLaunchKernelGGL(mix_kernel<2>, g, t, 0, s, out, iters, a, b, clk); break;
       case 4: hipLaunchKernelGGL(mix_kernel<4>, g, t, 0, s, out, iters, a, b, clk); break;
-      default: hipLaunchKernelGGL(mix_kernel<8>, g, t, 0, s, out, iters, a, b, clk); break;
+      case 5: hipLaunchKernelGGL(mix_kernel<8>, g, t, 0, s, out, iters, a, b, clk); break;
+      default: hipLaunchKernelGGL(dpp_kernel, g, t, 0, s, out, iters, a, clk); break;
     }
   };
   launch();                                                   // warm-up
