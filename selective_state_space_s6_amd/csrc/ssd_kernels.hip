@@ -286,15 +286,15 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdParams p) {
 // H [N x 64] held in the matrix cores' accumulator registers; no state touches memory.
 // Wavefront w owns the head channels p in [16 w, 16 w + 16): its state columns and its output
 // columns.  Each chunk's inputs are loaded into registers one chunk ahead, so the global
-// loads overlap the previous chunk's arithmetic.  Per chunk (three workgroup barriers):
+// loads overlap the previous chunk's arithmetic.  Per chunk (five workgroup barriers):
 //   stage C and B rows, w-scaled B^T and x^T into LDS: every thread owns an 8-token block of
 //     B and x and transposes it in registers, so the transposed rows go out 16 bytes at a
 //     time; every wavefront forms the chunk's decay prefix itself (one token per lane);
-//   Y[:, cols] = e^cum (C H[:, cols]) + M X[:, cols]: the causal C B^T tiles are formed by
-//     each wavefront as B C^T, whose accumulator layout (lane: 4 consecutive tokens s of one
-//     row t) is, after the decay mask, the A operand of M X under a fixed permutation of the
-//     contraction index that X's operand repeats -- M never touches LDS; C H takes H straight
-//     from the accumulators (the 16x16x16 B operand has the accumulator layout);
+//   M = (C B^T) o decay o mask: the 10 causal 16x16 tiles are shared out over the
+//     wavefronts (C B^T and the mask are the same for every channel of the head), each
+//     formed as B C^T, and written as bf16 over B's rows once every wavefront has read B;
+//   Y[:, cols] = e^cum (C H[:, cols]) + M X[:, cols]: C H takes H straight from the
+//     accumulators (the 16x16x16 B operand has the accumulator layout);
 //   H[:, cols] <- e^cum_end H[:, cols] + B^T diag(w) X[:, cols];
 //   feed-through, gate and 4-byte stores through an fp32 tile in LDS, with x, z and D from
 //     registers.
@@ -512,6 +512,55 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       dtr = load_dt(p, b, h, l0 + kT);
     }
 
+    // M = (C B^T) o decay o causal mask, 10 causal 16 x 16 tiles (ti, tj), tj <= ti, tile k of
+    // them formed by wavefront k mod NW and written over B's rows (which nothing reads once
+    // every wavefront has formed its tiles) as [t][s] bf16 with row stride kRowK.  Lane
+    // (q, r) of tile (ti, tj) holds M[16 ti + r][16 tj + 4 q + i], i < 4: the G result layout.
+    constexpr int kMTiles = 10, kMSlots = (kMTiles + NW - 1) / NW;
+    __bf16* const sM = &sB[0][0];
+    uint2 mres[kMSlots];
+#pragma unroll
+    for (int slot = 0; slot < kMSlots; ++slot) {
+      const int k = w + NW * slot;                         // uniform over the wavefront
+      if (k < kMTiles) {
+        const int ti = k == 0 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+        const int tj = k - ti * (ti + 1) / 2;
+        const int t = 16 * ti + r;
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < N / 32; ++kk) g = mfma(frag(&sB[16 * tj + r][32 * kk + 8 * q]), frag(&sC[t][32 * kk + 8 * q]), g);
+        const float cum_t = s_cum[t];
+        const float4 cs = *reinterpret_cast<const float4*>(&s_cum[16 * tj + 4 * q]);
+        const float4 cw = *reinterpret_cast<const float4*>(&s_c[16 * tj + 4 * q]);
+        const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, cwv[4] = {cw.x, cw.y, cw.z, cw.w};
+        float mv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int sidx = 16 * tj + 4 * q + i;
+          const float m = g[i] * __builtin_amdgcn_exp2f((cum_t - csv[i]) * kLog2e) * cwv[i];
+          mv[i] = sidx <= t ? m : 0.f;                     // a select: the causal mask
+        }
+        mres[slot] = make_uint2(pack_bf16(mv[0], mv[1]), pack_bf16(mv[2], mv[3]));
+      }
+    }
+    __syncthreads();                                      // every wavefront has read B
+#pragma unroll
+    for (int slot = 0; slot < kMSlots; ++slot) {
+      const int k = w + NW * slot;
+      if (k < kMTiles) {
+        const int ti = k == 0 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+        const int tj = k - ti * (ti + 1) / 2;
+        *reinterpret_cast<uint2*>(&sM[(16 * ti + r) * kRowK + 16 * tj + 4 * q]) = mres[slot];
+      }
+    }
+    // the two tiles above the diagonal that the 32-token contraction steps read, (0, 1) and
+    // (2, 3), are zero
+    if (w == NW - 1 || w == NW - 2) {
+      const int ti = w == NW - 1 ? 0 : 2;
+      *reinterpret_cast<uint2*>(&sM[(16 * ti + r) * kRowK + 16 * (ti + 1) + 4 * q]) = make_uint2(0u, 0u);
+    }
+    __syncthreads();                                      // M is complete
+
     // Y[:, cols] = e^cum (C H) + M X
     s16x4 hb[kKT];
 #pragma unroll
@@ -532,49 +581,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       acc[1] *= __builtin_amdgcn_exp2f(ct.y * kLog2e);
       acc[2] *= __builtin_amdgcn_exp2f(ct.z * kLog2e);
       acc[3] *= __builtin_amdgcn_exp2f(ct.w * kLog2e);
-      const int t = 16 * ti + r;                           // this lane's row of M
-      const float cum_t = s_cum[t];
-      bf16x8 cfr[N / 32];                                  // row t of C, the B operand of B C^T
+      // M X over tokens s = 32 kk + 8 q + j (the causal range of row tile ti)
 #pragma unroll
-      for (int k = 0; k < N / 32; ++k) cfr[k] = frag(&sC[t][32 * k + 8 * q]);
-#pragma unroll
-      for (int kk = 0; kk <= ti / 2; ++kk) {
-        // M[t][s] for s = 32 kk + 4q + i (i < 4) and 32 kk + 16 + 4q + i: contraction slot
-        // 8q + j of the 32 holds token 32 kk + 4q + j (j < 4), 32 kk + 16 + 4q + j - 4 (j >= 4)
-        bf16x8 am;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int tj = 2 * kk + half;
-          if (tj > ti) {                                    // above the diagonal: M is zero
-#pragma unroll
-            for (int i = 0; i < 4; ++i) am[4 * half + i] = to_bf16(0.f);
-            continue;
-          }
-          f32x4 g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < N / 32; ++k) g = mfma(frag(&sB[16 * tj + r][32 * k + 8 * q]), cfr[k], g);
-          const float4 cs = *reinterpret_cast<const float4*>(&s_cum[16 * tj + 4 * q]);
-          const float4 cw = *reinterpret_cast<const float4*>(&s_c[16 * tj + 4 * q]);
-          const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, cwv[4] = {cw.x, cw.y, cw.z, cw.w};
-          float mv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int s = 16 * tj + 4 * q + i;
-            const float m = g[i] * __builtin_amdgcn_exp2f((cum_t - csv[i]) * kLog2e) * cwv[i];
-            mv[i] = s <= t ? m : 0.f;                        // a select: the causal mask
-          }
-          const uint2 mp = make_uint2(pack_bf16(mv[0], mv[1]), pack_bf16(mv[2], mv[3]));
-          const bf16x2 m01 = __builtin_bit_cast(bf16x2, mp.x), m23 = __builtin_bit_cast(bf16x2, mp.y);
-          am[4 * half + 0] = m01[0];
-          am[4 * half + 1] = m01[1];
-          am[4 * half + 2] = m23[0];
-          am[4 * half + 3] = m23[1];
-        }
-        const uint2 x0 = *reinterpret_cast<const uint2*>(&sXT[pc][32 * kk + 4 * q]);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(&sXT[pc][32 * kk + 16 + 4 * q]);
-        const uint4 xv = make_uint4(x0.x, x0.y, x1.x, x1.y);
-        acc = mfma(am, __builtin_bit_cast(bf16x8, xv), acc);
-      }
+      for (int kk = 0; kk <= ti / 2; ++kk)
+        acc = mfma(frag(&sM[(16 * ti + r) * kRowK + 32 * kk + 8 * q]), frag(&sXT[pc][32 * kk + 8 * q]), acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sY[16 * ti + 4 * q + i][pc] = acc[i];
     }
