@@ -294,15 +294,11 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdParams p) {
 //     wavefronts (C B^T and the mask are the same for every channel of the head), each
 //     formed as B C^T, and written as bf16 over B's rows once every wavefront has read B;
 //   Y[:, cols] = e^cum (C H[:, cols]) + M X[:, cols]: C H takes H straight from the
-//     accumulators (the 16x16x16 B operand has the accumulator layout);
+//     accumulators (two 16-state tiles' registers form one 32-deep B operand, the
+//     contraction index permuted to match, C's operand read with the same permutation);
 //   H[:, cols] <- e^cum_end H[:, cols] + B^T diag(w) X[:, cols];
 //   feed-through, gate and 4-byte stores through an fp32 tile in LDS, with x, z and D from
 //     registers.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 
 // One chunk's inputs as a thread holds them between the global loads and the LDS staging.
 // Thread t < 256: C pieces t + 256 k (16 bytes each); tokens 8 (t >> 5) .. + 7 of B
@@ -561,21 +557,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     __syncthreads();                                      // M is complete
 
-    // Y[:, cols] = e^cum (C H) + M X
-    s16x4 hb[kKT];
+    // Y[:, cols] = e^cum (C H) + M X.  C H runs over pairs of 16-state tiles (2m, 2m + 1) as
+    // 32-deep products whose contraction slots 8q + j hold states 32m + 4q + j (j < 4) and
+    // 32m + 16 + 4q + j - 4 (j >= 4): the state's accumulator layout, with C read to match.
+    bf16x8 hb[kKT / 2];
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-      const uint32_t lo2 = pack_bf16(hs[kt][0], hs[kt][1]), hi2 = pack_bf16(hs[kt][2], hs[kt][3]);
-      hb[kt] = __builtin_bit_cast(s16x4, make_uint2(lo2, hi2));
-    }
+    for (int m = 0; m < kKT / 2; ++m)
+      hb[m] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(hs[2 * m][0], hs[2 * m][1]),
+                                                    pack_bf16(hs[2 * m][2], hs[2 * m][3]),
+                                                    pack_bf16(hs[2 * m + 1][0], hs[2 * m + 1][1]),
+                                                    pack_bf16(hs[2 * m + 1][2], hs[2 * m + 1][3])));
 #pragma unroll
     for (int ti = 0; ti < kT / 16; ++ti) {
       __builtin_amdgcn_sched_barrier(0);                   // one row tile at a time: bounds the live set
       if (NW == 8 && half != ((ti == 1 || ti == 2) ? 1 : 0)) continue;   // the other wavefront's tile
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
-        acc = mfma16(*reinterpret_cast<const s16x4*>(&sC[16 * ti + r][16 * kt + 4 * q]), hb[kt], acc);
+      for (int m = 0; m < kKT / 2; ++m) {
+        const uint2 c0 = *reinterpret_cast<const uint2*>(&sC[16 * ti + r][32 * m + 4 * q]);
+        const uint2 c1 = *reinterpret_cast<const uint2*>(&sC[16 * ti + r][32 * m + 16 + 4 * q]);
+        acc = mfma(__builtin_bit_cast(bf16x8, make_uint4(c0.x, c0.y, c1.x, c1.y)), hb[m], acc);
+      }
       const float4 ct = *reinterpret_cast<const float4*>(&s_cum[16 * ti + 4 * q]);
       acc[0] *= __builtin_amdgcn_exp2f(ct.x * kLog2e);
       acc[1] *= __builtin_amdgcn_exp2f(ct.y * kLog2e);
