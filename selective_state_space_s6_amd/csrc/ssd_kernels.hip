@@ -407,7 +407,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __align__(16) float sY[kT][kRowY];           // the chunk's output before D, gate
   __shared__ __align__(16) float s_cum[kT], s_c[kT], s_w[kT];
 
-  const int64_t bh = blockIdx.x, h = bh % p.H, b = bh / p.H;
+  // the heads of one batch row read the same B and C rows: the XCD-contiguous order keeps
+  // them on one XCD (two for 80 heads), whose L2 then fetches those rows once
+  const int64_t bh = xcd_contiguous_block(blockIdx.x, gridDim.x), h = bh % p.H, b = bh / p.H;
   const int64_t L = p.L, H = p.H;
   const float A = p.A[h];
   const bool euler = p.euler != 0;
