@@ -12,7 +12,9 @@
 //   dB_t     = sum_d lambda_t c_t u_t,   dC_t = sum_d dyp_t h_t,   dDskip = sum_{b,t} dyp_t u_t
 //   dz_t     = dy_t yp_t sigmoid(z_t) (1 + z_t (1 - sigmoid(z_t)))
 // dc/ddelta is Abar (ZOH, also at A == 0) or 1 (first order); dc/da is delta^2 phi(delta a)
-// with phi(x) = (x e^x - (e^x - 1)) / x^2 (ZOH; phi(0) = 1/2) or 0 (first order).
+// with phi(x) = (x e^x - (e^x - 1)) / x^2 (ZOH; phi(0) = 1/2) or 0 (first order).  Where every
+// rate of a workgroup is away from zero (ZOH), a dA_t = delta_t g_t - lambda_t c_t B_t u_t with
+// g_t the token's ddelta term, so dA is accumulated in that form and divided by a once.
 //
 // Work decomposition: SL = N/4 (4, 8 or 16) lanes share a channel and each owns 4 of its
 // states, in VGPRs; a workgroup of four wavefronts owns (batch row b, chunk of the sequence,
