@@ -362,9 +362,12 @@ struct BwdPlan {
   size_t off_state = 0, off_dsum = 0, off_adjG = 0, off_adjS = 0, off_adjin = 0, off_ckdsum = 0, bytes = 0;
 };
 
-// Main-pass workgroups resident on MI355X at once: 256 compute units x 2 (every main-pass
-// instantiation takes 256 VGPRs per lane and at most 80.6 KB of LDS).
+// Main-pass workgroups resident on MI355X at once: 256 compute units x 2 (the selective
+// main-pass instantiations take 214-256 VGPRs per lane and at most 80.9 KB of LDS; those of
+// fixed coefficients 173-203 up to 32 states), or x 3 for fixed coefficients with 16 lanes
+// per channel (33..64 states: 153-154 VGPRs, three wavefronts per SIMD).
 constexpr int64_t kBwdSlots = 512;
+constexpr int64_t kBwdSlotsTi16 = 768;
 
 // Validate dims for the backward pass and lay out its workspace (groups: channel groups of
 // one workgroup, 64, 32 or 16 channels):
@@ -389,8 +392,9 @@ int make_bwd_plan(const selscan_dims* dims, BwdPlan* out) {
   if (items > 0 && d.seqlen >= 128) {
     int64_t max_nc = d.seqlen / 64;                              // chunks of at least 64 tokens
     if (max_nc > kMaxChunks) max_nc = kMaxChunks;
+    const int64_t slots = (plan.ti && selscan::bwd_lanes_per_channel(d.dstate) == 16) ? kBwdSlotsTi16 : kBwdSlots;
     auto cost = [&](int64_t n) {
-      const int64_t rounds = (items * n + kBwdSlots - 1) / kBwdSlots;
+      const int64_t rounds = (items * n + slots - 1) / slots;
       return rounds * round_up((d.seqlen + n - 1) / n, 16);
     };
     int64_t best = cost(1);
