@@ -385,8 +385,8 @@ def main():
                     choices=sorted(s6_workloads.WORKLOADS) + sorted(s6_workloads.SSD_WORKLOADS))
     ap.add_argument("--path", default="auto", choices=["auto", "single", "chunked", "conv"],
                     help="conv: the convolution mode (fixed coefficients only)")
-    ap.add_argument("--ssd-path", default="auto", choices=["auto", "fused", "chunked"],
-                    help="scalar-decay workloads: state kept on chip (fused) or chunk-parallel")
+    ap.add_argument("--ssd-path", default="auto", choices=["auto", "fused", "chunked", "segmented"],
+                    help="scalar-decay workloads: automatic, on chip over the whole sequence (fused), chunk-parallel, or on chip over sequence segments")
     ap.add_argument("--step-size", default="given", choices=["given", "softplus"],
                     help="softplus: the kernel computes softplus(raw + bias) from a pre-activation")
     ap.add_argument("--discretization", default="zoh", choices=["zoh", "euler"])

@@ -345,8 +345,13 @@ typedef struct selscan_ssd_dims {
   int64_t dstate;          /* N: 64 or 128 */
   int32_t path;            /* 0 automatic; 1 one workgroup per (batch, head) walking the chunks
                               with the state on chip (no workspace); 2 chunk-parallel (chunk
-                              states in the workspace, a scan over them, then the outputs) */
-  int32_t reserved;        /* 0 */
+                              states in the workspace, a scan over them, then the outputs);
+                              3 on chip over sequence segments: each segment's end state from
+                              zero (a state-only walk), composed across segments, then one
+                              workgroup per (batch, segment, head) walks its segment from the
+                              state carried in (segment states in the workspace) */
+  int32_t segments;        /* path 3: number of sequence segments (equal runs of 64-token chunks,
+                              at most one per chunk), 0 to choose automatically; 0 otherwise */
 } selscan_ssd_dims;
 
 /*
@@ -370,9 +375,12 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
                            size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of selective_scan_ssd_fwd (0 for an empty call, invalid dims or the
- * on-chip path): for the chunk-parallel path, per (batch row, head, 64-token chunk) one fp32
- * [dstate][headdim] chunk state, one decay, and one bf16 carried-in state.  The automatic
- * path takes the on-chip one when batch * nheads >= 96 (measured crossover on MI355X). */
+ * on-chip path over the whole sequence): for the chunk-parallel path, per (batch row, head,
+ * 64-token chunk) one fp32 [dstate][headdim] chunk state, one decay, and one bf16 carried-in
+ * state; for the on-chip path over segments, per (batch row, head, segment) one fp32 state
+ * and one decay.  The automatic path takes the chunk-parallel one when batch * nheads *
+ * ceil(seqlen / 64) <= 512, else the on-chip one over the segment count a cost model of
+ * MI355X times picks (one segment, the whole sequence, where splitting does not pay). */
 size_t selective_scan_ssd_workspace_size(const selscan_ssd_dims* dims);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

@@ -496,17 +496,18 @@ class SsdDims(ctypes.Structure):
     """Mirror of ``selscan_ssd_dims`` in include/selscan.h."""
     _fields_ = [("abi_version", ctypes.c_int32), ("discretization", ctypes.c_int32), ("batch", ctypes.c_int64),
                 ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
-                ("dstate", ctypes.c_int64), ("path", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("dstate", ctypes.c_int64), ("path", ctypes.c_int32), ("segments", ctypes.c_int32)]
 
 
-SSD_PATHS = {"auto": 0, "fused": 1, "chunked": 2}
+SSD_PATHS = {"auto": 0, "fused": 1, "chunked": 2, "segmented": 3}
 
 
-def ssd_dims(batch, seqlen, nheads, headdim, dstate, discretization="zoh", path="auto") -> SsdDims:
+def ssd_dims(batch, seqlen, nheads, headdim, dstate, discretization="zoh", path="auto", segments=0) -> SsdDims:
     d = SsdDims()
     d.abi_version = SELSCAN_ABI_VERSION
     d.discretization = DISCRETIZATIONS[discretization]
     d.path = SSD_PATHS[path]
+    d.segments = int(segments)
     d.batch, d.seqlen, d.nheads, d.headdim, d.dstate = int(batch), int(seqlen), int(nheads), int(headdim), int(dstate)
     return d
 
@@ -517,11 +518,12 @@ def ssd_workspace_size(dims: SsdDims) -> int:
 
 def selective_scan_ssd_fwd(x, delta, A, B, C, Dskip=None, z=None, y=None, *, initial_state=None,
                            return_last_state: bool = False, discretization: str = "zoh", path: str = "auto",
-                           workspace=None, stream=None):
+                           segments: int = 0, workspace=None, stream=None):
     """The scalar-decay (Mamba-2) layer on the GPU (bf16 x, delta, B, C, z, y; fp32 A, Dskip,
     states).  x, z: [batch, L, H, 64]; delta: [batch, L, H]; A: [H]; B, C: [batch, L, N] with
     N = 64 or 128; Dskip: [H * 64]; initial_state: [batch, H, 64, N].  All contiguous.
-    Returns (y, last_state or None)."""
+    path: "auto", "fused" (on chip), "chunked" (chunk-parallel) or "segmented" (on chip over
+    `segments` sequence segments, 0 = chosen by the library).  Returns (y, last_state or None)."""
     import torch
     if x.dim() != 4:
         raise ValueError("x must be [batch, L, H, headdim]")
@@ -538,7 +540,7 @@ def selective_scan_ssd_fwd(x, delta, A, B, C, Dskip=None, z=None, y=None, *, ini
     if y is None:
         y = torch.empty_like(x)
     last = torch.empty((batch, H, P, N), dtype=torch.float32, device=x.device) if return_last_state else None
-    dims = ssd_dims(batch, L, H, P, N, discretization, path)
+    dims = ssd_dims(batch, L, H, P, N, discretization, path, segments)
     torch_stream = stream if (stream is None or hasattr(stream, "cuda_stream")) else None
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream

@@ -198,10 +198,14 @@ struct SsdParams {
   float* state;         // workspace [batch][H][n_chunks][64][N]: chunk states (transposed)
   uint16_t* carry;      // workspace [batch][H][n_chunks][64][N]: bf16 state entering each chunk
   float* decay;         // workspace [batch][H][n_chunks]: exp(A sum delta) of each chunk
+  float* seg_state;     // workspace [batch][H][n_seg][64][N]: segment end states, then carried-in states
+  float* seg_decay;     // workspace [batch][H][n_seg]: exp(A sum delta) of each segment
   int64_t batch, L, H, N;
   int64_t n_chunks;     // ceil(L / 64)
+  int64_t n_seg;        // on-chip path: sequence segments (1: the whole sequence per workgroup)
+  int64_t seg_chunks;   // chunks per segment (the last may have fewer)
   int32_t euler;
-  int32_t fused;        // 1: one workgroup per (batch, head) keeps the state on chip (no workspace)
+  int32_t fused;        // 1: on chip, one workgroup per (batch, segment, head), the state in registers
 };
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);
 

@@ -726,9 +726,78 @@ int selective_scan_bwd(const void* u, const void* delta, const float* delta_bias
   return st;
 }
 
-constexpr int64_t kSsdFusedMinItems = 96;    // (batch, head) workgroups from which the on-chip path is faster
+// Automatic path: chunk-parallel up to this many (batch, head, 64-token chunk) units (short,
+// narrow calls, where launches dominate), else on chip over the modelled best segment count
+// (measured crossover on MI355X).
+constexpr int64_t kSsdChunkParallelMaxUnits = 512;
 
-static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chunks, bool* fused) {
+struct SsdPlan {
+  int64_t n_chunks = 0;
+  bool fused = false;
+  int64_t n_seg = 1, seg_chunks = 0;
+  size_t ws_bytes = 0;
+  size_t seg_state_bytes = 0;                 // offset of the segment decays in the workspace
+};
+
+// Segments of n_chunks chunks for a requested count: equal runs of ceil(n_chunks / count)
+// chunks, none empty.
+static void ssd_set_segments(SsdPlan& pl, int64_t count) {
+  const int64_t nc = pl.n_chunks > 0 ? pl.n_chunks : 1;
+  const int64_t want = count < 1 ? 1 : count > nc ? nc : count;
+  pl.seg_chunks = (nc + want - 1) / want;
+  pl.n_seg = (nc + pl.seg_chunks - 1) / pl.seg_chunks;
+}
+
+// Modelled time (us, N = 128) of the on-chip path over `count` segments, from times measured
+// on MI355X (256 CUs): the output walk costs t_pair per 64-token chunk for each of two
+// workgroups sharing a CU (four wavefronts each), t_alone for a workgroup alone on its CU,
+// and its workgroups are dealt out in rounds of two per CU; the segment state pass costs
+// t_state1 per chunk alone on a CU plus t_state_more per further workgroup sharing it (up to
+// four at once); the segment carries move every segment state twice at about 5 TB/s; and
+// splitting at all costs two more launches and the carried-in states' loads (t_split).
+static double ssd_onchip_cost(int64_t items, int64_t nc, int64_t dstate, int64_t count) {
+  constexpr double t_pair = 6.25, t_alone = 4.1, t_state1 = 1.6, t_state_more = 0.6, t_split = 12.0;
+  constexpr int64_t kCUs = 256;
+  SsdPlan pl;
+  pl.n_chunks = nc;
+  ssd_set_segments(pl, count);
+  const double len = double(pl.seg_chunks);
+  const int64_t w = items * pl.n_seg;
+  double t;
+  if (w <= kCUs) {
+    t = len * t_alone;                                   // one eight-wavefront workgroup per CU
+  } else {
+    const int64_t full = w / (2 * kCUs), rem = w % (2 * kCUs);
+    t = double(full) * len * t_pair + (rem == 0 ? 0.0 : rem <= kCUs ? len * t_alone : len * t_pair);
+  }
+  if (pl.n_seg > 1) {
+    const int64_t per_cu = (items * (pl.n_seg - 1) + kCUs - 1) / kCUs;
+    const int64_t rounds = (per_cu + 3) / 4, conc = per_cu < 4 ? per_cu : 4;
+    t += double(rounds) * len * (t_state1 + double(conc - 1) * t_state_more);
+    t += double(w) * double(dstate) * 64.0 * 8.0 / 5.0e6 + t_split;
+  }
+  return t;
+}
+
+// Segment count of the automatic on-chip path: the modelled fastest split, fewer segments on
+// a near tie; no split unless it saves at least 8 % (a split re-reads x for the segment state
+// pass and moves the segment states, about 1.4x the layer's bytes at 2.7B widths).
+static int64_t ssd_auto_segments(int64_t items, int64_t nc, int64_t dstate) {
+  static const int64_t kCounts[] = {2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32, 48, 64, 96, 128};
+  int64_t best = 0;
+  double best_t = 0.0;
+  for (int64_t c : kCounts) {
+    if (c > nc) break;
+    const double t = ssd_onchip_cost(items, nc, dstate, c);
+    if (best == 0 || t < best_t * 0.98) {
+      best = c;
+      best_t = t;
+    }
+  }
+  return best != 0 && best_t < 0.92 * ssd_onchip_cost(items, nc, dstate, 1) ? best : 1;
+}
+
+static int ssd_check(const selscan_ssd_dims* d, SsdPlan* pl) {
   if (!d) return SELSCAN_ERR_NULL;
   if (d->abi_version != SELSCAN_ABI_VERSION) return SELSCAN_ERR_ABI;
   if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1) return SELSCAN_ERR_DIMS;
@@ -737,32 +806,44 @@ static int ssd_check(const selscan_ssd_dims* d, size_t* ws_bytes, int64_t* n_chu
   const int64_t nc = (d->seqlen + 63) / 64;
   if (d->batch * d->nheads * nc > (int64_t(1) << 31) - 1 || d->batch * d->nheads * d->dstate * 64 > (int64_t(1) << 36))
     return SELSCAN_ERR_UNSUPPORTED;
-  if (d->path < 0 || d->path > 2 || d->reserved != 0) return SELSCAN_ERR_UNSUPPORTED;
-  const int64_t bhc = d->batch * d->nheads * nc;
-  *n_chunks = nc;
-  *fused = d->path == 1 || (d->path == 0 && d->batch * d->nheads >= kSsdFusedMinItems);
-  *ws_bytes = (d->batch * d->seqlen > 0 && !*fused)
-                  ? size_t(round_up(bhc * d->dstate * 64 * int64_t(sizeof(float)), 256) +
-                           round_up(bhc * int64_t(sizeof(float)), 256) + round_up(bhc * d->dstate * 64 * 2, 256))
-                  : 0;
+  if (d->path < 0 || d->path > 3 || d->segments < 0 || (d->segments != 0 && d->path != 3)) return SELSCAN_ERR_UNSUPPORTED;
+  const int64_t items = d->batch * d->nheads, bhc = items * nc;
+  SsdPlan p;
+  p.n_chunks = nc;
+  p.fused = d->path == 1 || d->path == 3 || (d->path == 0 && items * nc > kSsdChunkParallelMaxUnits);
+  // the segment state pass addresses one batch row of x through a buffer resource (32-bit offsets)
+  const bool seg_ok = (d->seqlen + 64) * d->nheads * 64 * 2 < (int64_t(1) << 31);
+  if (d->path == 3 && !seg_ok) return SELSCAN_ERR_UNSUPPORTED;
+  if (d->path == 3) ssd_set_segments(p, d->segments > 0 ? d->segments : ssd_auto_segments(items, nc, d->dstate));
+  else if (d->path == 0 && p.fused && seg_ok) ssd_set_segments(p, ssd_auto_segments(items, nc, d->dstate));
+  else ssd_set_segments(p, 1);
+  if (d->batch * d->seqlen == 0) {
+    p.ws_bytes = 0;
+  } else if (!p.fused) {
+    p.ws_bytes = size_t(round_up(bhc * d->dstate * 64 * int64_t(sizeof(float)), 256) +
+                        round_up(bhc * int64_t(sizeof(float)), 256) + round_up(bhc * d->dstate * 64 * 2, 256));
+  } else if (p.n_seg > 1) {
+    p.seg_state_bytes = size_t(round_up(items * p.n_seg * d->dstate * 64 * int64_t(sizeof(float)), 256));
+    p.ws_bytes = p.seg_state_bytes + size_t(round_up(items * p.n_seg * int64_t(sizeof(float)), 256));
+  }
+  *pl = p;
   return SELSCAN_OK;
 }
 
 size_t selective_scan_ssd_workspace_size(const selscan_ssd_dims* dims) {
-  size_t ws = 0;
-  int64_t nc = 0;
-  bool fused = false;
-  return ssd_check(dims, &ws, &nc, &fused) == SELSCAN_OK ? ws : 0;
+  SsdPlan pl;
+  return ssd_check(dims, &pl) == SELSCAN_OK ? pl.ws_bytes : 0;
 }
 
 int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                            const float* Dskip, const void* z, void* y, const float* initial_state, float* last_state,
                            const selscan_ssd_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
-  size_t need = 0;
-  int64_t nc = 0;
-  bool fused = false;
-  int st = ssd_check(dims, &need, &nc, &fused);
+  SsdPlan pl;
+  int st = ssd_check(dims, &pl);
   if (st != SELSCAN_OK) return st;
+  const size_t need = pl.ws_bytes;
+  const int64_t nc = pl.n_chunks;
+  const bool fused = pl.fused;
   const selscan_ssd_dims& d = *dims;
   const bool no_tokens = d.batch * d.seqlen == 0;
   if (!A || (!no_tokens && (!x || !delta || !B || !C || !y))) return SELSCAN_ERR_NULL;
@@ -794,6 +875,12 @@ int selective_scan_ssd_fwd(const void* x, const void* delta, const float* A, con
   p.batch = d.batch; p.L = d.seqlen; p.H = d.nheads; p.N = d.dstate; p.n_chunks = nc;
   p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
   p.fused = fused ? 1 : 0;
+  p.n_seg = pl.n_seg;
+  p.seg_chunks = pl.seg_chunks;
+  if (fused && pl.n_seg > 1) {
+    p.seg_state = static_cast<float*>(ws);
+    p.seg_decay = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.seg_state_bytes);
+  }
   if (!fused) {
     p.state = static_cast<float*>(ws);
     const int64_t bhc = d.batch * d.nheads * nc;

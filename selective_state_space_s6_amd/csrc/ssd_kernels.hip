@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "scan_launch.h"
 
@@ -315,7 +317,8 @@ struct ChunkRegs {
 
 // Loads address memory as a chunk base common to the workgroup plus a 32-bit offset per
 // thread, so that no 64-bit address per token stays live in vector registers.
-template <int N>
+// WITH_C false: B and x only (the segment state pass reads no C).
+template <int N, bool WITH_C = true>
 __device__ __forceinline__ void load_chunk(ChunkRegs<N>& rg, const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
   const int tid = threadIdx.x, sb = tid >> 5, lo = tid & 31;
   const int64_t L = p.L, H = p.H;
@@ -329,6 +332,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<N>& rg, const SsdParams& p,
   // are zeroed when staged, and their C and z reach only outputs that are never stored.
 #pragma unroll
   for (int k = 0; k < ChunkRegs<N>::kCv; ++k) {
+    if (!WITH_C) break;
     const int i = tid + 256 * k, t = i / (N / 8), n0 = (i % (N / 8)) * 8;
     rg.c[k] = *reinterpret_cast<const uint4*>(Cc + uint32_t(min(t, rows - 1) * N + n0));
   }
@@ -391,11 +395,67 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// x^T rows 2 lo, 2 lo + 1 of this thread's 8-token block, 16 bytes each
+template <int kRowK>
+__device__ __forceinline__ void stage_xt(const uint32_t (&x)[8], __bf16 (*sXT)[kRowK], int sb, int lo) {
+  uint32_t o0[4], o1[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const uint32_t a0 = x[j], a1 = x[j + 1];
+    o0[j >> 1] = (a0 & 0xffffu) | (a1 << 16);
+    o1[j >> 1] = (a0 >> 16) | (a1 & 0xffff0000u);
+  }
+  *reinterpret_cast<uint4*>(&sXT[2 * lo][8 * sb]) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+  *reinterpret_cast<uint4*>(&sXT[2 * lo + 1][8 * sb]) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+}
+
+// w-scaled B^T rows (states lo N/32 ..) of this thread's 8-token block
+template <int N, int kRowK>
+__device__ __forceinline__ void stage_bt(const uint32_t (&bw)[8][N / 64], const float* s_w, __bf16 (*sBT)[kRowK],
+                                         int sb, int lo) {
+  constexpr int kNV = N / 32;
+  const float4 wa = *reinterpret_cast<const float4*>(&s_w[8 * sb]);
+  const float4 wb = *reinterpret_cast<const float4*>(&s_w[8 * sb + 4]);
+  const float wj[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+  for (int e = 0; e < kNV; ++e) {
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const uint32_t w0 = bw[j][e >> 1], w1 = bw[j + 1][e >> 1];
+      const float v0 = (e & 1) ? bf16_hi(w0) : bf16_lo(w0);
+      const float v1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
+      o[j >> 1] = pack_bf16(v0 * wj[j], v1 * wj[j + 1]);
+    }
+    *reinterpret_cast<uint4*>(&sBT[lo * kNV + e][8 * sb]) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// H[:, cols] <- dec H + B^T diag(w) X[:, cols], on the accumulators that hold the state
+template <int N, int kRowK>
+__device__ __forceinline__ void state_update(f32x4 (&hs)[N / 16], const __bf16 (*sBT)[kRowK],
+                                             const __bf16 (*sXT)[kRowK], int pc, int q, int r, float dec) {
+  const bf16x8 xf0 = frag(&sXT[pc][8 * q]), xf1 = frag(&sXT[pc][32 + 8 * q]);
+#pragma unroll
+  for (int kt = 0; kt < N / 16; ++kt) {
+    f32x4 acc = hs[kt] * dec;
+    acc = mfma(frag(&sBT[16 * kt + r][8 * q]), xf0, acc);
+    acc = mfma(frag(&sBT[16 * kt + r][32 + 8 * q]), xf1, acc);
+    hs[kt] = acc;
+  }
+}
+
 // NW = 4: wavefront w owns channel block w and all four 16-token output tiles of a chunk.
 // NW = 8 (for at most one workgroup per CU): wavefronts w and w + 4 share channel block w & 3,
 // each holding its state (updated identically by both), and split the output tiles
 // {0, 3} / {1, 2} (equal causal work); the first four stage the chunk and store the output.
-template <int N, int NW>
+//
+// Sequence segments (SM_SEG_OUT): the chunks are split into n_seg runs of seg_chunks, and a
+// workgroup walks one (batch row, segment, head) from the segment's carried-in state, which
+// ssd_seg_state_kernel and ssd_seg_prefix_kernel leave in the workspace.  SM_WHOLE is the
+// walk over the whole sequence, compiled without the segment bookkeeping.
+enum { SM_WHOLE = 0, SM_SEG_OUT = 1 };
+template <int N, int NW, int SM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_fused_kernel(SsdParams p) {
   constexpr int kRowN = N + 8, kRowK = kT + 8, kRowY = kP + 4;
   constexpr int kKT = N / 16;                              // 16-state tiles of the state
@@ -409,7 +469,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // the heads of one batch row read the same B and C rows: the XCD-contiguous order keeps
   // them on one XCD (two for 80 heads), whose L2 then fetches those rows once
-  const int64_t bh = xcd_contiguous_block(blockIdx.x, gridDim.x), h = bh % p.H, b = bh / p.H;
+  // (the segments of one batch row too: item = (b * segments + seg) * H + h)
+  constexpr bool SEGS = SM == SM_SEG_OUT;
+  const int64_t nseg = SEGS ? p.n_seg : 1;
+  const int64_t item = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int64_t h = item % p.H, bsg = item / p.H, seg = SEGS ? bsg % nseg : 0, b = SEGS ? bsg / nseg : bsg;
+  const int64_t bh = b * p.H + h;
+  const int64_t c_begin = SEGS ? seg * p.seg_chunks : 0;
+  const int64_t c_end = !SEGS ? p.n_chunks : c_begin + p.seg_chunks < p.n_chunks ? c_begin + p.seg_chunks : p.n_chunks;
   const int64_t L = p.L, H = p.H;
   const float A = p.A[h];
   const bool euler = p.euler != 0;
@@ -427,20 +494,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const float d0 = p.Dskip != nullptr ? p.Dskip[h * kP + 2 * lo] : 0.f;
   const float d1 = p.Dskip != nullptr ? p.Dskip[h * kP + 2 * lo + 1] : 0.f;
 
-  // the state: tile kt covers rows n = 16 kt + 4q + i of column pc
+  // the state: tile kt covers rows n = 16 kt + 4q + i of column pc.  It starts from the
+  // segment's carried-in state (after ssd_seg_prefix_kernel), the initial state, or zero.
+  const float* const h_in = SEGS ? p.seg_state + (bh * nseg + seg) * kP * N
+                                 : p.h0 != nullptr ? p.h0 + bh * kP * N : nullptr;
   f32x4 hs[kKT];
 #pragma unroll
   for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hs[kt][i] = p.h0 != nullptr ? p.h0[(bh * kP + pc) * N + 16 * kt + 4 * q + i] : 0.f;
+    for (int i = 0; i < 4; ++i) hs[kt][i] = h_in != nullptr ? h_in[pc * N + 16 * kt + 4 * q + i] : 0.f;
 
   ChunkRegs<N> rg;
-  if (stager) load_chunk<N>(rg, p, b, h, 0);
-  uint32_t dtr = load_dt(p, b, h, 0);
+  if (stager) load_chunk<N>(rg, p, b, h, c_begin * kT);
+  uint32_t dtr = load_dt(p, b, h, c_begin * kT);
   uint32_t zr[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  if (gate) load_gate<JN>(zr, p, b, h, 0, j0);
+  if (gate) load_gate<JN>(zr, p, b, h, c_begin * kT, j0);
   const float invA = A != 0.f ? 1.f / A : 0.f;
-  for (int64_t chunk = 0; chunk < p.n_chunks; ++chunk) {
+  for (int64_t chunk = c_begin; chunk < c_end; ++chunk) {
     const int64_t l0 = chunk * kT;
     const int rows = int(L - l0 < kT ? L - l0 : kT);      // tokens of this chunk inside the sequence
     // the chunk's decay prefix, formed by every wavefront (token = lane)
@@ -474,38 +544,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       else
         *reinterpret_cast<uint32_t*>(&sB[8 * sb + j][lo * kNV]) = rg.b[j][0];
     }
-    {                                                      // x^T rows 2 lo, 2 lo + 1
-      uint32_t o0[4], o1[4];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const uint32_t a0 = rg.x[j], a1 = rg.x[j + 1];
-        o0[j >> 1] = (a0 & 0xffffu) | (a1 << 16);
-        o1[j >> 1] = (a0 >> 16) | (a1 & 0xffff0000u);
-      }
-      *reinterpret_cast<uint4*>(&sXT[2 * lo][8 * sb]) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-      *reinterpret_cast<uint4*>(&sXT[2 * lo + 1][8 * sb]) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-    }
+    stage_xt(rg.x, sXT, sb, lo);
     }
     __syncthreads();                                      // C, B, x and the decay prefix are staged
-    if (stager) {                                          // w-scaled B^T rows, 8 tokens each
-      const float4 wa = *reinterpret_cast<const float4*>(&s_w[8 * sb]);
-      const float4 wb = *reinterpret_cast<const float4*>(&s_w[8 * sb + 4]);
-      const float wj[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-#pragma unroll
-      for (int e = 0; e < kNV; ++e) {
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const uint32_t w0 = rg.b[j][e >> 1], w1 = rg.b[j + 1][e >> 1];
-          const float v0 = (e & 1) ? bf16_hi(w0) : bf16_lo(w0);
-          const float v1 = (e & 1) ? bf16_hi(w1) : bf16_lo(w1);
-          o[j >> 1] = pack_bf16(v0 * wj[j], v1 * wj[j + 1]);
-        }
-        *reinterpret_cast<uint4*>(&sBT[lo * kNV + e][8 * sb]) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    }
+    if (stager) stage_bt<N>(rg.b, s_w, sBT, sb, lo);
     __builtin_amdgcn_sched_barrier(0);                     // the staged registers are free: reuse them
-    if (chunk + 1 < p.n_chunks) {                          // lands during the arithmetic
+    if (chunk + 1 < c_end) {                               // lands during the arithmetic
       if (stager) load_chunk<N>(rg, p, b, h, l0 + kT);
       dtr = load_dt(p, b, h, l0 + kT);
     }
@@ -593,16 +637,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int i = 0; i < 4; ++i) sY[16 * ti + 4 * q + i][pc] = acc[i];
     }
     __syncthreads();                                      // the output tile and B^T are complete
-    // H[:, cols] <- e^cum_end H + B^T diag(w) X[:, cols]
-    const float dec = __builtin_amdgcn_exp2f(cum_end * kLog2e);
-    const bf16x8 xf0 = frag(&sXT[pc][8 * q]), xf1 = frag(&sXT[pc][32 + 8 * q]);
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-      f32x4 acc = hs[kt] * dec;
-      acc = mfma(frag(&sBT[16 * kt + r][8 * q]), xf0, acc);
-      acc = mfma(frag(&sBT[16 * kt + r][32 + 8 * q]), xf1, acc);
-      hs[kt] = acc;
-    }
+    state_update<N>(hs, sBT, sXT, pc, q, r, __builtin_amdgcn_exp2f(cum_end * kLog2e));
     // feed-through, gate, bf16 stores: tokens 8 sb + j0 .. + JN - 1, channels 2 lo, 2 lo + 1
     uint16_t* const yc = yg + ((b * L + l0) * H + h) * kP;
     const uint4 xa = *reinterpret_cast<const uint4*>(&sXT[2 * lo][8 * sb]);      // x[8 sb + j][2 lo]
@@ -630,14 +665,161 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (8 * sb + j0 + jj < rows)
           *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j0 + jj) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[jj];
     }
-    if (gate && chunk + 1 < p.n_chunks) load_gate<JN>(zr, p, b, h, l0 + kT, j0);   // lands during the next chunk
+    if (gate && chunk + 1 < c_end) load_gate<JN>(zr, p, b, h, l0 + kT, j0);   // lands during the next chunk
   }
-  if (p.last_state != nullptr && half == 0) {                // (NW = 8: both halves hold the same state)
+  if (p.last_state != nullptr && half == 0 && (!SEGS || seg == nseg - 1)) {   // (NW = 8: both halves hold the same state)
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) p.last_state[(bh * kP + pc) * N + 16 * kt + 4 * q + i] = hs[kt][i];
   }
+}
+
+// Segment end states.  The end state of a segment walked from zero is one contraction over
+// its tokens, S = sum_s exp(cum_seg_end - cum_s) c_s B_s x_s^T, so no running state has to be
+// decayed chunk by chunk: the chunks are walked from the segment's end backwards, carrying
+// R = log of the decay from the current chunk's end to the segment's end, and each chunk adds
+// B^T diag(w) X with w_s = exp(R + cum_end - cum_s) c_s (at most c_s: nothing overflows) onto
+// the accumulators.  w scales x (64 channels) rather than B (N states).  Operands arrive
+// through buffer resources over the batch row, so tokens past the sequence end read as zero
+// and a load needs no address arithmetic; they are issued two chunks ahead (two register
+// sets, used alternately).  Every segment but the last (whose end state is never carried);
+// leaves S as [p][n] and the segment's decay exp(A sum delta).  One workgroup (4 wavefronts)
+// per (batch row, segment, head); wavefront w owns states w N/4 .. (w+1) N/4 - 1 of all 64
+// channels, and stages tokens 16 w .. 16 w + 15 of each chunk.
+template <int N>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void ssd_seg_state_kernel(SsdParams p) {
+  constexpr int kRowK = kT + 8, kNV = N / 32, kRT = N / 64;   // kRT: 16-state row tiles per wavefront
+  constexpr int kRsrcWord3 = 0x00020000;
+  __shared__ __align__(16) __bf16 sBT[N][kRowK];          // B[s][n] as [n][s]
+  __shared__ __align__(16) __bf16 sXT[kP][kRowK];         // w_s x[s][p] as [p][s]
+  __shared__ __align__(16) float s_w[4][kT];              // each wavefront's own copy of the weights
+  const int64_t nseg = p.n_seg, nrun = nseg - 1;
+  const int64_t item = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int64_t h = item % p.H, bsg = item / p.H, seg = bsg % nrun, b = bsg / nrun, bh = b * p.H + h;
+  const int64_t L = p.L, H = p.H;
+  const int c_begin = int(seg * p.seg_chunks);
+  const int c_end = int(c_begin + p.seg_chunks < p.n_chunks ? c_begin + p.seg_chunks : p.n_chunks);
+  const float A = p.A[h];
+  const float invA = A != 0.f ? 1.f / A : 0.f;
+  const bool euler = p.euler != 0;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, q = lane >> 4, r = lane & 15;
+  const int sb = tid >> 5, lo = tid & 31, n0 = w * (N / 4);
+  // batch row b (x and delta: from head h), sized to the sequence end; the host keeps a row
+  // under 2^31 bytes
+  const auto rX = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(p.x) + (b * L * H + h) * kP), (short)0,
+      int((L * H - h) * kP * 2), kRsrcWord3);
+  const auto rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(static_cast<const uint16_t*>(p.B) + b * L * N),
+                                                    (short)0, int(L * N * 2), kRsrcWord3);
+  const auto rD = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(p.delta) + b * L * H + h), (short)0, int((L * H - h) * 2),
+      kRsrcWord3);
+  const int tokX = int(H) * kP * 2, tokB = N * 2, tokD = int(H) * 2;   // bytes between tokens
+  const uint32_t voX = uint32_t(8 * sb * tokX + 4 * lo), voB = uint32_t(8 * sb * tokB + 2 * kNV * lo);
+  const uint32_t voD = uint32_t(lane * tokD);
+  uint32_t xr[2][8], br[2][8][N / 64], dr[2] = {0u, 0u};
+  auto load = [&](int chunk, auto set_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xr[S][j] = __builtin_amdgcn_raw_buffer_load_b32(rX, voX, (chunk * kT + j) * tokX, 0);
+      if constexpr (N == 128) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rB, voB, (chunk * kT + j) * tokB, 0);
+        br[S][j][0] = v[0];
+        br[S][j][1 % (N / 64)] = v[1];
+      } else {
+        br[S][j][0] = __builtin_amdgcn_raw_buffer_load_b32(rB, voB, (chunk * kT + j) * tokB, 0);
+      }
+    }
+    dr[S] = __builtin_amdgcn_raw_buffer_load_b16(rD, voD, chunk * kT * tokD, 0);
+  };
+  f32x4 hs[kRT][4];                                        // S[n0 + 16 kt + 4q + i][16 ct + r]
+#pragma unroll
+  for (int kt = 0; kt < kRT; ++kt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) hs[kt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float R = 0.f;                                           // log decay from this chunk's end to the segment's
+  auto step = [&](int chunk, auto set_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+    const float dt = __uint_as_float(uint32_t(dr[S]) << 16);   // zero past the sequence end
+    const float cum = wave_prefix_sum(dt * A);
+    const float a = __builtin_amdgcn_exp2f(dt * A * kLog2e);
+    const float cc = euler ? dt : zoh_coeff_exact(dt, A, invA, a);
+    const float cum_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
+    s_w[w][lane] = __builtin_amdgcn_exp2f((R + cum_end - cum) * kLog2e) * cc;
+    R += cum_end;
+    __syncthreads();                                      // the previous chunk's LDS reads are done
+    {                                                      // w-scaled x^T rows 2 lo, 2 lo + 1
+      const float4 wa = *reinterpret_cast<const float4*>(&s_w[w][8 * sb]);
+      const float4 wb = *reinterpret_cast<const float4*>(&s_w[w][8 * sb + 4]);
+      const float wj[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+      uint32_t xs[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[j] = pack_bf16(bf16_lo(xr[S][j]) * wj[j], bf16_hi(xr[S][j]) * wj[j]);
+      stage_xt(xs, sXT, sb, lo);
+    }
+#pragma unroll
+    for (int e = 0; e < kNV; ++e) {                       // B^T rows lo kNV + e
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const uint32_t w0 = br[S][j][e >> 1], w1 = br[S][j + 1][e >> 1];
+        o[j >> 1] = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+      }
+      *reinterpret_cast<uint4*>(&sBT[lo * kNV + e][8 * sb]) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (chunk - 2 >= c_begin) load(chunk - 2, set_tag);  // two chunks ahead, into the registers just staged
+    __syncthreads();                                      // x^T and B^T are complete
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 bt[kRT], xt[4];
+#pragma unroll
+      for (int kt = 0; kt < kRT; ++kt) bt[kt] = frag(&sBT[n0 + 16 * kt + r][32 * ks + 8 * q]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) xt[ct] = frag(&sXT[16 * ct + r][32 * ks + 8 * q]);
+#pragma unroll
+      for (int kt = 0; kt < kRT; ++kt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) hs[kt][ct] = mfma(bt[kt], xt[ct], hs[kt][ct]);
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  load(c_end - 1, S0{});
+  if (c_end - 2 >= c_begin) load(c_end - 2, S1{});
+  for (int chunk = c_end - 1; chunk >= c_begin; chunk -= 2) {
+    step(chunk, S0{});
+    if (chunk - 1 >= c_begin) step(chunk - 1, S1{});
+  }
+  float* const so = p.seg_state + (bh * nseg + seg) * kP * N;
+#pragma unroll
+  for (int kt = 0; kt < kRT; ++kt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      *reinterpret_cast<f32x4*>(&so[(16 * ct + r) * N + n0 + 16 * kt + 4 * q]) = hs[kt][ct];
+  if (tid == 0) p.seg_decay[bh * nseg + seg] = __builtin_amdgcn_exp2f(R * kLog2e);
+}
+
+// Segment carries: the state entering segment s, H_in(s + 1) = decay(s) H_in(s) + S(s) from
+// H_in(0) = the initial state (or zero), written over S(s) in the workspace (each slot is read
+// before it is written).  One thread per (b, h, p, n).
+__global__ __launch_bounds__(256) void ssd_seg_prefix_kernel(SsdParams p, int N) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t np = int64_t(N) * kP;
+  if (i >= p.batch * p.H * np) return;
+  const int64_t bh = i / np, e = i % np;
+  const int64_t nseg = p.n_seg;
+  float run = p.h0 != nullptr ? p.h0[bh * np + e] : 0.f;
+  float* const S = p.seg_state + bh * nseg * np + e;
+  const float* const dec = p.seg_decay + bh * nseg;
+  for (int64_t s = 0; s + 1 < nseg; ++s) {
+    const float sv = S[s * np];
+    S[s * np] = run;
+    run = fmaf(dec[s], run, sv);
+  }
+  S[(nseg - 1) * np] = run;
 }
 
 constexpr int64_t kFusedWideMaxItems = 256;   // (batch, head) workgroups: one per CU of MI355X
@@ -646,12 +828,26 @@ template <int N>
 hipError_t launch_ssd_n(const SsdParams& p, hipStream_t stream) {
   if (p.batch * p.H == 0) return hipSuccess;
   if (p.fused) {
+    const int64_t items = p.batch * p.H * p.n_seg;
+    if (p.n_seg > 1) {                       // segment end states, then their carries
+      hipLaunchKernelGGL(ssd_seg_state_kernel<N>, dim3(unsigned(p.batch * p.H * (p.n_seg - 1))), dim3(256), 0, stream, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t m = p.batch * p.H * int64_t(N) * kP;
+      hipLaunchKernelGGL(ssd_seg_prefix_kernel, dim3(unsigned((m + 255) / 256)), dim3(256), 0, stream, p, N);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     // up to one workgroup per CU: eight wavefronts, two per SIMD, split each chunk's output
     // tiles; beyond that four, so that two workgroups share a CU
-    if (p.batch * p.H <= kFusedWideMaxItems)
-      hipLaunchKernelGGL((ssd_fused_kernel<N, 8>), dim3(unsigned(p.batch * p.H)), dim3(512), 0, stream, p);
+    if (p.n_seg > 1 && items <= kFusedWideMaxItems)
+      hipLaunchKernelGGL((ssd_fused_kernel<N, 8, SM_SEG_OUT>), dim3(unsigned(items)), dim3(512), 0, stream, p);
+    else if (p.n_seg > 1)
+      hipLaunchKernelGGL((ssd_fused_kernel<N, 4, SM_SEG_OUT>), dim3(unsigned(items)), dim3(256), 0, stream, p);
+    else if (items <= kFusedWideMaxItems)
+      hipLaunchKernelGGL((ssd_fused_kernel<N, 8, SM_WHOLE>), dim3(unsigned(items)), dim3(512), 0, stream, p);
     else
-      hipLaunchKernelGGL((ssd_fused_kernel<N, 4>), dim3(unsigned(p.batch * p.H)), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((ssd_fused_kernel<N, 4, SM_WHOLE>), dim3(unsigned(items)), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   const int64_t blocks = p.batch * p.H * p.n_chunks;

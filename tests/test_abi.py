@@ -241,8 +241,18 @@ def test_ssd_errors():
     assert ss.ssd_workspace_size(ss.ssd_dims(2, 200, 24, 64, 128)) > 0                   # automatic: chunks
     assert ss.ssd_workspace_size(ss.ssd_dims(2, 200, 3, 64, 128, path="chunked")) == need
     bad_path = ss.ssd_dims(2, 200, 3, 64, 128)
-    bad_path.path = 3
+    bad_path.path = 4
     assert call(bad_path) == ss.SELSCAN_ERR_UNSUPPORTED
+    # segments: only with the segmented path, never negative
+    assert call(ss.ssd_dims(2, 200, 3, 64, 128, path="fused", segments=2)) == ss.SELSCAN_ERR_UNSUPPORTED
+    assert call(ss.ssd_dims(2, 200, 3, 64, 128, path="segmented", segments=-1)) == ss.SELSCAN_ERR_UNSUPPORTED
+    # segmented: one fp32 state and one decay per (batch row, head, segment); 200 tokens are
+    # 4 chunks, so 3 segments are runs of 2, 2 (two segments) and 100 are 4 segments of one chunk
+    seg_ws = lambda k: ss.ssd_workspace_size(ss.ssd_dims(2, 200, 3, 64, 128, path="segmented", segments=k))
+    rnd = lambda v: (v + 255) // 256 * 256
+    assert seg_ws(1) == 0
+    assert seg_ws(3) == rnd(6 * 2 * 128 * 64 * 4) + rnd(6 * 2 * 4)
+    assert seg_ws(100) == rnd(6 * 4 * 128 * 64 * 4) + rnd(6 * 4 * 4)
 
 
 def test_ssd_struct_layout_matches_header():

@@ -4,7 +4,8 @@
 chunk products run on bf16 matrix cores with fp32 accumulation, so the bar is the bf16 one:
 max|y - y_ref| / max|y_ref| <= 2e-2, and the same for the final state.  Cases: several 64-token
 chunks with a ragged last one, one chunk, a single token, both state sizes, both input
-coefficients, with and without gate and feed-through, and an initial state."""
+coefficients, with and without gate and feed-through, an initial state, and the on-chip walk
+over sequence segments (forced segment counts, ragged segments, both workgroup widths)."""
 import numpy as np
 import pytest
 
@@ -32,7 +33,7 @@ def make(rng, b, L, H, N, gate=True, dskip=True):
     return x, dl, A, B, C, Ds, z
 
 
-def run(inp, h0=None, euler=False, path="auto"):
+def run_gpu(inp, h0=None, euler=False, path="auto", segments=0):
     import selective_state_space_s6_amd as ss
     t = torch()
     x, dl, A, B, C, Ds, z = inp
@@ -41,10 +42,16 @@ def run(inp, h0=None, euler=False, path="auto"):
                                         None if Ds is None else t.from_numpy(Ds).cuda(), g(z),
                                         initial_state=None if h0 is None else t.from_numpy(h0).cuda(),
                                         return_last_state=True, discretization="euler" if euler else "zoh",
-                                        path=path)
+                                        path=path, segments=segments)
     t.cuda.synchronize()
+    return y.float().cpu().numpy(), last.cpu().numpy()
+
+
+def run(inp, h0=None, euler=False, path="auto", segments=0):
+    y, last = run_gpu(inp, h0=h0, euler=euler, path=path, segments=segments)
+    x, dl, A, B, C, Ds, z = inp
     y_ref, l_ref = oracle.ssd_fwd(x, dl, A, B, C, Ds, z, h0=h0, euler=euler)
-    return rel_err(y.float().cpu().numpy(), y_ref), rel_err(last.cpu().numpy(), l_ref)
+    return rel_err(y, y_ref), rel_err(last, l_ref)
 
 
 @pytest.mark.parametrize("path", ["fused", "chunked"])
@@ -82,6 +89,46 @@ def test_ssd_many_heads_long(path):
     assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
 
 
+@pytest.mark.parametrize("segments", [2, 3, 5, 100])
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("L", [200, 1000])
+def test_ssd_segmented_parity(L, N, segments):
+    """On chip over sequence segments: segment end states from zero, composed across segments,
+    then each segment walked from its carried-in state.  Ragged last chunks and segments, a
+    segment count above the chunk count (one chunk per segment), an initial state."""
+    rng = np.random.default_rng(L + N + segments)
+    h0 = rng.standard_normal((2, 3, 64, N)).astype(np.float32) if segments % 2 else None
+    e_y, e_l = run(make(rng, 2, L, 3, N), h0=h0, path="segmented", segments=segments)
+    log_errors("ssd/segmented L=%d N=%d segments=%d" % (L, N, segments), y=e_y, last_state=e_l, io="bf16")
+    assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
+
+
+@pytest.mark.parametrize("euler", [False, True])
+def test_ssd_segmented_four_wavefront_workgroups(euler):
+    """More than 256 (batch, segment, head) workgroups: the four-wavefront output pass.  The
+    oracle runs on three of the heads (heads are independent given B and C)."""
+    rng = np.random.default_rng(11 + euler)
+    x, dl, A, B, C, Ds, z = make(rng, 2, 700, 66, 64)
+    h0 = rng.standard_normal((2, 66, 64, 64)).astype(np.float32)
+    y, last = run_gpu((x, dl, A, B, C, Ds, z), h0=h0, euler=euler, path="segmented", segments=3)
+    hs = np.array([0, 31, 65])
+    ch = (hs[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+    y_ref, l_ref = oracle.ssd_fwd(x[:, :, hs], dl[:, :, hs], A[hs], B, C, Ds[ch], z[:, :, hs], h0=h0[:, hs],
+                                  euler=euler)
+    e_y, e_l = rel_err(y[:, :, hs], y_ref), rel_err(last[:, hs], l_ref)
+    log_errors("ssd/segmented/nw4 euler=%s" % euler, y=e_y, last_state=e_l, io="bf16")
+    assert e_y <= TOL["bf16"] and e_l <= TOL["bf16"], (e_y, e_l)
+
+
+def test_ssd_one_segment_is_the_on_chip_walk():
+    """One segment is the on-chip path itself: the same kernel, bit for bit."""
+    rng = np.random.default_rng(12)
+    inp = make(rng, 2, 333, 3, 128)
+    a = run_gpu(inp, path="fused")
+    b = run_gpu(inp, path="segmented", segments=1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 _FULL_REF = {}
 
 
@@ -99,11 +146,11 @@ def _full_reference(name):
     return _FULL_REF[name]
 
 
-@pytest.mark.parametrize("path", ["auto", "chunked"])
+@pytest.mark.parametrize("path", ["auto", "fused", "segmented", "chunked"])
 @pytest.mark.parametrize("name", sorted(s6_workloads.SSD_WORKLOADS))
 def test_ssd_full_size_sampled_heads(name, path):
     """The benchmark's workloads at full size (the automatic path, which the benchmark times,
-    and the chunk-parallel one), checked against the oracle on three heads."""
+    and every forced one), checked against the oracle on three heads."""
     import selective_state_space_s6_amd as ss
     t = torch()
     inp, hs, y_ref, l_ref = _full_reference(name)
