@@ -460,15 +460,21 @@ void bwd_kernel(BwdParams p) {
       if (j % 4 == 0) {
         __builtin_amdgcn_sched_barrier(0);
         wave_sync();
-        // outputs (array, token j + jj, state n) of the group, SL / 2 per lane
+        // outputs (array, token j + jj, state n) of the group, SL / 2 per lane; four partial
+        // sums over channels cc = k mod 4, so that four reads are in flight at once
 #pragma unroll
         for (int r = 0; r < SL / 2; ++r) {
           const int o = lane + 64 * r;
           const int arr = o / (4 * NP), jj = (o / NP) % 4, n = o % NP;
-          float acc = 0.f;
+          const float* const col = &sRed[w][arr][jj][n];
+          float a4[4];
 #pragma unroll
-          for (int cc = 0; cc < CW; ++cc) acc += sRed[w][arr][jj][cc * NP + n];
-          sBC[w][arr][j + jj][n] = acc;
+          for (int k = 0; k < 4; ++k) a4[k] = col[k * NP];
+#pragma unroll
+          for (int cc = 4; cc < CW; cc += 4)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) a4[k] += col[(cc + k) * NP];
+          sBC[w][arr][j + jj][n] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
         }
         wave_sync();
         __builtin_amdgcn_sched_barrier(0);
