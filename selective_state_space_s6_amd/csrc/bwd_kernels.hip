@@ -70,6 +70,38 @@ __device__ __forceinline__ float chan_sum(float v) {
   return v;
 }
 
+// Four consecutive channels of one token as raw bits, through a buffer resource (reads past
+// its size return zero, writes past it are dropped).
+template <typename IO> struct quad4;
+template <> struct quad4<float> {
+  using raw = uint32_t __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
+    return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
+  }
+  static __device__ __forceinline__ float get(const raw& v, int i) { return __uint_as_float(v[i]); }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so, const float (&x)[4]) {
+    const raw v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                           vo, so, 0);
+  }
+};
+template <> struct quad4<uint16_t> {
+  using raw = uint32_t __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so) {
+    return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0));
+  }
+  static __device__ __forceinline__ float get(const raw& v, int i) {
+    const uint32_t w = v[i >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t vo, int so, const float (&x)[4]) {
+    const raw v = {uint32_t(bf16_rne(x[0])) | (uint32_t(bf16_rne(x[1])) << 16),
+                   uint32_t(bf16_rne(x[2])) | (uint32_t(bf16_rne(x[3])) << 16)};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r,
+                                          vo, so, 0);
+  }
+};
+
 // at least this many wavefronts per SIMD (caps the registers)
 constexpr int kBwdMinWaves = 2;
 
@@ -95,7 +127,11 @@ enum { BWD_ADJOINT = 0, BWD_MAIN = 1, BWD_MAIN_EULER = 2, BWD_MAIN_EXACT = 3 };
 //       (zoh_coeff_exact); a workgroup whose channels own a rate below kSmallRate (zero
 //       included) runs in the second, every other one in the first, and each exits at once
 //       in the other kernel.
-template <typename IO, int SL, int MODE>
+// VEC: u, delta, dy, z and du, ddelta, dz move as 4-channel vectors through buffer resources
+// (D % 4 == 0, rows and batch strides on 4-element boundaries, aligned bases; the host checks),
+// one access per (token, 4 channels) with no per-element address arithmetic; otherwise one
+// element per access.
+template <typename IO, int SL, int MODE, bool VEC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwdMinWaves)))
 void bwd_kernel(BwdParams p) {
   using T = io_traits<IO>;
@@ -199,12 +235,57 @@ void bwd_kernel(BwdParams p) {
   IO xu[ET], xd[ET], xy[ET], xz[ET], xB[EB], xC[EB];
   float xH[4], xS = 0.f;
   int pend_nt = kBTile;                                     // valid tokens of the tile in flight
+  // VEC: thread (token vj, channel quad vq) of the tile moves channels d0 + 4 vq .. + 3 of
+  // token vj; threads past the tile's 16 x CWG / 4 vectors (whole wavefronts) move nothing.
+  // Resources are based at (b, the chunk's first token, d0) and end at the chunk's last
+  // element, so the ragged last tile and channels past D read zero and write nothing.
+  using Q4 = quad4<IO>;
+  constexpr int kVT = kBTile * CWG / 4;
+  constexpr uint32_t kOOB = 0x80000000u;                    // an offset past every resource
+  const int vj = tid % kBTile, vq = tid / kBTile;
+  const bool vthr = tid < kVT;
+  const bool von = vthr && d0 + 4 * vq < D;
+  const int64_t vrows = l_end - l_begin;
+  auto vrsrc = [&](const void* base, int64_t sb, int64_t sl) __attribute__((always_inline)) {
+    const char* const p0 = static_cast<const char*>(base) + (b * sb + l_begin * sl + d0) * int64_t(sizeof(IO));
+    const int64_t bytes = vrows > 0 ? ((vrows - 1) * sl + (D - d0)) * int64_t(sizeof(IO)) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p0), (short)0, int(bytes), 0x00020000);
+  };
+  auto voff = [&](int64_t sl) __attribute__((always_inline)) {
+    return von ? uint32_t((vj * sl + 4 * vq) * int64_t(sizeof(IO))) : kOOB;
+  };
+  const auto rU = vrsrc(VEC ? p.u : nullptr, p.u_sb, p.u_sl), rD = vrsrc(VEC ? p.delta : nullptr, p.delta_sb, p.delta_sl);
+  const auto rY = vrsrc(VEC ? p.dy : nullptr, p.dy_sb, p.dy_sl);
+  const auto rZ = vrsrc(VEC && gated ? p.z : nullptr, p.z_sb, p.z_sl);
+  const uint32_t voU = voff(p.u_sl), voD = voff(p.delta_sl), voY = voff(p.dy_sl), voZ = voff(p.z_sl);
+  const int tsU = int(kBTile * p.u_sl * int64_t(sizeof(IO))), tsD = int(kBTile * p.delta_sl * int64_t(sizeof(IO)));
+  const int tsY = int(kBTile * p.dy_sl * int64_t(sizeof(IO))), tsZ = int(kBTile * p.z_sl * int64_t(sizeof(IO)));
+  // outputs: contiguous [batch][L][D]
+  const auto rDU = vrsrc(VEC && MODE != BWD_ADJOINT ? p.du : nullptr, L * D, D);
+  const auto rDD = vrsrc(VEC && MODE != BWD_ADJOINT ? p.ddelta : nullptr, L * D, D);
+  const auto rDZ = vrsrc(VEC && MODE != BWD_ADJOINT ? p.dz : nullptr, L * D, D);
+  typename Q4::raw vU{}, vD{}, vY{}, vZ{};
+  float vbias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (VEC && von && p.delta_bias != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vbias[i] = p.delta_bias[d0 + 4 * vq + i];
+  }
   auto issue = [&](int64_t t, bool all) __attribute__((always_inline)) {
     const int nt = t == ntiles - 1 ? last_nt : kBTile;
     pend_nt = nt;
     const int64_t l0 = l_begin + t * kBTile;
+    if constexpr (VEC) {
+      if (vthr) {                                            // wave-uniform
+        if (MODE != BWD_ADJOINT) vU = Q4::load(rU, voU, int(t) * tsU);
+        vD = Q4::load(rD, voD, int(t) * tsD);
+        if (all) {
+          vY = Q4::load(rY, voY, int(t) * tsY);
+          if (gated) vZ = Q4::load(rZ, voZ, int(t) * tsZ);
+        }
+      }
+    }
 #pragma unroll
-    for (int r = 0; r < ET; ++r) {
+    for (int r = 0; r < (VEC ? 0 : ET); ++r) {
       const int j = tj0 + kTStep * r;
       const int jq = j < nt ? j : nt - 1;
       if (MODE != BWD_ADJOINT) xu[r] = u_b[(l0 + jq) * p.u_sl + tdq];   // the adjoint needs no u, B
@@ -229,8 +310,35 @@ void bwd_kernel(BwdParams p) {
   };
   auto stage = [&](bool all) __attribute__((always_inline)) {
     const int nt = pend_nt;
+    if constexpr (VEC) {
+      if (vthr) {                                            // wave-uniform
 #pragma unroll
-    for (int r = 0; r < ET; ++r) {
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 4 * vq + i;
+          const float vd = Q4::get(vD, i);                   // zero past the chunk's end and D
+          if (MODE != BWD_ADJOINT) sTok[0][ch][vj] = Q4::get(vU, i);
+          const float x = vd + vbias[i];
+          sTok[1][ch][vj] = p.dxf ? (sp ? softplus_f32(x) : x) : vd;
+          if (all) {
+            const float vy = Q4::get(vY, i);
+            float dyp = vy, gzf = 0.f;
+            if (gated) {
+              const float zz = Q4::get(vZ, i);
+              const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+              dyp = vy * zz * sg;
+              gzf = vy * sg * fmaf(zz, 1.f - sg, 1.f);
+            }
+            sTok[2][ch][vj] = dyp;
+            if (MODE != BWD_ADJOINT) {
+              sTok[3][ch][vj] = gzf;
+              sTok[4][ch][vj] = sp ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < (VEC ? 0 : ET); ++r) {
       const int j = tj0 + kTStep * r;
       const bool ok = tcok && j < nt;
       const float vd = ok ? T::widen(xd[r]) : 0.f;
@@ -505,7 +613,22 @@ void bwd_kernel(BwdParams p) {
       }
     }
     // the tile's du, ddelta (and dz), coalesced over the workgroup's channels
-    {
+    if constexpr (VEC) {
+      if (vthr) {                                            // wave-uniform
+        float o0[4], o1[4], o2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o0[i] = sTok[0][4 * vq + i][vj];
+          o1[i] = sTok[1][4 * vq + i][vj];
+          o2[i] = sTok[2][4 * vq + i][vj];
+        }
+        const int ts = int(kBTile * D * int64_t(sizeof(IO)));
+        const uint32_t vo = von ? uint32_t((vj * D + 4 * vq) * int64_t(sizeof(IO))) : kOOB;
+        Q4::store(rDU, vo, int(t) * ts, o0);
+        Q4::store(rDD, vo, int(t) * ts, o1);
+        if (p.dz != nullptr) Q4::store(rDZ, vo, int(t) * ts, o2);
+      }
+    } else {
       const int64_t o = (b * L + l_begin + t * kBTile) * D + d0 + tc;
       IO* const du_t = static_cast<IO*>(p.du) + o;
       IO* const ddl_t = static_cast<IO*>(p.ddelta) + o;
@@ -592,7 +715,10 @@ template <typename IO, int SL, int MODE>
 hipError_t launch_bwd_k(const BwdParams& p, hipStream_t stream) {
   const int64_t blocks = p.batch * int64_t(MODE == BWD_ADJOINT ? p.n_chunks - 1 : p.n_chunks) * p.groups;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_kernel<IO, SL, MODE>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  if (p.vec)
+    hipLaunchKernelGGL((bwd_kernel<IO, SL, MODE, true>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((bwd_kernel<IO, SL, MODE, false>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

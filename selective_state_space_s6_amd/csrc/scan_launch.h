@@ -163,6 +163,10 @@ struct BwdParams {
   float* sdsum;
   // fixed coefficients: B_sd, C_sd (element stride between channels of B[d][n], C[d][n])
   int64_t B_sd, C_sd;
+  // 1: u, delta, dy, z and du, ddelta, dz move as 4-channel vectors (D % 4 == 0; their row
+  // and batch strides multiples of 4 elements, rows at least D long; bases aligned to 4
+  // elements; a chunk's span under 2^31 bytes)
+  int32_t vec;
 };
 // lanes per channel of the backward kernel (4 states per lane): 4, 8 or 16
 int bwd_lanes_per_channel(int64_t N);

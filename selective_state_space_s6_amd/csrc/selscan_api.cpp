@@ -537,6 +537,17 @@ int bwd_run(const void* u, const void* delta, const float* delta_bias, const flo
   p.euler = d.discretization == SELSCAN_DISC_EULER ? 1 : 0;
   p.softplus = d.delta_softplus != 0 ? 1 : 0;
   p.dxf = (p.softplus || delta_bias != nullptr) ? 1 : 0;
+  {
+    const int64_t es = bf16 ? 2 : 4, span_max = (int64_t(1) << 31) / es - d.dim;
+    auto vec_ok = [&](const void* q, int64_t sb, int64_t sl) {
+      return q == nullptr || (aligned(q, size_t(4 * es)) && sb % 4 == 0 && sl % 4 == 0 && sl >= d.dim &&
+                              plan.chunk_len * sl < span_max);
+    };
+    p.vec = (d.dim % 4 == 0 && vec_ok(u, d.u_sb, d.u_sl) && vec_ok(delta, d.delta_sb, d.delta_sl) &&
+             vec_ok(dy, d.y_sb, d.y_sl) && vec_ok(z, d.z_sb, d.z_sl) && vec_ok(du, d.seqlen * d.dim, d.dim) &&
+             vec_ok(ddelta, d.seqlen * d.dim, d.dim) && vec_ok(z ? dz : nullptr, d.seqlen * d.dim, d.dim))
+                ? 1 : 0;
+  }
   if (plan.ti) return bwd_run_ti(p, A, h0, ddelta, ddelta_bias, dA, dB, dC, dDskip, d, plan, ws, stream);
   if (plan.n_chunks > 1) {
     // the state entering every chunk: the forward's chunked state pass and prefix
