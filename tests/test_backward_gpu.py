@@ -20,7 +20,8 @@ def torch():
     return t
 
 
-def run_case(inp, *, delta=None, bias=None, softplus=False, euler=False, h0=None, dlast=None, seed=5):
+def run_case(inp, *, delta=None, bias=None, softplus=False, euler=False, h0=None, dlast=None, seed=5, row_pad=0):
+    """row_pad > 0: u, delta, z and dy are views into rows of D + row_pad elements."""
     import selective_state_space_s6_amd as ss
     t = torch()
     rng = np.random.default_rng(seed)
@@ -32,9 +33,17 @@ def run_case(inp, *, delta=None, bias=None, softplus=False, euler=False, h0=None
     ref = oracle.bwd(inp.u, dl, inp.A, inp.B, inp.C, inp.Dskip, inp.z, dy=dy, dlast=dlast, h0=h0, delta_bias=bias,
                      euler=euler, delta_softplus=softplus)
     io = inp.io
+
+    def tok(x):
+        if x is None or row_pad == 0:
+            return dev(x, io)
+        wide = np.zeros(x.shape[:2] + (D + row_pad,), np.float32)
+        wide[..., :D] = x
+        return dev(wide, io)[..., :D]
+
     g = ss.selective_scan_bwd(
-        dev(inp.u, io), dev(dl, io), t.from_numpy(inp.A).cuda(), dev(inp.B, io), dev(inp.C, io),
-        None if inp.Dskip is None else t.from_numpy(inp.Dskip).cuda(), dev(inp.z, io), dy=dev(dy, io),
+        tok(inp.u), tok(dl), t.from_numpy(inp.A).cuda(), dev(inp.B, io), dev(inp.C, io),
+        None if inp.Dskip is None else t.from_numpy(inp.Dskip).cuda(), tok(inp.z), dy=tok(dy),
         dlast_state=None if dlast is None else t.from_numpy(dlast).cuda(),
         initial_state=None if h0 is None else t.from_numpy(h0).cuda(),
         delta_bias=None if bias is None else t.from_numpy(bias).cuda(), delta_softplus=softplus,
@@ -64,6 +73,17 @@ CASES = {
 def test_backward_parity(name):
     inp = s6_workloads.generate(name, "active", **CASES[name])
     check(run_case(inp), inp.io, name)
+
+
+@pytest.mark.parametrize("name", ["mamba130m_f32", "longctx_bf16"])
+@pytest.mark.parametrize("layout", ["odd_channels", "padded_rows"])
+def test_backward_element_staging(name, layout):
+    """Layouts that the 4-channel vector staging does not take -- a channel count off the
+    4-channel grid, rows of u, delta, z and dy 2 elements longer than D -- take the element-wise
+    staging; same bar."""
+    D = 18 if layout == "odd_channels" else 20
+    inp = s6_workloads.generate(name, "active", batch=2, L=150, D=D)
+    check(run_case(inp, row_pad=2 if layout == "padded_rows" else 0), inp.io, "%s/%s" % (name, layout))
 
 
 @pytest.mark.parametrize("N", [3, 8, 16, 17, 32, 48, 64])
