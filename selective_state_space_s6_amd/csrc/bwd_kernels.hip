@@ -715,10 +715,18 @@ template <typename IO, int SL, int MODE>
 hipError_t launch_bwd_k(const BwdParams& p, hipStream_t stream) {
   const int64_t blocks = p.batch * int64_t(MODE == BWD_ADJOINT ? p.n_chunks - 1 : p.n_chunks) * p.groups;
   if (blocks == 0) return hipSuccess;
-  if (p.vec)
-    hipLaunchKernelGGL((bwd_kernel<IO, SL, MODE, true>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((bwd_kernel<IO, SL, MODE, false>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+  // The vector staging's accesses cover 16 token rows x 4 channels per wavefront: 32-byte row
+  // pieces in bf16.  The bf16 main pass, whose loads overlap a long walk, measured faster
+  // with the element-wise staging (one full 128-byte row per access); the adjoint pass and
+  // fp32 faster with the vectors.
+  constexpr bool kVecOk = MODE == BWD_ADJOINT || sizeof(IO) == 4;
+  if constexpr (kVecOk) {
+    if (p.vec) {
+      hipLaunchKernelGGL((bwd_kernel<IO, SL, MODE, true>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_kernel<IO, SL, MODE, false>), dim3(unsigned(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
