@@ -92,9 +92,11 @@ SLOTS_PER_TOKEN_SOFTPLUS = 14
 #             per (b, l, d): gate and its derivative (about 12), Dskip terms (2)      = 14
 SLOTS_BWD_PER_ELEMENT = 21
 SLOTS_BWD_PER_TOKEN_D = 14
-#   backward of fixed coefficients, per (b, l, d, n): h_t (2), lambda (1), Abar h (1), B u (1),
-#             readout (1), du (1), dB (1), dC (1), ddelta (3), dA (3), carry (1)        = 16
-SLOTS_BWD_TI_PER_ELEMENT = 16
+#   backward of fixed coefficients, per (b, l, d, n): h_t (2), lambda (1), readout (1), du (1),
+#             sum lambda h_{t-1} (1), sum lambda u (1, dB's), dC (1), carry (1)         = 9
+#             (dA and ddelta follow per (d, n) and chunk from the two sums: delta, B and
+#             dc/da are fixed)
+SLOTS_BWD_TI_PER_ELEMENT = 9
 
 
 def algorithmic_bytes(inp: s6_workloads.Inputs, want_last: bool, bias: bool = False) -> int:
