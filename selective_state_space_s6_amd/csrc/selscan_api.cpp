@@ -815,7 +815,9 @@ static int ssd_check(const selscan_ssd_dims* d, SsdPlan* pl) {
   if (d->headdim != 64 || (d->dstate != 64 && d->dstate != 128)) return SELSCAN_ERR_UNSUPPORTED;
   if (d->discretization != SELSCAN_DISC_ZOH && d->discretization != SELSCAN_DISC_EULER) return SELSCAN_ERR_UNSUPPORTED;
   const int64_t nc = (d->seqlen + 63) / 64;
-  if (d->batch * d->nheads * nc > (int64_t(1) << 31) - 1 || d->batch * d->nheads * d->dstate * 64 > (int64_t(1) << 36))
+  // (the on-chip kernels address a chunk of one head's x, z and y with 32-bit offsets)
+  if (d->batch * d->nheads * nc > (int64_t(1) << 31) - 1 || d->batch * d->nheads * d->dstate * 64 > (int64_t(1) << 36) ||
+      d->nheads * 64 * 64 * 2 >= (int64_t(1) << 31))
     return SELSCAN_ERR_UNSUPPORTED;
   if (d->path < 0 || d->path > 3 || d->segments < 0 || (d->segments != 0 && d->path != 3)) return SELSCAN_ERR_UNSUPPORTED;
   const int64_t items = d->batch * d->nheads, bhc = items * nc;

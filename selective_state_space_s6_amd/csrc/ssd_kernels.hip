@@ -315,64 +315,81 @@ struct ChunkRegs {
   uint32_t x[8];
 };
 
-// Loads address memory as a chunk base common to the workgroup plus a 32-bit offset per
-// thread, so that no 64-bit address per token stays live in vector registers.
-// WITH_C false: B and x only (the segment state pass reads no C).
-template <int N, bool WITH_C = true>
-__device__ __forceinline__ void load_chunk(ChunkRegs<N>& rg, const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
-  const int tid = threadIdx.x, sb = tid >> 5, lo = tid & 31;
+// A buffer resource over the rows of one stream from token l0 of its batch row (row r at
+// r * row_bytes from base0's row l0; width bytes used in a row), ending after the sequence's
+// last row: reads past the end return zero and writes past it are dropped, so a chunk's
+// padded tokens need no clamps or masks.  The chunk's own offsets stay small (32-bit).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base0, int64_t l0, int64_t L, int64_t row_bytes,
+                                                            int64_t width) {
+  const char* const p0 = static_cast<const char*>(base0) + l0 * row_bytes;
+  int64_t bytes = (L - l0 - 1) * row_bytes + width;
+  if (bytes > 0x7fffffff) bytes = 0x7fffffff;              // the chunk's offsets lie far below
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p0), (short)0, int(bytes), 0x00020000);
+}
+
+// Per-thread byte offsets of the chunk loads and of the output row (loop invariants).
+struct ChunkOffs {
+  uint32_t c;     // C piece tid (pieces tid + 256 k follow at k * 256 * 16 bytes)
+  uint32_t b;     // B word of token 8 sb (token 8 sb + j at j * N * 2 bytes)
+  uint32_t x;     // x (and z, y) pair of token 8 sb (token 8 sb + j at j * H * 128 bytes)
+  uint32_t d;     // delta of token lane
+};
+template <int N>
+__device__ __forceinline__ ChunkOffs chunk_offs(int64_t H) {
+  const int tid = threadIdx.x, sb = (tid >> 5) & 7, lo = tid & 31, lane = tid & 63;
+  ChunkOffs o;
+  o.c = uint32_t((tid / (N / 8)) * N * 2 + (tid % (N / 8)) * 16);
+  o.b = uint32_t(8 * sb * N * 2 + lo * (N / 32) * 2);
+  o.x = uint32_t(8 * sb * H * kP * 2 + 4 * lo);
+  o.d = uint32_t(lane * H * 2);
+  return o;
+}
+
+// One chunk's C, B and x into registers.  Tokens past the sequence end read zero, so B and x
+// of padded tokens never reach the state.  The values stay as loaded (a use here would wait
+// for the load).
+template <int N>
+__device__ __forceinline__ void load_chunk(ChunkRegs<N>& rg, const SsdParams& p, const ChunkOffs& o, int64_t b,
+                                           int64_t h, int64_t l0) {
   const int64_t L = p.L, H = p.H;
-  const int rows = int(L - l0 < kT ? L - l0 : kT);        // tokens of this chunk inside the sequence
-  const uint16_t* const Bc = static_cast<const uint16_t*>(p.B) + (b * L + l0) * N;
-  const uint16_t* const Cc = static_cast<const uint16_t*>(p.C) + (b * L + l0) * N;
-  const uint16_t* const xc = static_cast<const uint16_t*>(p.x) + ((b * L + l0) * H + h) * kP;
-  const uint32_t tok_stride = uint32_t(H) * kP;            // elements between tokens of x, z
-  // Tokens past the sequence end read the last token's row (in bounds).  The values stay
-  // as loaded (a use here would wait for the load); B, x and the step size of such tokens
-  // are zeroed when staged, and their C and z reach only outputs that are never stored.
+  const auto rB = rows_rsrc(static_cast<const uint16_t*>(p.B) + b * L * N, l0, L, N * 2, N * 2);
+  const auto rC = rows_rsrc(static_cast<const uint16_t*>(p.C) + b * L * N, l0, L, N * 2, N * 2);
+  const auto rX = rows_rsrc(static_cast<const uint16_t*>(p.x) + (b * L * H + h) * kP, l0, L, H * kP * 2, kP * 2);
+  const int tokX = int(H * kP * 2);
 #pragma unroll
-  for (int k = 0; k < ChunkRegs<N>::kCv; ++k) {
-    if (!WITH_C) break;
-    const int i = tid + 256 * k, t = i / (N / 8), n0 = (i % (N / 8)) * 8;
-    rg.c[k] = *reinterpret_cast<const uint4*>(Cc + uint32_t(min(t, rows - 1) * N + n0));
-  }
+  for (int k = 0; k < ChunkRegs<N>::kCv; ++k)
+    rg.c[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rC, o.c, k * 256 * 16, 0));
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int tc = min(8 * sb + j, rows - 1);
-    const uint32_t* const bs = reinterpret_cast<const uint32_t*>(Bc + uint32_t(tc * N + lo * (N / 32)));
     if constexpr (ChunkRegs<N>::kBw == 2) {
-      const uint2 v = *reinterpret_cast<const uint2*>(bs);
-      rg.b[j][0] = v.x;
-      rg.b[j][1] = v.y;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rB, o.b, j * N * 2, 0);
+      rg.b[j][0] = v[0];
+      rg.b[j][ChunkRegs<N>::kBw - 1] = v[1];
     } else {
-      rg.b[j][0] = *bs;
+      rg.b[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rB, o.b, j * N * 2, 0);
     }
-    rg.x[j] = *reinterpret_cast<const uint32_t*>(xc + (uint32_t(tc) * tok_stride + uint32_t(2 * lo)));
+    rg.x[j] = __builtin_amdgcn_raw_buffer_load_b32(rX, o.x, j * tokX, 0);
   }
 }
 
 // The step size of token (lane) of the chunk at l0, for the decay prefix every wavefront
-// forms (past the sequence end: the last token's, masked when used).
-__device__ __forceinline__ uint32_t load_dt(const SsdParams& p, int64_t b, int64_t h, int64_t l0) {
+// forms (zero past the sequence end).
+__device__ __forceinline__ uint32_t load_dt(const SsdParams& p, const ChunkOffs& o, int64_t b, int64_t h, int64_t l0) {
   const int64_t L = p.L, H = p.H;
-  const int rows = int(L - l0 < kT ? L - l0 : kT);
-  const int t = threadIdx.x & 63;
-  return static_cast<const uint16_t*>(p.delta)[(b * L + l0) * H + h + uint32_t(min(t, rows - 1)) * uint32_t(H)];
+  const auto rD = rows_rsrc(static_cast<const uint16_t*>(p.delta) + b * L * H + h, l0, L, H * 2, 2);
+  return __builtin_amdgcn_raw_buffer_load_b16(rD, o.d, 0, 0);
 }
 
-// z of tokens 8 sb + j0 .. + JN - 1 (sb = (t >> 5) & 7), channels 2 lo, 2 lo + 1
+// z of tokens 8 sb + j0 .. + JN - 1 (sb = (t >> 5) & 7), channels 2 lo, 2 lo + 1 (zero past
+// the sequence end, where no output is stored)
 template <int JN>
-__device__ __forceinline__ void load_gate(uint32_t (&zr)[8], const SsdParams& p, int64_t b, int64_t h, int64_t l0,
-                                          int j0) {
-  const int sb = (threadIdx.x >> 5) & 7, lo = threadIdx.x & 31;
+__device__ __forceinline__ void load_gate(uint32_t (&zr)[8], const SsdParams& p, const ChunkOffs& o, int64_t b,
+                                          int64_t h, int64_t l0, int j0) {
   const int64_t L = p.L, H = p.H;
-  const int rows = int(L - l0 < kT ? L - l0 : kT);
-  const uint16_t* const zc = static_cast<const uint16_t*>(p.z) + ((b * L + l0) * H + h) * kP;
+  const auto rZ = rows_rsrc(static_cast<const uint16_t*>(p.z) + (b * L * H + h) * kP, l0, L, H * kP * 2, kP * 2);
+  const int tokX = int(H * kP * 2);
 #pragma unroll
-  for (int j = 0; j < JN; ++j) {
-    const int t = min(8 * sb + j0 + j, rows - 1);          // past the end: read in bounds, never stored
-    zr[j] = *reinterpret_cast<const uint32_t*>(zc + (uint32_t(t) * uint32_t(H * kP) + uint32_t(2 * lo)));
-  }
+  for (int j = 0; j < JN; ++j) zr[j] = __builtin_amdgcn_raw_buffer_load_b32(rZ, o.x, (j0 + j) * tokX, 0);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront: within rows of 16 lanes by DPP row
@@ -505,10 +522,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int i = 0; i < 4; ++i) hs[kt][i] = h_in != nullptr ? h_in[pc * N + 16 * kt + 4 * q + i] : 0.f;
 
   ChunkRegs<N> rg;
-  if (stager) load_chunk<N>(rg, p, b, h, c_begin * kT);
-  uint32_t dtr = load_dt(p, b, h, c_begin * kT);
+  const ChunkOffs offs = chunk_offs<N>(H);
+  if (stager) load_chunk<N>(rg, p, offs, b, h, c_begin * kT);
+  uint32_t dtr = load_dt(p, offs, b, h, c_begin * kT);
   uint32_t zr[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  if (gate) load_gate<JN>(zr, p, b, h, c_begin * kT, j0);
+  if (gate) load_gate<JN>(zr, p, offs, b, h, c_begin * kT, j0);
   const float invA = A != 0.f ? 1.f / A : 0.f;
   for (int64_t chunk = c_begin; chunk < c_end; ++chunk) {
     const int64_t l0 = chunk * kT;
@@ -532,13 +550,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const uint4 cv = rg.c[k];
       *reinterpret_cast<uint4*>(&sC[t][n0]) = make_uint4(cv.x, cv.y, cv.z, cv.w);   // by value: keeps rg in registers
     }
-    // B and x of padded tokens are zero (they must not reach the state)
+    // (B and x of padded tokens were read as zero: they never reach the state)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bool ok = 8 * sb + j < rows;
-#pragma unroll
-      for (int e = 0; e < ChunkRegs<N>::kBw; ++e) rg.b[j][e] = ok ? rg.b[j][e] : 0u;
-      rg.x[j] = ok ? rg.x[j] : 0u;
       if constexpr (ChunkRegs<N>::kBw == 2)
         *reinterpret_cast<uint2*>(&sB[8 * sb + j][lo * kNV]) = make_uint2(rg.b[j][0], rg.b[j][1]);
       else
@@ -550,8 +564,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (stager) stage_bt<N>(rg.b, s_w, sBT, sb, lo);
     __builtin_amdgcn_sched_barrier(0);                     // the staged registers are free: reuse them
     if (chunk + 1 < c_end) {                               // lands during the arithmetic
-      if (stager) load_chunk<N>(rg, p, b, h, l0 + kT);
-      dtr = load_dt(p, b, h, l0 + kT);
+      if (stager) load_chunk<N>(rg, p, offs, b, h, l0 + kT);
+      dtr = load_dt(p, offs, b, h, l0 + kT);
     }
 
     // M = (C B^T) o decay o causal mask, 10 causal 16 x 16 tiles (ti, tj), tj <= ti, tile k of
@@ -639,7 +653,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __syncthreads();                                      // the output tile and B^T are complete
     state_update<N>(hs, sBT, sXT, pc, q, r, __builtin_amdgcn_exp2f(cum_end * kLog2e));
     // feed-through, gate, bf16 stores: tokens 8 sb + j0 .. + JN - 1, channels 2 lo, 2 lo + 1
-    uint16_t* const yc = yg + ((b * L + l0) * H + h) * kP;
     const uint4 xa = *reinterpret_cast<const uint4*>(&sXT[2 * lo][8 * sb]);      // x[8 sb + j][2 lo]
     const uint4 xb = *reinterpret_cast<const uint4*>(&sXT[2 * lo + 1][8 * sb]);  // x[8 sb + j][2 lo + 1]
     uint32_t yo[8];
@@ -655,17 +668,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
       yo[jj] = pack_bf16(y0, y1);
     }
-    if (rows == kT) {
+    {                                                      // stores past the sequence end are dropped
+      const auto rY = rows_rsrc(yg + (b * L * H + h) * kP, l0, L, H * kP * 2, kP * 2);
+      const int tokX = int(H * kP * 2);
 #pragma unroll
-      for (int jj = 0; jj < JN; ++jj)
-        *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j0 + jj) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[jj];
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < JN; ++jj)
-        if (8 * sb + j0 + jj < rows)
-          *reinterpret_cast<uint32_t*>(yc + (uint32_t(8 * sb + j0 + jj) * uint32_t(H * kP) + uint32_t(2 * lo))) = yo[jj];
+      for (int jj = 0; jj < JN; ++jj) __builtin_amdgcn_raw_buffer_store_b32(yo[jj], rY, offs.x, (j0 + jj) * tokX, 0);
     }
-    if (gate && chunk + 1 < c_end) load_gate<JN>(zr, p, b, h, l0 + kT, j0);   // lands during the next chunk
+    if (gate && chunk + 1 < c_end) load_gate<JN>(zr, p, offs, b, h, l0 + kT, j0);   // lands during the next chunk
   }
   if (p.last_state != nullptr && half == 0 && (!SEGS || seg == nseg - 1)) {   // (NW = 8: both halves hold the same state)
 #pragma unroll
