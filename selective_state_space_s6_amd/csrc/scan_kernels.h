@@ -496,8 +496,26 @@ void scan_kernel(ScanParams p) {
 // steps overwrite it (a wavefront's LDS accesses run in issue order, and a compiler fence
 // keeps that order).  Full tiles run in the loop; a ragged last tile runs after it with a
 // step count (its padded tokens must not touch the state).
+//
+// Partial readouts (selective coefficients): before the LDS transpose, the readouts of
+// states s and s ^ 1 are summed across the lane pair (a DPP add), so each channel's block
+// holds 8 state-pair rows: half the LDS bytes of the transpose and 7 instead of 15 adds in
+// the finalise, for 16 DPP adds per tile.  Time-invariant coefficients (a few VALU per state
+// and token, their K states already summed in the lane) keep 16 rows.
+//
+// Issue priority: a compute unit holds two or three workgroups at once, and its arbiter
+// prefers the oldest wavefront, so the first workgroup dealt to a compute unit ran ahead and
+// the last one finished its sequence alone, with one wavefront per SIMD to hide latency.  The
+// workgroups sharing a compute unit therefore take turns at the top priority: time is cut
+// into slices of 2^11 ticks of the 100 MHz constant clock (20.48 us), and in each slice the
+// workgroups of dispatch rounds r, r + 1 and r + 2 (mod 3) hold priorities 3, 2 and 1.  This
+// changes only the order in which ready instructions issue.  The clock is read after a
+// tile's barrier and acted on at the next tile's, so its latency is never waited for.
 
-constexpr int kChanP = 264;               // LDS block of one channel's 16 x 16 partial readouts (+8)
+// LDS block of one channel's partial readouts: 8 (pair-summed, selective) or 16 rows of 16
+// tokens, + 8 floats
+template <bool TI> struct part_rows { static constexpr int R = TI ? 16 : 8; static constexpr int kChanP = 16 * R + 8; };
+constexpr int kFairSliceShift = 11;       // priority rotation slice: 2^11 ticks of the 100 MHz clock
 
 // Wavefronts per workgroup: 4 for selective coefficients (u, delta, z, B, C to share);
 // 2 for time-invariant ones, where only u (and z) move per token and the per-tile work is
@@ -521,7 +539,7 @@ struct coop_lds {
   static constexpr int kNBuf = 3;
   static constexpr int kT4 = 16 * kRowPad;                      // a token tile of 4 vectors (16 channels)
   static constexpr int kSink = kT4 > kB ? kT4 : kB;             // writes of idle staging lanes and roles
-  static constexpr int kP = READOUT ? 4 * kChanP : 0;           // per wavefront
+  static constexpr int kP = READOUT ? 4 * part_rows<TI>::kChanP : 0;   // per wavefront
   static constexpr int kY = READOUT ? 2 * kTile * kRowY : 0;    // [2][16 tokens][kRowY]
   static constexpr int total = kNBuf * kBuf + kSink + W * kP + kY;
 };
@@ -572,10 +590,11 @@ __device__ __forceinline__ void static_for_impl(F&& f) {
 template <int Nn, typename F>
 __device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, Nn>(f); }
 
-// Position of (state lane r, token j) in a channel's partial-readout block: rows of 16
-// tokens, the four 4-token groups of row r XOR-rotated by (r >> 1) & 3 so that the
-// 128-bit row writes of eight neighbouring lanes, and the column reads of the finalise
-// (a channel block starts 8 banks after the previous one), hit distinct banks.
+// Position of (row r, token j) in a channel's partial-readout block: rows of 16 tokens, the
+// four 4-token groups of row r XOR-rotated by (r >> 1) & 3 so that the 128-bit row writes of
+// a channel's lanes (its eight even lanes, or all 16) spread evenly over the 32 banks, and the
+// column reads of the finalise (a channel block starts 8 banks after the previous one) hit
+// every bank twice, the least a 64-lane read can.
 __device__ __forceinline__ int part_pos(int r, int j) { return r * 16 + 4 * ((j >> 2) ^ ((r >> 1) & 3)) + (j & 3); }
 
 // The value lane L of this lane's 16-lane row holds (DPP row_newbcast; folded into the VOP2
@@ -803,6 +822,7 @@ void scan_kernel_coop(ScanParams p) {
   // lane that holds it, so that the input term is one multiply.  The exact ZOH form
   // (V_EXACT) and time-invariant coefficients read u and delta four tokens at a time.
   float dsum = 0.f;
+  constexpr int kChanP = part_rows<TI>::kChanP, PR = part_rows<TI>::R;
   float* const prow = sP + c * kChanP;
   const int cw = 4 * w + c;                  // step channel within the workgroup
   float4 rU4[2], rD4[2], rB4[2][K], rC4[2][K];
@@ -873,24 +893,40 @@ void scan_kernel_coop(ScanParams p) {
       }
       pacc[j] = acc;
     });
-    if (READOUT)
+    if (READOUT && PR == 16) {
       *reinterpret_cast<float4*>(prow + s * 16 + 4 * (grp ^ ((s >> 1) & 3))) =
           make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
+    } else if (READOUT) {
+      // states s and s ^ 1 summed across the lane pair (DPP quad_perm [1,0,3,2]); the even
+      // lane writes row s / 2
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pacc[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(pacc[j]), 0xB1, 0xF, 0xF, false));
+      // the sums stay in the common block (the compiler would sink them into the even lanes'
+      // branch, where the DPP move no longer folds into the add)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) __asm__ volatile("" : "+v"(pacc[j]));
+      if ((s & 1) == 0) {
+        const int r = s >> 1;
+        *reinterpret_cast<float4*>(prow + r * 16 + 4 * (grp ^ ((r >> 1) & 3))) =
+            make_float4(pacc[0], pacc[1], pacc[2], pacc[3]);
+      }
+    }
   };
 
-  // ---- finalise: the 16 partial readouts of (token it, channel 4w + ic), feed-through and
-  // gate with u and z from the staged tile, result into the y tile.
-  float part[16], uF = 0.f, zF = 0.f;
+  // ---- finalise: the PR (pair-summed) partial readouts of (token it, channel 4w + ic),
+  // feed-through and gate with u and z from the staged tile, result into the y tile.
+  float part[PR], uF = 0.f, zF = 0.f;
   auto fin_read = [&](int q) __attribute__((always_inline)) {
     const float* const col = sP + ic * kChanP;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part[r] = col[part_pos(r, it)];
+    for (int r = 0; r < PR; ++r) part[r] = col[part_pos(r, it)];
     uF = bufU(q)[(4 * w + ic) * kRowPad + it];
     zF = bufZ(q)[(4 * w + ic) * kRowPad + it];
   };
   auto fin_sum = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int wd = 8; wd >= 1; wd >>= 1) {
+    for (int wd = PR / 2; wd >= 1; wd >>= 1) {
 #pragma unroll
       for (int r = 0; r < wd; ++r) part[r] += part[r + wd];
     }
@@ -939,6 +975,15 @@ void scan_kernel_coop(ScanParams p) {
   };
   // RES = t mod 6, known at compile time: the LDS buffers (t mod 3), the y tile (t mod 2) and
   // the load set ((t + 1) mod NS) are constants, folded into the instructions' offsets
+  // the issue-priority turn of this workgroup's dispatch round (see the kernel's header)
+  const uint32_t fair_round = p.sched_round > 0 ? uint32_t(blockIdx.x) / uint32_t(p.sched_round) : 0u;
+  uint64_t fair_clock = 0;                     // read after the previous tile's barrier
+  auto fair_share = [&]() __attribute__((always_inline)) {
+    const uint32_t ph = (uint32_t(fair_clock >> kFairSliceShift) + fair_round) % 3u;
+    if (ph == 0) __builtin_amdgcn_s_setprio(3);
+    else if (ph == 1) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(1);
+  };
   auto iteration = [&](int t, auto res_tag, auto var_tag, auto fin_tag, auto yst_tag) __attribute__((always_inline)) {
     constexpr int RES = decltype(res_tag)::value;
     constexpr bool FIN = decltype(fin_tag)::value && READOUT;
@@ -946,8 +991,10 @@ void scan_kernel_coop(ScanParams p) {
     constexpr int q0 = RES % 3, q1 = (RES + 1) % 3, qm = (RES + 2) % 3;   // buffers of t, t+1, t-1
     using SET = std::integral_constant<int, (RES + 1) % NS>;
     checkpoint(t);
+    fair_share();
     region();
     block_lds_sync();
+    fair_clock = __builtin_amdgcn_s_memrealtime();
     if (FIN) fin_read(qm);                             // tile t-1
     if (YST) y_store(t - 2, RES & 1);                  // tile t-2
     order_lds();

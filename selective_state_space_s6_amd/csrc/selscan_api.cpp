@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "scan_launch.h"
@@ -167,6 +168,28 @@ int check_pointers(const void* u, const void* delta, const float* A, const void*
   return SELSCAN_OK;
 }
 
+// Compute units of the GPU that `stream` belongs to, looked up once per GPU; 0 if the lookup
+// fails (the issue-priority rotation of scan_kernel_coop then takes every workgroup as round 0).
+constexpr int kMaxCuDevices = 64;
+std::atomic<int> g_cu_count[kMaxCuDevices];
+int compute_units(hipStream_t stream) {
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    (void)hipGetLastError();              // not an error of this call's launches
+    return 0;
+  }
+  if (dev < 0 || dev >= kMaxCuDevices) return 0;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Kernel parameters of one forward call (chunk plan, options, path choice); the chunked
 // path's workspace pointers are set by the caller.
 selscan::ScanParams scan_params(const void* u, const void* delta, const float* delta_bias, const float* A,
@@ -232,6 +255,7 @@ int run(const void* u, const void* delta, const float* delta_bias, const float* 
     return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
   }
   selscan::ScanParams p = scan_params(u, delta, delta_bias, A, B, C, Dskip, z, y, h0, last_state, d, plan);
+  p.sched_round = compute_units(stream);
   if (!plan.chunked) {
     e = selscan::launch_scan_pass(selscan::kPassSingle, plan.bf16, plan.ti, plan.S, plan.K, p, stream);
     return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
@@ -552,6 +576,7 @@ int bwd_run(const void* u, const void* delta, const float* delta_bias, const flo
   if (plan.n_chunks > 1) {
     // the state entering every chunk: the forward's chunked state pass and prefix
     selscan::ScanParams f = scan_params(u, delta, delta_bias, A, B, C, Dskip, z, nullptr, h0, nullptr, d, plan.fwd);
+    f.sched_round = compute_units(stream);
     f.ws_state = reinterpret_cast<float*>(ws + plan.off_state);
     f.ws_dsum = reinterpret_cast<float*>(ws + plan.off_dsum);
     if (f.pipelined) {                                    // the state pass also checkpoints its tiles
