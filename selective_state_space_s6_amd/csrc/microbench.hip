@@ -67,7 +67,12 @@ __global__ __launch_bounds__(kThreads) void exp_kernel(float* out, int iters, fl
 }
 
 // kChains chains x[c] = bcast15(x[c]) * a: the row-broadcast operand folds into the multiply
-__global__ __launch_bounds__(kThreads) void dpp_kernel(float* out, int iters, float a, uint64_t* clk) {
+// (one v_mul_f32_dpp) only when the other operand is a VGPR, as in the scan, where it is a
+// per-lane constant; a is therefore held in a VGPR (a multiply by an SGPR would issue a
+// separate v_mov_b32_dpp first)
+__global__ __launch_bounds__(kThreads) void dpp_kernel(float* out, int iters, float a_arg, uint64_t* clk) {
+  float a = a_arg;
+  __asm__ volatile("" : "+v"(a));
   float x[kChains];
 #pragma unroll
   for (int c = 0; c < kChains; ++c) x[c] = float(threadIdx.x) * 1e-3f + float(c);

@@ -508,7 +508,8 @@ void scan_kernel(ScanParams p) {
 // the last one finished its sequence alone, with one wavefront per SIMD to hide latency.  The
 // workgroups sharing a compute unit therefore take turns at the top priority: time is cut
 // into slices of 2^11 ticks of the 100 MHz constant clock (20.48 us), and in each slice the
-// workgroups of dispatch rounds r, r + 1 and r + 2 (mod 3) hold priorities 3, 2 and 1.  This
+// workgroups of dispatch rounds r, r + 1 and r + 2 (mod 3) hold priorities 3, 2 and 1 (when the
+// whole grid is resident at once; a longer grid keeps its compute units full by itself).  This
 // changes only the order in which ready instructions issue.  The clock is read after a
 // tile's barrier and acted on at the next tile's, so its latency is never waited for.
 
@@ -976,9 +977,13 @@ void scan_kernel_coop(ScanParams p) {
   // RES = t mod 6, known at compile time: the LDS buffers (t mod 3), the y tile (t mod 2) and
   // the load set ((t + 1) mod NS) are constants, folded into the instructions' offsets
   // the issue-priority turn of this workgroup's dispatch round (see the kernel's header)
-  const uint32_t fair_round = p.sched_round > 0 ? uint32_t(blockIdx.x) / uint32_t(p.sched_round) : 0u;
+  // (only when the whole grid is resident at once, at most four workgroups per compute unit:
+  // with more, finished workgroups are replaced and the compute units stay full anyway)
+  const bool fair = p.sched_round > 0 && gridDim.x <= 4u * uint32_t(p.sched_round);
+  const uint32_t fair_round = fair ? uint32_t(blockIdx.x) / uint32_t(p.sched_round) : 0u;
   uint64_t fair_clock = 0;                     // read after the previous tile's barrier
   auto fair_share = [&]() __attribute__((always_inline)) {
+    if (!fair) return;
     const uint32_t ph = (uint32_t(fair_clock >> kFairSliceShift) + fair_round) % 3u;
     if (ph == 0) __builtin_amdgcn_s_setprio(3);
     else if (ph == 1) __builtin_amdgcn_s_setprio(2);
@@ -994,7 +999,7 @@ void scan_kernel_coop(ScanParams p) {
     fair_share();
     region();
     block_lds_sync();
-    fair_clock = __builtin_amdgcn_s_memrealtime();
+    if (fair) fair_clock = __builtin_amdgcn_s_memrealtime();
     if (FIN) fin_read(qm);                             // tile t-1
     if (YST) y_store(t - 2, RES & 1);                  // tile t-2
     order_lds();

@@ -46,8 +46,8 @@ struct ScanParams {
   int32_t state_all;    // scan_kernel_coop: the state pass runs the last chunk too (its end
                         //    state is never carried; wanted for its checkpoints)
   int32_t sched_round;  // workgroups the GPU deals out per round (its compute units; 0 if
-                        //    unknown): workgroup b arrives on its compute unit in round
-                        //    b / sched_round, which sets its turn in scan_kernel_coop's
+                        //    unknown: no rotation): workgroup b arrives on its compute unit in
+                        //    round b / sched_round, which sets its turn in scan_kernel_coop's
                         //    issue-priority rotation
 };
 
