@@ -211,9 +211,23 @@ void conv_ti_kernel(ConvParams p) {
   typename Io::raw_t nxt = load_u(0);
   stage_u(sU[0], nxt);
   if (ntile > 1) nxt = load_u(kSup);
+  // The two workgroups sharing a compute unit take turns at the top issue priority, in slices of
+  // 2^11 ticks of the 100 MHz clock (the arbiter otherwise prefers the older one, and the
+  // younger finishes alone); only when the whole grid is resident at once (two per compute
+  // unit).  The clock is read after a super-tile's barrier and used at the next one's.
+  const bool fair = p.sched_round > 0 && gridDim.x <= 2u * uint32_t(p.sched_round);
+  const uint32_t fair_round = fair ? uint32_t(blockIdx.x) / uint32_t(p.sched_round) : 0u;
+  uint64_t fair_clock = 0;
   for (int64_t it = 0; it < ntile; ++it) {
     const int cur = int(it & 1);
+    if (fair) {
+      const uint32_t ph = (uint32_t(fair_clock >> 11) + fair_round) % 3u;
+      if (ph == 0) __builtin_amdgcn_s_setprio(3);
+      else if (ph == 1) __builtin_amdgcn_s_setprio(2);
+      else __builtin_amdgcn_s_setprio(1);
+    }
     __syncthreads();                                      // tile it staged; the other buffer and sY are free
+    if (fair) fair_clock = __builtin_amdgcn_s_memrealtime();
     typename Io::raw_t zr = Io::zero();
     if (zb != nullptr && qvalid && it * kSup + tt < L) zr = Io::load(zb, (it * kSup + tt) * p.z_sl + dq);
     const float* const uc = sU[cur] + w * kRow;

@@ -114,6 +114,8 @@ struct ConvParams {
   int32_t euler, dxf, softplus;
   int64_t batch, L, D, N;
   int64_t u_sb, u_sl, z_sb, z_sl, y_sb, y_sl, B_sd, C_sd;
+  int32_t sched_round;       // compute units of the GPU (0 if unknown): the workgroup's dispatch
+                             //    round, blockIdx / sched_round, sets its issue-priority turn
 };
 hipError_t launch_conv_ti(bool bf16, const ConvParams& p, hipStream_t stream);
 

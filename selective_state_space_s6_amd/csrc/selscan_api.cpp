@@ -251,6 +251,7 @@ int run(const void* u, const void* delta, const float* delta_bias, const float* 
     c.batch = d.batch; c.L = d.seqlen; c.D = d.dim; c.N = d.dstate;
     c.u_sb = d.u_sb; c.u_sl = d.u_sl; c.z_sb = d.z_sb; c.z_sl = d.z_sl; c.y_sb = d.y_sb; c.y_sl = d.y_sl;
     c.B_sd = d.B_sd; c.C_sd = d.C_sd;
+    c.sched_round = compute_units(stream);
     e = selscan::launch_conv_ti(plan.bf16, c, stream);
     return e == hipSuccess ? SELSCAN_OK : hip_fail(e);
   }
