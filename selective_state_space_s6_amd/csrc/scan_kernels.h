@@ -630,9 +630,9 @@ void scan_kernel_coop(ScanParams p) {
   constexpr int ES = T::kBytes;
   constexpr uint32_t kOOB = 0x80000000u;
   constexpr int kRsrcWord3 = 0x00020000;
-  // tiles of global loads in flight: measured best at 3 for bf16 and 2 for fp32 (whose
-  // load sets are twice as wide); 1 for 64 states per channel
-  constexpr int NS = K >= 4 ? 1 : (ES == 2 ? 3 : 2);
+  // tiles of global loads in flight: measured best at 3 for both element types (fp32 at 130
+  // VGPRs, within the three wavefronts per SIMD its grids take); 1 for 64 states per channel
+  constexpr int NS = K >= 4 ? 1 : 3;
 
   extern __shared__ __align__(16) float smem[];
   const int lane = threadIdx.x & 63;
