@@ -633,6 +633,9 @@ void scan_kernel_coop(ScanParams p) {
   // tiles of global loads in flight: measured best at 3 for both element types (fp32 at 130
   // VGPRs, within the three wavefronts per SIMD its grids take); 1 for 64 states per channel
   constexpr int NS = K >= 4 ? 1 : 3;
+  // the loop is unrolled by six (below): a tile's load set, (t + 1) mod NS at its issue and at
+  // its staging NS iterations later, is the same compile-time residue only if NS divides 6
+  static_assert(6 % NS == 0, "load depth must divide the six-fold unroll");
 
   extern __shared__ __align__(16) float smem[];
   const int lane = threadIdx.x & 63;
