@@ -788,12 +788,14 @@ static void ssd_set_segments(SsdPlan& pl, int64_t count) {
 // Modelled time (us, N = 128) of the on-chip path over `count` segments, from times measured
 // on MI355X (256 CUs): the output walk costs t_pair per 64-token chunk for each of two
 // workgroups sharing a CU (four wavefronts each), t_alone for a workgroup alone on its CU,
-// and its workgroups are dealt out in rounds of two per CU; the segment state pass costs
+// t_alone8 when every workgroup has a CU of its own and so runs eight wavefronts (measured on
+// the whole-sequence walk at 130M widths: 0.142 ms for 32 chunks), and its workgroups are
+// dealt out in rounds of two per CU; the segment state pass costs
 // t_state1 per chunk alone on a CU plus t_state_more per further workgroup sharing it (up to
 // four at once); the segment carries move every segment state twice at about 5 TB/s; and
 // splitting at all costs two more launches and the carried-in states' loads (t_split).
 static double ssd_onchip_cost(int64_t items, int64_t nc, int64_t dstate, int64_t count) {
-  constexpr double t_pair = 6.25, t_alone = 4.1, t_state1 = 1.6, t_state_more = 0.6, t_split = 12.0;
+  constexpr double t_pair = 6.25, t_alone = 4.1, t_alone8 = 4.45, t_state1 = 1.6, t_state_more = 0.6, t_split = 12.0;
   constexpr int64_t kCUs = 256;
   SsdPlan pl;
   pl.n_chunks = nc;
@@ -802,7 +804,7 @@ static double ssd_onchip_cost(int64_t items, int64_t nc, int64_t dstate, int64_t
   const int64_t w = items * pl.n_seg;
   double t;
   if (w <= kCUs) {
-    t = len * t_alone;                                   // one eight-wavefront workgroup per CU
+    t = len * t_alone8;                                  // one eight-wavefront workgroup per CU
   } else {
     const int64_t full = w / (2 * kCUs), rem = w % (2 * kCUs);
     t = double(full) * len * t_pair + (rem == 0 ? 0.0 : rem <= kCUs ? len * t_alone : len * t_pair);
