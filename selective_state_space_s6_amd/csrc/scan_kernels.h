@@ -977,8 +977,6 @@ void scan_kernel_coop(ScanParams p) {
       }
     }
   };
-  // RES = t mod 6, known at compile time: the LDS buffers (t mod 3), the y tile (t mod 2) and
-  // the load set ((t + 1) mod NS) are constants, folded into the instructions' offsets
   // the issue-priority turn of this workgroup's dispatch round (see the kernel's header)
   // (only when the whole grid is resident at once, at most four workgroups per compute unit:
   // with more, finished workgroups are replaced and the compute units stay full anyway)
@@ -992,6 +990,8 @@ void scan_kernel_coop(ScanParams p) {
     else if (ph == 1) __builtin_amdgcn_s_setprio(2);
     else __builtin_amdgcn_s_setprio(1);
   };
+  // RES = t mod 6, known at compile time: the LDS buffers (t mod 3), the y tile (t mod 2) and
+  // the load set ((t + 1) mod NS) are constants, folded into the instructions' offsets
   auto iteration = [&](int t, auto res_tag, auto var_tag, auto fin_tag, auto yst_tag) __attribute__((always_inline)) {
     constexpr int RES = decltype(res_tag)::value;
     constexpr bool FIN = decltype(fin_tag)::value && READOUT;
