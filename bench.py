@@ -333,7 +333,49 @@ def run_microbench():
                        "gbs": round(moved / (ms.value * 1e-3) / 1e9, 1)})
     out["bandwidth"] = bw
     out["wall_clock_khz"] = wall_khz
+    out["arbitration"] = arbitration_probe(lib)
     print(json.dumps({"microbench": out}), flush=True)
+
+
+def arbitration_probe(lib) -> list:
+    """The arbitration probe of libselscan_microbench.so: 2.5 workgroups of four wavefronts per
+    compute unit (the long-context scan's grid shape), each repeating 64 FMAs and a barrier,
+    with 40 KB of LDS per workgroup (at most four per compute unit), without and with the
+    scan's issue-priority rotation.  Reports where the dispatcher put the workgroups (per
+    compute unit, per SIMD) and the wavefronts' durations by how many share their SIMD."""
+    import ctypes
+    import collections
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = (5 * cus) // 2, 3000
+    lib.selscan_mb_arbiter.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_float)]
+    res = []
+    for rotate in (0, 1):
+        rec = (ctypes.c_uint64 * (blocks * 16))()
+        ms = ctypes.c_float()
+        if lib.selscan_mb_arbiter(rotate, blocks, iters, 40960, rec, ctypes.byref(ms)) != 0:
+            raise RuntimeError("arbitration probe failed (hip %d)" % lib.selscan_mb_last_error())
+        a = np.frombuffer(rec, dtype=np.uint64).reshape(blocks * 4, 4).astype(np.int64)
+        t0, t1, hw, xcc = a[:, 0], a[:, 1], a[:, 2], a[:, 3] & 0xF
+        # HW_ID: SIMD bits 5:4, compute unit 11:8, shader array 12, shader engine 15:13
+        cu = xcc * 1000 + ((hw >> 13) & 7) * 100 + ((hw >> 12) & 1) * 16 + ((hw >> 8) & 0xF)
+        simd = cu * 4 + ((hw >> 4) & 3)
+        wg_per_cu = collections.Counter(cu[0::4].tolist())
+        waves_per_simd = collections.Counter(simd.tolist())
+        dur = (t1 - t0) * 1e-2                                   # 100 MHz ticks -> us
+        by = collections.defaultdict(list)
+        for i in range(blocks * 4):
+            by[waves_per_simd[int(simd[i])]].append(float(dur[i]))
+        res.append({"rotate": rotate, "workgroups": blocks, "kernel_ms": round(ms.value, 4),
+                    "span_us": round(float((t1.max() - t0.min()) * 1e-2), 1),
+                    "starts_within_us": round(float((t0.max() - t0.min()) * 1e-2), 2),
+                    "workgroups_per_cu": {str(k): v for k, v in sorted(collections.Counter(wg_per_cu.values()).items())},
+                    "waves_per_simd": {str(k): v for k, v in sorted(collections.Counter(waves_per_simd.values()).items())},
+                    "wave_us_by_waves_on_simd": {str(k): {"min": round(min(v), 1), "mean": round(float(np.mean(v)), 1),
+                                                          "max": round(max(v), 1), "waves": len(v)}
+                                                 for k, v in sorted(by.items())}})
+    return res
 
 
 def time_calls(step, stream, steps: int, warmup: int) -> dict:

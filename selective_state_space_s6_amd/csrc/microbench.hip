@@ -8,6 +8,11 @@
 //             lane (v_mul_f32 with row_newbcast), the form the scan uses for u and delta
 //   copy    : streaming 16-byte-per-lane copy of one buffer into another (HBM read + write)
 //   fill    : streaming 16-byte-per-lane writes (HBM write only)
+//   arbiter : workgroups of four wavefronts that repeat 64 FMAs and a workgroup barrier (the
+//             per-tile shape of the scan), launched 2.5 per compute unit; every wavefront
+//             records its compute unit, SIMD, start and end, with and without the scan's
+//             issue-priority rotation (how the dispatcher places workgroups, and how the
+//             arbiter shares a SIMD between the wavefronts of workgroups dealt to it in turn)
 // Every probe records, in wavefront 0 of workgroup 0, the shader-clock counter (clock64) and the
 // constant-rate wall counter (wall_clock64) around its loop, so that the clock the GPU ran at is
 // measured too.  Host entry points return the kernel time from HIP events on their own stream.
@@ -90,6 +95,50 @@ __global__ __launch_bounds__(kThreads) void dpp_kernel(float* out, int iters, fl
 #pragma unroll
   for (int c = 0; c < kChains; ++c) s += x[c];
   out[blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+// Arbitration probe.  Each wavefront runs `iters` iterations of 64 FMAs (8 chains) and a
+// workgroup barrier; `lds` bytes of dynamic LDS per workgroup bound how many share a compute
+// unit.  Lane 0 of every wavefront records [start, end] (s_memrealtime, 100 MHz), HW_ID and
+// XCC_ID into rec[(block * 4 + wave) * 4 ...].  ROTATE: the workgroups of dispatch rounds
+// (block / cus) take turns at the top issue priority in slices of 2^11 ticks, as the scan does.
+template <bool ROTATE>
+__global__ __launch_bounds__(kThreads) void arbiter_kernel(float* out, uint64_t* rec, int iters, float a, float b,
+                                                           int cus) {
+  extern __shared__ float lds_pad[];
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+  const uint32_t round = uint32_t(blockIdx.x) / uint32_t(cus);
+  uint64_t clk = 0;
+  float x[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) x[c] = float(threadIdx.x) * 1e-3f + float(c);
+  for (int i = 0; i < iters; ++i) {
+    if (ROTATE) {
+      const uint32_t ph = (uint32_t(clk >> 11) + round) % 3u;
+      if (ph == 0) __builtin_amdgcn_s_setprio(3);
+      else if (ph == 1) __builtin_amdgcn_s_setprio(2);
+      else __builtin_amdgcn_s_setprio(1);
+    }
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) x[c] = fmaf(x[c], a, b);
+    }
+    __syncthreads();
+    if (ROTATE) clk = __builtin_amdgcn_s_memrealtime();
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) sum += x[c];
+  if (iters < 0) lds_pad[threadIdx.x] = sum;   // never taken; keeps the LDS request
+  out[blockIdx.x * kThreads + threadIdx.x] = sum;
+  if ((threadIdx.x & 63) == 0) {
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    uint64_t* q = rec + (size_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 4;
+    q[0] = t0; q[1] = t1; q[2] = hw; q[3] = xcc;
+  }
 }
 
 // RATIO fma per exp2: kChains exp2 chains and kChains fma chains, each fma chain stepped RATIO
@@ -224,6 +273,35 @@ int selscan_mb_bandwidth(int kind, int64_t bytes, int blocks, int reps, float* m
   (void)hipStreamDestroy(s);
   (void)hipFree(a);
   (void)hipFree(b);
+  return rc;
+}
+
+// Arbitration probe (see arbiter_kernel): `blocks` workgroups, `iters` iterations, `lds_bytes`
+// of LDS per workgroup (at most 65536), rotate 0/1.  rec (host, blocks * 16 values) receives
+// each wavefront's [start, end, HW_ID, XCC_ID]; ms the kernel time (HIP events, second run).
+int selscan_mb_arbiter(int rotate, int blocks, int iters, int lds_bytes, uint64_t* rec, float* ms) {
+  if (blocks < 1 || iters < 1 || lds_bytes < 0 || lds_bytes > 65536 || rec == nullptr) return -2;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return -1;
+  float* out = nullptr;
+  uint64_t* drec = nullptr;
+  hipStream_t s = nullptr;
+  const size_t rec_bytes = size_t(blocks) * 16 * sizeof(uint64_t);
+  if (hipMalloc(&out, size_t(blocks) * kThreads * sizeof(float)) != hipSuccess) return -1;
+  if (hipMalloc(&drec, rec_bytes) != hipSuccess) { (void)hipFree(out); return -1; }
+  if (hipStreamCreate(&s) != hipSuccess) { (void)hipFree(out); (void)hipFree(drec); return -1; }
+  auto launch = [&]() {
+    const dim3 g{unsigned(blocks)}, t{unsigned(kThreads)};
+    if (rotate) hipLaunchKernelGGL(arbiter_kernel<true>, g, t, size_t(lds_bytes), s, out, drec, iters, 0.999f, 1e-3f, cus);
+    else hipLaunchKernelGGL(arbiter_kernel<false>, g, t, size_t(lds_bytes), s, out, drec, iters, 0.999f, 1e-3f, cus);
+  };
+  launch();                                                   // warm-up
+  int rc = hipStreamSynchronize(s) == hipSuccess ? timed(launch, s, ms) : -1;
+  if (rc == 0 && hipMemcpy(rec, drec, rec_bytes, hipMemcpyDeviceToHost) != hipSuccess) rc = -1;
+  (void)hipStreamDestroy(s);
+  (void)hipFree(out);
+  (void)hipFree(drec);
   return rc;
 }
 
