@@ -29,7 +29,9 @@ evicts the L2 caches and the 256 MB Infinity Cache ("cold_cache").
 
 --microbench instead prints the issue-rate and bandwidth probes of libselscan_microbench.so
 (fp32 FMA and v_exp_f32 rates against wavefronts per SIMD, their overlap, streaming copy and
-write bandwidth, and the shader clock the GPU held), the practical roofs of the scan.
+write bandwidth, and the shader clock the GPU held), the practical roofs of the scan, and the
+arbitration probe (where 2.5 workgroups per compute unit are placed and how long their
+wavefronts run, without and with the scan's issue-priority rotation).
 """
 from __future__ import annotations
 
